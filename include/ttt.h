@@ -1,0 +1,189 @@
+/*
+ * ttt.h -- C ABI of the MI355X (gfx950) TTT-E2E test-time inner loop.
+ *
+ * The method (End-to-End Test-Time Training for Long Context): a standard
+ * decoder-only Transformer with sliding-window attention reads its context
+ * in chunks ("mini-batches", ~1K tokens at the 3B operating point, podcast
+ * 6:36) and, for each chunk, runs the forward pass, takes the next-token
+ * cross-entropy at the end of the network (NVIDIA blog, "Our method"),
+ * back-propagates into the MLP weights of the last quarter of the blocks
+ * only (podcast 6:36 and 7:08; forum post TL;DR "Inner Loop") and applies a
+ * plain SGD step before the next chunk.  Generation afterwards has constant
+ * per-token cost (paper summary "Key claims"; blog Figure 1 caption).
+ *
+ * Conventions for every call:
+ *  - Every function returns TTT_OK (0) or a negative ttt_status; nothing
+ *    throws, aborts or exits.  ttt_last_error() gives a message for the
+ *    last failure on the calling thread.
+ *  - Pointers documented "device" are HIP device memory owned by the
+ *    caller; they must stay valid until the stream has executed the call.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue
+ *    work and return; outputs are valid after the stream is synchronised.
+ *    Calls that must report a device-detected error (bad token, non-finite
+ *    loss) synchronise the stream before returning.
+ *  - A model handle is not thread-safe; separate handles are independent.
+ *  - The library performs no device allocation of its own: all device
+ *    state lives in the caller's workspace (ttt_workspace_bytes).
+ */
+#ifndef TTT_H
+#define TTT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TTT_OK = 0,
+  TTT_ERR_ARG = -1,        /* invalid argument (NULL, size out of range, non-finite lr) */
+  TTT_ERR_CONFIG = -2,     /* configuration not supported (see ttt_config) */
+  TTT_ERR_HIP = -3,        /* a HIP runtime call failed */
+  TTT_ERR_TOKEN = -4,      /* a token id outside [0, vocab) was read */
+  TTT_ERR_NONFINITE = -5,  /* a chunk loss was not finite */
+  TTT_ERR_STATE = -6,      /* call out of order (decode before prefill) */
+  TTT_ERR_WORKSPACE = -7   /* workspace missing, misaligned or too small */
+} ttt_status;
+
+enum { TTT_MLP_GELU = 0, TTT_MLP_SWIGLU = 1 };
+enum { TTT_FP32 = 0, TTT_BF16 = 1 };
+
+/*
+ * Model shape and capacity.  Architecture readings (where the pages are
+ * silent): pre-LN blocks, LayerNorm without affine parameters (eps ln_eps),
+ * final LayerNorm before an untied head, no biases, multi-head attention,
+ * rotate-half RoPE on absolute positions (base rope_base, float64 angles),
+ * window = number of keys a query sees (itself included).
+ *
+ * Supported: head_dim in {16, 32, 64, 96, 128}; n_heads * head_dim ==
+ * d_model; d_model % 16 == 0; d_ff % 16 == 0; vocab % 8 == 0;
+ * 1 <= n_fast <= n_layers; window >= 1; 1 <= max_chunk.
+ */
+typedef struct {
+  int32_t n_layers, d_model, n_heads, head_dim, d_ff, vocab, window;
+  int32_t n_fast;        /* the last n_fast blocks' MLPs are the fast weights */
+  int32_t mlp;           /* TTT_MLP_GELU (exact erf) or TTT_MLP_SWIGLU */
+  int32_t dtype;         /* TTT_BF16: bf16 weights/activations, fp32 accumulate,
+                            fp32 master of the fast weights; TTT_FP32: check mode */
+  float rope_base;       /* 10000 */
+  float ln_eps;          /* 1e-5 */
+  int32_t max_chunk;     /* largest chunk a prefill call may use */
+  int32_t prefill_block; /* tokens per frozen-layer block; 0 = default (8192) */
+} ttt_config;
+
+/* Workspace bytes needed for `cfg` (device memory, 256-byte aligned). */
+int ttt_workspace_bytes(const ttt_config* cfg, size_t* bytes);
+
+/*
+ * Create a model.  `weights` is a host array of `n_weights` device pointers
+ * in canonical order and layout, element type bf16 (TTT_BF16) or float
+ * (TTT_FP32):
+ *   E [vocab][d_model];
+ *   for each layer: Wq, Wk, Wv, Wo [d_model][d_model], then
+ *     GELU:   W1 [d_model][d_ff], W2 [d_ff][d_model]
+ *     SwiGLU: Wg [d_model][d_ff], Wu [d_model][d_ff], Wd [d_ff][d_model];
+ *   U [d_model][vocab].
+ * Every matrix is [in][out] row-major (a layer computes y = x W).  The
+ * weights are copied into the workspace (in the library's own layout), so
+ * the caller may free them after the stream has executed the call.
+ * `workspace` (device, ws_bytes >= ttt_workspace_bytes) is owned by the
+ * caller and must outlive the model.  On success *out receives a handle in
+ * the reset state.
+ */
+int ttt_model_load(const ttt_config* cfg, const void* const* weights, int32_t n_weights,
+                   void* workspace, size_t ws_bytes, void* stream, struct ttt_model** out);
+
+/*
+ * The inner loop over a whole context.  Resets the model (fast weights back
+ * to their loaded values, empty K/V rings), then for each chunk k of
+ * positions [k*chunk, min((k+1)*chunk, T)) and each of `steps` steps:
+ * forward with the current fast weights (attention over the window of
+ * earlier positions, whose K/V are kept as computed when read), mean
+ * next-token cross-entropy over the chunk's targets (position t predicts
+ * tokens[t+1]; the last position has none), gradient into the fast MLP
+ * weights only, SGD phi <- phi - lr * g.
+ *   tokens       device int32 [T], 2 <= T
+ *   chunk        1 <= chunk <= max_chunk
+ *   lr           finite
+ *   steps        >= 1
+ *   chunk_losses device float [ceil(T/chunk) * steps], the loss of each
+ *                step before its update (natural log); a chunk with no
+ *                target reports 0 and makes no update.
+ * Errors: TTT_ERR_TOKEN (a token outside [0, vocab)), TTT_ERR_NONFINITE;
+ * both are detected on the device and reported after a stream sync.
+ */
+int ttt_prefill(struct ttt_model* m, const int32_t* tokens, int64_t T, int32_t chunk, float lr,
+                int32_t steps, float* chunk_losses, void* stream);
+
+/*
+ * Copy fast-weight matrix `mat` of fast layer `fast_idx` (0 = the first
+ * fast layer) as float32 in canonical [in][out] layout into `dst` (device,
+ * n floats, n == rows*cols).  mat: GELU 0 = W1, 1 = W2; SwiGLU 0 = Wg,
+ * 1 = Wu, 2 = Wd.
+ */
+int ttt_fast_weight(struct ttt_model* m, int32_t fast_idx, int32_t mat, float* dst, int64_t n,
+                    void* stream);
+
+/*
+ * One greedy decode step after ttt_prefill (or a previous decode step).
+ * The first call emits argmax of the last prefill position's logits; every
+ * call then reads the emitted token at the next position (its K/V join the
+ * rings) and prepares the next argmax (lowest id on ties).  When `chunk`
+ * decode positions are complete, that chunk makes the same update as a
+ * prefill chunk.
+ *   next_token  device int32 [1]: the token emitted by this call
+ *   logits      device float [vocab] or NULL: logits of the position read
+ *               by this call (whose argmax the next call emits)
+ *   update_loss device float [1] or NULL: loss of the update made by this
+ *               call, NaN when none was made
+ */
+int ttt_decode_step(struct ttt_model* m, int32_t* next_token, float* logits, float* update_loss,
+                    void* stream);
+
+/* Back to the loaded state (fast weights, empty rings, position 0). */
+int ttt_reset(struct ttt_model* m, void* stream);
+
+/* Destroy the handle (the caller's workspace is not touched). */
+void ttt_model_free(struct ttt_model* m);
+
+/* Message for a status code, and for the last failure on this thread. */
+const char* ttt_status_str(int status);
+const char* ttt_last_error(void);
+
+/*
+ * Kernel timing (measurement aid).  When enabled, every launch of the
+ * kernel class `cls` is bracketed by HIP events on its stream:
+ *   cls 0 = all matrix-core GEMM launches of the inner loop
+ *   cls 1 = sliding-window attention forward
+ *   cls 2 = sliding-window attention backward
+ *   cls 3 = fused head + cross-entropy (statistics, gradient, input grad)
+ *   cls 4 = the weight-gradient GEMMs with the fused SGD update
+ * ttt_timing_read synchronises the stream and returns the summed event time
+ * (ms), the number of launches and the algorithmic FLOPs of those launches.
+ */
+int ttt_timing_enable(struct ttt_model* m, int32_t cls, int32_t on);
+int ttt_timing_read(struct ttt_model* m, int32_t cls, double* total_ms, int64_t* launches,
+                    double* flops);
+
+/*
+ * Diagnostic access to the inner loop's matrix-core GEMM kernel, for
+ * kernel-level parity tests.  Computes C[M][N] (device float, row stride
+ * ldc) = sum_k A[m,k] * B[n,k] with element type bf16 (dtype TTT_BF16) or
+ * float (TTT_FP32), fp32 accumulation:
+ *   a_kc = 1: A is [M][K] (row stride lda); 0: A is [K][M]
+ *   b_kc = 1: B is [N][K] (row stride ldb); 0: B is [K][N]
+ * Layouts (a_kc, b_kc) = (1,1), (1,0) overwrite C; (0,0) is the weight-
+ * gradient kernel and ADDS the product to C (its SGD epilogue run with
+ * lr = -1).  Row strides must be multiples of 8 elements, pointers 16-byte
+ * aligned.
+ */
+int ttt_diag_gemm(int32_t dtype, int32_t a_kc, int32_t b_kc, int32_t M, int32_t N, int32_t K,
+                  const void* A, int64_t lda, const void* B, int64_t ldb, float* C, int64_t ldc,
+                  void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TTT_H */

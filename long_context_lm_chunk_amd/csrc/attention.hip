@@ -1,0 +1,390 @@
+// Banded-causal ("sliding window") flash attention for gfx950.
+//
+// Query at absolute position t attends to keys at positions j with
+// t - W < j <= t (W keys, itself included), the short-term memory of the
+// method (NVIDIA blog "Our method"; podcast 4:41 and 6:36 on the ~8K window).
+// Keys and values live in a per-layer ring buffer, row (position mod cap),
+// so the memory is bounded by the window whatever the context length.
+//
+// Layout of the work: a workgroup = 4 waves = 64 queries (forward, dQ) or 64
+// keys (dK/dV) of one head; K/V (or Q/dO) tiles of 64 positions are staged
+// in LDS, once k-contiguous and, where a product reduces over positions,
+// once transposed.  Scores are computed transposed (S^T = K Q^T) so that each
+// lane owns one query column; the accumulator layout of S^T is then exactly
+// the operand layout that the P.V product needs, and the online softmax
+// rescaling stays inside the lane.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace ttt {
+namespace {
+
+constexpr int TQ = 64;     // positions per tile
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+template <typename T, int HD> struct AttnCfg {
+  static constexpr int KS = (HD + 31) / 32;          // 32-wide k steps over head_dim
+  static constexpr int HDP = KS * 32;                // head_dim padded with zeros
+  static constexpr int HB = HD / 16;                 // 16-row blocks of head_dim
+  static constexpr int PAD = 16 / sizeof(T);
+  static constexpr int LSN = HDP + PAD;              // natural tile row stride [pos][hd]
+  static constexpr int LST = TQ + PAD;               // transposed tile row stride [hd][pos]
+};
+
+// Load a 64-position tile of one head from a ring ([cap][ld]) in natural
+// layout (positions >= nvalid zero-filled, hd >= HD zero-filled).
+template <typename T, int HD>
+DEVI void load_nat(T* lds, const T* base, int64_t ld, int nvalid, int tid) {
+  using C = AttnCfg<T, HD>;
+  tile_copy_rows<T, TQ, C::HDP, C::LSN, 256>(lds, base, ld, nvalid, HD, tid);
+}
+template <typename T, int HD>
+DEVI void load_tr(T* lds, const T* base, int64_t ld, int nvalid, int tid) {
+  using C = AttnCfg<T, HD>;
+  tile_copy_transpose<T, TQ, HD, C::LST, 256>(lds, base, ld, nvalid, HD, tid);
+}
+
+// operand fragment (8 k-slots over head_dim) of row r from a natural tile
+template <typename T, int HD>
+DEVI typename Frag<T>::type nat_frag(const T* lds, int r, int ks, int lane) {
+  using C = AttnCfg<T, HD>;
+  return lds_frag8<T>(lds + r * C::LSN + ks * 32 + 8 * (lane >> 4));
+}
+// operand fragment of head-dim row r from a transposed tile, k-slots = 32
+// positions of pair pp laid out as two accumulator blocks (see header).
+template <typename T, int HD>
+DEVI typename Frag<T>::type tr_frag(const T* lds, int r, int pp, int lane) {
+  using C = AttnCfg<T, HD>;
+  const T* row = lds + r * C::LST + 4 * (lane >> 4);
+  return lds_frag4x2<T>(row + (2 * pp) * 16, row + (2 * pp + 1) * 16);
+}
+// operand fragment built from two accumulator blocks (values per lane: 4 + 4)
+template <typename T>
+DEVI typename Frag<T>::type acc_frag(const f32x4& a, const f32x4& b) {
+  float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return pack8<T>(v);
+}
+
+// register fragments of 16 rows (one per lane, row = l%16) of a [n][ld] matrix
+template <typename T, int HD>
+DEVI void row_frags(typename Frag<T>::type* f, const T* base, int64_t ld,
+                    bool row_ok, int lane) {
+#pragma unroll
+  for (int ks = 0; ks < AttnCfg<T, HD>::KS; ++ks) {
+    const int c = ks * 32 + 8 * (lane >> 4);
+    f[ks] = g_frag8<T>(base + c, row_ok && c < HD);
+  }
+}
+
+// ------------------------------------------------------------------ forward
+template <typename T, int HD>
+__global__ __launch_bounds__(256) void swa_fwd_k(AttnParams p) {
+  using C = AttnCfg<T, HD>;
+  __shared__ __attribute__((aligned(16))) T Ks[TQ * C::LSN];
+  __shared__ __attribute__((aligned(16))) T Vt[HD * C::LST];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = blockIdx.y;
+  const int qs = blockIdx.x * TQ;
+  const int d = p.H * HD;
+  const T* Q = static_cast<const T*>(p.q);
+  const T* KR = static_cast<const T*>(p.kring);
+  const T* VR = static_cast<const T*>(p.vring);
+
+  const int qrow = qs + wave * 16 + (lane & 15);
+  const bool qok = qrow < p.n;
+  const int64_t qpos = p.pos0 + qrow;
+  typename Frag<T>::type qf[C::KS];
+  row_frags<T, HD>(qf, Q + (int64_t)qrow * p.ldq + h * HD, p.ldq, qok, lane);
+
+  const float sc = LOG2E / sqrtf((float)HD);
+  float m = -INFINITY, l = 0.f;
+  f32x4 oacc[C::HB];
+#pragma unroll
+  for (int b = 0; b < C::HB; ++b) oacc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int64_t first = p.pos0 + qs;
+  const int64_t last = p.pos0 + min(qs + TQ, p.n) - 1;
+  int64_t lo = first - p.window + 1;
+  if (lo < 0) lo = 0;
+  const int64_t kt0 = (lo / TQ) * TQ;
+  for (int64_t kt = kt0; kt <= last; kt += TQ) {
+    const int nvalid = (int)min<int64_t>(TQ, last - kt + 1);
+    const int64_t slot = kt % p.cap;
+    __syncthreads();
+    load_nat<T, HD>(Ks, KR + slot * d + h * HD, d, nvalid, tid);
+    load_tr<T, HD>(Vt, VR + slot * d + h * HD, d, nvalid, tid);
+    __syncthreads();
+
+    f32x4 s[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks)
+        mma16x16x32(nat_frag<T, HD>(Ks, kb * 16 + (lane & 15), ks, lane), qf[ks], s[kb]);
+    }
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t kp = kt + kb * 16 + 4 * (lane >> 4) + i;
+        const bool ok = kp <= qpos && kp > qpos - p.window;
+        const float v = ok ? s[kb][i] * sc : -INFINITY;
+        s[kb][i] = v;
+        tmax = fmaxf(tmax, v);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float mn = fmaxf(m, tmax);
+    const float alpha = (mn == -INFINITY) ? 1.f : exp2f(m - mn);
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float e = (mn == -INFINITY) ? 0.f : exp2f(s[kb][i] - mn);
+        s[kb][i] = e;
+        rs += e;
+      }
+    rs += __shfl_xor(rs, 16, 64);
+    rs += __shfl_xor(rs, 32, 64);
+    l = l * alpha + rs;
+    m = mn;
+#pragma unroll
+    for (int b = 0; b < C::HB; ++b) oacc[b] *= alpha;
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp) {
+      const typename Frag<T>::type pf = acc_frag<T>(s[2 * pp], s[2 * pp + 1]);
+#pragma unroll
+      for (int b = 0; b < C::HB; ++b)
+        mma16x16x32(tr_frag<T, HD>(Vt, b * 16 + (lane & 15), pp, lane), pf, oacc[b]);
+    }
+  }
+
+  if (qok) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    T* O = static_cast<T*>(p.o) + (int64_t)qrow * p.ldo + h * HD;
+#pragma unroll
+    for (int b = 0; b < C::HB; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) O[b * 16 + 4 * (lane >> 4) + i] = from_f32<T>(oacc[b][i] * inv);
+    if (p.lse && (lane >> 4) == 0) p.lse[(int64_t)h * p.n + qrow] = (m + log2f(l)) * LN2;
+  }
+}
+
+// ------------------------------------------------------------ backward dQ
+template <typename T, int HD>
+__global__ __launch_bounds__(256) void swa_bwd_dq_k(AttnParams p) {
+  using C = AttnCfg<T, HD>;
+  __shared__ __attribute__((aligned(16))) T Ks[TQ * C::LSN];
+  __shared__ __attribute__((aligned(16))) T Vs[TQ * C::LSN];
+  __shared__ __attribute__((aligned(16))) T Kt[HD * C::LST];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = blockIdx.y;
+  const int qs = blockIdx.x * TQ;
+  const int d = p.H * HD;
+  const T* KR = static_cast<const T*>(p.kring);
+  const T* VR = static_cast<const T*>(p.vring);
+
+  const int qrow = qs + wave * 16 + (lane & 15);
+  const bool qok = qrow < p.n;
+  const int64_t qpos = p.pos0 + qrow;
+  typename Frag<T>::type qf[C::KS], gf[C::KS];
+  row_frags<T, HD>(qf, static_cast<const T*>(p.q) + (int64_t)qrow * p.ldq + h * HD, p.ldq, qok, lane);
+  row_frags<T, HD>(gf, static_cast<const T*>(p.dout) + (int64_t)qrow * p.lddo + h * HD, p.lddo, qok, lane);
+  const float lse2 = qok ? p.lse[(int64_t)h * p.n + qrow] * LOG2E : 0.f;
+  const float Dq = qok ? p.D[(int64_t)h * p.n + qrow] : 0.f;
+  const float sc = LOG2E / sqrtf((float)HD);
+
+  f32x4 dacc[C::HB];
+#pragma unroll
+  for (int b = 0; b < C::HB; ++b) dacc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int64_t first = p.pos0 + qs;
+  const int64_t last = p.pos0 + min(qs + TQ, p.n) - 1;
+  int64_t lo = first - p.window + 1;
+  if (lo < 0) lo = 0;
+  for (int64_t kt = (lo / TQ) * TQ; kt <= last; kt += TQ) {
+    const int nvalid = (int)min<int64_t>(TQ, last - kt + 1);
+    const int64_t slot = kt % p.cap;
+    __syncthreads();
+    load_nat<T, HD>(Ks, KR + slot * d + h * HD, d, nvalid, tid);
+    load_nat<T, HD>(Vs, VR + slot * d + h * HD, d, nvalid, tid);
+    load_tr<T, HD>(Kt, KR + slot * d + h * HD, d, nvalid, tid);
+    __syncthreads();
+
+    f32x4 s[4], dp[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dp[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        mma16x16x32(nat_frag<T, HD>(Ks, kb * 16 + (lane & 15), ks, lane), qf[ks], s[kb]);
+        mma16x16x32(nat_frag<T, HD>(Vs, kb * 16 + (lane & 15), ks, lane), gf[ks], dp[kb]);
+      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t kp = kt + kb * 16 + 4 * (lane >> 4) + i;
+        const bool ok = qok && kp <= qpos && kp > qpos - p.window;
+        const float pr = ok ? exp2f(s[kb][i] * sc - lse2) : 0.f;
+        s[kb][i] = pr * (dp[kb][i] - Dq);   // dS^T
+      }
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp) {
+      const typename Frag<T>::type df = acc_frag<T>(s[2 * pp], s[2 * pp + 1]);
+#pragma unroll
+      for (int b = 0; b < C::HB; ++b)
+        mma16x16x32(tr_frag<T, HD>(Kt, b * 16 + (lane & 15), pp, lane), df, dacc[b]);
+    }
+  }
+  if (qok) {
+    const float scale = 1.f / sqrtf((float)HD);
+    T* G = static_cast<T*>(p.dq) + (int64_t)qrow * p.ldg + h * HD;
+#pragma unroll
+    for (int b = 0; b < C::HB; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) G[b * 16 + 4 * (lane >> 4) + i] = from_f32<T>(dacc[b][i] * scale);
+  }
+}
+
+// --------------------------------------------------------- backward dK, dV
+// Keys are the in-chunk positions (query rows of this chunk); cached keys
+// of earlier chunks are constants and receive no gradient.
+template <typename T, int HD>
+__global__ __launch_bounds__(256) void swa_bwd_dkdv_k(AttnParams p) {
+  using C = AttnCfg<T, HD>;
+  __shared__ __attribute__((aligned(16))) T Qs[TQ * C::LSN];
+  __shared__ __attribute__((aligned(16))) T Gs[TQ * C::LSN];
+  __shared__ __attribute__((aligned(16))) T Qt[HD * C::LST];
+  __shared__ __attribute__((aligned(16))) T Gt[HD * C::LST];
+  __shared__ float lse_s[TQ], D_s[TQ];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = blockIdx.y;
+  const int ks0 = blockIdx.x * TQ;
+  const int d = p.H * HD;
+  const T* Q = static_cast<const T*>(p.q);
+  const T* G = static_cast<const T*>(p.dout);
+  const T* KR = static_cast<const T*>(p.kring);
+  const T* VR = static_cast<const T*>(p.vring);
+
+  const int krow = ks0 + wave * 16 + (lane & 15);     // chunk-relative key index
+  const bool kok = krow < p.n;
+  const int64_t kpos = p.pos0 + krow;
+  const int64_t kslot = (kok ? kpos : p.pos0) % p.cap;
+  typename Frag<T>::type kf[C::KS], vf[C::KS];
+  row_frags<T, HD>(kf, KR + kslot * d + h * HD, d, kok, lane);
+  row_frags<T, HD>(vf, VR + kslot * d + h * HD, d, kok, lane);
+  const float sc = LOG2E / sqrtf((float)HD);
+
+  f32x4 dk[C::HB], dv[C::HB];
+#pragma unroll
+  for (int b = 0; b < C::HB; ++b) { dk[b] = f32x4{0.f, 0.f, 0.f, 0.f}; dv[b] = f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+  const int kmax = min(ks0 + TQ, p.n) - 1;
+  const int64_t qend = min<int64_t>((int64_t)p.n - 1, (int64_t)kmax + p.window - 1);
+  for (int qt = ks0; qt <= qend; qt += TQ) {
+    const int nvalid = min(TQ, p.n - qt);
+    __syncthreads();
+    load_nat<T, HD>(Qs, Q + (int64_t)qt * p.ldq + h * HD, p.ldq, nvalid, tid);
+    load_nat<T, HD>(Gs, G + (int64_t)qt * p.lddo + h * HD, p.lddo, nvalid, tid);
+    load_tr<T, HD>(Qt, Q + (int64_t)qt * p.ldq + h * HD, p.ldq, nvalid, tid);
+    load_tr<T, HD>(Gt, G + (int64_t)qt * p.lddo + h * HD, p.lddo, nvalid, tid);
+    if (tid < TQ) {
+      const bool ok = tid < nvalid;
+      lse_s[tid] = ok ? p.lse[(int64_t)h * p.n + qt + tid] * LOG2E : 0.f;
+      D_s[tid] = ok ? p.D[(int64_t)h * p.n + qt + tid] : 0.f;
+    }
+    __syncthreads();
+
+    f32x4 s[4], dp[4];
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      s[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dp[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        mma16x16x32(nat_frag<T, HD>(Qs, qb * 16 + (lane & 15), ks, lane), kf[ks], s[qb]);
+        mma16x16x32(nat_frag<T, HD>(Gs, qb * 16 + (lane & 15), ks, lane), vf[ks], dp[qb]);
+      }
+    }
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int qi = qb * 16 + 4 * (lane >> 4) + i;
+        const int64_t qp = p.pos0 + qt + qi;
+        const bool ok = kok && (qt + qi < p.n) && kpos <= qp && kpos > qp - p.window;
+        const float pr = ok ? exp2f(s[qb][i] * sc - lse_s[qi]) : 0.f;
+        s[qb][i] = pr;                              // P
+        dp[qb][i] = pr * (dp[qb][i] - D_s[qi]);     // dS
+      }
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp) {
+      const typename Frag<T>::type pf = acc_frag<T>(s[2 * pp], s[2 * pp + 1]);
+      const typename Frag<T>::type df = acc_frag<T>(dp[2 * pp], dp[2 * pp + 1]);
+#pragma unroll
+      for (int b = 0; b < C::HB; ++b) {
+        mma16x16x32(tr_frag<T, HD>(Gt, b * 16 + (lane & 15), pp, lane), pf, dv[b]);
+        mma16x16x32(tr_frag<T, HD>(Qt, b * 16 + (lane & 15), pp, lane), df, dk[b]);
+      }
+    }
+  }
+  if (kok) {
+    const float scale = 1.f / sqrtf((float)HD);
+    T* DK = static_cast<T*>(p.dk) + (int64_t)krow * p.ldg + h * HD;
+    T* DV = static_cast<T*>(p.dv) + (int64_t)krow * p.ldg + h * HD;
+#pragma unroll
+    for (int b = 0; b < C::HB; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        DK[b * 16 + 4 * (lane >> 4) + i] = from_f32<T>(dk[b][i] * scale);
+        DV[b * 16 + 4 * (lane >> 4) + i] = from_f32<T>(dv[b][i]);
+      }
+  }
+}
+
+template <typename T, template <typename, int> class K> struct HdDispatch;
+
+template <typename T>
+void fwd_t(const AttnParams& p, hipStream_t s) {
+  dim3 grid((p.n + TQ - 1) / TQ, p.H);
+  switch (p.hd) {
+    case 16: hipLaunchKernelGGL((swa_fwd_k<T, 16>), grid, dim3(256), 0, s, p); break;
+    case 32: hipLaunchKernelGGL((swa_fwd_k<T, 32>), grid, dim3(256), 0, s, p); break;
+    case 64: hipLaunchKernelGGL((swa_fwd_k<T, 64>), grid, dim3(256), 0, s, p); break;
+    case 96: hipLaunchKernelGGL((swa_fwd_k<T, 96>), grid, dim3(256), 0, s, p); break;
+    case 128: hipLaunchKernelGGL((swa_fwd_k<T, 128>), grid, dim3(256), 0, s, p); break;
+    default: break;
+  }
+}
+template <typename T>
+void bwd_t(const AttnParams& p, hipStream_t s) {
+  dim3 grid((p.n + TQ - 1) / TQ, p.H);
+  switch (p.hd) {
+#define CASE(HDV) case HDV: \
+    hipLaunchKernelGGL((swa_bwd_dq_k<T, HDV>), grid, dim3(256), 0, s, p); \
+    hipLaunchKernelGGL((swa_bwd_dkdv_k<T, HDV>), grid, dim3(256), 0, s, p); break;
+    CASE(16) CASE(32) CASE(64) CASE(96) CASE(128)
+#undef CASE
+    default: break;
+  }
+}
+
+}  // namespace
+
+void swa_fwd(const AttnParams& p, bool bf, hipStream_t s) {
+  if (p.n <= 0) return;
+  if (bf) fwd_t<bf16>(p, s); else fwd_t<float>(p, s);
+}
+void swa_bwd(const AttnParams& p, bool bf, hipStream_t s) {
+  if (p.n <= 0) return;
+  if (bf) bwd_t<bf16>(p, s); else bwd_t<float>(p, s);
+}
+
+}  // namespace ttt

@@ -1,0 +1,209 @@
+// One-token decode kernels: HBM-bound matrix-vector products, split-key
+// sliding-window attention over the ring, and the greedy argmax.  Per-token
+// cost is bounded by the window and the weights, not by the context length
+// (the constant-latency claim of the paper summary, "Key claims", and of the
+// NVIDIA blog's Figure 1 caption).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace ttt {
+namespace {
+
+// y[n] = sum_k W[n][k] x[k] (+ resid[n]); W [N][K] k-contiguous.
+// One wave per output row, 16-byte loads along k.
+template <typename T, typename X>
+__global__ __launch_bounds__(256) void gemv_k(const T* __restrict__ W, int N, int K,
+                                              const X* __restrict__ x, float* __restrict__ y,
+                                              const float* __restrict__ resid) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= N) return;
+  constexpr int V = Vec16<T>::N;
+  const T* w = W + (int64_t)row * K;
+  float s = 0.f;
+  for (int k = lane * V; k < K; k += 64 * V) {
+    const U128 wv = ld128(w + k);
+#pragma unroll
+    for (int e = 0; e < V; ++e) s += to_f32(elem<T>(wv, e)) * to_f32(x[k + e]);
+  }
+  s = wave_sum(s);
+  if (lane == 0) y[row] = s + (resid ? resid[row] : 0.f);
+}
+
+template <typename T>
+__global__ void swiglu_vec_k(const float* __restrict__ z, int F, T* __restrict__ act) {
+  const int f = blockIdx.x * blockDim.x + threadIdx.x;
+  if (f >= F) return;
+  const int c = (f / 16) * 32 + (f % 16);
+  const float g = z[c], u = z[c + 16];
+  act[f] = from_f32<T>(g / (1.f + __expf(-g)) * u);
+}
+template <typename T>
+__global__ void gelu_vec_k(const float* __restrict__ z, int F, T* __restrict__ act) {
+  const int f = blockIdx.x * blockDim.x + threadIdx.x;
+  if (f >= F) return;
+  const float v = z[f];
+  act[f] = from_f32<T>(0.5f * v * (1.f + erff(v * 0.70710678118654752f)));
+}
+
+constexpr int DK = 256;   // keys per split
+
+// Partial attention of one query (position pos) over keys
+// [lo + split*DK, ...) of head h.  ws layout per (h, split): m, l, o[hd].
+template <typename T>
+__global__ __launch_bounds__(256) void swa_decode_part_k(const T* __restrict__ q,
+                                                         const T* __restrict__ kr,
+                                                         const T* __restrict__ vr, int64_t cap,
+                                                         int H, int hd, int64_t lo, int64_t pos,
+                                                         float* __restrict__ ws, int nsplit) {
+  __shared__ float qs[128];
+  __shared__ float ps[DK];
+  __shared__ float red[256];
+  __shared__ float oacc[4][128];
+  const int h = blockIdx.y, sp = blockIdx.x, tid = threadIdx.x;
+  const int d = H * hd;
+  for (int i = tid; i < hd; i += 256) qs[i] = to_f32(q[h * hd + i]);
+  __syncthreads();
+  const int64_t kp = lo + (int64_t)sp * DK + tid;
+  float s = -INFINITY;
+  if (kp <= pos) {
+    const T* k = kr + (kp % cap) * d + h * hd;
+    float acc = 0.f;
+    constexpr int V = Vec16<T>::N;
+    for (int c = 0; c < hd; c += V) {
+      const U128 kv = ld128(k + c);
+#pragma unroll
+      for (int e = 0; e < V; ++e) acc += to_f32(elem<T>(kv, e)) * qs[c + e];
+    }
+    s = acc / sqrtf((float)hd);
+  }
+  red[tid] = s;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
+    __syncthreads();
+  }
+  const float m = red[0];
+  __syncthreads();
+  const float e = (s == -INFINITY) ? 0.f : __expf(s - m);
+  ps[tid] = e;
+  red[tid] = e;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) red[tid] += red[tid + o];
+    __syncthreads();
+  }
+  const float l = red[0];
+  // o[j] = sum_k p_k v_k[j]: thread (g = tid / hd_groups) handles keys g, g+G, ...
+  const int G = 256 / hd > 4 ? 4 : (256 / hd);    // key groups (hd <= 128 -> >= 2)
+  const int j = tid % hd, g = tid / hd;
+  if (g < G) {
+    float a = 0.f;
+    for (int kk = g; kk < DK; kk += G) {
+      const int64_t p2 = lo + (int64_t)sp * DK + kk;
+      if (p2 > pos) break;
+      a += ps[kk] * to_f32(vr[(p2 % cap) * d + h * hd + j]);
+    }
+    oacc[g][j] = a;
+  }
+  __syncthreads();
+  float* w = ws + ((int64_t)h * nsplit + sp) * (2 + hd);
+  if (tid < hd) {
+    float a = 0.f;
+    for (int gg = 0; gg < G; ++gg) a += oacc[gg][tid];
+    w[2 + tid] = a;
+  }
+  if (tid == 0) { w[0] = m; w[1] = l; }
+}
+
+template <typename T>
+__global__ void swa_decode_combine_k(const float* __restrict__ ws, int nsplit, int H, int hd,
+                                     T* __restrict__ o) {
+  const int h = blockIdx.x, j = threadIdx.x;
+  if (j >= hd) return;
+  float M = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ws[((int64_t)h * nsplit + s) * (2 + hd)]);
+  float L = 0.f, acc = 0.f;
+  for (int s = 0; s < nsplit; ++s) {
+    const float* w = ws + ((int64_t)h * nsplit + s) * (2 + hd);
+    const float f = (w[0] == -INFINITY) ? 0.f : __expf(w[0] - M);
+    L += w[1] * f;
+    acc += w[2 + j] * f;
+  }
+  o[h * hd + j] = from_f32<T>(acc / L);
+}
+
+// Greedy choice: largest logit, lowest id on ties.
+__global__ void argmax_k(const float* __restrict__ z, int V, int32_t* __restrict__ out,
+                         int32_t* __restrict__ hist) {
+  __shared__ float bv[1024];
+  __shared__ int bi[1024];
+  float best = -INFINITY;
+  int idx = 0x7fffffff;
+  for (int i = threadIdx.x; i < V; i += blockDim.x) {
+    const float v = z[i];
+    if (v > best || (v == best && i < idx)) { best = v; idx = i; }
+  }
+  bv[threadIdx.x] = best;
+  bi[threadIdx.x] = idx;
+  __syncthreads();
+  for (int o = blockDim.x / 2; o > 0; o >>= 1) {
+    if (threadIdx.x < o) {
+      const float v2 = bv[threadIdx.x + o];
+      const int i2 = bi[threadIdx.x + o];
+      if (v2 > bv[threadIdx.x] || (v2 == bv[threadIdx.x] && i2 < bi[threadIdx.x])) {
+        bv[threadIdx.x] = v2;
+        bi[threadIdx.x] = i2;
+      }
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const int r = bi[0] == 0x7fffffff ? 0 : bi[0];
+    *out = r;
+    if (hist) *hist = r;
+  }
+}
+
+}  // namespace
+
+void gemv(const void* W, int N, int K, const void* x, bool x_f32, float* y, const float* resid,
+          bool bf, hipStream_t s) {
+  dim3 grid((N + 3) / 4);
+  if (bf) {
+    if (x_f32) hipLaunchKernelGGL((gemv_k<bf16, float>), grid, dim3(256), 0, s, (const bf16*)W, N, K, (const float*)x, y, resid);
+    else hipLaunchKernelGGL((gemv_k<bf16, bf16>), grid, dim3(256), 0, s, (const bf16*)W, N, K, (const bf16*)x, y, resid);
+  } else {
+    hipLaunchKernelGGL((gemv_k<float, float>), grid, dim3(256), 0, s, (const float*)W, N, K, (const float*)x, y, resid);
+  }
+}
+
+void swiglu_vec(const float* z, int F, void* act, bool bf, hipStream_t s) {
+  if (bf) hipLaunchKernelGGL(swiglu_vec_k<bf16>, dim3((F + 255) / 256), dim3(256), 0, s, z, F, (bf16*)act);
+  else hipLaunchKernelGGL(swiglu_vec_k<float>, dim3((F + 255) / 256), dim3(256), 0, s, z, F, (float*)act);
+}
+void gelu_vec(const float* z, int F, void* act, bool bf, hipStream_t s) {
+  if (bf) hipLaunchKernelGGL(gelu_vec_k<bf16>, dim3((F + 255) / 256), dim3(256), 0, s, z, F, (bf16*)act);
+  else hipLaunchKernelGGL(gelu_vec_k<float>, dim3((F + 255) / 256), dim3(256), 0, s, z, F, (float*)act);
+}
+
+void swa_decode(const void* q, const void* kring, const void* vring, int64_t cap, int H, int hd,
+                int window, int64_t pos, void* o, float* ws, bool bf, hipStream_t s) {
+  int64_t lo = pos - window + 1;
+  if (lo < 0) lo = 0;
+  const int nsplit = (int)((pos - lo + 1 + DK - 1) / DK);
+  dim3 grid(nsplit, H);
+  if (bf) {
+    hipLaunchKernelGGL(swa_decode_part_k<bf16>, grid, dim3(256), 0, s, (const bf16*)q, (const bf16*)kring, (const bf16*)vring, cap, H, hd, lo, pos, ws, nsplit);
+    hipLaunchKernelGGL(swa_decode_combine_k<bf16>, dim3(H), dim3(128), 0, s, ws, nsplit, H, hd, (bf16*)o);
+  } else {
+    hipLaunchKernelGGL(swa_decode_part_k<float>, grid, dim3(256), 0, s, (const float*)q, (const float*)kring, (const float*)vring, cap, H, hd, lo, pos, ws, nsplit);
+    hipLaunchKernelGGL(swa_decode_combine_k<float>, dim3(H), dim3(128), 0, s, ws, nsplit, H, hd, (float*)o);
+  }
+}
+
+void argmax_tok(const float* logits, int V, int32_t* out_tok, int32_t* tok_hist, hipStream_t s) {
+  hipLaunchKernelGGL(argmax_k, dim3(1), dim3(1024), 0, s, logits, V, out_tok, tok_hist);
+}
+
+}  // namespace ttt

@@ -1,0 +1,417 @@
+// Bandwidth-bound kernels of the inner loop: embedding gather, LayerNorm
+// forward/backward (fp32 statistics), RoPE with float64 angles written
+// straight into the K/V ring, activation backward, weight layout conversion
+// and the cross-entropy row combine.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace ttt {
+namespace {
+
+template <typename T>
+__global__ void embed_k(const int32_t* __restrict__ tok, int n, const T* __restrict__ E, int d, int V,
+                        float* __restrict__ out, int* __restrict__ err) {
+  const int t = blockIdx.x;
+  if (t >= n) return;
+  int id = tok[t];
+  if (id < 0 || id >= V) {
+    if (threadIdx.x == 0) atomicOr(err, 1);
+    id = 0;
+  }
+  for (int i = threadIdx.x; i < d; i += blockDim.x)
+    out[(int64_t)t * d + i] = to_f32(E[(int64_t)id * d + i]);
+}
+
+// One wave per row.  y = (x - mean) * rstd, biased variance.
+template <typename T>
+__global__ void ln_fwd_k(const float* __restrict__ x, int64_t ldx, int n, int d, float eps,
+                         T* __restrict__ y, int64_t ldy, float* __restrict__ mean,
+                         float* __restrict__ rstd) {
+  const int row = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= n) return;
+  const float* xr = x + (int64_t)row * ldx;
+  float s = 0.f;
+  for (int i = lane; i < d; i += 64) s += xr[i];
+  const float mu = wave_sum(s) / d;
+  float v = 0.f;
+  for (int i = lane; i < d; i += 64) { const float c = xr[i] - mu; v += c * c; }
+  const float rs = rsqrtf(wave_sum(v) / d + eps);
+  T* yr = y + (int64_t)row * ldy;
+  for (int i = lane; i < d; i += 64) yr[i] = from_f32<T>((xr[i] - mu) * rs);
+  if (lane == 0) {
+    if (mean) mean[row] = mu;
+    if (rstd) rstd[row] = rs;
+  }
+}
+
+// acc += rstd * (dy - mean(dy) - yhat * mean(dy * yhat)); acc_lo = round(acc)
+template <typename T>
+__global__ void ln_bwd_k(const float* __restrict__ dy, const float* __restrict__ x,
+                         const float* __restrict__ mean, const float* __restrict__ rstd, int n, int d,
+                         float* __restrict__ acc, T* __restrict__ acc_lo) {
+  const int row = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= n) return;
+  const float* g = dy + (int64_t)row * d;
+  const float* xr = x + (int64_t)row * d;
+  const float mu = mean[row], rs = rstd[row];
+  float s1 = 0.f, s2 = 0.f;
+  for (int i = lane; i < d; i += 64) {
+    const float yh = (xr[i] - mu) * rs;
+    s1 += g[i];
+    s2 += g[i] * yh;
+  }
+  const float m1 = wave_sum(s1) / d, m2 = wave_sum(s2) / d;
+  float* a = acc + (int64_t)row * d;
+  for (int i = lane; i < d; i += 64) {
+    const float yh = (xr[i] - mu) * rs;
+    const float nv = a[i] + rs * (g[i] - m1 - yh * m2);
+    a[i] = nv;
+    if (acc_lo) acc_lo[(int64_t)row * d + i] = from_f32<T>(nv);
+  }
+}
+
+template <typename T>
+__global__ void cast_k(const float* __restrict__ s, T* __restrict__ d, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    d[i] = from_f32<T>(s[i]);
+}
+
+template <typename T>
+__global__ void widen_k(const T* __restrict__ s, float* __restrict__ d, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    d[i] = to_f32(s[i]);
+}
+
+__global__ void fill_k(float* __restrict__ p, int64_t n, float v) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+// Angle of pair i at position pos, in float64, reduced before the float
+// rotation (positions reach 5e5, where a float angle would be off by 0.03).
+DEVI void rope_cs(int64_t pos, const double* theta, int i, float& c, float& s) {
+  const double a = (double)pos * theta[i];
+  double sd, cd;
+  sincos(a, &sd, &cd);
+  c = (float)cd;
+  s = (float)sd;
+}
+
+// qkv [n][3*H*hd]; writes q_out [n][H*hd] (rotated), K (rotated) and V to
+// ring slot (pos0 + t) mod cap.  One thread per (t, h, i < hd/2).
+template <typename T>
+__global__ void rope_qkv_k(const T* __restrict__ qkv, int n, int H, int hd, int64_t pos0,
+                           const double* __restrict__ theta, T* __restrict__ qo, T* __restrict__ kr,
+                           T* __restrict__ vr, int64_t cap) {
+  const int half = hd >> 1;
+  const int64_t total = (int64_t)n * H * half;
+  const int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const int i = idx % half;
+  const int h = (idx / half) % H;
+  const int t = idx / ((int64_t)half * H);
+  const int d = H * hd;
+  const int64_t pos = pos0 + t;
+  float c, s;
+  rope_cs(pos, theta, i, c, s);
+  const T* row = qkv + (int64_t)t * 3 * d;
+  const int j1 = h * hd + i, j2 = j1 + half;
+  const float q1 = to_f32(row[j1]), q2 = to_f32(row[j2]);
+  const float k1 = to_f32(row[d + j1]), k2 = to_f32(row[d + j2]);
+  qo[(int64_t)t * d + j1] = from_f32<T>(q1 * c - q2 * s);
+  qo[(int64_t)t * d + j2] = from_f32<T>(q2 * c + q1 * s);
+  const int64_t slot = pos % cap;
+  kr[slot * d + j1] = from_f32<T>(k1 * c - k2 * s);
+  kr[slot * d + j2] = from_f32<T>(k2 * c + k1 * s);
+  vr[slot * d + j1] = row[2 * d + j1];
+  vr[slot * d + j2] = row[2 * d + j2];
+}
+
+template <typename T>
+__global__ void rope_qkv_f32in_k(const float* __restrict__ qkv, int H, int hd, int64_t pos,
+                                 const double* __restrict__ theta, T* __restrict__ qo,
+                                 T* __restrict__ kr, T* __restrict__ vr, int64_t cap) {
+  const int half = hd >> 1;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= H * half) return;
+  const int i = idx % half, h = idx / half;
+  const int d = H * hd;
+  float c, s;
+  rope_cs(pos, theta, i, c, s);
+  const int j1 = h * hd + i, j2 = j1 + half;
+  const float q1 = qkv[j1], q2 = qkv[j2], k1 = qkv[d + j1], k2 = qkv[d + j2];
+  qo[j1] = from_f32<T>(q1 * c - q2 * s);
+  qo[j2] = from_f32<T>(q2 * c + q1 * s);
+  const int64_t slot = pos % cap;
+  kr[slot * d + j1] = from_f32<T>(k1 * c - k2 * s);
+  kr[slot * d + j2] = from_f32<T>(k2 * c + k1 * s);
+  vr[slot * d + j1] = from_f32<T>(qkv[2 * d + j1]);
+  vr[slot * d + j2] = from_f32<T>(qkv[2 * d + j2]);
+}
+
+// Transposed rotation of dQ and dK inside dqkv [n][3d].
+template <typename T>
+__global__ void rope_bwd_k(T* __restrict__ g, int n, int H, int hd, int64_t pos0,
+                           const double* __restrict__ theta) {
+  const int half = hd >> 1;
+  const int64_t total = (int64_t)n * H * half;
+  const int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const int i = idx % half;
+  const int h = (idx / half) % H;
+  const int t = idx / ((int64_t)half * H);
+  const int d = H * hd;
+  float c, s;
+  rope_cs(pos0 + t, theta, i, c, s);
+  T* row = g + (int64_t)t * 3 * d;
+  const int j1 = h * hd + i, j2 = j1 + half;
+#pragma unroll
+  for (int part = 0; part < 2; ++part) {
+    T* r = row + part * d;
+    const float a = to_f32(r[j1]), b = to_f32(r[j2]);
+    r[j1] = from_f32<T>(a * c + b * s);
+    r[j2] = from_f32<T>(b * c - a * s);
+  }
+}
+
+// dz from dact (fp32 [n][F]) and the saved pre-activations.
+// SwiGLU: z [n][2F] with gate/up in alternating blocks of 16 columns.
+template <typename T>
+__global__ void act_bwd_k(const float* __restrict__ dact, const T* __restrict__ z, int n, int F,
+                          int swiglu, T* __restrict__ dz) {
+  const int64_t total = (int64_t)n * F;
+  const int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const int f = idx % F;
+  const int64_t t = idx / F;
+  const float da = dact[idx];
+  if (swiglu) {
+    const int64_t cg = t * 2 * F + (f / 16) * 32 + (f % 16);
+    const float g = to_f32(z[cg]), u = to_f32(z[cg + 16]);
+    const float sg = 1.f / (1.f + __expf(-g));
+    const float si = g * sg;
+    dz[cg] = from_f32<T>(da * u * sg * (1.f + g * (1.f - sg)));
+    dz[cg + 16] = from_f32<T>(da * si);
+  } else {
+    const float zz = to_f32(z[idx]);
+    const float cdf = 0.5f * (1.f + erff(zz * 0.70710678118654752f));
+    const float pdf = 0.39894228040143268f * __expf(-0.5f * zz * zz);
+    dz[idx] = from_f32<T>(da * (cdf + zz * pdf));
+  }
+}
+
+// Canonical [rows=in][cols=out] -> internal [out][in] (transpose), optionally
+// into the gate (half 0) or up (half 1) rows of a block-16 interleaved matrix.
+template <typename T>
+__global__ void convert_k(const T* __restrict__ src, int rows, int cols, int transpose, int ilv,
+                          T* __restrict__ dst) {
+  __shared__ T tile[32][33];
+  const int bx = blockIdx.x * 32, by = blockIdx.y * 32;  // bx over cols, by over rows of src
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5; // 256 threads: 32 x 8
+  if (!transpose) {
+    for (int r = ty; r < 32; r += 8) {
+      const int rr = by + r, cc = bx + tx;
+      if (rr < rows && cc < cols) dst[(int64_t)rr * cols + cc] = src[(int64_t)rr * cols + cc];
+    }
+    return;
+  }
+  for (int r = ty; r < 32; r += 8) {
+    const int rr = by + r, cc = bx + tx;
+    if (rr < rows && cc < cols) tile[r][tx] = src[(int64_t)rr * cols + cc];
+  }
+  __syncthreads();
+  for (int c = ty; c < 32; c += 8) {
+    const int oc = bx + c;   // output row (= src col)
+    const int orr = by + tx; // output col (= src row)
+    if (oc < cols && orr < rows) {
+      int64_t drow = oc;
+      if (ilv >= 0) drow = (int64_t)(oc / 16) * 32 + ilv * 16 + (oc % 16);
+      dst[drow * rows + orr] = tile[tx][c];
+    }
+  }
+}
+
+// Internal fp32 master [out][in] (optionally interleaved, taking half
+// `which`) -> canonical fp32 [in][out].
+__global__ void export_k(const float* __restrict__ m, int out_dim, int in_dim, int ilv, int which,
+                         float* __restrict__ dst) {
+  const int64_t total = (int64_t)out_dim * in_dim;
+  const int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const int f = idx % out_dim;          // output column (out index)
+  const int j = idx / out_dim;          // input row
+  int64_t r = f;
+  if (ilv) r = (int64_t)(f / 16) * 32 + which * 16 + (f % 16);
+  dst[idx] = m[r * in_dim + j];
+}
+
+// One wave per row: combine the per-part (max, sumexp) into the row LSE and
+// the row loss (natural log).
+__global__ void ce_rows_k(const float* __restrict__ pmax, const float* __restrict__ psum, int nparts,
+                          int64_t ldp, const float* __restrict__ tl, int n_rows, int n_tgt,
+                          float* __restrict__ lse, float* __restrict__ rowloss) {
+  const int row = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= n_rows) return;
+  float m = -INFINITY;
+  for (int p = lane; p < nparts; p += 64) m = fmaxf(m, pmax[(int64_t)p * ldp + row]);
+  m = wave_max(m);
+  float s = 0.f;
+  for (int p = lane; p < nparts; p += 64) s += psum[(int64_t)p * ldp + row] * __expf(pmax[(int64_t)p * ldp + row] - m);
+  s = wave_sum(s);
+  if (lane == 0) {
+    const float l = m + __logf(s);
+    lse[row] = l;
+    rowloss[row] = row < n_tgt ? l - tl[row] : 0.f;
+  }
+}
+
+// Deterministic mean over the target rows; flags a non-finite loss.
+__global__ void ce_mean_k(const float* __restrict__ rowloss, int n_tgt, float* __restrict__ out,
+                          int* __restrict__ err) {
+  __shared__ float red[1024];
+  float s = 0.f;
+  for (int i = threadIdx.x; i < n_tgt; i += blockDim.x) s += rowloss[i];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int o = blockDim.x / 2; o > 0; o >>= 1) {
+    if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const float v = n_tgt > 0 ? red[0] / n_tgt : 0.f;
+    *out = v;
+    if (!isfinite(v)) atomicOr(err, 2);
+  }
+}
+
+// D[h][t] = sum_i dO[t][h,i] * O[t][h,i]; one wave per (t, h)
+template <typename T>
+__global__ void rowdot_k(const T* __restrict__ o, const T* __restrict__ g, int n, int H, int hd,
+                         float* __restrict__ D) {
+  const int w = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (w >= n * H) return;
+  const int t = w / H, h = w % H;
+  const int64_t base = (int64_t)t * H * hd + h * hd;
+  float s = 0.f;
+  for (int i = lane; i < hd; i += 64) s += to_f32(o[base + i]) * to_f32(g[base + i]);
+  s = wave_sum(s);
+  if (lane == 0) D[(int64_t)h * n + t] = s;
+}
+
+inline unsigned nblk(int64_t n, int b) { return (unsigned)((n + b - 1) / b); }
+inline unsigned gs_blocks(int64_t n) { int64_t b = (n + 255) / 256; return (unsigned)(b > 65536 ? 65536 : (b < 1 ? 1 : b)); }
+
+}  // namespace
+
+#define TSEL(bf, call_bf, call_f) do { if (bf) { call_bf; } else { call_f; } } while (0)
+
+void embed(const int32_t* tok, int n, const void* E, int d, int V, bool bf, float* out, int* err,
+           hipStream_t s) {
+  if (n <= 0) return;
+  TSEL(bf, hipLaunchKernelGGL(embed_k<bf16>, dim3(n), dim3(256), 0, s, tok, n, (const bf16*)E, d, V, out, err),
+       hipLaunchKernelGGL(embed_k<float>, dim3(n), dim3(256), 0, s, tok, n, (const float*)E, d, V, out, err));
+}
+
+void layernorm_fwd(const float* x, int64_t ldx, int n, int d, float eps, void* y, int64_t ldy,
+                   float* mean, float* rstd, bool bf, hipStream_t s) {
+  if (n <= 0) return;
+  TSEL(bf, hipLaunchKernelGGL(ln_fwd_k<bf16>, dim3(nblk(n, 4)), dim3(256), 0, s, x, ldx, n, d, eps, (bf16*)y, ldy, mean, rstd),
+       hipLaunchKernelGGL(ln_fwd_k<float>, dim3(nblk(n, 4)), dim3(256), 0, s, x, ldx, n, d, eps, (float*)y, ldy, mean, rstd));
+}
+
+void layernorm_bwd_acc(const float* dy, const float* x, const float* mean, const float* rstd, int n,
+                       int d, float* acc, void* acc_lo, bool bf, hipStream_t s) {
+  if (n <= 0) return;
+  TSEL(bf, hipLaunchKernelGGL(ln_bwd_k<bf16>, dim3(nblk(n, 4)), dim3(256), 0, s, dy, x, mean, rstd, n, d, acc, (bf16*)acc_lo),
+       hipLaunchKernelGGL(ln_bwd_k<float>, dim3(nblk(n, 4)), dim3(256), 0, s, dy, x, mean, rstd, n, d, acc, (float*)acc_lo));
+}
+
+void cast_rows(const float* src, void* dst, int64_t n, bool bf, hipStream_t s) {
+  copy_cast_from_f32(src, dst, n, bf, s);
+}
+
+void copy_cast_from_f32(const float* src, void* dst, int64_t n, bool bf, hipStream_t s) {
+  if (n <= 0) return;
+  TSEL(bf, hipLaunchKernelGGL(cast_k<bf16>, dim3(gs_blocks(n)), dim3(256), 0, s, src, (bf16*)dst, n),
+       hipLaunchKernelGGL(cast_k<float>, dim3(gs_blocks(n)), dim3(256), 0, s, src, (float*)dst, n));
+}
+
+void widen(const void* src, float* dst, int64_t n, bool bf, hipStream_t s) {
+  if (n <= 0) return;
+  TSEL(bf, hipLaunchKernelGGL(widen_k<bf16>, dim3(gs_blocks(n)), dim3(256), 0, s, (const bf16*)src, dst, n),
+       hipLaunchKernelGGL(widen_k<float>, dim3(gs_blocks(n)), dim3(256), 0, s, (const float*)src, dst, n));
+}
+
+void fill_f32(float* p, int64_t n, float v, hipStream_t s) {
+  if (n <= 0) return;
+  hipLaunchKernelGGL(fill_k, dim3(gs_blocks(n)), dim3(256), 0, s, p, n, v);
+}
+
+void rope_qkv(const void* qkv, int n, int H, int hd, int64_t pos0, const double* theta, void* q_out,
+              void* kring, void* vring, int64_t cap, bool bf, hipStream_t s) {
+  const int64_t total = (int64_t)n * H * (hd / 2);
+  if (total <= 0) return;
+  TSEL(bf, hipLaunchKernelGGL(rope_qkv_k<bf16>, dim3(nblk(total, 256)), dim3(256), 0, s, (const bf16*)qkv, n, H, hd, pos0, theta, (bf16*)q_out, (bf16*)kring, (bf16*)vring, cap),
+       hipLaunchKernelGGL(rope_qkv_k<float>, dim3(nblk(total, 256)), dim3(256), 0, s, (const float*)qkv, n, H, hd, pos0, theta, (float*)q_out, (float*)kring, (float*)vring, cap));
+}
+
+void rope_qkv_f32in(const float* qkv, int H, int hd, int64_t pos, const double* theta, void* q_out,
+                    void* kring, void* vring, int64_t cap, bool bf, hipStream_t s) {
+  const int total = H * (hd / 2);
+  TSEL(bf, hipLaunchKernelGGL(rope_qkv_f32in_k<bf16>, dim3(nblk(total, 256)), dim3(256), 0, s, qkv, H, hd, pos, theta, (bf16*)q_out, (bf16*)kring, (bf16*)vring, cap),
+       hipLaunchKernelGGL(rope_qkv_f32in_k<float>, dim3(nblk(total, 256)), dim3(256), 0, s, qkv, H, hd, pos, theta, (float*)q_out, (float*)kring, (float*)vring, cap));
+}
+
+void rope_bwd(void* dqkv, int n, int H, int hd, int64_t pos0, const double* theta, bool bf,
+              hipStream_t s) {
+  const int64_t total = (int64_t)n * H * (hd / 2);
+  if (total <= 0) return;
+  TSEL(bf, hipLaunchKernelGGL(rope_bwd_k<bf16>, dim3(nblk(total, 256)), dim3(256), 0, s, (bf16*)dqkv, n, H, hd, pos0, theta),
+       hipLaunchKernelGGL(rope_bwd_k<float>, dim3(nblk(total, 256)), dim3(256), 0, s, (float*)dqkv, n, H, hd, pos0, theta));
+}
+
+void act_bwd(const float* dact, const void* z, int n, int F, bool swiglu, void* dz, bool bf,
+             hipStream_t s) {
+  const int64_t total = (int64_t)n * F;
+  if (total <= 0) return;
+  TSEL(bf, hipLaunchKernelGGL(act_bwd_k<bf16>, dim3(nblk(total, 256)), dim3(256), 0, s, dact, (const bf16*)z, n, F, (int)swiglu, (bf16*)dz),
+       hipLaunchKernelGGL(act_bwd_k<float>, dim3(nblk(total, 256)), dim3(256), 0, s, dact, (const float*)z, n, F, (int)swiglu, (float*)dz));
+}
+
+void convert_weight(const void* src, int rows, int cols, bool transpose, int ilv, void* dst, bool bf,
+                    hipStream_t s) {
+  dim3 grid(nblk(cols, 32), nblk(rows, 32));
+  TSEL(bf, hipLaunchKernelGGL(convert_k<bf16>, grid, dim3(256), 0, s, (const bf16*)src, rows, cols, (int)transpose, ilv, (bf16*)dst),
+       hipLaunchKernelGGL(convert_k<float>, grid, dim3(256), 0, s, (const float*)src, rows, cols, (int)transpose, ilv, (float*)dst));
+}
+
+void export_weight(const float* master, int out_dim, int in_dim, int ilv, int which, float* dst,
+                   hipStream_t s) {
+  const int64_t total = (int64_t)out_dim * in_dim;
+  hipLaunchKernelGGL(export_k, dim3(nblk(total, 256)), dim3(256), 0, s, master, out_dim, in_dim, ilv, which, dst);
+}
+
+void ce_finish(const float* part_max, const float* part_sum, int nparts, int64_t ldpart,
+               const float* tgt_logit, int n_rows, int n_tgt, float* lse, float* loss_out, int* err,
+               hipStream_t s) {
+  // rowloss reuses the tail of lse's buffer region provided by the caller:
+  // lse has room for 2*n_rows floats.
+  float* rowloss = lse + n_rows;
+  hipLaunchKernelGGL(ce_rows_k, dim3(nblk(n_rows, 4)), dim3(256), 0, s, part_max, part_sum, nparts, ldpart,
+                     tgt_logit, n_rows, n_tgt, lse, rowloss);
+  hipLaunchKernelGGL(ce_mean_k, dim3(1), dim3(1024), 0, s, rowloss, n_tgt, loss_out, err);
+}
+
+void attn_rowdot(const void* o, const void* dout, int n, int H, int hd, float* D, bool bf,
+                 hipStream_t s) {
+  const int waves = n * H;
+  if (waves <= 0) return;
+  TSEL(bf, hipLaunchKernelGGL(rowdot_k<bf16>, dim3(nblk(waves, 4)), dim3(256), 0, s, (const bf16*)o, (const bf16*)dout, n, H, hd, D),
+       hipLaunchKernelGGL(rowdot_k<float>, dim3(nblk(waves, 4)), dim3(256), 0, s, (const float*)o, (const float*)dout, n, H, hd, D));
+}
+
+}  // namespace ttt

@@ -1,0 +1,316 @@
+// Tiled matrix-core GEMM for gfx950 with fused epilogues.
+//
+//   C[M,N] = sum_k A[m,k] * B[n,k]
+//
+// A is given either k-contiguous ([M][K] row-major) or m-contiguous
+// ([K][M] row-major); B either k-contiguous ([N][K]) or n-contiguous
+// ([K][N]).  Both are staged in LDS k-contiguous, so one compute loop serves
+// the forward products (y = x W), the input-gradient products (dx = dy W^T)
+// and the weight-gradient products (dW = x^T dy, reduction over tokens).
+//
+// Workgroup tile 128x128, 4 waves in 2x2, each wave 64x64 = 4x4 blocks of
+// 16x16 matrix-core accumulators; K staged 128 bytes per step (64 bf16 or
+// 32 fp32) with a double-buffered LDS tile and register prefetch.
+//
+// Epilogues (fused so that intermediate products never round-trip HBM):
+//   STORE   out = acc                              (T or fp32)
+//   RESID   out_f32 = resid_f32 + acc              (residual stream)
+//   GELU    z = acc, act = gelu_erf(acc)
+//   SWIGLU  columns come in blocks of 16 gate / 16 up; z = acc,
+//           act = silu(gate) * up
+//   SGD     master_f32 -= lr * acc ; shadow = round(master)   (fast weights)
+//   CESTAT  per-row partial max / sum(exp) of the logits and the target logit
+//   CEGRAD  g = (softmax - onehot(target)) / n_targets, rows without a target 0
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace ttt {
+
+namespace {
+
+constexpr int BM = 128, BN = 128, NT = 256;
+
+template <typename T> struct GemmCfg {
+  static constexpr int BK = 128 / sizeof(T);      // 64 bf16, 32 fp32
+  static constexpr int PAD = 16 / sizeof(T);
+  static constexpr int LS = BK + PAD;             // LDS row stride (elements)
+  static constexpr int V = Vec16<T>::N;
+};
+
+// Register-staged loader for one operand tile (rows x BK).
+template <typename T, bool KC, int ROWS> struct TileLoader {
+  using C = GemmCfg<T>;
+  static constexpr int V = C::V;
+  // k-contiguous: ROWS*BK/V vectors; m-contiguous: (ROWS/V)*(BK/4) groups of 4 vectors
+  static constexpr int NV = KC ? (ROWS * C::BK / V) / NT : 4 * ((ROWS / V) * (C::BK / 4)) / NT;
+  U128 r[NV];
+
+  DEVI void load(const T* __restrict__ g, int64_t ld, int row0, int row_lim, int k0, int K, int tid) {
+    if constexpr (KC) {
+      constexpr int VPR = C::BK / V;
+#pragma unroll
+      for (int it = 0; it < NV; ++it) {
+        int idx = it * NT + tid;
+        int rr = idx / VPR, c = (idx % VPR) * V;
+        bool ok = (row0 + rr < row_lim) && (k0 + c < K);
+        r[it] = ok ? ld128(g + (int64_t)(row0 + rr) * ld + k0 + c) : zero128();
+      }
+    } else {
+      constexpr int MV = ROWS / V;
+#pragma unroll
+      for (int it = 0; it < NV / 4; ++it) {
+        int idx = it * NT + tid;
+        int mv = idx % MV, kb = idx / MV;
+        int m = row0 + mv * V, k = k0 + kb * 4;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          bool ok = (k + q < K) && (m < row_lim);
+          r[it * 4 + q] = ok ? ld128(g + (int64_t)(k + q) * ld + m) : zero128();
+        }
+      }
+    }
+  }
+
+  DEVI void store(T* __restrict__ lds, int tid) const {
+    if constexpr (KC) {
+      constexpr int VPR = C::BK / V;
+#pragma unroll
+      for (int it = 0; it < NV; ++it) {
+        int idx = it * NT + tid;
+        int rr = idx / VPR, c = (idx % VPR) * V;
+        st128(lds + rr * C::LS + c, r[it]);
+      }
+    } else {
+      constexpr int MV = ROWS / V;
+#pragma unroll
+      for (int it = 0; it < NV / 4; ++it) {
+        int idx = it * NT + tid;
+        int mv = idx % MV, kb = idx / MV;
+        int m0 = mv * V, k0 = kb * 4;
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          T t4[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) t4[q] = elem<T>(r[it * 4 + q], e);
+          T* dst = lds + (m0 + e) * C::LS + k0;
+          if constexpr (sizeof(T) == 2) {
+            uint2 w;
+            w.x = (uint32_t)__builtin_bit_cast(uint16_t, t4[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, t4[1]) << 16);
+            w.y = (uint32_t)__builtin_bit_cast(uint16_t, t4[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, t4[3]) << 16);
+            *reinterpret_cast<uint2*>(dst) = w;
+          } else {
+            float4 w; w.x = t4[0]; w.y = t4[1]; w.z = t4[2]; w.w = t4[3];
+            *reinterpret_cast<float4*>(dst) = w;
+          }
+        }
+      }
+    }
+  }
+};
+
+DEVI float gelu_erf(float z) { return 0.5f * z * (1.f + erff(z * 0.70710678118654752f)); }
+DEVI float silu(float z) { return z / (1.f + __expf(-z)); }
+
+template <typename T, bool A_KC, bool B_KC, int EPI, typename TO>
+__global__ __launch_bounds__(NT) void gemm_kernel(GemmParams p) {
+  using C = GemmCfg<T>;
+  __shared__ __attribute__((aligned(16))) T lds[2][(BM + BN) * C::LS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const T* __restrict__ A = static_cast<const T*>(p.A);
+  const T* __restrict__ B = static_cast<const T*>(p.B);
+
+  TileLoader<T, A_KC, BM> la;
+  TileLoader<T, B_KC, BN> lb;
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = (p.K + C::BK - 1) / C::BK;
+  la.load(A, p.lda, m0, p.M, 0, p.K, tid);
+  lb.load(B, p.ldb, n0, p.N, 0, p.K, tid);
+  la.store(lds[0], tid);
+  lb.store(lds[0] + BM * C::LS, tid);
+  __syncthreads();
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) {
+      la.load(A, p.lda, m0, p.M, (kt + 1) * C::BK, p.K, tid);
+      lb.load(B, p.ldb, n0, p.N, (kt + 1) * C::BK, p.K, tid);
+    }
+    const T* As = lds[cur];
+    const T* Bs = lds[cur] + BM * C::LS;
+#pragma unroll
+    for (int ks = 0; ks < C::BK / 32; ++ks) {
+      typename Frag<T>::type af[4], bfr[4];
+      const int kk = ks * 32 + 8 * (lane >> 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[i] = lds_frag8<T>(As + (wm * 64 + i * 16 + (lane & 15)) * C::LS + kk);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bfr[j] = lds_frag8<T>(Bs + (wn * 64 + j * 16 + (lane & 15)) * C::LS + kk);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mma16x16x32(af[i], bfr[j], acc[i][j]);
+    }
+    if (kt + 1 < nk) {
+      la.store(lds[cur ^ 1], tid);
+      lb.store(lds[cur ^ 1] + BM * C::LS, tid);
+    }
+    __syncthreads();
+  }
+
+  // ---------------------------------------------------------------- epilogue
+  const int rbase = m0 + wm * 64 + 4 * (lane >> 4);
+  const int cbase = n0 + wn * 64 + (lane & 15);
+
+  if constexpr (EPI == EPI_CESTAT) {
+    // rows = tokens, cols = vocab; partial (max, sumexp) of this wave's 64
+    // columns, plus the target logit where the target falls in them.
+    const int* tgt = p.tgt;
+    const int part = blockIdx.x * 2 + wn;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = rbase + i * 16 + e;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int col = cbase + j * 16;
+          if (col < p.N) mx = fmaxf(mx, acc[i][j][e]);
+        }
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+        float s = 0.f;
+        float tv = 0.f;
+        bool has = false;
+        const int t = (row < p.n_tgt) ? tgt[row] : -1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int col = cbase + j * 16;
+          if (col < p.N) s += __expf(acc[i][j][e] - mx);
+          if (col == t) { tv = acc[i][j][e]; has = true; }
+        }
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o, 64);
+        if (row < p.M) {
+          if ((lane & 15) == 0) {
+            p.part_max[(int64_t)part * p.ldpart + row] = mx;
+            p.part_sum[(int64_t)part * p.ldpart + row] = s;
+          }
+          if (has) p.tgt_logit[row] = tv;
+        }
+      }
+    }
+    return;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = rbase + i * 16 + e;
+        if (row >= p.M) continue;
+        if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+          for (int pr = 0; pr < 2; ++pr) {
+            const int colg = cbase + (2 * pr) * 16;
+            const int colu = colg + 16;
+            if (colu < p.N) {
+              const float g = acc[i][2 * pr][e], u = acc[i][2 * pr + 1][e];
+              TO* z = static_cast<TO*>(p.C);
+              z[(int64_t)row * p.ldc + colg] = from_f32<TO>(g);
+              z[(int64_t)row * p.ldc + colu] = from_f32<TO>(u);
+              const int ca = (n0 + wn * 64) / 2 + pr * 16 + (lane & 15);
+              static_cast<TO*>(p.C2)[(int64_t)row * p.ldc2 + ca] = from_f32<TO>(silu(g) * u);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int col = cbase + j * 16;
+            if (col >= p.N) continue;
+            const float v = acc[i][j][e];
+            const int64_t ci = (int64_t)row * p.ldc + col;
+            if constexpr (EPI == EPI_STORE) {
+              static_cast<TO*>(p.C)[ci] = from_f32<TO>(v);
+            } else if constexpr (EPI == EPI_RESID) {
+              static_cast<float*>(p.C)[ci] = p.R[(int64_t)row * p.ldr + col] + v;
+            } else if constexpr (EPI == EPI_GELU) {
+              static_cast<TO*>(p.C)[ci] = from_f32<TO>(v);
+              static_cast<TO*>(p.C2)[(int64_t)row * p.ldc2 + col] = from_f32<TO>(gelu_erf(v));
+            } else if constexpr (EPI == EPI_SGD) {
+              float* w = static_cast<float*>(p.C);
+              const float nw = w[ci] - p.alpha * v;
+              w[ci] = nw;
+              if (p.C2) static_cast<TO*>(p.C2)[(int64_t)row * p.ldc2 + col] = from_f32<TO>(nw);
+            } else if constexpr (EPI == EPI_CEGRAD) {
+              float g = 0.f;
+              if (row < p.n_tgt) {
+                g = __expf(v - p.lse[row]);
+                if (col == p.tgt[row]) g -= 1.f;
+                g *= p.alpha;
+              }
+              static_cast<TO*>(p.C)[ci] = from_f32<TO>(g);
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+template <typename T, bool AK, bool BK_, int EPI, typename TO>
+void launch_t(const GemmParams& p, hipStream_t s) {
+  dim3 grid((p.N + BN - 1) / BN, (p.M + BM - 1) / BM);
+  hipLaunchKernelGGL((gemm_kernel<T, AK, BK_, EPI, TO>), grid, dim3(NT), 0, s, p);
+}
+
+template <typename T>
+int dispatch(const GemmParams& p, bool a_kc, bool b_kc, int epi, bool out_f32, hipStream_t s) {
+  // The instantiations used by the inner loop.
+  if (a_kc && b_kc) {
+    switch (epi) {
+      case EPI_STORE:
+        if (out_f32) launch_t<T, true, true, EPI_STORE, float>(p, s);
+        else launch_t<T, true, true, EPI_STORE, T>(p, s);
+        return 0;
+      case EPI_RESID: launch_t<T, true, true, EPI_RESID, float>(p, s); return 0;
+      case EPI_GELU: launch_t<T, true, true, EPI_GELU, T>(p, s); return 0;
+      case EPI_SWIGLU: launch_t<T, true, true, EPI_SWIGLU, T>(p, s); return 0;
+      case EPI_CESTAT: launch_t<T, true, true, EPI_CESTAT, float>(p, s); return 0;
+      case EPI_CEGRAD: launch_t<T, true, true, EPI_CEGRAD, T>(p, s); return 0;
+      default: return -1;
+    }
+  }
+  if (a_kc && !b_kc) {
+    if (epi != EPI_STORE) return -1;
+    if (out_f32) launch_t<T, true, false, EPI_STORE, float>(p, s);
+    else launch_t<T, true, false, EPI_STORE, T>(p, s);
+    return 0;
+  }
+  if (!a_kc && !b_kc) {
+    if (epi != EPI_SGD) return -1;
+    launch_t<T, false, false, EPI_SGD, T>(p, s);
+    return 0;
+  }
+  return -1;
+}
+
+}  // namespace
+
+int gemm(const GemmParams& p, bool bf16_operands, bool a_kc, bool b_kc, int epi, bool out_f32,
+         hipStream_t s) {
+  if (p.M <= 0 || p.N <= 0) return 0;
+  return bf16_operands ? dispatch<bf16>(p, a_kc, b_kc, epi, out_f32, s)
+                       : dispatch<float>(p, a_kc, b_kc, epi, out_f32, s);
+}
+
+}  // namespace ttt

@@ -1,0 +1,87 @@
+// Host-side launchers of the HIP kernels (internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ttt {
+
+enum Epi { EPI_STORE = 0, EPI_RESID, EPI_GELU, EPI_SWIGLU, EPI_SGD, EPI_CESTAT, EPI_CEGRAD };
+
+struct GemmParams {
+  const void* A = nullptr; int64_t lda = 0;  // k-contiguous [M][K] or m-contiguous [K][M]
+  const void* B = nullptr; int64_t ldb = 0;  // k-contiguous [N][K] or n-contiguous [K][N]
+  int M = 0, N = 0, K = 0;
+  void* C = nullptr; int64_t ldc = 0;        // primary output
+  const float* R = nullptr; int64_t ldr = 0; // residual input (RESID)
+  void* C2 = nullptr; int64_t ldc2 = 0;      // act (GELU/SWIGLU), bf16 shadow (SGD)
+  float alpha = 0.f;                         // SGD: lr; CEGRAD: 1/n_targets
+  // cross-entropy epilogues
+  const int* tgt = nullptr; int n_tgt = 0;
+  float* part_max = nullptr; float* part_sum = nullptr; int64_t ldpart = 0;
+  float* tgt_logit = nullptr; const float* lse = nullptr;
+};
+
+// Returns 0, or -1 for an epilogue/layout combination that is not built.
+int gemm(const GemmParams& p, bool bf16_operands, bool a_kc, bool b_kc, int epi, bool out_f32,
+         hipStream_t s);
+
+// ---- elementwise (elementwise.hip); T is bf16 when bf16 != 0, else float
+void embed(const int32_t* tok, int n, const void* E, int d, int V, bool bf16, float* out, int* err,
+           hipStream_t s);
+void layernorm_fwd(const float* x, int64_t ldx, int n, int d, float eps, void* y, int64_t ldy,
+                   float* mean, float* rstd, bool bf16, hipStream_t s);
+// acc += LN_backward(dy) ; optionally acc_lo = low-precision copy of the new acc
+void layernorm_bwd_acc(const float* dy, const float* x, const float* mean, const float* rstd, int n,
+                       int d, float* acc, void* acc_lo, bool bf16, hipStream_t s);
+// acc_lo = low-precision copy of acc
+void cast_rows(const float* src, void* dst, int64_t n, bool bf16, hipStream_t s);
+void rope_qkv(const void* qkv, int n, int H, int hd, int64_t pos0, const double* theta, void* q_out,
+              void* kring, void* vring, int64_t cap, bool bf16, hipStream_t s);
+void rope_bwd(void* dqkv, int n, int H, int hd, int64_t pos0, const double* theta, bool bf16,
+              hipStream_t s);
+void act_bwd(const float* dact, const void* z, int n, int F, bool swiglu, void* dz, bool bf16,
+             hipStream_t s);
+void convert_weight(const void* src, int rows, int cols, bool transpose, int interleave16_half,
+                    void* dst, bool bf16, hipStream_t s);
+void export_weight(const float* master, int out_dim, int in_dim, int interleave_half, int which,
+                   float* dst, hipStream_t s);
+void widen(const void* src, float* dst, int64_t n, bool bf16, hipStream_t s);
+void copy_cast_from_f32(const float* src, void* dst, int64_t n, bool bf16, hipStream_t s);
+void fill_f32(float* p, int64_t n, float v, hipStream_t s);
+void ce_finish(const float* part_max, const float* part_sum, int nparts, int64_t ldpart,
+               const float* tgt_logit, int n_rows, int n_tgt, float* lse, float* loss_out,
+               int* err, hipStream_t s);
+void attn_rowdot(const void* o, const void* dout, int n, int H, int hd, float* D, bool bf16,
+                 hipStream_t s);
+
+// ---- attention (attention.hip)
+struct AttnParams {
+  const void* q = nullptr;   // [n][H*hd], row stride ldq
+  int64_t ldq = 0;
+  const void* kring = nullptr; const void* vring = nullptr;  // [cap][H*hd]
+  int64_t cap = 0;
+  int n = 0, H = 0, hd = 0, window = 0;
+  int64_t pos0 = 0;          // absolute position of query row 0
+  void* o = nullptr; int64_t ldo = 0;
+  float* lse = nullptr;      // [H][n] natural-log LSE (may be null)
+  // backward
+  const void* dout = nullptr; int64_t lddo = 0;
+  const float* D = nullptr;  // [H][n] rowsum(dO*O)
+  void* dq = nullptr; void* dk = nullptr; void* dv = nullptr; int64_t ldg = 0;
+  int64_t kmin = 0;          // smallest key position that receives dK/dV (chunk start)
+};
+void swa_fwd(const AttnParams& p, bool bf16, hipStream_t s);
+void swa_bwd(const AttnParams& p, bool bf16, hipStream_t s);
+
+// ---- decode (decode.hip)
+void gemv(const void* W, int N, int K, const void* x, bool x_f32, float* y, const float* resid,
+          bool bf16, hipStream_t s);
+void swiglu_vec(const float* z, int F, void* act, bool bf16, hipStream_t s);
+void gelu_vec(const float* z, int F, void* act, bool bf16, hipStream_t s);
+void swa_decode(const void* q, const void* kring, const void* vring, int64_t cap, int H, int hd,
+                int window, int64_t pos, void* o, float* ws, bool bf16, hipStream_t s);
+void argmax_tok(const float* logits, int V, int32_t* out_tok, int32_t* tok_hist, hipStream_t s);
+void rope_qkv_f32in(const float* qkv, int H, int hd, int64_t pos, const double* theta, void* q_out,
+                    void* kring, void* vring, int64_t cap, bool bf16, hipStream_t s);
+
+}  // namespace ttt

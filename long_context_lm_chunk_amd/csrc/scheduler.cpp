@@ -1,0 +1,790 @@
+// Chunk scheduler and C ABI of the TTT-E2E inner loop.
+//
+// Per context (ttt_prefill):
+//   phase A  for a block of whole chunks (prefill_block tokens): embed, then
+//            every frozen block 0 .. L-q-1 and the attention half of block
+//            L-q, batched over the whole block.  None of this depends on the
+//            fast weights: only the MLPs of the last q blocks are updated
+//            (podcast 6:36 and 7:08), and attention/embeddings stay static.
+//   phase B  for each chunk of the block, sequentially (the next chunk needs
+//            the weights updated by this one): forward of the top q blocks
+//            with the current fast weights, fused head + next-token
+//            cross-entropy (NVIDIA blog, "Our method": the loss at the end of
+//            the network), backward into the fast MLPs only, fused SGD in the
+//            weight-gradient epilogue (forum post TL;DR: mini-gradient
+//            descent on the context during inference).
+// Keys/values are written to per-layer rings when a position is read and
+// are never recomputed, so attention memory stays bounded by the window.
+//
+// Everything stays resident in the caller's workspace; the host only
+// enqueues kernels on one stream and reads back an error flag.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "kernels.hpp"
+#include "../../include/ttt.h"
+
+using namespace ttt;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+#define HIPCHK(x)                                                                 \
+  do {                                                                            \
+    hipError_t e_ = (x);                                                          \
+    if (e_ != hipSuccess) return fail(TTT_ERR_HIP, std::string(#x) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+constexpr int NCLS = 8;
+
+struct Timing {
+  bool on = false;
+  std::vector<hipEvent_t> ev;   // pairs
+  size_t used = 0;
+  int64_t launches = 0;
+  double flops = 0.0;
+};
+
+// Bump allocator over the workspace (base == nullptr computes the size).
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  template <typename P> P* take(size_t bytes) {
+    off = (off + 255) & ~size_t(255);
+    P* p = base ? reinterpret_cast<P*>(base + off) : nullptr;
+    off += bytes;
+    return p;
+  }
+};
+
+struct FastLayer {
+  float* m_up = nullptr;  // fp32 master [F2][d]
+  float* m_dn = nullptr;  // fp32 master [d][F]
+  void* s_up = nullptr;   // bf16 shadow (== master in fp32 mode)
+  void* s_dn = nullptr;
+};
+
+struct Layer {
+  void* wqkv = nullptr;  // [3d][d]  out-major
+  void* wo = nullptr;    // [d][d]
+  void* wup = nullptr;   // [F2][d] (SwiGLU: gate/up interleaved in 16-row blocks)
+  void* wdn = nullptr;   // [d][F]
+  void* kring = nullptr; void* vring = nullptr;  // [cap][d]
+  int64_t cap = 0;
+};
+
+struct PB {  // phase-B buffers of one fast layer (chunk rows)
+  float* xin = nullptr; float* x2 = nullptr;
+  float* mean1 = nullptr; float* rstd1 = nullptr; float* mean2 = nullptr; float* rstd2 = nullptr;
+  void* a = nullptr; void* q = nullptr; void* o = nullptr; float* lse = nullptr;
+  void* b = nullptr; void* z = nullptr; void* act = nullptr;
+};
+
+}  // namespace
+
+struct ttt_model {
+  ttt_config c{};
+  bool bf = true;
+  size_t es = 2;          // element size of weights/activations
+  int d = 0, F = 0, F2 = 0, V = 0, L = 0, q = 0, f0 = 0, H = 0, hd = 0, W = 0, Cmax = 0, MA = 0;
+  int nparts = 0;
+  void* E = nullptr; void* U = nullptr;
+  std::vector<Layer> layers;
+  std::vector<FastLayer> fast;
+  double* theta = nullptr;
+  // phase A
+  float* hA = nullptr; void* aA = nullptr; void* qkvA = nullptr; void* qA = nullptr; void* oA = nullptr;
+  void* zA = nullptr; void* actA = nullptr;
+  // phase B
+  std::vector<PB> pb;
+  float* xL = nullptr; float* meanf = nullptr; float* rstdf = nullptr; void* fN = nullptr;
+  void* qkvB = nullptr;
+  float* pmax = nullptr; float* psum = nullptr; float* tlog = nullptr; float* lse_ce = nullptr;
+  void* G = nullptr;
+  float* dh = nullptr; void* dh_lo = nullptr; float* dact = nullptr; void* dz = nullptr;
+  float* dtmp = nullptr; void* dout = nullptr; void* dqkv = nullptr; float* Dattn = nullptr;
+  // decode
+  float* xd = nullptr; void* ad = nullptr; float* qkvd = nullptr; void* qd = nullptr; void* od = nullptr;
+  float* zd = nullptr; void* actd = nullptr; float* logits = nullptr; float* attn_ws = nullptr;
+  int32_t* hist = nullptr; int32_t* cur_tok = nullptr;
+  int* err = nullptr;
+  float* nanv = nullptr;
+  // state
+  int64_t pos = 0;        // next position to read
+  int64_t dchunk0 = 0;    // first position of the current decode chunk
+  bool prefilled = false;
+  float lr = 0.f; int steps = 1; int chunk = 1;
+  Timing tm[NCLS];
+};
+
+namespace {
+
+size_t esz(const ttt_config& c) { return c.dtype == TTT_BF16 ? 2 : 4; }
+
+int check_config(const ttt_config* c) {
+  if (!c) return fail(TTT_ERR_ARG, "config is NULL");
+  if (c->dtype != TTT_BF16 && c->dtype != TTT_FP32) return fail(TTT_ERR_CONFIG, "dtype must be TTT_BF16 or TTT_FP32");
+  if (c->mlp != TTT_MLP_GELU && c->mlp != TTT_MLP_SWIGLU) return fail(TTT_ERR_CONFIG, "mlp must be GELU or SwiGLU");
+  const int hd = c->head_dim;
+  if (!(hd == 16 || hd == 32 || hd == 64 || hd == 96 || hd == 128)) return fail(TTT_ERR_CONFIG, "head_dim must be 16, 32, 64, 96 or 128");
+  if (c->n_heads <= 0 || c->n_heads * hd != c->d_model) return fail(TTT_ERR_CONFIG, "n_heads * head_dim must equal d_model");
+  if (c->d_model % 16 || c->d_ff % 16 || c->d_ff <= 0) return fail(TTT_ERR_CONFIG, "d_model and d_ff must be positive multiples of 16");
+  if (c->vocab <= 0 || c->vocab % 8) return fail(TTT_ERR_CONFIG, "vocab must be a positive multiple of 8");
+  if (c->n_layers <= 0 || c->n_fast < 1 || c->n_fast > c->n_layers) return fail(TTT_ERR_CONFIG, "need 1 <= n_fast <= n_layers");
+  if (c->window < 1) return fail(TTT_ERR_CONFIG, "window must be >= 1");
+  if (c->max_chunk < 1 || c->max_chunk > (1 << 16)) return fail(TTT_ERR_CONFIG, "max_chunk must be in [1, 65536]");
+  if (c->prefill_block < 0) return fail(TTT_ERR_CONFIG, "prefill_block must be >= 0");
+  if (!(c->ln_eps > 0.f) || !(c->rope_base > 1.f)) return fail(TTT_ERR_CONFIG, "ln_eps > 0 and rope_base > 1 required");
+  return TTT_OK;
+}
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// Lay the model out in the workspace (m->... pointers); returns bytes used.
+size_t layout(ttt_model* m, void* base) {
+  Carver cv(base);
+  const ttt_config& c = m->c;
+  const size_t es = m->es;
+  const int d = m->d, F = m->F, F2 = m->F2, V = m->V, C = m->Cmax, MA = m->MA, H = m->H;
+  m->E = cv.take<void>((size_t)V * d * es);
+  m->U = cv.take<void>((size_t)V * d * es);
+  m->layers.assign(m->L, Layer());
+  const int64_t capA = round_up((int64_t)m->W + MA, 64);
+  const int64_t capB = round_up((int64_t)m->W + C, 64);
+  for (int l = 0; l < m->L; ++l) {
+    Layer& ly = m->layers[l];
+    ly.wqkv = cv.take<void>((size_t)3 * d * d * es);
+    ly.wo = cv.take<void>((size_t)d * d * es);
+    ly.wup = cv.take<void>((size_t)F2 * d * es);
+    ly.wdn = cv.take<void>((size_t)d * F * es);
+    ly.cap = (l <= m->f0) ? capA : capB;
+    ly.kring = cv.take<void>((size_t)ly.cap * d * es);
+    ly.vring = cv.take<void>((size_t)ly.cap * d * es);
+  }
+  m->fast.assign(m->q, FastLayer());
+  for (int j = 0; j < m->q; ++j) {
+    FastLayer& f = m->fast[j];
+    f.m_up = cv.take<float>((size_t)F2 * d * 4);
+    f.m_dn = cv.take<float>((size_t)d * F * 4);
+    if (m->bf) {
+      f.s_up = cv.take<void>((size_t)F2 * d * es);
+      f.s_dn = cv.take<void>((size_t)d * F * es);
+    } else {
+      f.s_up = f.m_up;
+      f.s_dn = f.m_dn;
+    }
+  }
+  m->theta = cv.take<double>((size_t)(m->hd / 2) * 8);
+  // phase A
+  m->hA = cv.take<float>((size_t)MA * d * 4);
+  m->aA = cv.take<void>((size_t)MA * d * es);
+  m->qkvA = cv.take<void>((size_t)MA * 3 * d * es);
+  m->qA = cv.take<void>((size_t)MA * d * es);
+  m->oA = cv.take<void>((size_t)MA * d * es);
+  m->zA = cv.take<void>((size_t)MA * F2 * es);
+  m->actA = cv.take<void>((size_t)MA * F * es);
+  // phase B
+  m->pb.assign(m->q, PB());
+  for (int j = 0; j < m->q; ++j) {
+    PB& b = m->pb[j];
+    if (j > 0) {
+      b.xin = cv.take<float>((size_t)C * d * 4);
+      b.x2 = cv.take<float>((size_t)C * d * 4);
+      b.mean1 = cv.take<float>((size_t)C * 4);
+      b.rstd1 = cv.take<float>((size_t)C * 4);
+      b.a = cv.take<void>((size_t)C * d * es);
+      b.q = cv.take<void>((size_t)C * d * es);
+      b.o = cv.take<void>((size_t)C * d * es);
+      b.lse = cv.take<float>((size_t)H * C * 4);
+    }
+    b.mean2 = cv.take<float>((size_t)C * 4);
+    b.rstd2 = cv.take<float>((size_t)C * 4);
+    b.b = cv.take<void>((size_t)C * d * es);
+    b.z = cv.take<void>((size_t)C * F2 * es);
+    b.act = cv.take<void>((size_t)C * F * es);
+  }
+  m->xL = cv.take<float>((size_t)C * d * 4);
+  m->meanf = cv.take<float>((size_t)C * 4);
+  m->rstdf = cv.take<float>((size_t)C * 4);
+  m->fN = cv.take<void>((size_t)C * d * es);
+  m->qkvB = cv.take<void>((size_t)C * 3 * d * es);
+  m->nparts = 2 * ((V + 127) / 128);
+  m->pmax = cv.take<float>((size_t)m->nparts * C * 4);
+  m->psum = cv.take<float>((size_t)m->nparts * C * 4);
+  m->tlog = cv.take<float>((size_t)C * 4);
+  m->lse_ce = cv.take<float>((size_t)2 * C * 4);
+  m->G = cv.take<void>((size_t)C * V * es);
+  m->dh = cv.take<float>((size_t)C * d * 4);
+  m->dh_lo = cv.take<void>((size_t)C * d * es);
+  m->dact = cv.take<float>((size_t)C * F * 4);
+  m->dz = cv.take<void>((size_t)C * F2 * es);
+  m->dtmp = cv.take<float>((size_t)C * d * 4);
+  m->dout = cv.take<void>((size_t)C * d * es);
+  m->dqkv = cv.take<void>((size_t)C * 3 * d * es);
+  m->Dattn = cv.take<float>((size_t)H * C * 4);
+  // decode
+  m->xd = cv.take<float>((size_t)d * 4);
+  m->ad = cv.take<void>((size_t)d * es);
+  m->qkvd = cv.take<float>((size_t)3 * d * 4);
+  m->qd = cv.take<void>((size_t)d * es);
+  m->od = cv.take<void>((size_t)d * es);
+  m->zd = cv.take<float>((size_t)F2 * 4);
+  m->actd = cv.take<void>((size_t)F * es);
+  m->logits = cv.take<float>((size_t)V * 4);
+  const int64_t nsplit = (m->W + 255) / 256 + 1;
+  m->attn_ws = cv.take<float>((size_t)H * nsplit * (2 + m->hd) * 4);
+  m->hist = cv.take<int32_t>((size_t)(C + 2) * 4);
+  m->cur_tok = cv.take<int32_t>(4);
+  m->err = cv.take<int>(4);
+  m->nanv = cv.take<float>(4);
+  (void)c;
+  return cv.off + 256;
+}
+
+void init_dims(ttt_model* m, const ttt_config& c) {
+  m->c = c;
+  m->bf = c.dtype == TTT_BF16;
+  m->es = esz(c);
+  m->d = c.d_model; m->F = c.d_ff; m->F2 = c.mlp == TTT_MLP_SWIGLU ? 2 * c.d_ff : c.d_ff;
+  m->V = c.vocab; m->L = c.n_layers; m->q = c.n_fast; m->f0 = c.n_layers - c.n_fast;
+  m->H = c.n_heads; m->hd = c.head_dim; m->W = c.window; m->Cmax = c.max_chunk;
+  int ma = c.prefill_block > 0 ? c.prefill_block : 8192;
+  if (ma < c.max_chunk) ma = c.max_chunk;
+  m->MA = ma;
+}
+
+// ---------------------------------------------------------------- timing
+struct Scope {
+  ttt_model* m; int cls; hipStream_t s; bool on;
+  Scope(ttt_model* m_, int cls_, hipStream_t s_, double flops) : m(m_), cls(cls_), s(s_) {
+    on = m->tm[cls].on;
+    if (!on) return;
+    Timing& t = m->tm[cls];
+    if (t.used + 2 > t.ev.size()) {
+      for (int i = 0; i < 256; ++i) {
+        hipEvent_t e;
+        if (hipEventCreate(&e) == hipSuccess) t.ev.push_back(e);
+      }
+    }
+    if (t.used + 2 > t.ev.size()) { on = false; return; }
+    hipEventRecord(t.ev[t.used], s);
+    t.launches += 1;
+    t.flops += flops;
+  }
+  ~Scope() {
+    if (!on) return;
+    Timing& t = m->tm[cls];
+    hipEventRecord(t.ev[t.used + 1], s);
+    t.used += 2;
+  }
+};
+
+enum { CLS_GEMM = 0, CLS_ATTN_FWD = 1, CLS_ATTN_BWD = 2, CLS_CE = 3, CLS_SGD = 4, CLS_MLP_UP = 5 };
+
+int run_gemm(ttt_model* m, const GemmParams& p, bool a_kc, bool b_kc, int epi, bool out_f32,
+             hipStream_t s) {
+  const double fl = 2.0 * p.M * (double)p.N * p.K;
+  int rc;
+  {
+    Scope t0(m, CLS_GEMM, s, fl);
+    Scope t4(m, epi == EPI_SGD ? CLS_SGD : (epi == EPI_GELU || epi == EPI_SWIGLU) ? CLS_MLP_UP : NCLS - 1, s,
+             (epi == EPI_SGD || epi == EPI_GELU || epi == EPI_SWIGLU) ? fl : 0.0);
+    rc = gemm(p, m->bf, a_kc, b_kc, epi, out_f32, s);
+  }
+  return rc == 0 ? TTT_OK : fail(TTT_ERR_CONFIG, "internal: GEMM variant not built");
+}
+
+// Algorithmic attention work: the number of (query, key) pairs inside the
+// window for queries at positions [p0, p0+n), i.e. sum_t min(t+1, W), and
+// (inchunk) the pairs whose key is >= kmin = p0.
+double window_sum(int64_t a, int64_t b, int64_t W) {   // sum_{t=a}^{b-1} min(t+1, W)
+  if (b <= a) return 0.0;
+  const int64_t e = std::min<int64_t>(b, W - 1);        // t < W-1 contributes t+1
+  double s = 0.0;
+  if (e > a) s += 0.5 * (double)(e - a) * (double)(a + 1 + e);
+  const int64_t f = std::max<int64_t>(a, W - 1);
+  if (b > f) s += (double)W * (double)(b - f);
+  return s;
+}
+double pairs(int64_t p0, int n, int64_t W, int64_t kmin, double* inchunk) {
+  if (inchunk) *inchunk = window_sum(p0 - kmin, p0 - kmin + n, W);
+  return window_sum(p0, p0 + n, W);
+}
+
+// --------------------------------------------------------------- phase A
+int phase_a(ttt_model* m, const int32_t* tokens, int64_t B0, int nb, hipStream_t s) {
+  const int d = m->d, F = m->F, F2 = m->F2;
+  const bool bf = m->bf;
+  embed(tokens + B0, nb, m->E, d, m->V, bf, m->hA, m->err, s);
+  for (int l = 0; l <= m->f0; ++l) {
+    Layer& ly = m->layers[l];
+    layernorm_fwd(m->hA, d, nb, d, m->c.ln_eps, m->aA, d, nullptr, nullptr, bf, s);
+    GemmParams g;
+    g.A = m->aA; g.lda = d; g.B = ly.wqkv; g.ldb = d; g.M = nb; g.N = 3 * d; g.K = d;
+    g.C = m->qkvA; g.ldc = 3 * d;
+    int rc = run_gemm(m, g, true, true, EPI_STORE, false, s); if (rc) return rc;
+    rope_qkv(m->qkvA, nb, m->H, m->hd, B0, m->theta, m->qA, ly.kring, ly.vring, ly.cap, bf, s);
+    AttnParams ap;
+    ap.q = m->qA; ap.ldq = d; ap.kring = ly.kring; ap.vring = ly.vring; ap.cap = ly.cap;
+    ap.n = nb; ap.H = m->H; ap.hd = m->hd; ap.window = m->W; ap.pos0 = B0; ap.o = m->oA; ap.ldo = d;
+    {
+      Scope t(m, CLS_ATTN_FWD, s, 4.0 * d * pairs(B0, nb, m->W, 0, nullptr));
+      swa_fwd(ap, bf, s);
+    }
+    GemmParams go;
+    go.A = m->oA; go.lda = d; go.B = ly.wo; go.ldb = d; go.M = nb; go.N = d; go.K = d;
+    go.C = m->hA; go.ldc = d; go.R = m->hA; go.ldr = d;
+    rc = run_gemm(m, go, true, true, EPI_RESID, true, s); if (rc) return rc;
+    if (l == m->f0) break;
+    layernorm_fwd(m->hA, d, nb, d, m->c.ln_eps, m->aA, d, nullptr, nullptr, bf, s);
+    GemmParams gu;
+    gu.A = m->aA; gu.lda = d; gu.B = ly.wup; gu.ldb = d; gu.M = nb; gu.N = F2; gu.K = d;
+    gu.C = m->zA; gu.ldc = F2; gu.C2 = m->actA; gu.ldc2 = F;
+    rc = run_gemm(m, gu, true, true, m->c.mlp == TTT_MLP_SWIGLU ? EPI_SWIGLU : EPI_GELU, false, s);
+    if (rc) return rc;
+    GemmParams gd;
+    gd.A = m->actA; gd.lda = F; gd.B = ly.wdn; gd.ldb = F; gd.M = nb; gd.N = d; gd.K = F;
+    gd.C = m->hA; gd.ldc = d; gd.R = m->hA; gd.ldr = d;
+    rc = run_gemm(m, gd, true, true, EPI_RESID, true, s); if (rc) return rc;
+  }
+  return TTT_OK;
+}
+
+// --------------------------------------------------------------- phase B
+// One step on one chunk: positions [p0, p0+n), x2_0 = residual stream after
+// the attention of the first fast block ([n][d] fp32), targets tgt[0..n_tgt).
+int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t* tgt, int n_tgt,
+               float lr, float* loss_out, hipStream_t s) {
+  const int d = m->d, F = m->F, F2 = m->F2, V = m->V, q = m->q;
+  const bool bf = m->bf;
+  const float eps = m->c.ln_eps;
+  const int upepi = m->c.mlp == TTT_MLP_SWIGLU ? EPI_SWIGLU : EPI_GELU;
+  int rc;
+  // ---------------- forward of the fast blocks
+  for (int j = 0; j < q; ++j) {
+    const int l = m->f0 + j;
+    Layer& ly = m->layers[l];
+    PB& b = m->pb[j];
+    const float* x2 = x2_0;
+    if (j > 0) {
+      layernorm_fwd(b.xin, d, n, d, eps, b.a, d, b.mean1, b.rstd1, bf, s);
+      GemmParams g;
+      g.A = b.a; g.lda = d; g.B = ly.wqkv; g.ldb = d; g.M = n; g.N = 3 * d; g.K = d;
+      g.C = m->qkvB; g.ldc = 3 * d;
+      rc = run_gemm(m, g, true, true, EPI_STORE, false, s); if (rc) return rc;
+      rope_qkv(m->qkvB, n, m->H, m->hd, p0, m->theta, b.q, ly.kring, ly.vring, ly.cap, bf, s);
+      AttnParams ap;
+      ap.q = b.q; ap.ldq = d; ap.kring = ly.kring; ap.vring = ly.vring; ap.cap = ly.cap;
+      ap.n = n; ap.H = m->H; ap.hd = m->hd; ap.window = m->W; ap.pos0 = p0; ap.o = b.o; ap.ldo = d;
+      ap.lse = b.lse;
+      {
+        Scope t(m, CLS_ATTN_FWD, s, 4.0 * d * pairs(p0, n, m->W, 0, nullptr));
+        swa_fwd(ap, bf, s);
+      }
+      GemmParams go;
+      go.A = b.o; go.lda = d; go.B = ly.wo; go.ldb = d; go.M = n; go.N = d; go.K = d;
+      go.C = b.x2; go.ldc = d; go.R = b.xin; go.ldr = d;
+      rc = run_gemm(m, go, true, true, EPI_RESID, true, s); if (rc) return rc;
+      x2 = b.x2;
+    }
+    layernorm_fwd(x2, d, n, d, eps, b.b, d, b.mean2, b.rstd2, bf, s);
+    GemmParams gu;
+    gu.A = b.b; gu.lda = d; gu.B = m->fast[j].s_up; gu.ldb = d; gu.M = n; gu.N = F2; gu.K = d;
+    gu.C = b.z; gu.ldc = F2; gu.C2 = b.act; gu.ldc2 = F;
+    rc = run_gemm(m, gu, true, true, upepi, false, s); if (rc) return rc;
+    GemmParams gd;
+    gd.A = b.act; gd.lda = F; gd.B = m->fast[j].s_dn; gd.ldb = F; gd.M = n; gd.N = d; gd.K = F;
+    gd.C = (j + 1 < q) ? m->pb[j + 1].xin : m->xL; gd.ldc = d; gd.R = x2; gd.ldr = d;
+    rc = run_gemm(m, gd, true, true, EPI_RESID, true, s); if (rc) return rc;
+  }
+  layernorm_fwd(m->xL, d, n, d, eps, m->fN, d, m->meanf, m->rstdf, bf, s);
+
+  // ---------------- fused head + cross-entropy
+  {
+    Scope t(m, CLS_CE, s, 2.0 * n * (double)d * V);
+    GemmParams gs;
+    gs.A = m->fN; gs.lda = d; gs.B = m->U; gs.ldb = d; gs.M = n; gs.N = V; gs.K = d;
+    gs.tgt = tgt; gs.n_tgt = n_tgt; gs.part_max = m->pmax; gs.part_sum = m->psum;
+    gs.ldpart = m->Cmax; gs.tgt_logit = m->tlog;
+    if (gemm(gs, bf, true, true, EPI_CESTAT, true, s)) return fail(TTT_ERR_CONFIG, "internal: CE variant");
+    ce_finish(m->pmax, m->psum, m->nparts, m->Cmax, m->tlog, n, n_tgt, m->lse_ce, loss_out, m->err, s);
+  }
+  if (n_tgt <= 0) return TTT_OK;   // nothing to learn from this chunk
+  {
+    Scope t(m, CLS_CE, s, 4.0 * n * (double)d * V);
+    GemmParams gg;
+    gg.A = m->fN; gg.lda = d; gg.B = m->U; gg.ldb = d; gg.M = n; gg.N = V; gg.K = d;
+    gg.C = m->G; gg.ldc = V; gg.tgt = tgt; gg.n_tgt = n_tgt; gg.lse = m->lse_ce;
+    gg.alpha = 1.f / (float)n_tgt;
+    if (gemm(gg, bf, true, true, EPI_CEGRAD, false, s)) return fail(TTT_ERR_CONFIG, "internal: CE variant");
+    GemmParams gx;   // dHf = G . U^T  (U stored [V][d]: reduction over V, n-contiguous)
+    gx.A = m->G; gx.lda = V; gx.B = m->U; gx.ldb = d; gx.M = n; gx.N = d; gx.K = V;
+    gx.C = m->dtmp; gx.ldc = d;
+    if (gemm(gx, bf, true, false, EPI_STORE, true, s)) return fail(TTT_ERR_CONFIG, "internal: CE variant");
+  }
+  fill_f32(m->dh, (int64_t)n * d, 0.f, s);
+  layernorm_bwd_acc(m->dtmp, m->xL, m->meanf, m->rstdf, n, d, m->dh, m->dh_lo, bf, s);
+
+  // ---------------- backward through the fast blocks, SGD fused
+  for (int j = q - 1; j >= 0; --j) {
+    const int l = m->f0 + j;
+    Layer& ly = m->layers[l];
+    PB& b = m->pb[j];
+    FastLayer& fw = m->fast[j];
+    const float* x2 = (j > 0) ? b.x2 : x2_0;
+    // dact = dh . Wdn  (reads the weights before their update)
+    GemmParams ga;
+    ga.A = m->dh_lo; ga.lda = d; ga.B = fw.s_dn; ga.ldb = F; ga.M = n; ga.N = F; ga.K = d;
+    ga.C = m->dact; ga.ldc = F;
+    rc = run_gemm(m, ga, true, false, EPI_STORE, true, s); if (rc) return rc;
+    // Wdn -= lr * dh^T act   ([d][F], reduction over the chunk's tokens)
+    GemmParams gw;
+    gw.A = m->dh_lo; gw.lda = d; gw.B = b.act; gw.ldb = F; gw.M = d; gw.N = F; gw.K = n;
+    gw.C = fw.m_dn; gw.ldc = F; gw.C2 = bf ? fw.s_dn : nullptr; gw.ldc2 = F; gw.alpha = lr;
+    rc = run_gemm(m, gw, false, false, EPI_SGD, true, s); if (rc) return rc;
+    act_bwd(m->dact, b.z, n, F, m->c.mlp == TTT_MLP_SWIGLU, m->dz, bf, s);
+    if (j > 0) {
+      GemmParams gb;   // db = dz . Wup (before its update)
+      gb.A = m->dz; gb.lda = F2; gb.B = fw.s_up; gb.ldb = d; gb.M = n; gb.N = d; gb.K = F2;
+      gb.C = m->dtmp; gb.ldc = d;
+      rc = run_gemm(m, gb, true, false, EPI_STORE, true, s); if (rc) return rc;
+    }
+    GemmParams gw2;   // Wup -= lr * dz^T b
+    gw2.A = m->dz; gw2.lda = F2; gw2.B = b.b; gw2.ldb = d; gw2.M = F2; gw2.N = d; gw2.K = n;
+    gw2.C = fw.m_up; gw2.ldc = d; gw2.C2 = bf ? fw.s_up : nullptr; gw2.ldc2 = d; gw2.alpha = lr;
+    rc = run_gemm(m, gw2, false, false, EPI_SGD, true, s); if (rc) return rc;
+    if (j == 0) break;   // no gradient below the first fast MLP
+    layernorm_bwd_acc(m->dtmp, x2, b.mean2, b.rstd2, n, d, m->dh, m->dh_lo, bf, s);
+    GemmParams gdo;   // dO = dh . Wo
+    gdo.A = m->dh_lo; gdo.lda = d; gdo.B = ly.wo; gdo.ldb = d; gdo.M = n; gdo.N = d; gdo.K = d;
+    gdo.C = m->dout; gdo.ldc = d;
+    rc = run_gemm(m, gdo, true, false, EPI_STORE, false, s); if (rc) return rc;
+    attn_rowdot(b.o, m->dout, n, m->H, m->hd, m->Dattn, bf, s);
+    AttnParams ap;
+    ap.q = b.q; ap.ldq = d; ap.kring = ly.kring; ap.vring = ly.vring; ap.cap = ly.cap;
+    ap.n = n; ap.H = m->H; ap.hd = m->hd; ap.window = m->W; ap.pos0 = p0;
+    ap.lse = b.lse; ap.dout = m->dout; ap.lddo = d; ap.D = m->Dattn;
+    ap.dq = m->dqkv; ap.dk = static_cast<char*>(m->dqkv) + (size_t)d * m->es;
+    ap.dv = static_cast<char*>(m->dqkv) + (size_t)2 * d * m->es; ap.ldg = 3 * d; ap.kmin = p0;
+    {
+      double in = 0;
+      const double tot = pairs(p0, n, m->W, p0, &in);
+      Scope t(m, CLS_ATTN_BWD, s, 4.0 * d * (tot + in));
+      swa_bwd(ap, bf, s);
+    }
+    rope_bwd(m->dqkv, n, m->H, m->hd, p0, m->theta, bf, s);
+    GemmParams gq;   // da = dqkv . Wqkv
+    gq.A = m->dqkv; gq.lda = 3 * d; gq.B = ly.wqkv; gq.ldb = d; gq.M = n; gq.N = d; gq.K = 3 * d;
+    gq.C = m->dtmp; gq.ldc = d;
+    rc = run_gemm(m, gq, true, false, EPI_STORE, true, s); if (rc) return rc;
+    layernorm_bwd_acc(m->dtmp, b.xin, b.mean1, b.rstd1, n, d, m->dh, m->dh_lo, bf, s);
+  }
+  return TTT_OK;
+}
+
+int sync_and_check(ttt_model* m, hipStream_t s) {
+  HIPCHK(hipStreamSynchronize(s));
+  int e = 0;
+  HIPCHK(hipMemcpy(&e, m->err, sizeof(int), hipMemcpyDeviceToHost));
+  if (e & 1) return fail(TTT_ERR_TOKEN, "a token id outside [0, vocab) was read");
+  if (e & 2) return fail(TTT_ERR_NONFINITE, "a chunk loss was not finite");
+  return TTT_OK;
+}
+
+int reset_state(ttt_model* m, hipStream_t s) {
+  const int d = m->d, F = m->F, F2 = m->F2;
+  for (int j = 0; j < m->q; ++j) {
+    Layer& ly = m->layers[m->f0 + j];
+    FastLayer& f = m->fast[j];
+    widen(ly.wup, f.m_up, (int64_t)F2 * d, m->bf, s);
+    widen(ly.wdn, f.m_dn, (int64_t)d * F, m->bf, s);
+    if (m->bf) {
+      HIPCHK(hipMemcpyAsync(f.s_up, ly.wup, (size_t)F2 * d * m->es, hipMemcpyDeviceToDevice, s));
+      HIPCHK(hipMemcpyAsync(f.s_dn, ly.wdn, (size_t)d * F * m->es, hipMemcpyDeviceToDevice, s));
+    }
+  }
+  for (int l = 0; l < m->L; ++l) {
+    Layer& ly = m->layers[l];
+    const int64_t n = ly.cap * d * (int64_t)m->es / 4;
+    fill_f32(static_cast<float*>(ly.kring), n, 0.f, s);
+    fill_f32(static_cast<float*>(ly.vring), n, 0.f, s);
+  }
+  fill_f32(reinterpret_cast<float*>(m->err), 1, 0.f, s);
+  m->pos = 0;
+  m->dchunk0 = 0;
+  m->prefilled = false;
+  return TTT_OK;
+}
+
+}  // namespace
+
+// ======================================================================= ABI
+extern "C" {
+
+int ttt_workspace_bytes(const ttt_config* cfg, size_t* bytes) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (!bytes) return fail(TTT_ERR_ARG, "bytes is NULL");
+  ttt_model tmp;
+  init_dims(&tmp, *cfg);
+  *bytes = layout(&tmp, nullptr);
+  return TTT_OK;
+}
+
+int ttt_model_load(const ttt_config* cfg, const void* const* weights, int32_t n_weights,
+                   void* workspace, size_t ws_bytes, void* stream, ttt_model** out) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (!out) return fail(TTT_ERR_ARG, "out is NULL");
+  *out = nullptr;
+  const int per = 4 + (cfg->mlp == TTT_MLP_SWIGLU ? 3 : 2);
+  if (!weights || n_weights != 2 + cfg->n_layers * per)
+    return fail(TTT_ERR_ARG, "n_weights must be 2 + n_layers * (4 + mlp matrices)");
+  for (int i = 0; i < n_weights; ++i)
+    if (!weights[i]) return fail(TTT_ERR_ARG, "a weight pointer is NULL");
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255))
+    return fail(TTT_ERR_WORKSPACE, "workspace must be non-NULL and 256-byte aligned");
+  ttt_model* m = new ttt_model();
+  init_dims(m, *cfg);
+  const size_t need = layout(m, workspace);
+  if (ws_bytes < need) {
+    delete m;
+    return fail(TTT_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need) + " bytes");
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int d = m->d, F = m->F, V = m->V;
+  const bool bf = m->bf;
+  // E [V][d] stays as is; U canonical [d][V] -> [V][d]
+  convert_weight(weights[0], V, d, false, -1, m->E, bf, s);
+  convert_weight(weights[n_weights - 1], d, V, true, -1, m->U, bf, s);
+  for (int l = 0; l < m->L; ++l) {
+    const void* const* w = weights + 1 + l * per;
+    Layer& ly = m->layers[l];
+    char* qkv = static_cast<char*>(ly.wqkv);
+    for (int p = 0; p < 3; ++p)   // Wq, Wk, Wv [d][d] -> rows p*d.. of [3d][d]
+      convert_weight(w[p], d, d, true, -1, qkv + (size_t)p * d * d * m->es, bf, s);
+    convert_weight(w[3], d, d, true, -1, ly.wo, bf, s);
+    if (cfg->mlp == TTT_MLP_SWIGLU) {
+      convert_weight(w[4], d, F, true, 0, ly.wup, bf, s);
+      convert_weight(w[5], d, F, true, 1, ly.wup, bf, s);
+      convert_weight(w[6], F, d, true, -1, ly.wdn, bf, s);
+    } else {
+      convert_weight(w[4], d, F, true, -1, ly.wup, bf, s);
+      convert_weight(w[5], F, d, true, -1, ly.wdn, bf, s);
+    }
+  }
+  // RoPE frequencies theta_i = base^(-2i/hd), float64 on the host
+  std::vector<double> th(m->hd / 2);
+  for (int i = 0; i < m->hd / 2; ++i) th[i] = std::pow((double)cfg->rope_base, -2.0 * i / m->hd);
+  hipError_t e = hipMemcpyAsync(m->theta, th.data(), th.size() * 8, hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) { delete m; return fail(TTT_ERR_HIP, hipGetErrorString(e)); }
+  float nan = NAN;
+  e = hipMemcpyAsync(m->nanv, &nan, 4, hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) { delete m; return fail(TTT_ERR_HIP, hipGetErrorString(e)); }
+  rc = reset_state(m, s);
+  if (!rc) {
+    e = hipStreamSynchronize(s);
+    if (e != hipSuccess) rc = fail(TTT_ERR_HIP, hipGetErrorString(e));
+  }
+  if (rc) { delete m; return rc; }
+  *out = m;
+  return TTT_OK;
+}
+
+int ttt_prefill(ttt_model* m, const int32_t* tokens, int64_t T, int32_t chunk, float lr,
+                int32_t steps, float* chunk_losses, void* stream) {
+  if (!m || !tokens || !chunk_losses) return fail(TTT_ERR_ARG, "NULL argument");
+  if (T < 2) return fail(TTT_ERR_ARG, "T must be >= 2");
+  if (chunk < 1 || chunk > m->Cmax) return fail(TTT_ERR_ARG, "chunk must be in [1, max_chunk]");
+  if (steps < 1) return fail(TTT_ERR_ARG, "steps must be >= 1");
+  if (!std::isfinite(lr)) return fail(TTT_ERR_ARG, "lr must be finite");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int rc = reset_state(m, s);
+  if (rc) return rc;
+  m->lr = lr;
+  m->steps = steps;
+  m->chunk = chunk;
+  const int d = m->d;
+  const int64_t blk = std::max<int64_t>(chunk, (m->MA / chunk) * (int64_t)chunk);
+  int64_t k = 0;
+  for (int64_t B0 = 0; B0 < T; B0 += blk) {
+    const int nb = (int)std::min<int64_t>(blk, T - B0);
+    rc = phase_a(m, tokens, B0, nb, s);
+    if (rc) return rc;
+    for (int64_t c0 = B0; c0 < B0 + nb; c0 += chunk, ++k) {
+      const int n = (int)std::min<int64_t>(chunk, T - c0);
+      const int n_tgt = (int)std::min<int64_t>(n, T - 1 - c0);
+      for (int st = 0; st < steps; ++st) {
+        rc = chunk_step(m, c0, n, m->hA + (c0 - B0) * (int64_t)d, tokens + c0 + 1, n_tgt, lr,
+                        chunk_losses + k * steps + st, s);
+        if (rc) return rc;
+      }
+      if (c0 + n == T) {
+        // first decode token: argmax of the last position's logits from this
+        // chunk's last read
+        const char* frow = static_cast<const char*>(m->fN) + (size_t)(n - 1) * d * m->es;
+        gemv(m->U, m->V, d, frow, !m->bf, m->logits, nullptr, m->bf, s);
+        argmax_tok(m->logits, m->V, m->cur_tok, nullptr, s);
+      }
+    }
+  }
+  rc = sync_and_check(m, s);
+  if (rc) return rc;
+  m->pos = T;
+  m->dchunk0 = T;
+  m->prefilled = true;
+  return TTT_OK;
+}
+
+int ttt_fast_weight(ttt_model* m, int32_t fast_idx, int32_t mat, float* dst, int64_t n,
+                    void* stream) {
+  if (!m || !dst) return fail(TTT_ERR_ARG, "NULL argument");
+  if (fast_idx < 0 || fast_idx >= m->q) return fail(TTT_ERR_ARG, "fast_idx out of range");
+  const bool sw = m->c.mlp == TTT_MLP_SWIGLU;
+  const int nmat = sw ? 3 : 2;
+  if (mat < 0 || mat >= nmat) return fail(TTT_ERR_ARG, "mat out of range");
+  const int d = m->d, F = m->F;
+  if (n != (int64_t)d * F) return fail(TTT_ERR_ARG, "n must equal d_model * d_ff");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  FastLayer& f = m->fast[fast_idx];
+  if (mat == nmat - 1) export_weight(f.m_dn, d, F, 0, 0, dst, s);          // [F][d] canonical
+  else export_weight(f.m_up, F, d, sw ? 1 : 0, mat, dst, s);               // [d][F] canonical
+  return TTT_OK;
+}
+
+int ttt_decode_step(ttt_model* m, int32_t* next_token, float* logits_out, float* update_loss,
+                    void* stream) {
+  if (!m || !next_token) return fail(TTT_ERR_ARG, "NULL argument");
+  if (!m->prefilled) return fail(TTT_ERR_STATE, "decode needs a prefill first");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int d = m->d, F = m->F, F2 = m->F2, V = m->V;
+  const bool bf = m->bf;
+  const float eps = m->c.ln_eps;
+  const int64_t p = m->pos;
+  const int64_t ci = p - m->dchunk0;   // index within the decode chunk
+  HIPCHK(hipMemcpyAsync(next_token, m->cur_tok, 4, hipMemcpyDeviceToDevice, s));
+  HIPCHK(hipMemcpyAsync(m->hist + ci, m->cur_tok, 4, hipMemcpyDeviceToDevice, s));
+  embed(m->cur_tok, 1, m->E, d, V, bf, m->xd, m->err, s);
+  for (int l = 0; l < m->L; ++l) {
+    Layer& ly = m->layers[l];
+    const int j = l - m->f0;
+    layernorm_fwd(m->xd, d, 1, d, eps, m->ad, d, nullptr, nullptr, bf, s);
+    gemv(ly.wqkv, 3 * d, d, m->ad, !bf, m->qkvd, nullptr, bf, s);
+    rope_qkv_f32in(m->qkvd, m->H, m->hd, p, m->theta, m->qd, ly.kring, ly.vring, ly.cap, bf, s);
+    swa_decode(m->qd, ly.kring, ly.vring, ly.cap, m->H, m->hd, m->W, p, m->od, m->attn_ws, bf, s);
+    gemv(ly.wo, d, d, m->od, !bf, m->xd, m->xd, bf, s);
+    if (j == 0)   // phase-B input of this position, for the decode-chunk update
+      HIPCHK(hipMemcpyAsync(m->hA + ci * d, m->xd, (size_t)d * 4, hipMemcpyDeviceToDevice, s));
+    layernorm_fwd(m->xd, d, 1, d, eps, m->ad, d, nullptr, nullptr, bf, s);
+    const void* wup = j >= 0 ? m->fast[j].s_up : ly.wup;
+    const void* wdn = j >= 0 ? m->fast[j].s_dn : ly.wdn;
+    gemv(wup, F2, d, m->ad, !bf, m->zd, nullptr, bf, s);
+    if (m->c.mlp == TTT_MLP_SWIGLU) swiglu_vec(m->zd, F, m->actd, bf, s);
+    else gelu_vec(m->zd, F, m->actd, bf, s);
+    gemv(wdn, d, F, m->actd, !bf, m->xd, m->xd, bf, s);
+  }
+  layernorm_fwd(m->xd, d, 1, d, eps, m->ad, d, nullptr, nullptr, bf, s);
+  gemv(m->U, V, d, m->ad, !bf, m->logits, nullptr, bf, s);
+  argmax_tok(m->logits, V, m->cur_tok, m->hist + ci + 1, s);
+  if (logits_out) HIPCHK(hipMemcpyAsync(logits_out, m->logits, (size_t)V * 4, hipMemcpyDeviceToDevice, s));
+  m->pos = p + 1;
+  bool updated = false;
+  if (m->pos - m->dchunk0 == m->chunk) {
+    const int n = m->chunk;
+    for (int st = 0; st < m->steps; ++st) {
+      int rc = chunk_step(m, m->dchunk0, n, m->hA, m->hist + 1, n, m->lr,
+                          update_loss ? update_loss : m->dtmp, s);
+      if (rc) return rc;
+    }
+    m->dchunk0 = m->pos;
+    updated = true;
+  }
+  if (update_loss && !updated) HIPCHK(hipMemcpyAsync(update_loss, m->nanv, 4, hipMemcpyDeviceToDevice, s));
+  return TTT_OK;
+}
+
+int ttt_reset(ttt_model* m, void* stream) {
+  if (!m) return fail(TTT_ERR_ARG, "NULL model");
+  return reset_state(m, static_cast<hipStream_t>(stream));
+}
+
+void ttt_model_free(ttt_model* m) {
+  if (!m) return;
+  for (auto& t : m->tm)
+    for (auto e : t.ev) hipEventDestroy(e);
+  delete m;
+}
+
+const char* ttt_status_str(int st) {
+  switch (st) {
+    case TTT_OK: return "ok";
+    case TTT_ERR_ARG: return "invalid argument";
+    case TTT_ERR_CONFIG: return "unsupported configuration";
+    case TTT_ERR_HIP: return "HIP runtime error";
+    case TTT_ERR_TOKEN: return "token id out of range";
+    case TTT_ERR_NONFINITE: return "non-finite loss";
+    case TTT_ERR_STATE: return "call out of order";
+    case TTT_ERR_WORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+const char* ttt_last_error(void) { return g_err.c_str(); }
+
+int ttt_timing_enable(ttt_model* m, int32_t cls, int32_t on) {
+  if (!m || cls < 0 || cls >= NCLS - 1) return fail(TTT_ERR_ARG, "bad timing class");
+  Timing& t = m->tm[cls];
+  t.on = on != 0;
+  t.used = 0;
+  t.launches = 0;
+  t.flops = 0;
+  return TTT_OK;
+}
+
+int ttt_timing_read(ttt_model* m, int32_t cls, double* total_ms, int64_t* launches, double* flops) {
+  if (!m || cls < 0 || cls >= NCLS - 1 || !total_ms) return fail(TTT_ERR_ARG, "bad timing read");
+  Timing& t = m->tm[cls];
+  double tot = 0;
+  for (size_t i = 0; i + 1 < t.used; i += 2) {
+    HIPCHK(hipEventSynchronize(t.ev[i + 1]));
+    float ms = 0.f;
+    HIPCHK(hipEventElapsedTime(&ms, t.ev[i], t.ev[i + 1]));
+    tot += ms;
+  }
+  *total_ms = tot;
+  if (launches) *launches = t.launches;
+  if (flops) *flops = t.flops;
+  return TTT_OK;
+}
+
+int ttt_diag_gemm(int32_t dtype, int32_t a_kc, int32_t b_kc, int32_t M, int32_t N, int32_t K,
+                  const void* A, int64_t lda, const void* B, int64_t ldb, float* C, int64_t ldc,
+                  void* stream) {
+  if (!A || !B || !C || M < 0 || N < 0 || K < 0) return fail(TTT_ERR_ARG, "bad GEMM arguments");
+  if (dtype != TTT_BF16 && dtype != TTT_FP32) return fail(TTT_ERR_ARG, "bad dtype");
+  const int vec = dtype == TTT_BF16 ? 8 : 4;
+  if (lda % vec || ldb % vec || (!a_kc && M % vec) || (!b_kc && N % vec) || ((a_kc || b_kc) && K % vec))
+    return fail(TTT_ERR_ARG, "strides / vector dims must be multiples of 16 bytes");
+  GemmParams p;
+  p.A = A; p.lda = lda; p.B = B; p.ldb = ldb; p.M = M; p.N = N; p.K = K; p.C = C; p.ldc = ldc;
+  int epi = EPI_STORE;
+  if (!a_kc && !b_kc) { epi = EPI_SGD; p.alpha = -1.f; }
+  else if (!a_kc) return fail(TTT_ERR_ARG, "layout (0,1) is not used by the inner loop");
+  if (gemm(p, dtype == TTT_BF16, a_kc != 0, b_kc != 0, epi, true, static_cast<hipStream_t>(stream)))
+    return fail(TTT_ERR_ARG, "GEMM variant not built");
+  return TTT_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,250 @@
+"""Parity of the HIP path (through the C ABI) with the float64 oracle.
+
+Every test runs the library's kernels on the GPU and the oracle on the CPU
+on the same seeded inputs.  Relative errors (the checks of the inner loop):
+  losses:        max_k |l_k - l*_k| / |l*_k|
+  fast weights:  ||W - W*||_F / ||W*||_F for every fast matrix
+Bars: 1e-4 in the float32 check mode, 2e-2 with bf16 storage.  Also
+asserted, looser, as diagnostics that are not dominated by W0 and ln V:
+  dW:    ||(W - W0) - (W* - W0)|| / ||W* - W0||
+  dloss: the loss change caused by the updates, (l(lr) - l(0)) vs oracle.
+"""
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import ttt_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+BAR = {"fp32": 1e-4, "bf16": 2e-2}
+
+
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import long_context_lm_chunk_amd as T
+    return T
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def rel(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def small_cfg(**kw):
+    base = dict(name="small", n_layers=3, d_model=64, n_heads=2, head_dim=32, d_ff=128,
+                vocab=256, window=48, n_fast=2, mlp="swiglu", dtype="fp32", T=200, chunk=32,
+                lr=0.05, steps=1, seg=16, period=64, dmin=50, dmax=None, token_seed=11,
+                weight_seed=111)
+    base.update(kw)
+    return synth.config(base)
+
+
+def run_pair(cfg, dtype=None, std=0.02, T=None, chunk=None, lr=None, steps=1, prefill_block=0,
+             lr0_too=True):
+    """GPU prefill and oracle prefill on the same inputs; returns errors."""
+    T_ = _gpu()
+    dtype = dtype or cfg["dtype"]
+    T = T or cfg["T"]
+    chunk = chunk or cfg["chunk"]
+    lr = cfg["lr"] if lr is None else lr
+    say(f"case {cfg['name']} dtype={dtype} T={T} chunk={chunk} lr={lr} steps={steps} "
+        f"L={cfg['n_layers']} d={cfg['d_model']} hd={cfg['head_dim']} q={cfg['n_fast']} {cfg['mlp']}")
+    w = synth.gen_weights(cfg, std=std, device="cpu")
+    if dtype == "fp32":
+        w = [t.float() for t in w]
+    x = synth.gen_tokens(cfg, T=T)
+    m = T_.Model(cfg, [t.cuda() for t in w], dtype=dtype, max_chunk=chunk, prefill_block=prefill_block)
+    tok = torch.from_numpy(x).cuda()
+    losses = m.prefill(tok, chunk, lr, steps).cpu().numpy()
+    fw = [t.cpu().numpy() for t in m.fast_weights()]
+    ref = O.prefill(cfg, w, x, chunk, lr, steps)
+    rfw = O.fast_weights_canonical(ref)
+    model0 = O.OracleModel(cfg, w)
+    w0 = [a for f in model0.initial_fast() for a in f.values()]
+    out = dict(
+        loss=float(np.max(np.abs(losses - ref["losses"]) / np.abs(ref["losses"]))),
+        W=max(rel(a, b) for a, b in zip(fw, rfw)),
+        dW=max(rel(a - c, b - c) for a, b, c in zip(fw, rfw, w0)),
+        losses=losses, ref=ref["losses"], model=m, w=w, x=x)
+    if lr0_too:
+        l0 = m.prefill(tok, chunk, 0.0, steps).cpu().numpy()
+        r0 = O.prefill(cfg, w, x, chunk, 0.0, steps)["losses"]
+        dg, dr = losses - l0, ref["losses"] - r0
+        out["dloss"] = float(np.linalg.norm(dg - dr) / max(np.linalg.norm(dr), 1e-300))
+        out["loss0"] = float(np.max(np.abs(l0 - r0) / np.abs(r0)))
+    say(f"  errors: loss {out['loss']:.2e} W {out['W']:.2e} dW {out['dW']:.2e} "
+        f"dloss {out.get('dloss', float('nan')):.2e} loss(lr=0) {out.get('loss0', float('nan')):.2e}")
+    return out
+
+
+# ------------------------------------------------------------- GEMM kernel
+
+@pytest.mark.parametrize("dt", ["fp32", "bf16"])
+@pytest.mark.parametrize("layout", [(1, 1), (1, 0), (0, 0)])
+@pytest.mark.parametrize("shape", [(200, 256, 96), (128, 128, 64), (64, 384, 1000), (1, 16, 8)])
+def test_gemm_kernel_matches_torch(dt, layout, shape):
+    """The matrix-core GEMM (every operand layout the inner loop uses,
+    ragged M/K tails) against a float64 product of the same values."""
+    T = _gpu()
+    M, N, K = shape
+    a_kc, b_kc = layout
+    if not a_kc and M % 8:
+        M = 8 * ((M + 7) // 8)
+    if (a_kc or b_kc) and K % 8:
+        K = 8 * ((K + 7) // 8)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    say(f"case gemm {dt} layout={layout} M={M} N={N} K={K}")
+    g = torch.Generator().manual_seed(M * 7 + N * 3 + K)
+    A = torch.randn(M, K, generator=g).to(tdt)
+    B = torch.randn(N, K, generator=g).to(tdt)
+    ref = (A.double() @ B.double().T)
+    Ad = (A if a_kc else A.T).contiguous().cuda()
+    Bd = (B if b_kc else B.T).contiguous().cuda()
+    C = T.diag_gemm(Ad, Bd, M, N, K, bool(a_kc), bool(b_kc))
+    torch.cuda.synchronize()
+    err = (C.double().cpu() - ref).abs().max().item() / max(ref.abs().max().item(), 1e-30)
+    assert err < 1e-5, err
+
+
+# ------------------------------------------------------- whole inner loop
+
+def test_prefill_tiny_fp32_workload():
+    """The tiny fp32 workload (2 layers, d 64, hd 16, GELU, window 32, chunk
+    16, T 256, lr 0.01): losses and fast weights within 1e-4."""
+    r = run_pair(synth.config("c1"))
+    assert r["loss"] < BAR["fp32"] and r["W"] < BAR["fp32"]
+    assert r["dW"] < 1e-2 and r["dloss"] < 1e-2 and r["loss0"] < BAR["fp32"]
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("mlp,hd,q", [("swiglu", 32, 2), ("gelu", 64, 3), ("swiglu", 16, 3),
+                                      ("gelu", 96, 2), ("swiglu", 128, 2)])
+def test_prefill_small_models(dtype, mlp, hd, q):
+    """Several fast blocks (attention backward through the window, cached
+    keys held constant), every head size, both MLPs, a ragged last chunk
+    (T = 200 with chunk 32) and several phase-A blocks (block 64)."""
+    H = 2 if hd <= 64 else 1
+    cfg = small_cfg(mlp=mlp, head_dim=hd, n_heads=H, d_model=H * hd, n_fast=q,
+                    n_layers=max(3, q + 1))
+    r = run_pair(cfg, dtype=dtype, std=0.05, prefill_block=64)
+    assert r["loss"] < BAR[dtype] and r["W"] < BAR[dtype]
+    assert r["loss0"] < BAR[dtype]
+    assert r["dW"] < (1e-2 if dtype == "fp32" else 0.1)
+    assert r["dloss"] < (1e-2 if dtype == "fp32" else 0.2)
+
+
+def test_prefill_two_steps_per_chunk_fp32():
+    r = run_pair(small_cfg(n_fast=2), steps=2, std=0.05)
+    assert r["loss"] < 1e-4 and r["W"] < 1e-4
+
+
+def test_window_larger_than_context_and_window_one():
+    for W in (1, 1000):
+        r = run_pair(small_cfg(window=W, T=96), std=0.05)
+        assert r["loss"] < 1e-4 and r["W"] < 1e-4
+
+
+def test_chunk_of_one_and_chunk_covering_context():
+    for C in (1, 97):
+        r = run_pair(small_cfg(T=97), chunk=C, std=0.05, lr0_too=False)
+        assert r["loss"] < 1e-4 and r["W"] < 1e-4
+
+
+def test_prefill_125m_shape_prefix_bf16():
+    """The 125M-shape workload (12 layers, d 768, 12 heads of 64, GELU 3072,
+    vocab 32000, window 1024, 3 fast blocks, chunk 256, lr 1e-3) on the first
+    1280 tokens: 5 chunks, the window fills, a ragged vocabulary tile."""
+    r = run_pair(synth.config("c2"), T=1280)
+    assert r["loss"] < BAR["bf16"] and r["W"] < BAR["bf16"]
+    assert r["dW"] < 0.1
+
+
+def test_prefill_125m_shape_prefix_fp32_check_mode():
+    r = run_pair(synth.config("c2"), dtype="fp32", T=768)
+    assert r["loss"] < BAR["fp32"] and r["W"] < BAR["fp32"]
+
+
+def test_decode_teacher_forced_matches_oracle():
+    """Prefill, then greedy decode through two decode-chunk updates; the
+    oracle replays the emitted tokens (teacher forcing) and must give the
+    same logits and update losses; the argmax must agree wherever the
+    oracle's top-2 gap is clear."""
+    T_ = _gpu()
+    cfg = small_cfg(T=64, chunk=16, n_fast=2, window=24)
+    say("case decode small fp32")
+    w = [t.float() for t in synth.gen_weights(cfg, std=0.3)]
+    x = synth.gen_tokens(cfg, T=64)
+    m = T_.Model(cfg, [t.cuda() for t in w], max_chunk=16)
+    m.prefill(torch.from_numpy(x).cuda(), 16, 0.05)
+    toks, logits, upd = [], [], []
+    for i in range(40):
+        t, lg, ul = m.decode_step(want_logits=True)
+        toks.append(int(t.item()))
+        logits.append(lg.cpu().numpy())
+        upd.append(float(ul.item()))
+    st = O.prefill(cfg, w, x, 16, 0.05, return_state=True)
+    first = int(np.argmax(st["last_logits"]))
+    assert toks[0] == first
+    d = O.decode(st, 40, forced=np.array(toks + [int(np.argmax(logits[-1]))]))
+    L = np.array(logits)
+    err = np.abs(L - d["logits"]).max() / np.abs(d["logits"]).max()
+    say(f"  decode logits err {err:.2e}")
+    assert err < 1e-4
+    for i in range(39):
+        srt = np.sort(d["logits"][i])
+        if srt[-1] - srt[-2] > 1e-3:
+            assert toks[i + 1] == int(np.argmax(d["logits"][i]))
+    got = [u for u in upd if not math.isnan(u)]
+    assert len(got) == 2 and len(d["update_losses"]) == 2
+    np.testing.assert_allclose(got, d["update_losses"], rtol=1e-4)
+
+
+def test_prefill_is_deterministic():
+    T_ = _gpu()
+    cfg = small_cfg(dtype="bf16")
+    say("case determinism")
+    w = [t.cuda() for t in synth.gen_weights(cfg, std=0.05)]
+    x = torch.from_numpy(synth.gen_tokens(cfg)).cuda()
+    m = T_.Model(cfg, w, max_chunk=32)
+    a = m.prefill(x, 32, 0.05).cpu()
+    fa = [t.cpu() for t in m.fast_weights()]
+    b = m.prefill(x, 32, 0.05).cpu()
+    fb = [t.cpu() for t in m.fast_weights()]
+    assert torch.equal(a, b)
+    assert all(torch.equal(p, q) for p, q in zip(fa, fb))
+
+
+def test_device_detected_errors():
+    T_ = _gpu()
+    cfg = small_cfg()
+    say("case errors")
+    w = [t.float().cuda() for t in synth.gen_weights(cfg)]
+    m = T_.Model(cfg, w, max_chunk=32)
+    bad = torch.from_numpy(synth.gen_tokens(cfg)).cuda()
+    bad[17] = cfg["vocab"] + 5
+    with pytest.raises(T_.TTTError) as e:
+        m.prefill(bad, 32, 0.05)
+    assert e.value.status == -4
+    ok = torch.from_numpy(synth.gen_tokens(cfg)).cuda()
+    with pytest.raises(T_.TTTError) as e:
+        m.prefill(ok, 32, 1e30)
+    assert e.value.status == -5
+    with pytest.raises(T_.TTTError) as e:
+        m.prefill(ok, 64, 0.05)        # chunk > max_chunk
+    assert e.value.status == -1
+    # the model is still usable afterwards
+    r = m.prefill(ok, 32, 0.05)
+    assert torch.isfinite(r).all()
