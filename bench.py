@@ -1,0 +1,196 @@
+"""Benchmark of the TTT-E2E inner loop on one MI355X.
+
+One step = one whole prefill of the 3B-shape workload: 28 layers, d 3072,
+24 heads of 128, SwiGLU 8192, vocab 32000, window 8192, T = 131072 tokens in
+chunks of 1024, the MLPs of the last 7 blocks updated by SGD (lr 1e-4) after
+every chunk.  Inputs are synthetic (Zipf(1.1) tokens with planted repeats
+16K-64K apart, N(0, 0.02) weights rounded to bf16) and resident in HBM
+before the timed region.
+
+Prints one JSON line: prefill context tokens/s (value), decode ms/token
+after the prefill, the MFMA utilisation of the whole prefill against the
+bf16 dense peak, the roofline of the dominant kernel (HIP events around its
+launches inside the timed region) and the float64 oracle's rate on the host
+cores for a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0
+
+
+def prefill_flops(cfg, T):
+    """Algorithmic FLOPs of one prefill (forward of every layer, head,
+    backward of the fast blocks; recomputation not counted)."""
+    L, d, F, V, W, C, q = (cfg[k] for k in ("n_layers", "d_model", "d_ff", "vocab", "window",
+                                            "chunk", "n_fast"))
+    k = 3 if cfg["mlp"] == "swiglu" else 2
+    sum_n = sum(min(t + 1, W) for t in range(T))
+    sum_m = 0
+    for c0 in range(0, T, C):
+        n = min(C, T - c0)
+        sum_m += sum(min(u + 1, W) for u in range(n))
+    fwd = 2 * (T * L * (4 * d * d + k * d * F) + L * d * 2 * sum_n + (T - 1) * d * V)
+    bwd = 2 * ((T - 1) * d * V + T * (k + 1) * d * F + (q - 1) * T * (2 * k * d * F + 4 * d * d)
+               + (q - 1) * d * (2 * sum_n + 2 * sum_m))
+    return float(fwd + bwd)
+
+
+def cpu_baseline(cfg, weights_gpu, tokens_np, sample_tokens=256):
+    """The float64 oracle on the host cores: the first `sample_tokens` tokens
+    of the workload read as one chunk (forward through every layer, CE,
+    backward through the fast blocks, SGD)."""
+    import numpy as np
+    import torch
+    from oracle import ttt_oracle as O
+    w = [t.cpu() for t in weights_gpu]
+    model = O.OracleModel(cfg, w)
+    del w
+    threads = torch.get_num_threads()
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max([i.get("num_threads", 0) for i in info] + [1])
+    except Exception:
+        pass
+    x = tokens_np[:sample_tokens + 1]
+    t0 = time.perf_counter()
+    O.prefill(cfg, None, x[:sample_tokens], sample_tokens, cfg["lr"], model=model)
+    dt = time.perf_counter() - t0
+    return {"value": sample_tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {sample_tokens} tokens of the workload as one chunk "
+                      f"({dt:.1f} s; attention windows <= {sample_tokens} keys, so this overstates "
+                      f"the oracle's steady-state rate)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--config", default="c4")
+    ap.add_argument("--T", type=int, default=None)
+    ap.add_argument("--decode-tokens", type=int, default=64)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=256)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); the inner loop of one "
+              "context is sequential over chunks and this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import synth
+    import long_context_lm_chunk_amd as T_
+
+    cfg = synth.config(args.config)
+    T = args.T or cfg["T"]
+    dev = torch.device("cuda:0")
+    t_setup = time.perf_counter()
+    weights = synth.gen_weights(cfg, device=dev)
+    tokens_np = synth.gen_tokens(cfg, T=T)
+    tokens = torch.from_numpy(tokens_np).to(dev)
+    model = T_.Model(cfg, weights, max_chunk=cfg["chunk"])
+    torch.cuda.synchronize()
+    print(f"# setup {time.perf_counter() - t_setup:.1f}s, workspace "
+          f"{model.workspace.numel() / 1e9:.2f} GB", file=sys.stderr, flush=True)
+
+    losses = None
+    for i in range(args.warmup):
+        losses = model.prefill(tokens, cfg["chunk"], cfg["lr"])
+        torch.cuda.synchronize()
+        print(f"# warmup {i} done", file=sys.stderr, flush=True)
+
+    # dominant kernel (the MLP up-projection GEMM of the frozen blocks) and
+    # the other classes timed with HIP events on the library's stream
+    classes = {0: "gemm_all", 1: "attn_fwd", 2: "attn_bwd", 3: "head_ce", 4: "dw_sgd", 5: "mlp_up"}
+    for c in classes:
+        model.timing_enable(c, True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        losses = model.prefill(tokens, cfg["chunk"], cfg["lr"])
+        print(f"# step {i} done", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ktime = {}
+    for c, name in classes.items():
+        ms, n, fl = model.timing_read(c)
+        ktime[name] = dict(ms=ms / args.steps, launches=n // args.steps, flops=fl / args.steps)
+        model.timing_enable(c, False)
+    ms_per_step = dt * 1000.0 / args.steps
+    tok_s = T / (dt / args.steps)
+    fl = prefill_flops(dict(cfg, T=T), T)
+    mfma_pct = 100.0 * fl / (dt / args.steps) / (PEAK_BF16_TFLOPS * 1e12)
+    print("# kernel classes per step: " + ", ".join(
+        f"{k} {v['ms']:.1f} ms/{v['launches']} launches/"
+        f"{(v['flops'] / max(v['ms'], 1e-9) / 1e9) if v['flops'] else 0:.0f} TF/s"
+        for k, v in ktime.items()), file=sys.stderr, flush=True)
+    lh = losses.cpu().numpy()
+    assert np.all(np.isfinite(lh)), "non-finite chunk loss"
+
+    # decode after the prefill (constant per-token cost once T >= window)
+    dec_ms = None
+    if args.decode_tokens > 0:
+        for _ in range(4):
+            model.decode_step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.decode_tokens):
+            model.decode_step()
+        e1.record()
+        torch.cuda.synchronize()
+        dec_ms = e0.elapsed_time(e1) / args.decode_tokens
+
+    up = ktime["mlp_up"]
+    roof = None
+    if up["launches"]:
+        avg_ms = up["ms"] / up["launches"]
+        ach = up["flops"] / up["launches"] / (avg_ms / 1e3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "kernel": "gemm_kernel<bf16, A k-contig, B k-contig, SWIGLU, bf16, single B> "
+                          "(frozen-block MLP up-projection, M=8192 N=16384 K=3072)",
+                "avg_launch_ms": round(avg_ms, 4), "launches_per_step": up["launches"]}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("# cpu baseline (oracle) ...", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(cfg, weights, tokens_np, args.cpu_sample)
+
+    out = {
+        "metric": "TTT-E2E prefill context tokens/s at 3B/128K (decode ms/token and MFMA util % alongside)",
+        "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 2), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (Zipf(1.1) tokens with planted repeats; N(0,0.02) weights, bf16)",
+        "config": {"workload": f"ttt-e2e prefill, {cfg['name']}", "T": T, "chunk": cfg["chunk"],
+                   "window": cfg["window"], "layers": cfg["n_layers"], "d_model": cfg["d_model"],
+                   "heads": cfg["n_heads"], "d_ff": cfg["d_ff"], "vocab": cfg["vocab"],
+                   "fast_layers": cfg["n_fast"], "lr": cfg["lr"], "steps_per_chunk": 1,
+                   "parallelism": "single GPU"},
+        "decode_ms_per_token": None if dec_ms is None else round(dec_ms, 3),
+        "mfma_util_pct": round(mfma_pct, 2),
+        "algorithmic_tflop_per_step": round(fl / 1e12, 1),
+        "kernel_classes_ms_per_step": {k: round(v["ms"], 2) for k, v in ktime.items()},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "mean_chunk_loss": float(lh.mean()),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -12,9 +12,9 @@ namespace {
 // y[n] = sum_k W[n][k] x[k] (+ resid[n]); W [N][K] k-contiguous.
 // One wave per output row, 16-byte loads along k.
 template <typename T, typename X>
-__global__ __launch_bounds__(256) void gemv_k(const T* __restrict__ W, int N, int K,
-                                              const X* __restrict__ x, float* __restrict__ y,
-                                              const float* __restrict__ resid) {
+__global__ __launch_bounds__(256) void gemv_k(const T* __restrict__ W, const T* __restrict__ W2,
+                                              int N, int K, const X* __restrict__ x,
+                                              float* __restrict__ y, const float* __restrict__ resid) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= N) return;
@@ -25,6 +25,14 @@ __global__ __launch_bounds__(256) void gemv_k(const T* __restrict__ W, int N, in
     const U128 wv = ld128(w + k);
 #pragma unroll
     for (int e = 0; e < V; ++e) s += to_f32(elem<T>(wv, e)) * to_f32(x[k + e]);
+  }
+  if (W2) {   // fast weights: W0 + delta, summed in fp32
+    const T* w2 = W2 + (int64_t)row * K;
+    for (int k = lane * V; k < K; k += 64 * V) {
+      const U128 wv = ld128(w2 + k);
+#pragma unroll
+      for (int e = 0; e < V; ++e) s += to_f32(elem<T>(wv, e)) * to_f32(x[k + e]);
+    }
   }
   s = wave_sum(s);
   if (lane == 0) y[row] = s + (resid ? resid[row] : 0.f);
@@ -167,14 +175,14 @@ __global__ void argmax_k(const float* __restrict__ z, int V, int32_t* __restrict
 
 }  // namespace
 
-void gemv(const void* W, int N, int K, const void* x, bool x_f32, float* y, const float* resid,
-          bool bf, hipStream_t s) {
+void gemv(const void* W, const void* W2, int N, int K, const void* x, bool x_f32, float* y,
+          const float* resid, bool bf, hipStream_t s) {
   dim3 grid((N + 3) / 4);
   if (bf) {
-    if (x_f32) hipLaunchKernelGGL((gemv_k<bf16, float>), grid, dim3(256), 0, s, (const bf16*)W, N, K, (const float*)x, y, resid);
-    else hipLaunchKernelGGL((gemv_k<bf16, bf16>), grid, dim3(256), 0, s, (const bf16*)W, N, K, (const bf16*)x, y, resid);
+    if (x_f32) hipLaunchKernelGGL((gemv_k<bf16, float>), grid, dim3(256), 0, s, (const bf16*)W, (const bf16*)W2, N, K, (const float*)x, y, resid);
+    else hipLaunchKernelGGL((gemv_k<bf16, bf16>), grid, dim3(256), 0, s, (const bf16*)W, (const bf16*)W2, N, K, (const bf16*)x, y, resid);
   } else {
-    hipLaunchKernelGGL((gemv_k<float, float>), grid, dim3(256), 0, s, (const float*)W, N, K, (const float*)x, y, resid);
+    hipLaunchKernelGGL((gemv_k<float, float>), grid, dim3(256), 0, s, (const float*)W, (const float*)W2, N, K, (const float*)x, y, resid);
   }
 }
 

@@ -233,10 +233,11 @@ __global__ void convert_k(const T* __restrict__ src, int rows, int cols, int tra
   }
 }
 
-// Internal fp32 master [out][in] (optionally interleaved, taking half
-// `which`) -> canonical fp32 [in][out].
-__global__ void export_k(const float* __restrict__ m, int out_dim, int in_dim, int ilv, int which,
-                         float* __restrict__ dst) {
+// Internal [out][in] W0 (optionally interleaved, taking half `which`) plus
+// the fp32 delta -> canonical fp32 [in][out].
+template <typename T>
+__global__ void export_k(const T* __restrict__ w0, const float* __restrict__ dm, int out_dim,
+                         int in_dim, int ilv, int which, float* __restrict__ dst) {
   const int64_t total = (int64_t)out_dim * in_dim;
   const int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (idx >= total) return;
@@ -244,7 +245,7 @@ __global__ void export_k(const float* __restrict__ m, int out_dim, int in_dim, i
   const int j = idx / out_dim;          // input row
   int64_t r = f;
   if (ilv) r = (int64_t)(f / 16) * 32 + which * 16 + (f % 16);
-  dst[idx] = m[r * in_dim + j];
+  dst[idx] = to_f32(w0[r * in_dim + j]) + dm[r * in_dim + j];
 }
 
 // One wave per row: combine the per-part (max, sumexp) into the row LSE and
@@ -389,10 +390,11 @@ void convert_weight(const void* src, int rows, int cols, bool transpose, int ilv
        hipLaunchKernelGGL(convert_k<float>, grid, dim3(256), 0, s, (const float*)src, rows, cols, (int)transpose, ilv, (float*)dst));
 }
 
-void export_weight(const float* master, int out_dim, int in_dim, int ilv, int which, float* dst,
-                   hipStream_t s) {
+void export_weight(const void* w0, const float* delta, int out_dim, int in_dim, int ilv, int which,
+                   float* dst, bool bf, hipStream_t s) {
   const int64_t total = (int64_t)out_dim * in_dim;
-  hipLaunchKernelGGL(export_k, dim3(nblk(total, 256)), dim3(256), 0, s, master, out_dim, in_dim, ilv, which, dst);
+  TSEL(bf, hipLaunchKernelGGL(export_k<bf16>, dim3(nblk(total, 256)), dim3(256), 0, s, (const bf16*)w0, delta, out_dim, in_dim, ilv, which, dst),
+       hipLaunchKernelGGL(export_k<float>, dim3(nblk(total, 256)), dim3(256), 0, s, (const float*)w0, delta, out_dim, in_dim, ilv, which, dst));
 }
 
 void ce_finish(const float* part_max, const float* part_sum, int nparts, int64_t ldpart,

@@ -111,7 +111,7 @@ template <typename T, bool KC, int ROWS> struct TileLoader {
 DEVI float gelu_erf(float z) { return 0.5f * z * (1.f + erff(z * 0.70710678118654752f)); }
 DEVI float silu(float z) { return z / (1.f + __expf(-z)); }
 
-template <typename T, bool A_KC, bool B_KC, int EPI, typename TO>
+template <typename T, bool A_KC, bool B_KC, int EPI, typename TO, bool DUAL>
 __global__ __launch_bounds__(NT) void gemm_kernel(GemmParams p) {
   using C = GemmCfg<T>;
   __shared__ __attribute__((aligned(16))) T lds[2][(BM + BN) * C::LS];
@@ -132,7 +132,11 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = (p.K + C::BK - 1) / C::BK;
+  // With DUAL the reduction runs twice over K, against B then B2: the fast
+  // weights are applied as W0 + delta without rounding their sum.
+  const int nk1 = (p.K + C::BK - 1) / C::BK;
+  const int nk = DUAL ? 2 * nk1 : nk1;
+  const T* __restrict__ B2 = static_cast<const T*>(p.B2);
   la.load(A, p.lda, m0, p.M, 0, p.K, tid);
   lb.load(B, p.ldb, n0, p.N, 0, p.K, tid);
   la.store(lds[0], tid);
@@ -142,8 +146,11 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmParams p) {
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
     if (kt + 1 < nk) {
-      la.load(A, p.lda, m0, p.M, (kt + 1) * C::BK, p.K, tid);
-      lb.load(B, p.ldb, n0, p.N, (kt + 1) * C::BK, p.K, tid);
+      const int nt = kt + 1;
+      const bool second = DUAL && nt >= nk1;
+      const int k0 = (second ? nt - nk1 : nt) * C::BK;
+      la.load(A, p.lda, m0, p.M, k0, p.K, tid);
+      lb.load(second ? B2 : B, p.ldb, n0, p.N, k0, p.K, tid);
     }
     const T* As = lds[cur];
     const T* Bs = lds[cur] + BM * C::LS;
@@ -270,7 +277,8 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmParams p) {
 template <typename T, bool AK, bool BK_, int EPI, typename TO>
 void launch_t(const GemmParams& p, hipStream_t s) {
   dim3 grid((p.N + BN - 1) / BN, (p.M + BM - 1) / BM);
-  hipLaunchKernelGGL((gemm_kernel<T, AK, BK_, EPI, TO>), grid, dim3(NT), 0, s, p);
+  if (p.B2) hipLaunchKernelGGL((gemm_kernel<T, AK, BK_, EPI, TO, true>), grid, dim3(NT), 0, s, p);
+  else hipLaunchKernelGGL((gemm_kernel<T, AK, BK_, EPI, TO, false>), grid, dim3(NT), 0, s, p);
 }
 
 template <typename T>
@@ -297,7 +305,7 @@ int dispatch(const GemmParams& p, bool a_kc, bool b_kc, int epi, bool out_f32, h
     return 0;
   }
   if (!a_kc && !b_kc) {
-    if (epi != EPI_SGD) return -1;
+    if (epi != EPI_SGD || p.B2) return -1;
     launch_t<T, false, false, EPI_SGD, T>(p, s);
     return 0;
   }

@@ -10,6 +10,7 @@ enum Epi { EPI_STORE = 0, EPI_RESID, EPI_GELU, EPI_SWIGLU, EPI_SGD, EPI_CESTAT, 
 struct GemmParams {
   const void* A = nullptr; int64_t lda = 0;  // k-contiguous [M][K] or m-contiguous [K][M]
   const void* B = nullptr; int64_t ldb = 0;  // k-contiguous [N][K] or n-contiguous [K][N]
+  const void* B2 = nullptr;                  // optional second B (same layout): C = A.(B + B2)
   int M = 0, N = 0, K = 0;
   void* C = nullptr; int64_t ldc = 0;        // primary output
   const float* R = nullptr; int64_t ldr = 0; // residual input (RESID)
@@ -43,8 +44,9 @@ void act_bwd(const float* dact, const void* z, int n, int F, bool swiglu, void* 
              hipStream_t s);
 void convert_weight(const void* src, int rows, int cols, bool transpose, int interleave16_half,
                     void* dst, bool bf16, hipStream_t s);
-void export_weight(const float* master, int out_dim, int in_dim, int interleave_half, int which,
-                   float* dst, hipStream_t s);
+// dst (canonical [in][out] fp32) = W0 + delta, from the internal [out][in] layout
+void export_weight(const void* w0, const float* delta, int out_dim, int in_dim, int interleave_half,
+                   int which, float* dst, bool bf16, hipStream_t s);
 void widen(const void* src, float* dst, int64_t n, bool bf16, hipStream_t s);
 void copy_cast_from_f32(const float* src, void* dst, int64_t n, bool bf16, hipStream_t s);
 void fill_f32(float* p, int64_t n, float v, hipStream_t s);
@@ -74,8 +76,9 @@ void swa_fwd(const AttnParams& p, bool bf16, hipStream_t s);
 void swa_bwd(const AttnParams& p, bool bf16, hipStream_t s);
 
 // ---- decode (decode.hip)
-void gemv(const void* W, int N, int K, const void* x, bool x_f32, float* y, const float* resid,
-          bool bf16, hipStream_t s);
+// y = (W + W2) x (+ resid); W2 may be null
+void gemv(const void* W, const void* W2, int N, int K, const void* x, bool x_f32, float* y,
+          const float* resid, bool bf16, hipStream_t s);
 void swiglu_vec(const float* z, int F, void* act, bool bf16, hipStream_t s);
 void gelu_vec(const float* z, int F, void* act, bool bf16, hipStream_t s);
 void swa_decode(const void* q, const void* kring, const void* vring, int64_t cap, int H, int hd,

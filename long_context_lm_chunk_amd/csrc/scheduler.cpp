@@ -69,10 +69,16 @@ struct Carver {
   }
 };
 
+// A fast MLP is held as W0 + delta: W0 is the loaded matrix (exact, in the
+// storage type), delta the accumulated SGD updates.  delta's fp32 master takes
+// the updates; its copy in the storage type (the master itself in fp32 mode)
+// feeds the products, which run over W0 and delta in one fp32 accumulation.
+// Updates of lr*g ~ 1e-8 are far below a bf16 ulp of W (~1e-4), so rounding
+// W0 + delta to bf16 would erase them; delta's own ulp scales with delta.
 struct FastLayer {
-  float* m_up = nullptr;  // fp32 master [F2][d]
-  float* m_dn = nullptr;  // fp32 master [d][F]
-  void* s_up = nullptr;   // bf16 shadow (== master in fp32 mode)
+  float* m_up = nullptr;  // fp32 delta master [F2][d]
+  float* m_dn = nullptr;  // fp32 delta master [d][F]
+  void* s_up = nullptr;   // delta in the storage type (== master in fp32 mode)
   void* s_dn = nullptr;
 };
 
@@ -401,11 +407,11 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
     }
     layernorm_fwd(x2, d, n, d, eps, b.b, d, b.mean2, b.rstd2, bf, s);
     GemmParams gu;
-    gu.A = b.b; gu.lda = d; gu.B = m->fast[j].s_up; gu.ldb = d; gu.M = n; gu.N = F2; gu.K = d;
+    gu.A = b.b; gu.lda = d; gu.B = ly.wup; gu.B2 = m->fast[j].s_up; gu.ldb = d; gu.M = n; gu.N = F2; gu.K = d;
     gu.C = b.z; gu.ldc = F2; gu.C2 = b.act; gu.ldc2 = F;
     rc = run_gemm(m, gu, true, true, upepi, false, s); if (rc) return rc;
     GemmParams gd;
-    gd.A = b.act; gd.lda = F; gd.B = m->fast[j].s_dn; gd.ldb = F; gd.M = n; gd.N = d; gd.K = F;
+    gd.A = b.act; gd.lda = F; gd.B = ly.wdn; gd.B2 = m->fast[j].s_dn; gd.ldb = F; gd.M = n; gd.N = d; gd.K = F;
     gd.C = (j + 1 < q) ? m->pb[j + 1].xin : m->xL; gd.ldc = d; gd.R = x2; gd.ldr = d;
     rc = run_gemm(m, gd, true, true, EPI_RESID, true, s); if (rc) return rc;
   }
@@ -446,7 +452,7 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
     const float* x2 = (j > 0) ? b.x2 : x2_0;
     // dact = dh . Wdn  (reads the weights before their update)
     GemmParams ga;
-    ga.A = m->dh_lo; ga.lda = d; ga.B = fw.s_dn; ga.ldb = F; ga.M = n; ga.N = F; ga.K = d;
+    ga.A = m->dh_lo; ga.lda = d; ga.B = ly.wdn; ga.B2 = fw.s_dn; ga.ldb = F; ga.M = n; ga.N = F; ga.K = d;
     ga.C = m->dact; ga.ldc = F;
     rc = run_gemm(m, ga, true, false, EPI_STORE, true, s); if (rc) return rc;
     // Wdn -= lr * dh^T act   ([d][F], reduction over the chunk's tokens)
@@ -457,7 +463,7 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
     act_bwd(m->dact, b.z, n, F, m->c.mlp == TTT_MLP_SWIGLU, m->dz, bf, s);
     if (j > 0) {
       GemmParams gb;   // db = dz . Wup (before its update)
-      gb.A = m->dz; gb.lda = F2; gb.B = fw.s_up; gb.ldb = d; gb.M = n; gb.N = d; gb.K = F2;
+      gb.A = m->dz; gb.lda = F2; gb.B = ly.wup; gb.B2 = fw.s_up; gb.ldb = d; gb.M = n; gb.N = d; gb.K = F2;
       gb.C = m->dtmp; gb.ldc = d;
       rc = run_gemm(m, gb, true, false, EPI_STORE, true, s); if (rc) return rc;
     }
@@ -508,11 +514,12 @@ int reset_state(ttt_model* m, hipStream_t s) {
   for (int j = 0; j < m->q; ++j) {
     Layer& ly = m->layers[m->f0 + j];
     FastLayer& f = m->fast[j];
-    widen(ly.wup, f.m_up, (int64_t)F2 * d, m->bf, s);
-    widen(ly.wdn, f.m_dn, (int64_t)d * F, m->bf, s);
-    if (m->bf) {
-      HIPCHK(hipMemcpyAsync(f.s_up, ly.wup, (size_t)F2 * d * m->es, hipMemcpyDeviceToDevice, s));
-      HIPCHK(hipMemcpyAsync(f.s_dn, ly.wdn, (size_t)d * F * m->es, hipMemcpyDeviceToDevice, s));
+    (void)ly;
+    fill_f32(f.m_up, (int64_t)F2 * d, 0.f, s);
+    fill_f32(f.m_dn, (int64_t)d * F, 0.f, s);
+    if (m->bf) {   // zero bits are 0 in bf16 too
+      fill_f32(static_cast<float*>(f.s_up), (int64_t)F2 * d * (int64_t)m->es / 4, 0.f, s);
+      fill_f32(static_cast<float*>(f.s_dn), (int64_t)d * F * (int64_t)m->es / 4, 0.f, s);
     }
   }
   for (int l = 0; l < m->L; ++l) {
@@ -635,7 +642,7 @@ int ttt_prefill(ttt_model* m, const int32_t* tokens, int64_t T, int32_t chunk, f
         // first decode token: argmax of the last position's logits from this
         // chunk's last read
         const char* frow = static_cast<const char*>(m->fN) + (size_t)(n - 1) * d * m->es;
-        gemv(m->U, m->V, d, frow, !m->bf, m->logits, nullptr, m->bf, s);
+        gemv(m->U, nullptr, m->V, d, frow, !m->bf, m->logits, nullptr, m->bf, s);
         argmax_tok(m->logits, m->V, m->cur_tok, nullptr, s);
       }
     }
@@ -659,8 +666,9 @@ int ttt_fast_weight(ttt_model* m, int32_t fast_idx, int32_t mat, float* dst, int
   if (n != (int64_t)d * F) return fail(TTT_ERR_ARG, "n must equal d_model * d_ff");
   hipStream_t s = static_cast<hipStream_t>(stream);
   FastLayer& f = m->fast[fast_idx];
-  if (mat == nmat - 1) export_weight(f.m_dn, d, F, 0, 0, dst, s);          // [F][d] canonical
-  else export_weight(f.m_up, F, d, sw ? 1 : 0, mat, dst, s);               // [d][F] canonical
+  Layer& ly = m->layers[m->f0 + fast_idx];
+  if (mat == nmat - 1) export_weight(ly.wdn, f.m_dn, d, F, 0, 0, dst, m->bf, s);          // [F][d]
+  else export_weight(ly.wup, f.m_up, F, d, sw ? 1 : 0, mat, dst, m->bf, s);               // [d][F]
   return TTT_OK;
 }
 
@@ -681,22 +689,22 @@ int ttt_decode_step(ttt_model* m, int32_t* next_token, float* logits_out, float*
     Layer& ly = m->layers[l];
     const int j = l - m->f0;
     layernorm_fwd(m->xd, d, 1, d, eps, m->ad, d, nullptr, nullptr, bf, s);
-    gemv(ly.wqkv, 3 * d, d, m->ad, !bf, m->qkvd, nullptr, bf, s);
+    gemv(ly.wqkv, nullptr, 3 * d, d, m->ad, !bf, m->qkvd, nullptr, bf, s);
     rope_qkv_f32in(m->qkvd, m->H, m->hd, p, m->theta, m->qd, ly.kring, ly.vring, ly.cap, bf, s);
     swa_decode(m->qd, ly.kring, ly.vring, ly.cap, m->H, m->hd, m->W, p, m->od, m->attn_ws, bf, s);
-    gemv(ly.wo, d, d, m->od, !bf, m->xd, m->xd, bf, s);
+    gemv(ly.wo, nullptr, d, d, m->od, !bf, m->xd, m->xd, bf, s);
     if (j == 0)   // phase-B input of this position, for the decode-chunk update
       HIPCHK(hipMemcpyAsync(m->hA + ci * d, m->xd, (size_t)d * 4, hipMemcpyDeviceToDevice, s));
     layernorm_fwd(m->xd, d, 1, d, eps, m->ad, d, nullptr, nullptr, bf, s);
-    const void* wup = j >= 0 ? m->fast[j].s_up : ly.wup;
-    const void* wdn = j >= 0 ? m->fast[j].s_dn : ly.wdn;
-    gemv(wup, F2, d, m->ad, !bf, m->zd, nullptr, bf, s);
+    const void* dup = j >= 0 ? m->fast[j].s_up : nullptr;
+    const void* ddn = j >= 0 ? m->fast[j].s_dn : nullptr;
+    gemv(ly.wup, dup, F2, d, m->ad, !bf, m->zd, nullptr, bf, s);
     if (m->c.mlp == TTT_MLP_SWIGLU) swiglu_vec(m->zd, F, m->actd, bf, s);
     else gelu_vec(m->zd, F, m->actd, bf, s);
-    gemv(wdn, d, F, m->actd, !bf, m->xd, m->xd, bf, s);
+    gemv(ly.wdn, ddn, d, F, m->actd, !bf, m->xd, m->xd, bf, s);
   }
   layernorm_fwd(m->xd, d, 1, d, eps, m->ad, d, nullptr, nullptr, bf, s);
-  gemv(m->U, V, d, m->ad, !bf, m->logits, nullptr, bf, s);
+  gemv(m->U, nullptr, V, d, m->ad, !bf, m->logits, nullptr, bf, s);
   argmax_tok(m->logits, V, m->cur_tok, m->hist + ci + 1, s);
   if (logits_out) HIPCHK(hipMemcpyAsync(logits_out, m->logits, (size_t)V * 4, hipMemcpyDeviceToDevice, s));
   m->pos = p + 1;

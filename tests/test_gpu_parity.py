@@ -75,7 +75,7 @@ def run_pair(cfg, dtype=None, std=0.02, T=None, chunk=None, lr=None, steps=1, pr
     model0 = O.OracleModel(cfg, w)
     w0 = [a for f in model0.initial_fast() for a in f.values()]
     out = dict(
-        loss=float(np.max(np.abs(losses - ref["losses"]) / np.abs(ref["losses"]))),
+        loss=float(np.max(np.abs(losses - ref["losses"]) / np.maximum(np.abs(ref["losses"]), 1e-12))),
         W=max(rel(a, b) for a, b in zip(fw, rfw)),
         dW=max(rel(a - c, b - c) for a, b, c in zip(fw, rfw, w0)),
         losses=losses, ref=ref["losses"], model=m, w=w, x=x)
@@ -84,7 +84,7 @@ def run_pair(cfg, dtype=None, std=0.02, T=None, chunk=None, lr=None, steps=1, pr
         r0 = O.prefill(cfg, w, x, chunk, 0.0, steps)["losses"]
         dg, dr = losses - l0, ref["losses"] - r0
         out["dloss"] = float(np.linalg.norm(dg - dr) / max(np.linalg.norm(dr), 1e-300))
-        out["loss0"] = float(np.max(np.abs(l0 - r0) / np.abs(r0)))
+        out["loss0"] = float(np.max(np.abs(l0 - r0) / np.maximum(np.abs(r0), 1e-12)))
     say(f"  errors: loss {out['loss']:.2e} W {out['W']:.2e} dW {out['dW']:.2e} "
         f"dloss {out.get('dloss', float('nan')):.2e} loss(lr=0) {out.get('loss0', float('nan')):.2e}")
     return out
