@@ -57,6 +57,9 @@ def run_pair(cfg, dtype=None, std=0.02, T=None, chunk=None, lr=None, steps=1, pr
     """GPU prefill and oracle prefill on the same inputs; returns errors."""
     T_ = _gpu()
     dtype = dtype or cfg["dtype"]
+    if dtype == "bf16":
+        # bf16 runs draw bf16-rounded weights, so both sides see the same values
+        cfg = synth.config(cfg, dtype="bf16")
     T = T or cfg["T"]
     chunk = chunk or cfg["chunk"]
     lr = cfg["lr"] if lr is None else lr
