@@ -78,99 +78,147 @@ DEVI void row_frags(typename Frag<T>::type* f, const T* base, int64_t ld,
 }
 
 // ------------------------------------------------------------------ forward
-template <typename T, int HD>
+// Each wave owns QB blocks of 16 queries, so every K / V^T fragment read
+// from LDS feeds QB matrix-core products; K/V tiles are double-buffered
+// (global reads for tile t+1 are in flight while tile t is consumed); only
+// tiles that straddle the band edges evaluate the mask.
+template <typename T, int HD, int QB>
 __global__ __launch_bounds__(256) void swa_fwd_k(AttnParams p) {
   using C = AttnCfg<T, HD>;
-  __shared__ __attribute__((aligned(16))) T Ks[TQ * C::LSN];
-  __shared__ __attribute__((aligned(16))) T Vt[HD * C::LST];
+  constexpr int QW = 16 * QB;
+  constexpr int QT = 4 * QW;
+  __shared__ __attribute__((aligned(16))) T Ks[2][TQ * C::LSN];
+  __shared__ __attribute__((aligned(16))) T Vt[2][HD * C::LST];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.y;
-  const int qs = blockIdx.x * TQ;
+  const int qs = blockIdx.x * QT;
   const int d = p.H * HD;
   const T* Q = static_cast<const T*>(p.q);
   const T* KR = static_cast<const T*>(p.kring);
   const T* VR = static_cast<const T*>(p.vring);
 
-  const int qrow = qs + wave * 16 + (lane & 15);
-  const bool qok = qrow < p.n;
-  const int64_t qpos = p.pos0 + qrow;
-  typename Frag<T>::type qf[C::KS];
-  row_frags<T, HD>(qf, Q + (int64_t)qrow * p.ldq + h * HD, p.ldq, qok, lane);
-
-  const float sc = LOG2E / sqrtf((float)HD);
-  float m = -INFINITY, l = 0.f;
-  f32x4 oacc[C::HB];
+  typename Frag<T>::type qf[QB][C::KS];
+  float m[QB], l[QB];
+  f32x4 oacc[QB][C::HB];
 #pragma unroll
-  for (int b = 0; b < C::HB; ++b) oacc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = qs + wave * QW + qb * 16 + (lane & 15);
+    row_frags<T, HD>(qf[qb], Q + (int64_t)row * p.ldq + h * HD, p.ldq, row < p.n, lane);
+    m[qb] = -INFINITY;
+    l[qb] = 0.f;
+#pragma unroll
+    for (int b = 0; b < C::HB; ++b) oacc[qb][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const float sc = LOG2E / sqrtf((float)HD);
 
   const int64_t first = p.pos0 + qs;
-  const int64_t last = p.pos0 + min(qs + TQ, p.n) - 1;
+  const int64_t last = p.pos0 + min(qs + QT, p.n) - 1;
   int64_t lo = first - p.window + 1;
   if (lo < 0) lo = 0;
   const int64_t kt0 = (lo / TQ) * TQ;
-  for (int64_t kt = kt0; kt <= last; kt += TQ) {
-    const int nvalid = (int)min<int64_t>(TQ, last - kt + 1);
-    const int64_t slot = kt % p.cap;
-    __syncthreads();
-    load_nat<T, HD>(Ks, KR + slot * d + h * HD, d, nvalid, tid);
-    load_tr<T, HD>(Vt, VR + slot * d + h * HD, d, nvalid, tid);
-    __syncthreads();
+  const int ntile = (int)((last - kt0) / TQ) + 1;
 
-    f32x4 s[4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks)
-        mma16x16x32(nat_frag<T, HD>(Ks, kb * 16 + (lane & 15), ks, lane), qf[ks], s[kb]);
+  StagedRows<T, TQ, C::HDP, C::LSN, 256> lk;
+  StagedTrans<T, TQ, HD, C::LST, 256> lv;
+  {
+    const int nv = (int)min<int64_t>(TQ, last - kt0 + 1);
+    const int64_t slot = kt0 % p.cap;
+    lk.load(KR + slot * d + h * HD, d, nv, HD, tid);
+    lv.load(VR + slot * d + h * HD, d, nv, HD, tid);
+    lk.store(Ks[0], tid);
+    lv.store(Vt[0], tid);
+  }
+  __syncthreads();
+
+  for (int it = 0; it < ntile; ++it) {
+    const int cur = it & 1;
+    const int64_t kt = kt0 + (int64_t)it * TQ;
+    if (it + 1 < ntile) {
+      const int64_t kn = kt + TQ;
+      const int nv = (int)min<int64_t>(TQ, last - kn + 1);
+      const int64_t slot = kn % p.cap;
+      lk.load(KR + slot * d + h * HD, d, nv, HD, tid);
+      lv.load(VR + slot * d + h * HD, d, nv, HD, tid);
     }
-    float tmax = -INFINITY;
+    const bool interior = (kt + TQ - 1 <= first) && (kt > last - p.window);
+    const int kq0 = (int)(kt - first);   // key offset relative to the first query
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int qb = 0; qb < QB; ++qb) {
+      f32x4 s[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t kp = kt + kb * 16 + 4 * (lane >> 4) + i;
-        const bool ok = kp <= qpos && kp > qpos - p.window;
-        const float v = ok ? s[kb][i] * sc : -INFINITY;
-        s[kb][i] = v;
-        tmax = fmaxf(tmax, v);
+      for (int kb = 0; kb < 4; ++kb) {
+        s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks)
+          mma16x16x32(nat_frag<T, HD>(Ks[cur], kb * 16 + (lane & 15), ks, lane), qf[qb][ks], s[kb]);
       }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float mn = fmaxf(m, tmax);
-    const float alpha = (mn == -INFINITY) ? 1.f : exp2f(m - mn);
-    float rs = 0.f;
+      float tmax = -INFINITY;
+      if (interior) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float e = (mn == -INFINITY) ? 0.f : exp2f(s[kb][i] - mn);
-        s[kb][i] = e;
-        rs += e;
+          for (int i = 0; i < 4; ++i) {
+            s[kb][i] *= sc;
+            tmax = fmaxf(tmax, s[kb][i]);
+          }
+      } else {
+        const int qoff = wave * QW + qb * 16 + (lane & 15);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int rel = kq0 + kb * 16 + 4 * (lane >> 4) + i - qoff;   // key - query
+            const float v = (rel <= 0 && rel > -p.window) ? s[kb][i] * sc : -INFINITY;
+            s[kb][i] = v;
+            tmax = fmaxf(tmax, v);
+          }
       }
-    rs += __shfl_xor(rs, 16, 64);
-    rs += __shfl_xor(rs, 32, 64);
-    l = l * alpha + rs;
-    m = mn;
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      const float mn = fmaxf(m[qb], tmax);
+      const bool none = (mn == -INFINITY);
+      const float alpha = none ? 1.f : exp2f(m[qb] - mn);
+      float rs = 0.f;
 #pragma unroll
-    for (int b = 0; b < C::HB; ++b) oacc[b] *= alpha;
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-    for (int pp = 0; pp < 2; ++pp) {
-      const typename Frag<T>::type pf = acc_frag<T>(s[2 * pp], s[2 * pp + 1]);
+        for (int i = 0; i < 4; ++i) {
+          const float e = none ? 0.f : exp2f(s[kb][i] - mn);
+          s[kb][i] = e;
+          rs += e;
+        }
+      rs += __shfl_xor(rs, 16, 64);
+      rs += __shfl_xor(rs, 32, 64);
+      l[qb] = l[qb] * alpha + rs;
+      m[qb] = mn;
 #pragma unroll
-      for (int b = 0; b < C::HB; ++b)
-        mma16x16x32(tr_frag<T, HD>(Vt, b * 16 + (lane & 15), pp, lane), pf, oacc[b]);
+      for (int b = 0; b < C::HB; ++b) oacc[qb][b] *= alpha;
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        const typename Frag<T>::type pf = acc_frag<T>(s[2 * pp], s[2 * pp + 1]);
+#pragma unroll
+        for (int b = 0; b < C::HB; ++b)
+          mma16x16x32(tr_frag<T, HD>(Vt[cur], b * 16 + (lane & 15), pp, lane), pf, oacc[qb][b]);
+      }
     }
+    if (it + 1 < ntile) {
+      lk.store(Ks[cur ^ 1], tid);
+      lv.store(Vt[cur ^ 1], tid);
+    }
+    __syncthreads();
   }
 
-  if (qok) {
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    T* O = static_cast<T*>(p.o) + (int64_t)qrow * p.ldo + h * HD;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = qs + wave * QW + qb * 16 + (lane & 15);
+    if (row >= p.n) continue;
+    const float inv = l[qb] > 0.f ? 1.f / l[qb] : 0.f;
+    T* O = static_cast<T*>(p.o) + (int64_t)row * p.ldo + h * HD;
 #pragma unroll
     for (int b = 0; b < C::HB; ++b)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) O[b * 16 + 4 * (lane >> 4) + i] = from_f32<T>(oacc[b][i] * inv);
-    if (p.lse && (lane >> 4) == 0) p.lse[(int64_t)h * p.n + qrow] = (m + log2f(l)) * LN2;
+      for (int i = 0; i < 4; ++i) O[b * 16 + 4 * (lane >> 4) + i] = from_f32<T>(oacc[qb][b][i] * inv);
+    if (p.lse && (lane >> 4) == 0) p.lse[(int64_t)h * p.n + row] = (m[qb] + log2f(l[qb])) * LN2;
   }
 }
 
@@ -353,13 +401,14 @@ template <typename T, template <typename, int> class K> struct HdDispatch;
 
 template <typename T>
 void fwd_t(const AttnParams& p, hipStream_t s) {
-  dim3 grid((p.n + TQ - 1) / TQ, p.H);
+  constexpr int QB = sizeof(T) == 2 ? 2 : 1;
+  dim3 grid((p.n + 64 * QB - 1) / (64 * QB), p.H);
   switch (p.hd) {
-    case 16: hipLaunchKernelGGL((swa_fwd_k<T, 16>), grid, dim3(256), 0, s, p); break;
-    case 32: hipLaunchKernelGGL((swa_fwd_k<T, 32>), grid, dim3(256), 0, s, p); break;
-    case 64: hipLaunchKernelGGL((swa_fwd_k<T, 64>), grid, dim3(256), 0, s, p); break;
-    case 96: hipLaunchKernelGGL((swa_fwd_k<T, 96>), grid, dim3(256), 0, s, p); break;
-    case 128: hipLaunchKernelGGL((swa_fwd_k<T, 128>), grid, dim3(256), 0, s, p); break;
+    case 16: hipLaunchKernelGGL((swa_fwd_k<T, 16, QB>), grid, dim3(256), 0, s, p); break;
+    case 32: hipLaunchKernelGGL((swa_fwd_k<T, 32, QB>), grid, dim3(256), 0, s, p); break;
+    case 64: hipLaunchKernelGGL((swa_fwd_k<T, 64, QB>), grid, dim3(256), 0, s, p); break;
+    case 96: hipLaunchKernelGGL((swa_fwd_k<T, 96, QB>), grid, dim3(256), 0, s, p); break;
+    case 128: hipLaunchKernelGGL((swa_fwd_k<T, 128, QB>), grid, dim3(256), 0, s, p); break;
     default: break;
   }
 }

@@ -133,6 +133,84 @@ DEVI void tile_copy_transpose(T* __restrict__ lds, const T* __restrict__ g, int6
   }
 }
 
+// Register-staged versions of the two tile copies above: load() issues the
+// global reads (so they can overlap compute on the other LDS buffer),
+// store() writes LDS.
+template <typename T, int ROWS, int COLS, int LDS_STRIDE, int NTHREADS>
+struct StagedRows {
+  static constexpr int V = Vec16<T>::N;
+  static constexpr int VPR = COLS / V;
+  static constexpr int TOTAL = ROWS * VPR;
+  static constexpr int IT = (TOTAL + NTHREADS - 1) / NTHREADS;
+  U128 r[IT];
+  DEVI void load(const T* __restrict__ g, int64_t ld, int row_lim, int col_lim, int tid) {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int idx = it * NTHREADS + tid;
+      const int rr = idx / VPR, c = (idx % VPR) * V;
+      const bool ok = (TOTAL % NTHREADS == 0 || idx < TOTAL) && rr < row_lim && c < col_lim;
+      r[it] = ok ? ld128(g + (int64_t)rr * ld + c) : zero128();
+    }
+  }
+  DEVI void store(T* __restrict__ lds, int tid) const {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int idx = it * NTHREADS + tid;
+      if (TOTAL % NTHREADS == 0 || idx < TOTAL) {
+        const int rr = idx / VPR, c = (idx % VPR) * V;
+        st128(lds + rr * LDS_STRIDE + c, r[it]);
+      }
+    }
+  }
+};
+
+template <typename T, int KR, int MC, int LDS_STRIDE, int NTHREADS>
+struct StagedTrans {
+  static constexpr int V = Vec16<T>::N;
+  static constexpr int MV = MC / V;
+  static constexpr int KB = KR / 4;
+  static constexpr int TOTAL = MV * KB;
+  static constexpr int IT = (TOTAL + NTHREADS - 1) / NTHREADS;
+  U128 r[IT][4];
+  DEVI void load(const T* __restrict__ g, int64_t ld, int k_lim, int m_lim, int tid) {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int idx = it * NTHREADS + tid;
+      const int mv = idx % MV, kb = idx / MV;
+      const int m0 = mv * V, k0 = kb * 4;
+      const bool live = TOTAL % NTHREADS == 0 || idx < TOTAL;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        r[it][q] = (live && k0 + q < k_lim && m0 < m_lim) ? ld128(g + (int64_t)(k0 + q) * ld + m0) : zero128();
+    }
+  }
+  DEVI void store(T* __restrict__ lds, int tid) const {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int idx = it * NTHREADS + tid;
+      if (!(TOTAL % NTHREADS == 0 || idx < TOTAL)) continue;
+      const int mv = idx % MV, kb = idx / MV;
+      const int m0 = mv * V, k0 = kb * 4;
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        T t4[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) t4[q] = elem<T>(r[it][q], e);
+        T* dst = lds + (m0 + e) * LDS_STRIDE + k0;
+        if constexpr (sizeof(T) == 2) {
+          uint2 w;
+          w.x = (uint32_t)__builtin_bit_cast(uint16_t, t4[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, t4[1]) << 16);
+          w.y = (uint32_t)__builtin_bit_cast(uint16_t, t4[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, t4[3]) << 16);
+          *reinterpret_cast<uint2*>(dst) = w;
+        } else {
+          float4 w; w.x = t4[0]; w.y = t4[1]; w.z = t4[2]; w.w = t4[3];
+          *reinterpret_cast<float4*>(dst) = w;
+        }
+      }
+    }
+  }
+};
+
 // Read an 8-element operand fragment from an LDS row (k contiguous).
 template <typename T> DEVI typename Frag<T>::type lds_frag8(const T* p);
 template <> DEVI bf16x8 lds_frag8<bf16>(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }

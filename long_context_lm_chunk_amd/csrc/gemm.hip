@@ -18,7 +18,8 @@
 //   GELU    z = acc, act = gelu_erf(acc)
 //   SWIGLU  columns come in blocks of 16 gate / 16 up; z = acc,
 //           act = silu(gate) * up
-//   SGD     master_f32 -= lr * acc ; shadow = round(master)   (fast weights)
+//   SGD     delta_f32 -= lr * acc ; delta copy = round(delta) ;
+//           current = round(W0 + delta)                    (fast weights)
 //   CESTAT  per-row partial max / sum(exp) of the logits and the target logit
 //   CEGRAD  g = (softmax - onehot(target)) / n_targets, rows without a target 0
 #include "common.hpp"
@@ -258,6 +259,8 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmParams p) {
               const float nw = w[ci] - p.alpha * v;
               w[ci] = nw;
               if (p.C2) static_cast<TO*>(p.C2)[(int64_t)row * p.ldc2 + col] = from_f32<TO>(nw);
+              if (p.C3)
+                static_cast<TO*>(p.C3)[ci] = from_f32<TO>(to_f32(static_cast<const TO*>(p.W0)[ci]) + nw);
             } else if constexpr (EPI == EPI_CEGRAD) {
               float g = 0.f;
               if (row < p.n_tgt) {

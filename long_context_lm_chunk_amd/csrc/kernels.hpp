@@ -14,7 +14,8 @@ struct GemmParams {
   int M = 0, N = 0, K = 0;
   void* C = nullptr; int64_t ldc = 0;        // primary output
   const float* R = nullptr; int64_t ldr = 0; // residual input (RESID)
-  void* C2 = nullptr; int64_t ldc2 = 0;      // act (GELU/SWIGLU), bf16 shadow (SGD)
+  void* C2 = nullptr; int64_t ldc2 = 0;      // act (GELU/SWIGLU), delta copy (SGD)
+  void* C3 = nullptr; const void* W0 = nullptr;  // SGD: C3 = round(W0 + delta), same layout as C
   float alpha = 0.f;                         // SGD: lr; CEGRAD: 1/n_targets
   // cross-entropy epilogues
   const int* tgt = nullptr; int n_tgt = 0;

@@ -75,11 +75,17 @@ struct Carver {
 // feeds the products, which run over W0 and delta in one fp32 accumulation.
 // Updates of lr*g ~ 1e-8 are far below a bf16 ulp of W (~1e-4), so rounding
 // W0 + delta to bf16 would erase them; delta's own ulp scales with delta.
+//
+// The input-gradient products of the backward pass only need the current
+// weights to working precision, so they read one rounded copy
+// round(W0 + delta) (c_up / c_dn), refreshed by the SGD epilogue.
 struct FastLayer {
   float* m_up = nullptr;  // fp32 delta master [F2][d]
   float* m_dn = nullptr;  // fp32 delta master [d][F]
   void* s_up = nullptr;   // delta in the storage type (== master in fp32 mode)
   void* s_dn = nullptr;
+  void* c_up = nullptr;   // round(W0 + delta) in the storage type
+  void* c_dn = nullptr;
 };
 
 struct Layer {
@@ -191,6 +197,8 @@ size_t layout(ttt_model* m, void* base) {
       f.s_up = f.m_up;
       f.s_dn = f.m_dn;
     }
+    f.c_up = cv.take<void>((size_t)F2 * d * es);
+    f.c_dn = cv.take<void>((size_t)d * F * es);
   }
   m->theta = cv.take<double>((size_t)(m->hd / 2) * 8);
   // phase A
@@ -452,24 +460,26 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
     const float* x2 = (j > 0) ? b.x2 : x2_0;
     // dact = dh . Wdn  (reads the weights before their update)
     GemmParams ga;
-    ga.A = m->dh_lo; ga.lda = d; ga.B = ly.wdn; ga.B2 = fw.s_dn; ga.ldb = F; ga.M = n; ga.N = F; ga.K = d;
+    ga.A = m->dh_lo; ga.lda = d; ga.B = fw.c_dn; ga.ldb = F; ga.M = n; ga.N = F; ga.K = d;
     ga.C = m->dact; ga.ldc = F;
     rc = run_gemm(m, ga, true, false, EPI_STORE, true, s); if (rc) return rc;
     // Wdn -= lr * dh^T act   ([d][F], reduction over the chunk's tokens)
     GemmParams gw;
     gw.A = m->dh_lo; gw.lda = d; gw.B = b.act; gw.ldb = F; gw.M = d; gw.N = F; gw.K = n;
     gw.C = fw.m_dn; gw.ldc = F; gw.C2 = bf ? fw.s_dn : nullptr; gw.ldc2 = F; gw.alpha = lr;
+    gw.C3 = fw.c_dn; gw.W0 = ly.wdn;
     rc = run_gemm(m, gw, false, false, EPI_SGD, true, s); if (rc) return rc;
     act_bwd(m->dact, b.z, n, F, m->c.mlp == TTT_MLP_SWIGLU, m->dz, bf, s);
     if (j > 0) {
       GemmParams gb;   // db = dz . Wup (before its update)
-      gb.A = m->dz; gb.lda = F2; gb.B = ly.wup; gb.B2 = fw.s_up; gb.ldb = d; gb.M = n; gb.N = d; gb.K = F2;
+      gb.A = m->dz; gb.lda = F2; gb.B = fw.c_up; gb.ldb = d; gb.M = n; gb.N = d; gb.K = F2;
       gb.C = m->dtmp; gb.ldc = d;
       rc = run_gemm(m, gb, true, false, EPI_STORE, true, s); if (rc) return rc;
     }
     GemmParams gw2;   // Wup -= lr * dz^T b
     gw2.A = m->dz; gw2.lda = F2; gw2.B = b.b; gw2.ldb = d; gw2.M = F2; gw2.N = d; gw2.K = n;
     gw2.C = fw.m_up; gw2.ldc = d; gw2.C2 = bf ? fw.s_up : nullptr; gw2.ldc2 = d; gw2.alpha = lr;
+    gw2.C3 = fw.c_up; gw2.W0 = ly.wup;
     rc = run_gemm(m, gw2, false, false, EPI_SGD, true, s); if (rc) return rc;
     if (j == 0) break;   // no gradient below the first fast MLP
     layernorm_bwd_acc(m->dtmp, x2, b.mean2, b.rstd2, n, d, m->dh, m->dh_lo, bf, s);
@@ -514,13 +524,14 @@ int reset_state(ttt_model* m, hipStream_t s) {
   for (int j = 0; j < m->q; ++j) {
     Layer& ly = m->layers[m->f0 + j];
     FastLayer& f = m->fast[j];
-    (void)ly;
     fill_f32(f.m_up, (int64_t)F2 * d, 0.f, s);
     fill_f32(f.m_dn, (int64_t)d * F, 0.f, s);
     if (m->bf) {   // zero bits are 0 in bf16 too
       fill_f32(static_cast<float*>(f.s_up), (int64_t)F2 * d * (int64_t)m->es / 4, 0.f, s);
       fill_f32(static_cast<float*>(f.s_dn), (int64_t)d * F * (int64_t)m->es / 4, 0.f, s);
     }
+    HIPCHK(hipMemcpyAsync(f.c_up, ly.wup, (size_t)F2 * d * m->es, hipMemcpyDeviceToDevice, s));
+    HIPCHK(hipMemcpyAsync(f.c_dn, ly.wdn, (size_t)d * F * m->es, hipMemcpyDeviceToDevice, s));
   }
   for (int l = 0; l < m->L; ++l) {
     Layer& ly = m->layers[l];
