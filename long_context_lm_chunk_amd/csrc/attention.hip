@@ -152,47 +152,50 @@ __global__ __launch_bounds__(256) void swa_fwd_k(AttnParams p) {
         for (int ks = 0; ks < C::KS; ++ks)
           mma16x16x32(nat_frag<T, HD>(Ks[cur], kb * 16 + (lane & 15), ks, lane), qf[qb][ks], s[kb]);
       }
-      float tmax = -INFINITY;
-      if (interior) {
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            s[kb][i] *= sc;
-            tmax = fmaxf(tmax, s[kb][i]);
-          }
-      } else {
+      if (!interior) {
         const int qoff = wave * QW + qb * 16 + (lane & 15);
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int rel = kq0 + kb * 16 + 4 * (lane >> 4) + i - qoff;   // key - query
-            const float v = (rel <= 0 && rel > -p.window) ? s[kb][i] * sc : -INFINITY;
-            s[kb][i] = v;
-            tmax = fmaxf(tmax, v);
+            if (!(rel <= 0 && rel > -p.window)) s[kb][i] = -INFINITY;
           }
       }
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        tmax = fmaxf(fmaxf(tmax, fmaxf(s[kb][0], s[kb][1])), fmaxf(s[kb][2], s[kb][3]));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float mn = fmaxf(m[qb], tmax);
-      const bool none = (mn == -INFINITY);
-      const float alpha = none ? 1.f : exp2f(m[qb] - mn);
+      tmax *= sc;   // scores enter the exponent as s * sc (log2 units)
+      // Lazy rescaling: the reference maximum only moves when the tile's
+      // maximum exceeds it by more than 8 (log2 units), so probabilities stay
+      // below 2^8 (harmless in fp32 sums and in bf16) and the accumulator
+      // rescale is skipped on almost every tile.  The result does not depend
+      // on the reference, so this is exact.
+      const bool bump = tmax > m[qb] + 8.f;
+      if (__any(bump)) {
+        const float mn = bump ? tmax : m[qb];
+        const float alpha = (m[qb] == -INFINITY) ? 0.f : fast_exp2(m[qb] - mn);
+        l[qb] *= alpha;
+#pragma unroll
+        for (int b = 0; b < C::HB; ++b) oacc[qb][b] *= alpha;
+        m[qb] = mn;
+      }
+      const float mref = (m[qb] == -INFINITY) ? 0.f : m[qb];
       float rs = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float e = none ? 0.f : exp2f(s[kb][i] - mn);
+          const float e = fast_exp2(fmaf(s[kb][i], sc, -mref));   // -inf -> 0
           s[kb][i] = e;
           rs += e;
         }
       rs += __shfl_xor(rs, 16, 64);
       rs += __shfl_xor(rs, 32, 64);
-      l[qb] = l[qb] * alpha + rs;
-      m[qb] = mn;
-#pragma unroll
-      for (int b = 0; b < C::HB; ++b) oacc[qb][b] *= alpha;
+      l[qb] += rs;
 #pragma unroll
       for (int pp = 0; pp < 2; ++pp) {
         const typename Frag<T>::type pf = acc_frag<T>(s[2 * pp], s[2 * pp + 1]);
@@ -280,7 +283,7 @@ __global__ __launch_bounds__(256) void swa_bwd_dq_k(AttnParams p) {
       for (int i = 0; i < 4; ++i) {
         const int64_t kp = kt + kb * 16 + 4 * (lane >> 4) + i;
         const bool ok = qok && kp <= qpos && kp > qpos - p.window;
-        const float pr = ok ? exp2f(s[kb][i] * sc - lse2) : 0.f;
+        const float pr = ok ? fast_exp2(fmaf(s[kb][i], sc, -lse2)) : 0.f;
         s[kb][i] = pr * (dp[kb][i] - Dq);   // dS^T
       }
 #pragma unroll
@@ -368,7 +371,7 @@ __global__ __launch_bounds__(256) void swa_bwd_dkdv_k(AttnParams p) {
         const int qi = qb * 16 + 4 * (lane >> 4) + i;
         const int64_t qp = p.pos0 + qt + qi;
         const bool ok = kok && (qt + qi < p.n) && kpos <= qp && kpos > qp - p.window;
-        const float pr = ok ? exp2f(s[qb][i] * sc - lse_s[qi]) : 0.f;
+        const float pr = ok ? fast_exp2(fmaf(s[qb][i], sc, -lse_s[qi])) : 0.f;
         s[qb][i] = pr;                              // P
         dp[qb][i] = pr * (dp[qb][i] - D_s[qi]);     // dS
       }

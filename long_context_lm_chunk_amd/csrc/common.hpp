@@ -105,7 +105,7 @@ DEVI void tile_copy_transpose(T* __restrict__ lds, const T* __restrict__ g, int6
   for (int it = 0; it < (TOTAL + NTHREADS - 1) / NTHREADS; ++it) {
     int idx = it * NTHREADS + tid;
     if (TOTAL % NTHREADS == 0 || idx < TOTAL) {
-      int mv = idx % MV, kb = idx / MV;
+      int kb = idx % KB, mv = idx / KB;   // k-groups fastest (bank conflicts)
       int m0 = mv * V, k0 = kb * 4;
       U128 r[4];
 #pragma unroll
@@ -176,7 +176,7 @@ struct StagedTrans {
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
       const int idx = it * NTHREADS + tid;
-      const int mv = idx % MV, kb = idx / MV;
+      const int kb = idx % KB, mv = idx / KB;   // k-groups fastest: see store()
       const int m0 = mv * V, k0 = kb * 4;
       const bool live = TOTAL % NTHREADS == 0 || idx < TOTAL;
 #pragma unroll
@@ -189,7 +189,11 @@ struct StagedTrans {
     for (int it = 0; it < IT; ++it) {
       const int idx = it * NTHREADS + tid;
       if (!(TOTAL % NTHREADS == 0 || idx < TOTAL)) continue;
-      const int mv = idx % MV, kb = idx / MV;
+      // Lanes of a wave differ mostly in kb, i.e. in the column of the
+      // transposed row they write; with the usual row pitch of (multiple of
+      // 64) + 16 bytes this keeps a wave's 8-byte writes at most 2-way
+      // bank-conflicted (m-fastest lanes would hit the same bank 8 ways).
+      const int kb = idx % KB, mv = idx / KB;
       const int m0 = mv * V, k0 = kb * 4;
 #pragma unroll
       for (int e = 0; e < V; ++e) {
@@ -263,4 +267,6 @@ template <> DEVI f32x8 pack8<float>(const float* v) {
   f32x8 r; for (int i = 0; i < 8; ++i) r[i] = v[i]; return r;
 }
 
+// 2^x with the hardware instruction (no denormal range fix-up; the inputs
+// here are <= 8 and results below 2^-126 may flush to zero).
 DEVI float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

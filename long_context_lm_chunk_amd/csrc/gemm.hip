@@ -57,11 +57,11 @@ template <typename T, bool KC, int ROWS> struct TileLoader {
         r[it] = ok ? ld128(g + (int64_t)(row0 + rr) * ld + k0 + c) : zero128();
       }
     } else {
-      constexpr int MV = ROWS / V;
+      constexpr int KB = C::BK / 4;
 #pragma unroll
       for (int it = 0; it < NV / 4; ++it) {
         int idx = it * NT + tid;
-        int mv = idx % MV, kb = idx / MV;
+        int kb = idx % KB, mv = idx / KB;
         int m = row0 + mv * V, k = k0 + kb * 4;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -82,11 +82,13 @@ template <typename T, bool KC, int ROWS> struct TileLoader {
         st128(lds + rr * C::LS + c, r[it]);
       }
     } else {
-      constexpr int MV = ROWS / V;
+      // k-groups fastest across lanes: a wave's transposed 8-byte LDS
+      // writes then spread over the banks instead of colliding 8 ways
+      constexpr int KB = C::BK / 4;
 #pragma unroll
       for (int it = 0; it < NV / 4; ++it) {
         int idx = it * NT + tid;
-        int mv = idx % MV, kb = idx / MV;
+        int kb = idx % KB, mv = idx / KB;
         int m0 = mv * V, k0 = kb * 4;
 #pragma unroll
         for (int e = 0; e < V; ++e) {
