@@ -81,7 +81,7 @@ def main():
     ap.add_argument("--T", type=int, default=None)
     ap.add_argument("--decode-tokens", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=256)
+    ap.add_argument("--cpu-sample", type=int, default=1024)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); the inner loop of one "

@@ -159,6 +159,7 @@ const char* ttt_last_error(void);
  *   cls 2 = sliding-window attention backward
  *   cls 3 = fused head + cross-entropy (statistics, gradient, input grad)
  *   cls 4 = the weight-gradient GEMMs with the fused SGD update
+ *   cls 5 = the MLP up-projection GEMM of the frozen blocks (one kernel)
  * ttt_timing_read synchronises the stream and returns the summed event time
  * (ms), the number of launches and the algorithmic FLOPs of those launches.
  */

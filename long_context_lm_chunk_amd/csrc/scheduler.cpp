@@ -313,8 +313,11 @@ int run_gemm(ttt_model* m, const GemmParams& p, bool a_kc, bool b_kc, int epi, b
   int rc;
   {
     Scope t0(m, CLS_GEMM, s, fl);
-    Scope t4(m, epi == EPI_SGD ? CLS_SGD : (epi == EPI_GELU || epi == EPI_SWIGLU) ? CLS_MLP_UP : NCLS - 1, s,
-             (epi == EPI_SGD || epi == EPI_GELU || epi == EPI_SWIGLU) ? fl : 0.0);
+    // class 5 is one kernel symbol: the up-projection with a single B (the
+    // frozen blocks); the fast blocks' two-B launches are a different kernel
+    const bool up1 = (epi == EPI_GELU || epi == EPI_SWIGLU) && p.B2 == nullptr;
+    Scope t4(m, epi == EPI_SGD ? CLS_SGD : up1 ? CLS_MLP_UP : NCLS - 1, s,
+             (epi == EPI_SGD || up1) ? fl : 0.0);
     rc = gemm(p, m->bf, a_kc, b_kc, epi, out_f32, s);
   }
   return rc == 0 ? TTT_OK : fail(TTT_ERR_CONFIG, "internal: GEMM variant not built");
