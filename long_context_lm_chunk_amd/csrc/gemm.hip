@@ -111,6 +111,23 @@ template <typename T, bool KC, int ROWS> struct TileLoader {
   }
 };
 
+template <typename T> DEVI void store4(T* p, const float4& v);
+template <> DEVI void store4<float>(float* p, const float4& v) { *reinterpret_cast<float4*>(p) = v; }
+template <> DEVI void store4<bf16>(bf16* p, const float4& v) {
+  bf16x4 b;
+  b[0] = static_cast<bf16>(v.x); b[1] = static_cast<bf16>(v.y);
+  b[2] = static_cast<bf16>(v.z); b[3] = static_cast<bf16>(v.w);
+  *reinterpret_cast<bf16x4*>(p) = b;
+}
+template <typename T> DEVI float4 load4(const T* p);
+template <> DEVI float4 load4<float>(const float* p) { return *reinterpret_cast<const float4*>(p); }
+template <> DEVI float4 load4<bf16>(const bf16* p) {
+  const bf16x4 b = *reinterpret_cast<const bf16x4*>(p);
+  float4 v; v.x = static_cast<float>(b[0]); v.y = static_cast<float>(b[1]);
+  v.z = static_cast<float>(b[2]); v.w = static_cast<float>(b[3]);
+  return v;
+}
+
 DEVI float gelu_erf(float z) { return 0.5f * z * (1.f + erff(z * 0.70710678118654752f)); }
 DEVI float silu(float z) { return z / (1.f + __expf(-z)); }
 
@@ -222,57 +239,78 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmParams p) {
     }
     return;
   } else {
+    // Stage the 128x128 fp32 tile through LDS (the operand buffers are free
+    // after the last barrier of the main loop), then let every thread apply
+    // the epilogue to runs of 4 consecutive columns with 16-byte (fp32) or
+    // 8-byte (bf16) vector accesses instead of the scattered per-element
+    // stores of the matrix-core layout.
+    constexpr int ES = BN + 4;                         // fp32 row pitch in LDS
+    static_assert(BM * ES * 4 <= 2 * (BM + BN) * C::LS * (int)sizeof(T), "epilogue tile fits");
+    float* st = reinterpret_cast<float*>(&lds[0][0]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = rbase + i * 16 + e;
-        if (row >= p.M) continue;
-        if constexpr (EPI == EPI_SWIGLU) {
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-          for (int pr = 0; pr < 2; ++pr) {
-            const int colg = cbase + (2 * pr) * 16;
-            const int colu = colg + 16;
-            if (colu < p.N) {
-              const float g = acc[i][2 * pr][e], u = acc[i][2 * pr + 1][e];
-              TO* z = static_cast<TO*>(p.C);
-              z[(int64_t)row * p.ldc + colg] = from_f32<TO>(g);
-              z[(int64_t)row * p.ldc + colu] = from_f32<TO>(u);
-              const int ca = (n0 + wn * 64) / 2 + pr * 16 + (lane & 15);
-              static_cast<TO*>(p.C2)[(int64_t)row * p.ldc2 + ca] = from_f32<TO>(silu(g) * u);
-            }
+        for (int e = 0; e < 4; ++e)
+          st[(wm * 64 + i * 16 + 4 * (lane >> 4) + e) * ES + wn * 64 + j * 16 + (lane & 15)] = acc[i][j][e];
+    __syncthreads();
+    if constexpr (EPI == EPI_SWIGLU) {
+      // columns: gate block 32c..32c+15, up block 32c+16..32c+31 -> act 16c..16c+15
+      for (int g = tid; g < BM * (BN / 8); g += NT) {
+        const int r = g / (BN / 8), q = g % (BN / 8);      // q: 4-wide group of act columns
+        const int row = m0 + r;
+        const int cg = (q / 4) * 32 + (q % 4) * 4;          // gate column in the tile
+        if (row >= p.M || n0 + cg >= p.N) continue;   // N % 32 == 0: gate in => up in
+        const float4 gv = *reinterpret_cast<const float4*>(st + r * ES + cg);
+        const float4 uv = *reinterpret_cast<const float4*>(st + r * ES + cg + 16);
+        TO* z = static_cast<TO*>(p.C) + (int64_t)row * p.ldc + n0;
+        store4<TO>(z + cg, gv);
+        store4<TO>(z + cg + 16, uv);
+        float4 a;
+        a.x = silu(gv.x) * uv.x; a.y = silu(gv.y) * uv.y; a.z = silu(gv.z) * uv.z; a.w = silu(gv.w) * uv.w;
+        store4<TO>(static_cast<TO*>(p.C2) + (int64_t)row * p.ldc2 + n0 / 2 + (q / 4) * 16 + (q % 4) * 4, a);
+      }
+    } else {
+      for (int g = tid; g < BM * (BN / 4); g += NT) {
+        const int r = g / (BN / 4), c = (g % (BN / 4)) * 4;
+        const int row = m0 + r, col = n0 + c;
+        if (row >= p.M || col >= p.N) continue;         // N is a multiple of 4
+        const float4 v = *reinterpret_cast<const float4*>(st + r * ES + c);
+        const int64_t ci = (int64_t)row * p.ldc + col;
+        if constexpr (EPI == EPI_STORE) {
+          store4<TO>(static_cast<TO*>(p.C) + ci, v);
+        } else if constexpr (EPI == EPI_RESID) {
+          const float4 rr = *reinterpret_cast<const float4*>(p.R + (int64_t)row * p.ldr + col);
+          float4 o; o.x = rr.x + v.x; o.y = rr.y + v.y; o.z = rr.z + v.z; o.w = rr.w + v.w;
+          *reinterpret_cast<float4*>(static_cast<float*>(p.C) + ci) = o;
+        } else if constexpr (EPI == EPI_GELU) {
+          store4<TO>(static_cast<TO*>(p.C) + ci, v);
+          float4 a; a.x = gelu_erf(v.x); a.y = gelu_erf(v.y); a.z = gelu_erf(v.z); a.w = gelu_erf(v.w);
+          store4<TO>(static_cast<TO*>(p.C2) + (int64_t)row * p.ldc2 + col, a);
+        } else if constexpr (EPI == EPI_SGD) {
+          float4* wp = reinterpret_cast<float4*>(static_cast<float*>(p.C) + ci);
+          float4 w = *wp;
+          w.x -= p.alpha * v.x; w.y -= p.alpha * v.y; w.z -= p.alpha * v.z; w.w -= p.alpha * v.w;
+          *wp = w;
+          if (p.C2) store4<TO>(static_cast<TO*>(p.C2) + (int64_t)row * p.ldc2 + col, w);
+          if (p.C3) {
+            const float4 w0 = load4<TO>(static_cast<const TO*>(p.W0) + ci);
+            float4 cur; cur.x = w0.x + w.x; cur.y = w0.y + w.y; cur.z = w0.z + w.z; cur.w = w0.w + w.w;
+            store4<TO>(static_cast<TO*>(p.C3) + ci, cur);
           }
-        } else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int col = cbase + j * 16;
-            if (col >= p.N) continue;
-            const float v = acc[i][j][e];
-            const int64_t ci = (int64_t)row * p.ldc + col;
-            if constexpr (EPI == EPI_STORE) {
-              static_cast<TO*>(p.C)[ci] = from_f32<TO>(v);
-            } else if constexpr (EPI == EPI_RESID) {
-              static_cast<float*>(p.C)[ci] = p.R[(int64_t)row * p.ldr + col] + v;
-            } else if constexpr (EPI == EPI_GELU) {
-              static_cast<TO*>(p.C)[ci] = from_f32<TO>(v);
-              static_cast<TO*>(p.C2)[(int64_t)row * p.ldc2 + col] = from_f32<TO>(gelu_erf(v));
-            } else if constexpr (EPI == EPI_SGD) {
-              float* w = static_cast<float*>(p.C);
-              const float nw = w[ci] - p.alpha * v;
-              w[ci] = nw;
-              if (p.C2) static_cast<TO*>(p.C2)[(int64_t)row * p.ldc2 + col] = from_f32<TO>(nw);
-              if (p.C3)
-                static_cast<TO*>(p.C3)[ci] = from_f32<TO>(to_f32(static_cast<const TO*>(p.W0)[ci]) + nw);
-            } else if constexpr (EPI == EPI_CEGRAD) {
-              float g = 0.f;
-              if (row < p.n_tgt) {
-                g = __expf(v - p.lse[row]);
-                if (col == p.tgt[row]) g -= 1.f;
-                g *= p.alpha;
-              }
-              static_cast<TO*>(p.C)[ci] = from_f32<TO>(g);
-            }
+        } else if constexpr (EPI == EPI_CEGRAD) {
+          float4 gq = {0.f, 0.f, 0.f, 0.f};
+          if (row < p.n_tgt) {
+            const float l = p.lse[row];
+            const int t = p.tgt[row];
+            gq.x = __expf(v.x - l) - (col == t ? 1.f : 0.f);
+            gq.y = __expf(v.y - l) - (col + 1 == t ? 1.f : 0.f);
+            gq.z = __expf(v.z - l) - (col + 2 == t ? 1.f : 0.f);
+            gq.w = __expf(v.w - l) - (col + 3 == t ? 1.f : 0.f);
+            gq.x *= p.alpha; gq.y *= p.alpha; gq.z *= p.alpha; gq.w *= p.alpha;
           }
+          store4<TO>(static_cast<TO*>(p.C) + ci, gq);
         }
       }
     }
