@@ -225,6 +225,181 @@ __global__ __launch_bounds__(256) void swa_fwd_k(AttnParams p) {
   }
 }
 
+// ------------------------------------------- forward, 32x32 matrix cores
+// Each wave owns 32 queries.  Scores are formed transposed, Sᵀ[32 keys x 32
+// queries] = K·Qᵀ with the 32x32x16 step, so a lane holds 16 keys of one
+// query and the row max/sum need one cross-half exchange only.  Eight
+// consecutive accumulator values of a lane are exactly the k-slots of the
+// next P·V step (keys 16h..16h+15 of a 32-key block), so probabilities go
+// from accumulator to operand without leaving registers.  V is read from
+// its transposed ring copy ([H*hd][cap]), so both tiles are plain copies.
+template <typename T, int HD> struct Attn32 {
+  static constexpr int KS = HD / 16;              // 16-wide k steps of Qᵀ
+  static constexpr int HB = (HD + 31) / 32;       // 32-row blocks of Oᵀ
+  static constexpr int HDR = HB * 32;             // Vᵀ tile rows (zero beyond HD)
+  static constexpr int PAD = 16 / sizeof(T);
+  static constexpr int LSN = HD + PAD;            // K tile pitch  [key][hd]
+  static constexpr int LSV = TQ + PAD;            // Vᵀ tile pitch [hd][key]
+};
+
+template <typename T, int HD>
+__global__ __launch_bounds__(256) void swa_fwd32_k(AttnParams p) {
+  using C = Attn32<T, HD>;
+  constexpr int QT = 128;
+  __shared__ __attribute__((aligned(16))) T Ks[2][TQ * C::LSN];
+  __shared__ __attribute__((aligned(16))) T Vt[2][C::HDR * C::LSV];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hl = lane >> 5, ql = lane & 31;
+  const int h = blockIdx.y;
+  const int qs = blockIdx.x * QT;
+  const int d = p.H * HD;
+  const T* Q = static_cast<const T*>(p.q);
+  const T* KR = static_cast<const T*>(p.kring);
+  const T* VT = static_cast<const T*>(p.vtring) + (int64_t)h * HD * p.cap;
+
+  const int qrow = qs + wave * 32 + ql;
+  typename Frag<T>::type qf[C::KS];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks)
+    qf[ks] = g_frag8<T>(Q + (int64_t)qrow * p.ldq + h * HD + ks * 16 + 8 * hl, qrow < p.n);
+  float m = -INFINITY, l = 0.f;
+  f32x16 oacc[C::HB];
+#pragma unroll
+  for (int b = 0; b < C::HB; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[b][r] = 0.f;
+  const float sc = LOG2E / sqrtf((float)HD);
+
+  const int64_t first = p.pos0 + qs;
+  const int64_t last = p.pos0 + min(qs + QT, p.n) - 1;
+  int64_t lo = first - p.window + 1;
+  if (lo < 0) lo = 0;
+  const int64_t kt0 = (lo / TQ) * TQ;
+  const int ntile = (int)((last - kt0) / TQ) + 1;
+
+  // Whole tiles are copied (the ring rows exist for every slot); keys past
+  // the last query are masked by causality.
+  StagedRows<T, TQ, HD, C::LSN, 256> lk;
+  StagedRows<T, C::HDR, TQ, C::LSV, 256> lv;
+  {
+    const int64_t slot = kt0 % p.cap;
+    lk.load(KR + slot * d + h * HD, d, TQ, HD, tid);
+    lv.load(VT + slot, p.cap, HD, TQ, tid);
+    lk.store(Ks[0], tid);
+    lv.store(Vt[0], tid);
+  }
+  __syncthreads();
+
+  for (int it = 0; it < ntile; ++it) {
+    const int cur = it & 1;
+    const int64_t kt = kt0 + (int64_t)it * TQ;
+    if (it + 1 < ntile) {
+      const int64_t slot = (kt + TQ) % p.cap;
+      lk.load(KR + slot * d + h * HD, d, TQ, HD, tid);
+      lv.load(VT + slot, p.cap, HD, TQ, tid);
+    }
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks)
+        mma32x32x16(lds_frag8<T>(Ks[cur] + (kb * 32 + ql) * C::LSN + ks * 16 + 8 * hl), qf[ks], s[kb]);
+    }
+    const bool interior = (kt + TQ - 1 <= first) && (kt > last - p.window);
+    if (!interior) {
+      const int kq0 = (int)(kt - first) - (wave * 32 + ql);   // key - query of s[0][0]
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rel = kq0 + kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+          if (!(rel <= 0 && rel > -p.window)) s[kb][r] = -INFINITY;
+        }
+    }
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) tmax = fmaxf(tmax, fmaxf(s[kb][r], s[kb][r + 1]));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * sc;
+    // lazy rescaling (see the 16x16 kernel above): exact, rarely taken
+    const bool bump = tmax > m + 8.f;
+    if (__any(bump)) {
+      const float mn = bump ? tmax : m;
+      const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - mn);
+      l *= alpha;
+#pragma unroll
+      for (int b = 0; b < C::HB; ++b) oacc[b] *= alpha;
+      m = mn;
+    }
+    const float mref = (m == -INFINITY) ? 0.f : m;
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = fast_exp2(fmaf(s[kb][r], sc, -mref));
+        s[kb][r] = e;
+        rs += e;
+      }
+    l += rs + __shfl_xor(rs, 32, 64);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        float pv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pv[j] = s[kb][8 * hf + j];
+        const typename Frag<T>::type pf = pack8<T>(pv);
+        const int koff = kb * 32 + 16 * hf + 4 * hl;
+#pragma unroll
+        for (int b = 0; b < C::HB; ++b) {
+          const T* row = Vt[cur] + (b * 32 + ql) * C::LSV + koff;
+          mma32x32x16(lds_frag4x2<T>(row, row + 8), pf, oacc[b]);
+        }
+      }
+    if (it + 1 < ntile) {
+      lk.store(Ks[cur ^ 1], tid);
+      lv.store(Vt[cur ^ 1], tid);
+    }
+    __syncthreads();
+  }
+
+  if (qrow < p.n) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    T* O = static_cast<T*>(p.o) + (int64_t)qrow * p.ldo + h * HD;
+#pragma unroll
+    for (int b = 0; b < C::HB; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int c = b * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+        if (c < HD) O[c] = from_f32<T>(oacc[b][r] * inv);
+      }
+    if (p.lse && hl == 0) p.lse[(int64_t)h * p.n + qrow] = (m + log2f(l)) * LN2;
+  }
+}
+
+// Vᵀ ring copy: rows h*hd + i, column (position mod cap); one block per 64
+// positions of one head, transposed through LDS so both sides coalesce.
+template <typename T>
+__global__ __launch_bounds__(256) void ring_vt_k(const T* __restrict__ qkv, int n, int H, int hd,
+                                                 int64_t pos0, T* __restrict__ vt, int64_t cap) {
+  __shared__ T tile[64][128 + 2];
+  const int h = blockIdx.y, t0 = blockIdx.x * 64, tid = threadIdx.x;
+  const int d = H * hd;
+  for (int idx = tid; idx < 64 * hd; idx += 256) {
+    const int t = idx / hd, i = idx % hd;
+    tile[t][i] = (t0 + t < n) ? qkv[(int64_t)(t0 + t) * 3 * d + 2 * d + h * hd + i] : from_f32<T>(0.f);
+  }
+  __syncthreads();
+  for (int idx = tid; idx < hd * 64; idx += 256) {
+    const int i = idx / 64, t = idx % 64;
+    if (t0 + t < n) vt[(int64_t)(h * hd + i) * cap + (pos0 + t0 + t) % cap] = tile[t][i];
+  }
+}
+
 // ------------------------------------------------------------ backward dQ
 template <typename T, int HD>
 __global__ __launch_bounds__(256) void swa_bwd_dq_k(AttnParams p) {
@@ -404,14 +579,13 @@ template <typename T, template <typename, int> class K> struct HdDispatch;
 
 template <typename T>
 void fwd_t(const AttnParams& p, hipStream_t s) {
-  constexpr int QB = sizeof(T) == 2 ? 2 : 1;
-  dim3 grid((p.n + 64 * QB - 1) / (64 * QB), p.H);
+  dim3 grid((p.n + 127) / 128, p.H);
   switch (p.hd) {
-    case 16: hipLaunchKernelGGL((swa_fwd_k<T, 16, QB>), grid, dim3(256), 0, s, p); break;
-    case 32: hipLaunchKernelGGL((swa_fwd_k<T, 32, QB>), grid, dim3(256), 0, s, p); break;
-    case 64: hipLaunchKernelGGL((swa_fwd_k<T, 64, QB>), grid, dim3(256), 0, s, p); break;
-    case 96: hipLaunchKernelGGL((swa_fwd_k<T, 96, QB>), grid, dim3(256), 0, s, p); break;
-    case 128: hipLaunchKernelGGL((swa_fwd_k<T, 128, QB>), grid, dim3(256), 0, s, p); break;
+    case 16: hipLaunchKernelGGL((swa_fwd32_k<T, 16>), grid, dim3(256), 0, s, p); break;
+    case 32: hipLaunchKernelGGL((swa_fwd32_k<T, 32>), grid, dim3(256), 0, s, p); break;
+    case 64: hipLaunchKernelGGL((swa_fwd32_k<T, 64>), grid, dim3(256), 0, s, p); break;
+    case 96: hipLaunchKernelGGL((swa_fwd32_k<T, 96>), grid, dim3(256), 0, s, p); break;
+    case 128: hipLaunchKernelGGL((swa_fwd32_k<T, 128>), grid, dim3(256), 0, s, p); break;
     default: break;
   }
 }
@@ -434,6 +608,14 @@ void swa_fwd(const AttnParams& p, bool bf, hipStream_t s) {
   if (p.n <= 0) return;
   if (bf) fwd_t<bf16>(p, s); else fwd_t<float>(p, s);
 }
+void ring_write_vt(const void* qkv, int n, int H, int hd, int64_t pos0, void* vt, int64_t cap, bool bf,
+                   hipStream_t s) {
+  if (n <= 0) return;
+  dim3 grid((n + 63) / 64, H);
+  if (bf) hipLaunchKernelGGL(ring_vt_k<bf16>, grid, dim3(256), 0, s, (const bf16*)qkv, n, H, hd, pos0, (bf16*)vt, cap);
+  else hipLaunchKernelGGL(ring_vt_k<float>, grid, dim3(256), 0, s, (const float*)qkv, n, H, hd, pos0, (float*)vt, cap);
+}
+
 void swa_bwd(const AttnParams& p, bool bf, hipStream_t s) {
   if (p.n <= 0) return;
   if (bf) bwd_t<bf16>(p, s); else bwd_t<float>(p, s);

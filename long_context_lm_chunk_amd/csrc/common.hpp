@@ -35,6 +35,17 @@ DEVI void mma16x16x32(const f32x8& a, const f32x8& b, f32x4& c) {
   for (int j = 0; j < 8; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], c, 0, 0, 0);
 }
 
+// 32x32x16 step: lane l holds A[row l%32][kslot 8*(l/32)+j], B[kslot
+// 8*(l/32)+j][col l%32]; accumulator c[r] = C[8*(r/4) + 4*(l/32) + r%4][l%32].
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+DEVI void mma32x32x16(const bf16x8& a, const bf16x8& b, f32x16& c) {
+  c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+DEVI void mma32x32x16(const f32x8& a, const f32x8& b, f32x16& c) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[j], b[j], c, 0, 0, 0);
+}
+
 template <typename T> DEVI T from_f32(float x);
 template <> DEVI float from_f32<float>(float x) { return x; }
 template <> DEVI bf16 from_f32<bf16>(float x) { return static_cast<bf16>(x); }

@@ -132,7 +132,8 @@ __global__ void rope_qkv_k(const T* __restrict__ qkv, int n, int H, int hd, int6
 template <typename T>
 __global__ void rope_qkv_f32in_k(const float* __restrict__ qkv, int H, int hd, int64_t pos,
                                  const double* __restrict__ theta, T* __restrict__ qo,
-                                 T* __restrict__ kr, T* __restrict__ vr, int64_t cap) {
+                                 T* __restrict__ kr, T* __restrict__ vr, T* __restrict__ vt,
+                                 int64_t cap) {
   const int half = hd >> 1;
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= H * half) return;
@@ -149,6 +150,8 @@ __global__ void rope_qkv_f32in_k(const float* __restrict__ qkv, int H, int hd, i
   kr[slot * d + j2] = from_f32<T>(k2 * c + k1 * s);
   vr[slot * d + j1] = from_f32<T>(qkv[2 * d + j1]);
   vr[slot * d + j2] = from_f32<T>(qkv[2 * d + j2]);
+  vt[(int64_t)j1 * cap + slot] = from_f32<T>(qkv[2 * d + j1]);
+  vt[(int64_t)j2 * cap + slot] = from_f32<T>(qkv[2 * d + j2]);
 }
 
 // Transposed rotation of dQ and dK inside dqkv [n][3d].
@@ -361,10 +364,10 @@ void rope_qkv(const void* qkv, int n, int H, int hd, int64_t pos0, const double*
 }
 
 void rope_qkv_f32in(const float* qkv, int H, int hd, int64_t pos, const double* theta, void* q_out,
-                    void* kring, void* vring, int64_t cap, bool bf, hipStream_t s) {
+                    void* kring, void* vring, void* vtring, int64_t cap, bool bf, hipStream_t s) {
   const int total = H * (hd / 2);
-  TSEL(bf, hipLaunchKernelGGL(rope_qkv_f32in_k<bf16>, dim3(nblk(total, 256)), dim3(256), 0, s, qkv, H, hd, pos, theta, (bf16*)q_out, (bf16*)kring, (bf16*)vring, cap),
-       hipLaunchKernelGGL(rope_qkv_f32in_k<float>, dim3(nblk(total, 256)), dim3(256), 0, s, qkv, H, hd, pos, theta, (float*)q_out, (float*)kring, (float*)vring, cap));
+  TSEL(bf, hipLaunchKernelGGL(rope_qkv_f32in_k<bf16>, dim3(nblk(total, 256)), dim3(256), 0, s, qkv, H, hd, pos, theta, (bf16*)q_out, (bf16*)kring, (bf16*)vring, (bf16*)vtring, cap),
+       hipLaunchKernelGGL(rope_qkv_f32in_k<float>, dim3(nblk(total, 256)), dim3(256), 0, s, qkv, H, hd, pos, theta, (float*)q_out, (float*)kring, (float*)vring, (float*)vtring, cap));
 }
 
 void rope_bwd(void* dqkv, int n, int H, int hd, int64_t pos0, const double* theta, bool bf,

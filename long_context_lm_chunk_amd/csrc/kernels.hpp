@@ -62,6 +62,7 @@ struct AttnParams {
   const void* q = nullptr;   // [n][H*hd], row stride ldq
   int64_t ldq = 0;
   const void* kring = nullptr; const void* vring = nullptr;  // [cap][H*hd]
+  const void* vtring = nullptr;                               // [H*hd][cap] (V transposed)
   int64_t cap = 0;
   int n = 0, H = 0, hd = 0, window = 0;
   int64_t pos0 = 0;          // absolute position of query row 0
@@ -74,6 +75,9 @@ struct AttnParams {
   int64_t kmin = 0;          // smallest key position that receives dK/dV (chunk start)
 };
 void swa_fwd(const AttnParams& p, bool bf16, hipStream_t s);
+// V of positions [pos0, pos0+n) from qkv [n][3d] into the transposed ring
+void ring_write_vt(const void* qkv, int n, int H, int hd, int64_t pos0, void* vt, int64_t cap,
+                   bool bf16, hipStream_t s);
 void swa_bwd(const AttnParams& p, bool bf16, hipStream_t s);
 
 // ---- decode (decode.hip)
@@ -86,6 +90,6 @@ void swa_decode(const void* q, const void* kring, const void* vring, int64_t cap
                 int window, int64_t pos, void* o, float* ws, bool bf16, hipStream_t s);
 void argmax_tok(const float* logits, int V, int32_t* out_tok, int32_t* tok_hist, hipStream_t s);
 void rope_qkv_f32in(const float* qkv, int H, int hd, int64_t pos, const double* theta, void* q_out,
-                    void* kring, void* vring, int64_t cap, bool bf16, hipStream_t s);
+                    void* kring, void* vring, void* vtring, int64_t cap, bool bf16, hipStream_t s);
 
 }  // namespace ttt

@@ -94,6 +94,7 @@ struct Layer {
   void* wup = nullptr;   // [F2][d] (SwiGLU: gate/up interleaved in 16-row blocks)
   void* wdn = nullptr;   // [d][F]
   void* kring = nullptr; void* vring = nullptr;  // [cap][d]
+  void* vtring = nullptr;                          // [d][cap]: V transposed, read by the forward
   int64_t cap = 0;
 };
 
@@ -184,6 +185,7 @@ size_t layout(ttt_model* m, void* base) {
     ly.cap = (l <= m->f0) ? capA : capB;
     ly.kring = cv.take<void>((size_t)ly.cap * d * es);
     ly.vring = cv.take<void>((size_t)ly.cap * d * es);
+    ly.vtring = cv.take<void>((size_t)ly.cap * d * es);
   }
   m->fast.assign(m->q, FastLayer());
   for (int j = 0; j < m->q; ++j) {
@@ -353,8 +355,9 @@ int phase_a(ttt_model* m, const int32_t* tokens, int64_t B0, int nb, hipStream_t
     g.C = m->qkvA; g.ldc = 3 * d;
     int rc = run_gemm(m, g, true, true, EPI_STORE, false, s); if (rc) return rc;
     rope_qkv(m->qkvA, nb, m->H, m->hd, B0, m->theta, m->qA, ly.kring, ly.vring, ly.cap, bf, s);
+    ring_write_vt(m->qkvA, nb, m->H, m->hd, B0, ly.vtring, ly.cap, bf, s);
     AttnParams ap;
-    ap.q = m->qA; ap.ldq = d; ap.kring = ly.kring; ap.vring = ly.vring; ap.cap = ly.cap;
+    ap.q = m->qA; ap.ldq = d; ap.kring = ly.kring; ap.vring = ly.vring; ap.vtring = ly.vtring; ap.cap = ly.cap;
     ap.n = nb; ap.H = m->H; ap.hd = m->hd; ap.window = m->W; ap.pos0 = B0; ap.o = m->oA; ap.ldo = d;
     {
       Scope t(m, CLS_ATTN_FWD, s, 4.0 * d * pairs(B0, nb, m->W, 0, nullptr));
@@ -402,8 +405,9 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
       g.C = m->qkvB; g.ldc = 3 * d;
       rc = run_gemm(m, g, true, true, EPI_STORE, false, s); if (rc) return rc;
       rope_qkv(m->qkvB, n, m->H, m->hd, p0, m->theta, b.q, ly.kring, ly.vring, ly.cap, bf, s);
+      ring_write_vt(m->qkvB, n, m->H, m->hd, p0, ly.vtring, ly.cap, bf, s);
       AttnParams ap;
-      ap.q = b.q; ap.ldq = d; ap.kring = ly.kring; ap.vring = ly.vring; ap.cap = ly.cap;
+      ap.q = b.q; ap.ldq = d; ap.kring = ly.kring; ap.vring = ly.vring; ap.vtring = ly.vtring; ap.cap = ly.cap;
       ap.n = n; ap.H = m->H; ap.hd = m->hd; ap.window = m->W; ap.pos0 = p0; ap.o = b.o; ap.ldo = d;
       ap.lse = b.lse;
       {
@@ -541,6 +545,7 @@ int reset_state(ttt_model* m, hipStream_t s) {
     const int64_t n = ly.cap * d * (int64_t)m->es / 4;
     fill_f32(static_cast<float*>(ly.kring), n, 0.f, s);
     fill_f32(static_cast<float*>(ly.vring), n, 0.f, s);
+    fill_f32(static_cast<float*>(ly.vtring), n, 0.f, s);
   }
   fill_f32(reinterpret_cast<float*>(m->err), 1, 0.f, s);
   m->pos = 0;
@@ -704,7 +709,7 @@ int ttt_decode_step(ttt_model* m, int32_t* next_token, float* logits_out, float*
     const int j = l - m->f0;
     layernorm_fwd(m->xd, d, 1, d, eps, m->ad, d, nullptr, nullptr, bf, s);
     gemv(ly.wqkv, nullptr, 3 * d, d, m->ad, !bf, m->qkvd, nullptr, bf, s);
-    rope_qkv_f32in(m->qkvd, m->H, m->hd, p, m->theta, m->qd, ly.kring, ly.vring, ly.cap, bf, s);
+    rope_qkv_f32in(m->qkvd, m->H, m->hd, p, m->theta, m->qd, ly.kring, ly.vring, ly.vtring, ly.cap, bf, s);
     swa_decode(m->qd, ly.kring, ly.vring, ly.cap, m->H, m->hd, m->W, p, m->od, m->attn_ws, bf, s);
     gemv(ly.wo, nullptr, d, d, m->od, !bf, m->xd, m->xd, bf, s);
     if (j == 0)   // phase-B input of this position, for the decode-chunk update
