@@ -77,154 +77,6 @@ DEVI void row_frags(typename Frag<T>::type* f, const T* base, int64_t ld,
   }
 }
 
-// ------------------------------------------------------------------ forward
-// Each wave owns QB blocks of 16 queries, so every K / V^T fragment read
-// from LDS feeds QB matrix-core products; K/V tiles are double-buffered
-// (global reads for tile t+1 are in flight while tile t is consumed); only
-// tiles that straddle the band edges evaluate the mask.
-template <typename T, int HD, int QB>
-__global__ __launch_bounds__(256) void swa_fwd_k(AttnParams p) {
-  using C = AttnCfg<T, HD>;
-  constexpr int QW = 16 * QB;
-  constexpr int QT = 4 * QW;
-  __shared__ __attribute__((aligned(16))) T Ks[2][TQ * C::LSN];
-  __shared__ __attribute__((aligned(16))) T Vt[2][HD * C::LST];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int h = blockIdx.y;
-  const int qs = blockIdx.x * QT;
-  const int d = p.H * HD;
-  const T* Q = static_cast<const T*>(p.q);
-  const T* KR = static_cast<const T*>(p.kring);
-  const T* VR = static_cast<const T*>(p.vring);
-
-  typename Frag<T>::type qf[QB][C::KS];
-  float m[QB], l[QB];
-  f32x4 oacc[QB][C::HB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int row = qs + wave * QW + qb * 16 + (lane & 15);
-    row_frags<T, HD>(qf[qb], Q + (int64_t)row * p.ldq + h * HD, p.ldq, row < p.n, lane);
-    m[qb] = -INFINITY;
-    l[qb] = 0.f;
-#pragma unroll
-    for (int b = 0; b < C::HB; ++b) oacc[qb][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  const float sc = LOG2E / sqrtf((float)HD);
-
-  const int64_t first = p.pos0 + qs;
-  const int64_t last = p.pos0 + min(qs + QT, p.n) - 1;
-  int64_t lo = first - p.window + 1;
-  if (lo < 0) lo = 0;
-  const int64_t kt0 = (lo / TQ) * TQ;
-  const int ntile = (int)((last - kt0) / TQ) + 1;
-
-  StagedRows<T, TQ, C::HDP, C::LSN, 256> lk;
-  StagedTrans<T, TQ, HD, C::LST, 256> lv;
-  {
-    const int nv = (int)min<int64_t>(TQ, last - kt0 + 1);
-    const int64_t slot = kt0 % p.cap;
-    lk.load(KR + slot * d + h * HD, d, nv, HD, tid);
-    lv.load(VR + slot * d + h * HD, d, nv, HD, tid);
-    lk.store(Ks[0], tid);
-    lv.store(Vt[0], tid);
-  }
-  __syncthreads();
-
-  for (int it = 0; it < ntile; ++it) {
-    const int cur = it & 1;
-    const int64_t kt = kt0 + (int64_t)it * TQ;
-    if (it + 1 < ntile) {
-      const int64_t kn = kt + TQ;
-      const int nv = (int)min<int64_t>(TQ, last - kn + 1);
-      const int64_t slot = kn % p.cap;
-      lk.load(KR + slot * d + h * HD, d, nv, HD, tid);
-      lv.load(VR + slot * d + h * HD, d, nv, HD, tid);
-    }
-    const bool interior = (kt + TQ - 1 <= first) && (kt > last - p.window);
-    const int kq0 = (int)(kt - first);   // key offset relative to the first query
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      f32x4 s[4];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks)
-          mma16x16x32(nat_frag<T, HD>(Ks[cur], kb * 16 + (lane & 15), ks, lane), qf[qb][ks], s[kb]);
-      }
-      if (!interior) {
-        const int qoff = wave * QW + qb * 16 + (lane & 15);
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int rel = kq0 + kb * 16 + 4 * (lane >> 4) + i - qoff;   // key - query
-            if (!(rel <= 0 && rel > -p.window)) s[kb][i] = -INFINITY;
-          }
-      }
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-        tmax = fmaxf(fmaxf(tmax, fmaxf(s[kb][0], s[kb][1])), fmaxf(s[kb][2], s[kb][3]));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      tmax *= sc;   // scores enter the exponent as s * sc (log2 units)
-      // Lazy rescaling: the reference maximum only moves when the tile's
-      // maximum exceeds it by more than 8 (log2 units), so probabilities stay
-      // below 2^8 (harmless in fp32 sums and in bf16) and the accumulator
-      // rescale is skipped on almost every tile.  The result does not depend
-      // on the reference, so this is exact.
-      const bool bump = tmax > m[qb] + 8.f;
-      if (__any(bump)) {
-        const float mn = bump ? tmax : m[qb];
-        const float alpha = (m[qb] == -INFINITY) ? 0.f : fast_exp2(m[qb] - mn);
-        l[qb] *= alpha;
-#pragma unroll
-        for (int b = 0; b < C::HB; ++b) oacc[qb][b] *= alpha;
-        m[qb] = mn;
-      }
-      const float mref = (m[qb] == -INFINITY) ? 0.f : m[qb];
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float e = fast_exp2(fmaf(s[kb][i], sc, -mref));   // -inf -> 0
-          s[kb][i] = e;
-          rs += e;
-        }
-      rs += __shfl_xor(rs, 16, 64);
-      rs += __shfl_xor(rs, 32, 64);
-      l[qb] += rs;
-#pragma unroll
-      for (int pp = 0; pp < 2; ++pp) {
-        const typename Frag<T>::type pf = acc_frag<T>(s[2 * pp], s[2 * pp + 1]);
-#pragma unroll
-        for (int b = 0; b < C::HB; ++b)
-          mma16x16x32(tr_frag<T, HD>(Vt[cur], b * 16 + (lane & 15), pp, lane), pf, oacc[qb][b]);
-      }
-    }
-    if (it + 1 < ntile) {
-      lk.store(Ks[cur ^ 1], tid);
-      lv.store(Vt[cur ^ 1], tid);
-    }
-    __syncthreads();
-  }
-
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int row = qs + wave * QW + qb * 16 + (lane & 15);
-    if (row >= p.n) continue;
-    const float inv = l[qb] > 0.f ? 1.f / l[qb] : 0.f;
-    T* O = static_cast<T*>(p.o) + (int64_t)row * p.ldo + h * HD;
-#pragma unroll
-    for (int b = 0; b < C::HB; ++b)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) O[b * 16 + 4 * (lane >> 4) + i] = from_f32<T>(oacc[qb][b][i] * inv);
-    if (p.lse && (lane >> 4) == 0) p.lse[(int64_t)h * p.n + row] = (m[qb] + log2f(l[qb])) * LN2;
-  }
-}
-
 // ------------------------------------------- forward, 32x32 matrix cores
 // Each wave owns 32 queries.  Scores are formed transposed, Sᵀ[32 keys x 32
 // queries] = K·Qᵀ with the 32x32x16 step, so a lane holds 16 keys of one
@@ -243,7 +95,7 @@ template <typename T, int HD> struct Attn32 {
 };
 
 template <typename T, int HD>
-__global__ __launch_bounds__(256) void swa_fwd32_k(AttnParams p) {
+__global__ __launch_bounds__(256, 2) void swa_fwd32_k(AttnParams p) {
   using C = Attn32<T, HD>;
   constexpr int QT = 128;
   __shared__ __attribute__((aligned(16))) T Ks[2][TQ * C::LSN];
@@ -274,14 +126,19 @@ __global__ __launch_bounds__(256) void swa_fwd32_k(AttnParams p) {
   const int64_t last = p.pos0 + min(qs + QT, p.n) - 1;
   int64_t lo = first - p.window + 1;
   if (lo < 0) lo = 0;
-  const int64_t kt0 = (lo / TQ) * TQ;
-  const int ntile = (int)((last - kt0) / TQ) + 1;
+  // split z of gridDim.z takes a contiguous run of the key tiles
+  const int64_t ktA = (lo / TQ) * TQ;
+  const int nall = (int)((last - ktA) / TQ) + 1;
+  const int per = (nall + (int)gridDim.z - 1) / (int)gridDim.z;
+  const int tb = min(nall, (int)blockIdx.z * per), te = min(nall, tb + per);
+  const int64_t kt0 = ktA + (int64_t)tb * TQ;
+  const int ntile = te - tb;
 
   // Whole tiles are copied (the ring rows exist for every slot); keys past
   // the last query are masked by causality.
   StagedRows<T, TQ, HD, C::LSN, 256> lk;
   StagedRows<T, C::HDR, TQ, C::LSV, 256> lv;
-  {
+  if (ntile > 0) {
     const int64_t slot = kt0 % p.cap;
     lk.load(KR + slot * d + h * HD, d, TQ, HD, tid);
     lv.load(VT + slot, p.cap, HD, TQ, tid);
@@ -368,198 +225,306 @@ __global__ __launch_bounds__(256) void swa_fwd32_k(AttnParams p) {
   }
 
   if (qrow < p.n) {
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    T* O = static_cast<T*>(p.o) + (int64_t)qrow * p.ldo + h * HD;
+    if (gridDim.z == 1) {
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      T* O = static_cast<T*>(p.o) + (int64_t)qrow * p.ldo + h * HD;
 #pragma unroll
-    for (int b = 0; b < C::HB; ++b)
+      for (int b = 0; b < C::HB; ++b)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int c = b * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-        if (c < HD) O[c] = from_f32<T>(oacc[b][r] * inv);
+        for (int r = 0; r < 16; ++r) {
+          const int c = b * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+          if (c < HD) O[c] = from_f32<T>(oacc[b][r] * inv);
+        }
+      if (p.lse && hl == 0) p.lse[(int64_t)h * p.n + qrow] = (m + log2f(l)) * LN2;
+    } else {
+      // unnormalised partial of this key range, combined by swa_combine_k
+      float* O = p.part + ((int64_t)blockIdx.z * p.n + qrow) * d + h * HD;
+#pragma unroll
+      for (int b = 0; b < C::HB; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int c = b * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+          if (c < HD) O[c] = oacc[b][r];
+        }
+      if (hl == 0) {
+        float* ml = p.part_ml + ((int64_t)blockIdx.z * p.H + h) * p.n * 2;
+        ml[2 * qrow] = m;
+        ml[2 * qrow + 1] = l;
       }
-    if (p.lse && hl == 0) p.lse[(int64_t)h * p.n + qrow] = (m + log2f(l)) * LN2;
+    }
   }
 }
 
-// Vᵀ ring copy: rows h*hd + i, column (position mod cap); one block per 64
-// positions of one head, transposed through LDS so both sides coalesce.
+// Combine key-range partials: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
 template <typename T>
-__global__ __launch_bounds__(256) void ring_vt_k(const T* __restrict__ qkv, int n, int H, int hd,
-                                                 int64_t pos0, T* __restrict__ vt, int64_t cap) {
+__global__ void swa_combine_k(AttnParams p, int nsplit) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;   // over n * H * hd
+  const int d = p.H * p.hd;
+  if (idx >= p.n * d) return;
+  const int row = idx / d, c = idx % d, h = c / p.hd;
+  float M = -INFINITY;
+  for (int z = 0; z < nsplit; ++z) M = fmaxf(M, p.part_ml[(((int64_t)z * p.H + h) * p.n + row) * 2]);
+  float L = 0.f, acc = 0.f;
+  for (int z = 0; z < nsplit; ++z) {
+    const float* ml = p.part_ml + (((int64_t)z * p.H + h) * p.n + row) * 2;
+    const float f = (ml[0] == -INFINITY) ? 0.f : fast_exp2(ml[0] - M);
+    L += ml[1] * f;
+    acc += p.part[((int64_t)z * p.n + row) * d + c] * f;
+  }
+  static_cast<T*>(p.o)[(int64_t)row * p.ldo + c] = from_f32<T>(L > 0.f ? acc / L : 0.f);
+  if (p.lse && c % p.hd == 0) p.lse[(int64_t)h * p.n + row] = (M + log2f(L)) * LN2;
+}
+
+// Transposed ring copy: rows h*hd + i, column (position mod cap); one block
+// per 64 positions of one head, transposed through LDS so both sides
+// coalesce.  The source row of position t is src + t*ld (linear) or, for a
+// ring source (src_cap > 0), src + ((pos0 + t) mod src_cap) * ld.
+template <typename T>
+__global__ __launch_bounds__(256) void ring_tr_k(const T* __restrict__ src, int64_t ld, int64_t src_cap,
+                                                 int n, int H, int hd, int64_t pos0, T* __restrict__ dst,
+                                                 int64_t cap) {
   __shared__ T tile[64][128 + 2];
   const int h = blockIdx.y, t0 = blockIdx.x * 64, tid = threadIdx.x;
-  const int d = H * hd;
   for (int idx = tid; idx < 64 * hd; idx += 256) {
     const int t = idx / hd, i = idx % hd;
-    tile[t][i] = (t0 + t < n) ? qkv[(int64_t)(t0 + t) * 3 * d + 2 * d + h * hd + i] : from_f32<T>(0.f);
+    T v = from_f32<T>(0.f);
+    if (t0 + t < n) {
+      const int64_t r = src_cap > 0 ? (pos0 + t0 + t) % src_cap : (int64_t)(t0 + t);
+      v = src[r * ld + h * hd + i];
+    }
+    tile[t][i] = v;
   }
   __syncthreads();
   for (int idx = tid; idx < hd * 64; idx += 256) {
     const int i = idx / 64, t = idx % 64;
-    if (t0 + t < n) vt[(int64_t)(h * hd + i) * cap + (pos0 + t0 + t) % cap] = tile[t][i];
+    if (t0 + t < n) dst[(int64_t)(h * hd + i) * cap + (pos0 + t0 + t) % cap] = tile[t][i];
   }
 }
 
 // ------------------------------------------------------------ backward dQ
+// dQ = scale * sum_keys dS K with dS = P (dP - D), P = exp(S - LSE),
+// dP = dO Vᵀ, over every key of the window (cached keys included).  Lanes
+// own queries as in the forward; Sᵀ and dPᵀ come from K and V tiles, the dQᵀ
+// product from the transposed K ring copy.  Single-buffered tiles; two
+// workgroups share a CU.
 template <typename T, int HD>
-__global__ __launch_bounds__(256) void swa_bwd_dq_k(AttnParams p) {
-  using C = AttnCfg<T, HD>;
+__global__ __launch_bounds__(256, 2) void swa_bwd_dq32_k(AttnParams p) {
+  using C = Attn32<T, HD>;
+  constexpr int QT = 128;
   __shared__ __attribute__((aligned(16))) T Ks[TQ * C::LSN];
   __shared__ __attribute__((aligned(16))) T Vs[TQ * C::LSN];
-  __shared__ __attribute__((aligned(16))) T Kt[HD * C::LST];
+  __shared__ __attribute__((aligned(16))) T Kt[C::HDR * C::LSV];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hl = lane >> 5, ql = lane & 31;
   const int h = blockIdx.y;
-  const int qs = blockIdx.x * TQ;
+  const int qs = blockIdx.x * QT;
   const int d = p.H * HD;
   const T* KR = static_cast<const T*>(p.kring);
   const T* VR = static_cast<const T*>(p.vring);
+  const T* KT = static_cast<const T*>(p.ktring) + (int64_t)h * HD * p.cap;
 
-  const int qrow = qs + wave * 16 + (lane & 15);
+  const int qrow = qs + wave * 32 + ql;
   const bool qok = qrow < p.n;
-  const int64_t qpos = p.pos0 + qrow;
   typename Frag<T>::type qf[C::KS], gf[C::KS];
-  row_frags<T, HD>(qf, static_cast<const T*>(p.q) + (int64_t)qrow * p.ldq + h * HD, p.ldq, qok, lane);
-  row_frags<T, HD>(gf, static_cast<const T*>(p.dout) + (int64_t)qrow * p.lddo + h * HD, p.lddo, qok, lane);
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) {
+    qf[ks] = g_frag8<T>(static_cast<const T*>(p.q) + (int64_t)qrow * p.ldq + h * HD + ks * 16 + 8 * hl, qok);
+    gf[ks] = g_frag8<T>(static_cast<const T*>(p.dout) + (int64_t)qrow * p.lddo + h * HD + ks * 16 + 8 * hl, qok);
+  }
   const float lse2 = qok ? p.lse[(int64_t)h * p.n + qrow] * LOG2E : 0.f;
   const float Dq = qok ? p.D[(int64_t)h * p.n + qrow] : 0.f;
   const float sc = LOG2E / sqrtf((float)HD);
-
-  f32x4 dacc[C::HB];
+  f32x16 dacc[C::HB];
 #pragma unroll
-  for (int b = 0; b < C::HB; ++b) dacc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int b = 0; b < C::HB; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dacc[b][r] = 0.f;
 
   const int64_t first = p.pos0 + qs;
-  const int64_t last = p.pos0 + min(qs + TQ, p.n) - 1;
+  const int64_t last = p.pos0 + min(qs + QT, p.n) - 1;
   int64_t lo = first - p.window + 1;
   if (lo < 0) lo = 0;
-  for (int64_t kt = (lo / TQ) * TQ; kt <= last; kt += TQ) {
-    const int nvalid = (int)min<int64_t>(TQ, last - kt + 1);
+  const int64_t ktA = (lo / TQ) * TQ;
+  const int nall = (int)((last - ktA) / TQ) + 1;
+  const int per = (nall + (int)gridDim.z - 1) / (int)gridDim.z;
+  const int tb = min(nall, (int)blockIdx.z * per), te = min(nall, tb + per);
+  for (int it = tb; it < te; ++it) {
+    const int64_t kt = ktA + (int64_t)it * TQ;
     const int64_t slot = kt % p.cap;
     __syncthreads();
-    load_nat<T, HD>(Ks, KR + slot * d + h * HD, d, nvalid, tid);
-    load_nat<T, HD>(Vs, VR + slot * d + h * HD, d, nvalid, tid);
-    load_tr<T, HD>(Kt, KR + slot * d + h * HD, d, nvalid, tid);
+    tile_copy_rows<T, TQ, HD, C::LSN, 256>(Ks, KR + slot * d + h * HD, d, TQ, HD, tid);
+    tile_copy_rows<T, TQ, HD, C::LSN, 256>(Vs, VR + slot * d + h * HD, d, TQ, HD, tid);
+    tile_copy_rows<T, C::HDR, TQ, C::LSV, 256>(Kt, KT + slot, p.cap, HD, TQ, tid);
     __syncthreads();
-
-    f32x4 s[4], dp[4];
+    f32x16 s[2], dp[2];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      dp[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) { s[kb][r] = 0.f; dp[kb][r] = 0.f; }
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
-        mma16x16x32(nat_frag<T, HD>(Ks, kb * 16 + (lane & 15), ks, lane), qf[ks], s[kb]);
-        mma16x16x32(nat_frag<T, HD>(Vs, kb * 16 + (lane & 15), ks, lane), gf[ks], dp[kb]);
+        mma32x32x16(lds_frag8<T>(Ks + (kb * 32 + ql) * C::LSN + ks * 16 + 8 * hl), qf[ks], s[kb]);
+        mma32x32x16(lds_frag8<T>(Vs + (kb * 32 + ql) * C::LSN + ks * 16 + 8 * hl), gf[ks], dp[kb]);
       }
     }
+    const bool interior = (kt + TQ - 1 <= first) && (kt > last - p.window);
+    const int kq0 = (int)(kt - first) - (wave * 32 + ql);
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t kp = kt + kb * 16 + 4 * (lane >> 4) + i;
-        const bool ok = qok && kp <= qpos && kp > qpos - p.window;
-        const float pr = ok ? fast_exp2(fmaf(s[kb][i], sc, -lse2)) : 0.f;
-        s[kb][i] = pr * (dp[kb][i] - Dq);   // dS^T
+      for (int r = 0; r < 16; ++r) {
+        const int rel = kq0 + kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+        const bool ok = qok && (interior || (rel <= 0 && rel > -p.window));
+        const float pr = ok ? fast_exp2(fmaf(s[kb][r], sc, -lse2)) : 0.f;
+        s[kb][r] = pr * (dp[kb][r] - Dq);   // dSᵀ
       }
 #pragma unroll
-    for (int pp = 0; pp < 2; ++pp) {
-      const typename Frag<T>::type df = acc_frag<T>(s[2 * pp], s[2 * pp + 1]);
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int b = 0; b < C::HB; ++b)
-        mma16x16x32(tr_frag<T, HD>(Kt, b * 16 + (lane & 15), pp, lane), df, dacc[b]);
-    }
+      for (int hf = 0; hf < 2; ++hf) {
+        float dv8[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dv8[j] = s[kb][8 * hf + j];
+        const typename Frag<T>::type df = pack8<T>(dv8);
+        const int koff = kb * 32 + 16 * hf + 4 * hl;
+#pragma unroll
+        for (int b = 0; b < C::HB; ++b) {
+          const T* row = Kt + (b * 32 + ql) * C::LSV + koff;
+          mma32x32x16(lds_frag4x2<T>(row, row + 8), df, dacc[b]);
+        }
+      }
   }
   if (qok) {
     const float scale = 1.f / sqrtf((float)HD);
-    T* G = static_cast<T*>(p.dq) + (int64_t)qrow * p.ldg + h * HD;
+    if (gridDim.z == 1) {
+      T* G = static_cast<T*>(p.dq) + (int64_t)qrow * p.ldg + h * HD;
 #pragma unroll
-    for (int b = 0; b < C::HB; ++b)
+      for (int b = 0; b < C::HB; ++b)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) G[b * 16 + 4 * (lane >> 4) + i] = from_f32<T>(dacc[b][i] * scale);
+        for (int r = 0; r < 16; ++r) {
+          const int c = b * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+          if (c < HD) G[c] = from_f32<T>(dacc[b][r] * scale);
+        }
+    } else {
+      float* G = p.part + ((int64_t)blockIdx.z * p.n + qrow) * d + h * HD;
+#pragma unroll
+      for (int b = 0; b < C::HB; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int c = b * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+          if (c < HD) G[c] = dacc[b][r] * scale;
+        }
+    }
   }
 }
 
+template <typename T>
+__global__ void dq_combine_k(AttnParams p, int nsplit) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  const int d = p.H * p.hd;
+  if (idx >= p.n * d) return;
+  const int row = idx / d, c = idx % d;
+  float acc = 0.f;
+  for (int z = 0; z < nsplit; ++z) acc += p.part[((int64_t)z * p.n + row) * d + c];
+  static_cast<T*>(p.dq)[(int64_t)row * p.ldg + c] = from_f32<T>(acc);
+}
+
 // --------------------------------------------------------- backward dK, dV
-// Keys are the in-chunk positions (query rows of this chunk); cached keys
-// of earlier chunks are constants and receive no gradient.
+// Keys are the in-chunk positions; cached keys of earlier chunks are
+// constants and receive no gradient.  Each wave owns 32 keys (lane = key);
+// per 64-query tile: S = Q Kᵀ, dP = dO Vᵀ, then dVᵀ += dOᵀ P and dKᵀ += Qᵀ dS
+// with the probabilities fed from the accumulators.
 template <typename T, int HD>
-__global__ __launch_bounds__(256) void swa_bwd_dkdv_k(AttnParams p) {
-  using C = AttnCfg<T, HD>;
+__global__ __launch_bounds__(256) void swa_bwd_dkdv32_k(AttnParams p) {
+  using C = Attn32<T, HD>;
+  constexpr int KT_ = 128;
   __shared__ __attribute__((aligned(16))) T Qs[TQ * C::LSN];
   __shared__ __attribute__((aligned(16))) T Gs[TQ * C::LSN];
-  __shared__ __attribute__((aligned(16))) T Qt[HD * C::LST];
-  __shared__ __attribute__((aligned(16))) T Gt[HD * C::LST];
+  __shared__ __attribute__((aligned(16))) T Qt[C::HDR * C::LSV];
+  __shared__ __attribute__((aligned(16))) T Gt[C::HDR * C::LSV];
   __shared__ float lse_s[TQ], D_s[TQ];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hl = lane >> 5, ql = lane & 31;
   const int h = blockIdx.y;
-  const int ks0 = blockIdx.x * TQ;
+  const int ks0 = blockIdx.x * KT_;
   const int d = p.H * HD;
   const T* Q = static_cast<const T*>(p.q);
   const T* G = static_cast<const T*>(p.dout);
   const T* KR = static_cast<const T*>(p.kring);
   const T* VR = static_cast<const T*>(p.vring);
 
-  const int krow = ks0 + wave * 16 + (lane & 15);     // chunk-relative key index
+  const int krow = ks0 + wave * 32 + ql;
   const bool kok = krow < p.n;
   const int64_t kpos = p.pos0 + krow;
   const int64_t kslot = (kok ? kpos : p.pos0) % p.cap;
   typename Frag<T>::type kf[C::KS], vf[C::KS];
-  row_frags<T, HD>(kf, KR + kslot * d + h * HD, d, kok, lane);
-  row_frags<T, HD>(vf, VR + kslot * d + h * HD, d, kok, lane);
-  const float sc = LOG2E / sqrtf((float)HD);
-
-  f32x4 dk[C::HB], dv[C::HB];
 #pragma unroll
-  for (int b = 0; b < C::HB; ++b) { dk[b] = f32x4{0.f, 0.f, 0.f, 0.f}; dv[b] = f32x4{0.f, 0.f, 0.f, 0.f}; }
+  for (int ks = 0; ks < C::KS; ++ks) {
+    kf[ks] = g_frag8<T>(KR + kslot * d + h * HD + ks * 16 + 8 * hl, kok);
+    vf[ks] = g_frag8<T>(VR + kslot * d + h * HD + ks * 16 + 8 * hl, kok);
+  }
+  const float sc = LOG2E / sqrtf((float)HD);
+  f32x16 dk[C::HB], dv[C::HB];
+#pragma unroll
+  for (int b = 0; b < C::HB; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { dk[b][r] = 0.f; dv[b][r] = 0.f; }
 
-  const int kmax = min(ks0 + TQ, p.n) - 1;
+  const int kmax = min(ks0 + KT_, p.n) - 1;
   const int64_t qend = min<int64_t>((int64_t)p.n - 1, (int64_t)kmax + p.window - 1);
-  for (int qt = ks0; qt <= qend; qt += TQ) {
+  for (int qt = (ks0 / TQ) * TQ; qt <= qend; qt += TQ) {
     const int nvalid = min(TQ, p.n - qt);
     __syncthreads();
-    load_nat<T, HD>(Qs, Q + (int64_t)qt * p.ldq + h * HD, p.ldq, nvalid, tid);
-    load_nat<T, HD>(Gs, G + (int64_t)qt * p.lddo + h * HD, p.lddo, nvalid, tid);
-    load_tr<T, HD>(Qt, Q + (int64_t)qt * p.ldq + h * HD, p.ldq, nvalid, tid);
-    load_tr<T, HD>(Gt, G + (int64_t)qt * p.lddo + h * HD, p.lddo, nvalid, tid);
+    tile_copy_rows<T, TQ, HD, C::LSN, 256>(Qs, Q + (int64_t)qt * p.ldq + h * HD, p.ldq, nvalid, HD, tid);
+    tile_copy_rows<T, TQ, HD, C::LSN, 256>(Gs, G + (int64_t)qt * p.lddo + h * HD, p.lddo, nvalid, HD, tid);
+    tile_copy_transpose<T, TQ, HD, C::LSV, 256>(Qt, Q + (int64_t)qt * p.ldq + h * HD, p.ldq, nvalid, HD, tid);
+    tile_copy_transpose<T, TQ, HD, C::LSV, 256>(Gt, G + (int64_t)qt * p.lddo + h * HD, p.lddo, nvalid, HD, tid);
     if (tid < TQ) {
       const bool ok = tid < nvalid;
       lse_s[tid] = ok ? p.lse[(int64_t)h * p.n + qt + tid] * LOG2E : 0.f;
       D_s[tid] = ok ? p.D[(int64_t)h * p.n + qt + tid] : 0.f;
     }
     __syncthreads();
-
-    f32x4 s[4], dp[4];
+    f32x16 s[2], dp[2];
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
-      s[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      dp[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) { s[qb][r] = 0.f; dp[qb][r] = 0.f; }
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
-        mma16x16x32(nat_frag<T, HD>(Qs, qb * 16 + (lane & 15), ks, lane), kf[ks], s[qb]);
-        mma16x16x32(nat_frag<T, HD>(Gs, qb * 16 + (lane & 15), ks, lane), vf[ks], dp[qb]);
+        mma32x32x16(lds_frag8<T>(Qs + (qb * 32 + ql) * C::LSN + ks * 16 + 8 * hl), kf[ks], s[qb]);
+        mma32x32x16(lds_frag8<T>(Gs + (qb * 32 + ql) * C::LSN + ks * 16 + 8 * hl), vf[ks], dp[qb]);
       }
     }
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb)
+    for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int qi = qb * 16 + 4 * (lane >> 4) + i;
+      for (int r = 0; r < 16; ++r) {
+        const int qi = qb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
         const int64_t qp = p.pos0 + qt + qi;
         const bool ok = kok && (qt + qi < p.n) && kpos <= qp && kpos > qp - p.window;
-        const float pr = ok ? fast_exp2(fmaf(s[qb][i], sc, -lse_s[qi])) : 0.f;
-        s[qb][i] = pr;                              // P
-        dp[qb][i] = pr * (dp[qb][i] - D_s[qi]);     // dS
+        const float pr = ok ? fast_exp2(fmaf(s[qb][r], sc, -lse_s[qi])) : 0.f;
+        s[qb][r] = pr;                                 // P
+        dp[qb][r] = pr * (dp[qb][r] - D_s[qi]);        // dS
       }
 #pragma unroll
-    for (int pp = 0; pp < 2; ++pp) {
-      const typename Frag<T>::type pf = acc_frag<T>(s[2 * pp], s[2 * pp + 1]);
-      const typename Frag<T>::type df = acc_frag<T>(dp[2 * pp], dp[2 * pp + 1]);
+    for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int b = 0; b < C::HB; ++b) {
-        mma16x16x32(tr_frag<T, HD>(Gt, b * 16 + (lane & 15), pp, lane), pf, dv[b]);
-        mma16x16x32(tr_frag<T, HD>(Qt, b * 16 + (lane & 15), pp, lane), df, dk[b]);
+      for (int hf = 0; hf < 2; ++hf) {
+        float a8[8], b8[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) { a8[j] = s[qb][8 * hf + j]; b8[j] = dp[qb][8 * hf + j]; }
+        const typename Frag<T>::type pf = pack8<T>(a8);
+        const typename Frag<T>::type df = pack8<T>(b8);
+        const int qoff = qb * 32 + 16 * hf + 4 * hl;
+#pragma unroll
+        for (int b = 0; b < C::HB; ++b) {
+          const T* grow = Gt + (b * 32 + ql) * C::LSV + qoff;
+          const T* qrow_ = Qt + (b * 32 + ql) * C::LSV + qoff;
+          mma32x32x16(lds_frag4x2<T>(grow, grow + 8), pf, dv[b]);
+          mma32x32x16(lds_frag4x2<T>(qrow_, qrow_ + 8), df, dk[b]);
+        }
       }
-    }
   }
   if (kok) {
     const float scale = 1.f / sqrtf((float)HD);
@@ -568,37 +533,57 @@ __global__ __launch_bounds__(256) void swa_bwd_dkdv_k(AttnParams p) {
 #pragma unroll
     for (int b = 0; b < C::HB; ++b)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        DK[b * 16 + 4 * (lane >> 4) + i] = from_f32<T>(dk[b][i] * scale);
-        DV[b * 16 + 4 * (lane >> 4) + i] = from_f32<T>(dv[b][i]);
+      for (int r = 0; r < 16; ++r) {
+        const int c = b * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+        if (c < HD) {
+          DK[c] = from_f32<T>(dk[b][r] * scale);
+          DV[c] = from_f32<T>(dv[b][r]);
+        }
       }
   }
 }
 
-template <typename T, template <typename, int> class K> struct HdDispatch;
+// Key-range splits for launches too small to fill the GPU (the per-chunk
+// calls): aim at ~2 workgroups per CU when a partial buffer is provided.
+inline int pick_split(const AttnParams& p, int wgs) {
+  if (!p.part || !p.part_ml) return 1;
+  int z = (512 + wgs - 1) / wgs;
+  return z < 1 ? 1 : (z > p.max_split ? p.max_split : z);
+}
 
 template <typename T>
 void fwd_t(const AttnParams& p, hipStream_t s) {
-  dim3 grid((p.n + 127) / 128, p.H);
+  const int nz = pick_split(p, ((p.n + 127) / 128) * p.H);
+  dim3 grid((p.n + 127) / 128, p.H, nz);
   switch (p.hd) {
     case 16: hipLaunchKernelGGL((swa_fwd32_k<T, 16>), grid, dim3(256), 0, s, p); break;
     case 32: hipLaunchKernelGGL((swa_fwd32_k<T, 32>), grid, dim3(256), 0, s, p); break;
     case 64: hipLaunchKernelGGL((swa_fwd32_k<T, 64>), grid, dim3(256), 0, s, p); break;
     case 96: hipLaunchKernelGGL((swa_fwd32_k<T, 96>), grid, dim3(256), 0, s, p); break;
     case 128: hipLaunchKernelGGL((swa_fwd32_k<T, 128>), grid, dim3(256), 0, s, p); break;
-    default: break;
+    default: return;
+  }
+  if (nz > 1) {
+    const int tot = p.n * p.H * p.hd;
+    hipLaunchKernelGGL(swa_combine_k<T>, dim3((tot + 255) / 256), dim3(256), 0, s, p, nz);
   }
 }
 template <typename T>
 void bwd_t(const AttnParams& p, hipStream_t s) {
-  dim3 grid((p.n + TQ - 1) / TQ, p.H);
+  const int nz = pick_split(p, ((p.n + 127) / 128) * p.H);
+  dim3 gq((p.n + 127) / 128, p.H, nz);
+  dim3 gk((p.n + 127) / 128, p.H);
   switch (p.hd) {
 #define CASE(HDV) case HDV: \
-    hipLaunchKernelGGL((swa_bwd_dq_k<T, HDV>), grid, dim3(256), 0, s, p); \
-    hipLaunchKernelGGL((swa_bwd_dkdv_k<T, HDV>), grid, dim3(256), 0, s, p); break;
+    hipLaunchKernelGGL((swa_bwd_dq32_k<T, HDV>), gq, dim3(256), 0, s, p); \
+    hipLaunchKernelGGL((swa_bwd_dkdv32_k<T, HDV>), gk, dim3(256), 0, s, p); break;
     CASE(16) CASE(32) CASE(64) CASE(96) CASE(128)
 #undef CASE
-    default: break;
+    default: return;
+  }
+  if (nz > 1) {
+    const int tot = p.n * p.H * p.hd;
+    hipLaunchKernelGGL(dq_combine_k<T>, dim3((tot + 255) / 256), dim3(256), 0, s, p, nz);
   }
 }
 
@@ -608,12 +593,12 @@ void swa_fwd(const AttnParams& p, bool bf, hipStream_t s) {
   if (p.n <= 0) return;
   if (bf) fwd_t<bf16>(p, s); else fwd_t<float>(p, s);
 }
-void ring_write_vt(const void* qkv, int n, int H, int hd, int64_t pos0, void* vt, int64_t cap, bool bf,
-                   hipStream_t s) {
+void ring_transpose(const void* src, int64_t ld, int64_t src_cap, int n, int H, int hd, int64_t pos0,
+                    void* dst, int64_t cap, bool bf, hipStream_t s) {
   if (n <= 0) return;
   dim3 grid((n + 63) / 64, H);
-  if (bf) hipLaunchKernelGGL(ring_vt_k<bf16>, grid, dim3(256), 0, s, (const bf16*)qkv, n, H, hd, pos0, (bf16*)vt, cap);
-  else hipLaunchKernelGGL(ring_vt_k<float>, grid, dim3(256), 0, s, (const float*)qkv, n, H, hd, pos0, (float*)vt, cap);
+  if (bf) hipLaunchKernelGGL(ring_tr_k<bf16>, grid, dim3(256), 0, s, (const bf16*)src, ld, src_cap, n, H, hd, pos0, (bf16*)dst, cap);
+  else hipLaunchKernelGGL(ring_tr_k<float>, grid, dim3(256), 0, s, (const float*)src, ld, src_cap, n, H, hd, pos0, (float*)dst, cap);
 }
 
 void swa_bwd(const AttnParams& p, bool bf, hipStream_t s) {

@@ -63,6 +63,7 @@ struct AttnParams {
   int64_t ldq = 0;
   const void* kring = nullptr; const void* vring = nullptr;  // [cap][H*hd]
   const void* vtring = nullptr;                               // [H*hd][cap] (V transposed)
+  const void* ktring = nullptr;                               // [H*hd][cap] (K transposed)
   int64_t cap = 0;
   int n = 0, H = 0, hd = 0, window = 0;
   int64_t pos0 = 0;          // absolute position of query row 0
@@ -73,11 +74,15 @@ struct AttnParams {
   const float* D = nullptr;  // [H][n] rowsum(dO*O)
   void* dq = nullptr; void* dk = nullptr; void* dv = nullptr; int64_t ldg = 0;
   int64_t kmin = 0;          // smallest key position that receives dK/dV (chunk start)
+  // key-range split scratch (optional): part [max_split][n][H*hd] fp32,
+  // part_ml [max_split][H][n][2]
+  float* part = nullptr; float* part_ml = nullptr; int max_split = 1;
 };
 void swa_fwd(const AttnParams& p, bool bf16, hipStream_t s);
-// V of positions [pos0, pos0+n) from qkv [n][3d] into the transposed ring
-void ring_write_vt(const void* qkv, int n, int H, int hd, int64_t pos0, void* vt, int64_t cap,
-                   bool bf16, hipStream_t s);
+// rows of positions [pos0, pos0+n) (src row t at src + t*ld, or at slot
+// (pos0+t) mod src_cap of a ring) into a transposed ring [H*hd][cap]
+void ring_transpose(const void* src, int64_t ld, int64_t src_cap, int n, int H, int hd, int64_t pos0,
+                    void* dst, int64_t cap, bool bf16, hipStream_t s);
 void swa_bwd(const AttnParams& p, bool bf16, hipStream_t s);
 
 // ---- decode (decode.hip)

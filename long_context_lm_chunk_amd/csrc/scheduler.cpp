@@ -47,6 +47,7 @@ int fail(int code, const std::string& msg) {
   } while (0)
 
 constexpr int NCLS = 8;
+constexpr int kMaxSplit = 4;   // key-range splits of the per-chunk attention launches
 
 struct Timing {
   bool on = false;
@@ -95,6 +96,7 @@ struct Layer {
   void* wdn = nullptr;   // [d][F]
   void* kring = nullptr; void* vring = nullptr;  // [cap][d]
   void* vtring = nullptr;                          // [d][cap]: V transposed, read by the forward
+  void* ktring = nullptr;                          // [d][cap]: K transposed (fast blocks: dQ)
   int64_t cap = 0;
 };
 
@@ -128,6 +130,7 @@ struct ttt_model {
   void* G = nullptr;
   float* dh = nullptr; void* dh_lo = nullptr; float* dact = nullptr; void* dz = nullptr;
   float* dtmp = nullptr; void* dout = nullptr; void* dqkv = nullptr; float* Dattn = nullptr;
+  float* attn_part = nullptr; float* attn_ml = nullptr;   // key-range split partials
   // decode
   float* xd = nullptr; void* ad = nullptr; float* qkvd = nullptr; void* qd = nullptr; void* od = nullptr;
   float* zd = nullptr; void* actd = nullptr; float* logits = nullptr; float* attn_ws = nullptr;
@@ -186,6 +189,7 @@ size_t layout(ttt_model* m, void* base) {
     ly.kring = cv.take<void>((size_t)ly.cap * d * es);
     ly.vring = cv.take<void>((size_t)ly.cap * d * es);
     ly.vtring = cv.take<void>((size_t)ly.cap * d * es);
+    ly.ktring = (l > m->f0) ? cv.take<void>((size_t)ly.cap * d * es) : nullptr;
   }
   m->fast.assign(m->q, FastLayer());
   for (int j = 0; j < m->q; ++j) {
@@ -250,6 +254,8 @@ size_t layout(ttt_model* m, void* base) {
   m->dout = cv.take<void>((size_t)C * d * es);
   m->dqkv = cv.take<void>((size_t)C * 3 * d * es);
   m->Dattn = cv.take<float>((size_t)H * C * 4);
+  m->attn_part = cv.take<float>((size_t)kMaxSplit * C * d * 4);
+  m->attn_ml = cv.take<float>((size_t)kMaxSplit * H * C * 2 * 4);
   // decode
   m->xd = cv.take<float>((size_t)d * 4);
   m->ad = cv.take<void>((size_t)d * es);
@@ -355,7 +361,8 @@ int phase_a(ttt_model* m, const int32_t* tokens, int64_t B0, int nb, hipStream_t
     g.C = m->qkvA; g.ldc = 3 * d;
     int rc = run_gemm(m, g, true, true, EPI_STORE, false, s); if (rc) return rc;
     rope_qkv(m->qkvA, nb, m->H, m->hd, B0, m->theta, m->qA, ly.kring, ly.vring, ly.cap, bf, s);
-    ring_write_vt(m->qkvA, nb, m->H, m->hd, B0, ly.vtring, ly.cap, bf, s);
+    ring_transpose(static_cast<char*>(m->qkvA) + (size_t)2 * d * m->es, 3 * d, 0, nb, m->H, m->hd, B0,
+                   ly.vtring, ly.cap, bf, s);
     AttnParams ap;
     ap.q = m->qA; ap.ldq = d; ap.kring = ly.kring; ap.vring = ly.vring; ap.vtring = ly.vtring; ap.cap = ly.cap;
     ap.n = nb; ap.H = m->H; ap.hd = m->hd; ap.window = m->W; ap.pos0 = B0; ap.o = m->oA; ap.ldo = d;
@@ -405,11 +412,14 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
       g.C = m->qkvB; g.ldc = 3 * d;
       rc = run_gemm(m, g, true, true, EPI_STORE, false, s); if (rc) return rc;
       rope_qkv(m->qkvB, n, m->H, m->hd, p0, m->theta, b.q, ly.kring, ly.vring, ly.cap, bf, s);
-      ring_write_vt(m->qkvB, n, m->H, m->hd, p0, ly.vtring, ly.cap, bf, s);
+      ring_transpose(static_cast<char*>(m->qkvB) + (size_t)2 * d * m->es, 3 * d, 0, n, m->H, m->hd, p0,
+                     ly.vtring, ly.cap, bf, s);
+      ring_transpose(ly.kring, d, ly.cap, n, m->H, m->hd, p0, ly.ktring, ly.cap, bf, s);
       AttnParams ap;
       ap.q = b.q; ap.ldq = d; ap.kring = ly.kring; ap.vring = ly.vring; ap.vtring = ly.vtring; ap.cap = ly.cap;
       ap.n = n; ap.H = m->H; ap.hd = m->hd; ap.window = m->W; ap.pos0 = p0; ap.o = b.o; ap.ldo = d;
       ap.lse = b.lse;
+      ap.part = m->attn_part; ap.part_ml = m->attn_ml; ap.max_split = kMaxSplit;
       {
         Scope t(m, CLS_ATTN_FWD, s, 4.0 * d * pairs(p0, n, m->W, 0, nullptr));
         swa_fwd(ap, bf, s);
@@ -499,6 +509,8 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
     ap.q = b.q; ap.ldq = d; ap.kring = ly.kring; ap.vring = ly.vring; ap.cap = ly.cap;
     ap.n = n; ap.H = m->H; ap.hd = m->hd; ap.window = m->W; ap.pos0 = p0;
     ap.lse = b.lse; ap.dout = m->dout; ap.lddo = d; ap.D = m->Dattn;
+    ap.ktring = ly.ktring;
+    ap.part = m->attn_part; ap.part_ml = m->attn_ml; ap.max_split = kMaxSplit;
     ap.dq = m->dqkv; ap.dk = static_cast<char*>(m->dqkv) + (size_t)d * m->es;
     ap.dv = static_cast<char*>(m->dqkv) + (size_t)2 * d * m->es; ap.ldg = 3 * d; ap.kmin = p0;
     {
@@ -546,6 +558,7 @@ int reset_state(ttt_model* m, hipStream_t s) {
     fill_f32(static_cast<float*>(ly.kring), n, 0.f, s);
     fill_f32(static_cast<float*>(ly.vring), n, 0.f, s);
     fill_f32(static_cast<float*>(ly.vtring), n, 0.f, s);
+    if (ly.ktring) fill_f32(static_cast<float*>(ly.ktring), n, 0.f, s);
   }
   fill_f32(reinterpret_cast<float*>(m->err), 1, 0.f, s);
   m->pos = 0;
