@@ -153,19 +153,28 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmParams p) {
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // With DUAL the reduction runs twice over K, against B then B2: the fast
-  // weights are applied as W0 + delta without rounding their sum.
+  // weights are applied as W0 + delta without rounding their sum.  With a
+  // split (gridDim.z > 1) this workgroup takes one contiguous run of the
+  // k-tiles and writes an fp32 partial for gemm_reduce_k.
   const int nk1 = (p.K + C::BK - 1) / C::BK;
-  const int nk = DUAL ? 2 * nk1 : nk1;
+  const int ntot = DUAL ? 2 * nk1 : nk1;
+  const int per = (ntot + (int)gridDim.z - 1) / (int)gridDim.z;
+  const int kt_begin = min(ntot, (int)blockIdx.z * per);
+  const int kt_end = min(ntot, kt_begin + per);
   const T* __restrict__ B2 = static_cast<const T*>(p.B2);
-  la.load(A, p.lda, m0, p.M, 0, p.K, tid);
-  lb.load(B, p.ldb, n0, p.N, 0, p.K, tid);
-  la.store(lds[0], tid);
-  lb.store(lds[0] + BM * C::LS, tid);
+  if (kt_begin < kt_end) {
+    const bool second = DUAL && kt_begin >= nk1;
+    const int k0 = (second ? kt_begin - nk1 : kt_begin) * C::BK;
+    la.load(A, p.lda, m0, p.M, k0, p.K, tid);
+    lb.load(second ? B2 : B, p.ldb, n0, p.N, k0, p.K, tid);
+    la.store(lds[0], tid);
+    lb.store(lds[0] + BM * C::LS, tid);
+  }
   __syncthreads();
 
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) {
+  for (int kt = kt_begin; kt < kt_end; ++kt) {
+    const int cur = (kt - kt_begin) & 1;
+    if (kt + 1 < kt_end) {
       const int nt = kt + 1;
       const bool second = DUAL && nt >= nk1;
       const int k0 = (second ? nt - nk1 : nt) * C::BK;
@@ -187,7 +196,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmParams p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) mma16x16x32(af[i], bfr[j], acc[i][j]);
     }
-    if (kt + 1 < nk) {
+    if (kt + 1 < kt_end) {
       la.store(lds[cur ^ 1], tid);
       lb.store(lds[cur ^ 1] + BM * C::LS, tid);
     }
@@ -255,6 +264,18 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmParams p) {
         for (int e = 0; e < 4; ++e)
           st[(wm * 64 + i * 16 + 4 * (lane >> 4) + e) * ES + wn * 64 + j * 16 + (lane & 15)] = acc[i][j][e];
     __syncthreads();
+    if (gridDim.z > 1) {
+      // split-K partial: slab z of [z][M][N] fp32
+      float* slab = p.split_ws + (int64_t)blockIdx.z * p.M * p.N;
+      for (int g = tid; g < BM * (BN / 4); g += NT) {
+        const int r = g / (BN / 4), c = (g % (BN / 4)) * 4;
+        const int row = m0 + r, col = n0 + c;
+        if (row >= p.M || col >= p.N) continue;
+        *reinterpret_cast<float4*>(slab + (int64_t)row * p.N + col) =
+            *reinterpret_cast<const float4*>(st + r * ES + c);
+      }
+      return;
+    }
     if constexpr (EPI == EPI_SWIGLU) {
       // columns: gate block 32c..32c+15, up block 32c+16..32c+31 -> act 16c..16c+15
       for (int g = tid; g < BM * (BN / 8); g += NT) {
@@ -317,11 +338,53 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmParams p) {
   }
 }
 
+// Sum of the split-K slabs in a fixed order (deterministic), then the
+// STORE or RESID epilogue.
+template <int EPI, typename TO>
+__global__ void gemm_reduce_k(GemmParams p, int nz) {
+  const int64_t g = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;   // 4-column groups
+  const int64_t total = (int64_t)p.M * (p.N / 4);
+  if (g >= total) return;
+  const int row = (int)(g / (p.N / 4)), col = (int)(g % (p.N / 4)) * 4;
+  float4 v = *reinterpret_cast<const float4*>(p.split_ws + (int64_t)row * p.N + col);
+  for (int z = 1; z < nz; ++z) {
+    const float4 w = *reinterpret_cast<const float4*>(p.split_ws + ((int64_t)z * p.M + row) * p.N + col);
+    v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
+  }
+  const int64_t ci = (int64_t)row * p.ldc + col;
+  if constexpr (EPI == EPI_RESID) {
+    const float4 r = *reinterpret_cast<const float4*>(p.R + (int64_t)row * p.ldr + col);
+    v.x += r.x; v.y += r.y; v.z += r.z; v.w += r.w;
+    *reinterpret_cast<float4*>(static_cast<float*>(p.C) + ci) = v;
+  } else {
+    store4<TO>(static_cast<TO*>(p.C) + ci, v);
+  }
+}
+
 template <typename T, bool AK, bool BK_, int EPI, typename TO>
 void launch_t(const GemmParams& p, hipStream_t s) {
-  dim3 grid((p.N + BN - 1) / BN, (p.M + BM - 1) / BM);
+  const int tiles = ((p.N + BN - 1) / BN) * ((p.M + BM - 1) / BM);
+  int nz = 1;
+  if constexpr (EPI == EPI_STORE || EPI == EPI_RESID) {
+    // Too few tiles to give every CU two workgroups, and a long reduction:
+    // split K so that ~2 workgroups per CU run, each with >= 8 k-tiles.
+    const int ktiles = ((p.K + GemmCfg<T>::BK - 1) / GemmCfg<T>::BK) * (p.B2 ? 2 : 1);
+    if (p.split_ws && tiles < 256 && ktiles >= 16) {
+      nz = (512 + tiles - 1) / tiles;
+      if (nz > ktiles / 8) nz = ktiles / 8;
+      if (nz > 4) nz = 4;
+      if ((int64_t)nz * p.M * p.N > p.split_cap || p.N % 4) nz = 1;
+    }
+  }
+  dim3 grid((p.N + BN - 1) / BN, (p.M + BM - 1) / BM, nz);
   if (p.B2) hipLaunchKernelGGL((gemm_kernel<T, AK, BK_, EPI, TO, true>), grid, dim3(NT), 0, s, p);
   else hipLaunchKernelGGL((gemm_kernel<T, AK, BK_, EPI, TO, false>), grid, dim3(NT), 0, s, p);
+  if constexpr (EPI == EPI_STORE || EPI == EPI_RESID) {
+    if (nz > 1) {
+      const int64_t groups = (int64_t)p.M * (p.N / 4);
+      hipLaunchKernelGGL((gemm_reduce_k<EPI, TO>), dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, s, p, nz);
+    }
+  }
 }
 
 template <typename T>

@@ -21,6 +21,9 @@ struct GemmParams {
   const int* tgt = nullptr; int n_tgt = 0;
   float* part_max = nullptr; float* part_sum = nullptr; int64_t ldpart = 0;
   float* tgt_logit = nullptr; const float* lse = nullptr;
+  // split-K scratch (optional; STORE/RESID launches with too few tiles):
+  // split_ws holds up to split_cap floats
+  float* split_ws = nullptr; int64_t split_cap = 0;
 };
 
 // Returns 0, or -1 for an epilogue/layout combination that is not built.

@@ -20,6 +20,7 @@
 // enqueues kernels on one stream and reads back an error flag.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -131,6 +132,7 @@ struct ttt_model {
   float* dh = nullptr; void* dh_lo = nullptr; float* dact = nullptr; void* dz = nullptr;
   float* dtmp = nullptr; void* dout = nullptr; void* dqkv = nullptr; float* Dattn = nullptr;
   float* attn_part = nullptr; float* attn_ml = nullptr;   // key-range split partials
+  float* split_ws = nullptr; int64_t split_cap = 0;         // split-K partials of the GEMMs
   // decode
   float* xd = nullptr; void* ad = nullptr; float* qkvd = nullptr; void* qd = nullptr; void* od = nullptr;
   float* zd = nullptr; void* actd = nullptr; float* logits = nullptr; float* attn_ws = nullptr;
@@ -256,6 +258,8 @@ size_t layout(ttt_model* m, void* base) {
   m->Dattn = cv.take<float>((size_t)H * C * 4);
   m->attn_part = cv.take<float>((size_t)kMaxSplit * C * d * 4);
   m->attn_ml = cv.take<float>((size_t)kMaxSplit * H * C * 2 * 4);
+  m->split_cap = (int64_t)4 * C * std::max(d, 3 * d);
+  m->split_ws = cv.take<float>((size_t)m->split_cap * 4);
   // decode
   m->xd = cv.take<float>((size_t)d * 4);
   m->ad = cv.take<void>((size_t)d * es);
@@ -315,8 +319,11 @@ struct Scope {
 
 enum { CLS_GEMM = 0, CLS_ATTN_FWD = 1, CLS_ATTN_BWD = 2, CLS_CE = 3, CLS_SGD = 4, CLS_MLP_UP = 5 };
 
-int run_gemm(ttt_model* m, const GemmParams& p, bool a_kc, bool b_kc, int epi, bool out_f32,
+int run_gemm(ttt_model* m, const GemmParams& p0, bool a_kc, bool b_kc, int epi, bool out_f32,
              hipStream_t s) {
+  GemmParams p = p0;
+  p.split_ws = m->split_ws;
+  p.split_cap = m->split_cap;
   const double fl = 2.0 * p.M * (double)p.N * p.K;
   int rc;
   {
@@ -463,6 +470,7 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
     GemmParams gx;   // dHf = G . U^T  (U stored [V][d]: reduction over V, n-contiguous)
     gx.A = m->G; gx.lda = V; gx.B = m->U; gx.ldb = d; gx.M = n; gx.N = d; gx.K = V;
     gx.C = m->dtmp; gx.ldc = d;
+    gx.split_ws = m->split_ws; gx.split_cap = m->split_cap;
     if (gemm(gx, bf, true, false, EPI_STORE, true, s)) return fail(TTT_ERR_CONFIG, "internal: CE variant");
   }
   fill_f32(m->dh, (int64_t)n * d, 0.f, s);
