@@ -38,7 +38,23 @@ template <typename T> struct GemmCfg {
   static constexpr int V = Vec16<T>::N;
 };
 
-// Register-staged loader for one operand tile (rows x BK).
+// Register-staged loader for one operand tile (rows x BK), reading through
+// a buffer resource: 32-bit offsets instead of 64-bit addresses, and
+// elements outside the matrix get an out-of-range offset, for which the
+// hardware returns zero (no branches around the loads).
+constexpr uint32_t OOB = 0x80000000u;
+
+DEVI __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes > 0x7fffffff ? 0x7fffffff : (int)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+DEVI U128 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  U128 u; u.w[0] = v[0]; u.w[1] = v[1]; u.w[2] = v[2]; u.w[3] = v[3];
+  return u;
+}
+
 template <typename T, bool KC, int ROWS> struct TileLoader {
   using C = GemmCfg<T>;
   static constexpr int V = C::V;
@@ -46,7 +62,8 @@ template <typename T, bool KC, int ROWS> struct TileLoader {
   static constexpr int NV = KC ? (ROWS * C::BK / V) / NT : 4 * ((ROWS / V) * (C::BK / 4)) / NT;
   U128 r[NV];
 
-  DEVI void load(const T* __restrict__ g, int64_t ld, int row0, int row_lim, int k0, int K, int tid) {
+  DEVI void load(__amdgpu_buffer_rsrc_t rs, int64_t ld, int row0, int row_lim, int k0, int K, int tid) {
+    const uint32_t ldb = (uint32_t)ld * (uint32_t)sizeof(T);
     if constexpr (KC) {
       constexpr int VPR = C::BK / V;
 #pragma unroll
@@ -54,7 +71,8 @@ template <typename T, bool KC, int ROWS> struct TileLoader {
         int idx = it * NT + tid;
         int rr = idx / VPR, c = (idx % VPR) * V;
         bool ok = (row0 + rr < row_lim) && (k0 + c < K);
-        r[it] = ok ? ld128(g + (int64_t)(row0 + rr) * ld + k0 + c) : zero128();
+        const uint32_t off = (uint32_t)(row0 + rr) * ldb + (uint32_t)(k0 + c) * (uint32_t)sizeof(T);
+        r[it] = bload(rs, ok ? off : OOB);
       }
     } else {
       constexpr int KB = C::BK / 4;
@@ -66,7 +84,8 @@ template <typename T, bool KC, int ROWS> struct TileLoader {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           bool ok = (k + q < K) && (m < row_lim);
-          r[it * 4 + q] = ok ? ld128(g + (int64_t)(k + q) * ld + m) : zero128();
+          const uint32_t off = (uint32_t)(k + q) * ldb + (uint32_t)m * (uint32_t)sizeof(T);
+          r[it * 4 + q] = bload(rs, ok ? off : OOB);
         }
       }
     }
@@ -132,7 +151,7 @@ DEVI float gelu_erf(float z) { return 0.5f * z * (1.f + erff(z * 0.7071067811865
 DEVI float silu(float z) { return z / (1.f + __expf(-z)); }
 
 template <typename T, bool A_KC, bool B_KC, int EPI, typename TO, bool DUAL>
-__global__ __launch_bounds__(NT) void gemm_kernel(GemmParams p) {
+__global__ __launch_bounds__(NT, 2) void gemm_kernel(GemmParams p) {
   using C = GemmCfg<T>;
   __shared__ __attribute__((aligned(16))) T lds[2][(BM + BN) * C::LS];
 
@@ -162,11 +181,20 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmParams p) {
   const int kt_begin = min(ntot, (int)blockIdx.z * per);
   const int kt_end = min(ntot, kt_begin + per);
   const T* __restrict__ B2 = static_cast<const T*>(p.B2);
+  // matrix extents in bytes for the buffer resources
+  const int64_t abytes = (A_KC ? (int64_t)p.M * p.lda : (int64_t)p.K * p.lda) * (int64_t)sizeof(T);
+  const int64_t bbytes = (B_KC ? (int64_t)p.N * p.ldb : (int64_t)p.K * p.ldb) * (int64_t)sizeof(T);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, abytes);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(B, bbytes);
+  const __amdgpu_buffer_rsrc_t rb2 = make_rsrc(DUAL ? (const void*)B2 : (const void*)B, bbytes);
+  auto load = [&](int t) {
+    const bool second = DUAL && t >= nk1;
+    const int k0 = (second ? t - nk1 : t) * C::BK;
+    la.load(ra, p.lda, m0, p.M, k0, p.K, tid);
+    lb.load(second ? rb2 : rb, p.ldb, n0, p.N, k0, p.K, tid);
+  };
   if (kt_begin < kt_end) {
-    const bool second = DUAL && kt_begin >= nk1;
-    const int k0 = (second ? kt_begin - nk1 : kt_begin) * C::BK;
-    la.load(A, p.lda, m0, p.M, k0, p.K, tid);
-    lb.load(second ? B2 : B, p.ldb, n0, p.N, k0, p.K, tid);
+    load(kt_begin);
     la.store(lds[0], tid);
     lb.store(lds[0] + BM * C::LS, tid);
   }
@@ -174,13 +202,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmParams p) {
 
   for (int kt = kt_begin; kt < kt_end; ++kt) {
     const int cur = (kt - kt_begin) & 1;
-    if (kt + 1 < kt_end) {
-      const int nt = kt + 1;
-      const bool second = DUAL && nt >= nk1;
-      const int k0 = (second ? nt - nk1 : nt) * C::BK;
-      la.load(A, p.lda, m0, p.M, k0, p.K, tid);
-      lb.load(second ? B2 : B, p.ldb, n0, p.N, k0, p.K, tid);
-    }
+    if (kt + 1 < kt_end) load(kt + 1);
     const T* As = lds[cur];
     const T* Bs = lds[cur] + BM * C::LS;
 #pragma unroll

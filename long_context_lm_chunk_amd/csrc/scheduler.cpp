@@ -121,7 +121,13 @@ struct ttt_model {
   std::vector<FastLayer> fast;
   double* theta = nullptr;
   // phase A
+  // phase A runs on its own stream, one block ahead of phase B; its output
+  // block is double-buffered (hAb[block % 2]); hA = hAb[0] also serves as the
+  // phase-B input of a decode chunk
+  float* hAb[2] = {nullptr, nullptr};
   float* hA = nullptr; void* aA = nullptr; void* qkvA = nullptr; void* qA = nullptr; void* oA = nullptr;
+  hipStream_t sa = nullptr;
+  hipEvent_t ev0 = nullptr, evA[2] = {nullptr, nullptr}, evB[2] = {nullptr, nullptr};
   void* zA = nullptr; void* actA = nullptr;
   // phase B
   std::vector<PB> pb;
@@ -210,7 +216,9 @@ size_t layout(ttt_model* m, void* base) {
   }
   m->theta = cv.take<double>((size_t)(m->hd / 2) * 8);
   // phase A
-  m->hA = cv.take<float>((size_t)MA * d * 4);
+  m->hAb[0] = cv.take<float>((size_t)MA * d * 4);
+  m->hAb[1] = cv.take<float>((size_t)MA * d * 4);
+  m->hA = m->hAb[0];
   m->aA = cv.take<void>((size_t)MA * d * es);
   m->qkvA = cv.take<void>((size_t)MA * 3 * d * es);
   m->qA = cv.take<void>((size_t)MA * d * es);
@@ -320,10 +328,12 @@ struct Scope {
 enum { CLS_GEMM = 0, CLS_ATTN_FWD = 1, CLS_ATTN_BWD = 2, CLS_CE = 3, CLS_SGD = 4, CLS_MLP_UP = 5 };
 
 int run_gemm(ttt_model* m, const GemmParams& p0, bool a_kc, bool b_kc, int epi, bool out_f32,
-             hipStream_t s) {
+             hipStream_t s, bool allow_split = true) {
   GemmParams p = p0;
-  p.split_ws = m->split_ws;
-  p.split_cap = m->split_cap;
+  // the split-K scratch belongs to the phase-B stream; phase A (large M)
+  // runs unsplit so the two streams never share it
+  p.split_ws = allow_split ? m->split_ws : nullptr;
+  p.split_cap = allow_split ? m->split_cap : 0;
   const double fl = 2.0 * p.M * (double)p.N * p.K;
   int rc;
   {
@@ -356,17 +366,17 @@ double pairs(int64_t p0, int n, int64_t W, int64_t kmin, double* inchunk) {
 }
 
 // --------------------------------------------------------------- phase A
-int phase_a(ttt_model* m, const int32_t* tokens, int64_t B0, int nb, hipStream_t s) {
+int phase_a(ttt_model* m, const int32_t* tokens, int64_t B0, int nb, float* hA, hipStream_t s) {
   const int d = m->d, F = m->F, F2 = m->F2;
   const bool bf = m->bf;
-  embed(tokens + B0, nb, m->E, d, m->V, bf, m->hA, m->err, s);
+  embed(tokens + B0, nb, m->E, d, m->V, bf, hA, m->err, s);
   for (int l = 0; l <= m->f0; ++l) {
     Layer& ly = m->layers[l];
-    layernorm_fwd(m->hA, d, nb, d, m->c.ln_eps, m->aA, d, nullptr, nullptr, bf, s);
+    layernorm_fwd(hA, d, nb, d, m->c.ln_eps, m->aA, d, nullptr, nullptr, bf, s);
     GemmParams g;
     g.A = m->aA; g.lda = d; g.B = ly.wqkv; g.ldb = d; g.M = nb; g.N = 3 * d; g.K = d;
     g.C = m->qkvA; g.ldc = 3 * d;
-    int rc = run_gemm(m, g, true, true, EPI_STORE, false, s); if (rc) return rc;
+    int rc = run_gemm(m, g, true, true, EPI_STORE, false, s, false); if (rc) return rc;
     rope_qkv(m->qkvA, nb, m->H, m->hd, B0, m->theta, m->qA, ly.kring, ly.vring, ly.cap, bf, s);
     ring_transpose(static_cast<char*>(m->qkvA) + (size_t)2 * d * m->es, 3 * d, 0, nb, m->H, m->hd, B0,
                    ly.vtring, ly.cap, bf, s);
@@ -379,19 +389,19 @@ int phase_a(ttt_model* m, const int32_t* tokens, int64_t B0, int nb, hipStream_t
     }
     GemmParams go;
     go.A = m->oA; go.lda = d; go.B = ly.wo; go.ldb = d; go.M = nb; go.N = d; go.K = d;
-    go.C = m->hA; go.ldc = d; go.R = m->hA; go.ldr = d;
-    rc = run_gemm(m, go, true, true, EPI_RESID, true, s); if (rc) return rc;
+    go.C = hA; go.ldc = d; go.R = hA; go.ldr = d;
+    rc = run_gemm(m, go, true, true, EPI_RESID, true, s, false); if (rc) return rc;
     if (l == m->f0) break;
-    layernorm_fwd(m->hA, d, nb, d, m->c.ln_eps, m->aA, d, nullptr, nullptr, bf, s);
+    layernorm_fwd(hA, d, nb, d, m->c.ln_eps, m->aA, d, nullptr, nullptr, bf, s);
     GemmParams gu;
     gu.A = m->aA; gu.lda = d; gu.B = ly.wup; gu.ldb = d; gu.M = nb; gu.N = F2; gu.K = d;
     gu.C = m->zA; gu.ldc = F2; gu.C2 = m->actA; gu.ldc2 = F;
-    rc = run_gemm(m, gu, true, true, m->c.mlp == TTT_MLP_SWIGLU ? EPI_SWIGLU : EPI_GELU, false, s);
+    rc = run_gemm(m, gu, true, true, m->c.mlp == TTT_MLP_SWIGLU ? EPI_SWIGLU : EPI_GELU, false, s, false);
     if (rc) return rc;
     GemmParams gd;
     gd.A = m->actA; gd.lda = F; gd.B = ly.wdn; gd.ldb = F; gd.M = nb; gd.N = d; gd.K = F;
-    gd.C = m->hA; gd.ldc = d; gd.R = m->hA; gd.ldr = d;
-    rc = run_gemm(m, gd, true, true, EPI_RESID, true, s); if (rc) return rc;
+    gd.C = hA; gd.ldc = d; gd.R = hA; gd.ldr = d;
+    rc = run_gemm(m, gd, true, true, EPI_RESID, true, s, false); if (rc) return rc;
   }
   return TTT_OK;
 }
@@ -610,6 +620,16 @@ int ttt_model_load(const ttt_config* cfg, const void* const* weights, int32_t n_
     delete m;
     return fail(TTT_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need) + " bytes");
   }
+  {
+    hipError_t e1 = hipStreamCreateWithFlags(&m->sa, hipStreamNonBlocking);
+    hipEvent_t* evs[5] = {&m->ev0, &m->evA[0], &m->evA[1], &m->evB[0], &m->evB[1]};
+    for (auto* e : evs)
+      if (e1 == hipSuccess) e1 = hipEventCreateWithFlags(e, hipEventDisableTiming);
+    if (e1 != hipSuccess) {
+      ttt_model_free(m);
+      return fail(TTT_ERR_HIP, std::string("stream/event creation: ") + hipGetErrorString(e1));
+    }
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int d = m->d, F = m->F, V = m->V;
   const bool bf = m->bf;
@@ -636,16 +656,16 @@ int ttt_model_load(const ttt_config* cfg, const void* const* weights, int32_t n_
   std::vector<double> th(m->hd / 2);
   for (int i = 0; i < m->hd / 2; ++i) th[i] = std::pow((double)cfg->rope_base, -2.0 * i / m->hd);
   hipError_t e = hipMemcpyAsync(m->theta, th.data(), th.size() * 8, hipMemcpyHostToDevice, s);
-  if (e != hipSuccess) { delete m; return fail(TTT_ERR_HIP, hipGetErrorString(e)); }
+  if (e != hipSuccess) { ttt_model_free(m); return fail(TTT_ERR_HIP, hipGetErrorString(e)); }
   float nan = NAN;
   e = hipMemcpyAsync(m->nanv, &nan, 4, hipMemcpyHostToDevice, s);
-  if (e != hipSuccess) { delete m; return fail(TTT_ERR_HIP, hipGetErrorString(e)); }
+  if (e != hipSuccess) { ttt_model_free(m); return fail(TTT_ERR_HIP, hipGetErrorString(e)); }
   rc = reset_state(m, s);
   if (!rc) {
     e = hipStreamSynchronize(s);
     if (e != hipSuccess) rc = fail(TTT_ERR_HIP, hipGetErrorString(e));
   }
-  if (rc) { delete m; return rc; }
+  if (rc) { ttt_model_free(m); return rc; }
   *out = m;
   return TTT_OK;
 }
@@ -665,16 +685,39 @@ int ttt_prefill(ttt_model* m, const int32_t* tokens, int64_t T, int32_t chunk, f
   m->chunk = chunk;
   const int d = m->d;
   const int64_t blk = std::max<int64_t>(chunk, (m->MA / chunk) * (int64_t)chunk);
-  int64_t k = 0;
-  for (int64_t B0 = 0; B0 < T; B0 += blk) {
+  const int64_t nblocks = (T + blk - 1) / blk;
+  // Phase A of block b+1 (frozen layers, independent of the fast weights)
+  // runs on m->sa while phase B of block b runs on s.  evA[b%2]: block b's
+  // phase-A output is ready; evB[b%2]: phase B is done reading it, so the
+  // buffer can take block b+2.
+  HIPCHK(hipEventRecord(m->ev0, s));
+  HIPCHK(hipStreamWaitEvent(m->sa, m->ev0, 0));
+  auto launch_a = [&](int64_t b) -> int {
+    const int64_t B0 = b * blk;
     const int nb = (int)std::min<int64_t>(blk, T - B0);
-    rc = phase_a(m, tokens, B0, nb, s);
-    if (rc) return rc;
+    if (b >= 2) HIPCHK(hipStreamWaitEvent(m->sa, m->evB[b % 2], 0));
+    const int r = phase_a(m, tokens, B0, nb, m->hAb[b % 2], m->sa);
+    if (r) return r;
+    HIPCHK(hipEventRecord(m->evA[b % 2], m->sa));
+    return TTT_OK;
+  };
+  rc = launch_a(0);
+  if (rc) return rc;
+  int64_t k = 0;
+  for (int64_t b = 0; b < nblocks; ++b) {
+    const int64_t B0 = b * blk;
+    const int nb = (int)std::min<int64_t>(blk, T - B0);
+    if (b + 1 < nblocks) {
+      rc = launch_a(b + 1);
+      if (rc) return rc;
+    }
+    HIPCHK(hipStreamWaitEvent(s, m->evA[b % 2], 0));
+    float* hAblk = m->hAb[b % 2];
     for (int64_t c0 = B0; c0 < B0 + nb; c0 += chunk, ++k) {
       const int n = (int)std::min<int64_t>(chunk, T - c0);
       const int n_tgt = (int)std::min<int64_t>(n, T - 1 - c0);
       for (int st = 0; st < steps; ++st) {
-        rc = chunk_step(m, c0, n, m->hA + (c0 - B0) * (int64_t)d, tokens + c0 + 1, n_tgt, lr,
+        rc = chunk_step(m, c0, n, hAblk + (c0 - B0) * (int64_t)d, tokens + c0 + 1, n_tgt, lr,
                         chunk_losses + k * steps + st, s);
         if (rc) return rc;
       }
@@ -686,6 +729,7 @@ int ttt_prefill(ttt_model* m, const int32_t* tokens, int64_t T, int32_t chunk, f
         argmax_tok(m->logits, m->V, m->cur_tok, nullptr, s);
       }
     }
+    HIPCHK(hipEventRecord(m->evB[b % 2], s));
   }
   rc = sync_and_check(m, s);
   if (rc) return rc;
@@ -770,8 +814,13 @@ int ttt_reset(ttt_model* m, void* stream) {
 
 void ttt_model_free(ttt_model* m) {
   if (!m) return;
+  if (m->sa) (void)hipStreamSynchronize(m->sa);
   for (auto& t : m->tm)
-    for (auto e : t.ev) hipEventDestroy(e);
+    for (auto e : t.ev) (void)hipEventDestroy(e);
+  hipEvent_t evs[5] = {m->ev0, m->evA[0], m->evA[1], m->evB[0], m->evB[1]};
+  for (auto e : evs)
+    if (e) (void)hipEventDestroy(e);
+  if (m->sa) (void)hipStreamDestroy(m->sa);
   delete m;
 }
 
