@@ -62,8 +62,14 @@ template <typename T>
 __global__ __launch_bounds__(256) void swa_decode_part_k(const T* __restrict__ q,
                                                          const T* __restrict__ kr,
                                                          const T* __restrict__ vr, int64_t cap,
-                                                         int H, int hd, int64_t lo, int64_t pos,
+                                                         int H, int hd, int window,
+                                                         const int64_t* __restrict__ dstate,
                                                          float* __restrict__ ws, int nsplit) {
+  // position of this token from the device-side decode state (so a captured
+  // graph replays unchanged); splits past the window write empty partials
+  const int64_t pos = dstate[0];
+  int64_t lo = pos - window + 1;
+  if (lo < 0) lo = 0;
   __shared__ float qs[128];
   __shared__ float ps[DK];
   __shared__ float red[256];
@@ -127,6 +133,7 @@ __global__ __launch_bounds__(256) void swa_decode_part_k(const T* __restrict__ q
 template <typename T>
 __global__ void swa_decode_combine_k(const float* __restrict__ ws, int nsplit, int H, int hd,
                                      T* __restrict__ o) {
+  // (every split writes its partial, possibly empty: m = -inf, l = 0)
   const int h = blockIdx.x, j = threadIdx.x;
   if (j >= hd) return;
   float M = -INFINITY;
@@ -141,9 +148,34 @@ __global__ void swa_decode_combine_k(const float* __restrict__ ws, int nsplit, i
   o[h * hd + j] = from_f32<T>(acc / L);
 }
 
-// Greedy choice: largest logit, lowest id on ties.
+// Decode bookkeeping kernels (graph-safe: no memcpy/memset nodes).
+// dstate = {pos, ci}: position being read, index within the decode chunk.
+__global__ void dec_begin_k(const int32_t* __restrict__ cur, const int64_t* __restrict__ dstate,
+                            int32_t* __restrict__ hist) {
+  if (threadIdx.x == 0) hist[dstate[1]] = *cur;
+}
+__global__ void dec_end_k(int64_t* __restrict__ dstate) {
+  if (threadIdx.x == 0) { dstate[0] += 1; dstate[1] += 1; }
+}
+__global__ void dec_row_k(const float* __restrict__ x, int d, const int64_t* __restrict__ dstate,
+                          float* __restrict__ rows) {
+  const int64_t ci = dstate[1];
+  for (int i = threadIdx.x; i < d; i += blockDim.x) rows[ci * d + i] = x[i];
+}
+__global__ void dec_set_k(int64_t* __restrict__ dstate, int64_t pos, int64_t ci) {
+  if (threadIdx.x == 0) { dstate[0] = pos; dstate[1] = ci; }
+}
+__global__ void copy_i32_k(const int32_t* __restrict__ a, int32_t* __restrict__ b) {
+  if (threadIdx.x == 0) *b = *a;
+}
+__global__ void copy_f32_k(const float* __restrict__ a, float* __restrict__ b, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) b[i] = a[i];
+}
+
+// Greedy choice: largest logit, lowest id on ties.  The chosen id also goes
+// to hist[ci + 1] (the target of the position just read).
 __global__ void argmax_k(const float* __restrict__ z, int V, int32_t* __restrict__ out,
-                         int32_t* __restrict__ hist) {
+                         int32_t* __restrict__ hist, const int64_t* __restrict__ dstate) {
   __shared__ float bv[1024];
   __shared__ int bi[1024];
   float best = -INFINITY;
@@ -169,7 +201,7 @@ __global__ void argmax_k(const float* __restrict__ z, int V, int32_t* __restrict
   if (threadIdx.x == 0) {
     const int r = bi[0] == 0x7fffffff ? 0 : bi[0];
     *out = r;
-    if (hist) *hist = r;
+    if (hist) hist[dstate ? dstate[1] + 1 : 0] = r;
   }
 }
 
@@ -196,22 +228,36 @@ void gelu_vec(const float* z, int F, void* act, bool bf, hipStream_t s) {
 }
 
 void swa_decode(const void* q, const void* kring, const void* vring, int64_t cap, int H, int hd,
-                int window, int64_t pos, void* o, float* ws, bool bf, hipStream_t s) {
-  int64_t lo = pos - window + 1;
-  if (lo < 0) lo = 0;
-  const int nsplit = (int)((pos - lo + 1 + DK - 1) / DK);
+                int window, const int64_t* dstate, void* o, float* ws, bool bf, hipStream_t s) {
+  const int nsplit = (window + DK - 1) / DK;   // covers a full window
   dim3 grid(nsplit, H);
   if (bf) {
-    hipLaunchKernelGGL(swa_decode_part_k<bf16>, grid, dim3(256), 0, s, (const bf16*)q, (const bf16*)kring, (const bf16*)vring, cap, H, hd, lo, pos, ws, nsplit);
+    hipLaunchKernelGGL(swa_decode_part_k<bf16>, grid, dim3(256), 0, s, (const bf16*)q, (const bf16*)kring, (const bf16*)vring, cap, H, hd, window, dstate, ws, nsplit);
     hipLaunchKernelGGL(swa_decode_combine_k<bf16>, dim3(H), dim3(128), 0, s, ws, nsplit, H, hd, (bf16*)o);
   } else {
-    hipLaunchKernelGGL(swa_decode_part_k<float>, grid, dim3(256), 0, s, (const float*)q, (const float*)kring, (const float*)vring, cap, H, hd, lo, pos, ws, nsplit);
+    hipLaunchKernelGGL(swa_decode_part_k<float>, grid, dim3(256), 0, s, (const float*)q, (const float*)kring, (const float*)vring, cap, H, hd, window, dstate, ws, nsplit);
     hipLaunchKernelGGL(swa_decode_combine_k<float>, dim3(H), dim3(128), 0, s, ws, nsplit, H, hd, (float*)o);
   }
 }
 
-void argmax_tok(const float* logits, int V, int32_t* out_tok, int32_t* tok_hist, hipStream_t s) {
-  hipLaunchKernelGGL(argmax_k, dim3(1), dim3(1024), 0, s, logits, V, out_tok, tok_hist);
+void dec_begin(const int32_t* cur, const int64_t* dstate, int32_t* hist, hipStream_t s) {
+  hipLaunchKernelGGL(dec_begin_k, dim3(1), dim3(64), 0, s, cur, dstate, hist);
+}
+void dec_end(int64_t* dstate, hipStream_t s) { hipLaunchKernelGGL(dec_end_k, dim3(1), dim3(64), 0, s, dstate); }
+void dec_row(const float* x, int d, const int64_t* dstate, float* rows, hipStream_t s) {
+  hipLaunchKernelGGL(dec_row_k, dim3(1), dim3(256), 0, s, x, d, dstate, rows);
+}
+void dec_set(int64_t* dstate, int64_t pos, int64_t ci, hipStream_t s) {
+  hipLaunchKernelGGL(dec_set_k, dim3(1), dim3(64), 0, s, dstate, pos, ci);
+}
+void copy_i32(const int32_t* a, int32_t* b, hipStream_t s) { hipLaunchKernelGGL(copy_i32_k, dim3(1), dim3(64), 0, s, a, b); }
+void copy_f32(const float* a, float* b, int n, hipStream_t s) {
+  hipLaunchKernelGGL(copy_f32_k, dim3((n + 255) / 256 > 1024 ? 1024 : (n + 255) / 256), dim3(256), 0, s, a, b, n);
+}
+
+void argmax_tok(const float* logits, int V, int32_t* out_tok, int32_t* tok_hist, const int64_t* dstate,
+                hipStream_t s) {
+  hipLaunchKernelGGL(argmax_k, dim3(1), dim3(1024), 0, s, logits, V, out_tok, tok_hist, dstate);
 }
 
 }  // namespace ttt

@@ -130,10 +130,12 @@ __global__ void rope_qkv_k(const T* __restrict__ qkv, int n, int H, int hd, int6
 }
 
 template <typename T>
-__global__ void rope_qkv_f32in_k(const float* __restrict__ qkv, int H, int hd, int64_t pos,
+__global__ void rope_qkv_f32in_k(const float* __restrict__ qkv, int H, int hd,
+                                 const int64_t* __restrict__ dstate,
                                  const double* __restrict__ theta, T* __restrict__ qo,
                                  T* __restrict__ kr, T* __restrict__ vr, T* __restrict__ vt,
                                  int64_t cap) {
+  const int64_t pos = dstate[0];   // decode position from the device-side state
   const int half = hd >> 1;
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= H * half) return;
@@ -363,11 +365,11 @@ void rope_qkv(const void* qkv, int n, int H, int hd, int64_t pos0, const double*
        hipLaunchKernelGGL(rope_qkv_k<float>, dim3(nblk(total, 256)), dim3(256), 0, s, (const float*)qkv, n, H, hd, pos0, theta, (float*)q_out, (float*)kring, (float*)vring, cap));
 }
 
-void rope_qkv_f32in(const float* qkv, int H, int hd, int64_t pos, const double* theta, void* q_out,
+void rope_qkv_f32in(const float* qkv, int H, int hd, const int64_t* dstate, const double* theta, void* q_out,
                     void* kring, void* vring, void* vtring, int64_t cap, bool bf, hipStream_t s) {
   const int total = H * (hd / 2);
-  TSEL(bf, hipLaunchKernelGGL(rope_qkv_f32in_k<bf16>, dim3(nblk(total, 256)), dim3(256), 0, s, qkv, H, hd, pos, theta, (bf16*)q_out, (bf16*)kring, (bf16*)vring, (bf16*)vtring, cap),
-       hipLaunchKernelGGL(rope_qkv_f32in_k<float>, dim3(nblk(total, 256)), dim3(256), 0, s, qkv, H, hd, pos, theta, (float*)q_out, (float*)kring, (float*)vring, (float*)vtring, cap));
+  TSEL(bf, hipLaunchKernelGGL(rope_qkv_f32in_k<bf16>, dim3(nblk(total, 256)), dim3(256), 0, s, qkv, H, hd, dstate, theta, (bf16*)q_out, (bf16*)kring, (bf16*)vring, (bf16*)vtring, cap),
+       hipLaunchKernelGGL(rope_qkv_f32in_k<float>, dim3(nblk(total, 256)), dim3(256), 0, s, qkv, H, hd, dstate, theta, (float*)q_out, (float*)kring, (float*)vring, (float*)vtring, cap));
 }
 
 void rope_bwd(void* dqkv, int n, int H, int hd, int64_t pos0, const double* theta, bool bf,

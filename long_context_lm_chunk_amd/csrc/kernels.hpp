@@ -94,10 +94,20 @@ void gemv(const void* W, const void* W2, int N, int K, const void* x, bool x_f32
           const float* resid, bool bf16, hipStream_t s);
 void swiglu_vec(const float* z, int F, void* act, bool bf16, hipStream_t s);
 void gelu_vec(const float* z, int F, void* act, bool bf16, hipStream_t s);
+// decode kernels read the position from dstate = {pos, ci} on the device,
+// so one token's launches can be captured once and replayed
 void swa_decode(const void* q, const void* kring, const void* vring, int64_t cap, int H, int hd,
-                int window, int64_t pos, void* o, float* ws, bool bf16, hipStream_t s);
-void argmax_tok(const float* logits, int V, int32_t* out_tok, int32_t* tok_hist, hipStream_t s);
-void rope_qkv_f32in(const float* qkv, int H, int hd, int64_t pos, const double* theta, void* q_out,
-                    void* kring, void* vring, void* vtring, int64_t cap, bool bf16, hipStream_t s);
+                int window, const int64_t* dstate, void* o, float* ws, bool bf16, hipStream_t s);
+void argmax_tok(const float* logits, int V, int32_t* out_tok, int32_t* tok_hist, const int64_t* dstate,
+                hipStream_t s);
+void rope_qkv_f32in(const float* qkv, int H, int hd, const int64_t* dstate, const double* theta,
+                    void* q_out, void* kring, void* vring, void* vtring, int64_t cap, bool bf16,
+                    hipStream_t s);
+void dec_begin(const int32_t* cur, const int64_t* dstate, int32_t* hist, hipStream_t s);
+void dec_end(int64_t* dstate, hipStream_t s);
+void dec_row(const float* x, int d, const int64_t* dstate, float* rows, hipStream_t s);
+void dec_set(int64_t* dstate, int64_t pos, int64_t ci, hipStream_t s);
+void copy_i32(const int32_t* a, int32_t* b, hipStream_t s);
+void copy_f32(const float* a, float* b, int n, hipStream_t s);
 
 }  // namespace ttt

@@ -143,6 +143,8 @@ struct ttt_model {
   float* xd = nullptr; void* ad = nullptr; float* qkvd = nullptr; void* qd = nullptr; void* od = nullptr;
   float* zd = nullptr; void* actd = nullptr; float* logits = nullptr; float* attn_ws = nullptr;
   int32_t* hist = nullptr; int32_t* cur_tok = nullptr;
+  int64_t* dstate = nullptr;            // decode state on the device: {pos, ci}
+  hipGraphExec_t dec_exec = nullptr;    // one decode token, captured once
   int* err = nullptr;
   float* nanv = nullptr;
   // state
@@ -281,6 +283,7 @@ size_t layout(ttt_model* m, void* base) {
   m->attn_ws = cv.take<float>((size_t)H * nsplit * (2 + m->hd) * 4);
   m->hist = cv.take<int32_t>((size_t)(C + 2) * 4);
   m->cur_tok = cv.take<int32_t>(4);
+  m->dstate = cv.take<int64_t>(16);
   m->err = cv.take<int>(4);
   m->nanv = cv.take<float>(4);
   (void)c;
@@ -547,6 +550,39 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
   return TTT_OK;
 }
 
+// One decode token: read the current token at position dstate[0], append
+// its K/V to every ring, and leave the next greedy token in cur_tok.  No
+// argument depends on the position, so the launches can be captured once.
+void decode_body(ttt_model* m, hipStream_t s) {
+  const int d = m->d, F = m->F, F2 = m->F2, V = m->V;
+  const bool bf = m->bf;
+  const float eps = m->c.ln_eps;
+  dec_begin(m->cur_tok, m->dstate, m->hist, s);
+  embed(m->cur_tok, 1, m->E, d, V, bf, m->xd, m->err, s);
+  for (int l = 0; l < m->L; ++l) {
+    Layer& ly = m->layers[l];
+    const int j = l - m->f0;
+    layernorm_fwd(m->xd, d, 1, d, eps, m->ad, d, nullptr, nullptr, bf, s);
+    gemv(ly.wqkv, nullptr, 3 * d, d, m->ad, !bf, m->qkvd, nullptr, bf, s);
+    rope_qkv_f32in(m->qkvd, m->H, m->hd, m->dstate, m->theta, m->qd, ly.kring, ly.vring, ly.vtring,
+                   ly.cap, bf, s);
+    swa_decode(m->qd, ly.kring, ly.vring, ly.cap, m->H, m->hd, m->W, m->dstate, m->od, m->attn_ws, bf, s);
+    gemv(ly.wo, nullptr, d, d, m->od, !bf, m->xd, m->xd, bf, s);
+    if (j == 0) dec_row(m->xd, d, m->dstate, m->hA, s);   // phase-B input of this position
+    layernorm_fwd(m->xd, d, 1, d, eps, m->ad, d, nullptr, nullptr, bf, s);
+    const void* dup = j >= 0 ? m->fast[j].s_up : nullptr;
+    const void* ddn = j >= 0 ? m->fast[j].s_dn : nullptr;
+    gemv(ly.wup, dup, F2, d, m->ad, !bf, m->zd, nullptr, bf, s);
+    if (m->c.mlp == TTT_MLP_SWIGLU) swiglu_vec(m->zd, F, m->actd, bf, s);
+    else gelu_vec(m->zd, F, m->actd, bf, s);
+    gemv(ly.wdn, ddn, d, F, m->actd, !bf, m->xd, m->xd, bf, s);
+  }
+  layernorm_fwd(m->xd, d, 1, d, eps, m->ad, d, nullptr, nullptr, bf, s);
+  gemv(m->U, nullptr, V, d, m->ad, !bf, m->logits, nullptr, bf, s);
+  argmax_tok(m->logits, V, m->cur_tok, m->hist, m->dstate, s);
+  dec_end(m->dstate, s);
+}
+
 int sync_and_check(ttt_model* m, hipStream_t s) {
   HIPCHK(hipStreamSynchronize(s));
   int e = 0;
@@ -726,7 +762,8 @@ int ttt_prefill(ttt_model* m, const int32_t* tokens, int64_t T, int32_t chunk, f
         // chunk's last read
         const char* frow = static_cast<const char*>(m->fN) + (size_t)(n - 1) * d * m->es;
         gemv(m->U, nullptr, m->V, d, frow, !m->bf, m->logits, nullptr, m->bf, s);
-        argmax_tok(m->logits, m->V, m->cur_tok, nullptr, s);
+        argmax_tok(m->logits, m->V, m->cur_tok, nullptr, nullptr, s);
+        dec_set(m->dstate, T, 0, s);
       }
     }
     HIPCHK(hipEventRecord(m->evB[b % 2], s));
@@ -761,39 +798,29 @@ int ttt_decode_step(ttt_model* m, int32_t* next_token, float* logits_out, float*
   if (!m || !next_token) return fail(TTT_ERR_ARG, "NULL argument");
   if (!m->prefilled) return fail(TTT_ERR_STATE, "decode needs a prefill first");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int d = m->d, F = m->F, F2 = m->F2, V = m->V;
-  const bool bf = m->bf;
-  const float eps = m->c.ln_eps;
-  const int64_t p = m->pos;
-  const int64_t ci = p - m->dchunk0;   // index within the decode chunk
-  HIPCHK(hipMemcpyAsync(next_token, m->cur_tok, 4, hipMemcpyDeviceToDevice, s));
-  HIPCHK(hipMemcpyAsync(m->hist + ci, m->cur_tok, 4, hipMemcpyDeviceToDevice, s));
-  embed(m->cur_tok, 1, m->E, d, V, bf, m->xd, m->err, s);
-  for (int l = 0; l < m->L; ++l) {
-    Layer& ly = m->layers[l];
-    const int j = l - m->f0;
-    layernorm_fwd(m->xd, d, 1, d, eps, m->ad, d, nullptr, nullptr, bf, s);
-    gemv(ly.wqkv, nullptr, 3 * d, d, m->ad, !bf, m->qkvd, nullptr, bf, s);
-    rope_qkv_f32in(m->qkvd, m->H, m->hd, p, m->theta, m->qd, ly.kring, ly.vring, ly.vtring, ly.cap, bf, s);
-    swa_decode(m->qd, ly.kring, ly.vring, ly.cap, m->H, m->hd, m->W, p, m->od, m->attn_ws, bf, s);
-    gemv(ly.wo, nullptr, d, d, m->od, !bf, m->xd, m->xd, bf, s);
-    if (j == 0)   // phase-B input of this position, for the decode-chunk update
-      HIPCHK(hipMemcpyAsync(m->hA + ci * d, m->xd, (size_t)d * 4, hipMemcpyDeviceToDevice, s));
-    layernorm_fwd(m->xd, d, 1, d, eps, m->ad, d, nullptr, nullptr, bf, s);
-    const void* dup = j >= 0 ? m->fast[j].s_up : nullptr;
-    const void* ddn = j >= 0 ? m->fast[j].s_dn : nullptr;
-    gemv(ly.wup, dup, F2, d, m->ad, !bf, m->zd, nullptr, bf, s);
-    if (m->c.mlp == TTT_MLP_SWIGLU) swiglu_vec(m->zd, F, m->actd, bf, s);
-    else gelu_vec(m->zd, F, m->actd, bf, s);
-    gemv(ly.wdn, ddn, d, F, m->actd, !bf, m->xd, m->xd, bf, s);
+  copy_i32(m->cur_tok, next_token, s);   // the token this call emits (and reads)
+  if (!m->dec_exec) {
+    // Capture one token's launches once (on the library's own stream: the
+    // caller's may be the legacy default stream, which cannot be captured);
+    // every launch reads the position from the device-side state.
+    HIPCHK(hipStreamSynchronize(m->sa));
+    HIPCHK(hipStreamBeginCapture(m->sa, hipStreamCaptureModeThreadLocal));
+    decode_body(m, m->sa);
+    hipGraph_t g = nullptr;
+    HIPCHK(hipStreamEndCapture(m->sa, &g));
+    const hipError_t e = hipGraphInstantiate(&m->dec_exec, g, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(g);
+    if (e != hipSuccess) {
+      m->dec_exec = nullptr;
+      return fail(TTT_ERR_HIP, std::string("decode graph: ") + hipGetErrorString(e));
+    }
   }
-  layernorm_fwd(m->xd, d, 1, d, eps, m->ad, d, nullptr, nullptr, bf, s);
-  gemv(m->U, nullptr, V, d, m->ad, !bf, m->logits, nullptr, bf, s);
-  argmax_tok(m->logits, V, m->cur_tok, m->hist + ci + 1, s);
-  if (logits_out) HIPCHK(hipMemcpyAsync(logits_out, m->logits, (size_t)V * 4, hipMemcpyDeviceToDevice, s));
-  m->pos = p + 1;
+  HIPCHK(hipGraphLaunch(m->dec_exec, s));
+  if (logits_out) copy_f32(m->logits, logits_out, m->V, s);
+  m->pos += 1;
   bool updated = false;
   if (m->pos - m->dchunk0 == m->chunk) {
+    // the decode chunk is complete: its targets are known, make the update
     const int n = m->chunk;
     for (int st = 0; st < m->steps; ++st) {
       int rc = chunk_step(m, m->dchunk0, n, m->hA, m->hist + 1, n, m->lr,
@@ -801,9 +828,10 @@ int ttt_decode_step(ttt_model* m, int32_t* next_token, float* logits_out, float*
       if (rc) return rc;
     }
     m->dchunk0 = m->pos;
+    dec_set(m->dstate, m->pos, 0, s);
     updated = true;
   }
-  if (update_loss && !updated) HIPCHK(hipMemcpyAsync(update_loss, m->nanv, 4, hipMemcpyDeviceToDevice, s));
+  if (update_loss && !updated) copy_f32(m->nanv, update_loss, 1, s);
   return TTT_OK;
 }
 
@@ -815,6 +843,7 @@ int ttt_reset(ttt_model* m, void* stream) {
 void ttt_model_free(ttt_model* m) {
   if (!m) return;
   if (m->sa) (void)hipStreamSynchronize(m->sa);
+  if (m->dec_exec) (void)hipGraphExecDestroy(m->dec_exec);
   for (auto& t : m->tm)
     for (auto e : t.ev) (void)hipEventDestroy(e);
   hipEvent_t evs[5] = {m->ev0, m->evA[0], m->evA[1], m->evB[0], m->evB[1]};
