@@ -56,8 +56,10 @@ __global__ void gelu_vec_k(const float* __restrict__ z, int F, T* __restrict__ a
 
 constexpr int DK = 256;   // keys per split
 
-// Partial attention of one query (position pos) over keys
-// [lo + split*DK, ...) of head h.  ws layout per (h, split): m, l, o[hd].
+// Partial attention of one query over keys [lo + split*DK, ...) of head h,
+// bandwidth-bound.  Lanes work in groups of G = hd/8 (16 for hd = 128):
+// a group covers one key's row with one 16-byte load per lane, so a wave
+// reads 64/G whole rows per instruction.  ws per (h, split): m, l, o[hd].
 template <typename T>
 __global__ __launch_bounds__(256) void swa_decode_part_k(const T* __restrict__ q,
                                                          const T* __restrict__ kr,
@@ -70,63 +72,78 @@ __global__ __launch_bounds__(256) void swa_decode_part_k(const T* __restrict__ q
   const int64_t pos = dstate[0];
   int64_t lo = pos - window + 1;
   if (lo < 0) lo = 0;
-  __shared__ float qs[128];
+  constexpr int V = Vec16<T>::N;
   __shared__ float ps[DK];
-  __shared__ float red[256];
+  __shared__ float red[8];
   __shared__ float oacc[4][128];
   const int h = blockIdx.y, sp = blockIdx.x, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int d = H * hd;
-  for (int i = tid; i < hd; i += 256) qs[i] = to_f32(q[h * hd + i]);
-  __syncthreads();
-  const int64_t kp = lo + (int64_t)sp * DK + tid;
-  float s = -INFINITY;
-  if (kp <= pos) {
-    const T* k = kr + (kp % cap) * d + h * hd;
-    float acc = 0.f;
-    constexpr int V = Vec16<T>::N;
-    for (int c = 0; c < hd; c += V) {
-      const U128 kv = ld128(k + c);
+  int G = 1;                               // lanes per key row: hd/V rounded up to a power of two
+  while (G * V < hd) G <<= 1;
+  const int KPW = 64 / G;                  // keys per wave instruction
+  const int gi = lane % G, kg = lane / G;  // lane's vector within the row, key slot
+  const bool live = gi * V < hd;           // hd = 96: 12 of every 16 lanes carry data
+  const int64_t kbase = lo + (int64_t)sp * DK;
+  float qv[V];
+  {
+    const U128 qq = live ? ld128(q + h * hd + gi * V) : zero128();
 #pragma unroll
-      for (int e = 0; e < V; ++e) acc += to_f32(elem<T>(kv, e)) * qs[c + e];
+    for (int e = 0; e < V; ++e) qv[e] = to_f32(elem<T>(qq, e));
+  }
+  const float scale = 1.f / sqrtf((float)hd);
+  // scores: each wave takes keys wave*64 .. wave*64+63 of the split
+  for (int k0 = wave * 64; k0 < wave * 64 + 64; k0 += KPW) {
+    const int kk = k0 + kg;
+    const int64_t kp = kbase + kk;
+    float sacc = 0.f;
+    if (live && kp <= pos) {
+      const U128 kv = ld128(kr + (kp % cap) * d + h * hd + gi * V);
+#pragma unroll
+      for (int e = 0; e < V; ++e) sacc += to_f32(elem<T>(kv, e)) * qv[e];
     }
-    s = acc / sqrtf((float)hd);
+    for (int o = 1; o < G; o <<= 1) sacc += __shfl_xor(sacc, o, 64);
+    if (gi == 0 && kk < DK) ps[kk] = (kp <= pos) ? sacc * scale : -INFINITY;
   }
-  red[tid] = s;
   __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
-    __syncthreads();
-  }
-  const float m = red[0];
+  // max and sum over the split's 256 scores
+  float mx = wave_max(ps[tid]);
+  if (lane == 0) red[wave] = mx;
   __syncthreads();
-  const float e = (s == -INFINITY) ? 0.f : __expf(s - m);
+  const float m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float e = (ps[tid] == -INFINITY) ? 0.f : __expf(ps[tid] - m);
+  float sm = wave_sum(e);
+  __syncthreads();
   ps[tid] = e;
-  red[tid] = e;
+  if (lane == 0) red[4 + wave] = sm;
   __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (tid < o) red[tid] += red[tid + o];
-    __syncthreads();
-  }
-  const float l = red[0];
-  // o[j] = sum_k p_k v_k[j]: thread (g = tid / hd_groups) handles keys g, g+G, ...
-  const int G = 256 / hd > 4 ? 4 : (256 / hd);    // key groups (hd <= 128 -> >= 2)
-  const int j = tid % hd, g = tid / hd;
-  if (g < G) {
-    float a = 0.f;
-    for (int kk = g; kk < DK; kk += G) {
-      const int64_t p2 = lo + (int64_t)sp * DK + kk;
-      if (p2 > pos) break;
-      a += ps[kk] * to_f32(vr[(p2 % cap) * d + h * hd + j]);
+  const float l = red[4] + red[5] + red[6] + red[7];
+  // o = sum_k p_k v_k: same lane grouping, each lane accumulates its V
+  // elements over the keys of its slot, then slots and waves are summed
+  float o[V];
+#pragma unroll
+  for (int e2 = 0; e2 < V; ++e2) o[e2] = 0.f;
+  for (int k0 = wave * 64; k0 < wave * 64 + 64; k0 += KPW) {
+    const int kk = k0 + kg;
+    const int64_t kp = kbase + kk;
+    if (live && kk < DK && kp <= pos) {
+      const float pk = ps[kk];
+      const U128 vv = ld128(vr + (kp % cap) * d + h * hd + gi * V);
+#pragma unroll
+      for (int e2 = 0; e2 < V; ++e2) o[e2] += pk * to_f32(elem<T>(vv, e2));
     }
-    oacc[g][j] = a;
+  }
+  // reduce over key slots (lanes gi + G*kg) within the wave
+  for (int off = G; off < 64; off <<= 1)
+#pragma unroll
+    for (int e2 = 0; e2 < V; ++e2) o[e2] += __shfl_xor(o[e2], off, 64);
+  if (kg == 0 && live) {
+#pragma unroll
+    for (int e2 = 0; e2 < V; ++e2) oacc[wave][gi * V + e2] = o[e2];
   }
   __syncthreads();
   float* w = ws + ((int64_t)h * nsplit + sp) * (2 + hd);
-  if (tid < hd) {
-    float a = 0.f;
-    for (int gg = 0; gg < G; ++gg) a += oacc[gg][tid];
-    w[2 + tid] = a;
-  }
+  if (tid < hd) w[2 + tid] = oacc[0][tid] + oacc[1][tid] + oacc[2][tid] + oacc[3][tid];
   if (tid == 0) { w[0] = m; w[1] = l; }
 }
 
