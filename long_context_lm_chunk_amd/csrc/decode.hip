@@ -19,17 +19,22 @@ __global__ __launch_bounds__(256) void gemv_k(const T* __restrict__ W, const T* 
   const int lane = threadIdx.x & 63;
   if (row >= N) return;
   constexpr int V = Vec16<T>::N;
-  const T* w = W + (int64_t)row * K;
   float s = 0.f;
-  for (int k = lane * V; k < K; k += 64 * V) {
-    const U128 wv = ld128(w + k);
+  // 4 independent 16-byte loads in flight per lane per step
+  for (int pass = 0; pass < (W2 ? 2 : 1); ++pass) {   // fast weights: W0 + delta, one fp32 sum
+    const T* w = (pass ? W2 : W) + (int64_t)row * K;
+    int k = lane * V;
+    for (; k + 3 * 64 * V < K; k += 4 * 64 * V) {
+      U128 wv[4];
 #pragma unroll
-    for (int e = 0; e < V; ++e) s += to_f32(elem<T>(wv, e)) * to_f32(x[k + e]);
-  }
-  if (W2) {   // fast weights: W0 + delta, summed in fp32
-    const T* w2 = W2 + (int64_t)row * K;
-    for (int k = lane * V; k < K; k += 64 * V) {
-      const U128 wv = ld128(w2 + k);
+      for (int u = 0; u < 4; ++u) wv[u] = ld128(w + k + u * 64 * V);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < V; ++e) s += to_f32(elem<T>(wv[u], e)) * to_f32(x[k + u * 64 * V + e]);
+    }
+    for (; k < K; k += 64 * V) {
+      const U128 wv = ld128(w + k);
 #pragma unroll
       for (int e = 0; e < V; ++e) s += to_f32(elem<T>(wv, e)) * to_f32(x[k + e]);
     }
@@ -60,11 +65,11 @@ constexpr int DK = 256;   // keys per split
 // bandwidth-bound.  Lanes work in groups of G = hd/8 (16 for hd = 128):
 // a group covers one key's row with one 16-byte load per lane, so a wave
 // reads 64/G whole rows per instruction.  ws per (h, split): m, l, o[hd].
-template <typename T>
+template <typename T, int hd>
 __global__ __launch_bounds__(256) void swa_decode_part_k(const T* __restrict__ q,
                                                          const T* __restrict__ kr,
                                                          const T* __restrict__ vr, int64_t cap,
-                                                         int H, int hd, int window,
+                                                         int H, int window,
                                                          const int64_t* __restrict__ dstate,
                                                          float* __restrict__ ws, int nsplit) {
   // position of this token from the device-side decode state (so a captured
@@ -79,9 +84,10 @@ __global__ __launch_bounds__(256) void swa_decode_part_k(const T* __restrict__ q
   const int h = blockIdx.y, sp = blockIdx.x, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int d = H * hd;
-  int G = 1;                               // lanes per key row: hd/V rounded up to a power of two
-  while (G * V < hd) G <<= 1;
-  const int KPW = 64 / G;                  // keys per wave instruction
+  // lanes per key row: hd/V rounded up to a power of two
+  constexpr int G = (hd / V <= 1) ? 1 : (hd / V <= 2) ? 2 : (hd / V <= 4) ? 4 : (hd / V <= 8) ? 8
+                  : (hd / V <= 16) ? 16 : (hd / V <= 32) ? 32 : 64;
+  constexpr int KPW = 64 / G;              // keys per wave instruction
   const int gi = lane % G, kg = lane / G;  // lane's vector within the row, key slot
   const bool live = gi * V < hd;           // hd = 96: 12 of every 16 lanes carry data
   const int64_t kbase = lo + (int64_t)sp * DK;
@@ -93,6 +99,7 @@ __global__ __launch_bounds__(256) void swa_decode_part_k(const T* __restrict__ q
   }
   const float scale = 1.f / sqrtf((float)hd);
   // scores: each wave takes keys wave*64 .. wave*64+63 of the split
+#pragma unroll
   for (int k0 = wave * 64; k0 < wave * 64 + 64; k0 += KPW) {
     const int kk = k0 + kg;
     const int64_t kp = kbase + kk;
@@ -102,6 +109,7 @@ __global__ __launch_bounds__(256) void swa_decode_part_k(const T* __restrict__ q
 #pragma unroll
       for (int e = 0; e < V; ++e) sacc += to_f32(elem<T>(kv, e)) * qv[e];
     }
+#pragma unroll
     for (int o = 1; o < G; o <<= 1) sacc += __shfl_xor(sacc, o, 64);
     if (gi == 0 && kk < DK) ps[kk] = (kp <= pos) ? sacc * scale : -INFINITY;
   }
@@ -123,6 +131,7 @@ __global__ __launch_bounds__(256) void swa_decode_part_k(const T* __restrict__ q
   float o[V];
 #pragma unroll
   for (int e2 = 0; e2 < V; ++e2) o[e2] = 0.f;
+#pragma unroll
   for (int k0 = wave * 64; k0 < wave * 64 + 64; k0 += KPW) {
     const int kk = k0 + kg;
     const int64_t kp = kbase + kk;
@@ -151,18 +160,24 @@ template <typename T>
 __global__ void swa_decode_combine_k(const float* __restrict__ ws, int nsplit, int H, int hd,
                                      T* __restrict__ o) {
   // (every split writes its partial, possibly empty: m = -inf, l = 0)
+  __shared__ float fs[64];
+  __shared__ float Ls;
   const int h = blockIdx.x, j = threadIdx.x;
-  if (j >= hd) return;
-  float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ws[((int64_t)h * nsplit + s) * (2 + hd)]);
-  float L = 0.f, acc = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float* w = ws + ((int64_t)h * nsplit + s) * (2 + hd);
-    const float f = (w[0] == -INFINITY) ? 0.f : __expf(w[0] - M);
-    L += w[1] * f;
-    acc += w[2 + j] * f;
+  if (j < 64) {
+    float mv = -INFINITY;
+    if (j < nsplit) mv = ws[((int64_t)h * nsplit + j) * (2 + hd)];
+    const float M = wave_max(mv);
+    const float f = (j < nsplit && mv != -INFINITY) ? __expf(mv - M) : 0.f;
+    fs[j] = f;
+    const float lv = (j < nsplit) ? ws[((int64_t)h * nsplit + j) * (2 + hd) + 1] * f : 0.f;
+    const float L = wave_sum(lv);
+    if (j == 0) Ls = L;
   }
-  o[h * hd + j] = from_f32<T>(acc / L);
+  __syncthreads();
+  if (j >= hd) return;
+  float acc = 0.f;
+  for (int sp = 0; sp < nsplit; ++sp) acc += ws[((int64_t)h * nsplit + sp) * (2 + hd) + 2 + j] * fs[sp];
+  o[h * hd + j] = from_f32<T>(acc / Ls);
 }
 
 // Decode bookkeeping kernels (graph-safe: no memcpy/memset nodes).
@@ -244,17 +259,26 @@ void gelu_vec(const float* z, int F, void* act, bool bf, hipStream_t s) {
   else hipLaunchKernelGGL(gelu_vec_k<float>, dim3((F + 255) / 256), dim3(256), 0, s, z, F, (float*)act);
 }
 
-void swa_decode(const void* q, const void* kring, const void* vring, int64_t cap, int H, int hd,
-                int window, const int64_t* dstate, void* o, float* ws, bool bf, hipStream_t s) {
+template <typename T>
+void swa_decode_t(const void* q, const void* kring, const void* vring, int64_t cap, int H, int hd,
+                  int window, const int64_t* dstate, void* o, float* ws, hipStream_t s) {
   const int nsplit = (window + DK - 1) / DK;   // covers a full window
   dim3 grid(nsplit, H);
-  if (bf) {
-    hipLaunchKernelGGL(swa_decode_part_k<bf16>, grid, dim3(256), 0, s, (const bf16*)q, (const bf16*)kring, (const bf16*)vring, cap, H, hd, window, dstate, ws, nsplit);
-    hipLaunchKernelGGL(swa_decode_combine_k<bf16>, dim3(H), dim3(128), 0, s, ws, nsplit, H, hd, (bf16*)o);
-  } else {
-    hipLaunchKernelGGL(swa_decode_part_k<float>, grid, dim3(256), 0, s, (const float*)q, (const float*)kring, (const float*)vring, cap, H, hd, window, dstate, ws, nsplit);
-    hipLaunchKernelGGL(swa_decode_combine_k<float>, dim3(H), dim3(128), 0, s, ws, nsplit, H, hd, (float*)o);
+  switch (hd) {
+#define CASE(HDV) case HDV: hipLaunchKernelGGL((swa_decode_part_k<T, HDV>), grid, dim3(256), 0, s, \
+      (const T*)q, (const T*)kring, (const T*)vring, cap, H, window, dstate, ws, nsplit); break;
+    CASE(16) CASE(32) CASE(64) CASE(96) CASE(128)
+#undef CASE
+    default: return;
   }
+  // nsplit <= 64 for windows up to 16384 keys
+  hipLaunchKernelGGL(swa_decode_combine_k<T>, dim3(H), dim3(128), 0, s, ws, nsplit, H, hd, (T*)o);
+}
+
+void swa_decode(const void* q, const void* kring, const void* vring, int64_t cap, int H, int hd,
+                int window, const int64_t* dstate, void* o, float* ws, bool bf, hipStream_t s) {
+  if (bf) swa_decode_t<bf16>(q, kring, vring, cap, H, hd, window, dstate, o, ws, s);
+  else swa_decode_t<float>(q, kring, vring, cap, H, hd, window, dstate, o, ws, s);
 }
 
 void dec_begin(const int32_t* cur, const int64_t* dstate, int32_t* hist, hipStream_t s) {

@@ -45,6 +45,35 @@ __global__ void ln_fwd_k(const float* __restrict__ x, int64_t ldx, int n, int d,
   }
 }
 
+// Few rows (decode): one 256-thread block per row, two-level reduction, so a
+// single row costs a few microseconds instead of one wave's serial passes.
+template <typename T>
+__global__ __launch_bounds__(256) void ln_fwd_row_k(const float* __restrict__ x, int64_t ldx, int d,
+                                                    float eps, T* __restrict__ y, int64_t ldy,
+                                                    float* __restrict__ mean, float* __restrict__ rstd) {
+  __shared__ float red[8];
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float* xr = x + (int64_t)row * ldx;
+  float s = 0.f;
+  for (int i = tid; i < d; i += 256) s += xr[i];
+  s = wave_sum(s);
+  if (lane == 0) red[wave] = s;
+  __syncthreads();
+  const float mu = (red[0] + red[1] + red[2] + red[3]) / d;
+  float v = 0.f;
+  for (int i = tid; i < d; i += 256) { const float c = xr[i] - mu; v += c * c; }
+  v = wave_sum(v);
+  if (lane == 0) red[4 + wave] = v;
+  __syncthreads();
+  const float rs = rsqrtf((red[4] + red[5] + red[6] + red[7]) / d + eps);
+  T* yr = y + (int64_t)row * ldy;
+  for (int i = tid; i < d; i += 256) yr[i] = from_f32<T>((xr[i] - mu) * rs);
+  if (tid == 0) {
+    if (mean) mean[row] = mu;
+    if (rstd) rstd[row] = rs;
+  }
+}
+
 // acc += rstd * (dy - mean(dy) - yhat * mean(dy * yhat)); acc_lo = round(acc)
 template <typename T>
 __global__ void ln_bwd_k(const float* __restrict__ dy, const float* __restrict__ x,
@@ -325,6 +354,11 @@ void embed(const int32_t* tok, int n, const void* E, int d, int V, bool bf, floa
 void layernorm_fwd(const float* x, int64_t ldx, int n, int d, float eps, void* y, int64_t ldy,
                    float* mean, float* rstd, bool bf, hipStream_t s) {
   if (n <= 0) return;
+  if (n < 64) {
+    TSEL(bf, hipLaunchKernelGGL(ln_fwd_row_k<bf16>, dim3(n), dim3(256), 0, s, x, ldx, d, eps, (bf16*)y, ldy, mean, rstd),
+         hipLaunchKernelGGL(ln_fwd_row_k<float>, dim3(n), dim3(256), 0, s, x, ldx, d, eps, (float*)y, ldy, mean, rstd));
+    return;
+  }
   TSEL(bf, hipLaunchKernelGGL(ln_fwd_k<bf16>, dim3(nblk(n, 4)), dim3(256), 0, s, x, ldx, n, d, eps, (bf16*)y, ldy, mean, rstd),
        hipLaunchKernelGGL(ln_fwd_k<float>, dim3(nblk(n, 4)), dim3(256), 0, s, x, ldx, n, d, eps, (float*)y, ldy, mean, rstd));
 }
