@@ -58,7 +58,8 @@ enum { TTT_FP32 = 0, TTT_BF16 = 1 };
  *
  * Supported: head_dim in {16, 32, 64, 96, 128}; n_heads * head_dim ==
  * d_model; d_model % 16 == 0; d_ff % 16 == 0; vocab % 8 == 0;
- * 1 <= n_fast <= n_layers; window >= 1; 1 <= max_chunk.
+ * d_model, d_ff <= 16384 (bf16) or 8192 (fp32); 1 <= n_fast <= n_layers;
+ * 1 <= window <= 16384; 1 <= max_chunk <= 65536.
  */
 typedef struct {
   int32_t n_layers, d_model, n_heads, head_dim, d_ff, vocab, window;

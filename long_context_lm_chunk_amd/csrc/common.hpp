@@ -281,3 +281,14 @@ template <> DEVI f32x8 pack8<float>(const float* v) {
 // 2^x with the hardware instruction (no denormal range fix-up; the inputs
 // here are <= 8 and results below 2^-126 may flush to zero).
 DEVI float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// RoPE angle of pair i at position pos, in float64, reduced before the
+// float rotation (positions reach 5e5, where a float angle would be off by
+// 0.03).
+DEVI void rope_cs(int64_t pos, const double* theta, int i, float& c, float& s) {
+  const double a = (double)pos * theta[i];
+  double sd, cd;
+  sincos(a, &sd, &cd);
+  c = (float)cd;
+  s = (float)sd;
+}

@@ -1,70 +1,252 @@
-// One-token decode kernels: HBM-bound matrix-vector products, split-key
-// sliding-window attention over the ring, and the greedy argmax.  Per-token
-// cost is bounded by the window and the weights, not by the context length
-// (the constant-latency claim of the paper summary, "Key claims", and of the
-// NVIDIA blog's Figure 1 caption).
+// One-token decode kernels: HBM-bound matrix-vector products with the
+// LayerNorm, activation, RoPE and residual steps fused into them, split-key
+// sliding-window attention over the ring, and the greedy argmax.  Per-token cost is bounded by the window and the weights,
+// not by the context length (the constant-latency claim of the paper
+// summary, "Key claims", and of the NVIDIA blog's Figure 1 caption).
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace ttt {
 namespace {
 
-// y[n] = sum_k W[n][k] x[k] (+ resid[n]); W [N][K] k-contiguous.
-// One wave per output row, 16-byte loads along k.
-template <typename T, typename X>
-__global__ __launch_bounds__(256) void gemv_k(const T* __restrict__ W, const T* __restrict__ W2,
-                                              int N, int K, const X* __restrict__ x,
-                                              float* __restrict__ y, const float* __restrict__ resid) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= N) return;
-  constexpr int V = Vec16<T>::N;
-  float s = 0.f;
-  // 4 independent 16-byte loads in flight per lane per step
-  for (int pass = 0; pass < (W2 ? 2 : 1); ++pass) {   // fast weights: W0 + delta, one fp32 sum
-    const T* w = (pass ? W2 : W) + (int64_t)row * K;
-    int k = lane * V;
-    for (; k + 3 * 64 * V < K; k += 4 * 64 * V) {
-      U128 wv[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) wv[u] = ld128(w + k + u * 64 * V);
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int e = 0; e < V; ++e) s += to_f32(elem<T>(wv[u], e)) * to_f32(x[k + u * 64 * V + e]);
-    }
-    for (; k < K; k += 64 * V) {
-      const U128 wv = ld128(w + k);
-#pragma unroll
-      for (int e = 0; e < V; ++e) s += to_f32(elem<T>(wv, e)) * to_f32(x[k + e]);
-    }
+// ---------------------------------------------------------------------------
+// Matrix-vector products.  W [N][K] is k-contiguous (the library's weight
+// layout).  One wave owns one output "unit" (one row, or a pair of rows whose
+// results its epilogue combines) and streams its rows with 16-byte loads,
+// four k-steps in flight per lane; the input vector is read straight from
+// global memory (it is small and stays in L1/L2), so there is no prologue
+// and no barrier.
+//
+// LayerNorm of the input is fused algebraically: with c = x[0] as a shift
+// (against cancellation), mu' = mean(x - c) and rs = 1/sqrt(var(x) + eps),
+//   W . LN(x) = rs * (W . (x - c) - mu' * sum_k W[k]),
+// and every wave gathers sum(x - c), sum((x - c)^2) and the row sums in the
+// same pass as the dot product (the wave covers all of K).
+struct DecGemv {
+  const void* W; const void* W2;   // W2 (same shape) is added to W when set
+  int N, K;
+  const void* x; float eps;        // LN: fp32 row to normalise; else storage-type vector
+  float* y; const float* resid;    // OUT_F32: y = W x (+ resid); y may alias resid
+  float* rows; const int64_t* dstate;   // OUT_F32: y also to rows[dstate[1]][.] when set
+  float* amax;                     // OUT_F32: per-block (max, index) pairs when set
+  void* act;                       // OUT_SWIGLU / OUT_GELU: activation vector, storage type
+  int H, hd; const double* theta;  // OUT_ROPE
+  void* q; void* kr; void* vr; void* vt; int64_t cap;
+};
+
+enum { OUT_F32 = 0, OUT_SWIGLU = 1, OUT_GELU = 2, OUT_ROPE = 3 };
+
+template <int OUT> struct Units;
+// one row
+template <> struct Units<OUT_F32> {
+  static constexpr int R = 1;
+  DEVI static int count(const DecGemv& a) { return a.N; }
+  DEVI static void rows(const DecGemv&, int u, int* r) { r[0] = u; }
+};
+template <> struct Units<OUT_GELU> : Units<OUT_F32> {};
+// SwiGLU: gate and up rows of activation f (interleaved in blocks of 16)
+template <> struct Units<OUT_SWIGLU> {
+  static constexpr int R = 2;
+  DEVI static int count(const DecGemv& a) { return a.N / 2; }
+  DEVI static void rows(const DecGemv&, int u, int* r) {
+    r[0] = (u / 16) * 32 + (u % 16);
+    r[1] = r[0] + 16;
   }
-  s = wave_sum(s);
-  if (lane == 0) y[row] = s + (resid ? resid[row] : 0.f);
+};
+// RoPE: rows i and i + hd/2 of one head in the q, k or v part
+template <> struct Units<OUT_ROPE> {
+  static constexpr int R = 2;
+  DEVI static int count(const DecGemv& a) { return a.N / 2; }
+  DEVI static void rows(const DecGemv& a, int u, int* r) {
+    const int d = a.H * a.hd, half = a.hd >> 1, per = d >> 1;
+    const int part = u / per, idx = u - part * per;
+    const int h = idx / half, i = idx - h * half;
+    r[0] = part * d + h * a.hd + i;
+    r[1] = r[0] + half;
+  }
+};
+
+// V consecutive input elements as floats (x of storage type T, or fp32)
+template <typename T, bool XF32> DEVI void load_x(const void* x, int k, float* xv) {
+  constexpr int V = Vec16<T>::N;
+  if constexpr (XF32) {
+#pragma unroll
+    for (int h = 0; h < V; h += 4) {
+      const float4 f = *reinterpret_cast<const float4*>(static_cast<const float*>(x) + k + h);
+      xv[h] = f.x; xv[h + 1] = f.y; xv[h + 2] = f.z; xv[h + 3] = f.w;
+    }
+  } else {
+    const U128 u = ld128(static_cast<const T*>(x) + k);
+#pragma unroll
+    for (int e = 0; e < V; ++e) xv[e] = to_f32(elem<T>(u, e));
+  }
 }
 
-template <typename T>
-__global__ void swiglu_vec_k(const float* __restrict__ z, int F, T* __restrict__ act) {
-  const int f = blockIdx.x * blockDim.x + threadIdx.x;
-  if (f >= F) return;
-  const int c = (f / 16) * 32 + (f % 16);
-  const float g = z[c], u = z[c + 16];
-  act[f] = from_f32<T>(g / (1.f + __expf(-g)) * u);
+template <typename T, bool LN, int OUT, bool DUAL>
+__global__ __launch_bounds__(256) void dgemv_k(DecGemv a) {
+  __shared__ float bestv[4];
+  __shared__ int besti[4];
+  using U = Units<OUT>;
+  constexpr int R = U::R;
+  constexpr int P = DUAL ? 2 : 1;
+  constexpr int V = Vec16<T>::N;
+  constexpr int UN = 4;                      // k-steps in flight per lane
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int K = a.K;
+  const int u = blockIdx.x * 4 + wave;
+  const bool active = u < U::count(a);
+  float acc[R], rsum[R];
+#pragma unroll
+  for (int j = 0; j < R; ++j) { acc[j] = 0.f; rsum[j] = 0.f; }
+  float sx = 0.f, sxx = 0.f;
+  float c = 0.f;
+  if constexpr (LN) c = static_cast<const float*>(a.x)[0];
+  if (active) {
+    int r[2] = {0, 0};
+    U::rows(a, u, r);
+    const T* wr[R][P];
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      wr[j][0] = static_cast<const T*>(a.W) + (int64_t)r[j] * K;
+      if constexpr (DUAL) wr[j][1] = static_cast<const T*>(a.W2) + (int64_t)r[j] * K;
+    }
+    int k = lane * V;
+    for (; k + (UN - 1) * 64 * V < K; k += UN * 64 * V) {
+      U128 w[UN][R][P];
+#pragma unroll
+      for (int s2 = 0; s2 < UN; ++s2)
+#pragma unroll
+        for (int j = 0; j < R; ++j)
+#pragma unroll
+          for (int p = 0; p < P; ++p) w[s2][j][p] = ld128(wr[j][p] + k + s2 * 64 * V);
+#pragma unroll
+      for (int s2 = 0; s2 < UN; ++s2) {
+        float xv[V];
+        load_x<T, LN>(a.x, k + s2 * 64 * V, xv);
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          const float xe = xv[e] - c;
+          if constexpr (LN) { sx += xe; sxx += xe * xe; }
+#pragma unroll
+          for (int j = 0; j < R; ++j)
+#pragma unroll
+            for (int p = 0; p < P; ++p) {
+              const float we = to_f32(elem<T>(w[s2][j][p], e));
+              acc[j] += we * xe;
+              if constexpr (LN) rsum[j] += we;
+            }
+        }
+      }
+    }
+    for (; k < K; k += 64 * V) {
+      U128 w[R][P];
+#pragma unroll
+      for (int j = 0; j < R; ++j)
+#pragma unroll
+        for (int p = 0; p < P; ++p) w[j][p] = ld128(wr[j][p] + k);
+      float xv[V];
+      load_x<T, LN>(a.x, k, xv);
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const float xe = xv[e] - c;
+        if constexpr (LN) { sx += xe; sxx += xe * xe; }
+#pragma unroll
+        for (int j = 0; j < R; ++j)
+#pragma unroll
+          for (int p = 0; p < P; ++p) {
+            const float we = to_f32(elem<T>(w[j][p], e));
+            acc[j] += we * xe;
+            if constexpr (LN) rsum[j] += we;
+          }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < R; ++j) acc[j] = wave_sum(acc[j]);
+    if constexpr (LN) {
+      sx = wave_sum(sx);
+      sxx = wave_sum(sxx);
+      const float mu = sx / K;                              // mean of x - c
+      const float var = fmaxf(sxx / K - mu * mu, 0.f);
+      const float rs = rsqrtf(var + a.eps);
+#pragma unroll
+      for (int j = 0; j < R; ++j) acc[j] = rs * (acc[j] - mu * wave_sum(rsum[j]));
+    }
+  }
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  if (active && lane == 0) {
+    if constexpr (OUT == OUT_F32) {
+      const float v = acc[0] + (a.resid ? a.resid[u] : 0.f);
+      a.y[u] = v;
+      if (a.rows) a.rows[a.dstate[1] * a.N + u] = v;
+      bv = v;
+      bi = u;
+    } else if constexpr (OUT == OUT_GELU) {
+      const float v = acc[0];
+      static_cast<T*>(a.act)[u] = from_f32<T>(0.5f * v * (1.f + erff(v * 0.70710678118654752f)));
+    } else if constexpr (OUT == OUT_SWIGLU) {
+      const float g = acc[0], up = acc[1];
+      static_cast<T*>(a.act)[u] = from_f32<T>(g / (1.f + __expf(-g)) * up);
+    } else {
+      const int d = a.H * a.hd, half = a.hd >> 1, per = d >> 1;
+      const int part = u / per, idx = u - part * per;
+      const int h = idx / half, i = idx - h * half;
+      const int j1 = h * a.hd + i, j2 = j1 + half;
+      const int64_t pos = a.dstate[0];
+      const int64_t slot = pos % a.cap;
+      float v1 = acc[0], v2 = acc[1];
+      if (part < 2) {
+        float cs, sn;
+        rope_cs(pos, a.theta, i, cs, sn);
+        const float r1 = v1 * cs - v2 * sn, r2 = v2 * cs + v1 * sn;
+        v1 = r1;
+        v2 = r2;
+      }
+      if (part == 0) {
+        static_cast<T*>(a.q)[j1] = from_f32<T>(v1);
+        static_cast<T*>(a.q)[j2] = from_f32<T>(v2);
+      } else if (part == 1) {
+        static_cast<T*>(a.kr)[slot * d + j1] = from_f32<T>(v1);
+        static_cast<T*>(a.kr)[slot * d + j2] = from_f32<T>(v2);
+      } else {
+        static_cast<T*>(a.vr)[slot * d + j1] = from_f32<T>(v1);
+        static_cast<T*>(a.vr)[slot * d + j2] = from_f32<T>(v2);
+        static_cast<T*>(a.vt)[(int64_t)j1 * a.cap + slot] = from_f32<T>(v1);
+        static_cast<T*>(a.vt)[(int64_t)j2 * a.cap + slot] = from_f32<T>(v2);
+      }
+    }
+  }
+  if constexpr (OUT == OUT_F32) {
+    if (a.amax) {   // uniform over the block: per-block greedy candidate
+      if (lane == 0) { bestv[wave] = bv; besti[wave] = bi; }
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        float b = bestv[0];
+        int ib = besti[0];
+        for (int w2 = 1; w2 < 4; ++w2)
+          if (bestv[w2] > b || (bestv[w2] == b && besti[w2] < ib)) { b = bestv[w2]; ib = besti[w2]; }
+        a.amax[2 * blockIdx.x] = b;
+        a.amax[2 * blockIdx.x + 1] = __int_as_float(ib);
+      }
+    }
+  }
 }
-template <typename T>
-__global__ void gelu_vec_k(const float* __restrict__ z, int F, T* __restrict__ act) {
-  const int f = blockIdx.x * blockDim.x + threadIdx.x;
-  if (f >= F) return;
-  const float v = z[f];
-  act[f] = from_f32<T>(0.5f * v * (1.f + erff(v * 0.70710678118654752f)));
-}
+
+// ---------------------------------------------------------------------------
+// Split-key attention of the one new query over the window.
 
 constexpr int DK = 256;   // keys per split
 
 // Partial attention of one query over keys [lo + split*DK, ...) of head h,
-// bandwidth-bound.  Lanes work in groups of G = hd/8 (16 for hd = 128):
-// a group covers one key's row with one 16-byte load per lane, so a wave
-// reads 64/G whole rows per instruction.  ws per (h, split): m, l, o[hd].
+// bandwidth-bound.  Lanes work in groups of G = hd/8 (16 for hd = 128): a
+// group covers one key's row with one 16-byte load per lane, so a wave reads
+// 64/G whole rows per instruction.  Each wave takes 64 keys on its own: a
+// lane's group reduces the score of each of its keys by shuffles, so every
+// lane already holds the scores of exactly the keys whose V elements it
+// accumulates; the wave's softmax statistics come from wave reductions and
+// the four waves meet once, in LDS, at the end.  The V loads are issued as
+// soon as the K rows are consumed, so they overlap the softmax.
+// ws per (h, split): m, l, o[hd].
 template <typename T, int hd>
 __global__ __launch_bounds__(256) void swa_decode_part_k(const T* __restrict__ q,
                                                          const T* __restrict__ kr,
@@ -78,9 +260,8 @@ __global__ __launch_bounds__(256) void swa_decode_part_k(const T* __restrict__ q
   int64_t lo = pos - window + 1;
   if (lo < 0) lo = 0;
   constexpr int V = Vec16<T>::N;
-  __shared__ float ps[DK];
-  __shared__ float red[8];
-  __shared__ float oacc[4][128];
+  __shared__ float wml[4][2];
+  __shared__ float wo[4][hd];
   const int h = blockIdx.y, sp = blockIdx.x, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int d = H * hd;
@@ -88,74 +269,87 @@ __global__ __launch_bounds__(256) void swa_decode_part_k(const T* __restrict__ q
   constexpr int G = (hd / V <= 1) ? 1 : (hd / V <= 2) ? 2 : (hd / V <= 4) ? 4 : (hd / V <= 8) ? 8
                   : (hd / V <= 16) ? 16 : (hd / V <= 32) ? 32 : 64;
   constexpr int KPW = 64 / G;              // keys per wave instruction
+  constexpr int NI = 64 / KPW;             // instructions per wave (64 keys)
   const int gi = lane % G, kg = lane / G;  // lane's vector within the row, key slot
   const bool live = gi * V < hd;           // hd = 96: 12 of every 16 lanes carry data
   const int64_t kbase = lo + (int64_t)sp * DK;
+  // ring slot of the split's first key; every key read is < window <= cap
+  // past it, so one conditional subtraction replaces a 64-bit modulo
+  const int64_t s0 = kbase % cap;
   float qv[V];
   {
     const U128 qq = live ? ld128(q + h * hd + gi * V) : zero128();
+    const float scale = 1.f / sqrtf((float)hd);
 #pragma unroll
-    for (int e = 0; e < V; ++e) qv[e] = to_f32(elem<T>(qq, e));
+    for (int e = 0; e < V; ++e) qv[e] = to_f32(elem<T>(qq, e)) * scale;
   }
-  const float scale = 1.f / sqrtf((float)hd);
-  // scores: each wave takes keys wave*64 .. wave*64+63 of the split
+  int64_t off[NI];
+  bool ok[NI];
+  U128 kv[NI];
 #pragma unroll
-  for (int k0 = wave * 64; k0 < wave * 64 + 64; k0 += KPW) {
-    const int kk = k0 + kg;
-    const int64_t kp = kbase + kk;
-    float sacc = 0.f;
-    if (live && kp <= pos) {
-      const U128 kv = ld128(kr + (kp % cap) * d + h * hd + gi * V);
-#pragma unroll
-      for (int e = 0; e < V; ++e) sacc += to_f32(elem<T>(kv, e)) * qv[e];
-    }
-#pragma unroll
-    for (int o = 1; o < G; o <<= 1) sacc += __shfl_xor(sacc, o, 64);
-    if (gi == 0 && kk < DK) ps[kk] = (kp <= pos) ? sacc * scale : -INFINITY;
+  for (int it = 0; it < NI; ++it) {
+    const int kk = wave * 64 + it * KPW + kg;
+    int64_t slot = s0 + kk;
+    if (slot >= cap) slot -= cap;
+    off[it] = slot * d + h * hd + gi * V;
+    ok[it] = kbase + kk <= pos;
+    kv[it] = (live && ok[it]) ? ld128(kr + off[it]) : zero128();
   }
-  __syncthreads();
-  // max and sum over the split's 256 scores
-  float mx = wave_max(ps[tid]);
-  if (lane == 0) red[wave] = mx;
-  __syncthreads();
-  const float m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float e = (ps[tid] == -INFINITY) ? 0.f : __expf(ps[tid] - m);
-  float sm = wave_sum(e);
-  __syncthreads();
-  ps[tid] = e;
-  if (lane == 0) red[4 + wave] = sm;
-  __syncthreads();
-  const float l = red[4] + red[5] + red[6] + red[7];
-  // o = sum_k p_k v_k: same lane grouping, each lane accumulates its V
-  // elements over the keys of its slot, then slots and waves are summed
+  float sc[NI];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int it = 0; it < NI; ++it) {
+    float a = 0.f;
+#pragma unroll
+    for (int e = 0; e < V; ++e) a += to_f32(elem<T>(kv[it], e)) * qv[e];
+#pragma unroll
+    for (int o = 1; o < G; o <<= 1) a += __shfl_xor(a, o, 64);
+    sc[it] = ok[it] ? a : -INFINITY;
+    mx = fmaxf(mx, sc[it]);
+  }
+  U128 vv[NI];
+#pragma unroll
+  for (int it = 0; it < NI; ++it) vv[it] = (live && ok[it]) ? ld128(vr + off[it]) : zero128();
+  const float m = wave_max(mx);
+  float l = 0.f;
+#pragma unroll
+  for (int it = 0; it < NI; ++it) {
+    sc[it] = (sc[it] == -INFINITY) ? 0.f : __expf(sc[it] - m);
+    l += sc[it];
+  }
+  // every lane of a group holds the same scores: count each key once
+  l = wave_sum(gi == 0 ? l : 0.f);
   float o[V];
 #pragma unroll
-  for (int e2 = 0; e2 < V; ++e2) o[e2] = 0.f;
+  for (int e = 0; e < V; ++e) o[e] = 0.f;
 #pragma unroll
-  for (int k0 = wave * 64; k0 < wave * 64 + 64; k0 += KPW) {
-    const int kk = k0 + kg;
-    const int64_t kp = kbase + kk;
-    if (live && kk < DK && kp <= pos) {
-      const float pk = ps[kk];
-      const U128 vv = ld128(vr + (kp % cap) * d + h * hd + gi * V);
+  for (int it = 0; it < NI; ++it)
 #pragma unroll
-      for (int e2 = 0; e2 < V; ++e2) o[e2] += pk * to_f32(elem<T>(vv, e2));
-    }
-  }
+    for (int e = 0; e < V; ++e) o[e] += sc[it] * to_f32(elem<T>(vv[it], e));
   // reduce over key slots (lanes gi + G*kg) within the wave
-  for (int off = G; off < 64; off <<= 1)
+  for (int offs = G; offs < 64; offs <<= 1)
 #pragma unroll
-    for (int e2 = 0; e2 < V; ++e2) o[e2] += __shfl_xor(o[e2], off, 64);
+    for (int e = 0; e < V; ++e) o[e] += __shfl_xor(o[e], offs, 64);
   if (kg == 0 && live) {
 #pragma unroll
-    for (int e2 = 0; e2 < V; ++e2) oacc[wave][gi * V + e2] = o[e2];
+    for (int e = 0; e < V; ++e) wo[wave][gi * V + e] = o[e];
   }
+  if (lane == 0) { wml[wave][0] = m; wml[wave][1] = l; }
   __syncthreads();
+  // merge the four waves (a wave with no key in range has m = -inf, l = 0)
+  const float M = fmaxf(fmaxf(wml[0][0], wml[1][0]), fmaxf(wml[2][0], wml[3][0]));
+  float f[4];
+#pragma unroll
+  for (int w2 = 0; w2 < 4; ++w2) f[w2] = (wml[w2][0] == -INFINITY) ? 0.f : __expf(wml[w2][0] - M);
   float* w = ws + ((int64_t)h * nsplit + sp) * (2 + hd);
-  if (tid < hd) w[2 + tid] = oacc[0][tid] + oacc[1][tid] + oacc[2][tid] + oacc[3][tid];
-  if (tid == 0) { w[0] = m; w[1] = l; }
+  if (tid < hd) w[2 + tid] = wo[0][tid] * f[0] + wo[1][tid] * f[1] + wo[2][tid] * f[2] + wo[3][tid] * f[3];
+  if (tid == 0) {
+    w[0] = M;
+    w[1] = wml[0][1] * f[0] + wml[1][1] * f[1] + wml[2][1] * f[2] + wml[3][1] * f[3];
+  }
 }
 
+// Combine the splits of head h: o = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s.
 template <typename T>
 __global__ void swa_decode_combine_k(const float* __restrict__ ws, int nsplit, int H, int hd,
                                      T* __restrict__ o) {
@@ -180,19 +374,22 @@ __global__ void swa_decode_combine_k(const float* __restrict__ ws, int nsplit, i
   o[h * hd + j] = from_f32<T>(acc / Ls);
 }
 
+// ---------------------------------------------------------------------------
 // Decode bookkeeping kernels (graph-safe: no memcpy/memset nodes).
 // dstate = {pos, ci}: position being read, index within the decode chunk.
-__global__ void dec_begin_k(const int32_t* __restrict__ cur, const int64_t* __restrict__ dstate,
-                            int32_t* __restrict__ hist) {
-  if (threadIdx.x == 0) hist[dstate[1]] = *cur;
-}
-__global__ void dec_end_k(int64_t* __restrict__ dstate) {
-  if (threadIdx.x == 0) { dstate[0] += 1; dstate[1] += 1; }
-}
-__global__ void dec_row_k(const float* __restrict__ x, int d, const int64_t* __restrict__ dstate,
-                          float* __restrict__ rows) {
-  const int64_t ci = dstate[1];
-  for (int i = threadIdx.x; i < d; i += blockDim.x) rows[ci * d + i] = x[i];
+
+// x = E[cur] as fp32, and the token read at this position into hist[ci].
+template <typename T>
+__global__ void dec_embed_k(const int32_t* __restrict__ cur, const int64_t* __restrict__ dstate,
+                            int32_t* __restrict__ hist, const T* __restrict__ E, int d, int V,
+                            float* __restrict__ x, int* __restrict__ err) {
+  int id = *cur;
+  if (threadIdx.x == 0) hist[dstate[1]] = id;
+  if (id < 0 || id >= V) {
+    if (threadIdx.x == 0) atomicOr(err, 1);
+    id = 0;
+  }
+  for (int i = threadIdx.x; i < d; i += blockDim.x) x[i] = to_f32(E[(int64_t)id * d + i]);
 }
 __global__ void dec_set_k(int64_t* __restrict__ dstate, int64_t pos, int64_t ci) {
   if (threadIdx.x == 0) { dstate[0] = pos; dstate[1] = ci; }
@@ -204,16 +401,19 @@ __global__ void copy_f32_k(const float* __restrict__ a, float* __restrict__ b, i
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) b[i] = a[i];
 }
 
-// Greedy choice: largest logit, lowest id on ties.  The chosen id also goes
-// to hist[ci + 1] (the target of the position just read).
-__global__ void argmax_k(const float* __restrict__ z, int V, int32_t* __restrict__ out,
-                         int32_t* __restrict__ hist, const int64_t* __restrict__ dstate) {
-  __shared__ float bv[1024];
-  __shared__ int bi[1024];
+// Greedy choice over the per-block (max, index) pairs of the head product:
+// largest logit, lowest id on ties (a NaN logit is never chosen).  The id
+// goes to *out and, when hist is set, to hist[ci + 1] (the target of the
+// position just read); with advance set the decode state moves on by one.
+__global__ void argmax_part_k(const float* __restrict__ part, int nb, int32_t* __restrict__ out,
+                              int32_t* __restrict__ hist, int64_t* __restrict__ dstate, int advance) {
+  __shared__ float bv[256];
+  __shared__ int bi[256];
   float best = -INFINITY;
   int idx = 0x7fffffff;
-  for (int i = threadIdx.x; i < V; i += blockDim.x) {
-    const float v = z[i];
+  for (int b = threadIdx.x; b < nb; b += blockDim.x) {
+    const float v = part[2 * b];
+    const int i = __float_as_int(part[2 * b + 1]);
     if (v > best || (v == best && i < idx)) { best = v; idx = i; }
   }
   bv[threadIdx.x] = best;
@@ -233,36 +433,15 @@ __global__ void argmax_k(const float* __restrict__ z, int V, int32_t* __restrict
   if (threadIdx.x == 0) {
     const int r = bi[0] == 0x7fffffff ? 0 : bi[0];
     *out = r;
-    if (hist) hist[dstate ? dstate[1] + 1 : 0] = r;
+    if (hist) hist[dstate[1] + 1] = r;
+    if (advance) { dstate[0] += 1; dstate[1] += 1; }
   }
-}
-
-}  // namespace
-
-void gemv(const void* W, const void* W2, int N, int K, const void* x, bool x_f32, float* y,
-          const float* resid, bool bf, hipStream_t s) {
-  dim3 grid((N + 3) / 4);
-  if (bf) {
-    if (x_f32) hipLaunchKernelGGL((gemv_k<bf16, float>), grid, dim3(256), 0, s, (const bf16*)W, (const bf16*)W2, N, K, (const float*)x, y, resid);
-    else hipLaunchKernelGGL((gemv_k<bf16, bf16>), grid, dim3(256), 0, s, (const bf16*)W, (const bf16*)W2, N, K, (const bf16*)x, y, resid);
-  } else {
-    hipLaunchKernelGGL((gemv_k<float, float>), grid, dim3(256), 0, s, (const float*)W, (const float*)W2, N, K, (const float*)x, y, resid);
-  }
-}
-
-void swiglu_vec(const float* z, int F, void* act, bool bf, hipStream_t s) {
-  if (bf) hipLaunchKernelGGL(swiglu_vec_k<bf16>, dim3((F + 255) / 256), dim3(256), 0, s, z, F, (bf16*)act);
-  else hipLaunchKernelGGL(swiglu_vec_k<float>, dim3((F + 255) / 256), dim3(256), 0, s, z, F, (float*)act);
-}
-void gelu_vec(const float* z, int F, void* act, bool bf, hipStream_t s) {
-  if (bf) hipLaunchKernelGGL(gelu_vec_k<bf16>, dim3((F + 255) / 256), dim3(256), 0, s, z, F, (bf16*)act);
-  else hipLaunchKernelGGL(gelu_vec_k<float>, dim3((F + 255) / 256), dim3(256), 0, s, z, F, (float*)act);
 }
 
 template <typename T>
 void swa_decode_t(const void* q, const void* kring, const void* vring, int64_t cap, int H, int hd,
                   int window, const int64_t* dstate, void* o, float* ws, hipStream_t s) {
-  const int nsplit = (window + DK - 1) / DK;   // covers a full window
+  const int nsplit = (window + DK - 1) / DK;   // covers a full window (<= 64 splits)
   dim3 grid(nsplit, H);
   switch (hd) {
 #define CASE(HDV) case HDV: hipLaunchKernelGGL((swa_decode_part_k<T, HDV>), grid, dim3(256), 0, s, \
@@ -271,9 +450,33 @@ void swa_decode_t(const void* q, const void* kring, const void* vring, int64_t c
 #undef CASE
     default: return;
   }
-  // nsplit <= 64 for windows up to 16384 keys
   hipLaunchKernelGGL(swa_decode_combine_k<T>, dim3(H), dim3(128), 0, s, ws, nsplit, H, hd, (T*)o);
 }
+
+template <typename T, bool LN, int OUT, bool DUAL>
+void dgemv_launch(const DecGemv& a, hipStream_t s) {
+  const int units = (OUT == OUT_SWIGLU || OUT == OUT_ROPE) ? a.N / 2 : a.N;
+  hipLaunchKernelGGL((dgemv_k<T, LN, OUT, DUAL>), dim3((units + 3) / 4), dim3(256), 0, s, a);
+}
+
+template <typename T>
+void dgemv_t(const DecGemv& a, bool ln, int out, hipStream_t s) {
+  const bool dual = a.W2 != nullptr;
+  if (ln) {
+    switch (out) {
+      case OUT_ROPE: dgemv_launch<T, true, OUT_ROPE, false>(a, s); break;
+      case OUT_SWIGLU: dual ? dgemv_launch<T, true, OUT_SWIGLU, true>(a, s)
+                            : dgemv_launch<T, true, OUT_SWIGLU, false>(a, s); break;
+      case OUT_GELU: dual ? dgemv_launch<T, true, OUT_GELU, true>(a, s)
+                          : dgemv_launch<T, true, OUT_GELU, false>(a, s); break;
+      default: dgemv_launch<T, true, OUT_F32, false>(a, s); break;
+    }
+  } else {
+    dual ? dgemv_launch<T, false, OUT_F32, true>(a, s) : dgemv_launch<T, false, OUT_F32, false>(a, s);
+  }
+}
+
+}  // namespace
 
 void swa_decode(const void* q, const void* kring, const void* vring, int64_t cap, int H, int hd,
                 int window, const int64_t* dstate, void* o, float* ws, bool bf, hipStream_t s) {
@@ -281,12 +484,50 @@ void swa_decode(const void* q, const void* kring, const void* vring, int64_t cap
   else swa_decode_t<float>(q, kring, vring, cap, H, hd, window, dstate, o, ws, s);
 }
 
-void dec_begin(const int32_t* cur, const int64_t* dstate, int32_t* hist, hipStream_t s) {
-  hipLaunchKernelGGL(dec_begin_k, dim3(1), dim3(64), 0, s, cur, dstate, hist);
+void dgemv_ln_rope(const void* Wqkv, int d, const float* x, float eps, int H, int hd,
+                   const double* theta, const int64_t* dstate, void* q, void* kring, void* vring,
+                   void* vtring, int64_t cap, bool bf, hipStream_t s) {
+  DecGemv a{};
+  a.W = Wqkv; a.N = 3 * d; a.K = d; a.x = x; a.eps = eps;
+  a.H = H; a.hd = hd; a.theta = theta; a.dstate = dstate;
+  a.q = q; a.kr = kring; a.vr = vring; a.vt = vtring; a.cap = cap;
+  if (bf) dgemv_t<bf16>(a, true, OUT_ROPE, s);
+  else dgemv_t<float>(a, true, OUT_ROPE, s);
 }
-void dec_end(int64_t* dstate, hipStream_t s) { hipLaunchKernelGGL(dec_end_k, dim3(1), dim3(64), 0, s, dstate); }
-void dec_row(const float* x, int d, const int64_t* dstate, float* rows, hipStream_t s) {
-  hipLaunchKernelGGL(dec_row_k, dim3(1), dim3(256), 0, s, x, d, dstate, rows);
+
+void dgemv_ln_act(const void* Wup, const void* Wup2, int F, int d, const float* x, float eps,
+                  bool swiglu, void* act, bool bf, hipStream_t s) {
+  DecGemv a{};
+  a.W = Wup; a.W2 = Wup2; a.N = swiglu ? 2 * F : F; a.K = d; a.x = x; a.eps = eps; a.act = act;
+  const int out = swiglu ? OUT_SWIGLU : OUT_GELU;
+  if (bf) dgemv_t<bf16>(a, true, out, s);
+  else dgemv_t<float>(a, true, out, s);
+}
+
+void dgemv_vec(const void* W, const void* W2, int N, int K, const void* x, float* y,
+               const float* resid, float* rows, const int64_t* dstate, float* amax, bool bf,
+               hipStream_t s) {
+  DecGemv a{};
+  a.W = W; a.W2 = W2; a.N = N; a.K = K; a.x = x; a.y = y; a.resid = resid;
+  a.rows = rows; a.dstate = dstate; a.amax = amax;
+  if (bf) dgemv_t<bf16>(a, false, OUT_F32, s);
+  else dgemv_t<float>(a, false, OUT_F32, s);
+}
+
+void dgemv_ln_head(const void* U, int V, int d, const float* x, float eps, float* logits,
+                   float* amax, bool bf, hipStream_t s) {
+  DecGemv a{};
+  a.W = U; a.N = V; a.K = d; a.x = x; a.eps = eps; a.y = logits; a.amax = amax;
+  if (bf) dgemv_t<bf16>(a, true, OUT_F32, s);
+  else dgemv_t<float>(a, true, OUT_F32, s);
+}
+
+int dgemv_blocks(int units) { return (units + 3) / 4; }
+
+void dec_embed(const int32_t* cur, const int64_t* dstate, int32_t* hist, const void* E, int d, int V,
+               float* x, int* err, bool bf, hipStream_t s) {
+  if (bf) hipLaunchKernelGGL(dec_embed_k<bf16>, dim3(1), dim3(256), 0, s, cur, dstate, hist, (const bf16*)E, d, V, x, err);
+  else hipLaunchKernelGGL(dec_embed_k<float>, dim3(1), dim3(256), 0, s, cur, dstate, hist, (const float*)E, d, V, x, err);
 }
 void dec_set(int64_t* dstate, int64_t pos, int64_t ci, hipStream_t s) {
   hipLaunchKernelGGL(dec_set_k, dim3(1), dim3(64), 0, s, dstate, pos, ci);
@@ -295,10 +536,9 @@ void copy_i32(const int32_t* a, int32_t* b, hipStream_t s) { hipLaunchKernelGGL(
 void copy_f32(const float* a, float* b, int n, hipStream_t s) {
   hipLaunchKernelGGL(copy_f32_k, dim3((n + 255) / 256 > 1024 ? 1024 : (n + 255) / 256), dim3(256), 0, s, a, b, n);
 }
-
-void argmax_tok(const float* logits, int V, int32_t* out_tok, int32_t* tok_hist, const int64_t* dstate,
-                hipStream_t s) {
-  hipLaunchKernelGGL(argmax_k, dim3(1), dim3(1024), 0, s, logits, V, out_tok, tok_hist, dstate);
+void argmax_part(const float* part, int nb, int32_t* out_tok, int32_t* hist, int64_t* dstate,
+                 bool advance, hipStream_t s) {
+  hipLaunchKernelGGL(argmax_part_k, dim3(1), dim3(256), 0, s, part, nb, out_tok, hist, dstate, (int)advance);
 }
 
 }  // namespace ttt

@@ -118,16 +118,6 @@ __global__ void fill_k(float* __restrict__ p, int64_t n, float v) {
     p[i] = v;
 }
 
-// Angle of pair i at position pos, in float64, reduced before the float
-// rotation (positions reach 5e5, where a float angle would be off by 0.03).
-DEVI void rope_cs(int64_t pos, const double* theta, int i, float& c, float& s) {
-  const double a = (double)pos * theta[i];
-  double sd, cd;
-  sincos(a, &sd, &cd);
-  c = (float)cd;
-  s = (float)sd;
-}
-
 // qkv [n][3*H*hd]; writes q_out [n][H*hd] (rotated), K (rotated) and V to
 // ring slot (pos0 + t) mod cap.  One thread per (t, h, i < hd/2).
 template <typename T>
@@ -156,33 +146,6 @@ __global__ void rope_qkv_k(const T* __restrict__ qkv, int n, int H, int hd, int6
   kr[slot * d + j2] = from_f32<T>(k2 * c + k1 * s);
   vr[slot * d + j1] = row[2 * d + j1];
   vr[slot * d + j2] = row[2 * d + j2];
-}
-
-template <typename T>
-__global__ void rope_qkv_f32in_k(const float* __restrict__ qkv, int H, int hd,
-                                 const int64_t* __restrict__ dstate,
-                                 const double* __restrict__ theta, T* __restrict__ qo,
-                                 T* __restrict__ kr, T* __restrict__ vr, T* __restrict__ vt,
-                                 int64_t cap) {
-  const int64_t pos = dstate[0];   // decode position from the device-side state
-  const int half = hd >> 1;
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= H * half) return;
-  const int i = idx % half, h = idx / half;
-  const int d = H * hd;
-  float c, s;
-  rope_cs(pos, theta, i, c, s);
-  const int j1 = h * hd + i, j2 = j1 + half;
-  const float q1 = qkv[j1], q2 = qkv[j2], k1 = qkv[d + j1], k2 = qkv[d + j2];
-  qo[j1] = from_f32<T>(q1 * c - q2 * s);
-  qo[j2] = from_f32<T>(q2 * c + q1 * s);
-  const int64_t slot = pos % cap;
-  kr[slot * d + j1] = from_f32<T>(k1 * c - k2 * s);
-  kr[slot * d + j2] = from_f32<T>(k2 * c + k1 * s);
-  vr[slot * d + j1] = from_f32<T>(qkv[2 * d + j1]);
-  vr[slot * d + j2] = from_f32<T>(qkv[2 * d + j2]);
-  vt[(int64_t)j1 * cap + slot] = from_f32<T>(qkv[2 * d + j1]);
-  vt[(int64_t)j2 * cap + slot] = from_f32<T>(qkv[2 * d + j2]);
 }
 
 // Transposed rotation of dQ and dK inside dqkv [n][3d].
@@ -397,13 +360,6 @@ void rope_qkv(const void* qkv, int n, int H, int hd, int64_t pos0, const double*
   if (total <= 0) return;
   TSEL(bf, hipLaunchKernelGGL(rope_qkv_k<bf16>, dim3(nblk(total, 256)), dim3(256), 0, s, (const bf16*)qkv, n, H, hd, pos0, theta, (bf16*)q_out, (bf16*)kring, (bf16*)vring, cap),
        hipLaunchKernelGGL(rope_qkv_k<float>, dim3(nblk(total, 256)), dim3(256), 0, s, (const float*)qkv, n, H, hd, pos0, theta, (float*)q_out, (float*)kring, (float*)vring, cap));
-}
-
-void rope_qkv_f32in(const float* qkv, int H, int hd, const int64_t* dstate, const double* theta, void* q_out,
-                    void* kring, void* vring, void* vtring, int64_t cap, bool bf, hipStream_t s) {
-  const int total = H * (hd / 2);
-  TSEL(bf, hipLaunchKernelGGL(rope_qkv_f32in_k<bf16>, dim3(nblk(total, 256)), dim3(256), 0, s, qkv, H, hd, dstate, theta, (bf16*)q_out, (bf16*)kring, (bf16*)vring, (bf16*)vtring, cap),
-       hipLaunchKernelGGL(rope_qkv_f32in_k<float>, dim3(nblk(total, 256)), dim3(256), 0, s, qkv, H, hd, dstate, theta, (float*)q_out, (float*)kring, (float*)vring, (float*)vtring, cap));
 }
 
 void rope_bwd(void* dqkv, int n, int H, int hd, int64_t pos0, const double* theta, bool bf,

@@ -89,23 +89,39 @@ void ring_transpose(const void* src, int64_t ld, int64_t src_cap, int n, int H, 
 void swa_bwd(const AttnParams& p, bool bf16, hipStream_t s);
 
 // ---- decode (decode.hip)
-// y = (W + W2) x (+ resid); W2 may be null
-void gemv(const void* W, const void* W2, int N, int K, const void* x, bool x_f32, float* y,
-          const float* resid, bool bf16, hipStream_t s);
-void swiglu_vec(const float* z, int F, void* act, bool bf16, hipStream_t s);
-void gelu_vec(const float* z, int F, void* act, bool bf16, hipStream_t s);
-// decode kernels read the position from dstate = {pos, ci} on the device,
-// so one token's launches can be captured once and replayed
+// Every decode kernel reads the position from dstate = {pos, ci} on the
+// device, so one token's launches can be captured once and replayed.
+// Matrix-vector products (W [N][K] k-contiguous, W2 of the same shape added
+// when non-null); LN(x) is the LayerNorm of the fp32 row x, fused:
+//   dgemv_ln_rope: LN(x) -> Wqkv; RoPE on q and k, q to `q`, k and v to the
+//                  rings at slot pos % cap, v also to the transposed ring
+//   dgemv_ln_act:  LN(x) -> up-projection; act = silu(gate) * up (SwiGLU,
+//                  rows interleaved in blocks of 16) or gelu, storage type
+//   dgemv_vec:     y = (W + W2) x (+ resid; y may alias resid); optionally y
+//                  also to rows[dstate[1]][.] and per-block argmax pairs
+//   dgemv_ln_head: logits = U LN(x), per-block argmax pairs in amax
+// amax holds 2 floats per block; dgemv_blocks(units) gives the block count.
+void dgemv_ln_rope(const void* Wqkv, int d, const float* x, float eps, int H, int hd,
+                   const double* theta, const int64_t* dstate, void* q, void* kring, void* vring,
+                   void* vtring, int64_t cap, bool bf16, hipStream_t s);
+void dgemv_ln_act(const void* Wup, const void* Wup2, int F, int d, const float* x, float eps,
+                  bool swiglu, void* act, bool bf16, hipStream_t s);
+void dgemv_vec(const void* W, const void* W2, int N, int K, const void* x, float* y,
+               const float* resid, float* rows, const int64_t* dstate, float* amax, bool bf16,
+               hipStream_t s);
+void dgemv_ln_head(const void* U, int V, int d, const float* x, float eps, float* logits,
+                   float* amax, bool bf16, hipStream_t s);
+int dgemv_blocks(int units);
+// split-key attention of the new query over the window + per-head combine
 void swa_decode(const void* q, const void* kring, const void* vring, int64_t cap, int H, int hd,
                 int window, const int64_t* dstate, void* o, float* ws, bool bf16, hipStream_t s);
-void argmax_tok(const float* logits, int V, int32_t* out_tok, int32_t* tok_hist, const int64_t* dstate,
-                hipStream_t s);
-void rope_qkv_f32in(const float* qkv, int H, int hd, const int64_t* dstate, const double* theta,
-                    void* q_out, void* kring, void* vring, void* vtring, int64_t cap, bool bf16,
-                    hipStream_t s);
-void dec_begin(const int32_t* cur, const int64_t* dstate, int32_t* hist, hipStream_t s);
-void dec_end(int64_t* dstate, hipStream_t s);
-void dec_row(const float* x, int d, const int64_t* dstate, float* rows, hipStream_t s);
+// x = E[*cur] (fp32) and hist[ci] = *cur
+void dec_embed(const int32_t* cur, const int64_t* dstate, int32_t* hist, const void* E, int d, int V,
+               float* x, int* err, bool bf16, hipStream_t s);
+// greedy token from per-block argmax pairs; hist[ci + 1] = token when hist is
+// set; dstate advanced by one position when `advance`
+void argmax_part(const float* part, int nb, int32_t* out_tok, int32_t* hist, int64_t* dstate,
+                 bool advance, hipStream_t s);
 void dec_set(int64_t* dstate, int64_t pos, int64_t ci, hipStream_t s);
 void copy_i32(const int32_t* a, int32_t* b, hipStream_t s);
 void copy_f32(const float* a, float* b, int n, hipStream_t s);

@@ -140,10 +140,11 @@ struct ttt_model {
   float* attn_part = nullptr; float* attn_ml = nullptr;   // key-range split partials
   float* split_ws = nullptr; int64_t split_cap = 0;         // split-K partials of the GEMMs
   // decode
-  float* xd = nullptr; void* ad = nullptr; float* qkvd = nullptr; void* qd = nullptr; void* od = nullptr;
-  float* zd = nullptr; void* actd = nullptr; float* logits = nullptr; float* attn_ws = nullptr;
+  float* xd = nullptr; void* qd = nullptr; void* od = nullptr;
+  void* actd = nullptr; float* logits = nullptr; float* attn_ws = nullptr;
   int32_t* hist = nullptr; int32_t* cur_tok = nullptr;
   int64_t* dstate = nullptr;            // decode state on the device: {pos, ci}
+  float* amax = nullptr;                // per-block (max, index) pairs of the head product
   hipGraphExec_t dec_exec = nullptr;    // one decode token, captured once
   int* err = nullptr;
   float* nanv = nullptr;
@@ -169,7 +170,12 @@ int check_config(const ttt_config* c) {
   if (c->d_model % 16 || c->d_ff % 16 || c->d_ff <= 0) return fail(TTT_ERR_CONFIG, "d_model and d_ff must be positive multiples of 16");
   if (c->vocab <= 0 || c->vocab % 8) return fail(TTT_ERR_CONFIG, "vocab must be a positive multiple of 8");
   if (c->n_layers <= 0 || c->n_fast < 1 || c->n_fast > c->n_layers) return fail(TTT_ERR_CONFIG, "need 1 <= n_fast <= n_layers");
-  if (c->window < 1) return fail(TTT_ERR_CONFIG, "window must be >= 1");
+  if (c->window < 1 || c->window > 16384) return fail(TTT_ERR_CONFIG, "window must be in [1, 16384]");
+  {
+    const int kmax = c->dtype == TTT_BF16 ? 16384 : 8192;   // decode input vector held in LDS
+    if (c->d_model > kmax || c->d_ff > kmax)
+      return fail(TTT_ERR_CONFIG, "d_model and d_ff must be <= 16384 (bf16) or 8192 (fp32)");
+  }
   if (c->max_chunk < 1 || c->max_chunk > (1 << 16)) return fail(TTT_ERR_CONFIG, "max_chunk must be in [1, 65536]");
   if (c->prefill_block < 0) return fail(TTT_ERR_CONFIG, "prefill_block must be >= 0");
   if (!(c->ln_eps > 0.f) || !(c->rope_base > 1.f)) return fail(TTT_ERR_CONFIG, "ln_eps > 0 and rope_base > 1 required");
@@ -272,11 +278,8 @@ size_t layout(ttt_model* m, void* base) {
   m->split_ws = cv.take<float>((size_t)m->split_cap * 4);
   // decode
   m->xd = cv.take<float>((size_t)d * 4);
-  m->ad = cv.take<void>((size_t)d * es);
-  m->qkvd = cv.take<float>((size_t)3 * d * 4);
   m->qd = cv.take<void>((size_t)d * es);
   m->od = cv.take<void>((size_t)d * es);
-  m->zd = cv.take<float>((size_t)F2 * 4);
   m->actd = cv.take<void>((size_t)F * es);
   m->logits = cv.take<float>((size_t)V * 4);
   const int64_t nsplit = (m->W + 255) / 256 + 1;
@@ -284,6 +287,7 @@ size_t layout(ttt_model* m, void* base) {
   m->hist = cv.take<int32_t>((size_t)(C + 2) * 4);
   m->cur_tok = cv.take<int32_t>(4);
   m->dstate = cv.take<int64_t>(16);
+  m->amax = cv.take<float>((size_t)2 * dgemv_blocks(m->V) * 4);
   m->err = cv.take<int>(4);
   m->nanv = cv.take<float>(4);
   (void)c;
@@ -554,33 +558,30 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
 // its K/V to every ring, and leave the next greedy token in cur_tok.  No
 // argument depends on the position, so the launches can be captured once.
 void decode_body(ttt_model* m, hipStream_t s) {
-  const int d = m->d, F = m->F, F2 = m->F2, V = m->V;
+  const int d = m->d, F = m->F, V = m->V;
   const bool bf = m->bf;
   const float eps = m->c.ln_eps;
-  dec_begin(m->cur_tok, m->dstate, m->hist, s);
-  embed(m->cur_tok, 1, m->E, d, V, bf, m->xd, m->err, s);
+  const bool sw = m->c.mlp == TTT_MLP_SWIGLU;
+  dec_embed(m->cur_tok, m->dstate, m->hist, m->E, d, V, m->xd, m->err, bf, s);
   for (int l = 0; l < m->L; ++l) {
     Layer& ly = m->layers[l];
     const int j = l - m->f0;
-    layernorm_fwd(m->xd, d, 1, d, eps, m->ad, d, nullptr, nullptr, bf, s);
-    gemv(ly.wqkv, nullptr, 3 * d, d, m->ad, !bf, m->qkvd, nullptr, bf, s);
-    rope_qkv_f32in(m->qkvd, m->H, m->hd, m->dstate, m->theta, m->qd, ly.kring, ly.vring, ly.vtring,
-                   ly.cap, bf, s);
-    swa_decode(m->qd, ly.kring, ly.vring, ly.cap, m->H, m->hd, m->W, m->dstate, m->od, m->attn_ws, bf, s);
-    gemv(ly.wo, nullptr, d, d, m->od, !bf, m->xd, m->xd, bf, s);
-    if (j == 0) dec_row(m->xd, d, m->dstate, m->hA, s);   // phase-B input of this position
-    layernorm_fwd(m->xd, d, 1, d, eps, m->ad, d, nullptr, nullptr, bf, s);
+    // LN1 -> qkv -> RoPE -> rings
+    dgemv_ln_rope(ly.wqkv, d, m->xd, eps, m->H, m->hd, m->theta, m->dstate, m->qd, ly.kring,
+                  ly.vring, ly.vtring, ly.cap, bf, s);
+    swa_decode(m->qd, ly.kring, ly.vring, ly.cap, m->H, m->hd, m->W, m->dstate, m->od, m->attn_ws,
+               bf, s);
+    // x += o Wo; the first fast block's input row is also kept for the
+    // decode-chunk update
+    dgemv_vec(ly.wo, nullptr, d, d, m->od, m->xd, m->xd, j == 0 ? m->hA : nullptr, m->dstate,
+              nullptr, bf, s);
     const void* dup = j >= 0 ? m->fast[j].s_up : nullptr;
     const void* ddn = j >= 0 ? m->fast[j].s_dn : nullptr;
-    gemv(ly.wup, dup, F2, d, m->ad, !bf, m->zd, nullptr, bf, s);
-    if (m->c.mlp == TTT_MLP_SWIGLU) swiglu_vec(m->zd, F, m->actd, bf, s);
-    else gelu_vec(m->zd, F, m->actd, bf, s);
-    gemv(ly.wdn, ddn, d, F, m->actd, !bf, m->xd, m->xd, bf, s);
+    dgemv_ln_act(ly.wup, dup, F, d, m->xd, eps, sw, m->actd, bf, s);   // LN2 -> up -> act
+    dgemv_vec(ly.wdn, ddn, d, F, m->actd, m->xd, m->xd, nullptr, nullptr, nullptr, bf, s);
   }
-  layernorm_fwd(m->xd, d, 1, d, eps, m->ad, d, nullptr, nullptr, bf, s);
-  gemv(m->U, nullptr, V, d, m->ad, !bf, m->logits, nullptr, bf, s);
-  argmax_tok(m->logits, V, m->cur_tok, m->hist, m->dstate, s);
-  dec_end(m->dstate, s);
+  dgemv_ln_head(m->U, V, d, m->xd, eps, m->logits, m->amax, bf, s);
+  argmax_part(m->amax, dgemv_blocks(V), m->cur_tok, m->hist, m->dstate, true, s);
 }
 
 int sync_and_check(ttt_model* m, hipStream_t s) {
@@ -761,8 +762,9 @@ int ttt_prefill(ttt_model* m, const int32_t* tokens, int64_t T, int32_t chunk, f
         // first decode token: argmax of the last position's logits from this
         // chunk's last read
         const char* frow = static_cast<const char*>(m->fN) + (size_t)(n - 1) * d * m->es;
-        gemv(m->U, nullptr, m->V, d, frow, !m->bf, m->logits, nullptr, m->bf, s);
-        argmax_tok(m->logits, m->V, m->cur_tok, nullptr, nullptr, s);
+        dgemv_vec(m->U, nullptr, m->V, d, frow, m->logits, nullptr, nullptr, nullptr, m->amax,
+                  m->bf, s);
+        argmax_part(m->amax, dgemv_blocks(m->V), m->cur_tok, nullptr, nullptr, false, s);
         dec_set(m->dstate, T, 0, s);
       }
     }
