@@ -12,8 +12,8 @@ namespace {
 // ---------------------------------------------------------------------------
 // Matrix-vector products.  W [N][K] is k-contiguous (the library's weight
 // layout).  One wave owns one output "unit" (one row, or a pair of rows whose
-// results its epilogue combines) and streams its rows with 16-byte loads,
-// four k-steps in flight per lane; the input vector is read straight from
+// results its epilogue combines) and streams its rows with 16-byte loads, up
+// to sixteen in flight per lane; the input vector is read straight from
 // global memory (it is small and stays in L1/L2), so there is no prologue
 // and no barrier.
 //
@@ -82,18 +82,23 @@ template <typename T, bool XF32> DEVI void load_x(const void* x, int k, float* x
   }
 }
 
-template <typename T, bool LN, int OUT, bool DUAL>
+// UN = k-steps (16-byte loads per row) in flight per lane; KS = waves that
+// split one unit's k range (steps interleaved), reduced through LDS.
+template <typename T, bool LN, int OUT, bool DUAL, int UN, int KS>
 __global__ __launch_bounds__(256) void dgemv_k(DecGemv a) {
-  __shared__ float bestv[4];
-  __shared__ int besti[4];
   using U = Units<OUT>;
   constexpr int R = U::R;
   constexpr int P = DUAL ? 2 : 1;
   constexpr int V = Vec16<T>::N;
-  constexpr int UN = 4;                      // k-steps in flight per lane
+  constexpr int UPB = 4 / KS;                // units per block
+  constexpr int NP = 2 * R + 2;              // partials per wave
+  __shared__ float part[4][NP];
+  __shared__ float bestv[UPB];
+  __shared__ int besti[UPB];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ks = wave % KS, ul = wave / KS;
   const int K = a.K;
-  const int u = blockIdx.x * 4 + wave;
+  const int u = blockIdx.x * UPB + ul;
   const bool active = u < U::count(a);
   float acc[R], rsum[R];
 #pragma unroll
@@ -110,19 +115,21 @@ __global__ __launch_bounds__(256) void dgemv_k(DecGemv a) {
       wr[j][0] = static_cast<const T*>(a.W) + (int64_t)r[j] * K;
       if constexpr (DUAL) wr[j][1] = static_cast<const T*>(a.W2) + (int64_t)r[j] * K;
     }
-    int k = lane * V;
-    for (; k + (UN - 1) * 64 * V < K; k += UN * 64 * V) {
+    // k-step t of this wave covers elements ((t * KS + ks) * 64 + lane) * V
+    constexpr int SK = KS * 64 * V;          // elements between a wave's steps
+    int k = (ks * 64 + lane) * V;
+    for (; k + (UN - 1) * SK < K; k += UN * SK) {
       U128 w[UN][R][P];
 #pragma unroll
       for (int s2 = 0; s2 < UN; ++s2)
 #pragma unroll
         for (int j = 0; j < R; ++j)
 #pragma unroll
-          for (int p = 0; p < P; ++p) w[s2][j][p] = ld128(wr[j][p] + k + s2 * 64 * V);
+          for (int p = 0; p < P; ++p) w[s2][j][p] = ld128(wr[j][p] + k + s2 * SK);
 #pragma unroll
       for (int s2 = 0; s2 < UN; ++s2) {
         float xv[V];
-        load_x<T, LN>(a.x, k + s2 * 64 * V, xv);
+        load_x<T, LN>(a.x, k + s2 * SK, xv);
 #pragma unroll
         for (int e = 0; e < V; ++e) {
           const float xe = xv[e] - c;
@@ -138,7 +145,7 @@ __global__ __launch_bounds__(256) void dgemv_k(DecGemv a) {
         }
       }
     }
-    for (; k < K; k += 64 * V) {
+    for (; k < K; k += SK) {
       U128 w[R][P];
 #pragma unroll
       for (int j = 0; j < R; ++j)
@@ -161,20 +168,42 @@ __global__ __launch_bounds__(256) void dgemv_k(DecGemv a) {
       }
     }
 #pragma unroll
-    for (int j = 0; j < R; ++j) acc[j] = wave_sum(acc[j]);
+    for (int j = 0; j < R; ++j) {
+      acc[j] = wave_sum(acc[j]);
+      if constexpr (LN) rsum[j] = wave_sum(rsum[j]);
+    }
     if constexpr (LN) {
       sx = wave_sum(sx);
       sxx = wave_sum(sxx);
-      const float mu = sx / K;                              // mean of x - c
-      const float var = fmaxf(sxx / K - mu * mu, 0.f);
-      const float rs = rsqrtf(var + a.eps);
+    }
+  }
+  if constexpr (KS > 1) {
+    if (lane == 0) {
 #pragma unroll
-      for (int j = 0; j < R; ++j) acc[j] = rs * (acc[j] - mu * wave_sum(rsum[j]));
+      for (int j = 0; j < R; ++j) { part[wave][j] = acc[j]; part[wave][R + j] = rsum[j]; }
+      part[wave][2 * R] = sx;
+      part[wave][2 * R + 1] = sxx;
+    }
+    __syncthreads();
+    if (ks == 0 && lane == 0) {
+      for (int t = 1; t < KS; ++t) {
+#pragma unroll
+        for (int j = 0; j < R; ++j) { acc[j] += part[wave + t][j]; rsum[j] += part[wave + t][R + j]; }
+        sx += part[wave + t][2 * R];
+        sxx += part[wave + t][2 * R + 1];
+      }
     }
   }
   float bv = -INFINITY;
   int bi = 0x7fffffff;
-  if (active && lane == 0) {
+  if (active && ks == 0 && lane == 0) {
+    if constexpr (LN) {
+      const float mu = sx / K;                              // mean of x - c
+      const float var = fmaxf(sxx / K - mu * mu, 0.f);
+      const float rs = rsqrtf(var + a.eps);
+#pragma unroll
+      for (int j = 0; j < R; ++j) acc[j] = rs * (acc[j] - mu * rsum[j]);
+    }
     if constexpr (OUT == OUT_F32) {
       const float v = acc[0] + (a.resid ? a.resid[u] : 0.f);
       a.y[u] = v;
@@ -189,23 +218,23 @@ __global__ __launch_bounds__(256) void dgemv_k(DecGemv a) {
       static_cast<T*>(a.act)[u] = from_f32<T>(g / (1.f + __expf(-g)) * up);
     } else {
       const int d = a.H * a.hd, half = a.hd >> 1, per = d >> 1;
-      const int part = u / per, idx = u - part * per;
+      const int part_ = u / per, idx = u - part_ * per;
       const int h = idx / half, i = idx - h * half;
       const int j1 = h * a.hd + i, j2 = j1 + half;
       const int64_t pos = a.dstate[0];
       const int64_t slot = pos % a.cap;
       float v1 = acc[0], v2 = acc[1];
-      if (part < 2) {
+      if (part_ < 2) {
         float cs, sn;
         rope_cs(pos, a.theta, i, cs, sn);
         const float r1 = v1 * cs - v2 * sn, r2 = v2 * cs + v1 * sn;
         v1 = r1;
         v2 = r2;
       }
-      if (part == 0) {
+      if (part_ == 0) {
         static_cast<T*>(a.q)[j1] = from_f32<T>(v1);
         static_cast<T*>(a.q)[j2] = from_f32<T>(v2);
-      } else if (part == 1) {
+      } else if (part_ == 1) {
         static_cast<T*>(a.kr)[slot * d + j1] = from_f32<T>(v1);
         static_cast<T*>(a.kr)[slot * d + j2] = from_f32<T>(v2);
       } else {
@@ -218,12 +247,12 @@ __global__ __launch_bounds__(256) void dgemv_k(DecGemv a) {
   }
   if constexpr (OUT == OUT_F32) {
     if (a.amax) {   // uniform over the block: per-block greedy candidate
-      if (lane == 0) { bestv[wave] = bv; besti[wave] = bi; }
+      if (ks == 0 && lane == 0) { bestv[ul] = bv; besti[ul] = bi; }
       __syncthreads();
       if (threadIdx.x == 0) {
         float b = bestv[0];
         int ib = besti[0];
-        for (int w2 = 1; w2 < 4; ++w2)
+        for (int w2 = 1; w2 < UPB; ++w2)
           if (bestv[w2] > b || (bestv[w2] == b && besti[w2] < ib)) { b = bestv[w2]; ib = besti[w2]; }
         a.amax[2 * blockIdx.x] = b;
         a.amax[2 * blockIdx.x + 1] = __int_as_float(ib);
@@ -405,33 +434,40 @@ __global__ void copy_f32_k(const float* __restrict__ a, float* __restrict__ b, i
 // largest logit, lowest id on ties (a NaN logit is never chosen).  The id
 // goes to *out and, when hist is set, to hist[ci + 1] (the target of the
 // position just read); with advance set the decode state moves on by one.
-__global__ void argmax_part_k(const float* __restrict__ part, int nb, int32_t* __restrict__ out,
-                              int32_t* __restrict__ hist, int64_t* __restrict__ dstate, int advance) {
-  __shared__ float bv[256];
-  __shared__ int bi[256];
+DEVI void better(float& bv, int& bi, float v, int i) {
+  if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
+}
+__global__ __launch_bounds__(1024) void argmax_part_k(const float2* __restrict__ part, int nb,
+                                                      int32_t* __restrict__ out,
+                                                      int32_t* __restrict__ hist,
+                                                      int64_t* __restrict__ dstate, int advance) {
+  __shared__ float wv[16];
+  __shared__ int wi[16];
   float best = -INFINITY;
   int idx = 0x7fffffff;
-  for (int b = threadIdx.x; b < nb; b += blockDim.x) {
-    const float v = part[2 * b];
-    const int i = __float_as_int(part[2 * b + 1]);
-    if (v > best || (v == best && i < idx)) { best = v; idx = i; }
-  }
-  bv[threadIdx.x] = best;
-  bi[threadIdx.x] = idx;
-  __syncthreads();
-  for (int o = blockDim.x / 2; o > 0; o >>= 1) {
-    if (threadIdx.x < o) {
-      const float v2 = bv[threadIdx.x + o];
-      const int i2 = bi[threadIdx.x + o];
-      if (v2 > bv[threadIdx.x] || (v2 == bv[threadIdx.x] && i2 < bi[threadIdx.x])) {
-        bv[threadIdx.x] = v2;
-        bi[threadIdx.x] = i2;
-      }
+  // eight independent loads per thread per round (8192 pairs in one round)
+  for (int b0 = threadIdx.x; b0 < nb; b0 += 8 * 1024) {
+    float2 p[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int b = b0 + u * 1024;
+      p[u] = b < nb ? part[b] : make_float2(-INFINITY, __int_as_float(0x7fffffff));
     }
-    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 8; ++u) better(best, idx, p[u].x, __float_as_int(p[u].y));
   }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float v2 = __shfl_xor(best, o, 64);
+    const int i2 = __shfl_xor(idx, o, 64);
+    better(best, idx, v2, i2);
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) { wv[wave] = best; wi[wave] = idx; }
+  __syncthreads();
   if (threadIdx.x == 0) {
-    const int r = bi[0] == 0x7fffffff ? 0 : bi[0];
+    for (int w = 1; w < 16; ++w) better(best, idx, wv[w], wi[w]);
+    const int r = idx == 0x7fffffff ? 0 : idx;
     *out = r;
     if (hist) hist[dstate[1] + 1] = r;
     if (advance) { dstate[0] += 1; dstate[1] += 1; }
@@ -453,26 +489,40 @@ void swa_decode_t(const void* q, const void* kring, const void* vring, int64_t c
   hipLaunchKernelGGL(swa_decode_combine_k<T>, dim3(H), dim3(128), 0, s, ws, nsplit, H, hd, (T*)o);
 }
 
-template <typename T, bool LN, int OUT, bool DUAL>
+template <typename T, bool LN, int OUT, bool DUAL, int UN = 4, int KS = 1>
 void dgemv_launch(const DecGemv& a, hipStream_t s) {
   const int units = (OUT == OUT_SWIGLU || OUT == OUT_ROPE) ? a.N / 2 : a.N;
-  hipLaunchKernelGGL((dgemv_k<T, LN, OUT, DUAL>), dim3((units + 3) / 4), dim3(256), 0, s, a);
+  const int upb = 4 / KS;
+  hipLaunchKernelGGL((dgemv_k<T, LN, OUT, DUAL, UN, KS>), dim3((units + upb - 1) / upb), dim3(256), 0, s, a);
+}
+
+// Launch shapes from a sweep on MI355X (bf16, 3B shapes): two loads in flight
+// with the k range split over the block's four waves is best or within a
+// few per cent for the LayerNorm and down products; the 32000-row head
+// prefers one row per wave, the 3072-square output product UN = 2, KS = 1.
+enum { SHAPE_SPLIT = 0, SHAPE_ROWS = 1, SHAPE_ROWS2 = 2 };
+template <typename T, bool LN, int OUT, bool DUAL>
+void dgemv_shaped(const DecGemv& a, int shape, hipStream_t s) {
+  if (shape == SHAPE_ROWS) dgemv_launch<T, LN, OUT, DUAL, 1, 1>(a, s);
+  else if (shape == SHAPE_ROWS2) dgemv_launch<T, LN, OUT, DUAL, 2, 1>(a, s);
+  else dgemv_launch<T, LN, OUT, DUAL, 2, 4>(a, s);
 }
 
 template <typename T>
-void dgemv_t(const DecGemv& a, bool ln, int out, hipStream_t s) {
+void dgemv_t(const DecGemv& a, bool ln, int out, int shape, hipStream_t s) {
   const bool dual = a.W2 != nullptr;
   if (ln) {
     switch (out) {
-      case OUT_ROPE: dgemv_launch<T, true, OUT_ROPE, false>(a, s); break;
-      case OUT_SWIGLU: dual ? dgemv_launch<T, true, OUT_SWIGLU, true>(a, s)
-                            : dgemv_launch<T, true, OUT_SWIGLU, false>(a, s); break;
-      case OUT_GELU: dual ? dgemv_launch<T, true, OUT_GELU, true>(a, s)
-                          : dgemv_launch<T, true, OUT_GELU, false>(a, s); break;
-      default: dgemv_launch<T, true, OUT_F32, false>(a, s); break;
+      case OUT_ROPE: dgemv_shaped<T, true, OUT_ROPE, false>(a, shape, s); break;
+      case OUT_SWIGLU: dual ? dgemv_shaped<T, true, OUT_SWIGLU, true>(a, shape, s)
+                            : dgemv_shaped<T, true, OUT_SWIGLU, false>(a, shape, s); break;
+      case OUT_GELU: dual ? dgemv_shaped<T, true, OUT_GELU, true>(a, shape, s)
+                          : dgemv_shaped<T, true, OUT_GELU, false>(a, shape, s); break;
+      default: dgemv_shaped<T, true, OUT_F32, false>(a, shape, s); break;
     }
   } else {
-    dual ? dgemv_launch<T, false, OUT_F32, true>(a, s) : dgemv_launch<T, false, OUT_F32, false>(a, s);
+    dual ? dgemv_shaped<T, false, OUT_F32, true>(a, shape, s)
+         : dgemv_shaped<T, false, OUT_F32, false>(a, shape, s);
   }
 }
 
@@ -491,8 +541,8 @@ void dgemv_ln_rope(const void* Wqkv, int d, const float* x, float eps, int H, in
   a.W = Wqkv; a.N = 3 * d; a.K = d; a.x = x; a.eps = eps;
   a.H = H; a.hd = hd; a.theta = theta; a.dstate = dstate;
   a.q = q; a.kr = kring; a.vr = vring; a.vt = vtring; a.cap = cap;
-  if (bf) dgemv_t<bf16>(a, true, OUT_ROPE, s);
-  else dgemv_t<float>(a, true, OUT_ROPE, s);
+  if (bf) dgemv_t<bf16>(a, true, OUT_ROPE, SHAPE_SPLIT, s);
+  else dgemv_t<float>(a, true, OUT_ROPE, SHAPE_SPLIT, s);
 }
 
 void dgemv_ln_act(const void* Wup, const void* Wup2, int F, int d, const float* x, float eps,
@@ -500,8 +550,8 @@ void dgemv_ln_act(const void* Wup, const void* Wup2, int F, int d, const float* 
   DecGemv a{};
   a.W = Wup; a.W2 = Wup2; a.N = swiglu ? 2 * F : F; a.K = d; a.x = x; a.eps = eps; a.act = act;
   const int out = swiglu ? OUT_SWIGLU : OUT_GELU;
-  if (bf) dgemv_t<bf16>(a, true, out, s);
-  else dgemv_t<float>(a, true, out, s);
+  if (bf) dgemv_t<bf16>(a, true, out, SHAPE_SPLIT, s);
+  else dgemv_t<float>(a, true, out, SHAPE_SPLIT, s);
 }
 
 void dgemv_vec(const void* W, const void* W2, int N, int K, const void* x, float* y,
@@ -510,19 +560,21 @@ void dgemv_vec(const void* W, const void* W2, int N, int K, const void* x, float
   DecGemv a{};
   a.W = W; a.W2 = W2; a.N = N; a.K = K; a.x = x; a.y = y; a.resid = resid;
   a.rows = rows; a.dstate = dstate; a.amax = amax;
-  if (bf) dgemv_t<bf16>(a, false, OUT_F32, s);
-  else dgemv_t<float>(a, false, OUT_F32, s);
+  // amax pairs are per block: with them, one row per wave (4 rows per block)
+  const int shape = amax ? SHAPE_ROWS : (K < 4096 && !W2) ? SHAPE_ROWS2 : SHAPE_SPLIT;
+  if (bf) dgemv_t<bf16>(a, false, OUT_F32, shape, s);
+  else dgemv_t<float>(a, false, OUT_F32, shape, s);
 }
 
 void dgemv_ln_head(const void* U, int V, int d, const float* x, float eps, float* logits,
                    float* amax, bool bf, hipStream_t s) {
   DecGemv a{};
   a.W = U; a.N = V; a.K = d; a.x = x; a.eps = eps; a.y = logits; a.amax = amax;
-  if (bf) dgemv_t<bf16>(a, true, OUT_F32, s);
-  else dgemv_t<float>(a, true, OUT_F32, s);
+  if (bf) dgemv_t<bf16>(a, true, OUT_F32, SHAPE_ROWS, s);
+  else dgemv_t<float>(a, true, OUT_F32, SHAPE_ROWS, s);
 }
 
-int dgemv_blocks(int units) { return (units + 3) / 4; }
+int dgemv_blocks(int units) { return (units + 3) / 4; }   // SHAPE_ROWS: 4 rows per block
 
 void dec_embed(const int32_t* cur, const int64_t* dstate, int32_t* hist, const void* E, int d, int V,
                float* x, int* err, bool bf, hipStream_t s) {
@@ -538,7 +590,8 @@ void copy_f32(const float* a, float* b, int n, hipStream_t s) {
 }
 void argmax_part(const float* part, int nb, int32_t* out_tok, int32_t* hist, int64_t* dstate,
                  bool advance, hipStream_t s) {
-  hipLaunchKernelGGL(argmax_part_k, dim3(1), dim3(256), 0, s, part, nb, out_tok, hist, dstate, (int)advance);
+  hipLaunchKernelGGL(argmax_part_k, dim3(1), dim3(1024), 0, s, reinterpret_cast<const float2*>(part), nb,
+                     out_tok, hist, dstate, (int)advance);
 }
 
 }  // namespace ttt
