@@ -178,11 +178,23 @@ int ttt_timing_read(struct ttt_model* m, int32_t cls, double* total_ms, int64_t*
  * Layouts (a_kc, b_kc) = (1,1), (1,0) overwrite C; (0,0) is the weight-
  * gradient kernel and ADDS the product to C (its SGD epilogue run with
  * lr = -1).  Row strides must be multiples of 8 elements, pointers 16-byte
- * aligned.
+ * aligned; N and ldc multiples of 4 with ldc >= N (the output is written in
+ * groups of 4 columns).  Otherwise TTT_ERR_ARG and nothing is launched.
  */
 int ttt_diag_gemm(int32_t dtype, int32_t a_kc, int32_t b_kc, int32_t M, int32_t N, int32_t K,
                   const void* A, int64_t lda, const void* B, int64_t ldb, float* C, int64_t ldc,
                   void* stream);
+
+/*
+ * Diagnostic choice of the GEMM core for the bf16 products whose operands
+ * are both k-contiguous (forward products, head): mode 0 = by shape (the
+ * default: the 256x256 core for long reductions and large grids, the
+ * 128x128 core otherwise), 1 = the 256x256 core wherever it applies, 2 = the
+ * 128x128 core only.  Process-wide; returns the previous mode, or the
+ * current one unchanged for any other value.  For parity tests that must
+ * reach a core the default would not pick at their sizes.
+ */
+int ttt_diag_gemm_core(int32_t mode);
 
 #ifdef __cplusplus
 }

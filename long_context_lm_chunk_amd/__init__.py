@@ -57,6 +57,7 @@ def _load():
         "ttt_timing_read": ([vp, i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64),
                              ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
         "ttt_diag_gemm": ([i32, i32, i32, i32, i32, i32, vp, i64, vp, i64, vp, i64, vp], ctypes.c_int),
+        "ttt_diag_gemm_core": ([i32], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -69,7 +70,16 @@ lib = _load()
 
 EXPORTED = ["ttt_workspace_bytes", "ttt_model_load", "ttt_prefill", "ttt_fast_weight",
             "ttt_decode_step", "ttt_reset", "ttt_model_free", "ttt_status_str", "ttt_last_error",
-            "ttt_timing_enable", "ttt_timing_read", "ttt_diag_gemm"]
+            "ttt_timing_enable", "ttt_timing_read", "ttt_diag_gemm", "ttt_diag_gemm_core"]
+
+
+GEMM_CORE_AUTO, GEMM_CORE_BIG, GEMM_CORE_SMALL = 0, 1, 2
+
+
+def diag_gemm_core(mode: int) -> int:
+    """Select the GEMM core for bf16 k-contiguous products (see
+    ttt_diag_gemm_core); returns the previous mode."""
+    return int(lib.ttt_diag_gemm_core(int(mode)))
 
 
 def diag_gemm(A, B, M, N, K, a_kc: bool, b_kc: bool, C=None):

@@ -24,6 +24,7 @@
 //   CEGRAD  g = (softmax - onehot(target)) / n_targets, rows without a target 0
 #include "common.hpp"
 #include "kernels.hpp"
+#include <type_traits>
 
 namespace ttt {
 
@@ -149,6 +150,86 @@ template <> DEVI float4 load4<bf16>(const bf16* p) {
 
 DEVI float gelu_erf(float z) { return 0.5f * z * (1.f + erff(z * 0.70710678118654752f)); }
 DEVI float silu(float z) { return z / (1.f + __expf(-z)); }
+
+// Epilogue over an fp32 tile staged in LDS: rows [0, nr) x cols [0, nc) of
+// st (row pitch ES floats) are output rows row0.. and columns n0.. .  Every
+// thread takes runs of 4 consecutive columns (16-byte fp32 / 8-byte bf16
+// vector accesses).  With a K split (gridDim.z > 1) the raw partial goes to
+// slab z of split_ws instead.
+template <int EPI, typename TO>
+DEVI void epi_apply(const GemmParams& p, const float* st, int ES, int nr, int nc, int row0, int n0,
+                    int tid, int nthr) {
+  if (gridDim.z > 1) {
+    float* slab = p.split_ws + (int64_t)blockIdx.z * p.M * p.N;
+    for (int g = tid; g < nr * (nc / 4); g += nthr) {
+      const int r = g / (nc / 4), c = (g % (nc / 4)) * 4;
+      const int row = row0 + r, col = n0 + c;
+      if (row >= p.M || col >= p.N) continue;
+      *reinterpret_cast<float4*>(slab + (int64_t)row * p.N + col) =
+          *reinterpret_cast<const float4*>(st + r * ES + c);
+    }
+    return;
+  }
+  if constexpr (EPI == EPI_SWIGLU) {
+    // columns: gate block 32c..32c+15, up block 32c+16..32c+31 -> act 16c..16c+15
+    for (int g = tid; g < nr * (nc / 8); g += nthr) {
+      const int r = g / (nc / 8), q = g % (nc / 8);      // q: 4-wide group of act columns
+      const int row = row0 + r;
+      const int cg = (q / 4) * 32 + (q % 4) * 4;          // gate column in the tile
+      if (row >= p.M || n0 + cg >= p.N) continue;   // N % 32 == 0: gate in => up in
+      const float4 gv = *reinterpret_cast<const float4*>(st + r * ES + cg);
+      const float4 uv = *reinterpret_cast<const float4*>(st + r * ES + cg + 16);
+      TO* z = static_cast<TO*>(p.C) + (int64_t)row * p.ldc + n0;
+      store4<TO>(z + cg, gv);
+      store4<TO>(z + cg + 16, uv);
+      float4 a;
+      a.x = silu(gv.x) * uv.x; a.y = silu(gv.y) * uv.y; a.z = silu(gv.z) * uv.z; a.w = silu(gv.w) * uv.w;
+      store4<TO>(static_cast<TO*>(p.C2) + (int64_t)row * p.ldc2 + n0 / 2 + (q / 4) * 16 + (q % 4) * 4, a);
+    }
+  } else {
+    for (int g = tid; g < nr * (nc / 4); g += nthr) {
+      const int r = g / (nc / 4), c = (g % (nc / 4)) * 4;
+      const int row = row0 + r, col = n0 + c;
+      if (row >= p.M || col >= p.N) continue;         // N is a multiple of 4
+      const float4 v = *reinterpret_cast<const float4*>(st + r * ES + c);
+      const int64_t ci = (int64_t)row * p.ldc + col;
+      if constexpr (EPI == EPI_STORE) {
+        store4<TO>(static_cast<TO*>(p.C) + ci, v);
+      } else if constexpr (EPI == EPI_RESID) {
+        const float4 rr = *reinterpret_cast<const float4*>(p.R + (int64_t)row * p.ldr + col);
+        float4 o; o.x = rr.x + v.x; o.y = rr.y + v.y; o.z = rr.z + v.z; o.w = rr.w + v.w;
+        *reinterpret_cast<float4*>(static_cast<float*>(p.C) + ci) = o;
+      } else if constexpr (EPI == EPI_GELU) {
+        store4<TO>(static_cast<TO*>(p.C) + ci, v);
+        float4 a; a.x = gelu_erf(v.x); a.y = gelu_erf(v.y); a.z = gelu_erf(v.z); a.w = gelu_erf(v.w);
+        store4<TO>(static_cast<TO*>(p.C2) + (int64_t)row * p.ldc2 + col, a);
+      } else if constexpr (EPI == EPI_SGD) {
+        float4* wp = reinterpret_cast<float4*>(static_cast<float*>(p.C) + ci);
+        float4 w = *wp;
+        w.x -= p.alpha * v.x; w.y -= p.alpha * v.y; w.z -= p.alpha * v.z; w.w -= p.alpha * v.w;
+        *wp = w;
+        if (p.C2) store4<TO>(static_cast<TO*>(p.C2) + (int64_t)row * p.ldc2 + col, w);
+        if (p.C3) {
+          const float4 w0 = load4<TO>(static_cast<const TO*>(p.W0) + ci);
+          float4 cur; cur.x = w0.x + w.x; cur.y = w0.y + w.y; cur.z = w0.z + w.z; cur.w = w0.w + w.w;
+          store4<TO>(static_cast<TO*>(p.C3) + ci, cur);
+        }
+      } else if constexpr (EPI == EPI_CEGRAD) {
+        float4 gq = {0.f, 0.f, 0.f, 0.f};
+        if (row < p.n_tgt) {
+          const float l = p.lse[row];
+          const int t = p.tgt[row];
+          gq.x = __expf(v.x - l) - (col == t ? 1.f : 0.f);
+          gq.y = __expf(v.y - l) - (col + 1 == t ? 1.f : 0.f);
+          gq.z = __expf(v.z - l) - (col + 2 == t ? 1.f : 0.f);
+          gq.w = __expf(v.w - l) - (col + 3 == t ? 1.f : 0.f);
+          gq.x *= p.alpha; gq.y *= p.alpha; gq.z *= p.alpha; gq.w *= p.alpha;
+        }
+        store4<TO>(static_cast<TO*>(p.C) + ci, gq);
+      }
+    }
+  }
+}
 
 template <typename T, bool A_KC, bool B_KC, int EPI, typename TO, bool DUAL>
 __global__ __launch_bounds__(NT, 2) void gemm_kernel(GemmParams p) {
@@ -286,77 +367,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(GemmParams p) {
         for (int e = 0; e < 4; ++e)
           st[(wm * 64 + i * 16 + 4 * (lane >> 4) + e) * ES + wn * 64 + j * 16 + (lane & 15)] = acc[i][j][e];
     __syncthreads();
-    if (gridDim.z > 1) {
-      // split-K partial: slab z of [z][M][N] fp32
-      float* slab = p.split_ws + (int64_t)blockIdx.z * p.M * p.N;
-      for (int g = tid; g < BM * (BN / 4); g += NT) {
-        const int r = g / (BN / 4), c = (g % (BN / 4)) * 4;
-        const int row = m0 + r, col = n0 + c;
-        if (row >= p.M || col >= p.N) continue;
-        *reinterpret_cast<float4*>(slab + (int64_t)row * p.N + col) =
-            *reinterpret_cast<const float4*>(st + r * ES + c);
-      }
-      return;
-    }
-    if constexpr (EPI == EPI_SWIGLU) {
-      // columns: gate block 32c..32c+15, up block 32c+16..32c+31 -> act 16c..16c+15
-      for (int g = tid; g < BM * (BN / 8); g += NT) {
-        const int r = g / (BN / 8), q = g % (BN / 8);      // q: 4-wide group of act columns
-        const int row = m0 + r;
-        const int cg = (q / 4) * 32 + (q % 4) * 4;          // gate column in the tile
-        if (row >= p.M || n0 + cg >= p.N) continue;   // N % 32 == 0: gate in => up in
-        const float4 gv = *reinterpret_cast<const float4*>(st + r * ES + cg);
-        const float4 uv = *reinterpret_cast<const float4*>(st + r * ES + cg + 16);
-        TO* z = static_cast<TO*>(p.C) + (int64_t)row * p.ldc + n0;
-        store4<TO>(z + cg, gv);
-        store4<TO>(z + cg + 16, uv);
-        float4 a;
-        a.x = silu(gv.x) * uv.x; a.y = silu(gv.y) * uv.y; a.z = silu(gv.z) * uv.z; a.w = silu(gv.w) * uv.w;
-        store4<TO>(static_cast<TO*>(p.C2) + (int64_t)row * p.ldc2 + n0 / 2 + (q / 4) * 16 + (q % 4) * 4, a);
-      }
-    } else {
-      for (int g = tid; g < BM * (BN / 4); g += NT) {
-        const int r = g / (BN / 4), c = (g % (BN / 4)) * 4;
-        const int row = m0 + r, col = n0 + c;
-        if (row >= p.M || col >= p.N) continue;         // N is a multiple of 4
-        const float4 v = *reinterpret_cast<const float4*>(st + r * ES + c);
-        const int64_t ci = (int64_t)row * p.ldc + col;
-        if constexpr (EPI == EPI_STORE) {
-          store4<TO>(static_cast<TO*>(p.C) + ci, v);
-        } else if constexpr (EPI == EPI_RESID) {
-          const float4 rr = *reinterpret_cast<const float4*>(p.R + (int64_t)row * p.ldr + col);
-          float4 o; o.x = rr.x + v.x; o.y = rr.y + v.y; o.z = rr.z + v.z; o.w = rr.w + v.w;
-          *reinterpret_cast<float4*>(static_cast<float*>(p.C) + ci) = o;
-        } else if constexpr (EPI == EPI_GELU) {
-          store4<TO>(static_cast<TO*>(p.C) + ci, v);
-          float4 a; a.x = gelu_erf(v.x); a.y = gelu_erf(v.y); a.z = gelu_erf(v.z); a.w = gelu_erf(v.w);
-          store4<TO>(static_cast<TO*>(p.C2) + (int64_t)row * p.ldc2 + col, a);
-        } else if constexpr (EPI == EPI_SGD) {
-          float4* wp = reinterpret_cast<float4*>(static_cast<float*>(p.C) + ci);
-          float4 w = *wp;
-          w.x -= p.alpha * v.x; w.y -= p.alpha * v.y; w.z -= p.alpha * v.z; w.w -= p.alpha * v.w;
-          *wp = w;
-          if (p.C2) store4<TO>(static_cast<TO*>(p.C2) + (int64_t)row * p.ldc2 + col, w);
-          if (p.C3) {
-            const float4 w0 = load4<TO>(static_cast<const TO*>(p.W0) + ci);
-            float4 cur; cur.x = w0.x + w.x; cur.y = w0.y + w.y; cur.z = w0.z + w.z; cur.w = w0.w + w.w;
-            store4<TO>(static_cast<TO*>(p.C3) + ci, cur);
-          }
-        } else if constexpr (EPI == EPI_CEGRAD) {
-          float4 gq = {0.f, 0.f, 0.f, 0.f};
-          if (row < p.n_tgt) {
-            const float l = p.lse[row];
-            const int t = p.tgt[row];
-            gq.x = __expf(v.x - l) - (col == t ? 1.f : 0.f);
-            gq.y = __expf(v.y - l) - (col + 1 == t ? 1.f : 0.f);
-            gq.z = __expf(v.z - l) - (col + 2 == t ? 1.f : 0.f);
-            gq.w = __expf(v.w - l) - (col + 3 == t ? 1.f : 0.f);
-            gq.x *= p.alpha; gq.y *= p.alpha; gq.z *= p.alpha; gq.w *= p.alpha;
-          }
-          store4<TO>(static_cast<TO*>(p.C) + ci, gq);
-        }
-      }
-    }
+    epi_apply<EPI, TO>(p, st, ES, BM, BN, m0, n0, tid, NT);
   }
 }
 
@@ -383,8 +394,226 @@ __global__ void gemm_reduce_k(GemmParams p, int nz) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Large-tile core for bf16 operands that are both k-contiguous (the forward
+// products and everything else of the form C = A B^T with A [M][K], B [N][K]).
+//
+// Workgroup tile 256x256, eight waves in 2x4 (two per SIMD, so one wave's
+// barrier and load issue hide behind the other's products), each wave
+// 128x64 = 4x2 blocks of 32x32 accumulators (v_mfma_f32_32x32x16_bf16).
+// K advances 32 per stage through a ring of four 32 KB stages filled by
+// direct global->LDS 16-byte loads (buffer_load ... lds: no staging
+// registers; out-of-range rows and columns read as zero), issued three
+// stages ahead so that their latency hides behind three stages of products.
+// Every stage slot issues the same number of loads (past the end of K they
+// read zeros into a slot nobody uses), so the wait for a stage is a fixed
+// vmcnt.  LDS rows are 64 bytes; 16-byte chunk c of row r sits at slot
+// c ^ ((r >> 2) & 3): a fragment read (one chunk of 32 consecutive rows)
+// then runs at the full 128-bit LDS read rate (measured on gfx950 against
+// linear addressing; the unswizzled layout runs at a third of it).
+namespace big {
+constexpr int BM = 256, BN = 256, BK = 32, NS = 4;
+constexpr int WM = 2, WN = 4, NW = WM * WN, NT = 64 * NW;   // 8 waves, 2 per SIMD
+constexpr int TM = BM / WM, TN = BN / WN;    // wave tile 128 x 64
+constexpr int FI = TM / 32, FJ = TN / 32;    // 32x32 accumulator blocks per wave (4 x 2)
+constexpr int ROWB = BK * 2;                 // bytes per LDS row
+constexpr int STAGE_A = BM * ROWB;           // 16 KB
+constexpr int STAGE = (BM + BN) * ROWB;      // 32 KB
+constexpr int LDS_BYTES = NS * STAGE;        // 128 KB of the 160 KB per CU
+constexpr int SLAB_LOADS = BM * ROWB / 1024 / NW;   // 1 KB loads per wave per operand slab (2)
+constexpr int LOADS = 2 * SLAB_LOADS;        // per wave per stage
+constexpr int ES = BN + 8;                   // epilogue fp32 row pitch: the two lane
+                                             // halves (4 rows apart) on disjoint banks
+constexpr int EROWS = 64;                    // rows per epilogue pass
+static_assert(EROWS * ES * 4 <= LDS_BYTES, "epilogue pass fits");
+static_assert((NS - 2) * LOADS == 8, "vmcnt in the main loop");
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Issue the loads of one 256-row operand slab (rows row0.., k k0..k0+31)
+// into LDS at dst: 16 wave instructions of 1 KB (16 rows), SLAB_LOADS per wave.
+DEVI void load_slab(__amdgpu_buffer_rsrc_t rs, uint32_t ldb, int row0, int rows, int k0, int K,
+                    char* dst, int wave, int lane) {
+  const int rl = lane >> 2, p = lane & 3;
+#pragma unroll
+  for (int i = 0; i < SLAB_LOADS; ++i) {
+    const int blk = wave * SLAB_LOADS + i;              // 16-row block of the slab
+    const int r = blk * 16 + rl;                        // row within the slab
+    const int c = p ^ ((r >> 2) & 3);                   // logical chunk at slot p
+    const int k = k0 + 8 * c;
+    const bool ok = row0 + r < rows && k < K;
+    const uint32_t off = ok ? (uint32_t)(row0 + r) * ldb + (uint32_t)k * 2u : OOB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + blk * 1024), 16, off, 0, 0, 0);
+  }
+}
+}  // namespace big
+
+template <int EPI, typename TO, bool DUAL>
+__global__ __launch_bounds__(big::NT, 1) void gemm256_kernel(GemmParams p) {
+  constexpr int BM = big::BM, BN = big::BN, BK = big::BK, NT = big::NT, NS = big::NS, ROWB = big::ROWB;
+  constexpr int STAGE_A = big::STAGE_A, STAGE = big::STAGE, ES = big::ES, EROWS = big::EROWS;
+  constexpr int TM = big::TM, TN = big::TN, FI = big::FI, FJ = big::FJ, WN = big::WN;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  // Workgroups are dealt to the 8 XCDs round-robin; give each XCD a
+  // contiguous run of tiles, walked in groups of GM tile rows (column-major
+  // inside a group), so the ~32 workgroups an XCD runs at once cover a
+  // 4 x 8 patch of tiles and share 4 A slabs and 8 B slabs in its L2.
+  constexpr int GM = 4;
+  const int tm = (p.M + BM - 1) / BM, tn = (p.N + BN - 1) / BN, ntile = tm * tn;
+  const int b = blockIdx.x, x = b & 7, y = b >> 3;
+  const int q8 = ntile >> 3, r8 = ntile & 7;
+  const int t = x * q8 + min(x, r8) + y;
+  const int grp = t / (GM * tn), first = grp * GM, gm = min(tm - first, GM);
+  const int tl = t - grp * GM * tn;
+  const int m0 = (first + tl % gm) * BM, n0 = (tl / gm) * BN;
+
+  f32x16 acc[FI][FJ];
+#pragma unroll
+  for (int i = 0; i < FI; ++i)
+#pragma unroll
+    for (int j = 0; j < FJ; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  const int nk1 = (p.K + BK - 1) / BK;
+  const int ntot = DUAL ? 2 * nk1 : nk1;
+  const int per = (ntot + (int)gridDim.z - 1) / (int)gridDim.z;
+  const int kt_begin = min(ntot, (int)blockIdx.z * per);
+  const int kt_end = min(ntot, kt_begin + per);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A, (int64_t)p.M * p.lda * 2);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B, (int64_t)p.N * p.ldb * 2);
+  const __amdgpu_buffer_rsrc_t rb2 = make_rsrc(DUAL ? p.B2 : p.B, (int64_t)p.N * p.ldb * 2);
+  const uint32_t lda = (uint32_t)p.lda * 2u, ldb = (uint32_t)p.ldb * 2u;
+  // k-tile kt into ring slot kt % NS; past kt_end the loads read zeros
+  auto issue = [&](int kt) {
+    const bool live = kt < kt_end;
+    const bool second = DUAL && kt >= nk1;
+    const int k0 = live ? (second ? kt - nk1 : kt) * BK : p.K;
+    char* st = smem + ((kt - kt_begin) % NS) * STAGE;
+    big::load_slab(ra, lda, m0, p.M, k0, p.K, st, wave, lane);
+    big::load_slab(second ? rb2 : rb, ldb, n0, p.N, k0, p.K, st + STAGE_A, wave, lane);
+  };
+  // fragment addressing: lane reads row (l & 31) of a 32-row block, logical
+  // chunk 2*ks + (l >> 5), at slot chunk ^ ((row >> 2) & 3) = chunk ^ ((l >> 2) & 3)
+  const int frow = lane & 31, fsw = (lane >> 2) & 3, fhi = lane >> 5;
+  if (kt_begin < kt_end) {
+#pragma unroll
+    for (int u = 0; u < NS - 1; ++u) issue(kt_begin + u);
+  }
+  for (int kt = kt_begin; kt < kt_end; ++kt) {
+    // this wave's loads of stage kt have landed once at most the (NS - 2)
+    // younger stages' loads are outstanding; the barrier then covers every
+    // wave's loads and frees slot (kt - 1) % NS for stage kt + NS - 1
+    __builtin_amdgcn_s_waitcnt(0x0F78);    // vmcnt(8)
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    issue(kt + NS - 1);
+    const char* As = smem + ((kt - kt_begin) % NS) * STAGE + (wm * TM + frow) * ROWB;
+    const char* Bs = smem + ((kt - kt_begin) % NS) * STAGE + STAGE_A + (wn * TN + frow) * ROWB;
+    // fragments double-buffered over the k-steps of the stage: the reads of
+    // step ks + 1 are issued before the products of step ks (scheduling
+    // fences keep the compiler from sinking them)
+    bf16x8 fa[2][FI], fb[2][FJ];
+    auto frags = [&](int ks, bf16x8 (&a)[FI], bf16x8 (&b)[FJ]) {
+      const int slot = ((2 * ks + fhi) ^ fsw) * 16;
+#pragma unroll
+      for (int i = 0; i < FI; ++i) a[i] = *reinterpret_cast<const bf16x8*>(As + i * 32 * ROWB + slot);
+#pragma unroll
+      for (int j = 0; j < FJ; ++j) b[j] = *reinterpret_cast<const bf16x8*>(Bs + j * 32 * ROWB + slot);
+    };
+    frags(0, fa[0], fb[0]);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const int c = ks & 1;
+      if (ks + 1 < BK / 16) frags(ks + 1, fa[c ^ 1], fb[c ^ 1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < FI; ++i)
+#pragma unroll
+        for (int j = 0; j < FJ; ++j) mma32x32x16(fa[c][i], fb[c][j], acc[i][j]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0): the zero-fill loads past the end
+  __syncthreads();                         // all waves done with the operand stages
+
+  // Epilogue in four passes of 64 tile rows: the waves holding those rows
+  // stage them in LDS, then all threads apply the epilogue.
+  float* st = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int pass = 0; pass < BM / EROWS; ++pass) {
+    if (wm == pass / (TM / EROWS)) {
+#pragma unroll
+      for (int ii = 0; ii < EROWS / 32; ++ii) {
+        const int i = (pass % (TM / EROWS)) * (EROWS / 32) + ii;
+#pragma unroll
+        for (int j = 0; j < FJ; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            st[(ii * 32 + 8 * (r >> 2) + 4 * fhi + (r & 3)) * ES + wn * TN + j * 32 + frow] = acc[i][j][r];
+      }
+    }
+    __syncthreads();
+    epi_apply<EPI, TO>(p, st, ES, EROWS, BN, m0 + pass * EROWS, n0, tid, NT);
+    __syncthreads();
+  }
+}
+
+// The 256x256 core takes bf16 A [M][K] and B [N][K] with 16-byte aligned
+// rows; split K when there are too few tiles for the 256 CUs.
+template <int EPI, typename TO>
+bool launch_big(const GemmParams& p, hipStream_t s) {
+  if (p.K % 8 || p.lda % 8 || p.ldb % 8) return false;
+  if ((int64_t)p.M * p.lda * 2 > 0x7fffffff || (int64_t)p.N * p.ldb * 2 > 0x7fffffff) return false;
+  const int tiles = ((p.N + big::BN - 1) / big::BN) * ((p.M + big::BM - 1) / big::BM);
+  int nz = 1;
+  if constexpr (EPI == EPI_STORE || EPI == EPI_RESID) {
+    const int ktiles = ((p.K + big::BK - 1) / big::BK) * (p.B2 ? 2 : 1);
+    if (p.split_ws && tiles < 192 && ktiles >= 8) {
+      nz = (256 + tiles - 1) / tiles;
+      if (nz > ktiles / 4) nz = ktiles / 4;
+      if (nz > 4) nz = 4;
+      if ((int64_t)nz * p.M * p.N > p.split_cap || p.N % 4) nz = 1;
+    }
+  }
+  static bool attr_done[2][8][2] = {};
+  auto go = [&](auto kern, bool dual) {
+    bool& done = attr_done[dual][EPI][sizeof(TO) == 4];
+    if (!done) {
+      (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, big::LDS_BYTES);
+      done = true;
+    }
+    hipLaunchKernelGGL(kern, dim3(tiles, 1, nz), dim3(big::NT), big::LDS_BYTES, s, p);
+  };
+  if (p.B2) go(gemm256_kernel<EPI, TO, true>, true);
+  else go(gemm256_kernel<EPI, TO, false>, false);
+  if constexpr (EPI == EPI_STORE || EPI == EPI_RESID) {
+    if (nz > 1) {
+      const int64_t groups = (int64_t)p.M * (p.N / 4);
+      hipLaunchKernelGGL((gemm_reduce_k<EPI, TO>), dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, s, p, nz);
+    }
+  }
+  return true;
+}
+
+// Which core runs the bf16 k-contiguous products: measured on MI355X, the
+// 256x256 core wins on long reductions (K, doubled for W0 + delta, >= 6144)
+// and on grids of >= 1024 of its tiles; below that its 256 CUs are filled
+// unevenly and the 128x128 core is as fast or faster.
+int g_gemm_core = GEMM_CORE_AUTO;
+
 template <typename T, bool AK, bool BK_, int EPI, typename TO>
 void launch_t(const GemmParams& p, hipStream_t s) {
+  if constexpr (std::is_same<T, bf16>::value && AK && BK_ &&
+                (EPI == EPI_STORE || EPI == EPI_RESID || EPI == EPI_GELU || EPI == EPI_SWIGLU)) {
+    const int64_t keff = (int64_t)p.K * (p.B2 ? 2 : 1);
+    const int64_t tiles = (int64_t)((p.M + 255) / 256) * ((p.N + 255) / 256);
+    const bool want = g_gemm_core == GEMM_CORE_BIG ||
+                      (g_gemm_core == GEMM_CORE_AUTO && (keff >= 6144 || tiles >= 1024));
+    if (want && launch_big<EPI, TO>(p, s)) return;
+  }
   const int tiles = ((p.N + BN - 1) / BN) * ((p.M + BM - 1) / BM);
   int nz = 1;
   if constexpr (EPI == EPI_STORE || EPI == EPI_RESID) {
@@ -441,6 +670,12 @@ int dispatch(const GemmParams& p, bool a_kc, bool b_kc, int epi, bool out_f32, h
 }
 
 }  // namespace
+
+int gemm_core(int mode) {
+  const int prev = g_gemm_core;
+  if (mode == GEMM_CORE_AUTO || mode == GEMM_CORE_BIG || mode == GEMM_CORE_SMALL) g_gemm_core = mode;
+  return prev;
+}
 
 int gemm(const GemmParams& p, bool bf16_operands, bool a_kc, bool b_kc, int epi, bool out_f32,
          hipStream_t s) {

@@ -27,6 +27,10 @@ struct GemmParams {
 };
 
 // Returns 0, or -1 for an epilogue/layout combination that is not built.
+// core selection for the bf16 k-contiguous products (diagnostics): returns
+// the previous mode
+enum { GEMM_CORE_AUTO = 0, GEMM_CORE_BIG = 1, GEMM_CORE_SMALL = 2 };
+int gemm_core(int mode);
 int gemm(const GemmParams& p, bool bf16_operands, bool a_kc, bool b_kc, int epi, bool out_f32,
          hipStream_t s);
 

@@ -905,6 +905,8 @@ int ttt_diag_gemm(int32_t dtype, int32_t a_kc, int32_t b_kc, int32_t M, int32_t 
   const int vec = dtype == TTT_BF16 ? 8 : 4;
   if (lda % vec || ldb % vec || (!a_kc && M % vec) || (!b_kc && N % vec) || ((a_kc || b_kc) && K % vec))
     return fail(TTT_ERR_ARG, "strides / vector dims must be multiples of 16 bytes");
+  if (N % 4 || ldc % 4 || ldc < N)
+    return fail(TTT_ERR_ARG, "N and ldc must be multiples of 4 with ldc >= N (4-wide output groups)");
   GemmParams p;
   p.A = A; p.lda = lda; p.B = B; p.ldb = ldb; p.M = M; p.N = N; p.K = K; p.C = C; p.ldc = ldc;
   int epi = EPI_STORE;
@@ -914,5 +916,7 @@ int ttt_diag_gemm(int32_t dtype, int32_t a_kc, int32_t b_kc, int32_t M, int32_t 
     return fail(TTT_ERR_ARG, "GEMM variant not built");
   return TTT_OK;
 }
+
+int ttt_diag_gemm_core(int32_t mode) { return gemm_core(mode); }
 
 }  // extern "C"

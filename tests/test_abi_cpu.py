@@ -67,5 +67,13 @@ def test_argument_errors_without_device_work():
     h = ctypes.c_void_p(0)
     assert T.lib.ttt_model_load(ctypes.byref(c), None, 0, None, 0, None, ctypes.byref(h)) == -1
     assert T.lib.ttt_diag_gemm(1, 1, 1, 4, 4, 4, None, 8, None, 8, None, 8, None) == -1
+    # output width / stride not a multiple of 4: rejected before any launch
+    # (the pointers are never touched on this path)
+    dummy = ctypes.c_void_p(4096)
+    assert T.lib.ttt_diag_gemm(1, 1, 1, 4, 6, 8, dummy, 8, dummy, 8, dummy, 6, None) == -1
+    assert T.lib.ttt_diag_gemm(1, 1, 1, 4, 8, 8, dummy, 8, dummy, 8, dummy, 6, None) == -1
+    # the core selector only takes 0, 1, 2 and reports the mode in force
+    mode = T.lib.ttt_diag_gemm_core(7)
+    assert mode in (0, 1, 2) and T.lib.ttt_diag_gemm_core(7) == mode
     assert T.lib.ttt_status_str(-4) == b"token id out of range"
     T.lib.ttt_model_free(None)

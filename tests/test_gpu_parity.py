@@ -122,6 +122,50 @@ def test_gemm_kernel_matches_torch(dt, layout, shape):
     assert err < 1e-5, err
 
 
+@pytest.fixture
+def gemm_core():
+    """Select a GEMM core for one test, restore the shape-based choice after."""
+    T = _gpu()
+    yield T.diag_gemm_core
+    T.diag_gemm_core(T.GEMM_CORE_AUTO)
+
+
+@pytest.mark.parametrize("core", ["auto", "big"])
+@pytest.mark.parametrize("shape", [(300, 544, 6160), (257, 3104, 7000), (64, 96, 32), (513, 264, 8)])
+def test_gemm_large_tile_core_matches_torch(gemm_core, core, shape):
+    """The 256x256 bf16 core (direct-to-LDS four-stage ring, swizzled rows):
+    ragged M and N tails, a K that ends inside a 32-wide stage, K shorter
+    than one stage; reached by its own shape rule (long K) or forced."""
+    T = _gpu()
+    M, N, K = shape
+    gemm_core(T.GEMM_CORE_BIG if core == "big" else T.GEMM_CORE_AUTO)
+    say(f"case gemm large-tile core={core} M={M} N={N} K={K}")
+    g = torch.Generator().manual_seed(M * 5 + N * 11 + K)
+    A = torch.randn(M, K, generator=g).to(torch.bfloat16)
+    B = torch.randn(N, K, generator=g).to(torch.bfloat16)
+    ref = A.double() @ B.double().T
+    C = T.diag_gemm(A.cuda(), B.cuda(), M, N, K, True, True)
+    torch.cuda.synchronize()
+    err = (C.double().cpu() - ref).abs().max().item() / max(ref.abs().max().item(), 1e-30)
+    assert err < 1e-5, err
+
+
+@pytest.mark.parametrize("mlp,hd,q", [("swiglu", 128, 2), ("gelu", 64, 3)])
+def test_prefill_small_models_large_tile_core(gemm_core, mlp, hd, q):
+    """The bf16 small models with every k-contiguous product on the 256x256
+    core (its STORE, RESID, GELU and SWIGLU epilogues, W0 + delta, K split
+    over workgroups) against the oracle, to the same bar."""
+    T = _gpu()
+    gemm_core(T.GEMM_CORE_BIG)
+    H = 2 if hd <= 64 else 1
+    cfg = small_cfg(mlp=mlp, head_dim=hd, n_heads=H, d_model=H * hd, n_fast=q,
+                    n_layers=max(3, q + 1))
+    r = run_pair(cfg, dtype="bf16", std=0.05, prefill_block=64)
+    assert r["loss"] < BAR["bf16"] and r["W"] < BAR["bf16"]
+    assert r["loss0"] < BAR["bf16"]
+    assert r["dW"] < 0.1 and r["dloss"] < 0.2
+
+
 # ------------------------------------------------------- whole inner loop
 
 def test_prefill_tiny_fp32_workload():
