@@ -148,6 +148,30 @@ __global__ void rope_qkv_k(const T* __restrict__ qkv, int n, int H, int hd, int6
   vr[slot * d + j2] = row[2 * d + j2];
 }
 
+// dst[c][r] = src[r][c] for r < rows, c < cols; rows rows..rows_pad-1 of
+// dst's columns are written as zero (so that a reduction over r can run in
+// whole 16-byte vectors).  64x64 tiles through LDS: coalesced reads along c,
+// coalesced writes along r.
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_k(const T* __restrict__ src, int rows, int cols,
+                                                   int64_t lds_, T* __restrict__ dst, int64_t ldd,
+                                                   int rows_pad) {
+  __shared__ T tile[64][65];
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = r0 + ty * 16 + i, c = c0 + tx;
+    tile[ty * 16 + i][tx] = (r < rows && c < cols) ? src[(int64_t)r * lds_ + c] : from_f32<T>(0.f);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int c = c0 + ty * 16 + i, r = r0 + tx;
+    if (c < cols && r < rows_pad) dst[(int64_t)c * ldd + r] = tile[tx][ty * 16 + i];
+  }
+}
+
 // Transposed rotation of dQ and dK inside dqkv [n][3d].
 template <typename T>
 __global__ void rope_bwd_k(T* __restrict__ g, int n, int H, int hd, int64_t pos0,
@@ -360,6 +384,15 @@ void rope_qkv(const void* qkv, int n, int H, int hd, int64_t pos0, const double*
   if (total <= 0) return;
   TSEL(bf, hipLaunchKernelGGL(rope_qkv_k<bf16>, dim3(nblk(total, 256)), dim3(256), 0, s, (const bf16*)qkv, n, H, hd, pos0, theta, (bf16*)q_out, (bf16*)kring, (bf16*)vring, cap),
        hipLaunchKernelGGL(rope_qkv_k<float>, dim3(nblk(total, 256)), dim3(256), 0, s, (const float*)qkv, n, H, hd, pos0, theta, (float*)q_out, (float*)kring, (float*)vring, cap));
+}
+
+void transpose(const void* src, int rows, int cols, int64_t lds_, void* dst, int64_t ldd, int rows_pad,
+               bool bf, hipStream_t s) {
+  if (rows_pad < rows) rows_pad = rows;
+  if (rows_pad <= 0 || cols <= 0) return;
+  dim3 grid((cols + 63) / 64, (rows_pad + 63) / 64);
+  TSEL(bf, hipLaunchKernelGGL(transpose_k<bf16>, grid, dim3(256), 0, s, (const bf16*)src, rows, cols, lds_, (bf16*)dst, ldd, rows_pad),
+       hipLaunchKernelGGL(transpose_k<float>, grid, dim3(256), 0, s, (const float*)src, rows, cols, lds_, (float*)dst, ldd, rows_pad));
 }
 
 void rope_bwd(void* dqkv, int n, int H, int hd, int64_t pos0, const double* theta, bool bf,

@@ -157,7 +157,7 @@ DEVI float silu(float z) { return z / (1.f + __expf(-z)); }
 // vector accesses).  With a K split (gridDim.z > 1) the raw partial goes to
 // slab z of split_ws instead.
 template <int EPI, typename TO>
-DEVI void epi_apply(const GemmParams& p, const float* st, int ES, int nr, int nc, int row0, int n0,
+DEVI void epi_apply(const GemmParams& p, float* st, int ES, int nr, int nc, int row0, int n0,
                     int tid, int nthr) {
   if (gridDim.z > 1) {
     float* slab = p.split_ws + (int64_t)blockIdx.z * p.M * p.N;
@@ -170,7 +170,46 @@ DEVI void epi_apply(const GemmParams& p, const float* st, int ES, int nr, int nc
     }
     return;
   }
-  if constexpr (EPI == EPI_SWIGLU) {
+  if constexpr (EPI == EPI_SGD) {
+    // delta -= lr * acc (fp32 master C, row-major), its storage-type copy C2;
+    // the current weight W0 + delta goes back into the staged tile and then
+    // out transposed to C3[col][row] in runs of 4 rows (the input-gradient
+    // products read it as a k-contiguous operand)
+    for (int g = tid; g < nr * (nc / 4); g += nthr) {
+      const int r = g / (nc / 4), c = (g % (nc / 4)) * 4;
+      const int row = row0 + r, col = n0 + c;
+      if (row >= p.M || col >= p.N) continue;
+      float* sp = st + r * ES + c;
+      const float4 v = *reinterpret_cast<const float4*>(sp);
+      const int64_t ci = (int64_t)row * p.ldc + col;
+      float4* wp = reinterpret_cast<float4*>(static_cast<float*>(p.C) + ci);
+      float4 w = *wp;
+      w.x -= p.alpha * v.x; w.y -= p.alpha * v.y; w.z -= p.alpha * v.z; w.w -= p.alpha * v.w;
+      *wp = w;
+      if (p.C2) store4<TO>(static_cast<TO*>(p.C2) + (int64_t)row * p.ldc2 + col, w);
+      if (p.C3) {
+        const float4 w0 = load4<TO>(static_cast<const TO*>(p.W0) + ci);
+        float4 cur; cur.x = w0.x + w.x; cur.y = w0.y + w.y; cur.z = w0.z + w.z; cur.w = w0.w + w.w;
+        *reinterpret_cast<float4*>(sp) = cur;
+      }
+    }
+    if (p.C3) {
+      __syncthreads();
+      for (int g = tid; g < nc * (nr / 4); g += nthr) {
+        const int c = g / (nr / 4), r = (g % (nr / 4)) * 4;
+        const int row = row0 + r, col = n0 + c;
+        if (row >= p.M || col >= p.N) continue;
+        TO* dst = static_cast<TO*>(p.C3) + (int64_t)col * p.ldc3 + row;
+        if (row + 3 < p.M) {
+          float4 v;
+          v.x = st[r * ES + c]; v.y = st[(r + 1) * ES + c]; v.z = st[(r + 2) * ES + c]; v.w = st[(r + 3) * ES + c];
+          store4<TO>(dst, v);
+        } else {
+          for (int e = 0; row + e < p.M; ++e) dst[e] = from_f32<TO>(st[(r + e) * ES + c]);
+        }
+      }
+    }
+  } else if constexpr (EPI == EPI_SWIGLU) {
     // columns: gate block 32c..32c+15, up block 32c+16..32c+31 -> act 16c..16c+15
     for (int g = tid; g < nr * (nc / 8); g += nthr) {
       const int r = g / (nc / 8), q = g % (nc / 8);      // q: 4-wide group of act columns
@@ -203,17 +242,6 @@ DEVI void epi_apply(const GemmParams& p, const float* st, int ES, int nr, int nc
         store4<TO>(static_cast<TO*>(p.C) + ci, v);
         float4 a; a.x = gelu_erf(v.x); a.y = gelu_erf(v.y); a.z = gelu_erf(v.z); a.w = gelu_erf(v.w);
         store4<TO>(static_cast<TO*>(p.C2) + (int64_t)row * p.ldc2 + col, a);
-      } else if constexpr (EPI == EPI_SGD) {
-        float4* wp = reinterpret_cast<float4*>(static_cast<float*>(p.C) + ci);
-        float4 w = *wp;
-        w.x -= p.alpha * v.x; w.y -= p.alpha * v.y; w.z -= p.alpha * v.z; w.w -= p.alpha * v.w;
-        *wp = w;
-        if (p.C2) store4<TO>(static_cast<TO*>(p.C2) + (int64_t)row * p.ldc2 + col, w);
-        if (p.C3) {
-          const float4 w0 = load4<TO>(static_cast<const TO*>(p.W0) + ci);
-          float4 cur; cur.x = w0.x + w.x; cur.y = w0.y + w.y; cur.z = w0.z + w.z; cur.w = w0.w + w.w;
-          store4<TO>(static_cast<TO*>(p.C3) + ci, cur);
-        }
       } else if constexpr (EPI == EPI_CEGRAD) {
         float4 gq = {0.f, 0.f, 0.f, 0.f};
         if (row < p.n_tgt) {
@@ -607,7 +635,8 @@ int g_gemm_core = GEMM_CORE_AUTO;
 template <typename T, bool AK, bool BK_, int EPI, typename TO>
 void launch_t(const GemmParams& p, hipStream_t s) {
   if constexpr (std::is_same<T, bf16>::value && AK && BK_ &&
-                (EPI == EPI_STORE || EPI == EPI_RESID || EPI == EPI_GELU || EPI == EPI_SWIGLU)) {
+                (EPI == EPI_STORE || EPI == EPI_RESID || EPI == EPI_GELU || EPI == EPI_SWIGLU ||
+                 EPI == EPI_SGD)) {
     const int64_t keff = (int64_t)p.K * (p.B2 ? 2 : 1);
     const int64_t tiles = (int64_t)((p.M + 255) / 256) * ((p.N + 255) / 256);
     const bool want = g_gemm_core == GEMM_CORE_BIG ||
@@ -652,6 +681,7 @@ int dispatch(const GemmParams& p, bool a_kc, bool b_kc, int epi, bool out_f32, h
       case EPI_SWIGLU: launch_t<T, true, true, EPI_SWIGLU, T>(p, s); return 0;
       case EPI_CESTAT: launch_t<T, true, true, EPI_CESTAT, float>(p, s); return 0;
       case EPI_CEGRAD: launch_t<T, true, true, EPI_CEGRAD, T>(p, s); return 0;
+      case EPI_SGD: if (p.B2) return -1; launch_t<T, true, true, EPI_SGD, T>(p, s); return 0;
       default: return -1;
     }
   }

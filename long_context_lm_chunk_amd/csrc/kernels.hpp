@@ -15,7 +15,8 @@ struct GemmParams {
   void* C = nullptr; int64_t ldc = 0;        // primary output
   const float* R = nullptr; int64_t ldr = 0; // residual input (RESID)
   void* C2 = nullptr; int64_t ldc2 = 0;      // act (GELU/SWIGLU), delta copy (SGD)
-  void* C3 = nullptr; const void* W0 = nullptr;  // SGD: C3 = round(W0 + delta), same layout as C
+  void* C3 = nullptr; const void* W0 = nullptr;  // SGD: C3 = round(W0 + delta), written
+  int64_t ldc3 = 0;                              // transposed: C3[col][row], row stride ldc3
   float alpha = 0.f;                         // SGD: lr; CEGRAD: 1/n_targets
   // cross-entropy epilogues
   const int* tgt = nullptr; int n_tgt = 0;
@@ -35,6 +36,9 @@ int gemm(const GemmParams& p, bool bf16_operands, bool a_kc, bool b_kc, int epi,
          hipStream_t s);
 
 // ---- elementwise (elementwise.hip); T is bf16 when bf16 != 0, else float
+// dst[c][r] = src[r][c] (r < rows, c < cols); rows..rows_pad-1 written as 0
+void transpose(const void* src, int rows, int cols, int64_t ld_src, void* dst, int64_t ld_dst,
+               int rows_pad, bool bf16, hipStream_t s);
 void embed(const int32_t* tok, int n, const void* E, int d, int V, bool bf16, float* out, int* err,
            hipStream_t s);
 void layernorm_fwd(const float* x, int64_t ldx, int n, int d, float eps, void* y, int64_t ldy,

@@ -80,14 +80,15 @@ struct Carver {
 //
 // The input-gradient products of the backward pass only need the current
 // weights to working precision, so they read one rounded copy
-// round(W0 + delta) (c_up / c_dn), refreshed by the SGD epilogue.
+// round(W0 + delta), kept transposed (ct_up / ct_dn: the products then take
+// both operands k-contiguous) and rewritten by the SGD epilogue.
 struct FastLayer {
   float* m_up = nullptr;  // fp32 delta master [F2][d]
   float* m_dn = nullptr;  // fp32 delta master [d][F]
   void* s_up = nullptr;   // delta in the storage type (== master in fp32 mode)
   void* s_dn = nullptr;
-  void* c_up = nullptr;   // round(W0 + delta) in the storage type
-  void* c_dn = nullptr;
+  void* ct_up = nullptr;  // round(W0 + delta) in the storage type, transposed: [d][F2]
+  void* ct_dn = nullptr;  // [F][d] (k-contiguous operands of the input-gradient products)
 };
 
 struct Layer {
@@ -98,6 +99,8 @@ struct Layer {
   void* kring = nullptr; void* vring = nullptr;  // [cap][d]
   void* vtring = nullptr;                          // [d][cap]: V transposed, read by the forward
   void* ktring = nullptr;                          // [d][cap]: K transposed (fast blocks: dQ)
+  void* wqkvT = nullptr;  // [d][3d] and [d][d]: transposed copies for the input-gradient
+  void* woT = nullptr;    // products (fast blocks above the first)
   int64_t cap = 0;
 };
 
@@ -117,6 +120,7 @@ struct ttt_model {
   int d = 0, F = 0, F2 = 0, V = 0, L = 0, q = 0, f0 = 0, H = 0, hd = 0, W = 0, Cmax = 0, MA = 0;
   int nparts = 0;
   void* E = nullptr; void* U = nullptr;
+  void* UT = nullptr;                   // head transposed [d][V] (input gradient of the head)
   std::vector<Layer> layers;
   std::vector<FastLayer> fast;
   double* theta = nullptr;
@@ -136,6 +140,8 @@ struct ttt_model {
   float* pmax = nullptr; float* psum = nullptr; float* tlog = nullptr; float* lse_ce = nullptr;
   void* G = nullptr;
   float* dh = nullptr; void* dh_lo = nullptr; float* dact = nullptr; void* dz = nullptr;
+  void* dhT = nullptr; void* actT = nullptr; void* dzT = nullptr; void* bT = nullptr;
+  int64_t Cp = 0;                       // their row stride
   float* dtmp = nullptr; void* dout = nullptr; void* dqkv = nullptr; float* Dattn = nullptr;
   float* attn_part = nullptr; float* attn_ml = nullptr;   // key-range split partials
   float* split_ws = nullptr; int64_t split_cap = 0;         // split-K partials of the GEMMs
@@ -206,7 +212,12 @@ size_t layout(ttt_model* m, void* base) {
     ly.vring = cv.take<void>((size_t)ly.cap * d * es);
     ly.vtring = cv.take<void>((size_t)ly.cap * d * es);
     ly.ktring = (l > m->f0) ? cv.take<void>((size_t)ly.cap * d * es) : nullptr;
+    if (l > m->f0) {
+      ly.wqkvT = cv.take<void>((size_t)3 * d * d * es);
+      ly.woT = cv.take<void>((size_t)d * d * es);
+    }
   }
+  m->UT = cv.take<void>((size_t)V * d * es);
   m->fast.assign(m->q, FastLayer());
   for (int j = 0; j < m->q; ++j) {
     FastLayer& f = m->fast[j];
@@ -219,8 +230,8 @@ size_t layout(ttt_model* m, void* base) {
       f.s_up = f.m_up;
       f.s_dn = f.m_dn;
     }
-    f.c_up = cv.take<void>((size_t)F2 * d * es);
-    f.c_dn = cv.take<void>((size_t)d * F * es);
+    f.ct_up = cv.take<void>((size_t)F2 * d * es);
+    f.ct_dn = cv.take<void>((size_t)d * F * es);
   }
   m->theta = cv.take<double>((size_t)(m->hd / 2) * 8);
   // phase A
@@ -266,6 +277,13 @@ size_t layout(ttt_model* m, void* base) {
   m->G = cv.take<void>((size_t)C * V * es);
   m->dh = cv.take<float>((size_t)C * d * 4);
   m->dh_lo = cv.take<void>((size_t)C * d * es);
+  // transposed operands of the weight-gradient products: [features][Cp],
+  // Cp = the chunk capacity rounded up to a multiple of 8 (zero padded)
+  m->Cp = round_up((int64_t)C, 8);
+  m->dhT = cv.take<void>((size_t)m->Cp * d * es);
+  m->actT = cv.take<void>((size_t)m->Cp * F * es);
+  m->dzT = cv.take<void>((size_t)m->Cp * F2 * es);
+  m->bT = cv.take<void>((size_t)m->Cp * d * es);
   m->dact = cv.take<float>((size_t)C * F * 4);
   m->dz = cv.take<void>((size_t)C * F2 * es);
   m->dtmp = cv.take<float>((size_t)C * d * 4);
@@ -484,11 +502,11 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
     gg.C = m->G; gg.ldc = V; gg.tgt = tgt; gg.n_tgt = n_tgt; gg.lse = m->lse_ce;
     gg.alpha = 1.f / (float)n_tgt;
     if (gemm(gg, bf, true, true, EPI_CEGRAD, false, s)) return fail(TTT_ERR_CONFIG, "internal: CE variant");
-    GemmParams gx;   // dHf = G . U^T  (U stored [V][d]: reduction over V, n-contiguous)
-    gx.A = m->G; gx.lda = V; gx.B = m->U; gx.ldb = d; gx.M = n; gx.N = d; gx.K = V;
+    GemmParams gx;   // dHf = G . U  (through U^T [d][V], k-contiguous over the vocabulary)
+    gx.A = m->G; gx.lda = V; gx.B = m->UT; gx.ldb = V; gx.M = n; gx.N = d; gx.K = V;
     gx.C = m->dtmp; gx.ldc = d;
     gx.split_ws = m->split_ws; gx.split_cap = m->split_cap;
-    if (gemm(gx, bf, true, false, EPI_STORE, true, s)) return fail(TTT_ERR_CONFIG, "internal: CE variant");
+    if (gemm(gx, bf, true, true, EPI_STORE, true, s)) return fail(TTT_ERR_CONFIG, "internal: CE variant");
   }
   fill_f32(m->dh, (int64_t)n * d, 0.f, s);
   layernorm_bwd_acc(m->dtmp, m->xL, m->meanf, m->rstdf, n, d, m->dh, m->dh_lo, bf, s);
@@ -500,35 +518,45 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
     PB& b = m->pb[j];
     FastLayer& fw = m->fast[j];
     const float* x2 = (j > 0) ? b.x2 : x2_0;
-    // dact = dh . Wdn  (reads the weights before their update)
+    // Every product below runs with both operands k-contiguous: the weights
+    // through their transposed copies, the activations of the weight
+    // gradients transposed to [features][tokens] (tokens padded to a multiple
+    // of 8 with zeros, which add nothing to the reduction).
+    const int np = (n + 7) & ~7;
+    // dact = dh . Wdn  (reads the weights before their update: Wdn^T [F][d])
     GemmParams ga;
-    ga.A = m->dh_lo; ga.lda = d; ga.B = fw.c_dn; ga.ldb = F; ga.M = n; ga.N = F; ga.K = d;
+    ga.A = m->dh_lo; ga.lda = d; ga.B = fw.ct_dn; ga.ldb = d; ga.M = n; ga.N = F; ga.K = d;
     ga.C = m->dact; ga.ldc = F;
-    rc = run_gemm(m, ga, true, false, EPI_STORE, true, s); if (rc) return rc;
+    rc = run_gemm(m, ga, true, true, EPI_STORE, true, s); if (rc) return rc;
     // Wdn -= lr * dh^T act   ([d][F], reduction over the chunk's tokens)
+    transpose(m->dh_lo, n, d, d, m->dhT, m->Cp, np, bf, s);
+    transpose(b.act, n, F, F, m->actT, m->Cp, np, bf, s);
     GemmParams gw;
-    gw.A = m->dh_lo; gw.lda = d; gw.B = b.act; gw.ldb = F; gw.M = d; gw.N = F; gw.K = n;
+    gw.A = m->dhT; gw.lda = m->Cp; gw.B = m->actT; gw.ldb = m->Cp; gw.M = d; gw.N = F; gw.K = np;
     gw.C = fw.m_dn; gw.ldc = F; gw.C2 = bf ? fw.s_dn : nullptr; gw.ldc2 = F; gw.alpha = lr;
-    gw.C3 = fw.c_dn; gw.W0 = ly.wdn;
-    rc = run_gemm(m, gw, false, false, EPI_SGD, true, s); if (rc) return rc;
+    gw.C3 = fw.ct_dn; gw.ldc3 = d; gw.W0 = ly.wdn;
+    rc = run_gemm(m, gw, true, true, EPI_SGD, true, s); if (rc) return rc;
     act_bwd(m->dact, b.z, n, F, m->c.mlp == TTT_MLP_SWIGLU, m->dz, bf, s);
     if (j > 0) {
-      GemmParams gb;   // db = dz . Wup (before its update)
-      gb.A = m->dz; gb.lda = F2; gb.B = fw.c_up; gb.ldb = d; gb.M = n; gb.N = d; gb.K = F2;
+      GemmParams gb;   // db = dz . Wup (before its update: Wup^T [d][F2])
+      gb.A = m->dz; gb.lda = F2; gb.B = fw.ct_up; gb.ldb = F2; gb.M = n; gb.N = d; gb.K = F2;
       gb.C = m->dtmp; gb.ldc = d;
-      rc = run_gemm(m, gb, true, false, EPI_STORE, true, s); if (rc) return rc;
+      rc = run_gemm(m, gb, true, true, EPI_STORE, true, s); if (rc) return rc;
     }
-    GemmParams gw2;   // Wup -= lr * dz^T b
-    gw2.A = m->dz; gw2.lda = F2; gw2.B = b.b; gw2.ldb = d; gw2.M = F2; gw2.N = d; gw2.K = n;
+    // Wup -= lr * dz^T b
+    transpose(m->dz, n, F2, F2, m->dzT, m->Cp, np, bf, s);
+    transpose(b.b, n, d, d, m->bT, m->Cp, np, bf, s);
+    GemmParams gw2;
+    gw2.A = m->dzT; gw2.lda = m->Cp; gw2.B = m->bT; gw2.ldb = m->Cp; gw2.M = F2; gw2.N = d; gw2.K = np;
     gw2.C = fw.m_up; gw2.ldc = d; gw2.C2 = bf ? fw.s_up : nullptr; gw2.ldc2 = d; gw2.alpha = lr;
-    gw2.C3 = fw.c_up; gw2.W0 = ly.wup;
-    rc = run_gemm(m, gw2, false, false, EPI_SGD, true, s); if (rc) return rc;
+    gw2.C3 = fw.ct_up; gw2.ldc3 = F2; gw2.W0 = ly.wup;
+    rc = run_gemm(m, gw2, true, true, EPI_SGD, true, s); if (rc) return rc;
     if (j == 0) break;   // no gradient below the first fast MLP
     layernorm_bwd_acc(m->dtmp, x2, b.mean2, b.rstd2, n, d, m->dh, m->dh_lo, bf, s);
-    GemmParams gdo;   // dO = dh . Wo
-    gdo.A = m->dh_lo; gdo.lda = d; gdo.B = ly.wo; gdo.ldb = d; gdo.M = n; gdo.N = d; gdo.K = d;
+    GemmParams gdo;   // dO = dh . Wo  (Wo^T [d][d])
+    gdo.A = m->dh_lo; gdo.lda = d; gdo.B = ly.woT; gdo.ldb = d; gdo.M = n; gdo.N = d; gdo.K = d;
     gdo.C = m->dout; gdo.ldc = d;
-    rc = run_gemm(m, gdo, true, false, EPI_STORE, false, s); if (rc) return rc;
+    rc = run_gemm(m, gdo, true, true, EPI_STORE, false, s); if (rc) return rc;
     attn_rowdot(b.o, m->dout, n, m->H, m->hd, m->Dattn, bf, s);
     AttnParams ap;
     ap.q = b.q; ap.ldq = d; ap.kring = ly.kring; ap.vring = ly.vring; ap.cap = ly.cap;
@@ -545,10 +573,10 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
       swa_bwd(ap, bf, s);
     }
     rope_bwd(m->dqkv, n, m->H, m->hd, p0, m->theta, bf, s);
-    GemmParams gq;   // da = dqkv . Wqkv
-    gq.A = m->dqkv; gq.lda = 3 * d; gq.B = ly.wqkv; gq.ldb = d; gq.M = n; gq.N = d; gq.K = 3 * d;
+    GemmParams gq;   // da = dqkv . Wqkv  (Wqkv^T [d][3d])
+    gq.A = m->dqkv; gq.lda = 3 * d; gq.B = ly.wqkvT; gq.ldb = 3 * d; gq.M = n; gq.N = d; gq.K = 3 * d;
     gq.C = m->dtmp; gq.ldc = d;
-    rc = run_gemm(m, gq, true, false, EPI_STORE, true, s); if (rc) return rc;
+    rc = run_gemm(m, gq, true, true, EPI_STORE, true, s); if (rc) return rc;
     layernorm_bwd_acc(m->dtmp, b.xin, b.mean1, b.rstd1, n, d, m->dh, m->dh_lo, bf, s);
   }
   return TTT_OK;
@@ -604,8 +632,8 @@ int reset_state(ttt_model* m, hipStream_t s) {
       fill_f32(static_cast<float*>(f.s_up), (int64_t)F2 * d * (int64_t)m->es / 4, 0.f, s);
       fill_f32(static_cast<float*>(f.s_dn), (int64_t)d * F * (int64_t)m->es / 4, 0.f, s);
     }
-    HIPCHK(hipMemcpyAsync(f.c_up, ly.wup, (size_t)F2 * d * m->es, hipMemcpyDeviceToDevice, s));
-    HIPCHK(hipMemcpyAsync(f.c_dn, ly.wdn, (size_t)d * F * m->es, hipMemcpyDeviceToDevice, s));
+    transpose(ly.wup, F2, d, d, f.ct_up, F2, F2, m->bf, s);   // W0^T: no update yet
+    transpose(ly.wdn, d, F, F, f.ct_dn, d, d, m->bf, s);
   }
   for (int l = 0; l < m->L; ++l) {
     Layer& ly = m->layers[l];
@@ -688,6 +716,13 @@ int ttt_model_load(const ttt_config* cfg, const void* const* weights, int32_t n_
       convert_weight(w[4], d, F, true, -1, ly.wup, bf, s);
       convert_weight(w[5], F, d, true, -1, ly.wdn, bf, s);
     }
+  }
+  // transposed copies read by the input-gradient products
+  transpose(m->U, V, d, d, m->UT, V, V, bf, s);
+  for (int l = m->f0 + 1; l < m->L; ++l) {
+    Layer& ly = m->layers[l];
+    transpose(ly.wqkv, 3 * d, d, d, ly.wqkvT, 3 * d, 3 * d, bf, s);
+    transpose(ly.wo, d, d, d, ly.woT, d, d, bf, s);
   }
   // RoPE frequencies theta_i = base^(-2i/hd), float64 on the host
   std::vector<double> th(m->hd / 2);
