@@ -19,6 +19,24 @@
 namespace ttt {
 namespace {
 
+// Workgroups are dealt to the 8 XCDs round-robin by linear id, and the
+// query tiles of one head are consecutive ids: left as is, every XCD would
+// hold one tile of every head and its L2 would fetch every head's keys.
+// Renumber so that each XCD holds a contiguous run of logical ids (whole
+// heads, all their query tiles), which then share K/V lines in that L2.
+DEVI void attn_block(int& bx, int& by, int& bz) {
+  const int gx = gridDim.x, gy = gridDim.y;
+  const int total = gx * gy * (int)gridDim.z;
+  const int b = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+  const int x = b & 7, y = b >> 3, q8 = total >> 3, r8 = total & 7;
+  const int L = x * q8 + min(x, r8) + y;
+  bx = L % gx;
+  const int r = L / gx;
+  by = r % gy;
+  bz = r / gy;
+}
+
+
 constexpr int TQ = 64;     // positions per tile
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
@@ -102,8 +120,9 @@ __global__ __launch_bounds__(256, 2) void swa_fwd32_k(AttnParams p) {
   __shared__ __attribute__((aligned(16))) T Vt[2][C::HDR * C::LSV];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5, ql = lane & 31;
-  const int h = blockIdx.y;
-  const int qs = blockIdx.x * QT;
+  int bx, h, bz;
+  attn_block(bx, h, bz);
+  const int qs = bx * QT;
   const int d = p.H * HD;
   const T* Q = static_cast<const T*>(p.q);
   const T* KR = static_cast<const T*>(p.kring);
@@ -130,7 +149,7 @@ __global__ __launch_bounds__(256, 2) void swa_fwd32_k(AttnParams p) {
   const int64_t ktA = (lo / TQ) * TQ;
   const int nall = (int)((last - ktA) / TQ) + 1;
   const int per = (nall + (int)gridDim.z - 1) / (int)gridDim.z;
-  const int tb = min(nall, (int)blockIdx.z * per), te = min(nall, tb + per);
+  const int tb = min(nall, bz * per), te = min(nall, tb + per);
   const int64_t kt0 = ktA + (int64_t)tb * TQ;
   const int ntile = te - tb;
 
@@ -238,7 +257,7 @@ __global__ __launch_bounds__(256, 2) void swa_fwd32_k(AttnParams p) {
       if (p.lse && hl == 0) p.lse[(int64_t)h * p.n + qrow] = (m + log2f(l)) * LN2;
     } else {
       // unnormalised partial of this key range, combined by swa_combine_k
-      float* O = p.part + ((int64_t)blockIdx.z * p.n + qrow) * d + h * HD;
+      float* O = p.part + ((int64_t)bz * p.n + qrow) * d + h * HD;
 #pragma unroll
       for (int b = 0; b < C::HB; ++b)
 #pragma unroll
@@ -247,7 +266,7 @@ __global__ __launch_bounds__(256, 2) void swa_fwd32_k(AttnParams p) {
           if (c < HD) O[c] = oacc[b][r];
         }
       if (hl == 0) {
-        float* ml = p.part_ml + ((int64_t)blockIdx.z * p.H + h) * p.n * 2;
+        float* ml = p.part_ml + ((int64_t)bz * p.H + h) * p.n * 2;
         ml[2 * qrow] = m;
         ml[2 * qrow + 1] = l;
       }
@@ -316,8 +335,9 @@ __global__ __launch_bounds__(256, 2) void swa_bwd_dq32_k(AttnParams p) {
   __shared__ __attribute__((aligned(16))) T Kt[C::HDR * C::LSV];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5, ql = lane & 31;
-  const int h = blockIdx.y;
-  const int qs = blockIdx.x * QT;
+  int bx, h, bz;
+  attn_block(bx, h, bz);
+  const int qs = bx * QT;
   const int d = p.H * HD;
   const T* KR = static_cast<const T*>(p.kring);
   const T* VR = static_cast<const T*>(p.vring);
@@ -347,7 +367,7 @@ __global__ __launch_bounds__(256, 2) void swa_bwd_dq32_k(AttnParams p) {
   const int64_t ktA = (lo / TQ) * TQ;
   const int nall = (int)((last - ktA) / TQ) + 1;
   const int per = (nall + (int)gridDim.z - 1) / (int)gridDim.z;
-  const int tb = min(nall, (int)blockIdx.z * per), te = min(nall, tb + per);
+  const int tb = min(nall, bz * per), te = min(nall, tb + per);
   for (int it = tb; it < te; ++it) {
     const int64_t kt = ktA + (int64_t)it * TQ;
     const int64_t slot = kt % p.cap;
@@ -406,7 +426,7 @@ __global__ __launch_bounds__(256, 2) void swa_bwd_dq32_k(AttnParams p) {
           if (c < HD) G[c] = from_f32<T>(dacc[b][r] * scale);
         }
     } else {
-      float* G = p.part + ((int64_t)blockIdx.z * p.n + qrow) * d + h * HD;
+      float* G = p.part + ((int64_t)bz * p.n + qrow) * d + h * HD;
 #pragma unroll
       for (int b = 0; b < C::HB; ++b)
 #pragma unroll
@@ -445,8 +465,9 @@ __global__ __launch_bounds__(256) void swa_bwd_dkdv32_k(AttnParams p) {
   __shared__ float lse_s[TQ], D_s[TQ];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5, ql = lane & 31;
-  const int h = blockIdx.y;
-  const int ks0 = blockIdx.x * KT_;
+  int bx, h, bz;
+  attn_block(bx, h, bz);
+  const int ks0 = bx * KT_;
   const int d = p.H * HD;
   const T* Q = static_cast<const T*>(p.q);
   const T* G = static_cast<const T*>(p.dout);

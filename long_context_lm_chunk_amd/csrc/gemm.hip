@@ -161,6 +161,7 @@ DEVI void epi_apply(const GemmParams& p, float* st, int ES, int nr, int nc, int 
                     int tid, int nthr) {
   if (gridDim.z > 1) {
     float* slab = p.split_ws + (int64_t)blockIdx.z * p.M * p.N;
+#pragma unroll 4
     for (int g = tid; g < nr * (nc / 4); g += nthr) {
       const int r = g / (nc / 4), c = (g % (nc / 4)) * 4;
       const int row = row0 + r, col = n0 + c;
@@ -174,28 +175,49 @@ DEVI void epi_apply(const GemmParams& p, float* st, int ES, int nr, int nc, int 
     // delta -= lr * acc (fp32 master C, row-major), its storage-type copy C2;
     // the current weight W0 + delta goes back into the staged tile and then
     // out transposed to C3[col][row] in runs of 4 rows (the input-gradient
-    // products read it as a k-contiguous operand)
-    for (int g = tid; g < nr * (nc / 4); g += nthr) {
-      const int r = g / (nc / 4), c = (g % (nc / 4)) * 4;
-      const int row = row0 + r, col = n0 + c;
-      if (row >= p.M || col >= p.N) continue;
-      float* sp = st + r * ES + c;
-      const float4 v = *reinterpret_cast<const float4*>(sp);
-      const int64_t ci = (int64_t)row * p.ldc + col;
-      float4* wp = reinterpret_cast<float4*>(static_cast<float*>(p.C) + ci);
-      float4 w = *wp;
-      w.x -= p.alpha * v.x; w.y -= p.alpha * v.y; w.z -= p.alpha * v.z; w.w -= p.alpha * v.w;
-      *wp = w;
-      if (p.C2) store4<TO>(static_cast<TO*>(p.C2) + (int64_t)row * p.ldc2 + col, w);
-      if (p.C3) {
-        const float4 w0 = load4<TO>(static_cast<const TO*>(p.W0) + ci);
-        float4 cur; cur.x = w0.x + w.x; cur.y = w0.y + w.y; cur.z = w0.z + w.z; cur.w = w0.w + w.w;
-        *reinterpret_cast<float4*>(sp) = cur;
+    // products read it as a k-contiguous operand).  Groups are taken four at
+    // a time with every load issued before any store (the stores to the
+    // master could otherwise alias the next group's loads and serialise them).
+    constexpr int U = 4;
+    const int total = nr * (nc / 4);
+    for (int g0 = tid; g0 < total; g0 += U * nthr) {
+      float4 v[U], w[U], w0[U];
+      int64_t ci[U];
+      bool ok[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int g = g0 + u * nthr;
+        const int r = g / (nc / 4), c = (g % (nc / 4)) * 4;
+        const int row = row0 + r, col = n0 + c;
+        ok[u] = g < total && row < p.M && col < p.N;
+        ci[u] = (int64_t)row * p.ldc + col;
+        if (ok[u]) {
+          v[u] = *reinterpret_cast<const float4*>(st + r * ES + c);
+          w[u] = *reinterpret_cast<const float4*>(static_cast<const float*>(p.C) + ci[u]);
+          if (p.C3) w0[u] = load4<TO>(static_cast<const TO*>(p.W0) + ci[u]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (!ok[u]) continue;
+        const int g = g0 + u * nthr;
+        const int r = g / (nc / 4), c = (g % (nc / 4)) * 4;
+        const int row = row0 + r, col = n0 + c;
+        float4 x = w[u];
+        x.x -= p.alpha * v[u].x; x.y -= p.alpha * v[u].y; x.z -= p.alpha * v[u].z; x.w -= p.alpha * v[u].w;
+        *reinterpret_cast<float4*>(static_cast<float*>(p.C) + ci[u]) = x;
+        if (p.C2) store4<TO>(static_cast<TO*>(p.C2) + (int64_t)row * p.ldc2 + col, x);
+        if (p.C3) {
+          float4 cur;
+          cur.x = w0[u].x + x.x; cur.y = w0[u].y + x.y; cur.z = w0[u].z + x.z; cur.w = w0[u].w + x.w;
+          *reinterpret_cast<float4*>(st + r * ES + c) = cur;
+        }
       }
     }
     if (p.C3) {
       __syncthreads();
-      for (int g = tid; g < nc * (nr / 4); g += nthr) {
+  #pragma unroll 4
+    for (int g = tid; g < nc * (nr / 4); g += nthr) {
         const int c = g / (nr / 4), r = (g % (nr / 4)) * 4;
         const int row = row0 + r, col = n0 + c;
         if (row >= p.M || col >= p.N) continue;
@@ -211,6 +233,7 @@ DEVI void epi_apply(const GemmParams& p, float* st, int ES, int nr, int nc, int 
     }
   } else if constexpr (EPI == EPI_SWIGLU) {
     // columns: gate block 32c..32c+15, up block 32c+16..32c+31 -> act 16c..16c+15
+#pragma unroll 4
     for (int g = tid; g < nr * (nc / 8); g += nthr) {
       const int r = g / (nc / 8), q = g % (nc / 8);      // q: 4-wide group of act columns
       const int row = row0 + r;
@@ -226,6 +249,7 @@ DEVI void epi_apply(const GemmParams& p, float* st, int ES, int nr, int nc, int 
       store4<TO>(static_cast<TO*>(p.C2) + (int64_t)row * p.ldc2 + n0 / 2 + (q / 4) * 16 + (q % 4) * 4, a);
     }
   } else {
+#pragma unroll 4
     for (int g = tid; g < nr * (nc / 4); g += nthr) {
       const int r = g / (nc / 4), c = (g % (nc / 4)) * 4;
       const int row = row0 + r, col = n0 + c;
