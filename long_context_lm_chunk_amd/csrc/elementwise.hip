@@ -8,6 +8,24 @@
 namespace ttt {
 namespace {
 
+// 4 consecutive values to T (16 bytes of fp32 or 8 of bf16)
+template <typename T> DEVI void store4v(T* p, const float4& v);
+template <> DEVI void store4v<float>(float* p, const float4& v) { *reinterpret_cast<float4*>(p) = v; }
+template <> DEVI void store4v<bf16>(bf16* p, const float4& v) {
+  bf16x4 b;
+  b[0] = static_cast<bf16>(v.x); b[1] = static_cast<bf16>(v.y);
+  b[2] = static_cast<bf16>(v.z); b[3] = static_cast<bf16>(v.w);
+  *reinterpret_cast<bf16x4*>(p) = b;
+}
+template <typename T> DEVI float4 load4v(const T* p);
+template <> DEVI float4 load4v<float>(const float* p) { return *reinterpret_cast<const float4*>(p); }
+template <> DEVI float4 load4v<bf16>(const bf16* p) {
+  const bf16x4 b = *reinterpret_cast<const bf16x4*>(p);
+  return make_float4(static_cast<float>(b[0]), static_cast<float>(b[1]), static_cast<float>(b[2]),
+                     static_cast<float>(b[3]));
+}
+
+
 template <typename T>
 __global__ void embed_k(const int32_t* __restrict__ tok, int n, const T* __restrict__ E, int d, int V,
                         float* __restrict__ out, int* __restrict__ err) {
@@ -98,6 +116,88 @@ __global__ void ln_bwd_k(const float* __restrict__ dy, const float* __restrict__
     const float nv = a[i] + rs * (g[i] - m1 - yh * m2);
     a[i] = nv;
     if (acc_lo) acc_lo[(int64_t)row * d + i] = from_f32<T>(nv);
+  }
+}
+
+// Register-resident LayerNorm, d = 256 * NV: a lane holds NV float4 of its
+// row, all loaded at once, so the row is read from memory a single time and
+// every load of the wave is in flight together (the loop versions above
+// re-read the row per pass with one 4-byte load per lane per step).
+template <typename T, int NV>
+__global__ __launch_bounds__(256) void ln_fwd_reg_k(const float* __restrict__ x, int64_t ldx, int n,
+                                                    float eps, T* __restrict__ y, int64_t ldy,
+                                                    float* __restrict__ mean, float* __restrict__ rstd) {
+  constexpr int D = 256 * NV;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= n) return;
+  const float4* xr = reinterpret_cast<const float4*>(x + (int64_t)row * ldx);
+  float4 v[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) v[i] = xr[lane + 64 * i];
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+  const float mu = wave_sum(s) / D;
+  float q = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const float a = v[i].x - mu, b = v[i].y - mu, c = v[i].z - mu, e = v[i].w - mu;
+    q += (a * a + b * b) + (c * c + e * e);
+  }
+  const float rs = rsqrtf(wave_sum(q) / D + eps);
+  T* yr = y + (int64_t)row * ldy;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    float4 o;
+    o.x = (v[i].x - mu) * rs; o.y = (v[i].y - mu) * rs; o.z = (v[i].z - mu) * rs; o.w = (v[i].w - mu) * rs;
+    store4v<T>(yr + 4 * (lane + 64 * i), o);
+  }
+  if (lane == 0) {
+    if (mean) mean[row] = mu;
+    if (rstd) rstd[row] = rs;
+  }
+}
+
+template <typename T, int NV>
+__global__ __launch_bounds__(256) void ln_bwd_reg_k(const float* __restrict__ dy, const float* __restrict__ x,
+                                                    const float* __restrict__ mean,
+                                                    const float* __restrict__ rstd, int n,
+                                                    float* __restrict__ acc, T* __restrict__ acc_lo) {
+  constexpr int D = 256 * NV;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= n) return;
+  const float4* g = reinterpret_cast<const float4*>(dy + (int64_t)row * D);
+  const float4* xr = reinterpret_cast<const float4*>(x + (int64_t)row * D);
+  float4* a = reinterpret_cast<float4*>(acc + (int64_t)row * D);
+  const float mu = mean[row], rs = rstd[row];
+  float4 gv[NV], yh[NV], av[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    gv[i] = g[lane + 64 * i];
+    yh[i] = xr[lane + 64 * i];
+    av[i] = a[lane + 64 * i];
+  }
+  float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    yh[i].x = (yh[i].x - mu) * rs; yh[i].y = (yh[i].y - mu) * rs;
+    yh[i].z = (yh[i].z - mu) * rs; yh[i].w = (yh[i].w - mu) * rs;
+    s1 += (gv[i].x + gv[i].y) + (gv[i].z + gv[i].w);
+    s2 += (gv[i].x * yh[i].x + gv[i].y * yh[i].y) + (gv[i].z * yh[i].z + gv[i].w * yh[i].w);
+  }
+  const float m1 = wave_sum(s1) / D, m2 = wave_sum(s2) / D;
+  T* lo = acc_lo ? acc_lo + (int64_t)row * D : nullptr;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    float4 nv;
+    nv.x = av[i].x + rs * (gv[i].x - m1 - yh[i].x * m2);
+    nv.y = av[i].y + rs * (gv[i].y - m1 - yh[i].y * m2);
+    nv.z = av[i].z + rs * (gv[i].z - m1 - yh[i].z * m2);
+    nv.w = av[i].w + rs * (gv[i].w - m1 - yh[i].w * m2);
+    a[lane + 64 * i] = nv;
+    if (lo) store4v<T>(lo + 4 * (lane + 64 * i), nv);
   }
 }
 
@@ -199,27 +299,48 @@ __global__ void rope_bwd_k(T* __restrict__ g, int n, int H, int hd, int64_t pos0
 
 // dz from dact (fp32 [n][F]) and the saved pre-activations.
 // SwiGLU: z [n][2F] with gate/up in alternating blocks of 16 columns.
+// dz from d(act) and the pre-activations z, four activations per thread
+// (SwiGLU: gate columns 32c..32c+15, up columns 32c+16..32c+31 of z and dz
+// for activations 16c..16c+15).  F % 4 == 0, n * F < 2^31.
 template <typename T>
 __global__ void act_bwd_k(const float* __restrict__ dact, const T* __restrict__ z, int n, int F,
                           int swiglu, T* __restrict__ dz) {
-  const int64_t total = (int64_t)n * F;
-  const int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (idx >= total) return;
-  const int f = idx % F;
-  const int64_t t = idx / F;
-  const float da = dact[idx];
+  const int idx = (blockIdx.x * blockDim.x + threadIdx.x) * 4;   // first of 4 activations
+  if (idx >= n * F) return;
+  const int t = idx / F, f = idx - t * F;
+  const float4 da = *reinterpret_cast<const float4*>(dact + idx);
   if (swiglu) {
-    const int64_t cg = t * 2 * F + (f / 16) * 32 + (f % 16);
-    const float g = to_f32(z[cg]), u = to_f32(z[cg + 16]);
-    const float sg = 1.f / (1.f + __expf(-g));
-    const float si = g * sg;
-    dz[cg] = from_f32<T>(da * u * sg * (1.f + g * (1.f - sg)));
-    dz[cg + 16] = from_f32<T>(da * si);
+    const int64_t cg = (int64_t)t * 2 * F + (f / 16) * 32 + (f % 16);
+    const float4 g = load4v<T>(z + cg), u = load4v<T>(z + cg + 16);
+    float4 dg, du;
+    {
+      const float sg = 1.f / (1.f + __expf(-g.x));
+      dg.x = da.x * u.x * sg * (1.f + g.x * (1.f - sg)); du.x = da.x * g.x * sg;
+    }
+    {
+      const float sg = 1.f / (1.f + __expf(-g.y));
+      dg.y = da.y * u.y * sg * (1.f + g.y * (1.f - sg)); du.y = da.y * g.y * sg;
+    }
+    {
+      const float sg = 1.f / (1.f + __expf(-g.z));
+      dg.z = da.z * u.z * sg * (1.f + g.z * (1.f - sg)); du.z = da.z * g.z * sg;
+    }
+    {
+      const float sg = 1.f / (1.f + __expf(-g.w));
+      dg.w = da.w * u.w * sg * (1.f + g.w * (1.f - sg)); du.w = da.w * g.w * sg;
+    }
+    store4v<T>(dz + cg, dg);
+    store4v<T>(dz + cg + 16, du);
   } else {
-    const float zz = to_f32(z[idx]);
-    const float cdf = 0.5f * (1.f + erff(zz * 0.70710678118654752f));
-    const float pdf = 0.39894228040143268f * __expf(-0.5f * zz * zz);
-    dz[idx] = from_f32<T>(da * (cdf + zz * pdf));
+    const float4 zz = load4v<T>(z + idx);
+    auto gd = [](float v, float d) {
+      const float cdf = 0.5f * (1.f + erff(v * 0.70710678118654752f));
+      const float pdf = 0.39894228040143268f * __expf(-0.5f * v * v);
+      return d * (cdf + v * pdf);
+    };
+    float4 o;
+    o.x = gd(zz.x, da.x); o.y = gd(zz.y, da.y); o.z = gd(zz.z, da.z); o.w = gd(zz.w, da.w);
+    store4v<T>(dz + idx, o);
   }
 }
 
@@ -346,6 +467,16 @@ void layernorm_fwd(const float* x, int64_t ldx, int n, int d, float eps, void* y
          hipLaunchKernelGGL(ln_fwd_row_k<float>, dim3(n), dim3(256), 0, s, x, ldx, d, eps, (float*)y, ldy, mean, rstd));
     return;
   }
+  if (d % 256 == 0 && d <= 4096 && ldx % 4 == 0 && ldy % 4 == 0) {
+    switch (d / 256) {
+#define LNF(NV) case NV: TSEL(bf, hipLaunchKernelGGL((ln_fwd_reg_k<bf16, NV>), dim3(nblk(n, 4)), dim3(256), 0, s, x, ldx, n, eps, (bf16*)y, ldy, mean, rstd), \
+                               hipLaunchKernelGGL((ln_fwd_reg_k<float, NV>), dim3(nblk(n, 4)), dim3(256), 0, s, x, ldx, n, eps, (float*)y, ldy, mean, rstd)); return;
+      LNF(1) LNF(2) LNF(3) LNF(4) LNF(5) LNF(6) LNF(7) LNF(8) LNF(9) LNF(10) LNF(11) LNF(12)
+      LNF(13) LNF(14) LNF(15) LNF(16)
+#undef LNF
+      default: break;
+    }
+  }
   TSEL(bf, hipLaunchKernelGGL(ln_fwd_k<bf16>, dim3(nblk(n, 4)), dim3(256), 0, s, x, ldx, n, d, eps, (bf16*)y, ldy, mean, rstd),
        hipLaunchKernelGGL(ln_fwd_k<float>, dim3(nblk(n, 4)), dim3(256), 0, s, x, ldx, n, d, eps, (float*)y, ldy, mean, rstd));
 }
@@ -353,6 +484,16 @@ void layernorm_fwd(const float* x, int64_t ldx, int n, int d, float eps, void* y
 void layernorm_bwd_acc(const float* dy, const float* x, const float* mean, const float* rstd, int n,
                        int d, float* acc, void* acc_lo, bool bf, hipStream_t s) {
   if (n <= 0) return;
+  if (d % 256 == 0 && d <= 4096) {
+    switch (d / 256) {
+#define LNB(NV) case NV: TSEL(bf, hipLaunchKernelGGL((ln_bwd_reg_k<bf16, NV>), dim3(nblk(n, 4)), dim3(256), 0, s, dy, x, mean, rstd, n, acc, (bf16*)acc_lo), \
+                               hipLaunchKernelGGL((ln_bwd_reg_k<float, NV>), dim3(nblk(n, 4)), dim3(256), 0, s, dy, x, mean, rstd, n, acc, (float*)acc_lo)); return;
+      LNB(1) LNB(2) LNB(3) LNB(4) LNB(5) LNB(6) LNB(7) LNB(8) LNB(9) LNB(10) LNB(11) LNB(12)
+      LNB(13) LNB(14) LNB(15) LNB(16)
+#undef LNB
+      default: break;
+    }
+  }
   TSEL(bf, hipLaunchKernelGGL(ln_bwd_k<bf16>, dim3(nblk(n, 4)), dim3(256), 0, s, dy, x, mean, rstd, n, d, acc, (bf16*)acc_lo),
        hipLaunchKernelGGL(ln_bwd_k<float>, dim3(nblk(n, 4)), dim3(256), 0, s, dy, x, mean, rstd, n, d, acc, (float*)acc_lo));
 }
@@ -405,10 +546,10 @@ void rope_bwd(void* dqkv, int n, int H, int hd, int64_t pos0, const double* thet
 
 void act_bwd(const float* dact, const void* z, int n, int F, bool swiglu, void* dz, bool bf,
              hipStream_t s) {
-  const int64_t total = (int64_t)n * F;
+  const int64_t total = (int64_t)n * F;   // F % 16 == 0 (a configuration rule), n * F < 2^31
   if (total <= 0) return;
-  TSEL(bf, hipLaunchKernelGGL(act_bwd_k<bf16>, dim3(nblk(total, 256)), dim3(256), 0, s, dact, (const bf16*)z, n, F, (int)swiglu, (bf16*)dz),
-       hipLaunchKernelGGL(act_bwd_k<float>, dim3(nblk(total, 256)), dim3(256), 0, s, dact, (const float*)z, n, F, (int)swiglu, (float*)dz));
+  TSEL(bf, hipLaunchKernelGGL(act_bwd_k<bf16>, dim3(nblk(total / 4, 256)), dim3(256), 0, s, dact, (const bf16*)z, n, F, (int)swiglu, (bf16*)dz),
+       hipLaunchKernelGGL(act_bwd_k<float>, dim3(nblk(total / 4, 256)), dim3(256), 0, s, dact, (const float*)z, n, F, (int)swiglu, (float*)dz));
 }
 
 void convert_weight(const void* src, int rows, int cols, bool transpose, int ilv, void* dst, bool bf,
