@@ -140,8 +140,15 @@ struct ttt_model {
   float* pmax = nullptr; float* psum = nullptr; float* tlog = nullptr; float* lse_ce = nullptr;
   void* G = nullptr;
   float* dh = nullptr; void* dh_lo = nullptr; float* dact = nullptr; void* dz = nullptr;
-  void* dhT = nullptr; void* actT = nullptr; void* dzT = nullptr; void* bT = nullptr;
+  // transposed operands of the weight-gradient products, one set per fast
+  // block (the updates run on their own stream, concurrently with the rest
+  // of the backward pass): [features][Cp]
+  struct TOps { void* dhT = nullptr; void* actT = nullptr; void* dzT = nullptr; void* bT = nullptr; };
+  std::vector<TOps> tops;
   int64_t Cp = 0;                       // their row stride
+  hipStream_t sc = nullptr;             // fast-weight updates (SGD products)
+  std::vector<hipEvent_t> evT1, evT2;   // per fast block: update operands ready
+  hipEvent_t evC = nullptr;             // all updates of the chunk done
   float* dtmp = nullptr; void* dout = nullptr; void* dqkv = nullptr; float* Dattn = nullptr;
   float* attn_part = nullptr; float* attn_ml = nullptr;   // key-range split partials
   float* split_ws = nullptr; int64_t split_cap = 0;         // split-K partials of the GEMMs
@@ -280,10 +287,14 @@ size_t layout(ttt_model* m, void* base) {
   // transposed operands of the weight-gradient products: [features][Cp],
   // Cp = the chunk capacity rounded up to a multiple of 8 (zero padded)
   m->Cp = round_up((int64_t)C, 8);
-  m->dhT = cv.take<void>((size_t)m->Cp * d * es);
-  m->actT = cv.take<void>((size_t)m->Cp * F * es);
-  m->dzT = cv.take<void>((size_t)m->Cp * F2 * es);
-  m->bT = cv.take<void>((size_t)m->Cp * d * es);
+  m->tops.assign(m->q, ttt_model::TOps());
+  for (int j = 0; j < m->q; ++j) {
+    ttt_model::TOps& t = m->tops[j];
+    t.dhT = cv.take<void>((size_t)m->Cp * d * es);
+    t.actT = cv.take<void>((size_t)m->Cp * F * es);
+    t.dzT = cv.take<void>((size_t)m->Cp * F2 * es);
+    t.bT = cv.take<void>((size_t)m->Cp * d * es);
+  }
   m->dact = cv.take<float>((size_t)C * F * 4);
   m->dz = cv.take<void>((size_t)C * F2 * es);
   m->dtmp = cv.take<float>((size_t)C * d * 4);
@@ -528,14 +539,19 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
     ga.A = m->dh_lo; ga.lda = d; ga.B = fw.ct_dn; ga.ldb = d; ga.M = n; ga.N = F; ga.K = d;
     ga.C = m->dact; ga.ldc = F;
     rc = run_gemm(m, ga, true, true, EPI_STORE, true, s); if (rc) return rc;
-    // Wdn -= lr * dh^T act   ([d][F], reduction over the chunk's tokens)
-    transpose(m->dh_lo, n, d, d, m->dhT, m->Cp, np, bf, s);
-    transpose(b.act, n, F, F, m->actT, m->Cp, np, bf, s);
+    // Wdn -= lr * dh^T act   ([d][F], reduction over the chunk's tokens).
+    // The update runs on the update stream: its operands are transposed here
+    // (after ga has read the old weights), then the chain goes on at once.
+    ttt_model::TOps& to = m->tops[j];
+    transpose(m->dh_lo, n, d, d, to.dhT, m->Cp, np, bf, s);
+    transpose(b.act, n, F, F, to.actT, m->Cp, np, bf, s);
+    HIPCHK(hipEventRecord(m->evT1[j], s));
+    HIPCHK(hipStreamWaitEvent(m->sc, m->evT1[j], 0));
     GemmParams gw;
-    gw.A = m->dhT; gw.lda = m->Cp; gw.B = m->actT; gw.ldb = m->Cp; gw.M = d; gw.N = F; gw.K = np;
+    gw.A = to.dhT; gw.lda = m->Cp; gw.B = to.actT; gw.ldb = m->Cp; gw.M = d; gw.N = F; gw.K = np;
     gw.C = fw.m_dn; gw.ldc = F; gw.C2 = bf ? fw.s_dn : nullptr; gw.ldc2 = F; gw.alpha = lr;
     gw.C3 = fw.ct_dn; gw.ldc3 = d; gw.W0 = ly.wdn;
-    rc = run_gemm(m, gw, true, true, EPI_SGD, true, s); if (rc) return rc;
+    rc = run_gemm(m, gw, true, true, EPI_SGD, true, m->sc); if (rc) return rc;
     act_bwd(m->dact, b.z, n, F, m->c.mlp == TTT_MLP_SWIGLU, m->dz, bf, s);
     if (j > 0) {
       GemmParams gb;   // db = dz . Wup (before its update: Wup^T [d][F2])
@@ -543,14 +559,16 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
       gb.C = m->dtmp; gb.ldc = d;
       rc = run_gemm(m, gb, true, true, EPI_STORE, true, s); if (rc) return rc;
     }
-    // Wup -= lr * dz^T b
-    transpose(m->dz, n, F2, F2, m->dzT, m->Cp, np, bf, s);
-    transpose(b.b, n, d, d, m->bT, m->Cp, np, bf, s);
+    // Wup -= lr * dz^T b  (update stream, after gb has read the old weights)
+    transpose(m->dz, n, F2, F2, to.dzT, m->Cp, np, bf, s);
+    transpose(b.b, n, d, d, to.bT, m->Cp, np, bf, s);
+    HIPCHK(hipEventRecord(m->evT2[j], s));
+    HIPCHK(hipStreamWaitEvent(m->sc, m->evT2[j], 0));
     GemmParams gw2;
-    gw2.A = m->dzT; gw2.lda = m->Cp; gw2.B = m->bT; gw2.ldb = m->Cp; gw2.M = F2; gw2.N = d; gw2.K = np;
+    gw2.A = to.dzT; gw2.lda = m->Cp; gw2.B = to.bT; gw2.ldb = m->Cp; gw2.M = F2; gw2.N = d; gw2.K = np;
     gw2.C = fw.m_up; gw2.ldc = d; gw2.C2 = bf ? fw.s_up : nullptr; gw2.ldc2 = d; gw2.alpha = lr;
     gw2.C3 = fw.ct_up; gw2.ldc3 = F2; gw2.W0 = ly.wup;
-    rc = run_gemm(m, gw2, true, true, EPI_SGD, true, s); if (rc) return rc;
+    rc = run_gemm(m, gw2, true, true, EPI_SGD, true, m->sc); if (rc) return rc;
     if (j == 0) break;   // no gradient below the first fast MLP
     layernorm_bwd_acc(m->dtmp, x2, b.mean2, b.rstd2, n, d, m->dh, m->dh_lo, bf, s);
     GemmParams gdo;   // dO = dh . Wo  (Wo^T [d][d])
@@ -579,6 +597,10 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
     rc = run_gemm(m, gq, true, true, EPI_STORE, true, s); if (rc) return rc;
     layernorm_bwd_acc(m->dtmp, b.xin, b.mean1, b.rstd1, n, d, m->dh, m->dh_lo, bf, s);
   }
+  // every update of this chunk lands before anything else on s (the next
+  // chunk's forward reads the new weights)
+  HIPCHK(hipEventRecord(m->evC, m->sc));
+  HIPCHK(hipStreamWaitEvent(s, m->evC, 0));
   return TTT_OK;
 }
 
@@ -687,7 +709,11 @@ int ttt_model_load(const ttt_config* cfg, const void* const* weights, int32_t n_
   }
   {
     hipError_t e1 = hipStreamCreateWithFlags(&m->sa, hipStreamNonBlocking);
-    hipEvent_t* evs[5] = {&m->ev0, &m->evA[0], &m->evA[1], &m->evB[0], &m->evB[1]};
+    if (e1 == hipSuccess) e1 = hipStreamCreateWithFlags(&m->sc, hipStreamNonBlocking);
+    m->evT1.assign(m->q, nullptr);
+    m->evT2.assign(m->q, nullptr);
+    std::vector<hipEvent_t*> evs = {&m->ev0, &m->evA[0], &m->evA[1], &m->evB[0], &m->evB[1], &m->evC};
+    for (int j = 0; j < m->q; ++j) { evs.push_back(&m->evT1[j]); evs.push_back(&m->evT2[j]); }
     for (auto* e : evs)
       if (e1 == hipSuccess) e1 = hipEventCreateWithFlags(e, hipEventDisableTiming);
     if (e1 != hipSuccess) {
@@ -883,10 +909,14 @@ void ttt_model_free(ttt_model* m) {
   if (m->dec_exec) (void)hipGraphExecDestroy(m->dec_exec);
   for (auto& t : m->tm)
     for (auto e : t.ev) (void)hipEventDestroy(e);
-  hipEvent_t evs[5] = {m->ev0, m->evA[0], m->evA[1], m->evB[0], m->evB[1]};
+  if (m->sc) (void)hipStreamSynchronize(m->sc);
+  std::vector<hipEvent_t> evs = {m->ev0, m->evA[0], m->evA[1], m->evB[0], m->evB[1], m->evC};
+  evs.insert(evs.end(), m->evT1.begin(), m->evT1.end());
+  evs.insert(evs.end(), m->evT2.begin(), m->evT2.end());
   for (auto e : evs)
     if (e) (void)hipEventDestroy(e);
   if (m->sa) (void)hipStreamDestroy(m->sa);
+  if (m->sc) (void)hipStreamDestroy(m->sc);
   delete m;
 }
 
