@@ -590,14 +590,14 @@ void fwd_t(const AttnParams& p, hipStream_t s) {
   }
 }
 template <typename T>
-void bwd_t(const AttnParams& p, hipStream_t s) {
+void bwd_t(const AttnParams& p, hipStream_t s, hipStream_t s2) {
   const int nz = pick_split(p, ((p.n + 127) / 128) * p.H);
   dim3 gq((p.n + 127) / 128, p.H, nz);
   dim3 gk((p.n + 127) / 128, p.H);
   switch (p.hd) {
 #define CASE(HDV) case HDV: \
     hipLaunchKernelGGL((swa_bwd_dq32_k<T, HDV>), gq, dim3(256), 0, s, p); \
-    hipLaunchKernelGGL((swa_bwd_dkdv32_k<T, HDV>), gk, dim3(256), 0, s, p); break;
+    hipLaunchKernelGGL((swa_bwd_dkdv32_k<T, HDV>), gk, dim3(256), 0, s2, p); break;
     CASE(16) CASE(32) CASE(64) CASE(96) CASE(128)
 #undef CASE
     default: return;
@@ -622,9 +622,9 @@ void ring_transpose(const void* src, int64_t ld, int64_t src_cap, int n, int H, 
   else hipLaunchKernelGGL(ring_tr_k<float>, grid, dim3(256), 0, s, (const float*)src, ld, src_cap, n, H, hd, pos0, (float*)dst, cap);
 }
 
-void swa_bwd(const AttnParams& p, bool bf, hipStream_t s) {
+void swa_bwd(const AttnParams& p, bool bf, hipStream_t s, hipStream_t s_kv) {
   if (p.n <= 0) return;
-  if (bf) bwd_t<bf16>(p, s); else bwd_t<float>(p, s);
+  if (bf) bwd_t<bf16>(p, s, s_kv); else bwd_t<float>(p, s, s_kv);
 }
 
 }  // namespace ttt

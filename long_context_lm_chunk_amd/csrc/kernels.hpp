@@ -94,7 +94,9 @@ void swa_fwd(const AttnParams& p, bool bf16, hipStream_t s);
 // (pos0+t) mod src_cap of a ring) into a transposed ring [H*hd][cap]
 void ring_transpose(const void* src, int64_t ld, int64_t src_cap, int n, int H, int hd, int64_t pos0,
                     void* dst, int64_t cap, bool bf16, hipStream_t s);
-void swa_bwd(const AttnParams& p, bool bf16, hipStream_t s);
+// dQ on s, dK/dV on s_kv (the two are independent; the caller orders s_kv
+// after the inputs and joins it before using dK/dV; s_kv may equal s)
+void swa_bwd(const AttnParams& p, bool bf16, hipStream_t s, hipStream_t s_kv);
 
 // ---- decode (decode.hip)
 // Every decode kernel reads the position from dstate = {pos, ci} on the

@@ -149,6 +149,8 @@ struct ttt_model {
   hipStream_t sc = nullptr;             // fast-weight updates (SGD products)
   std::vector<hipEvent_t> evT1, evT2;   // per fast block: update operands ready
   hipEvent_t evC = nullptr;             // all updates of the chunk done
+  hipStream_t sk = nullptr;             // dK/dV of the attention backward, beside dQ
+  hipEvent_t evK0 = nullptr, evK1 = nullptr;
   float* dtmp = nullptr; void* dout = nullptr; void* dqkv = nullptr; float* Dattn = nullptr;
   float* attn_part = nullptr; float* attn_ml = nullptr;   // key-range split partials
   float* split_ws = nullptr; int64_t split_cap = 0;         // split-K partials of the GEMMs
@@ -588,7 +590,11 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
       double in = 0;
       const double tot = pairs(p0, n, m->W, p0, &in);
       Scope t(m, CLS_ATTN_BWD, s, 4.0 * d * (tot + in));
-      swa_bwd(ap, bf, s);
+      HIPCHK(hipEventRecord(m->evK0, s));            // inputs of dK/dV ready
+      HIPCHK(hipStreamWaitEvent(m->sk, m->evK0, 0));
+      swa_bwd(ap, bf, s, m->sk);
+      HIPCHK(hipEventRecord(m->evK1, m->sk));
+      HIPCHK(hipStreamWaitEvent(s, m->evK1, 0));     // dK/dV in place for the RoPE backward
     }
     rope_bwd(m->dqkv, n, m->H, m->hd, p0, m->theta, bf, s);
     GemmParams gq;   // da = dqkv . Wqkv  (Wqkv^T [d][3d])
@@ -710,9 +716,11 @@ int ttt_model_load(const ttt_config* cfg, const void* const* weights, int32_t n_
   {
     hipError_t e1 = hipStreamCreateWithFlags(&m->sa, hipStreamNonBlocking);
     if (e1 == hipSuccess) e1 = hipStreamCreateWithFlags(&m->sc, hipStreamNonBlocking);
+    if (e1 == hipSuccess) e1 = hipStreamCreateWithFlags(&m->sk, hipStreamNonBlocking);
     m->evT1.assign(m->q, nullptr);
     m->evT2.assign(m->q, nullptr);
-    std::vector<hipEvent_t*> evs = {&m->ev0, &m->evA[0], &m->evA[1], &m->evB[0], &m->evB[1], &m->evC};
+    std::vector<hipEvent_t*> evs = {&m->ev0, &m->evA[0], &m->evA[1], &m->evB[0], &m->evB[1], &m->evC,
+                                    &m->evK0, &m->evK1};
     for (int j = 0; j < m->q; ++j) { evs.push_back(&m->evT1[j]); evs.push_back(&m->evT2[j]); }
     for (auto* e : evs)
       if (e1 == hipSuccess) e1 = hipEventCreateWithFlags(e, hipEventDisableTiming);
@@ -910,13 +918,16 @@ void ttt_model_free(ttt_model* m) {
   for (auto& t : m->tm)
     for (auto e : t.ev) (void)hipEventDestroy(e);
   if (m->sc) (void)hipStreamSynchronize(m->sc);
-  std::vector<hipEvent_t> evs = {m->ev0, m->evA[0], m->evA[1], m->evB[0], m->evB[1], m->evC};
+  if (m->sk) (void)hipStreamSynchronize(m->sk);
+  std::vector<hipEvent_t> evs = {m->ev0, m->evA[0], m->evA[1], m->evB[0], m->evB[1], m->evC,
+                                 m->evK0, m->evK1};
   evs.insert(evs.end(), m->evT1.begin(), m->evT1.end());
   evs.insert(evs.end(), m->evT2.begin(), m->evT2.end());
   for (auto e : evs)
     if (e) (void)hipEventDestroy(e);
   if (m->sa) (void)hipStreamDestroy(m->sa);
   if (m->sc) (void)hipStreamDestroy(m->sc);
+  if (m->sk) (void)hipStreamDestroy(m->sk);
   delete m;
 }
 
