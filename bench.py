@@ -27,6 +27,23 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0
 
+# HBM bytes per launch of the fused weight-gradient + SGD kernel from two
+# rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE) over the 3B-shape prefill,
+# scaled by a plain 1 GiB elementwise copy measured in the same runs
+# (FETCH_SIZE reads 0.5x the bytes read, WRITE_SIZE 1.0x the bytes written),
+# averaged over the two launch shapes.  Valid only for the GEMM source it was
+# measured on (sha256 of csrc/gemm.hip); otherwise reported as null.
+SGD_TRAFFIC = {"gemm_src_sha256": "2e363b95c0f07be70da6b936e8044ec39dd06e07bdc171f94e74db664581f504",
+               "bytes_per_launch": 741.5e6,
+               "profile": "profiles/sgd_gemm_3B_chunk1024_traffic.md"}
+
+
+def _gemm_src_sha():
+    import hashlib
+    path = os.path.join(ROOT, "long_context_lm_chunk_amd", "csrc", "gemm.hip")
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
 
 def prefill_flops(cfg, T):
     """Algorithmic FLOPs of one prefill (forward of every layer, head,
@@ -43,6 +60,35 @@ def prefill_flops(cfg, T):
     bwd = 2 * ((T - 1) * d * V + T * (k + 1) * d * F + (q - 1) * T * (2 * k * d * F + 4 * d * d)
                + (q - 1) * d * (2 * sum_n + 2 * sum_m))
     return float(fwd + bwd)
+
+
+def sgd_bytes_per_launch(cfg, T):
+    """Algorithmic HBM bytes of one fused weight-gradient + SGD launch,
+    averaged over the launches of a prefill: the fp32 delta master read and
+    written (8 B), its storage-type copy (2 B), W0 read (2 B), the transposed
+    current weight written (2 B) per weight, plus both bf16 operands
+    ([out][tokens] and [in][tokens], tokens padded to 8)."""
+    d, F, C = cfg["d_model"], cfg["d_ff"], cfg["chunk"]
+    F2 = 2 * F if cfg["mlp"] == "swiglu" else F
+    tot, launches = 0.0, 0
+    for c0 in range(0, T - 1, C):
+        n = min(C, T - c0)
+        np_ = (n + 7) // 8 * 8
+        for (M, N) in ((d, F), (F2, d)):
+            tot += 14.0 * M * N + 2.0 * (M + N) * np_
+            launches += 1
+    return tot / max(launches, 1)
+
+
+def sgd_flops_per_launch(cfg, T):
+    d, F, C = cfg["d_model"], cfg["d_ff"], cfg["chunk"]
+    F2 = 2 * F if cfg["mlp"] == "swiglu" else F
+    tot, launches = 0.0, 0
+    for c0 in range(0, T - 1, C):
+        n = min(C, T - c0)
+        tot += 2.0 * (d * F + F2 * d) * n
+        launches += 2
+    return tot / max(launches, 1)
 
 
 def cpu_baseline(cfg, weights_gpu, tokens_np, sample_tokens=256):
@@ -82,6 +128,9 @@ def main():
     ap.add_argument("--decode-tokens", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=1024)
+    ap.add_argument("--copy-probe", type=int, default=0,
+                    help="MiB of a plain device copy run first, as the reference for "
+                         "FETCH_SIZE/WRITE_SIZE counter scaling")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); the inner loop of one "
@@ -105,6 +154,15 @@ def main():
     torch.cuda.synchronize()
     print(f"# setup {time.perf_counter() - t_setup:.1f}s, workspace "
           f"{model.workspace.numel() / 1e9:.2f} GB", file=sys.stderr, flush=True)
+
+    if args.copy_probe:
+        src = torch.ones(args.copy_probe * (1 << 18), dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)   # one elementwise kernel: N*4 bytes read, N*4 written
+        torch.cuda.synchronize()
+        print(f"# copy probe: {args.copy_probe} MiB read + {args.copy_probe} MiB written",
+              file=sys.stderr, flush=True)
+        del src, dst
 
     losses = None
     for i in range(args.warmup):
@@ -154,15 +212,33 @@ def main():
         torch.cuda.synchronize()
         dec_ms = e0.elapsed_time(e1) / args.decode_tokens
 
-    up = ktime["mlp_up"]
+    # Roofline of the dominant kernel (largest measured time of the classes
+    # that are one kernel symbol each): the fused weight-gradient + SGD
+    # products (bound by HBM: ~140 FLOP per byte, below the ridge point of
+    # 2.5 PFLOP/s / 8 TB/s) or the frozen-block MLP up-projection (MFMA).
     roof = None
-    if up["launches"]:
+    sg, up = ktime["dw_sgd"], ktime["mlp_up"]
+    if sg["launches"] and (sg["ms"] >= up["ms"] or not up["launches"]):
+        avg_ms = sg["ms"] / sg["launches"]
+        by = sgd_bytes_per_launch(dict(cfg, T=T), T)
+        ach = by / (avg_ms / 1e3) / 1e9
+        traffic = (SGD_TRAFFIC["bytes_per_launch"] if _gemm_src_sha() == SGD_TRAFFIC["gemm_src_sha256"]
+                   else None)
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic,
+                "kernel": "gemm_kernel<bf16, A k-contig, B k-contig, SGD epilogue> (fused weight "
+                          "gradient + SGD of the fast MLPs: [d][F] and [2F][d] over the chunk's tokens)",
+                "algorithmic_bytes_per_launch": round(by), "flops_per_launch": round(sgd_flops_per_launch(
+                    dict(cfg, T=T), T)),
+                "avg_launch_ms": round(avg_ms, 4), "launches_per_step": sg["launches"],
+                "stream": "fast-weight update stream (concurrent with the backward chain)"}
+    elif up["launches"]:
         avg_ms = up["ms"] / up["launches"]
         ach = up["flops"] / up["launches"] / (avg_ms / 1e3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                "kernel": "gemm_kernel<bf16, A k-contig, B k-contig, SWIGLU, bf16, single B> "
-                          "(frozen-block MLP up-projection, M=8192 N=16384 K=3072)",
+                "kernel": "gemm256_kernel<SWIGLU, bf16, single B> (frozen-block MLP up-projection, "
+                          "M=8192 N=16384 K=3072)",
                 "avg_launch_ms": round(avg_ms, 4), "launches_per_step": up["launches"]}
 
     cpu = None

@@ -1,42 +1,80 @@
 """Summarise a rocprofv3 kernel-trace database into a short markdown table.
 
-Usage: python -m long_context_lm_chunk_amd.profile_summary RESULTS_DB [TITLE] [COMMAND]
+Usage:
+  python -m long_context_lm_chunk_amd.profile_summary RESULTS_DB [--title T] [--cmd C]
+         [--per N] [--match SUBSTR ...] [--top K]
 
-Reads the per-dispatch kernel table that ``rocprofv3 --kernel-trace``
-writes (SQLite) and prints calls, total/average duration and share per
-kernel, with demangled-ish short names.  Raw databases stay out of the
-repository; only these summaries are kept.
+Reads the per-dispatch kernel table that ``rocprofv3 --kernel-trace`` writes
+(SQLite) and prints calls, total and average duration and share per kernel
+symbol (the unit in which a HIP-event average over one kernel's launches can
+be compared with the trace), with shortened names.  ``--per N`` also divides
+calls and time by N (e.g. the number of prefills in the run); ``--match``
+keeps only symbols containing one of the substrings.  Raw databases stay out
+of the repository; only these summaries are kept.
 """
 from __future__ import annotations
 
+import argparse
 import re
 import sqlite3
-import sys
 
 
 def short(name: str) -> str:
     n = re.sub(r"\s+", " ", name)
-    m = re.match(r"_ZN3ttt12_GLOBAL__N_1\d+(\w+?)I(.*)EEvN.*", n)
+    n = n.replace("void ttt::(anonymous namespace)::", "").replace("ttt::(anonymous namespace)::", "")
+    n = n.replace("bool _Accum, bool, E", "bf16, true")   # how the tool prints "__bf16, true"
+    m = re.match(r"_ZN3ttt12_GLOBAL__N_1\d+(\w+?)I(.+?)EEv", n)
     if m:
-        return f"{m.group(1)}<{m.group(2)}>"
-    return n[:110]
+        toks, a = [], m.group(2)
+        while a:
+            t = re.match(r"DF16b|f|Lb[01]E|Li-?\d+E", a)
+            if not t:
+                toks.append(a)
+                break
+            g = t.group(0)
+            toks.append({"DF16b": "bf16", "f": "float", "Lb1E": "true", "Lb0E": "false"}.get(
+                g, g[2:-1] if g.startswith("Li") else g))
+            a = a[len(g):]
+        return f"{m.group(1)}<{', '.join(toks)}>"
+    m = re.match(r"_ZN3ttt12_GLOBAL__N_1\d+(\w+?)E", n)
+    if m:
+        return m.group(1)
+    n = re.sub(r"\((ttt::|DecGemv|HIP_vector|float const|int const).*", "", n)
+    return n[:90]
 
 
-def summarise(db: str, title: str = "", cmd: str = "") -> str:
+def summarise(db: str, title: str = "", cmd: str = "", per: float = 1.0, match=None, top: int = 30) -> str:
     c = sqlite3.connect(db)
     rows = c.execute("select name, count(*), sum(duration), avg(duration) from kernels "
                      "group by name order by sum(duration) desc").fetchall()
+    if match:
+        rows = [r for r in rows if any(mm in r[0] for mm in match)]
     total = sum(r[2] for r in rows)
     out = [f"# {title}" if title else "# kernel summary", ""]
     if cmd:
         out += ["Command:", "", "```", cmd, "```", ""]
-    out += [f"Total kernel time {total / 1e6:.1f} ms over {sum(r[1] for r in rows)} dispatches.", "",
-            "| kernel | calls | total ms | avg us | share |", "|---|---|---|---|---|"]
-    for name, n, tot, avg in rows[:30]:
-        out.append(f"| `{short(name)}` | {n} | {tot / 1e6:.2f} | {avg / 1e3:.1f} | {100 * tot / total:.1f}% |")
+    out += [f"Total kernel time {total / 1e6:.1f} ms over {sum(r[1] for r in rows)} dispatches"
+            + (f" ({total / 1e6 / per:.1f} ms per unit, {per:g} units)." if per != 1 else "."), ""]
+    hdr = "| kernel | calls | total ms | avg us | share |"
+    if per != 1:
+        hdr = "| kernel | calls | total ms | calls/unit | ms/unit | avg us | share |"
+    out += [hdr, "|" + "---|" * (hdr.count("|") - 1)]
+    for name, n, tot, avg in rows[:top]:
+        if per != 1:
+            out.append(f"| `{short(name)}` | {n} | {tot / 1e6:.2f} | {n / per:g} | {tot / 1e6 / per:.3f} | "
+                       f"{avg / 1e3:.1f} | {100 * tot / total:.1f}% |")
+        else:
+            out.append(f"| `{short(name)}` | {n} | {tot / 1e6:.2f} | {avg / 1e3:.1f} | {100 * tot / total:.1f}% |")
     return "\n".join(out) + "\n"
 
 
 if __name__ == "__main__":
-    print(summarise(sys.argv[1], sys.argv[2] if len(sys.argv) > 2 else "",
-                    sys.argv[3] if len(sys.argv) > 3 else ""))
+    ap = argparse.ArgumentParser()
+    ap.add_argument("db")
+    ap.add_argument("--title", default="")
+    ap.add_argument("--cmd", default="")
+    ap.add_argument("--per", type=float, default=1.0)
+    ap.add_argument("--match", nargs="*", default=None)
+    ap.add_argument("--top", type=int, default=30)
+    a = ap.parse_args()
+    print(summarise(a.db, a.title, a.cmd, a.per, a.match, a.top))
