@@ -48,7 +48,7 @@ int fail(int code, const std::string& msg) {
   } while (0)
 
 constexpr int NCLS = 8;
-constexpr int kMaxSplit = 4;   // key-range splits of the per-chunk attention launches
+constexpr int kMaxSplit = 8;   // key-range splits of the per-chunk attention launches
 
 struct Timing {
   bool on = false;
