@@ -128,6 +128,8 @@ def main():
     ap.add_argument("--decode-tokens", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=1024)
+    ap.add_argument("--prefill-block", type=int, default=0,
+                    help="tokens per batched pass over the frozen blocks (0: the library default)")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="MiB of a plain device copy run first, as the reference for "
                          "FETCH_SIZE/WRITE_SIZE counter scaling")
@@ -150,7 +152,7 @@ def main():
     weights = synth.gen_weights(cfg, device=dev)
     tokens_np = synth.gen_tokens(cfg, T=T)
     tokens = torch.from_numpy(tokens_np).to(dev)
-    model = T_.Model(cfg, weights, max_chunk=cfg["chunk"])
+    model = T_.Model(cfg, weights, max_chunk=cfg["chunk"], prefill_block=args.prefill_block)
     torch.cuda.synchronize()
     print(f"# setup {time.perf_counter() - t_setup:.1f}s, workspace "
           f"{model.workspace.numel() / 1e9:.2f} GB", file=sys.stderr, flush=True)
