@@ -148,6 +148,8 @@ struct ttt_model {
   int64_t Cp = 0;                       // their row stride
   hipStream_t sc = nullptr;             // fast-weight updates (SGD products)
   std::vector<hipEvent_t> evT1, evT2;   // per fast block: update operands ready
+  std::vector<hipEvent_t> evR1, evR2;   // per fast block: dh_lo / dz read by the update stream
+  std::vector<hipEvent_t> evKT;         // per fast block: transposed K ring copy done
   hipEvent_t evC = nullptr;             // all updates of the chunk done
   hipStream_t sk = nullptr;             // dK/dV of the attention backward, beside dQ
   hipEvent_t evK0 = nullptr, evK1 = nullptr;
@@ -469,7 +471,12 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
       rope_qkv(m->qkvB, n, m->H, m->hd, p0, m->theta, b.q, ly.kring, ly.vring, ly.cap, bf, s);
       ring_transpose(static_cast<char*>(m->qkvB) + (size_t)2 * d * m->es, 3 * d, 0, n, m->H, m->hd, p0,
                      ly.vtring, ly.cap, bf, s);
-      ring_transpose(ly.kring, d, ly.cap, n, m->H, m->hd, p0, ly.ktring, ly.cap, bf, s);
+      // the transposed K copy is only read by this block's dQ, much later in
+      // the chunk: make it on the dK/dV stream, off the chain
+      HIPCHK(hipEventRecord(m->evKT[j], s));
+      HIPCHK(hipStreamWaitEvent(m->sk, m->evKT[j], 0));
+      ring_transpose(ly.kring, d, ly.cap, n, m->H, m->hd, p0, ly.ktring, ly.cap, bf, m->sk);
+      HIPCHK(hipEventRecord(m->evKT[j], m->sk));
       AttnParams ap;
       ap.q = b.q; ap.ldq = d; ap.kring = ly.kring; ap.vring = ly.vring; ap.vtring = ly.vtring; ap.cap = ly.cap;
       ap.n = n; ap.H = m->H; ap.hd = m->hd; ap.window = m->W; ap.pos0 = p0; ap.o = b.o; ap.ldo = d;
@@ -545,15 +552,18 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
     // The update runs on the update stream: its operands are transposed here
     // (after ga has read the old weights), then the chain goes on at once.
     ttt_model::TOps& to = m->tops[j];
-    transpose(m->dh_lo, n, d, d, to.dhT, m->Cp, np, bf, s);
-    transpose(b.act, n, F, F, to.actT, m->Cp, np, bf, s);
     HIPCHK(hipEventRecord(m->evT1[j], s));
     HIPCHK(hipStreamWaitEvent(m->sc, m->evT1[j], 0));
+    transpose(m->dh_lo, n, d, d, to.dhT, m->Cp, np, bf, m->sc);
+    transpose(b.act, n, F, F, to.actT, m->Cp, np, bf, m->sc);
+    HIPCHK(hipEventRecord(m->evR1[j], m->sc));      // dh_lo read: the chain may overwrite it
     GemmParams gw;
     gw.A = to.dhT; gw.lda = m->Cp; gw.B = to.actT; gw.ldb = m->Cp; gw.M = d; gw.N = F; gw.K = np;
     gw.C = fw.m_dn; gw.ldc = F; gw.C2 = bf ? fw.s_dn : nullptr; gw.ldc2 = F; gw.alpha = lr;
     gw.C3 = fw.ct_dn; gw.ldc3 = d; gw.W0 = ly.wdn;
     rc = run_gemm(m, gw, true, true, EPI_SGD, true, m->sc); if (rc) return rc;
+    // dz is rewritten here: the update stream must have read the block above's
+    if (j + 1 < q) HIPCHK(hipStreamWaitEvent(s, m->evR2[j + 1], 0));
     act_bwd(m->dact, b.z, n, F, m->c.mlp == TTT_MLP_SWIGLU, m->dz, bf, s);
     if (j > 0) {
       GemmParams gb;   // db = dz . Wup (before its update: Wup^T [d][F2])
@@ -562,16 +572,18 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
       rc = run_gemm(m, gb, true, true, EPI_STORE, true, s); if (rc) return rc;
     }
     // Wup -= lr * dz^T b  (update stream, after gb has read the old weights)
-    transpose(m->dz, n, F2, F2, to.dzT, m->Cp, np, bf, s);
-    transpose(b.b, n, d, d, to.bT, m->Cp, np, bf, s);
     HIPCHK(hipEventRecord(m->evT2[j], s));
     HIPCHK(hipStreamWaitEvent(m->sc, m->evT2[j], 0));
+    transpose(m->dz, n, F2, F2, to.dzT, m->Cp, np, bf, m->sc);
+    transpose(b.b, n, d, d, to.bT, m->Cp, np, bf, m->sc);
+    HIPCHK(hipEventRecord(m->evR2[j], m->sc));      // dz read
     GemmParams gw2;
     gw2.A = to.dzT; gw2.lda = m->Cp; gw2.B = to.bT; gw2.ldb = m->Cp; gw2.M = F2; gw2.N = d; gw2.K = np;
     gw2.C = fw.m_up; gw2.ldc = d; gw2.C2 = bf ? fw.s_up : nullptr; gw2.ldc2 = d; gw2.alpha = lr;
     gw2.C3 = fw.ct_up; gw2.ldc3 = F2; gw2.W0 = ly.wup;
     rc = run_gemm(m, gw2, true, true, EPI_SGD, true, m->sc); if (rc) return rc;
     if (j == 0) break;   // no gradient below the first fast MLP
+    HIPCHK(hipStreamWaitEvent(s, m->evR1[j], 0));   // dh_lo is rewritten below
     layernorm_bwd_acc(m->dtmp, x2, b.mean2, b.rstd2, n, d, m->dh, m->dh_lo, bf, s);
     GemmParams gdo;   // dO = dh . Wo  (Wo^T [d][d])
     gdo.A = m->dh_lo; gdo.lda = d; gdo.B = ly.woT; gdo.ldb = d; gdo.M = n; gdo.N = d; gdo.K = d;
@@ -590,6 +602,7 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
       double in = 0;
       const double tot = pairs(p0, n, m->W, p0, &in);
       Scope t(m, CLS_ATTN_BWD, s, 4.0 * d * (tot + in));
+      HIPCHK(hipStreamWaitEvent(s, m->evKT[j], 0));  // transposed K copy for dQ
       HIPCHK(hipEventRecord(m->evK0, s));            // inputs of dK/dV ready
       HIPCHK(hipStreamWaitEvent(m->sk, m->evK0, 0));
       swa_bwd(ap, bf, s, m->sk);
@@ -719,9 +732,15 @@ int ttt_model_load(const ttt_config* cfg, const void* const* weights, int32_t n_
     if (e1 == hipSuccess) e1 = hipStreamCreateWithFlags(&m->sk, hipStreamNonBlocking);
     m->evT1.assign(m->q, nullptr);
     m->evT2.assign(m->q, nullptr);
+    m->evR1.assign(m->q, nullptr);
+    m->evR2.assign(m->q, nullptr);
+    m->evKT.assign(m->q, nullptr);
     std::vector<hipEvent_t*> evs = {&m->ev0, &m->evA[0], &m->evA[1], &m->evB[0], &m->evB[1], &m->evC,
                                     &m->evK0, &m->evK1};
-    for (int j = 0; j < m->q; ++j) { evs.push_back(&m->evT1[j]); evs.push_back(&m->evT2[j]); }
+    for (int j = 0; j < m->q; ++j) {
+      evs.push_back(&m->evT1[j]); evs.push_back(&m->evT2[j]);
+      evs.push_back(&m->evR1[j]); evs.push_back(&m->evR2[j]); evs.push_back(&m->evKT[j]);
+    }
     for (auto* e : evs)
       if (e1 == hipSuccess) e1 = hipEventCreateWithFlags(e, hipEventDisableTiming);
     if (e1 != hipSuccess) {
@@ -921,8 +940,7 @@ void ttt_model_free(ttt_model* m) {
   if (m->sk) (void)hipStreamSynchronize(m->sk);
   std::vector<hipEvent_t> evs = {m->ev0, m->evA[0], m->evA[1], m->evB[0], m->evB[1], m->evC,
                                  m->evK0, m->evK1};
-  evs.insert(evs.end(), m->evT1.begin(), m->evT1.end());
-  evs.insert(evs.end(), m->evT2.begin(), m->evT2.end());
+  for (auto* v : {&m->evT1, &m->evT2, &m->evR1, &m->evR2, &m->evKT}) evs.insert(evs.end(), v->begin(), v->end());
   for (auto e : evs)
     if (e) (void)hipEventDestroy(e);
   if (m->sa) (void)hipStreamDestroy(m->sa);
