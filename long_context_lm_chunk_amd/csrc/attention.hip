@@ -294,14 +294,25 @@ __global__ void swa_combine_k(AttnParams p, int nsplit) {
   if (p.lse && c % p.hd == 0) p.lse[(int64_t)h * p.n + row] = (M + log2f(L)) * LN2;
 }
 
-// Transposed ring copy: rows h*hd + i, column (position mod cap); one block
-// per 64 positions of one head, transposed through LDS so both sides
-// coalesce.  The source row of position t is src + t*ld (linear) or, for a
-// ring source (src_cap > 0), src + ((pos0 + t) mod src_cap) * ld.
+// Column of ring slot s in a key-permuted transposed copy: inside every
+// aligned group of 16 slots the middle two quads are swapped (offsets 4..7
+// and 8..11), so the 8 keys {4h..4h+3, 8+4h..8+4h+3} of a group, which one
+// lane holds in a 32x32 accumulator of the transposed scores, sit in one
+// 16-byte run (offsets 8h..8h+7).
+DEVI int64_t kperm(int64_t s) {
+  const int o = (int)(s & 15);
+  return (s & ~(int64_t)15) | (o < 4 || o >= 12 ? o : (o < 8 ? o + 4 : o - 4));
+}
+
+// Transposed ring copy: rows h*hd + i, column (position mod cap), or its
+// key-permuted column (perm != 0, see kperm); one block per 64 positions of
+// one head, transposed through LDS so both sides coalesce.  The source row
+// of position t is src + t*ld (linear) or, for a ring source (src_cap > 0),
+// src + ((pos0 + t) mod src_cap) * ld.
 template <typename T>
 __global__ __launch_bounds__(256) void ring_tr_k(const T* __restrict__ src, int64_t ld, int64_t src_cap,
                                                  int n, int H, int hd, int64_t pos0, T* __restrict__ dst,
-                                                 int64_t cap) {
+                                                 int64_t cap, int perm) {
   __shared__ T tile[64][128 + 2];
   const int h = blockIdx.y, t0 = blockIdx.x * 64, tid = threadIdx.x;
   for (int idx = tid; idx < 64 * hd; idx += 256) {
@@ -316,7 +327,10 @@ __global__ __launch_bounds__(256) void ring_tr_k(const T* __restrict__ src, int6
   __syncthreads();
   for (int idx = tid; idx < hd * 64; idx += 256) {
     const int i = idx / 64, t = idx % 64;
-    if (t0 + t < n) dst[(int64_t)(h * hd + i) * cap + (pos0 + t0 + t) % cap] = tile[t][i];
+    if (t0 + t < n) {
+      const int64_t sl = (pos0 + t0 + t) % cap;
+      dst[(int64_t)(h * hd + i) * cap + (perm ? kperm(sl) : sl)] = tile[t][i];
+    }
   }
 }
 
@@ -406,12 +420,12 @@ __global__ __launch_bounds__(256, 2) void swa_bwd_dq32_k(AttnParams p) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) dv8[j] = s[kb][8 * hf + j];
         const typename Frag<T>::type df = pack8<T>(dv8);
-        const int koff = kb * 32 + 16 * hf + 4 * hl;
+        // the 8 keys of this lane's k-slots, one 16-byte run of the
+        // key-permuted transposed K copy
+        const int koff = kb * 32 + 16 * hf + 8 * hl;
 #pragma unroll
-        for (int b = 0; b < C::HB; ++b) {
-          const T* row = Kt + (b * 32 + ql) * C::LSV + koff;
-          mma32x32x16(lds_frag4x2<T>(row, row + 8), df, dacc[b]);
-        }
+        for (int b = 0; b < C::HB; ++b)
+          mma32x32x16(lds_frag8<T>(Kt + (b * 32 + ql) * C::LSV + koff), df, dacc[b]);
       }
   }
   if (qok) {
@@ -626,11 +640,12 @@ void swa_fwd(const AttnParams& p, bool bf, hipStream_t s) {
   if (bf) fwd_t<bf16>(p, s); else fwd_t<float>(p, s);
 }
 void ring_transpose(const void* src, int64_t ld, int64_t src_cap, int n, int H, int hd, int64_t pos0,
-                    void* dst, int64_t cap, bool bf, hipStream_t s) {
+                    void* dst, int64_t cap, bool key_perm, bool bf, hipStream_t s) {
   if (n <= 0) return;
   dim3 grid((n + 63) / 64, H);
-  if (bf) hipLaunchKernelGGL(ring_tr_k<bf16>, grid, dim3(256), 0, s, (const bf16*)src, ld, src_cap, n, H, hd, pos0, (bf16*)dst, cap);
-  else hipLaunchKernelGGL(ring_tr_k<float>, grid, dim3(256), 0, s, (const float*)src, ld, src_cap, n, H, hd, pos0, (float*)dst, cap);
+  const int pm = key_perm ? 1 : 0;
+  if (bf) hipLaunchKernelGGL(ring_tr_k<bf16>, grid, dim3(256), 0, s, (const bf16*)src, ld, src_cap, n, H, hd, pos0, (bf16*)dst, cap, pm);
+  else hipLaunchKernelGGL(ring_tr_k<float>, grid, dim3(256), 0, s, (const float*)src, ld, src_cap, n, H, hd, pos0, (float*)dst, cap, pm);
 }
 
 void swa_bwd(const AttnParams& p, bool bf, hipStream_t s, hipStream_t s_kv) {

@@ -91,9 +91,11 @@ struct AttnParams {
 };
 void swa_fwd(const AttnParams& p, bool bf16, hipStream_t s);
 // rows of positions [pos0, pos0+n) (src row t at src + t*ld, or at slot
-// (pos0+t) mod src_cap of a ring) into a transposed ring [H*hd][cap]
+// (pos0+t) mod src_cap of a ring) into a transposed ring [H*hd][cap]; with
+// key_perm the columns are permuted inside aligned groups of 16 slots (the
+// dQ product's operand order; cap % 16 == 0)
 void ring_transpose(const void* src, int64_t ld, int64_t src_cap, int n, int H, int hd, int64_t pos0,
-                    void* dst, int64_t cap, bool bf16, hipStream_t s);
+                    void* dst, int64_t cap, bool key_perm, bool bf16, hipStream_t s);
 // dQ on s, dK/dV on s_kv (the two are independent; the caller orders s_kv
 // after the inputs and joins it before using dK/dV; s_kv may equal s)
 void swa_bwd(const AttnParams& p, bool bf16, hipStream_t s, hipStream_t s_kv);
