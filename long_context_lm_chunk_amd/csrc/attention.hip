@@ -15,6 +15,7 @@
 // rescaling stays inside the lane.
 #include "common.hpp"
 #include "kernels.hpp"
+#include <type_traits>
 
 namespace ttt {
 namespace {
@@ -463,6 +464,181 @@ __global__ void dq_combine_k(AttnParams p, int nsplit) {
   static_cast<T*>(p.dq)[(int64_t)row * p.ldg + c] = from_f32<T>(acc);
 }
 
+// ------------------------------------------------ backward dQ, bf16, hd 128
+// The same product as swa_bwd_dq32_k for the bf16 / head_dim 128 case,
+// organised for throughput: a workgroup of 8 waves holds 256 queries (32 per
+// wave, two waves per SIMD so one's exponentials overlap the other's matrix
+// steps), and the 64-key tiles of K, V (natural, [key][hd]) and of the
+// key-permuted K^T copy ([hd][key]) are brought in by direct global->LDS
+// 16-byte loads into two stages, the next tile's loads in flight while the
+// current one is multiplied; each tile is loaded once for 256 queries.  LDS
+// rows are XOR-swizzled at 16-byte granularity (K/V rows of 256 B: slot
+// c ^ (row & 15); K^T rows of 128 B: slot c ^ ((row >> 1) & 7)) so the
+// fragment reads are conflict-free.
+namespace dq2 {
+constexpr int HD = 128, KT = 64, NW = 8, QT = 32 * NW, NTHR = 64 * NW;
+constexpr int ROWK = HD * 2;                 // bytes of a K/V row (one key)
+constexpr int TILE_K = KT * ROWK;            // 16 KB
+constexpr int ROWT = KT * 2;                 // bytes of a K^T row (one head dim)
+constexpr int TILE_T = HD * ROWT;            // 16 KB
+constexpr int STAGE = 2 * TILE_K + TILE_T;   // 48 KB
+constexpr int LDS_BYTES = 2 * STAGE;         // 96 KB: one workgroup per CU
+constexpr int PER = 16 / NW;                 // 1 KB load instructions per wave and array
+typedef __attribute__((address_space(3))) void lds_void;
+DEVI __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
+  const int nb = bytes > 0x7fffffff ? 0x7fffffff : (int)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nb, 0x00020000);
+}
+}  // namespace dq2
+
+__global__ __launch_bounds__(dq2::NTHR, 1) void swa_bwd_dq_bf16_128_k(AttnParams p) {
+  using namespace dq2;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hl = lane >> 5, ql = lane & 31;
+  int bx, h, bz;
+  attn_block(bx, h, bz);
+  const int qs = bx * QT;
+  const int d = p.H * HD;
+  const bf16* Q = static_cast<const bf16*>(p.q);
+  const bf16* G = static_cast<const bf16*>(p.dout);
+
+  // this lane's query and its operand fragments
+  const int qrow = qs + wave * 32 + ql;
+  const bool qok = qrow < p.n;
+  bf16x8 qf[8], gf[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    qf[ks] = g_frag8<bf16>(Q + (int64_t)qrow * p.ldq + h * HD + ks * 16 + 8 * hl, qok);
+    gf[ks] = g_frag8<bf16>(G + (int64_t)qrow * p.lddo + h * HD + ks * 16 + 8 * hl, qok);
+  }
+  // a row past the end gets P = exp2(. - inf) = 0
+  const float lse2 = qok ? p.lse[(int64_t)h * p.n + qrow] * LOG2E : INFINITY;
+  const float Dq = qok ? p.D[(int64_t)h * p.n + qrow] : 0.f;
+  const uint32_t wlen = (uint32_t)p.window;
+  const float sc = LOG2E / sqrtf((float)HD);
+  f32x16 dacc[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dacc[b][r] = 0.f;
+
+  // key tiles of the window of this workgroup's queries, split z's run
+  const int64_t first = p.pos0 + qs;
+  const int64_t last = p.pos0 + min(qs + QT, p.n) - 1;
+  int64_t lo = first - p.window + 1;
+  if (lo < 0) lo = 0;
+  const int64_t ktA = (lo / KT) * KT;
+  const int nall = (int)((last - ktA) / KT) + 1;
+  const int per = (nall + (int)gridDim.z - 1) / (int)gridDim.z;
+  const int tb = min(nall, bz * per), te = min(nall, tb + per);
+
+  const __amdgpu_buffer_rsrc_t rk = rsrc(p.kring, p.cap * d * 2);
+  const __amdgpu_buffer_rsrc_t rv = rsrc(p.vring, p.cap * d * 2);
+  const __amdgpu_buffer_rsrc_t rt = rsrc(p.ktring, (int64_t)d * p.cap * 2);
+  auto issue = [&](int it, int stage) {
+    const int64_t kt = ktA + (int64_t)it * KT;
+    const int64_t slot0 = kt % p.cap;            // tiles never wrap (cap % 64 == 0)
+    char* st = smem + stage * STAGE;
+    // K and V: 16 instructions of 4 rows (1 KB) each per tile
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int q = wave * PER + i;
+      const int row = q * 4 + (lane >> 4), pc = lane & 15;
+      const int c = pc ^ (row & 15);
+      const uint32_t off = (uint32_t)(((slot0 + row) * d + h * HD + 8 * c) * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(st + q * 1024), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(st + TILE_K + q * 1024), 16, off, 0, 0, 0);
+    }
+    // K^T: 16 instructions of 8 rows (head dims) each
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int q = wave * PER + i;
+      const int row = q * 8 + (lane >> 3), pc = lane & 7;
+      const int c = pc ^ ((row >> 1) & 7);
+      const uint32_t off = (uint32_t)((((int64_t)(h * HD + row)) * p.cap + slot0 + 8 * c) * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, (lds_void*)(st + 2 * TILE_K + q * 1024), 16, off, 0, 0, 0);
+    }
+  };
+
+  if (tb < te) issue(tb, 0);
+  for (int it = tb; it < te; ++it) {
+    const int stage = (it - tb) & 1;
+    __builtin_amdgcn_s_waitcnt(0x0F70);    // vmcnt(0): this wave's loads of tile it
+    __syncthreads();                       // every wave's; the other stage is free
+    if (it + 1 < te) issue(it + 1, stage ^ 1);
+    const char* Ks = smem + stage * STAGE;
+    const char* Vs = Ks + TILE_K;
+    const char* Ts = Ks + 2 * TILE_K;
+    const int64_t kt = ktA + (int64_t)it * KT;
+    const bool interior = (kt + KT - 1 <= first) && (kt > last - p.window);
+    // key - query of element r = 0 of this lane (key half 0)
+    const int kq0 = (int)(kt - first) - (wave * 32 + ql) + 4 * hl;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 s, dp;
+      const f32x16 zero = {};
+      const int krow = kb * 32 + ql;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const int slot = ((2 * ks + hl) ^ (krow & 15)) * 16;
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + krow * ROWK + slot);
+        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(Vs + krow * ROWK + slot);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], ks ? s : zero, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, gf[ks], ks ? dp : zero, 0, 0, 0);
+      }
+      // outside the band S = -inf (wave-uniform test: most tiles are inside)
+      if (!interior) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rel = kq0 + 32 * kb + 8 * (r >> 2) + (r & 3);
+          s[r] = (uint32_t)(-rel) < wlen ? s[r] : -INFINITY;
+        }
+      }
+      // dS^T = P (dP - D), P = exp(S - LSE)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = fast_exp2(fmaf(s[r], sc, -lse2)) * (dp[r] - Dq);
+      // dQ^T += K^T dS^T: the lane's 8 k-slots of half hf are one 16-byte run
+      // of the key-permuted K^T row
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        float v8[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v8[j] = s[8 * hf + j];
+        const bf16x8 df = pack8<bf16>(v8);
+        const int c = 4 * kb + 2 * hf + hl;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int trow = b * 32 + ql;
+          const bf16x8 tf = *reinterpret_cast<const bf16x8*>(Ts + trow * ROWT + ((c ^ ((trow >> 1) & 7)) * 16));
+          mma32x32x16(tf, df, dacc[b]);
+        }
+      }
+    }
+  }
+
+  if (!qok) return;
+  const float scale = 1.f / sqrtf((float)HD);
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int c = b * 32 + 8 * g + 4 * hl;      // 4 consecutive head dims
+      float4 v;
+      v.x = dacc[b][4 * g] * scale; v.y = dacc[b][4 * g + 1] * scale;
+      v.z = dacc[b][4 * g + 2] * scale; v.w = dacc[b][4 * g + 3] * scale;
+      if (gridDim.z == 1) {
+        bf16x4 o;
+        o[0] = static_cast<bf16>(v.x); o[1] = static_cast<bf16>(v.y);
+        o[2] = static_cast<bf16>(v.z); o[3] = static_cast<bf16>(v.w);
+        *reinterpret_cast<bf16x4*>(static_cast<bf16*>(p.dq) + (int64_t)qrow * p.ldg + h * HD + c) = o;
+      } else {
+        *reinterpret_cast<float4*>(p.part + ((int64_t)bz * p.n + qrow) * d + h * HD + c) = v;
+      }
+    }
+}
+
 // --------------------------------------------------------- backward dK, dV
 // Keys are the in-chunk positions; cached keys of earlier chunks are
 // constants and receive no gradient.  Each wave owns 32 keys (lane = key);
@@ -597,6 +773,25 @@ inline int pick_split(const AttnParams& p, int wgs, int zmax) {
   return best;
 }
 
+// Key-range split of the staged dQ kernel (one resident workgroup per CU,
+// 256 slots).  A run of t key tiles costs about t + 4 tile-times (fragment
+// loads and pipeline fill), rounds of resident workgroups add up, and each
+// split beyond the first adds a combine pass over the fp32 partials of about
+// 3 tile-times (measured on 1024-query chunks, 24 heads, window 8192).
+inline int pick_split_dq2(const AttnParams& p) {
+  if (!p.part || !p.part_ml) return 1;
+  const int wgs = ((p.n + dq2::QT - 1) / dq2::QT) * p.H;
+  const int64_t lo = p.pos0 - p.window + 1 > 0 ? p.pos0 - p.window + 1 : 0;
+  const double tiles = (double)((p.pos0 + p.n - 1 - lo) / dq2::KT + 1);
+  int best = 1;
+  double cost = 1e30;
+  for (int z = 1; z <= p.max_split && z <= 8; ++z) {
+    const double c = (double)((wgs * z + 255) / 256) * (tiles / z + 4.0) + (z > 1 ? 3.0 * z : 0.0);
+    if (c < cost - 1e-9) { cost = c; best = z; }
+  }
+  return best;
+}
+
 template <typename T>
 void fwd_t(const AttnParams& p, hipStream_t s) {
   const int nz = pick_split(p, ((p.n + 127) / 128) * p.H, 4);
@@ -616,12 +811,29 @@ void fwd_t(const AttnParams& p, hipStream_t s) {
 }
 template <typename T>
 void bwd_t(const AttnParams& p, hipStream_t s, hipStream_t s2) {
-  const int nz = pick_split(p, ((p.n + 127) / 128) * p.H, 8);
+  // bf16 / head_dim 128 / 64-aligned ring: the staged 256-query dQ kernel
+  // (one workgroup per CU: 256 resident workgroups); otherwise the general one
+  const bool wide = std::is_same<T, bf16>::value && p.hd == 128 && p.cap % 64 == 0 &&
+                    (int64_t)p.cap * p.H * p.hd * 2 <= 0x7fffffff;
+  int nz;
+  if (wide) {
+    nz = pick_split_dq2(p);
+    static bool attr = false;
+    if (!attr) {
+      (void)hipFuncSetAttribute((const void*)swa_bwd_dq_bf16_128_k, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                dq2::LDS_BYTES);
+      attr = true;
+    }
+    hipLaunchKernelGGL(swa_bwd_dq_bf16_128_k, dim3((p.n + dq2::QT - 1) / dq2::QT, p.H, nz), dim3(dq2::NTHR),
+                       dq2::LDS_BYTES, s, p);
+  } else {
+    nz = pick_split(p, ((p.n + 127) / 128) * p.H, 8);
+  }
   dim3 gq((p.n + 127) / 128, p.H, nz);
   dim3 gk((p.n + 127) / 128, p.H);
   switch (p.hd) {
 #define CASE(HDV) case HDV: \
-    hipLaunchKernelGGL((swa_bwd_dq32_k<T, HDV>), gq, dim3(256), 0, s, p); \
+    if (!wide) hipLaunchKernelGGL((swa_bwd_dq32_k<T, HDV>), gq, dim3(256), 0, s, p); \
     hipLaunchKernelGGL((swa_bwd_dkdv32_k<T, HDV>), gk, dim3(256), 0, s2, p); break;
     CASE(16) CASE(32) CASE(64) CASE(96) CASE(128)
 #undef CASE
