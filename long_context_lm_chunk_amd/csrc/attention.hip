@@ -15,6 +15,7 @@
 // rescaling stays inside the lane.
 #include "common.hpp"
 #include "kernels.hpp"
+#include <algorithm>
 #include <type_traits>
 
 namespace ttt {
@@ -42,60 +43,6 @@ constexpr int TQ = 64;     // positions per tile
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
-template <typename T, int HD> struct AttnCfg {
-  static constexpr int KS = (HD + 31) / 32;          // 32-wide k steps over head_dim
-  static constexpr int HDP = KS * 32;                // head_dim padded with zeros
-  static constexpr int HB = HD / 16;                 // 16-row blocks of head_dim
-  static constexpr int PAD = 16 / sizeof(T);
-  static constexpr int LSN = HDP + PAD;              // natural tile row stride [pos][hd]
-  static constexpr int LST = TQ + PAD;               // transposed tile row stride [hd][pos]
-};
-
-// Load a 64-position tile of one head from a ring ([cap][ld]) in natural
-// layout (positions >= nvalid zero-filled, hd >= HD zero-filled).
-template <typename T, int HD>
-DEVI void load_nat(T* lds, const T* base, int64_t ld, int nvalid, int tid) {
-  using C = AttnCfg<T, HD>;
-  tile_copy_rows<T, TQ, C::HDP, C::LSN, 256>(lds, base, ld, nvalid, HD, tid);
-}
-template <typename T, int HD>
-DEVI void load_tr(T* lds, const T* base, int64_t ld, int nvalid, int tid) {
-  using C = AttnCfg<T, HD>;
-  tile_copy_transpose<T, TQ, HD, C::LST, 256>(lds, base, ld, nvalid, HD, tid);
-}
-
-// operand fragment (8 k-slots over head_dim) of row r from a natural tile
-template <typename T, int HD>
-DEVI typename Frag<T>::type nat_frag(const T* lds, int r, int ks, int lane) {
-  using C = AttnCfg<T, HD>;
-  return lds_frag8<T>(lds + r * C::LSN + ks * 32 + 8 * (lane >> 4));
-}
-// operand fragment of head-dim row r from a transposed tile, k-slots = 32
-// positions of pair pp laid out as two accumulator blocks (see header).
-template <typename T, int HD>
-DEVI typename Frag<T>::type tr_frag(const T* lds, int r, int pp, int lane) {
-  using C = AttnCfg<T, HD>;
-  const T* row = lds + r * C::LST + 4 * (lane >> 4);
-  return lds_frag4x2<T>(row + (2 * pp) * 16, row + (2 * pp + 1) * 16);
-}
-// operand fragment built from two accumulator blocks (values per lane: 4 + 4)
-template <typename T>
-DEVI typename Frag<T>::type acc_frag(const f32x4& a, const f32x4& b) {
-  float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-  return pack8<T>(v);
-}
-
-// register fragments of 16 rows (one per lane, row = l%16) of a [n][ld] matrix
-template <typename T, int HD>
-DEVI void row_frags(typename Frag<T>::type* f, const T* base, int64_t ld,
-                    bool row_ok, int lane) {
-#pragma unroll
-  for (int ks = 0; ks < AttnCfg<T, HD>::KS; ++ks) {
-    const int c = ks * 32 + 8 * (lane >> 4);
-    f[ks] = g_frag8<T>(base + c, row_ok && c < HD);
-  }
-}
-
 // ------------------------------------------- forward, 32x32 matrix cores
 // Each wave owns 32 queries.  Scores are formed transposed, Sᵀ[32 keys x 32
 // queries] = K·Qᵀ with the 32x32x16 step, so a lane holds 16 keys of one
@@ -103,7 +50,8 @@ DEVI void row_frags(typename Frag<T>::type* f, const T* base, int64_t ld,
 // consecutive accumulator values of a lane are exactly the k-slots of the
 // next P·V step (keys 16h..16h+15 of a 32-key block), so probabilities go
 // from accumulator to operand without leaving registers.  V is read from
-// its transposed ring copy ([H*hd][cap]), so both tiles are plain copies.
+// its key-permuted transposed ring copy ([H*hd][cap], see kperm), so both
+// tiles are plain copies and each P.V operand fragment is one 16-byte read.
 template <typename T, int HD> struct Attn32 {
   static constexpr int KS = HD / 16;              // 16-wide k steps of Qᵀ
   static constexpr int HB = (HD + 31) / 32;       // 32-row blocks of Oᵀ
@@ -201,7 +149,9 @@ __global__ __launch_bounds__(256, 2) void swa_fwd32_k(AttnParams p) {
 #pragma unroll
       for (int r = 0; r < 16; r += 2) tmax = fmaxf(tmax, fmaxf(s[kb][r], s[kb][r + 1]));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * sc;
-    // lazy rescaling (see the 16x16 kernel above): exact, rarely taken
+    // lazy rescaling: the reference max m is raised only when a tile's max
+    // exceeds it by more than 2^8, so exponents stay below 2^8; exact, since
+    // l and O share the reference, and rarely taken
     const bool bump = tmax > m + 8.f;
     if (__any(bump)) {
       const float mn = bump ? tmax : m;
@@ -230,12 +180,11 @@ __global__ __launch_bounds__(256, 2) void swa_fwd32_k(AttnParams p) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) pv[j] = s[kb][8 * hf + j];
         const typename Frag<T>::type pf = pack8<T>(pv);
-        const int koff = kb * 32 + 16 * hf + 4 * hl;
+        // the 8 keys of this lane's k-slots: one run of the key-permuted V^T row
+        const int koff = kb * 32 + 16 * hf + 8 * hl;
 #pragma unroll
-        for (int b = 0; b < C::HB; ++b) {
-          const T* row = Vt[cur] + (b * 32 + ql) * C::LSV + koff;
-          mma32x32x16(lds_frag4x2<T>(row, row + 8), pf, oacc[b]);
-        }
+        for (int b = 0; b < C::HB; ++b)
+          mma32x32x16(lds_frag8<T>(Vt[cur] + (b * 32 + ql) * C::LSV + koff), pf, oacc[b]);
       }
     if (it + 1 < ntile) {
       lk.store(Ks[cur ^ 1], tid);
@@ -475,24 +424,26 @@ __global__ void dq_combine_k(AttnParams p, int nsplit) {
 // rows are XOR-swizzled at 16-byte granularity (K/V rows of 256 B: slot
 // c ^ (row & 15); K^T rows of 128 B: slot c ^ ((row >> 1) & 7)) so the
 // fragment reads are conflict-free.
-namespace dq2 {
+namespace stg {
 constexpr int HD = 128, KT = 64, NW = 8, QT = 32 * NW, NTHR = 64 * NW;
 constexpr int ROWK = HD * 2;                 // bytes of a K/V row (one key)
 constexpr int TILE_K = KT * ROWK;            // 16 KB
 constexpr int ROWT = KT * 2;                 // bytes of a K^T row (one head dim)
 constexpr int TILE_T = HD * ROWT;            // 16 KB
-constexpr int STAGE = 2 * TILE_K + TILE_T;   // 48 KB
+constexpr int STAGE = 2 * TILE_K + TILE_T;   // dQ: K, V, K^T (48 KB)
 constexpr int LDS_BYTES = 2 * STAGE;         // 96 KB: one workgroup per CU
+constexpr int STAGE_F = TILE_K + TILE_T;     // forward: K, V^T (32 KB)
+constexpr int LDS_F = 2 * STAGE_F;           // 64 KB
 constexpr int PER = 16 / NW;                 // 1 KB load instructions per wave and array
 typedef __attribute__((address_space(3))) void lds_void;
 DEVI __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
   const int nb = bytes > 0x7fffffff ? 0x7fffffff : (int)bytes;
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nb, 0x00020000);
 }
-}  // namespace dq2
+}  // namespace stg
 
-__global__ __launch_bounds__(dq2::NTHR, 1) void swa_bwd_dq_bf16_128_k(AttnParams p) {
-  using namespace dq2;
+__global__ __launch_bounds__(stg::NTHR, 1) void swa_bwd_dq_bf16_128_k(AttnParams p) {
+  using namespace stg;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -639,6 +590,180 @@ __global__ __launch_bounds__(dq2::NTHR, 1) void swa_bwd_dq_bf16_128_k(AttnParams
     }
 }
 
+// --------------------------------------------- forward, bf16, head_dim 128
+// The forward of swa_fwd32_k for the bf16 / head_dim 128 case with the
+// staging of the dQ kernel above: 8 waves x 32 queries per workgroup, the
+// 64-key tiles of K ([key][hd], rows of 256 B) and of the key-permuted V^T
+// copy ([hd][key], rows of 128 B) by direct global->LDS loads into two
+// stages, swizzled as there.
+__global__ __launch_bounds__(stg::NTHR, 1) void swa_fwd_bf16_128_k(AttnParams p) {
+  using namespace stg;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hl = lane >> 5, ql = lane & 31;
+  int bx, h, bz;
+  attn_block(bx, h, bz);
+  const int qs = bx * QT;
+  const int d = p.H * HD;
+  const bf16* Q = static_cast<const bf16*>(p.q);
+
+  const int qrow = qs + wave * 32 + ql;
+  const bool qok = qrow < p.n;
+  bf16x8 qf[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks)
+    qf[ks] = g_frag8<bf16>(Q + (int64_t)qrow * p.ldq + h * HD + ks * 16 + 8 * hl, qok);
+  float m = -INFINITY, l = 0.f;
+  f32x16 oacc[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[b][r] = 0.f;
+  const uint32_t wlen = (uint32_t)p.window;
+  const float sc = LOG2E / sqrtf((float)HD);
+
+  const int64_t first = p.pos0 + qs;
+  const int64_t last = p.pos0 + min(qs + QT, p.n) - 1;
+  int64_t lo = first - p.window + 1;
+  if (lo < 0) lo = 0;
+  const int64_t ktA = (lo / KT) * KT;
+  const int nall = (int)((last - ktA) / KT) + 1;
+  const int per = (nall + (int)gridDim.z - 1) / (int)gridDim.z;
+  const int tb = min(nall, bz * per), te = min(nall, tb + per);
+
+  const __amdgpu_buffer_rsrc_t rk = rsrc(p.kring, p.cap * d * 2);
+  const __amdgpu_buffer_rsrc_t rt = rsrc(p.vtring, (int64_t)d * p.cap * 2);
+  auto issue = [&](int it, int stage) {
+    const int64_t slot0 = (ktA + (int64_t)it * KT) % p.cap;   // tiles never wrap
+    char* st = smem + stage * STAGE_F;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int q = wave * PER + i;
+      const int row = q * 4 + (lane >> 4), pc = lane & 15;
+      const int c = pc ^ (row & 15);
+      const uint32_t off = (uint32_t)(((slot0 + row) * d + h * HD + 8 * c) * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(st + q * 1024), 16, off, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int q = wave * PER + i;
+      const int row = q * 8 + (lane >> 3), pc = lane & 7;
+      const int c = pc ^ ((row >> 1) & 7);
+      const uint32_t off = (uint32_t)((((int64_t)(h * HD + row)) * p.cap + slot0 + 8 * c) * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, (lds_void*)(st + TILE_K + q * 1024), 16, off, 0, 0, 0);
+    }
+  };
+
+  if (tb < te) issue(tb, 0);
+  for (int it = tb; it < te; ++it) {
+    const int stage = (it - tb) & 1;
+    __builtin_amdgcn_s_waitcnt(0x0F70);    // vmcnt(0): this wave's loads of tile it
+    __syncthreads();                       // every wave's; the other stage is free
+    if (it + 1 < te) issue(it + 1, stage ^ 1);
+    const char* Ks = smem + stage * STAGE_F;
+    const char* Vt = Ks + TILE_K;
+    const int64_t kt = ktA + (int64_t)it * KT;
+    f32x16 s[2];
+    const f32x16 zero = {};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int krow = kb * 32 + ql;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + krow * ROWK + (((2 * ks + hl) ^ (krow & 15)) * 16));
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], ks ? s[kb] : zero, 0, 0, 0);
+      }
+    }
+    const bool interior = (kt + KT - 1 <= first) && (kt > last - p.window);
+    if (!interior) {
+      const int kq0 = (int)(kt - first) - (wave * 32 + ql) + 4 * hl;   // key - query of s[0][0]
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rel = kq0 + 32 * kb + 8 * (r >> 2) + (r & 3);
+          s[kb][r] = (uint32_t)(-rel) < wlen ? s[kb][r] : -INFINITY;
+        }
+    }
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) tmax = fmaxf(tmax, fmaxf(s[kb][r], s[kb][r + 1]));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * sc;
+    // lazy rescaling as in swa_fwd32_k
+    const bool bump = tmax > m + 8.f;
+    if (__any(bump)) {
+      const float mn = bump ? tmax : m;
+      const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - mn);
+      l *= alpha;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) oacc[b] *= alpha;
+      m = mn;
+    }
+    const float mref = (m == -INFINITY) ? 0.f : m;
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = fast_exp2(fmaf(s[kb][r], sc, -mref));
+        s[kb][r] = e;
+        rs += e;
+      }
+    l += rs + __shfl_xor(rs, 32, 64);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        float pv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pv[j] = s[kb][8 * hf + j];
+        const bf16x8 pf = pack8<bf16>(pv);
+        const int c = 4 * kb + 2 * hf + hl;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int trow = b * 32 + ql;
+          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(Vt + trow * ROWT + ((c ^ ((trow >> 1) & 7)) * 16));
+          mma32x32x16(vf, pf, oacc[b]);
+        }
+      }
+  }
+
+  if (!qok) return;
+  if (gridDim.z == 1) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    bf16* O = static_cast<bf16*>(p.o) + (int64_t)qrow * p.ldo + h * HD;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] = static_cast<bf16>(oacc[b][4 * g + j] * inv);
+        *reinterpret_cast<bf16x4*>(O + b * 32 + 8 * g + 4 * hl) = o;
+      }
+    if (p.lse && hl == 0) p.lse[(int64_t)h * p.n + qrow] = (m + log2f(l)) * LN2;
+  } else {
+    // unnormalised partial of this key range, combined by swa_combine_k
+    float* O = p.part + ((int64_t)bz * p.n + qrow) * d + h * HD;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float4 v;
+        v.x = oacc[b][4 * g]; v.y = oacc[b][4 * g + 1]; v.z = oacc[b][4 * g + 2]; v.w = oacc[b][4 * g + 3];
+        *reinterpret_cast<float4*>(O + b * 32 + 8 * g + 4 * hl) = v;
+      }
+    if (hl == 0) {
+      float* ml = p.part_ml + ((int64_t)bz * p.H + h) * p.n * 2;
+      ml[2 * qrow] = m;
+      ml[2 * qrow + 1] = l;
+    }
+  }
+}
+
 // --------------------------------------------------------- backward dK, dV
 // Keys are the in-chunk positions; cached keys of earlier chunks are
 // constants and receive no gradient.  Each wave owns 32 keys (lane = key);
@@ -773,27 +898,53 @@ inline int pick_split(const AttnParams& p, int wgs, int zmax) {
   return best;
 }
 
-// Key-range split of the staged dQ kernel (one resident workgroup per CU,
-// 256 slots).  A run of t key tiles costs about t + 4 tile-times (fragment
-// loads and pipeline fill), rounds of resident workgroups add up, and each
-// split beyond the first adds a combine pass over the fp32 partials of about
-// 3 tile-times (measured on 1024-query chunks, 24 heads, window 8192).
-inline int pick_split_dq2(const AttnParams& p) {
+// Key-range split of the staged kernels (one resident workgroup per CU, 256
+// slots).  A run of t key tiles costs about t + 4 tile-times (fragment loads
+// and pipeline fill), rounds of resident workgroups add up, and each split
+// beyond the first adds a combine pass over the fp32 partials of about 4
+// tile-times (measured on 1024-query chunks, 24 heads, window 8192).  The
+// run length is that of the last workgroup, which spans the most keys.
+inline int pick_split_staged(const AttnParams& p) {
   if (!p.part || !p.part_ml) return 1;
-  const int wgs = ((p.n + dq2::QT - 1) / dq2::QT) * p.H;
-  const int64_t lo = p.pos0 - p.window + 1 > 0 ? p.pos0 - p.window + 1 : 0;
-  const double tiles = (double)((p.pos0 + p.n - 1 - lo) / dq2::KT + 1);
+  const int wgs = ((p.n + stg::QT - 1) / stg::QT) * p.H;
+  const int64_t qlast = p.pos0 + p.n - 1;
+  const int64_t qfirst = std::max<int64_t>(p.pos0, qlast - stg::QT + 1);
+  const int64_t klo = std::max<int64_t>(0, qfirst - p.window + 1);
+  const double tiles = (double)((qlast - (klo / stg::KT) * stg::KT) / stg::KT + 1);
   int best = 1;
   double cost = 1e30;
   for (int z = 1; z <= p.max_split && z <= 8; ++z) {
-    const double c = (double)((wgs * z + 255) / 256) * (tiles / z + 4.0) + (z > 1 ? 3.0 * z : 0.0);
+    const double c = (double)((wgs * z + 255) / 256) * (tiles / z + 4.0) + (z > 1 ? 4.0 * z : 0.0);
     if (c < cost - 1e-9) { cost = c; best = z; }
   }
   return best;
 }
+// bf16, head_dim 128, ring of whole 64-slot tiles addressable by 32-bit
+// buffer offsets: the staged kernels
+template <typename T>
+bool staged_ok(const AttnParams& p) {
+  return std::is_same<T, bf16>::value && p.hd == 128 && p.cap % 64 == 0 &&
+         (int64_t)p.cap * p.H * p.hd * 2 <= 0x7fffffff;
+}
 
 template <typename T>
 void fwd_t(const AttnParams& p, hipStream_t s) {
+  if (staged_ok<T>(p)) {
+    const int nz = pick_split_staged(p);
+    static bool attr = false;
+    if (!attr) {
+      (void)hipFuncSetAttribute((const void*)swa_fwd_bf16_128_k, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                stg::LDS_F);
+      attr = true;
+    }
+    hipLaunchKernelGGL(swa_fwd_bf16_128_k, dim3((p.n + stg::QT - 1) / stg::QT, p.H, nz), dim3(stg::NTHR),
+                       stg::LDS_F, s, p);
+    if (nz > 1) {
+      const int tot = p.n * p.H * p.hd;
+      hipLaunchKernelGGL(swa_combine_k<T>, dim3((tot + 255) / 256), dim3(256), 0, s, p, nz);
+    }
+    return;
+  }
   const int nz = pick_split(p, ((p.n + 127) / 128) * p.H, 4);
   dim3 grid((p.n + 127) / 128, p.H, nz);
   switch (p.hd) {
@@ -813,19 +964,18 @@ template <typename T>
 void bwd_t(const AttnParams& p, hipStream_t s, hipStream_t s2) {
   // bf16 / head_dim 128 / 64-aligned ring: the staged 256-query dQ kernel
   // (one workgroup per CU: 256 resident workgroups); otherwise the general one
-  const bool wide = std::is_same<T, bf16>::value && p.hd == 128 && p.cap % 64 == 0 &&
-                    (int64_t)p.cap * p.H * p.hd * 2 <= 0x7fffffff;
+  const bool wide = staged_ok<T>(p);
   int nz;
   if (wide) {
-    nz = pick_split_dq2(p);
+    nz = pick_split_staged(p);
     static bool attr = false;
     if (!attr) {
       (void)hipFuncSetAttribute((const void*)swa_bwd_dq_bf16_128_k, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                dq2::LDS_BYTES);
+                                stg::LDS_BYTES);
       attr = true;
     }
-    hipLaunchKernelGGL(swa_bwd_dq_bf16_128_k, dim3((p.n + dq2::QT - 1) / dq2::QT, p.H, nz), dim3(dq2::NTHR),
-                       dq2::LDS_BYTES, s, p);
+    hipLaunchKernelGGL(swa_bwd_dq_bf16_128_k, dim3((p.n + stg::QT - 1) / stg::QT, p.H, nz), dim3(stg::NTHR),
+                       stg::LDS_BYTES, s, p);
   } else {
     nz = pick_split(p, ((p.n + 127) / 128) * p.H, 8);
   }

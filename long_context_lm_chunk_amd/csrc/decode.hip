@@ -31,7 +31,7 @@ struct DecGemv {
   float* amax;                     // OUT_F32: per-block (max, index) pairs when set
   void* act;                       // OUT_SWIGLU / OUT_GELU: activation vector, storage type
   int H, hd; const double* theta;  // OUT_ROPE
-  void* q; void* kr; void* vr; void* vt; int64_t cap;
+  void* q; void* kr; void* vr; int64_t cap;
 };
 
 enum { OUT_F32 = 0, OUT_SWIGLU = 1, OUT_GELU = 2, OUT_ROPE = 3 };
@@ -240,8 +240,6 @@ __global__ __launch_bounds__(256) void dgemv_k(DecGemv a) {
       } else {
         static_cast<T*>(a.vr)[slot * d + j1] = from_f32<T>(v1);
         static_cast<T*>(a.vr)[slot * d + j2] = from_f32<T>(v2);
-        static_cast<T*>(a.vt)[(int64_t)j1 * a.cap + slot] = from_f32<T>(v1);
-        static_cast<T*>(a.vt)[(int64_t)j2 * a.cap + slot] = from_f32<T>(v2);
       }
     }
   }
@@ -536,11 +534,11 @@ void swa_decode(const void* q, const void* kring, const void* vring, int64_t cap
 
 void dgemv_ln_rope(const void* Wqkv, int d, const float* x, float eps, int H, int hd,
                    const double* theta, const int64_t* dstate, void* q, void* kring, void* vring,
-                   void* vtring, int64_t cap, bool bf, hipStream_t s) {
+                   int64_t cap, bool bf, hipStream_t s) {
   DecGemv a{};
   a.W = Wqkv; a.N = 3 * d; a.K = d; a.x = x; a.eps = eps;
   a.H = H; a.hd = hd; a.theta = theta; a.dstate = dstate;
-  a.q = q; a.kr = kring; a.vr = vring; a.vt = vtring; a.cap = cap;
+  a.q = q; a.kr = kring; a.vr = vring; a.cap = cap;
   if (bf) dgemv_t<bf16>(a, true, OUT_ROPE, SHAPE_SPLIT, s);
   else dgemv_t<float>(a, true, OUT_ROPE, SHAPE_SPLIT, s);
 }

@@ -73,8 +73,9 @@ struct AttnParams {
   const void* q = nullptr;   // [n][H*hd], row stride ldq
   int64_t ldq = 0;
   const void* kring = nullptr; const void* vring = nullptr;  // [cap][H*hd]
-  const void* vtring = nullptr;                               // [H*hd][cap] (V transposed)
-  const void* ktring = nullptr;                               // [H*hd][cap] (K transposed)
+  // [H*hd][cap] transposed copies, key-permuted (see ring_transpose)
+  const void* vtring = nullptr;                               // V (forward)
+  const void* ktring = nullptr;                               // K (dQ)
   int64_t cap = 0;
   int n = 0, H = 0, hd = 0, window = 0;
   int64_t pos0 = 0;          // absolute position of query row 0
@@ -106,7 +107,8 @@ void swa_bwd(const AttnParams& p, bool bf16, hipStream_t s, hipStream_t s_kv);
 // Matrix-vector products (W [N][K] k-contiguous, W2 of the same shape added
 // when non-null); LN(x) is the LayerNorm of the fp32 row x, fused:
 //   dgemv_ln_rope: LN(x) -> Wqkv; RoPE on q and k, q to `q`, k and v to the
-//                  rings at slot pos % cap, v also to the transposed ring
+//                  rings at slot pos % cap (the transposed copies are made
+//                  by the chunk forward of the update that reads them)
 //   dgemv_ln_act:  LN(x) -> up-projection; act = silu(gate) * up (SwiGLU,
 //                  rows interleaved in blocks of 16) or gelu, storage type
 //   dgemv_vec:     y = (W + W2) x (+ resid; y may alias resid); optionally y
@@ -115,7 +117,7 @@ void swa_bwd(const AttnParams& p, bool bf16, hipStream_t s, hipStream_t s_kv);
 // amax holds 2 floats per block; dgemv_blocks(units) gives the block count.
 void dgemv_ln_rope(const void* Wqkv, int d, const float* x, float eps, int H, int hd,
                    const double* theta, const int64_t* dstate, void* q, void* kring, void* vring,
-                   void* vtring, int64_t cap, bool bf16, hipStream_t s);
+                   int64_t cap, bool bf16, hipStream_t s);
 void dgemv_ln_act(const void* Wup, const void* Wup2, int F, int d, const float* x, float eps,
                   bool swiglu, void* act, bool bf16, hipStream_t s);
 void dgemv_vec(const void* W, const void* W2, int N, int K, const void* x, float* y,

@@ -97,7 +97,7 @@ struct Layer {
   void* wup = nullptr;   // [F2][d] (SwiGLU: gate/up interleaved in 16-row blocks)
   void* wdn = nullptr;   // [d][F]
   void* kring = nullptr; void* vring = nullptr;  // [cap][d]
-  void* vtring = nullptr;                          // [d][cap]: V transposed, read by the forward
+  void* vtring = nullptr;                          // [d][cap]: V transposed, key-permuted (forward)
   void* ktring = nullptr;                          // [d][cap]: K transposed, key-permuted (fast blocks: dQ)
   void* wqkvT = nullptr;  // [d][3d] and [d][d]: transposed copies for the input-gradient
   void* woT = nullptr;    // products (fast blocks above the first)
@@ -419,7 +419,7 @@ int phase_a(ttt_model* m, const int32_t* tokens, int64_t B0, int nb, float* hA, 
     int rc = run_gemm(m, g, true, true, EPI_STORE, false, s, false); if (rc) return rc;
     rope_qkv(m->qkvA, nb, m->H, m->hd, B0, m->theta, m->qA, ly.kring, ly.vring, ly.cap, bf, s);
     ring_transpose(static_cast<char*>(m->qkvA) + (size_t)2 * d * m->es, 3 * d, 0, nb, m->H, m->hd, B0,
-                   ly.vtring, ly.cap, false, bf, s);
+                   ly.vtring, ly.cap, true, bf, s);
     AttnParams ap;
     ap.q = m->qA; ap.ldq = d; ap.kring = ly.kring; ap.vring = ly.vring; ap.vtring = ly.vtring; ap.cap = ly.cap;
     ap.n = nb; ap.H = m->H; ap.hd = m->hd; ap.window = m->W; ap.pos0 = B0; ap.o = m->oA; ap.ldo = d;
@@ -470,7 +470,7 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
       rc = run_gemm(m, g, true, true, EPI_STORE, false, s); if (rc) return rc;
       rope_qkv(m->qkvB, n, m->H, m->hd, p0, m->theta, b.q, ly.kring, ly.vring, ly.cap, bf, s);
       ring_transpose(static_cast<char*>(m->qkvB) + (size_t)2 * d * m->es, 3 * d, 0, n, m->H, m->hd, p0,
-                     ly.vtring, ly.cap, false, bf, s);
+                     ly.vtring, ly.cap, true, bf, s);
       // the transposed K copy is only read by this block's dQ, much later in
       // the chunk: make it on the dK/dV stream, off the chain
       HIPCHK(hipEventRecord(m->evKT[j], s));
@@ -637,7 +637,7 @@ void decode_body(ttt_model* m, hipStream_t s) {
     const int j = l - m->f0;
     // LN1 -> qkv -> RoPE -> rings
     dgemv_ln_rope(ly.wqkv, d, m->xd, eps, m->H, m->hd, m->theta, m->dstate, m->qd, ly.kring,
-                  ly.vring, ly.vtring, ly.cap, bf, s);
+                  ly.vring, ly.cap, bf, s);
     swa_decode(m->qd, ly.kring, ly.vring, ly.cap, m->H, m->hd, m->W, m->dstate, m->od, m->attn_ws,
                bf, s);
     // x += o Wo; the first fast block's input row is also kept for the
