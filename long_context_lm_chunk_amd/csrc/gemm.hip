@@ -456,7 +456,7 @@ __global__ void gemm_reduce_k(GemmParams p, int nz) {
 // K advances 32 per stage through a ring of four 32 KB stages filled by
 // direct global->LDS 16-byte loads (buffer_load ... lds: no staging
 // registers; out-of-range rows and columns read as zero), issued three
-// stages ahead so that their latency hides behind three stages of products.
+// stages ahead.
 // Every stage slot issues the same number of loads (past the end of K they
 // read zeros into a slot nobody uses), so the wait for a stage is a fixed
 // vmcnt.  LDS rows are 64 bytes; 16-byte chunk c of row r sits at slot
@@ -471,14 +471,17 @@ constexpr int FI = TM / 32, FJ = TN / 32;    // 32x32 accumulator blocks per wav
 constexpr int ROWB = BK * 2;                 // bytes per LDS row
 constexpr int STAGE_A = BM * ROWB;           // 16 KB
 constexpr int STAGE = (BM + BN) * ROWB;      // 32 KB
-constexpr int LDS_BYTES = NS * STAGE;        // 128 KB of the 160 KB per CU
+constexpr int LDS_BYTES = NS * STAGE;        // 128 KB of the 160 KB per CU (a fifth
+                                             // stage measured no faster)
 constexpr int SLAB_LOADS = BM * ROWB / 1024 / NW;   // 1 KB loads per wave per operand slab (2)
 constexpr int LOADS = 2 * SLAB_LOADS;        // per wave per stage
 constexpr int ES = BN + 8;                   // epilogue fp32 row pitch: the two lane
                                              // halves (4 rows apart) on disjoint banks
 constexpr int EROWS = 64;                    // rows per epilogue pass
 static_assert(EROWS * ES * 4 <= LDS_BYTES, "epilogue pass fits");
-static_assert((NS - 2) * LOADS == 8, "vmcnt in the main loop");
+// s_waitcnt immediates with vmcnt n (expcnt and lgkmcnt not waited for)
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+static_assert((NS - 2) * LOADS < 64, "vmcnt range");
 typedef __attribute__((address_space(3))) void lds_void;
 
 // Issue the loads of one 256-row operand slab (rows row0.., k k0..k0+31)
@@ -550,43 +553,55 @@ __global__ __launch_bounds__(big::NT, 1) void gemm256_kernel(GemmParams p) {
   // fragment addressing: lane reads row (l & 31) of a 32-row block, logical
   // chunk 2*ks + (l >> 5), at slot chunk ^ ((row >> 2) & 3) = chunk ^ ((l >> 2) & 3)
   const int frow = lane & 31, fsw = (lane >> 2) & 3, fhi = lane >> 5;
+  const int abase = (wm * TM + frow) * ROWB, bbase = STAGE_A + (wn * TN + frow) * ROWB;
+  auto frags = [&](int kt, int ks, bf16x8 (&a)[FI], bf16x8 (&b)[FJ]) {
+    const char* st = smem + ((kt - kt_begin) % NS) * STAGE;
+    const int slot = ((2 * ks + fhi) ^ fsw) * 16;
+#pragma unroll
+    for (int i = 0; i < FI; ++i) a[i] = *reinterpret_cast<const bf16x8*>(st + abase + i * 32 * ROWB + slot);
+#pragma unroll
+    for (int j = 0; j < FJ; ++j) b[j] = *reinterpret_cast<const bf16x8*>(st + bbase + j * 32 * ROWB + slot);
+  };
+  // Fragments run one k-step ahead of the products, across stage borders:
+  // the reads of (kt, 1) go out before the products of (kt, 0), those of
+  // (kt + 1, 0) before the products of (kt, 1).  Stage kt + 1 must then be
+  // complete in LDS half-way through stage kt, so the wait and the barrier
+  // sit between the two k-steps: this wave's loads of stage kt + 1 have
+  // landed once only the NS - 3 younger stages' are outstanding, the
+  // barrier makes that hold for every wave and also frees slot
+  // (kt - 1) % NS, which nobody reads any more, for stage kt + NS - 1.
+  // (Against a wait and barrier at the start of each stage this removes
+  // the LDS-latency bubble before every stage's first products: 8-15 %
+  // on the large shapes.)
+  static_assert(BK == 32 && NS >= 4, "two k-steps per stage; stage kt + 1 waited for mid-stage");
+  bf16x8 fa0[FI], fb0[FJ], fa1[FI], fb1[FJ];
   if (kt_begin < kt_end) {
 #pragma unroll
     for (int u = 0; u < NS - 1; ++u) issue(kt_begin + u);
+    __builtin_amdgcn_s_waitcnt(big::vmcnt_imm((NS - 2) * big::LOADS));    // stage kt_begin
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    frags(kt_begin, 0, fa0, fb0);
   }
   for (int kt = kt_begin; kt < kt_end; ++kt) {
-    // this wave's loads of stage kt have landed once at most the (NS - 2)
-    // younger stages' loads are outstanding; the barrier then covers every
-    // wave's loads and frees slot (kt - 1) % NS for stage kt + NS - 1
-    __builtin_amdgcn_s_waitcnt(0x0F78);    // vmcnt(8)
+    frags(kt, 1, fa1, fb1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < FI; ++i)
+#pragma unroll
+      for (int j = 0; j < FJ; ++j) mma32x32x16(fa0[i], fb0[j], acc[i][j]);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(big::vmcnt_imm((NS - 3) * big::LOADS));    // stage kt + 1
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     issue(kt + NS - 1);
-    const char* As = smem + ((kt - kt_begin) % NS) * STAGE + (wm * TM + frow) * ROWB;
-    const char* Bs = smem + ((kt - kt_begin) % NS) * STAGE + STAGE_A + (wn * TN + frow) * ROWB;
-    // fragments double-buffered over the k-steps of the stage: the reads of
-    // step ks + 1 are issued before the products of step ks (scheduling
-    // fences keep the compiler from sinking them)
-    bf16x8 fa[2][FI], fb[2][FJ];
-    auto frags = [&](int ks, bf16x8 (&a)[FI], bf16x8 (&b)[FJ]) {
-      const int slot = ((2 * ks + fhi) ^ fsw) * 16;
+    frags(kt + 1, 0, fa0, fb0);            // past the end: zeros, unused
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < FI; ++i) a[i] = *reinterpret_cast<const bf16x8*>(As + i * 32 * ROWB + slot);
+    for (int i = 0; i < FI; ++i)
 #pragma unroll
-      for (int j = 0; j < FJ; ++j) b[j] = *reinterpret_cast<const bf16x8*>(Bs + j * 32 * ROWB + slot);
-    };
-    frags(0, fa[0], fb[0]);
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int c = ks & 1;
-      if (ks + 1 < BK / 16) frags(ks + 1, fa[c ^ 1], fb[c ^ 1]);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < FI; ++i)
-#pragma unroll
-        for (int j = 0; j < FJ; ++j) mma32x32x16(fa[c][i], fb[c][j], acc[i][j]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+      for (int j = 0; j < FJ; ++j) mma32x32x16(fa1[i], fb1[j], acc[i][j]);
+    __builtin_amdgcn_sched_barrier(0);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0): the zero-fill loads past the end
   __syncthreads();                         // all waves done with the operand stages
