@@ -244,15 +244,6 @@ __global__ void swa_combine_k(AttnParams p, int nsplit) {
   if (p.lse && c % p.hd == 0) p.lse[(int64_t)h * p.n + row] = (M + log2f(L)) * LN2;
 }
 
-// Column of ring slot s in a key-permuted transposed copy: inside every
-// aligned group of 16 slots the middle two quads are swapped (offsets 4..7
-// and 8..11), so the 8 keys {4h..4h+3, 8+4h..8+4h+3} of a group, which one
-// lane holds in a 32x32 accumulator of the transposed scores, sit in one
-// 16-byte run (offsets 8h..8h+7).
-DEVI int64_t kperm(int64_t s) {
-  const int o = (int)(s & 15);
-  return (s & ~(int64_t)15) | (o < 4 || o >= 12 ? o : (o < 8 ? o + 4 : o - 4));
-}
 
 // Transposed ring copy: rows h*hd + i, column (position mod cap), or its
 // key-permuted column (perm != 0, see kperm); one block per 64 positions of
@@ -435,6 +426,14 @@ constexpr int LDS_BYTES = 2 * STAGE;         // 96 KB: one workgroup per CU
 constexpr int STAGE_F = TILE_K + TILE_T;     // forward: K, V^T (32 KB)
 constexpr int LDS_F = 2 * STAGE_F;           // 64 KB
 constexpr int PER = 16 / NW;                 // 1 KB load instructions per wave and array
+// dK/dV: 4 waves x 32 keys; per 64-query tile Q and dO ([query][hd], rows
+// of 256 B), their transposes ([hd][query], rows of 128 B) and the tile's
+// LSE and D (256 B each)
+constexpr int KWAVES = 4, KB_ = 32 * KWAVES, QTL = 64;
+constexpr int TILE_Q = QTL * ROWK;           // 16 KB
+constexpr int TILE_QT = HD * QTL * 2;        // 16 KB
+constexpr int STAGE_B = 2 * TILE_Q + 2 * TILE_QT + 2 * QTL * 4;
+constexpr int LDS_B = 2 * STAGE_B;           // 129 KB
 typedef __attribute__((address_space(3))) void lds_void;
 DEVI __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
   const int nb = bytes > 0x7fffffff ? 0x7fffffff : (int)bytes;
@@ -488,9 +487,12 @@ __global__ __launch_bounds__(stg::NTHR, 1) void swa_bwd_dq_bf16_128_k(AttnParams
   const __amdgpu_buffer_rsrc_t rk = rsrc(p.kring, p.cap * d * 2);
   const __amdgpu_buffer_rsrc_t rv = rsrc(p.vring, p.cap * d * 2);
   const __amdgpu_buffer_rsrc_t rt = rsrc(p.ktring, (int64_t)d * p.cap * 2);
-  auto issue = [&](int it, int stage) {
-    const int64_t kt = ktA + (int64_t)it * KT;
-    const int64_t slot0 = kt % p.cap;            // tiles never wrap (cap % 64 == 0)
+  // ring slot of the next tile to load, advanced by one tile per issue
+  // (tiles never wrap: cap % 64 == 0)
+  int64_t slot_next = (ktA + (int64_t)tb * KT) % p.cap;
+  auto issue = [&](int stage) {
+    const int64_t slot0 = slot_next;
+    slot_next = slot_next + KT == p.cap ? 0 : slot_next + KT;
     char* st = smem + stage * STAGE;
     // K and V: 16 instructions of 4 rows (1 KB) each per tile
 #pragma unroll
@@ -513,12 +515,12 @@ __global__ __launch_bounds__(stg::NTHR, 1) void swa_bwd_dq_bf16_128_k(AttnParams
     }
   };
 
-  if (tb < te) issue(tb, 0);
+  if (tb < te) issue(0);
   for (int it = tb; it < te; ++it) {
     const int stage = (it - tb) & 1;
     __builtin_amdgcn_s_waitcnt(0x0F70);    // vmcnt(0): this wave's loads of tile it
     __syncthreads();                       // every wave's; the other stage is free
-    if (it + 1 < te) issue(it + 1, stage ^ 1);
+    if (it + 1 < te) issue(stage ^ 1);
     const char* Ks = smem + stage * STAGE;
     const char* Vs = Ks + TILE_K;
     const char* Ts = Ks + 2 * TILE_K;
@@ -539,6 +541,17 @@ __global__ __launch_bounds__(stg::NTHR, 1) void swa_bwd_dq_bf16_128_k(AttnParams
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], ks ? s : zero, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, gf[ks], ks ? dp : zero, 0, 0, 0);
       }
+      // the K^T fragments of this half's dQ products: their reads run under
+      // the exponentials
+      bf16x8 tf[2][4];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int c = 4 * kb + 2 * hf + hl, trow = b * 32 + ql;
+          tf[hf][b] = *reinterpret_cast<const bf16x8*>(Ts + trow * ROWT + ((c ^ ((trow >> 1) & 7)) * 16));
+        }
+      __builtin_amdgcn_sched_barrier(0);
       // outside the band S = -inf (wave-uniform test: most tiles are inside)
       if (!interior) {
 #pragma unroll
@@ -558,13 +571,8 @@ __global__ __launch_bounds__(stg::NTHR, 1) void swa_bwd_dq_bf16_128_k(AttnParams
 #pragma unroll
         for (int j = 0; j < 8; ++j) v8[j] = s[8 * hf + j];
         const bf16x8 df = pack8<bf16>(v8);
-        const int c = 4 * kb + 2 * hf + hl;
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const int trow = b * 32 + ql;
-          const bf16x8 tf = *reinterpret_cast<const bf16x8*>(Ts + trow * ROWT + ((c ^ ((trow >> 1) & 7)) * 16));
-          mma32x32x16(tf, df, dacc[b]);
-        }
+        for (int b = 0; b < 4; ++b) mma32x32x16(tf[hf][b], df, dacc[b]);
       }
     }
   }
@@ -634,8 +642,12 @@ __global__ __launch_bounds__(stg::NTHR, 1) void swa_fwd_bf16_128_k(AttnParams p)
 
   const __amdgpu_buffer_rsrc_t rk = rsrc(p.kring, p.cap * d * 2);
   const __amdgpu_buffer_rsrc_t rt = rsrc(p.vtring, (int64_t)d * p.cap * 2);
-  auto issue = [&](int it, int stage) {
-    const int64_t slot0 = (ktA + (int64_t)it * KT) % p.cap;   // tiles never wrap
+  // ring slot of the next tile to load, advanced by one tile per issue
+  // (tiles never wrap: cap % 64 == 0)
+  int64_t slot_next = (ktA + (int64_t)tb * KT) % p.cap;
+  auto issue = [&](int stage) {
+    const int64_t slot0 = slot_next;
+    slot_next = slot_next + KT == p.cap ? 0 : slot_next + KT;
     char* st = smem + stage * STAGE_F;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
@@ -655,26 +667,45 @@ __global__ __launch_bounds__(stg::NTHR, 1) void swa_fwd_bf16_128_k(AttnParams p)
     }
   };
 
-  if (tb < te) issue(tb, 0);
+  if (tb < te) issue(0);
   for (int it = tb; it < te; ++it) {
     const int stage = (it - tb) & 1;
     __builtin_amdgcn_s_waitcnt(0x0F70);    // vmcnt(0): this wave's loads of tile it
     __syncthreads();                       // every wave's; the other stage is free
-    if (it + 1 < te) issue(it + 1, stage ^ 1);
+    if (it + 1 < te) issue(stage ^ 1);
     const char* Ks = smem + stage * STAGE_F;
     const char* Vt = Ks + TILE_K;
     const int64_t kt = ktA + (int64_t)it * KT;
-    f32x16 s[2];
-    const f32x16 zero = {};
+    // all 16 K fragments of the tile first, then the 16 score products;
+    // the registers then take the 16 V^T fragments, whose reads run under
+    // the softmax arithmetic
+    bf16x8 fr[16];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int krow = kb * 32 + ql;
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + krow * ROWK + (((2 * ks + hl) ^ (krow & 15)) * 16));
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], ks ? s[kb] : zero, 0, 0, 0);
-      }
+      for (int ks = 0; ks < 8; ++ks)
+        fr[kb * 8 + ks] = *reinterpret_cast<const bf16x8*>(Ks + krow * ROWK + (((2 * ks + hl) ^ (krow & 15)) * 16));
     }
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 s[2];
+    const f32x16 zero = {};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[kb * 8 + ks], qf[ks], ks ? s[kb] : zero, 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int c = 4 * kb + 2 * hf + hl, trow = b * 32 + ql;
+          fr[kb * 8 + hf * 4 + b] = *reinterpret_cast<const bf16x8*>(Vt + trow * ROWT + ((c ^ ((trow >> 1) & 7)) * 16));
+        }
+    __builtin_amdgcn_sched_barrier(0);
     const bool interior = (kt + KT - 1 <= first) && (kt > last - p.window);
     if (!interior) {
       const int kq0 = (int)(kt - first) - (wave * 32 + ql) + 4 * hl;   // key - query of s[0][0]
@@ -721,13 +752,8 @@ __global__ __launch_bounds__(stg::NTHR, 1) void swa_fwd_bf16_128_k(AttnParams p)
 #pragma unroll
         for (int j = 0; j < 8; ++j) pv[j] = s[kb][8 * hf + j];
         const bf16x8 pf = pack8<bf16>(pv);
-        const int c = 4 * kb + 2 * hf + hl;
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const int trow = b * 32 + ql;
-          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(Vt + trow * ROWT + ((c ^ ((trow >> 1) & 7)) * 16));
-          mma32x32x16(vf, pf, oacc[b]);
-        }
+        for (int b = 0; b < 4; ++b) mma32x32x16(fr[kb * 8 + hf * 4 + b], pf, oacc[b]);
       }
   }
 
@@ -879,6 +905,180 @@ __global__ __launch_bounds__(256) void swa_bwd_dkdv32_k(AttnParams p) {
   }
 }
 
+// ------------------------------------------- backward dK, dV, bf16, hd 128
+// swa_bwd_dkdv32_k for the bf16 / head_dim 128 case, staged: the keys of a
+// workgroup (4 waves x 32, lane = key) keep their K and V fragments in
+// registers; per 64-query tile, Q and dO, their query-permuted transposes
+// and the tile's LSE and D arrive by direct global->LDS loads into two
+// stages (the next tile's in flight while the current one is multiplied).
+// S = Q K^T and dP = dO V^T come out with lane = key, so P and dS feed
+// dV^T += dO^T P and dK^T += Q^T dS straight from the accumulators, each
+// transposed operand fragment one 16-byte read.
+__global__ __launch_bounds__(256, 1) void swa_bwd_dkdv_bf16_128_k(AttnParams p) {
+  using namespace stg;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hl = lane >> 5, ql = lane & 31;
+  int bx, h, bz;
+  attn_block(bx, h, bz);
+  const int ks0 = bx * KB_;
+  const int d = p.H * HD;
+  const bf16* KR = static_cast<const bf16*>(p.kring);
+  const bf16* VR = static_cast<const bf16*>(p.vring);
+
+  const int kw = ks0 + wave * 32;              // this wave's first key (chunk row)
+  const int krow = kw + ql;
+  const bool kok = krow < p.n;
+  const int64_t kslot = (p.pos0 + (kok ? krow : 0)) % p.cap;
+  bf16x8 kf[8], vf[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    kf[ks] = g_frag8<bf16>(KR + kslot * d + h * HD + ks * 16 + 8 * hl, kok);
+    vf[ks] = g_frag8<bf16>(VR + kslot * d + h * HD + ks * 16 + 8 * hl, kok);
+  }
+  const float sc = LOG2E / sqrtf((float)HD);
+  const uint32_t wlen = (uint32_t)p.window;
+  f32x16 dk[4], dv[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { dk[b][r] = 0.f; dv[b][r] = 0.f; }
+
+  // query tiles: from the first key on, up to the last query the last key
+  // reaches (chunk rows; the window may end before the chunk does)
+  const int kmax = min(ks0 + KB_, p.n) - 1;
+  const int qend = (int)min<int64_t>((int64_t)p.n - 1, (int64_t)kmax + p.window - 1);
+  const int qt0 = (ks0 / QTL) * QTL;
+  const int ntile = qend >= qt0 ? (qend - qt0) / QTL + 1 : 0;
+
+  const __amdgpu_buffer_rsrc_t rq = rsrc(p.q, (int64_t)p.n * p.ldq * 2);
+  const __amdgpu_buffer_rsrc_t rg = rsrc(p.dout, (int64_t)p.n * p.lddo * 2);
+  const __amdgpu_buffer_rsrc_t rqt = rsrc(p.qtr, (int64_t)d * p.ldtr * 2);
+  const __amdgpu_buffer_rsrc_t rgt = rsrc(p.gtr, (int64_t)d * p.ldtr * 2);
+  const __amdgpu_buffer_rsrc_t rl = rsrc(p.lse + (int64_t)h * p.n, (int64_t)p.n * 4);
+  const __amdgpu_buffer_rsrc_t rd = rsrc(p.D + (int64_t)h * p.n, (int64_t)p.n * 4);
+  auto issue = [&](int t, int stage) {
+    const int qt = qt0 + t * QTL;
+    char* st = smem + stage * STAGE_B;
+    // Q, dO: 16 instructions of 4 rows each, 4 per wave; rows past n read 0
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = wave * 4 + i;
+      const int row = q * 4 + (lane >> 4), pc = lane & 15;
+      const int c = pc ^ (row & 15);
+      const uint32_t oq = (uint32_t)(((int64_t)(qt + row) * p.ldq + h * HD + 8 * c) * 2);
+      const uint32_t og = (uint32_t)(((int64_t)(qt + row) * p.lddo + h * HD + 8 * c) * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void*)(st + q * 1024), 16, oq, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rg, (lds_void*)(st + TILE_Q + q * 1024), 16, og, 0, 0, 0);
+    }
+    // Q^T, dO^T: 16 instructions of 8 rows (head dims) each, 4 per wave
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = wave * 4 + i;
+      const int row = q * 8 + (lane >> 3), pc = lane & 7;
+      const int c = pc ^ ((row >> 1) & 7);
+      const uint32_t off = (uint32_t)((((int64_t)(h * HD + row)) * p.ldtr + qt + 8 * c) * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rqt, (lds_void*)(st + 2 * TILE_Q + q * 1024), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rgt, (lds_void*)(st + 2 * TILE_Q + TILE_QT + q * 1024), 16, off, 0, 0, 0);
+    }
+    // LSE and D of the tile (4 bytes per lane); past n they read 0
+    char* ld = st + 2 * TILE_Q + 2 * TILE_QT;
+    if (wave == 0) __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lds_void*)ld, 4, (uint32_t)(qt + lane) * 4u, 0, 0, 0);
+    if (wave == 1) __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_void*)(ld + QTL * 4), 4, (uint32_t)(qt + lane) * 4u, 0, 0, 0);
+  };
+
+  if (ntile > 0) issue(0, 0);
+  for (int t = 0; t < ntile; ++t) {
+    const int stage = t & 1;
+    __builtin_amdgcn_s_waitcnt(0x0F70);    // vmcnt(0): this wave's loads of tile t
+    __syncthreads();                       // every wave's; the other stage is free
+    if (t + 1 < ntile) issue(t + 1, stage ^ 1);
+    const char* Qs = smem + stage * STAGE_B;
+    const char* Gs = Qs + TILE_Q;
+    const char* Qts = Qs + 2 * TILE_Q;
+    const char* Gts = Qts + TILE_QT;
+    const float* lse_s = reinterpret_cast<const float*>(Qts + 2 * TILE_QT);
+    const float* D_s = lse_s + QTL;
+    const int qt = qt0 + t * QTL;
+    // every (query, key) pair of the tile inside the band, every query < n
+    const bool interior = qt + QTL - 1 < p.n && qt >= kw + 31 && qt + QTL - 1 - kw < p.window;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      f32x16 s, dp;
+      const f32x16 zero = {};
+      const int qr = qb * 32 + ql;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const int slot = ((2 * ks + hl) ^ (qr & 15)) * 16;
+        const bf16x8 qf = *reinterpret_cast<const bf16x8*>(Qs + qr * ROWK + slot);
+        const bf16x8 gf = *reinterpret_cast<const bf16x8*>(Gs + qr * ROWK + slot);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf, kf[ks], ks ? s : zero, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gf, vf[ks], ks ? dp : zero, 0, 0, 0);
+      }
+      // element r: query qb*32 + 8(r/4) + 4hl + r%4 of the tile, key krow
+      if (!interior) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qi = qb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+          const int rel = qt + qi - krow;                       // query - key
+          const bool ok = (uint32_t)rel < wlen && qt + qi < p.n;
+          s[r] = ok ? s[r] : -INFINITY;
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 l4 = *reinterpret_cast<const float4*>(lse_s + qb * 32 + 8 * g + 4 * hl);
+        const float4 d4 = *reinterpret_cast<const float4*>(D_s + qb * 32 + 8 * g + 4 * hl);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          const float pr = fast_exp2(fmaf(s[r], sc, -lv[e] * LOG2E));
+          s[r] = pr;                                   // P
+          dp[r] = pr * (dp[r] - dv4[e]);               // dS
+        }
+      }
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        float a8[8], b8[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) { a8[j] = s[8 * hf + j]; b8[j] = dp[8 * hf + j]; }
+        const bf16x8 pf = pack8<bf16>(a8);
+        const bf16x8 df = pack8<bf16>(b8);
+        const int c = 4 * qb + 2 * hf + hl;    // the lane's 8 queries in the permuted rows
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int trow = b * 32 + ql;
+          const int off = trow * (QTL * 2) + ((c ^ ((trow >> 1) & 7)) * 16);
+          const bf16x8 gt = *reinterpret_cast<const bf16x8*>(Gts + off);
+          const bf16x8 qtf = *reinterpret_cast<const bf16x8*>(Qts + off);
+          dv[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gt, pf, dv[b], 0, 0, 0);
+          dk[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qtf, df, dk[b], 0, 0, 0);
+        }
+      }
+    }
+  }
+  if (!kok) return;
+  const float scale = 1.f / sqrtf((float)HD);
+  bf16* DK = static_cast<bf16*>(p.dk) + (int64_t)krow * p.ldg + h * HD;
+  bf16* DV = static_cast<bf16*>(p.dv) + (int64_t)krow * p.ldg + h * HD;
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int c = b * 32 + 8 * g + 4 * hl;        // 4 consecutive head dims
+      bf16x4 ok4, ov4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ok4[e] = static_cast<bf16>(dk[b][4 * g + e] * scale);
+        ov4[e] = static_cast<bf16>(dv[b][4 * g + e]);
+      }
+      *reinterpret_cast<bf16x4*>(DK + c) = ok4;
+      *reinterpret_cast<bf16x4*>(DV + c) = ov4;
+    }
+}
+
 // Key-range splits for launches too small to fill the GPU (the per-chunk
 // calls).  The GPU runs 512 of these workgroups at once (two per CU), so a
 // launch of wgs * z workgroups takes ceil(wgs * z / 512) rounds for 1/z of
@@ -981,10 +1181,24 @@ void bwd_t(const AttnParams& p, hipStream_t s, hipStream_t s2) {
   }
   dim3 gq((p.n + 127) / 128, p.H, nz);
   dim3 gk((p.n + 127) / 128, p.H);
+  // the staged dK/dV kernel also needs the transposed Q and dO
+  const bool wide_kv = wide && p.qtr && p.gtr && p.ldtr % 64 == 0 && p.ldtr >= ((p.n + 63) / 64) * 64 &&
+                       (int64_t)(p.n + 64) * std::max(p.ldq, p.lddo) * 2 <= 0x7fffffff &&
+                       (int64_t)p.H * p.hd * p.ldtr * 2 <= 0x7fffffff;
+  if (wide_kv) {
+    static bool attr = false;
+    if (!attr) {
+      (void)hipFuncSetAttribute((const void*)swa_bwd_dkdv_bf16_128_k, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                stg::LDS_B);
+      attr = true;
+    }
+    hipLaunchKernelGGL(swa_bwd_dkdv_bf16_128_k, dim3((p.n + stg::KB_ - 1) / stg::KB_, p.H), dim3(256),
+                       stg::LDS_B, s2, p);
+  }
   switch (p.hd) {
 #define CASE(HDV) case HDV: \
     if (!wide) hipLaunchKernelGGL((swa_bwd_dq32_k<T, HDV>), gq, dim3(256), 0, s, p); \
-    hipLaunchKernelGGL((swa_bwd_dkdv32_k<T, HDV>), gk, dim3(256), 0, s2, p); break;
+    if (!wide_kv) hipLaunchKernelGGL((swa_bwd_dkdv32_k<T, HDV>), gk, dim3(256), 0, s2, p); break;
     CASE(16) CASE(32) CASE(64) CASE(96) CASE(128)
 #undef CASE
     default: return;
@@ -1014,5 +1228,7 @@ void swa_bwd(const AttnParams& p, bool bf, hipStream_t s, hipStream_t s_kv) {
   if (p.n <= 0) return;
   if (bf) bwd_t<bf16>(p, s, s_kv); else bwd_t<float>(p, s, s_kv);
 }
+
+bool swa_bwd_reads_transposes(int hd, bool bf) { return bf && hd == stg::HD; }
 
 }  // namespace ttt

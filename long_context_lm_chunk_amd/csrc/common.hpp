@@ -278,6 +278,16 @@ template <> DEVI f32x8 pack8<float>(const float* v) {
   f32x8 r; for (int i = 0; i < 8; ++i) r[i] = v[i]; return r;
 }
 
+// Column of position slot s in a position-permuted transposed copy (of K,
+// V, Q or dO: [H*hd][slots]): inside every aligned group of 16 slots the
+// middle two quads are swapped (offsets 4..7 and 8..11), so the 8 positions
+// {4h..4h+3, 8+4h..8+4h+3} of a group, which one lane holds in a 32x32
+// accumulator of scores, sit in one 16-byte run (offsets 8h..8h+7).
+DEVI int64_t kperm(int64_t s) {
+  const int o = (int)(s & 15);
+  return (s & ~(int64_t)15) | (o < 4 || o >= 12 ? o : (o < 8 ? o + 4 : o - 4));
+}
+
 // 2^x with the hardware instruction (no denormal range fix-up; the inputs
 // here are <= 8 and results below 2^-126 may flush to zero).
 DEVI float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -255,7 +255,7 @@ __global__ void rope_qkv_k(const T* __restrict__ qkv, int n, int H, int hd, int6
 template <typename T>
 __global__ __launch_bounds__(256) void transpose_k(const T* __restrict__ src, int rows, int cols,
                                                    int64_t lds_, T* __restrict__ dst, int64_t ldd,
-                                                   int rows_pad) {
+                                                   int rows_pad, int perm) {
   __shared__ T tile[64][65];
   const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
@@ -268,7 +268,7 @@ __global__ __launch_bounds__(256) void transpose_k(const T* __restrict__ src, in
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int c = c0 + ty * 16 + i, r = r0 + tx;
-    if (c < cols && r < rows_pad) dst[(int64_t)c * ldd + r] = tile[tx][ty * 16 + i];
+    if (c < cols && r < rows_pad) dst[(int64_t)c * ldd + (perm ? kperm(r) : r)] = tile[tx][ty * 16 + i];
   }
 }
 
@@ -528,12 +528,13 @@ void rope_qkv(const void* qkv, int n, int H, int hd, int64_t pos0, const double*
 }
 
 void transpose(const void* src, int rows, int cols, int64_t lds_, void* dst, int64_t ldd, int rows_pad,
-               bool bf, hipStream_t s) {
+               bool bf, hipStream_t s, bool perm16) {
   if (rows_pad < rows) rows_pad = rows;
   if (rows_pad <= 0 || cols <= 0) return;
   dim3 grid((cols + 63) / 64, (rows_pad + 63) / 64);
-  TSEL(bf, hipLaunchKernelGGL(transpose_k<bf16>, grid, dim3(256), 0, s, (const bf16*)src, rows, cols, lds_, (bf16*)dst, ldd, rows_pad),
-       hipLaunchKernelGGL(transpose_k<float>, grid, dim3(256), 0, s, (const float*)src, rows, cols, lds_, (float*)dst, ldd, rows_pad));
+  const int pm = perm16 ? 1 : 0;
+  TSEL(bf, hipLaunchKernelGGL(transpose_k<bf16>, grid, dim3(256), 0, s, (const bf16*)src, rows, cols, lds_, (bf16*)dst, ldd, rows_pad, pm),
+       hipLaunchKernelGGL(transpose_k<float>, grid, dim3(256), 0, s, (const float*)src, rows, cols, lds_, (float*)dst, ldd, rows_pad, pm));
 }
 
 void rope_bwd(void* dqkv, int n, int H, int hd, int64_t pos0, const double* theta, bool bf,

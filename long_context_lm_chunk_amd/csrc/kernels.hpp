@@ -36,9 +36,10 @@ int gemm(const GemmParams& p, bool bf16_operands, bool a_kc, bool b_kc, int epi,
          hipStream_t s);
 
 // ---- elementwise (elementwise.hip); T is bf16 when bf16 != 0, else float
-// dst[c][r] = src[r][c] (r < rows, c < cols); rows..rows_pad-1 written as 0
+// dst[c][r] = src[r][c] (r < rows, c < cols); rows..rows_pad-1 written as 0;
+// with perm16 the columns of dst are permuted by kperm (rows_pad % 16 == 0)
 void transpose(const void* src, int rows, int cols, int64_t ld_src, void* dst, int64_t ld_dst,
-               int rows_pad, bool bf16, hipStream_t s);
+               int rows_pad, bool bf16, hipStream_t s, bool perm16 = false);
 void embed(const int32_t* tok, int n, const void* E, int d, int V, bool bf16, float* out, int* err,
            hipStream_t s);
 void layernorm_fwd(const float* x, int64_t ldx, int n, int d, float eps, void* y, int64_t ldy,
@@ -86,6 +87,9 @@ struct AttnParams {
   const float* D = nullptr;  // [H][n] rowsum(dO*O)
   void* dq = nullptr; void* dk = nullptr; void* dv = nullptr; int64_t ldg = 0;
   int64_t kmin = 0;          // smallest key position that receives dK/dV (chunk start)
+  // Q and dO transposed, [H*hd][ldtr], columns permuted by kperm and zero
+  // up to a multiple of 64 (optional: the staged dK/dV kernel reads them)
+  const void* qtr = nullptr; const void* gtr = nullptr; int64_t ldtr = 0;
   // key-range split scratch (optional): part [max_split][n][H*hd] fp32,
   // part_ml [max_split][H][n][2]
   float* part = nullptr; float* part_ml = nullptr; int max_split = 1;
@@ -100,6 +104,9 @@ void ring_transpose(const void* src, int64_t ld, int64_t src_cap, int n, int H, 
 // dQ on s, dK/dV on s_kv (the two are independent; the caller orders s_kv
 // after the inputs and joins it before using dK/dV; s_kv may equal s)
 void swa_bwd(const AttnParams& p, bool bf16, hipStream_t s, hipStream_t s_kv);
+// whether swa_bwd takes its staged dK/dV path (which reads qtr / gtr) for
+// this head size and type
+bool swa_bwd_reads_transposes(int hd, bool bf16);
 
 // ---- decode (decode.hip)
 // Every decode kernel reads the position from dstate = {pos, ci} on the

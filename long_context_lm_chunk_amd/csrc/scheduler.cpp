@@ -155,6 +155,9 @@ struct ttt_model {
   hipEvent_t evK0 = nullptr, evK1 = nullptr;
   float* dtmp = nullptr; void* dout = nullptr; void* dqkv = nullptr; float* Dattn = nullptr;
   float* attn_part = nullptr; float* attn_ml = nullptr;   // key-range split partials
+  // Q and dO of the chunk transposed for dK/dV: [d][Cq], Cq = the chunk
+  // capacity rounded up to a multiple of 64, columns permuted in groups of 16
+  void* qT = nullptr; void* gT = nullptr; int64_t Cq = 0;
   float* split_ws = nullptr; int64_t split_cap = 0;         // split-K partials of the GEMMs
   // decode
   float* xd = nullptr; void* qd = nullptr; void* od = nullptr;
@@ -307,6 +310,9 @@ size_t layout(ttt_model* m, void* base) {
   m->Dattn = cv.take<float>((size_t)H * C * 4);
   m->attn_part = cv.take<float>((size_t)kMaxSplit * C * d * 4);
   m->attn_ml = cv.take<float>((size_t)kMaxSplit * H * C * 2 * 4);
+  m->Cq = round_up((int64_t)C, 64);
+  m->qT = cv.take<void>((size_t)m->Cq * d * es);
+  m->gT = cv.take<void>((size_t)m->Cq * d * es);
   m->split_cap = (int64_t)4 * C * std::max(d, 3 * d);
   m->split_ws = cv.take<float>((size_t)m->split_cap * 4);
   // decode
@@ -605,6 +611,12 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
       HIPCHK(hipStreamWaitEvent(s, m->evKT[j], 0));  // transposed K copy for dQ
       HIPCHK(hipEventRecord(m->evK0, s));            // inputs of dK/dV ready
       HIPCHK(hipStreamWaitEvent(m->sk, m->evK0, 0));
+      if (swa_bwd_reads_transposes(m->hd, bf)) {
+        const int npad = (int)round_up((int64_t)n, 64);
+        transpose(b.q, n, d, d, m->qT, m->Cq, npad, bf, m->sk, true);
+        transpose(m->dout, n, d, d, m->gT, m->Cq, npad, bf, m->sk, true);
+        ap.qtr = m->qT; ap.gtr = m->gT; ap.ldtr = m->Cq;
+      }
       swa_bwd(ap, bf, s, m->sk);
       HIPCHK(hipEventRecord(m->evK1, m->sk));
       HIPCHK(hipStreamWaitEvent(s, m->evK1, 0));     // dK/dV in place for the RoPE backward
