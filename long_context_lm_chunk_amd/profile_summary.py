@@ -2,14 +2,14 @@
 
 Usage:
   python -m long_context_lm_chunk_amd.profile_summary RESULTS_DB [--title T] [--cmd C]
-         [--per N] [--match SUBSTR ...] [--top K]
+         [--per N] [--match SUBSTR ...] [--exclude SUBSTR ...] [--top K]
 
 Reads the per-dispatch kernel table that ``rocprofv3 --kernel-trace`` writes
 (SQLite) and prints calls, total and average duration and share per kernel
 symbol (the unit in which a HIP-event average over one kernel's launches can
 be compared with the trace), with shortened names.  ``--per N`` also divides
 calls and time by N (e.g. the number of prefills in the run); ``--match``
-keeps only symbols containing one of the substrings.  Raw databases stay out
+keeps only symbols containing one of the substrings, ``--exclude`` drops them.  Raw databases stay out
 of the repository; only these summaries are kept.
 """
 from __future__ import annotations
@@ -43,12 +43,15 @@ def short(name: str) -> str:
     return n[:90]
 
 
-def summarise(db: str, title: str = "", cmd: str = "", per: float = 1.0, match=None, top: int = 30) -> str:
+def summarise(db: str, title: str = "", cmd: str = "", per: float = 1.0, match=None, top: int = 30,
+              exclude=None) -> str:
     c = sqlite3.connect(db)
     rows = c.execute("select name, count(*), sum(duration), avg(duration) from kernels "
                      "group by name order by sum(duration) desc").fetchall()
     if match:
         rows = [r for r in rows if any(mm in r[0] for mm in match)]
+    if exclude:
+        rows = [r for r in rows if not any(mm in r[0] for mm in exclude)]
     total = sum(r[2] for r in rows)
     out = [f"# {title}" if title else "# kernel summary", ""]
     if cmd:
@@ -75,6 +78,7 @@ if __name__ == "__main__":
     ap.add_argument("--cmd", default="")
     ap.add_argument("--per", type=float, default=1.0)
     ap.add_argument("--match", nargs="*", default=None)
+    ap.add_argument("--exclude", nargs="*", default=None)
     ap.add_argument("--top", type=int, default=30)
     a = ap.parse_args()
-    print(summarise(a.db, a.title, a.cmd, a.per, a.match, a.top))
+    print(summarise(a.db, a.title, a.cmd, a.per, a.match, a.top, a.exclude))
