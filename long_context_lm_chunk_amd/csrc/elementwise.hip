@@ -411,6 +411,30 @@ __global__ void ce_rows_k(const float* __restrict__ pmax, const float* __restric
   }
 }
 
+// Gradient of the mean CE with respect to the logits, from stored fp32
+// logits: g = (exp(z - lse) - onehot(target)) / n_tgt on target rows, 0 on
+// the others; four columns per thread (V % 4 == 0).
+template <typename T>
+__global__ void ce_grad_k(const float* __restrict__ z, int64_t ldz, const float* __restrict__ lse,
+                          const int* __restrict__ tgt, int n_rows, int n_tgt, int V, float alpha,
+                          T* __restrict__ g, int64_t ldg) {
+  const int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;   // 4-column groups
+  const int64_t total = (int64_t)n_rows * (V / 4);
+  if (idx >= total) return;
+  const int row = (int)(idx / (V / 4)), col = (int)(idx % (V / 4)) * 4;
+  float4 o = {0.f, 0.f, 0.f, 0.f};
+  if (row < n_tgt) {
+    const float4 v = *reinterpret_cast<const float4*>(z + (int64_t)row * ldz + col);
+    const float l = lse[row];
+    const int t = tgt[row];
+    o.x = (__expf(v.x - l) - (col == t ? 1.f : 0.f)) * alpha;
+    o.y = (__expf(v.y - l) - (col + 1 == t ? 1.f : 0.f)) * alpha;
+    o.z = (__expf(v.z - l) - (col + 2 == t ? 1.f : 0.f)) * alpha;
+    o.w = (__expf(v.w - l) - (col + 3 == t ? 1.f : 0.f)) * alpha;
+  }
+  store4v<T>(g + (int64_t)row * ldg + col, o);
+}
+
 // Deterministic mean over the target rows; flags a non-finite loss.
 __global__ void ce_mean_k(const float* __restrict__ rowloss, int n_tgt, float* __restrict__ out,
                           int* __restrict__ err) {
@@ -576,6 +600,14 @@ void ce_finish(const float* part_max, const float* part_sum, int nparts, int64_t
   hipLaunchKernelGGL(ce_rows_k, dim3(nblk(n_rows, 4)), dim3(256), 0, s, part_max, part_sum, nparts, ldpart,
                      tgt_logit, n_rows, n_tgt, lse, rowloss);
   hipLaunchKernelGGL(ce_mean_k, dim3(1), dim3(1024), 0, s, rowloss, n_tgt, loss_out, err);
+}
+
+void ce_grad(const float* z, int64_t ldz, const float* lse, const int* tgt, int n_rows, int n_tgt,
+             int V, float alpha, void* g, int64_t ldg, bool bf, hipStream_t s) {
+  const int64_t total = (int64_t)n_rows * (V / 4);
+  if (total <= 0) return;
+  TSEL(bf, hipLaunchKernelGGL(ce_grad_k<bf16>, dim3((unsigned)nblk(total, 256)), dim3(256), 0, s, z, ldz, lse, tgt, n_rows, n_tgt, V, alpha, (bf16*)g, ldg),
+       hipLaunchKernelGGL(ce_grad_k<float>, dim3((unsigned)nblk(total, 256)), dim3(256), 0, s, z, ldz, lse, tgt, n_rows, n_tgt, V, alpha, (float*)g, ldg));
 }
 
 void attn_rowdot(const void* o, const void* dout, int n, int H, int hd, float* D, bool bf,

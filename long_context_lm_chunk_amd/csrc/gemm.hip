@@ -20,7 +20,8 @@
 //           act = silu(gate) * up
 //   SGD     delta_f32 -= lr * acc ; delta copy = round(delta) ;
 //           current = round(W0 + delta)                    (fast weights)
-//   CESTAT  per-row partial max / sum(exp) of the logits and the target logit
+//   CESTAT  per-row partial max / sum(exp) of the logits and the target logit;
+//           with C set, also the logits (fp32)
 //   CEGRAD  g = (softmax - onehot(target)) / n_targets, rows without a target 0
 #include "common.hpp"
 #include "kernels.hpp"
@@ -389,6 +390,8 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(GemmParams p) {
           const int col = cbase + j * 16;
           if (col < p.N) s += __expf(acc[i][j][e] - mx);
           if (col == t) { tv = acc[i][j][e]; has = true; }
+          // the logits themselves, for the gradient pass (optional)
+          if (p.C && row < p.M && col < p.N) static_cast<float*>(p.C)[(int64_t)row * p.ldc + col] = acc[i][j][e];
         }
 #pragma unroll
         for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o, 64);

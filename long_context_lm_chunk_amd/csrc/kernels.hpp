@@ -68,6 +68,10 @@ void ce_finish(const float* part_max, const float* part_sum, int nparts, int64_t
                int* err, hipStream_t s);
 void attn_rowdot(const void* o, const void* dout, int n, int H, int hd, float* D, bool bf16,
                  hipStream_t s);
+// g = (exp(z - lse) - onehot(tgt)) * alpha on rows < n_tgt, 0 on the other
+// rows < n_rows; z fp32 logits [n_rows][ldz], g [n_rows][ldg], V % 4 == 0
+void ce_grad(const float* z, int64_t ldz, const float* lse, const int* tgt, int n_rows, int n_tgt,
+             int V, float alpha, void* g, int64_t ldg, bool bf16, hipStream_t s);
 
 // ---- attention (attention.hip)
 struct AttnParams {

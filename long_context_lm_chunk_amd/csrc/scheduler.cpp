@@ -138,6 +138,7 @@ struct ttt_model {
   float* xL = nullptr; float* meanf = nullptr; float* rstdf = nullptr; void* fN = nullptr;
   void* qkvB = nullptr;
   float* pmax = nullptr; float* psum = nullptr; float* tlog = nullptr; float* lse_ce = nullptr;
+  float* zce = nullptr;                 // the chunk's logits [C][V] fp32 (head statistics pass)
   void* G = nullptr;
   float* dh = nullptr; void* dh_lo = nullptr; float* dact = nullptr; void* dz = nullptr;
   // transposed operands of the weight-gradient products, one set per fast
@@ -289,6 +290,7 @@ size_t layout(ttt_model* m, void* base) {
   m->tlog = cv.take<float>((size_t)C * 4);
   m->lse_ce = cv.take<float>((size_t)2 * C * 4);
   m->G = cv.take<void>((size_t)C * V * es);
+  m->zce = cv.take<float>((size_t)C * V * 4);
   m->dh = cv.take<float>((size_t)C * d * 4);
   m->dh_lo = cv.take<void>((size_t)C * d * es);
   // transposed operands of the weight-gradient products: [features][Cp],
@@ -517,17 +519,16 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
     gs.A = m->fN; gs.lda = d; gs.B = m->U; gs.ldb = d; gs.M = n; gs.N = V; gs.K = d;
     gs.tgt = tgt; gs.n_tgt = n_tgt; gs.part_max = m->pmax; gs.part_sum = m->psum;
     gs.ldpart = m->Cmax; gs.tgt_logit = m->tlog;
+    gs.C = m->zce; gs.ldc = V;      // logits kept for the gradient pass
     if (gemm(gs, bf, true, true, EPI_CESTAT, true, s)) return fail(TTT_ERR_CONFIG, "internal: CE variant");
     ce_finish(m->pmax, m->psum, m->nparts, m->Cmax, m->tlog, n, n_tgt, m->lse_ce, loss_out, m->err, s);
   }
   if (n_tgt <= 0) return TTT_OK;   // nothing to learn from this chunk
   {
-    Scope t(m, CLS_CE, s, 4.0 * n * (double)d * V);
-    GemmParams gg;
-    gg.A = m->fN; gg.lda = d; gg.B = m->U; gg.ldb = d; gg.M = n; gg.N = V; gg.K = d;
-    gg.C = m->G; gg.ldc = V; gg.tgt = tgt; gg.n_tgt = n_tgt; gg.lse = m->lse_ce;
-    gg.alpha = 1.f / (float)n_tgt;
-    if (gemm(gg, bf, true, true, EPI_CEGRAD, false, s)) return fail(TTT_ERR_CONFIG, "internal: CE variant");
+    Scope t(m, CLS_CE, s, 2.0 * n * (double)d * V);
+    // G = (softmax - onehot) / n_targets from the stored logits (a stream
+    // over C x V instead of recomputing the logits product)
+    ce_grad(m->zce, V, m->lse_ce, tgt, n, n_tgt, V, 1.f / (float)n_tgt, m->G, V, bf, s);
     GemmParams gx;   // dHf = G . U  (through U^T [d][V], k-contiguous over the vocabulary)
     gx.A = m->G; gx.lda = V; gx.B = m->UT; gx.ldb = V; gx.M = n; gx.N = d; gx.K = V;
     gx.C = m->dtmp; gx.ldc = d;
