@@ -245,35 +245,6 @@ __global__ void swa_combine_k(AttnParams p, int nsplit) {
 }
 
 
-// Transposed ring copy: rows h*hd + i, column (position mod cap), or its
-// key-permuted column (perm != 0, see kperm); one block per 64 positions of
-// one head, transposed through LDS so both sides coalesce.  The source row
-// of position t is src + t*ld (linear) or, for a ring source (src_cap > 0),
-// src + ((pos0 + t) mod src_cap) * ld.
-template <typename T>
-__global__ __launch_bounds__(256) void ring_tr_k(const T* __restrict__ src, int64_t ld, int64_t src_cap,
-                                                 int n, int H, int hd, int64_t pos0, T* __restrict__ dst,
-                                                 int64_t cap, int perm) {
-  __shared__ T tile[64][128 + 2];
-  const int h = blockIdx.y, t0 = blockIdx.x * 64, tid = threadIdx.x;
-  for (int idx = tid; idx < 64 * hd; idx += 256) {
-    const int t = idx / hd, i = idx % hd;
-    T v = from_f32<T>(0.f);
-    if (t0 + t < n) {
-      const int64_t r = src_cap > 0 ? (pos0 + t0 + t) % src_cap : (int64_t)(t0 + t);
-      v = src[r * ld + h * hd + i];
-    }
-    tile[t][i] = v;
-  }
-  __syncthreads();
-  for (int idx = tid; idx < hd * 64; idx += 256) {
-    const int i = idx / 64, t = idx % 64;
-    if (t0 + t < n) {
-      const int64_t sl = (pos0 + t0 + t) % cap;
-      dst[(int64_t)(h * hd + i) * cap + (perm ? kperm(sl) : sl)] = tile[t][i];
-    }
-  }
-}
 
 // ------------------------------------------------------------ backward dQ
 // dQ = scale * sum_keys dS K with dS = P (dP - D), P = exp(S - LSE),
@@ -1214,14 +1185,6 @@ void bwd_t(const AttnParams& p, hipStream_t s, hipStream_t s2) {
 void swa_fwd(const AttnParams& p, bool bf, hipStream_t s) {
   if (p.n <= 0) return;
   if (bf) fwd_t<bf16>(p, s); else fwd_t<float>(p, s);
-}
-void ring_transpose(const void* src, int64_t ld, int64_t src_cap, int n, int H, int hd, int64_t pos0,
-                    void* dst, int64_t cap, bool key_perm, bool bf, hipStream_t s) {
-  if (n <= 0) return;
-  dim3 grid((n + 63) / 64, H);
-  const int pm = key_perm ? 1 : 0;
-  if (bf) hipLaunchKernelGGL(ring_tr_k<bf16>, grid, dim3(256), 0, s, (const bf16*)src, ld, src_cap, n, H, hd, pos0, (bf16*)dst, cap, pm);
-  else hipLaunchKernelGGL(ring_tr_k<float>, grid, dim3(256), 0, s, (const float*)src, ld, src_cap, n, H, hd, pos0, (float*)dst, cap, pm);
 }
 
 void swa_bwd(const AttnParams& p, bool bf, hipStream_t s, hipStream_t s_kv) {

@@ -218,34 +218,150 @@ __global__ void fill_k(float* __restrict__ p, int64_t n, float v) {
     p[i] = v;
 }
 
-// qkv [n][3*H*hd]; writes q_out [n][H*hd] (rotated), K (rotated) and V to
-// ring slot (pos0 + t) mod cap.  One thread per (t, h, i < hd/2).
+
+// cos / sin of the rotary angle (pos0 + t) * theta_i for t < n, i < half,
+// formed in float64 (rope_cs) once per block of positions and shared by
+// every layer and head that reads those positions.
+__global__ void rope_table_k(int64_t pos0, int n, int half, const double* __restrict__ theta,
+                             float2* __restrict__ cs) {
+  const int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)n * half) return;
+  const int t = (int)(idx / half), i = (int)(idx % half);
+  float c, s;
+  rope_cs(pos0 + t, theta, i, c, s);
+  cs[idx] = make_float2(c, s);
+}
+
+template <typename T> DEVI void ld8(const T* p, float* v);
+template <> DEVI void ld8<bf16>(const bf16* p, float* v) {
+  const bf16x8 x = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = static_cast<float>(x[j]);
+}
+template <> DEVI void ld8<float>(const float* p, float* v) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+template <typename T> DEVI void st8(T* p, const float* v);
+template <> DEVI void st8<bf16>(bf16* p, const float* v) {
+  bf16x8 x;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = static_cast<bf16>(v[j]);
+  *reinterpret_cast<bf16x8*>(p) = x;
+}
+template <> DEVI void st8<float>(float* p, const float* v) {
+  reinterpret_cast<float4*>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
+  reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+// Rotary embedding of 64 positions of one head, in work items of 8 rotation
+// pairs with 16-byte (bf16) accesses: q -> q_out [n][H*hd]; k (rotated) and
+// v -> ring row (pos0 + t) mod cap; then, through one LDS tile, v and (when
+// kt is set) k -> the position-permuted transposed rings [H*hd][cap] (the
+// column of a slot is kperm(slot)).  qkv [n][3*H*hd]; hd <= 128, hd % 16 == 0.
 template <typename T>
-__global__ void rope_qkv_k(const T* __restrict__ qkv, int n, int H, int hd, int64_t pos0,
-                           const double* __restrict__ theta, T* __restrict__ qo, T* __restrict__ kr,
-                           T* __restrict__ vr, int64_t cap) {
-  const int half = hd >> 1;
-  const int64_t total = (int64_t)n * H * half;
+__global__ __launch_bounds__(256) void qkv_rope_k(const T* __restrict__ qkv, int n, int H, int hd,
+                                                  int64_t pos0, const float2* __restrict__ cs,
+                                                  T* __restrict__ qo, T* __restrict__ kr, T* __restrict__ vr,
+                                                  T* __restrict__ vt, T* __restrict__ kt, int64_t cap) {
+  constexpr int NI = 2;                        // work items per thread (64 positions x <= 8 chunks)
+  __shared__ T tile[64][128 + 2];
+  const int h = blockIdx.y, t0 = blockIdx.x * 64, tid = threadIdx.x;
+  const int half = hd >> 1, nc = half / 8, d = H * hd;
+  float kv[NI][16];
+#pragma unroll
+  for (int u = 0; u < NI; ++u) {
+    const int it = tid + 256 * u;
+    const int t = it / nc, c = it % nc, i0 = 8 * c;
+    if (it >= 64 * nc || t0 + t >= n) continue;
+    const int64_t slot = (pos0 + t0 + t) % cap;
+    const T* row = qkv + (int64_t)(t0 + t) * 3 * d + h * hd;
+    const float2* e = cs + (int64_t)(t0 + t) * half + i0;
+    float a[8], b[8], ra[8], rb[8];
+    ld8<T>(row + i0, a);
+    ld8<T>(row + half + i0, b);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float2 w = e[j];
+      ra[j] = a[j] * w.x - b[j] * w.y;
+      rb[j] = b[j] * w.x + a[j] * w.y;
+    }
+    T* qr = qo + (int64_t)(t0 + t) * d + h * hd;
+    st8<T>(qr + i0, ra);
+    st8<T>(qr + half + i0, rb);
+    ld8<T>(row + d + i0, a);
+    ld8<T>(row + d + half + i0, b);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float2 w = e[j];
+      kv[u][j] = a[j] * w.x - b[j] * w.y;
+      kv[u][8 + j] = b[j] * w.x + a[j] * w.y;
+    }
+    T* krow = kr + slot * d + h * hd;
+    st8<T>(krow + i0, kv[u]);
+    st8<T>(krow + half + i0, kv[u] + 8);
+    ld8<T>(row + 2 * d + i0, a);
+    ld8<T>(row + 2 * d + half + i0, b);
+    T* vrow = vr + slot * d + h * hd;
+    st8<T>(vrow + i0, a);
+    st8<T>(vrow + half + i0, b);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      tile[t][i0 + j] = from_f32<T>(a[j]);
+      tile[t][half + i0 + j] = from_f32<T>(b[j]);
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < hd * 64; idx += 256) {
+    const int i = idx / 64, t = idx % 64;
+    if (t0 + t < n) vt[(int64_t)(h * hd + i) * cap + kperm((pos0 + t0 + t) % cap)] = tile[t][i];
+  }
+  if (!kt) return;
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < NI; ++u) {
+    const int it = tid + 256 * u;
+    const int t = it / nc, c = it % nc, i0 = 8 * c;
+    if (it >= 64 * nc || t0 + t >= n) continue;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      tile[t][i0 + j] = from_f32<T>(kv[u][j]);
+      tile[t][half + i0 + j] = from_f32<T>(kv[u][8 + j]);
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < hd * 64; idx += 256) {
+    const int i = idx / 64, t = idx % 64;
+    if (t0 + t < n) kt[(int64_t)(h * hd + i) * cap + kperm((pos0 + t0 + t) % cap)] = tile[t][i];
+  }
+}
+
+// Transposed rotation of dQ and dK inside dqkv [n][3d] (the rotation's
+// transpose), 8 pairs per thread with 16-byte accesses, angles from the table.
+template <typename T>
+__global__ void rope_bwd_tab_k(T* __restrict__ g, int n, int H, int hd, const float2* __restrict__ cs) {
+  const int half = hd >> 1, nc = half / 8;
+  const int64_t total = (int64_t)n * H * nc;
   const int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (idx >= total) return;
-  const int i = idx % half;
-  const int h = (idx / half) % H;
-  const int t = idx / ((int64_t)half * H);
-  const int d = H * hd;
-  const int64_t pos = pos0 + t;
-  float c, s;
-  rope_cs(pos, theta, i, c, s);
-  const T* row = qkv + (int64_t)t * 3 * d;
-  const int j1 = h * hd + i, j2 = j1 + half;
-  const float q1 = to_f32(row[j1]), q2 = to_f32(row[j2]);
-  const float k1 = to_f32(row[d + j1]), k2 = to_f32(row[d + j2]);
-  qo[(int64_t)t * d + j1] = from_f32<T>(q1 * c - q2 * s);
-  qo[(int64_t)t * d + j2] = from_f32<T>(q2 * c + q1 * s);
-  const int64_t slot = pos % cap;
-  kr[slot * d + j1] = from_f32<T>(k1 * c - k2 * s);
-  kr[slot * d + j2] = from_f32<T>(k2 * c + k1 * s);
-  vr[slot * d + j1] = row[2 * d + j1];
-  vr[slot * d + j2] = row[2 * d + j2];
+  const int c = (int)(idx % nc), h = (int)((idx / nc) % H), t = (int)(idx / ((int64_t)nc * H));
+  const int d = H * hd, i0 = 8 * c;
+  const float2* e = cs + (int64_t)t * half + i0;
+#pragma unroll
+  for (int part = 0; part < 2; ++part) {
+    T* r = g + (int64_t)t * 3 * d + part * d + h * hd;
+    float a[8], b[8], ra[8], rb[8];
+    ld8<T>(r + i0, a);
+    ld8<T>(r + half + i0, b);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float2 w = e[j];
+      ra[j] = a[j] * w.x + b[j] * w.y;
+      rb[j] = b[j] * w.x - a[j] * w.y;
+    }
+    st8<T>(r + i0, ra);
+    st8<T>(r + half + i0, rb);
+  }
 }
 
 // dst[c][r] = src[r][c] for r < rows, c < cols; rows rows..rows_pad-1 of
@@ -272,30 +388,6 @@ __global__ __launch_bounds__(256) void transpose_k(const T* __restrict__ src, in
   }
 }
 
-// Transposed rotation of dQ and dK inside dqkv [n][3d].
-template <typename T>
-__global__ void rope_bwd_k(T* __restrict__ g, int n, int H, int hd, int64_t pos0,
-                           const double* __restrict__ theta) {
-  const int half = hd >> 1;
-  const int64_t total = (int64_t)n * H * half;
-  const int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (idx >= total) return;
-  const int i = idx % half;
-  const int h = (idx / half) % H;
-  const int t = idx / ((int64_t)half * H);
-  const int d = H * hd;
-  float c, s;
-  rope_cs(pos0 + t, theta, i, c, s);
-  T* row = g + (int64_t)t * 3 * d;
-  const int j1 = h * hd + i, j2 = j1 + half;
-#pragma unroll
-  for (int part = 0; part < 2; ++part) {
-    T* r = row + part * d;
-    const float a = to_f32(r[j1]), b = to_f32(r[j2]);
-    r[j1] = from_f32<T>(a * c + b * s);
-    r[j2] = from_f32<T>(b * c - a * s);
-  }
-}
 
 // dz from dact (fp32 [n][F]) and the saved pre-activations.
 // SwiGLU: z [n][2F] with gate/up in alternating blocks of 16 columns.
@@ -543,12 +635,18 @@ void fill_f32(float* p, int64_t n, float v, hipStream_t s) {
   hipLaunchKernelGGL(fill_k, dim3(gs_blocks(n)), dim3(256), 0, s, p, n, v);
 }
 
-void rope_qkv(const void* qkv, int n, int H, int hd, int64_t pos0, const double* theta, void* q_out,
-              void* kring, void* vring, int64_t cap, bool bf, hipStream_t s) {
-  const int64_t total = (int64_t)n * H * (hd / 2);
+void rope_table(int64_t pos0, int n, int half, const double* theta, float2* cs, hipStream_t s) {
+  const int64_t total = (int64_t)n * half;
   if (total <= 0) return;
-  TSEL(bf, hipLaunchKernelGGL(rope_qkv_k<bf16>, dim3(nblk(total, 256)), dim3(256), 0, s, (const bf16*)qkv, n, H, hd, pos0, theta, (bf16*)q_out, (bf16*)kring, (bf16*)vring, cap),
-       hipLaunchKernelGGL(rope_qkv_k<float>, dim3(nblk(total, 256)), dim3(256), 0, s, (const float*)qkv, n, H, hd, pos0, theta, (float*)q_out, (float*)kring, (float*)vring, cap));
+  hipLaunchKernelGGL(rope_table_k, dim3(nblk(total, 256)), dim3(256), 0, s, pos0, n, half, theta, cs);
+}
+
+void qkv_rope(const void* qkv, int n, int H, int hd, int64_t pos0, const float2* cs, void* q_out,
+              void* kring, void* vring, void* vtring, void* ktring, int64_t cap, bool bf, hipStream_t s) {
+  if (n <= 0) return;
+  dim3 grid((n + 63) / 64, H);
+  TSEL(bf, hipLaunchKernelGGL(qkv_rope_k<bf16>, grid, dim3(256), 0, s, (const bf16*)qkv, n, H, hd, pos0, cs, (bf16*)q_out, (bf16*)kring, (bf16*)vring, (bf16*)vtring, (bf16*)ktring, cap),
+       hipLaunchKernelGGL(qkv_rope_k<float>, grid, dim3(256), 0, s, (const float*)qkv, n, H, hd, pos0, cs, (float*)q_out, (float*)kring, (float*)vring, (float*)vtring, (float*)ktring, cap));
 }
 
 void transpose(const void* src, int rows, int cols, int64_t lds_, void* dst, int64_t ldd, int rows_pad,
@@ -561,12 +659,11 @@ void transpose(const void* src, int rows, int cols, int64_t lds_, void* dst, int
        hipLaunchKernelGGL(transpose_k<float>, grid, dim3(256), 0, s, (const float*)src, rows, cols, lds_, (float*)dst, ldd, rows_pad, pm));
 }
 
-void rope_bwd(void* dqkv, int n, int H, int hd, int64_t pos0, const double* theta, bool bf,
-              hipStream_t s) {
-  const int64_t total = (int64_t)n * H * (hd / 2);
+void rope_bwd(void* dqkv, int n, int H, int hd, const float2* cs, bool bf, hipStream_t s) {
+  const int64_t total = (int64_t)n * H * (hd / 16);
   if (total <= 0) return;
-  TSEL(bf, hipLaunchKernelGGL(rope_bwd_k<bf16>, dim3(nblk(total, 256)), dim3(256), 0, s, (bf16*)dqkv, n, H, hd, pos0, theta),
-       hipLaunchKernelGGL(rope_bwd_k<float>, dim3(nblk(total, 256)), dim3(256), 0, s, (float*)dqkv, n, H, hd, pos0, theta));
+  TSEL(bf, hipLaunchKernelGGL(rope_bwd_tab_k<bf16>, dim3(nblk(total, 256)), dim3(256), 0, s, (bf16*)dqkv, n, H, hd, cs),
+       hipLaunchKernelGGL(rope_bwd_tab_k<float>, dim3(nblk(total, 256)), dim3(256), 0, s, (float*)dqkv, n, H, hd, cs));
 }
 
 void act_bwd(const float* dact, const void* z, int n, int F, bool swiglu, void* dz, bool bf,

@@ -49,10 +49,16 @@ void layernorm_bwd_acc(const float* dy, const float* x, const float* mean, const
                        int d, float* acc, void* acc_lo, bool bf16, hipStream_t s);
 // acc_lo = low-precision copy of acc
 void cast_rows(const float* src, void* dst, int64_t n, bool bf16, hipStream_t s);
-void rope_qkv(const void* qkv, int n, int H, int hd, int64_t pos0, const double* theta, void* q_out,
-              void* kring, void* vring, int64_t cap, bool bf16, hipStream_t s);
-void rope_bwd(void* dqkv, int n, int H, int hd, int64_t pos0, const double* theta, bool bf16,
-              hipStream_t s);
+// cs[t][i] = (cos, sin) of (pos0 + t) * theta[i], angle in float64, t < n, i < half
+void rope_table(int64_t pos0, int n, int half, const double* theta, float2* cs, hipStream_t s);
+// q (rotated) -> q_out [n][H*hd]; k (rotated), v -> rings at slot
+// (pos0 + t) mod cap; v and (when ktring is set) k also to the transposed
+// rings [H*hd][cap], column kperm(slot); cs from rope_table(pos0, n, hd/2).
+// hd <= 128, hd % 16 == 0, cap % 16 == 0
+void qkv_rope(const void* qkv, int n, int H, int hd, int64_t pos0, const float2* cs, void* q_out,
+              void* kring, void* vring, void* vtring, void* ktring, int64_t cap, bool bf16, hipStream_t s);
+// the rotation's transpose applied to dQ and dK inside dqkv [n][3*H*hd]
+void rope_bwd(void* dqkv, int n, int H, int hd, const float2* cs, bool bf16, hipStream_t s);
 void act_bwd(const float* dact, const void* z, int n, int F, bool swiglu, void* dz, bool bf16,
              hipStream_t s);
 void convert_weight(const void* src, int rows, int cols, bool transpose, int interleave16_half,
@@ -78,7 +84,7 @@ struct AttnParams {
   const void* q = nullptr;   // [n][H*hd], row stride ldq
   int64_t ldq = 0;
   const void* kring = nullptr; const void* vring = nullptr;  // [cap][H*hd]
-  // [H*hd][cap] transposed copies, key-permuted (see ring_transpose)
+  // [H*hd][cap] transposed copies, columns permuted by kperm (written by qkv_rope)
   const void* vtring = nullptr;                               // V (forward)
   const void* ktring = nullptr;                               // K (dQ)
   int64_t cap = 0;
@@ -99,12 +105,6 @@ struct AttnParams {
   float* part = nullptr; float* part_ml = nullptr; int max_split = 1;
 };
 void swa_fwd(const AttnParams& p, bool bf16, hipStream_t s);
-// rows of positions [pos0, pos0+n) (src row t at src + t*ld, or at slot
-// (pos0+t) mod src_cap of a ring) into a transposed ring [H*hd][cap]; with
-// key_perm the columns are permuted inside aligned groups of 16 slots (the
-// dQ product's operand order; cap % 16 == 0)
-void ring_transpose(const void* src, int64_t ld, int64_t src_cap, int n, int H, int hd, int64_t pos0,
-                    void* dst, int64_t cap, bool key_perm, bool bf16, hipStream_t s);
 // dQ on s, dK/dV on s_kv (the two are independent; the caller orders s_kv
 // after the inputs and joins it before using dK/dV; s_kv may equal s)
 void swa_bwd(const AttnParams& p, bool bf16, hipStream_t s, hipStream_t s_kv);

@@ -124,6 +124,7 @@ struct ttt_model {
   std::vector<Layer> layers;
   std::vector<FastLayer> fast;
   double* theta = nullptr;
+  float2* csA = nullptr; float2* csB = nullptr;   // rotary cos/sin of a phase-A block / a chunk
   // phase A
   // phase A runs on its own stream, one block ahead of phase B; its output
   // block is double-buffered (hAb[block % 2]); hA = hAb[0] also serves as the
@@ -150,7 +151,6 @@ struct ttt_model {
   hipStream_t sc = nullptr;             // fast-weight updates (SGD products)
   std::vector<hipEvent_t> evT1, evT2;   // per fast block: update operands ready
   std::vector<hipEvent_t> evR1, evR2;   // per fast block: dh_lo / dz read by the update stream
-  std::vector<hipEvent_t> evKT;         // per fast block: transposed K ring copy done
   hipEvent_t evC = nullptr;             // all updates of the chunk done
   hipStream_t sk = nullptr;             // dK/dV of the attention backward, beside dQ
   hipEvent_t evK0 = nullptr, evK1 = nullptr;
@@ -249,6 +249,8 @@ size_t layout(ttt_model* m, void* base) {
     f.ct_dn = cv.take<void>((size_t)d * F * es);
   }
   m->theta = cv.take<double>((size_t)(m->hd / 2) * 8);
+  m->csA = cv.take<float2>((size_t)MA * (m->hd / 2) * 8);
+  m->csB = cv.take<float2>((size_t)C * (m->hd / 2) * 8);
   // phase A
   m->hAb[0] = cv.take<float>((size_t)MA * d * 4);
   m->hAb[1] = cv.take<float>((size_t)MA * d * 4);
@@ -418,6 +420,7 @@ int phase_a(ttt_model* m, const int32_t* tokens, int64_t B0, int nb, float* hA, 
   const int d = m->d, F = m->F, F2 = m->F2;
   const bool bf = m->bf;
   embed(tokens + B0, nb, m->E, d, m->V, bf, hA, m->err, s);
+  rope_table(B0, nb, m->hd / 2, m->theta, m->csA, s);
   for (int l = 0; l <= m->f0; ++l) {
     Layer& ly = m->layers[l];
     layernorm_fwd(hA, d, nb, d, m->c.ln_eps, m->aA, d, nullptr, nullptr, bf, s);
@@ -425,9 +428,8 @@ int phase_a(ttt_model* m, const int32_t* tokens, int64_t B0, int nb, float* hA, 
     g.A = m->aA; g.lda = d; g.B = ly.wqkv; g.ldb = d; g.M = nb; g.N = 3 * d; g.K = d;
     g.C = m->qkvA; g.ldc = 3 * d;
     int rc = run_gemm(m, g, true, true, EPI_STORE, false, s, false); if (rc) return rc;
-    rope_qkv(m->qkvA, nb, m->H, m->hd, B0, m->theta, m->qA, ly.kring, ly.vring, ly.cap, bf, s);
-    ring_transpose(static_cast<char*>(m->qkvA) + (size_t)2 * d * m->es, 3 * d, 0, nb, m->H, m->hd, B0,
-                   ly.vtring, ly.cap, true, bf, s);
+    qkv_rope(m->qkvA, nb, m->H, m->hd, B0, m->csA, m->qA, ly.kring, ly.vring, ly.vtring, nullptr, ly.cap,
+             bf, s);
     AttnParams ap;
     ap.q = m->qA; ap.ldq = d; ap.kring = ly.kring; ap.vring = ly.vring; ap.vtring = ly.vtring; ap.cap = ly.cap;
     ap.n = nb; ap.H = m->H; ap.hd = m->hd; ap.window = m->W; ap.pos0 = B0; ap.o = m->oA; ap.ldo = d;
@@ -464,6 +466,7 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
   const float eps = m->c.ln_eps;
   const int upepi = m->c.mlp == TTT_MLP_SWIGLU ? EPI_SWIGLU : EPI_GELU;
   int rc;
+  rope_table(p0, n, m->hd / 2, m->theta, m->csB, s);
   // ---------------- forward of the fast blocks
   for (int j = 0; j < q; ++j) {
     const int l = m->f0 + j;
@@ -476,15 +479,8 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
       g.A = b.a; g.lda = d; g.B = ly.wqkv; g.ldb = d; g.M = n; g.N = 3 * d; g.K = d;
       g.C = m->qkvB; g.ldc = 3 * d;
       rc = run_gemm(m, g, true, true, EPI_STORE, false, s); if (rc) return rc;
-      rope_qkv(m->qkvB, n, m->H, m->hd, p0, m->theta, b.q, ly.kring, ly.vring, ly.cap, bf, s);
-      ring_transpose(static_cast<char*>(m->qkvB) + (size_t)2 * d * m->es, 3 * d, 0, n, m->H, m->hd, p0,
-                     ly.vtring, ly.cap, true, bf, s);
-      // the transposed K copy is only read by this block's dQ, much later in
-      // the chunk: make it on the dK/dV stream, off the chain
-      HIPCHK(hipEventRecord(m->evKT[j], s));
-      HIPCHK(hipStreamWaitEvent(m->sk, m->evKT[j], 0));
-      ring_transpose(ly.kring, d, ly.cap, n, m->H, m->hd, p0, ly.ktring, ly.cap, true, bf, m->sk);
-      HIPCHK(hipEventRecord(m->evKT[j], m->sk));
+      qkv_rope(m->qkvB, n, m->H, m->hd, p0, m->csB, b.q, ly.kring, ly.vring, ly.vtring, ly.ktring, ly.cap,
+               bf, s);
       AttnParams ap;
       ap.q = b.q; ap.ldq = d; ap.kring = ly.kring; ap.vring = ly.vring; ap.vtring = ly.vtring; ap.cap = ly.cap;
       ap.n = n; ap.H = m->H; ap.hd = m->hd; ap.window = m->W; ap.pos0 = p0; ap.o = b.o; ap.ldo = d;
@@ -609,7 +605,6 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
       double in = 0;
       const double tot = pairs(p0, n, m->W, p0, &in);
       Scope t(m, CLS_ATTN_BWD, s, 4.0 * d * (tot + in));
-      HIPCHK(hipStreamWaitEvent(s, m->evKT[j], 0));  // transposed K copy for dQ
       HIPCHK(hipEventRecord(m->evK0, s));            // inputs of dK/dV ready
       HIPCHK(hipStreamWaitEvent(m->sk, m->evK0, 0));
       if (swa_bwd_reads_transposes(m->hd, bf)) {
@@ -622,7 +617,7 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
       HIPCHK(hipEventRecord(m->evK1, m->sk));
       HIPCHK(hipStreamWaitEvent(s, m->evK1, 0));     // dK/dV in place for the RoPE backward
     }
-    rope_bwd(m->dqkv, n, m->H, m->hd, p0, m->theta, bf, s);
+    rope_bwd(m->dqkv, n, m->H, m->hd, m->csB, bf, s);
     GemmParams gq;   // da = dqkv . Wqkv  (Wqkv^T [d][3d])
     gq.A = m->dqkv; gq.lda = 3 * d; gq.B = ly.wqkvT; gq.ldb = 3 * d; gq.M = n; gq.N = d; gq.K = 3 * d;
     gq.C = m->dtmp; gq.ldc = d;
@@ -747,12 +742,11 @@ int ttt_model_load(const ttt_config* cfg, const void* const* weights, int32_t n_
     m->evT2.assign(m->q, nullptr);
     m->evR1.assign(m->q, nullptr);
     m->evR2.assign(m->q, nullptr);
-    m->evKT.assign(m->q, nullptr);
     std::vector<hipEvent_t*> evs = {&m->ev0, &m->evA[0], &m->evA[1], &m->evB[0], &m->evB[1], &m->evC,
                                     &m->evK0, &m->evK1};
     for (int j = 0; j < m->q; ++j) {
       evs.push_back(&m->evT1[j]); evs.push_back(&m->evT2[j]);
-      evs.push_back(&m->evR1[j]); evs.push_back(&m->evR2[j]); evs.push_back(&m->evKT[j]);
+      evs.push_back(&m->evR1[j]); evs.push_back(&m->evR2[j]);
     }
     for (auto* e : evs)
       if (e1 == hipSuccess) e1 = hipEventCreateWithFlags(e, hipEventDisableTiming);
@@ -953,7 +947,7 @@ void ttt_model_free(ttt_model* m) {
   if (m->sk) (void)hipStreamSynchronize(m->sk);
   std::vector<hipEvent_t> evs = {m->ev0, m->evA[0], m->evA[1], m->evB[0], m->evB[1], m->evC,
                                  m->evK0, m->evK1};
-  for (auto* v : {&m->evT1, &m->evT2, &m->evR1, &m->evR2, &m->evKT}) evs.insert(evs.end(), v->begin(), v->end());
+  for (auto* v : {&m->evT1, &m->evT2, &m->evR1, &m->evR2}) evs.insert(evs.end(), v->begin(), v->end());
   for (auto e : evs)
     if (e) (void)hipEventDestroy(e);
   if (m->sa) (void)hipStreamDestroy(m->sa);
