@@ -288,6 +288,19 @@ DEVI int64_t kperm(int64_t s) {
   return (s & ~(int64_t)15) | (o < 4 || o >= 12 ? o : (o < 8 ? o + 4 : o - 4));
 }
 
+// Activation backward, shared by the standalone and the GEMM-epilogue forms:
+// SwiGLU act = silu(g) * u -> (d/dg, d/du); GELU (erf) -> d/dv.
+DEVI void swiglu_bwd(float da, float g, float u, float& dg, float& du) {
+  const float sg = 1.f / (1.f + __expf(-g));
+  dg = da * u * sg * (1.f + g * (1.f - sg));
+  du = da * g * sg;
+}
+DEVI float gelu_bwd(float v, float d) {
+  const float cdf = 0.5f * (1.f + erff(v * 0.70710678118654752f));
+  const float pdf = 0.39894228040143268f * __expf(-0.5f * v * v);
+  return d * (cdf + v * pdf);
+}
+
 // 2^x with the hardware instruction (no denormal range fix-up; the inputs
 // here are <= 8 and results below 2^-126 may flush to zero).
 DEVI float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

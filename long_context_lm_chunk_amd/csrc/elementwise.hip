@@ -389,52 +389,6 @@ __global__ __launch_bounds__(256) void transpose_k(const T* __restrict__ src, in
 }
 
 
-// dz from dact (fp32 [n][F]) and the saved pre-activations.
-// SwiGLU: z [n][2F] with gate/up in alternating blocks of 16 columns.
-// dz from d(act) and the pre-activations z, four activations per thread
-// (SwiGLU: gate columns 32c..32c+15, up columns 32c+16..32c+31 of z and dz
-// for activations 16c..16c+15).  F % 4 == 0, n * F < 2^31.
-template <typename T>
-__global__ void act_bwd_k(const float* __restrict__ dact, const T* __restrict__ z, int n, int F,
-                          int swiglu, T* __restrict__ dz) {
-  const int idx = (blockIdx.x * blockDim.x + threadIdx.x) * 4;   // first of 4 activations
-  if (idx >= n * F) return;
-  const int t = idx / F, f = idx - t * F;
-  const float4 da = *reinterpret_cast<const float4*>(dact + idx);
-  if (swiglu) {
-    const int64_t cg = (int64_t)t * 2 * F + (f / 16) * 32 + (f % 16);
-    const float4 g = load4v<T>(z + cg), u = load4v<T>(z + cg + 16);
-    float4 dg, du;
-    {
-      const float sg = 1.f / (1.f + __expf(-g.x));
-      dg.x = da.x * u.x * sg * (1.f + g.x * (1.f - sg)); du.x = da.x * g.x * sg;
-    }
-    {
-      const float sg = 1.f / (1.f + __expf(-g.y));
-      dg.y = da.y * u.y * sg * (1.f + g.y * (1.f - sg)); du.y = da.y * g.y * sg;
-    }
-    {
-      const float sg = 1.f / (1.f + __expf(-g.z));
-      dg.z = da.z * u.z * sg * (1.f + g.z * (1.f - sg)); du.z = da.z * g.z * sg;
-    }
-    {
-      const float sg = 1.f / (1.f + __expf(-g.w));
-      dg.w = da.w * u.w * sg * (1.f + g.w * (1.f - sg)); du.w = da.w * g.w * sg;
-    }
-    store4v<T>(dz + cg, dg);
-    store4v<T>(dz + cg + 16, du);
-  } else {
-    const float4 zz = load4v<T>(z + idx);
-    auto gd = [](float v, float d) {
-      const float cdf = 0.5f * (1.f + erff(v * 0.70710678118654752f));
-      const float pdf = 0.39894228040143268f * __expf(-0.5f * v * v);
-      return d * (cdf + v * pdf);
-    };
-    float4 o;
-    o.x = gd(zz.x, da.x); o.y = gd(zz.y, da.y); o.z = gd(zz.z, da.z); o.w = gd(zz.w, da.w);
-    store4v<T>(dz + idx, o);
-  }
-}
 
 // Canonical [rows=in][cols=out] -> internal [out][in] (transpose), optionally
 // into the gate (half 0) or up (half 1) rows of a block-16 interleaved matrix.
@@ -666,13 +620,6 @@ void rope_bwd(void* dqkv, int n, int H, int hd, const float2* cs, bool bf, hipSt
        hipLaunchKernelGGL(rope_bwd_tab_k<float>, dim3(nblk(total, 256)), dim3(256), 0, s, (float*)dqkv, n, H, hd, cs));
 }
 
-void act_bwd(const float* dact, const void* z, int n, int F, bool swiglu, void* dz, bool bf,
-             hipStream_t s) {
-  const int64_t total = (int64_t)n * F;   // F % 16 == 0 (a configuration rule), n * F < 2^31
-  if (total <= 0) return;
-  TSEL(bf, hipLaunchKernelGGL(act_bwd_k<bf16>, dim3(nblk(total / 4, 256)), dim3(256), 0, s, dact, (const bf16*)z, n, F, (int)swiglu, (bf16*)dz),
-       hipLaunchKernelGGL(act_bwd_k<float>, dim3(nblk(total / 4, 256)), dim3(256), 0, s, dact, (const float*)z, n, F, (int)swiglu, (float*)dz));
-}
 
 void convert_weight(const void* src, int rows, int cols, bool transpose, int ilv, void* dst, bool bf,
                     hipStream_t s) {

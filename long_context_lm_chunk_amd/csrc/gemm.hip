@@ -23,6 +23,7 @@
 //   CESTAT  per-row partial max / sum(exp) of the logits and the target logit;
 //           with C set, also the logits (fp32)
 //   CEGRAD  g = (softmax - onehot(target)) / n_targets, rows without a target 0
+//   ACTBWD  d(pre-activation) from the product d(act) and the saved Z
 #include "common.hpp"
 #include "kernels.hpp"
 #include <type_traits>
@@ -267,6 +268,26 @@ DEVI void epi_apply(const GemmParams& p, float* st, int ES, int nr, int nc, int 
         store4<TO>(static_cast<TO*>(p.C) + ci, v);
         float4 a; a.x = gelu_erf(v.x); a.y = gelu_erf(v.y); a.z = gelu_erf(v.z); a.w = gelu_erf(v.w);
         store4<TO>(static_cast<TO*>(p.C2) + (int64_t)row * p.ldc2 + col, a);
+      } else if constexpr (EPI == EPI_ACTBWD) {
+        // v = d(act) of activations col..col+3 (four of one 16-block)
+        const TO* z = static_cast<const TO*>(p.Z) + (int64_t)row * p.ldz;
+        TO* dz = static_cast<TO*>(p.C) + (int64_t)row * p.ldc;
+        if (p.act_swiglu) {
+          const int cg = (col / 16) * 32 + (col % 16);
+          const float4 g = load4<TO>(z + cg), u = load4<TO>(z + cg + 16);
+          float4 dg, du;
+          swiglu_bwd(v.x, g.x, u.x, dg.x, du.x);
+          swiglu_bwd(v.y, g.y, u.y, dg.y, du.y);
+          swiglu_bwd(v.z, g.z, u.z, dg.z, du.z);
+          swiglu_bwd(v.w, g.w, u.w, dg.w, du.w);
+          store4<TO>(dz + cg, dg);
+          store4<TO>(dz + cg + 16, du);
+        } else {
+          const float4 zz = load4<TO>(z + col);
+          float4 o;
+          o.x = gelu_bwd(zz.x, v.x); o.y = gelu_bwd(zz.y, v.y); o.z = gelu_bwd(zz.z, v.z); o.w = gelu_bwd(zz.w, v.w);
+          store4<TO>(dz + col, o);
+        }
       } else if constexpr (EPI == EPI_CEGRAD) {
         float4 gq = {0.f, 0.f, 0.f, 0.f};
         if (row < p.n_tgt) {
@@ -723,6 +744,7 @@ int dispatch(const GemmParams& p, bool a_kc, bool b_kc, int epi, bool out_f32, h
       case EPI_SWIGLU: launch_t<T, true, true, EPI_SWIGLU, T>(p, s); return 0;
       case EPI_CESTAT: launch_t<T, true, true, EPI_CESTAT, float>(p, s); return 0;
       case EPI_CEGRAD: launch_t<T, true, true, EPI_CEGRAD, T>(p, s); return 0;
+      case EPI_ACTBWD: launch_t<T, true, true, EPI_ACTBWD, T>(p, s); return 0;
       case EPI_SGD: if (p.B2) return -1; launch_t<T, true, true, EPI_SGD, T>(p, s); return 0;
       default: return -1;
     }

@@ -5,7 +5,7 @@
 
 namespace ttt {
 
-enum Epi { EPI_STORE = 0, EPI_RESID, EPI_GELU, EPI_SWIGLU, EPI_SGD, EPI_CESTAT, EPI_CEGRAD };
+enum Epi { EPI_STORE = 0, EPI_RESID, EPI_GELU, EPI_SWIGLU, EPI_SGD, EPI_CESTAT, EPI_CEGRAD, EPI_ACTBWD };
 
 struct GemmParams {
   const void* A = nullptr; int64_t lda = 0;  // k-contiguous [M][K] or m-contiguous [K][M]
@@ -22,6 +22,10 @@ struct GemmParams {
   const int* tgt = nullptr; int n_tgt = 0;
   float* part_max = nullptr; float* part_sum = nullptr; int64_t ldpart = 0;
   float* tgt_logit = nullptr; const float* lse = nullptr;
+  // ACTBWD: the product is d(act); Z holds the saved pre-activations (row
+  // stride ldz; SwiGLU gate/up interleaved in blocks of 16, else GELU) and C
+  // receives d(pre-activation) in Z's layout (row stride ldc)
+  const void* Z = nullptr; int64_t ldz = 0; int act_swiglu = 0;
   // split-K scratch (optional; STORE/RESID launches with too few tiles):
   // split_ws holds up to split_cap floats
   float* split_ws = nullptr; int64_t split_cap = 0;
@@ -59,8 +63,6 @@ void qkv_rope(const void* qkv, int n, int H, int hd, int64_t pos0, const float2*
               void* kring, void* vring, void* vtring, void* ktring, int64_t cap, bool bf16, hipStream_t s);
 // the rotation's transpose applied to dQ and dK inside dqkv [n][3*H*hd]
 void rope_bwd(void* dqkv, int n, int H, int hd, const float2* cs, bool bf16, hipStream_t s);
-void act_bwd(const float* dact, const void* z, int n, int F, bool swiglu, void* dz, bool bf16,
-             hipStream_t s);
 void convert_weight(const void* src, int rows, int cols, bool transpose, int interleave16_half,
                     void* dst, bool bf16, hipStream_t s);
 // dst (canonical [in][out] fp32) = W0 + delta, from the internal [out][in] layout

@@ -141,7 +141,7 @@ struct ttt_model {
   float* pmax = nullptr; float* psum = nullptr; float* tlog = nullptr; float* lse_ce = nullptr;
   float* zce = nullptr;                 // the chunk's logits [C][V] fp32 (head statistics pass)
   void* G = nullptr;
-  float* dh = nullptr; void* dh_lo = nullptr; float* dact = nullptr; void* dz = nullptr;
+  float* dh = nullptr; void* dh_lo = nullptr; void* dz = nullptr;
   // transposed operands of the weight-gradient products, one set per fast
   // block (the updates run on their own stream, concurrently with the rest
   // of the backward pass): [features][Cp]
@@ -306,7 +306,6 @@ size_t layout(ttt_model* m, void* base) {
     t.dzT = cv.take<void>((size_t)m->Cp * F2 * es);
     t.bT = cv.take<void>((size_t)m->Cp * d * es);
   }
-  m->dact = cv.take<float>((size_t)C * F * 4);
   m->dz = cv.take<void>((size_t)C * F2 * es);
   m->dtmp = cv.take<float>((size_t)C * d * 4);
   m->dout = cv.take<void>((size_t)C * d * es);
@@ -546,11 +545,15 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
     // gradients transposed to [features][tokens] (tokens padded to a multiple
     // of 8 with zeros, which add nothing to the reduction).
     const int np = (n + 7) & ~7;
-    // dact = dh . Wdn  (reads the weights before their update: Wdn^T [F][d])
+    // dz = act'(z) (dh . Wdn): the activation backward runs in the product's
+    // epilogue (the product reads the weights before their update: Wdn^T
+    // [F][d]).  dz is rewritten here: the update stream must have read the
+    // block above's.
+    if (j + 1 < q) HIPCHK(hipStreamWaitEvent(s, m->evR2[j + 1], 0));
     GemmParams ga;
     ga.A = m->dh_lo; ga.lda = d; ga.B = fw.ct_dn; ga.ldb = d; ga.M = n; ga.N = F; ga.K = d;
-    ga.C = m->dact; ga.ldc = F;
-    rc = run_gemm(m, ga, true, true, EPI_STORE, true, s); if (rc) return rc;
+    ga.C = m->dz; ga.ldc = F2; ga.Z = b.z; ga.ldz = F2; ga.act_swiglu = m->c.mlp == TTT_MLP_SWIGLU;
+    rc = run_gemm(m, ga, true, true, EPI_ACTBWD, false, s); if (rc) return rc;
     // Wdn -= lr * dh^T act   ([d][F], reduction over the chunk's tokens).
     // The update runs on the update stream: its operands are transposed here
     // (after ga has read the old weights), then the chain goes on at once.
@@ -565,9 +568,6 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
     gw.C = fw.m_dn; gw.ldc = F; gw.C2 = bf ? fw.s_dn : nullptr; gw.ldc2 = F; gw.alpha = lr;
     gw.C3 = fw.ct_dn; gw.ldc3 = d; gw.W0 = ly.wdn;
     rc = run_gemm(m, gw, true, true, EPI_SGD, true, m->sc); if (rc) return rc;
-    // dz is rewritten here: the update stream must have read the block above's
-    if (j + 1 < q) HIPCHK(hipStreamWaitEvent(s, m->evR2[j + 1], 0));
-    act_bwd(m->dact, b.z, n, F, m->c.mlp == TTT_MLP_SWIGLU, m->dz, bf, s);
     if (j > 0) {
       GemmParams gb;   // db = dz . Wup (before its update: Wup^T [d][F2])
       gb.A = m->dz; gb.lda = F2; gb.B = fw.ct_up; gb.ldb = F2; gb.M = n; gb.N = d; gb.K = F2;
