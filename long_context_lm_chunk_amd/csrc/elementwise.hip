@@ -96,24 +96,31 @@ __global__ __launch_bounds__(256) void ln_fwd_row_k(const float* __restrict__ x,
 template <typename T>
 __global__ void ln_bwd_k(const float* __restrict__ dy, const float* __restrict__ x,
                          const float* __restrict__ mean, const float* __restrict__ rstd, int n, int d,
-                         float* __restrict__ acc, T* __restrict__ acc_lo) {
+                         float* __restrict__ acc, T* __restrict__ acc_lo, int nslab, int64_t slab_stride) {
   const int row = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= n) return;
   const float* g = dy + (int64_t)row * d;
+  // dy of column i, the partial slabs of a K-split product summed in slab order
+  auto gval = [&](int i) {
+    float v = g[i];
+    for (int z = 1; z < nslab; ++z) v += g[z * slab_stride + i];
+    return v;
+  };
   const float* xr = x + (int64_t)row * d;
   const float mu = mean[row], rs = rstd[row];
   float s1 = 0.f, s2 = 0.f;
   for (int i = lane; i < d; i += 64) {
     const float yh = (xr[i] - mu) * rs;
-    s1 += g[i];
-    s2 += g[i] * yh;
+    const float gi = gval(i);
+    s1 += gi;
+    s2 += gi * yh;
   }
   const float m1 = wave_sum(s1) / d, m2 = wave_sum(s2) / d;
   float* a = acc + (int64_t)row * d;
   for (int i = lane; i < d; i += 64) {
     const float yh = (xr[i] - mu) * rs;
-    const float nv = a[i] + rs * (g[i] - m1 - yh * m2);
+    const float nv = a[i] + rs * (gval(i) - m1 - yh * m2);
     a[i] = nv;
     if (acc_lo) acc_lo[(int64_t)row * d + i] = from_f32<T>(nv);
   }
@@ -163,7 +170,8 @@ template <typename T, int NV>
 __global__ __launch_bounds__(256) void ln_bwd_reg_k(const float* __restrict__ dy, const float* __restrict__ x,
                                                     const float* __restrict__ mean,
                                                     const float* __restrict__ rstd, int n,
-                                                    float* __restrict__ acc, T* __restrict__ acc_lo) {
+                                                    float* __restrict__ acc, T* __restrict__ acc_lo,
+                                                    int nslab, int64_t slab_stride) {
   constexpr int D = 256 * NV;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -178,6 +186,15 @@ __global__ __launch_bounds__(256) void ln_bwd_reg_k(const float* __restrict__ dy
     gv[i] = g[lane + 64 * i];
     yh[i] = xr[lane + 64 * i];
     av[i] = a[lane + 64 * i];
+  }
+  // partial slabs of a K-split product, summed in slab order
+  for (int z = 1; z < nslab; ++z) {
+    const float4* gz = reinterpret_cast<const float4*>(dy + z * slab_stride + (int64_t)row * D);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const float4 w = gz[lane + 64 * i];
+      gv[i].x += w.x; gv[i].y += w.y; gv[i].z += w.z; gv[i].w += w.w;
+    }
   }
   float s1 = 0.f, s2 = 0.f;
 #pragma unroll
@@ -552,20 +569,21 @@ void layernorm_fwd(const float* x, int64_t ldx, int n, int d, float eps, void* y
 }
 
 void layernorm_bwd_acc(const float* dy, const float* x, const float* mean, const float* rstd, int n,
-                       int d, float* acc, void* acc_lo, bool bf, hipStream_t s) {
+                       int d, float* acc, void* acc_lo, bool bf, hipStream_t s, int nslab,
+                       int64_t slab_stride) {
   if (n <= 0) return;
   if (d % 256 == 0 && d <= 4096) {
     switch (d / 256) {
-#define LNB(NV) case NV: TSEL(bf, hipLaunchKernelGGL((ln_bwd_reg_k<bf16, NV>), dim3(nblk(n, 4)), dim3(256), 0, s, dy, x, mean, rstd, n, acc, (bf16*)acc_lo), \
-                               hipLaunchKernelGGL((ln_bwd_reg_k<float, NV>), dim3(nblk(n, 4)), dim3(256), 0, s, dy, x, mean, rstd, n, acc, (float*)acc_lo)); return;
+#define LNB(NV) case NV: TSEL(bf, hipLaunchKernelGGL((ln_bwd_reg_k<bf16, NV>), dim3(nblk(n, 4)), dim3(256), 0, s, dy, x, mean, rstd, n, acc, (bf16*)acc_lo, nslab, slab_stride), \
+                               hipLaunchKernelGGL((ln_bwd_reg_k<float, NV>), dim3(nblk(n, 4)), dim3(256), 0, s, dy, x, mean, rstd, n, acc, (float*)acc_lo, nslab, slab_stride)); return;
       LNB(1) LNB(2) LNB(3) LNB(4) LNB(5) LNB(6) LNB(7) LNB(8) LNB(9) LNB(10) LNB(11) LNB(12)
       LNB(13) LNB(14) LNB(15) LNB(16)
 #undef LNB
       default: break;
     }
   }
-  TSEL(bf, hipLaunchKernelGGL(ln_bwd_k<bf16>, dim3(nblk(n, 4)), dim3(256), 0, s, dy, x, mean, rstd, n, d, acc, (bf16*)acc_lo),
-       hipLaunchKernelGGL(ln_bwd_k<float>, dim3(nblk(n, 4)), dim3(256), 0, s, dy, x, mean, rstd, n, d, acc, (float*)acc_lo));
+  TSEL(bf, hipLaunchKernelGGL(ln_bwd_k<bf16>, dim3(nblk(n, 4)), dim3(256), 0, s, dy, x, mean, rstd, n, d, acc, (bf16*)acc_lo, nslab, slab_stride),
+       hipLaunchKernelGGL(ln_bwd_k<float>, dim3(nblk(n, 4)), dim3(256), 0, s, dy, x, mean, rstd, n, d, acc, (float*)acc_lo, nslab, slab_stride));
 }
 
 void cast_rows(const float* src, void* dst, int64_t n, bool bf, hipStream_t s) {

@@ -652,6 +652,15 @@ __global__ __launch_bounds__(big::NT, 1) void gemm256_kernel(GemmParams p) {
   }
 }
 
+// A split STORE with fp32 output whose caller takes the partial slabs
+// itself (split_defer set): report the slab count, skip the reduction.
+template <int EPI, typename TO>
+bool defer_split(const GemmParams& p, int nz) {
+  if (EPI != EPI_STORE || sizeof(TO) != 4 || !p.split_defer) return false;
+  *p.split_defer = nz;
+  return true;
+}
+
 // The 256x256 core takes bf16 A [M][K] and B [N][K] with 16-byte aligned
 // rows; split K when there are too few tiles for the 256 CUs.
 template <int EPI, typename TO>
@@ -681,6 +690,7 @@ bool launch_big(const GemmParams& p, hipStream_t s) {
   if (p.B2) go(gemm256_kernel<EPI, TO, true>, true);
   else go(gemm256_kernel<EPI, TO, false>, false);
   if constexpr (EPI == EPI_STORE || EPI == EPI_RESID) {
+    if (defer_split<EPI, TO>(p, nz)) return true;
     if (nz > 1) {
       const int64_t groups = (int64_t)p.M * (p.N / 4);
       hipLaunchKernelGGL((gemm_reduce_k<EPI, TO>), dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, s, p, nz);
@@ -722,6 +732,9 @@ void launch_t(const GemmParams& p, hipStream_t s) {
   dim3 grid((p.N + BN - 1) / BN, (p.M + BM - 1) / BM, nz);
   if (p.B2) hipLaunchKernelGGL((gemm_kernel<T, AK, BK_, EPI, TO, true>), grid, dim3(NT), 0, s, p);
   else hipLaunchKernelGGL((gemm_kernel<T, AK, BK_, EPI, TO, false>), grid, dim3(NT), 0, s, p);
+  if constexpr (EPI == EPI_STORE || EPI == EPI_RESID) {
+    if (defer_split<EPI, TO>(p, nz)) return;
+  }
   if constexpr (EPI == EPI_STORE || EPI == EPI_RESID) {
     if (nz > 1) {
       const int64_t groups = (int64_t)p.M * (p.N / 4);

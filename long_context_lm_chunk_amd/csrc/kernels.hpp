@@ -29,6 +29,11 @@ struct GemmParams {
   // split-K scratch (optional; STORE/RESID launches with too few tiles):
   // split_ws holds up to split_cap floats
   float* split_ws = nullptr; int64_t split_cap = 0;
+  // STORE with fp32 output only: when set, a split launch leaves its nz
+  // partial slabs in split_ws ([nz][M][N], summed by the consumer in slab
+  // order) instead of reducing them into C; *split_defer receives nz (1 when
+  // the launch was not split and C holds the result)
+  int* split_defer = nullptr;
 };
 
 // Returns 0, or -1 for an epilogue/layout combination that is not built.
@@ -48,9 +53,12 @@ void embed(const int32_t* tok, int n, const void* E, int d, int V, bool bf16, fl
            hipStream_t s);
 void layernorm_fwd(const float* x, int64_t ldx, int n, int d, float eps, void* y, int64_t ldy,
                    float* mean, float* rstd, bool bf16, hipStream_t s);
-// acc += LN_backward(dy) ; optionally acc_lo = low-precision copy of the new acc
+// acc += LN_backward(dy) ; optionally acc_lo = low-precision copy of the new acc.
+// dy may be nslab partial slabs (row r of slab z at dy + z*slab_stride +
+// r*d), summed in slab order.
 void layernorm_bwd_acc(const float* dy, const float* x, const float* mean, const float* rstd, int n,
-                       int d, float* acc, void* acc_lo, bool bf16, hipStream_t s);
+                       int d, float* acc, void* acc_lo, bool bf16, hipStream_t s, int nslab = 1,
+                       int64_t slab_stride = 0);
 // acc_lo = low-precision copy of acc
 void cast_rows(const float* src, void* dst, int64_t n, bool bf16, hipStream_t s);
 // cs[t][i] = (cos, sin) of (pos0 + t) * theta[i], angle in float64, t < n, i < half

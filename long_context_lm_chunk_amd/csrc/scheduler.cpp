@@ -519,6 +519,11 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
     ce_finish(m->pmax, m->psum, m->nparts, m->Cmax, m->tlog, n, n_tgt, m->lse_ce, loss_out, m->err, s);
   }
   if (n_tgt <= 0) return TTT_OK;   // nothing to learn from this chunk
+  // The products feeding a LayerNorm backward (d = G.U, db, da) leave their
+  // K-split partial slabs in the split scratch; the LayerNorm backward sums
+  // them (nsl slabs) instead of a separate reduction pass.
+  int nsl = 1;
+  auto dy_of = [&]() -> const float* { return nsl > 1 ? m->split_ws : m->dtmp; };
   {
     Scope t(m, CLS_CE, s, 2.0 * n * (double)d * V);
     // G = (softmax - onehot) / n_targets from the stored logits (a stream
@@ -527,11 +532,11 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
     GemmParams gx;   // dHf = G . U  (through U^T [d][V], k-contiguous over the vocabulary)
     gx.A = m->G; gx.lda = V; gx.B = m->UT; gx.ldb = V; gx.M = n; gx.N = d; gx.K = V;
     gx.C = m->dtmp; gx.ldc = d;
-    gx.split_ws = m->split_ws; gx.split_cap = m->split_cap;
+    gx.split_ws = m->split_ws; gx.split_cap = m->split_cap; gx.split_defer = &nsl;
     if (gemm(gx, bf, true, true, EPI_STORE, true, s)) return fail(TTT_ERR_CONFIG, "internal: CE variant");
   }
   fill_f32(m->dh, (int64_t)n * d, 0.f, s);
-  layernorm_bwd_acc(m->dtmp, m->xL, m->meanf, m->rstdf, n, d, m->dh, m->dh_lo, bf, s);
+  layernorm_bwd_acc(dy_of(), m->xL, m->meanf, m->rstdf, n, d, m->dh, m->dh_lo, bf, s, nsl, (int64_t)n * d);
 
   // ---------------- backward through the fast blocks, SGD fused
   for (int j = q - 1; j >= 0; --j) {
@@ -571,7 +576,8 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
     if (j > 0) {
       GemmParams gb;   // db = dz . Wup (before its update: Wup^T [d][F2])
       gb.A = m->dz; gb.lda = F2; gb.B = fw.ct_up; gb.ldb = F2; gb.M = n; gb.N = d; gb.K = F2;
-      gb.C = m->dtmp; gb.ldc = d;
+      gb.C = m->dtmp; gb.ldc = d; gb.split_defer = &nsl;
+      nsl = 1;
       rc = run_gemm(m, gb, true, true, EPI_STORE, true, s); if (rc) return rc;
     }
     // Wup -= lr * dz^T b  (update stream, after gb has read the old weights)
@@ -587,7 +593,7 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
     rc = run_gemm(m, gw2, true, true, EPI_SGD, true, m->sc); if (rc) return rc;
     if (j == 0) break;   // no gradient below the first fast MLP
     HIPCHK(hipStreamWaitEvent(s, m->evR1[j], 0));   // dh_lo is rewritten below
-    layernorm_bwd_acc(m->dtmp, x2, b.mean2, b.rstd2, n, d, m->dh, m->dh_lo, bf, s);
+    layernorm_bwd_acc(dy_of(), x2, b.mean2, b.rstd2, n, d, m->dh, m->dh_lo, bf, s, nsl, (int64_t)n * d);
     GemmParams gdo;   // dO = dh . Wo  (Wo^T [d][d])
     gdo.A = m->dh_lo; gdo.lda = d; gdo.B = ly.woT; gdo.ldb = d; gdo.M = n; gdo.N = d; gdo.K = d;
     gdo.C = m->dout; gdo.ldc = d;
@@ -620,9 +626,10 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
     rope_bwd(m->dqkv, n, m->H, m->hd, m->csB, bf, s);
     GemmParams gq;   // da = dqkv . Wqkv  (Wqkv^T [d][3d])
     gq.A = m->dqkv; gq.lda = 3 * d; gq.B = ly.wqkvT; gq.ldb = 3 * d; gq.M = n; gq.N = d; gq.K = 3 * d;
-    gq.C = m->dtmp; gq.ldc = d;
+    gq.C = m->dtmp; gq.ldc = d; gq.split_defer = &nsl;
+    nsl = 1;
     rc = run_gemm(m, gq, true, true, EPI_STORE, true, s); if (rc) return rc;
-    layernorm_bwd_acc(m->dtmp, b.xin, b.mean1, b.rstd1, n, d, m->dh, m->dh_lo, bf, s);
+    layernorm_bwd_acc(dy_of(), b.xin, b.mean1, b.rstd1, n, d, m->dh, m->dh_lo, bf, s, nsl, (int64_t)n * d);
   }
   // every update of this chunk lands before anything else on s (the next
   // chunk's forward reads the new weights)
