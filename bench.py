@@ -8,10 +8,13 @@ every chunk.  Inputs are synthetic (Zipf(1.1) tokens with planted repeats
 before the timed region.
 
 Prints one JSON line: prefill context tokens/s (value), decode ms/token
-after the prefill, the MFMA utilisation of the whole prefill against the
+after the prefill (2048 greedy tokens, so two decode-time updates are
+amortised in it), the MFMA utilisation of the whole prefill against the
 bf16 dense peak, the roofline of the dominant kernel (HIP events around its
-launches inside the timed region) and the float64 oracle's rate on the host
-cores for a bounded sample.
+launches inside the timed region), the same context read without updates
+(window 8192, and full attention with window = T: prefill and decode
+latency against TTT-E2E's) and the float64 oracle's rate on the host cores
+for a bounded sample.
 """
 from __future__ import annotations
 
@@ -60,6 +63,15 @@ def prefill_flops(cfg, T):
     bwd = 2 * ((T - 1) * d * V + T * (k + 1) * d * F + (q - 1) * T * (2 * k * d * F + 4 * d * d)
                + (q - 1) * d * (2 * sum_n + 2 * sum_m))
     return float(fwd + bwd)
+
+
+def forward_flops(cfg, T):
+    """Algorithmic FLOPs of one read of the context without updates (every
+    layer's forward and the head)."""
+    L, d, F, V, W = (cfg[k] for k in ("n_layers", "d_model", "d_ff", "vocab", "window"))
+    k = 3 if cfg["mlp"] == "swiglu" else 2
+    sum_n = sum(min(t + 1, W) for t in range(T))
+    return float(2 * (T * L * (4 * d * d + k * d * F) + L * d * 2 * sum_n + (T - 1) * d * V))
 
 
 def sgd_bytes_per_launch(cfg, T):
@@ -125,7 +137,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", default="c4")
     ap.add_argument("--T", type=int, default=None)
-    ap.add_argument("--decode-tokens", type=int, default=64)
+    ap.add_argument("--decode-tokens", type=int, default=2048,
+                    help="greedy decode tokens timed after the prefill (2048 reach two "
+                         "decode-time updates at chunk 1024)")
+    ap.add_argument("--no-static", action="store_true",
+                    help="skip the reads without updates (window 8192, and full attention)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=1024)
     ap.add_argument("--prefill-block", type=int, default=0,
@@ -200,19 +216,81 @@ def main():
     lh = losses.cpu().numpy()
     assert np.all(np.isfinite(lh)), "non-finite chunk loss"
 
-    # decode after the prefill (constant per-token cost once T >= window)
-    dec_ms = None
-    if args.decode_tokens > 0:
+    # decode after the prefill (constant per-token cost once T >= window); the
+    # decode-time updates fire when 1024 decode positions are complete, each
+    # token is bracketed by events so update tokens are seen separately
+    def timed_decode(mdl, n):
         for _ in range(4):
-            model.decode_step()
+            mdl.decode_step()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(args.decode_tokens):
-            model.decode_step()
-        e1.record()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        uls = []
+        ev[0].record()
+        for i in range(n):
+            uls.append(mdl.decode_step()[2])
+            ev[i + 1].record()
         torch.cuda.synchronize()
-        dec_ms = e0.elapsed_time(e1) / args.decode_tokens
+        per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(n)])
+        upd = np.array([not bool(torch.isnan(u).item()) for u in uls])
+        res = {"tokens": n, "ms_per_token": round(float(per.sum() / n), 4),
+               "ms_per_token_p50": round(float(np.percentile(per, 50)), 4),
+               "ms_per_token_p99": round(float(np.percentile(per, 99)), 4),
+               "updates": int(upd.sum()),
+               "update_token_ms": round(float(per[upd].mean()), 3) if upd.any() else None,
+               "ms_per_token_without_updates": round(float(per[~upd].mean()), 4) if (~upd).any() else None,
+               "first_position": int(T + 4)}
+        return res
+
+    dec = None
+    if args.decode_tokens > 0:
+        dec = timed_decode(model, args.decode_tokens)
+        print(f"# decode: {dec}", file=sys.stderr, flush=True)
+
+    # The same context read without updates (the static-weight models the
+    # pages compare TTT-E2E with): window 8192, then full attention (window
+    # = T), prefill and decode latency.
+    static = None
+    if not args.no_static:
+        def timed_forward(mdl, reps):
+            mdl.forward(tokens, cfg["chunk"])
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                out = mdl.forward(tokens, cfg["chunk"])
+            torch.cuda.synchronize()
+            assert bool(torch.isfinite(out).all().item()), "non-finite loss in the static read"
+            return (time.perf_counter() - t0) / reps
+        t_sw = timed_forward(model, 2)
+        print(f"# static read, window {cfg['window']}: {t_sw * 1e3:.1f} ms", file=sys.stderr, flush=True)
+        model.close()
+        del model
+        torch.cuda.empty_cache()
+        fcfg = synth.config(cfg, window=T)
+        fa = T_.Model(fcfg, weights, max_chunk=cfg["chunk"], prefill_block=args.prefill_block)
+        print(f"# full-attention model: workspace {fa.workspace.numel() / 1e9:.1f} GB", file=sys.stderr,
+              flush=True)
+        t_fa = timed_forward(fa, 2)
+        print(f"# full-attention read: {t_fa * 1e3:.1f} ms", file=sys.stderr, flush=True)
+        fdec = timed_decode(fa, 64) if args.decode_tokens > 0 else None
+        fa.close()
+        del fa
+        torch.cuda.empty_cache()
+        ttt_s = dt / args.steps
+        static = {
+            "T": T,
+            "window_static": {"window": cfg["window"], "ms": round(t_sw * 1e3, 1),
+                              "tokens_per_s": round(T / t_sw, 1),
+                              "mfma_util_pct": round(100.0 * forward_flops(cfg, T) / t_sw /
+                                                     (PEAK_BF16_TFLOPS * 1e12), 2)},
+            "full_attention": {"window": T, "ms": round(t_fa * 1e3, 1), "tokens_per_s": round(T / t_fa, 1),
+                               "mfma_util_pct": round(100.0 * forward_flops(fcfg, T) / t_fa /
+                                                      (PEAK_BF16_TFLOPS * 1e12), 2),
+                               "decode_ms_per_token": fdec["ms_per_token"] if fdec else None},
+            "prefill_latency_ratio_full_attention_over_ttt": round(t_fa / ttt_s, 3),
+            "decode_latency_ratio_full_attention_over_ttt": (round(fdec["ms_per_token_without_updates"] /
+                                                                   dec["ms_per_token_without_updates"], 3)
+                                                             if fdec and dec else None),
+        }
 
     # Roofline of the dominant kernel (largest measured time of the classes
     # that are one kernel symbol each): the fused weight-gradient + SGD
@@ -259,7 +337,9 @@ def main():
                    "heads": cfg["n_heads"], "d_ff": cfg["d_ff"], "vocab": cfg["vocab"],
                    "fast_layers": cfg["n_fast"], "lr": cfg["lr"], "steps_per_chunk": 1,
                    "parallelism": "single GPU"},
-        "decode_ms_per_token": None if dec_ms is None else round(dec_ms, 3),
+        "decode_ms_per_token": None if dec is None else dec["ms_per_token"],
+        "decode": dec,
+        "static_reads": static,
         "mfma_util_pct": round(mfma_pct, 2),
         "algorithmic_tflop_per_step": round(fl / 1e12, 1),
         "kernel_classes_ms_per_step": {k: round(v["ms"], 2) for k, v in ktime.items()},

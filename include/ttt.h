@@ -59,7 +59,8 @@ enum { TTT_FP32 = 0, TTT_BF16 = 1 };
  * Supported: head_dim in {16, 32, 64, 96, 128}; n_heads * head_dim ==
  * d_model; d_model % 16 == 0; d_ff % 16 == 0; vocab % 8 == 0;
  * d_model, d_ff <= 16384 (bf16) or 8192 (fp32); 1 <= n_fast <= n_layers;
- * 1 <= window <= 16384; 1 <= max_chunk <= 65536.
+ * 1 <= window <= 4194304 (the K/V rings hold window + prefill_block
+ * positions per layer, so memory bounds it in practice); 1 <= max_chunk <= 65536.
  */
 typedef struct {
   int32_t n_layers, d_model, n_heads, head_dim, d_ff, vocab, window;
@@ -118,6 +119,24 @@ int ttt_prefill(struct ttt_model* m, const int32_t* tokens, int64_t T, int32_t c
                 int32_t steps, float* chunk_losses, void* stream);
 
 /*
+ * The same context read without test-time training: the static-weight
+ * model whose latency the pages set against TTT-E2E (blog Figure 1, right
+ * panel; paper abstract: constant latency versus full attention, whose
+ * per-token cost grows with the context).  Resets the model, then every
+ * block, the fast ones with their loaded MLP weights, reads the positions in
+ * batches of whole chunks (prefill_block tokens); no gradient, no update.
+ * chunk_losses[k] is the mean next-token cross-entropy of chunk k
+ * (positions [k*chunk, min((k+1)*chunk, T))), i.e. what ttt_prefill returns
+ * at lr = 0.  With window >= T this is a plain full-attention Transformer.
+ *   tokens       device int32 [T], 2 <= T
+ *   chunk        1 <= chunk <= max_chunk (only groups the losses)
+ *   chunk_losses device float [ceil(T/chunk)]
+ * Decode steps may follow; they make no updates.  Errors as ttt_prefill.
+ */
+int ttt_forward(struct ttt_model* m, const int32_t* tokens, int64_t T, int32_t chunk,
+                float* chunk_losses, void* stream);
+
+/*
  * Copy fast-weight matrix `mat` of fast layer `fast_idx` (0 = the first
  * fast layer) as float32 in canonical [in][out] layout into `dst` (device,
  * n floats, n == rows*cols).  mat: GELU 0 = W1, 1 = W2; SwiGLU 0 = Wg,
@@ -127,7 +146,19 @@ int ttt_fast_weight(struct ttt_model* m, int32_t fast_idx, int32_t mat, float* d
                     void* stream);
 
 /*
- * One greedy decode step after ttt_prefill (or a previous decode step).
+ * The same matrix's change since loading, phi - phi0 (the sum of the SGD
+ * steps, forum post TL;DR "Inner Loop"), as float32 in the same layout and
+ * with the same arguments and errors.  It is read from the float32 master of
+ * the update, so it is exact where the difference of two ttt_fast_weight
+ * exports would round at the magnitude of the weights (at lr = 1e-4 the
+ * change per chunk is ~1e-8, below a float32 ulp of a weight of ~0.02).
+ */
+int ttt_fast_weight_delta(struct ttt_model* m, int32_t fast_idx, int32_t mat, float* dst, int64_t n,
+                          void* stream);
+
+/*
+ * One greedy decode step after ttt_prefill or ttt_forward (or a previous
+ * decode step).
  * The first call emits argmax of the last prefill position's logits; every
  * call then reads the emitted token at the next position (its K/V join the
  * rings) and prepares the next argmax (lowest id on ties).  When `chunk`

@@ -47,7 +47,9 @@ def _load():
         "ttt_model_load": ([ctypes.POINTER(TTTConfig), ctypes.POINTER(vp), i32, vp, ctypes.c_size_t, vp,
                             ctypes.POINTER(vp)], ctypes.c_int),
         "ttt_prefill": ([vp, vp, i64, i32, f32, i32, vp, vp], ctypes.c_int),
+        "ttt_forward": ([vp, vp, i64, i32, vp, vp], ctypes.c_int),
         "ttt_fast_weight": ([vp, i32, i32, vp, i64, vp], ctypes.c_int),
+        "ttt_fast_weight_delta": ([vp, i32, i32, vp, i64, vp], ctypes.c_int),
         "ttt_decode_step": ([vp, vp, vp, vp, vp], ctypes.c_int),
         "ttt_reset": ([vp, vp], ctypes.c_int),
         "ttt_model_free": ([vp], None),
@@ -68,7 +70,8 @@ def _load():
 
 lib = _load()
 
-EXPORTED = ["ttt_workspace_bytes", "ttt_model_load", "ttt_prefill", "ttt_fast_weight",
+EXPORTED = ["ttt_workspace_bytes", "ttt_model_load", "ttt_prefill", "ttt_forward", "ttt_fast_weight",
+            "ttt_fast_weight_delta",
             "ttt_decode_step", "ttt_reset", "ttt_model_free", "ttt_status_str", "ttt_last_error",
             "ttt_timing_enable", "ttt_timing_read", "ttt_diag_gemm", "ttt_diag_gemm_core"]
 
@@ -160,18 +163,32 @@ class Model:
                                out.data_ptr(), self._s()))
         return out
 
-    def fast_weight(self, fast_idx: int, mat: int):
+    def forward(self, tokens, chunk: int, out=None):
+        """The context read with the loaded weights and no update (per-chunk
+        losses as a prefill at lr = 0); with window >= T, full attention."""
+        torch = self.torch
+        tokens = tokens.to(self.device, torch.int32).contiguous()
+        T = tokens.numel()
+        if out is None:
+            out = torch.empty(math.ceil(T / chunk), dtype=torch.float32, device=self.device)
+        _check(lib.ttt_forward(self.h, tokens.data_ptr(), T, chunk, out.data_ptr(), self._s()))
+        return out
+
+    def fast_weight(self, fast_idx: int, mat: int, delta: bool = False):
+        """Fast matrix `mat` of fast layer `fast_idx`, float32 [in][out];
+        with delta, its change since loading (exact float32 master)."""
         torch = self.torch
         d, F = self.cfg["d_model"], self.cfg["d_ff"]
         nmat = 3 if self.cfg["mlp"] == "swiglu" else 2
         shape = (F, d) if mat == nmat - 1 else (d, F)
         out = torch.empty(shape, dtype=torch.float32, device=self.device)
-        _check(lib.ttt_fast_weight(self.h, fast_idx, mat, out.data_ptr(), out.numel(), self._s()))
+        fn = lib.ttt_fast_weight_delta if delta else lib.ttt_fast_weight
+        _check(fn(self.h, fast_idx, mat, out.data_ptr(), out.numel(), self._s()))
         return out
 
-    def fast_weights(self):
+    def fast_weights(self, delta: bool = False):
         nmat = 3 if self.cfg["mlp"] == "swiglu" else 2
-        return [self.fast_weight(j, m) for j in range(self.cfg["n_fast"]) for m in range(nmat)]
+        return [self.fast_weight(j, m, delta) for j in range(self.cfg["n_fast"]) for m in range(nmat)]
 
     def decode_step(self, want_logits: bool = False):
         torch = self.torch

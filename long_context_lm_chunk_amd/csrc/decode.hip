@@ -377,28 +377,33 @@ __global__ __launch_bounds__(256) void swa_decode_part_k(const T* __restrict__ q
 }
 
 // Combine the splits of head h: o = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s.
+// Any number of splits: the first wave finds M, then every output lane walks
+// the splits (every split wrote its partial, possibly empty: m = -inf, l = 0).
 template <typename T>
 __global__ void swa_decode_combine_k(const float* __restrict__ ws, int nsplit, int H, int hd,
                                      T* __restrict__ o) {
-  // (every split writes its partial, possibly empty: m = -inf, l = 0)
-  __shared__ float fs[64];
-  __shared__ float Ls;
+  __shared__ float Ms;
   const int h = blockIdx.x, j = threadIdx.x;
+  const float* wh = ws + (int64_t)h * nsplit * (2 + hd);
   if (j < 64) {
     float mv = -INFINITY;
-    if (j < nsplit) mv = ws[((int64_t)h * nsplit + j) * (2 + hd)];
+    for (int sp = j; sp < nsplit; sp += 64) mv = fmaxf(mv, wh[(int64_t)sp * (2 + hd)]);
     const float M = wave_max(mv);
-    const float f = (j < nsplit && mv != -INFINITY) ? __expf(mv - M) : 0.f;
-    fs[j] = f;
-    const float lv = (j < nsplit) ? ws[((int64_t)h * nsplit + j) * (2 + hd) + 1] * f : 0.f;
-    const float L = wave_sum(lv);
-    if (j == 0) Ls = L;
+    if (j == 0) Ms = M;
   }
   __syncthreads();
   if (j >= hd) return;
-  float acc = 0.f;
-  for (int sp = 0; sp < nsplit; ++sp) acc += ws[((int64_t)h * nsplit + sp) * (2 + hd) + 2 + j] * fs[sp];
-  o[h * hd + j] = from_f32<T>(acc / Ls);
+  const float M = Ms;
+  float acc = 0.f, L = 0.f;
+  for (int sp = 0; sp < nsplit; ++sp) {
+    const float* w = wh + (int64_t)sp * (2 + hd);
+    const float mv = w[0];
+    if (mv == -INFINITY) continue;
+    const float f = __expf(mv - M);
+    L += w[1] * f;
+    acc += w[2 + j] * f;
+  }
+  o[h * hd + j] = from_f32<T>(acc / L);
 }
 
 // ---------------------------------------------------------------------------
@@ -475,7 +480,7 @@ __global__ __launch_bounds__(1024) void argmax_part_k(const float2* __restrict__
 template <typename T>
 void swa_decode_t(const void* q, const void* kring, const void* vring, int64_t cap, int H, int hd,
                   int window, const int64_t* dstate, void* o, float* ws, hipStream_t s) {
-  const int nsplit = (window + DK - 1) / DK;   // covers a full window (<= 64 splits)
+  const int nsplit = (window + DK - 1) / DK;   // covers a full window
   dim3 grid(nsplit, H);
   switch (hd) {
 #define CASE(HDV) case HDV: hipLaunchKernelGGL((swa_decode_part_k<T, HDV>), grid, dim3(256), 0, s, \

@@ -450,7 +450,7 @@ __global__ void export_k(const T* __restrict__ w0, const float* __restrict__ dm,
   const int j = idx / out_dim;          // input row
   int64_t r = f;
   if (ilv) r = (int64_t)(f / 16) * 32 + which * 16 + (f % 16);
-  dst[idx] = to_f32(w0[r * in_dim + j]) + dm[r * in_dim + j];
+  dst[idx] = (w0 ? to_f32(w0[r * in_dim + j]) : 0.f) + dm[r * in_dim + j];   // no w0: the delta
 }
 
 // One wave per row: combine the per-part (max, sumexp) into the row LSE and

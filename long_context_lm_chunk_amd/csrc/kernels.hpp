@@ -73,7 +73,8 @@ void qkv_rope(const void* qkv, int n, int H, int hd, int64_t pos0, const float2*
 void rope_bwd(void* dqkv, int n, int H, int hd, const float2* cs, bool bf16, hipStream_t s);
 void convert_weight(const void* src, int rows, int cols, bool transpose, int interleave16_half,
                     void* dst, bool bf16, hipStream_t s);
-// dst (canonical [in][out] fp32) = W0 + delta, from the internal [out][in] layout
+// dst (canonical [in][out] fp32) = W0 + delta (delta alone when w0 is null), from the
+// internal [out][in] layout
 void export_weight(const void* w0, const float* delta, int out_dim, int in_dim, int interleave_half,
                    int which, float* dst, bool bf16, hipStream_t s);
 void widen(const void* src, float* dst, int64_t n, bool bf16, hipStream_t s);

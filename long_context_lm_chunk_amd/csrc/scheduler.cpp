@@ -173,6 +173,7 @@ struct ttt_model {
   int64_t pos = 0;        // next position to read
   int64_t dchunk0 = 0;    // first position of the current decode chunk
   bool prefilled = false;
+  bool no_update = false; // read by ttt_forward: decode makes no updates
   float lr = 0.f; int steps = 1; int chunk = 1;
   Timing tm[NCLS];
 };
@@ -191,7 +192,7 @@ int check_config(const ttt_config* c) {
   if (c->d_model % 16 || c->d_ff % 16 || c->d_ff <= 0) return fail(TTT_ERR_CONFIG, "d_model and d_ff must be positive multiples of 16");
   if (c->vocab <= 0 || c->vocab % 8) return fail(TTT_ERR_CONFIG, "vocab must be a positive multiple of 8");
   if (c->n_layers <= 0 || c->n_fast < 1 || c->n_fast > c->n_layers) return fail(TTT_ERR_CONFIG, "need 1 <= n_fast <= n_layers");
-  if (c->window < 1 || c->window > 16384) return fail(TTT_ERR_CONFIG, "window must be in [1, 16384]");
+  if (c->window < 1 || c->window > (1 << 22)) return fail(TTT_ERR_CONFIG, "window must be in [1, 4194304]");
   {
     const int kmax = c->dtype == TTT_BF16 ? 16384 : 8192;   // decode input vector held in LDS
     if (c->d_model > kmax || c->d_ff > kmax)
@@ -415,42 +416,56 @@ double pairs(int64_t p0, int n, int64_t W, int64_t kmin, double* inchunk) {
 }
 
 // --------------------------------------------------------------- phase A
-int phase_a(ttt_model* m, const int32_t* tokens, int64_t B0, int nb, float* hA, hipStream_t s) {
+// One pre-LN block with its loaded weights over nb rows of the residual
+// stream x (fp32 [nb][d], positions pos0 .. pos0+nb-1, updated in place):
+// LN1 -> QKV -> RoPE (K/V to the layer's rings) -> attention -> O + residual,
+// then, when `mlp`, LN2 -> up + activation -> down + residual.  cs holds the
+// rotary table rows of these positions.  Its temporaries are the phase-A
+// buffers, so it runs on one stream at a time.
+int block_fwd(ttt_model* m, int l, int64_t pos0, int nb, float* x, const float2* cs, bool mlp,
+              hipStream_t s) {
   const int d = m->d, F = m->F, F2 = m->F2;
   const bool bf = m->bf;
-  embed(tokens + B0, nb, m->E, d, m->V, bf, hA, m->err, s);
+  Layer& ly = m->layers[l];
+  layernorm_fwd(x, d, nb, d, m->c.ln_eps, m->aA, d, nullptr, nullptr, bf, s);
+  GemmParams g;
+  g.A = m->aA; g.lda = d; g.B = ly.wqkv; g.ldb = d; g.M = nb; g.N = 3 * d; g.K = d;
+  g.C = m->qkvA; g.ldc = 3 * d;
+  int rc = run_gemm(m, g, true, true, EPI_STORE, false, s, false); if (rc) return rc;
+  qkv_rope(m->qkvA, nb, m->H, m->hd, pos0, cs, m->qA, ly.kring, ly.vring, ly.vtring, nullptr, ly.cap,
+           bf, s);
+  AttnParams ap;
+  ap.q = m->qA; ap.ldq = d; ap.kring = ly.kring; ap.vring = ly.vring; ap.vtring = ly.vtring; ap.cap = ly.cap;
+  ap.n = nb; ap.H = m->H; ap.hd = m->hd; ap.window = m->W; ap.pos0 = pos0; ap.o = m->oA; ap.ldo = d;
+  {
+    Scope t(m, CLS_ATTN_FWD, s, 4.0 * d * pairs(pos0, nb, m->W, 0, nullptr));
+    swa_fwd(ap, bf, s);
+  }
+  GemmParams go;
+  go.A = m->oA; go.lda = d; go.B = ly.wo; go.ldb = d; go.M = nb; go.N = d; go.K = d;
+  go.C = x; go.ldc = d; go.R = x; go.ldr = d;
+  rc = run_gemm(m, go, true, true, EPI_RESID, true, s, false); if (rc) return rc;
+  if (!mlp) return TTT_OK;
+  layernorm_fwd(x, d, nb, d, m->c.ln_eps, m->aA, d, nullptr, nullptr, bf, s);
+  GemmParams gu;
+  gu.A = m->aA; gu.lda = d; gu.B = ly.wup; gu.ldb = d; gu.M = nb; gu.N = F2; gu.K = d;
+  gu.C = m->zA; gu.ldc = F2; gu.C2 = m->actA; gu.ldc2 = F;
+  rc = run_gemm(m, gu, true, true, m->c.mlp == TTT_MLP_SWIGLU ? EPI_SWIGLU : EPI_GELU, false, s, false);
+  if (rc) return rc;
+  GemmParams gd;
+  gd.A = m->actA; gd.lda = F; gd.B = ly.wdn; gd.ldb = F; gd.M = nb; gd.N = d; gd.K = F;
+  gd.C = x; gd.ldc = d; gd.R = x; gd.ldr = d;
+  return run_gemm(m, gd, true, true, EPI_RESID, true, s, false);
+}
+
+// Phase A of one block of positions [B0, B0+nb): embedding, every frozen
+// block and the attention half of the first fast block.
+int phase_a(ttt_model* m, const int32_t* tokens, int64_t B0, int nb, float* hA, hipStream_t s) {
+  embed(tokens + B0, nb, m->E, m->d, m->V, m->bf, hA, m->err, s);
   rope_table(B0, nb, m->hd / 2, m->theta, m->csA, s);
   for (int l = 0; l <= m->f0; ++l) {
-    Layer& ly = m->layers[l];
-    layernorm_fwd(hA, d, nb, d, m->c.ln_eps, m->aA, d, nullptr, nullptr, bf, s);
-    GemmParams g;
-    g.A = m->aA; g.lda = d; g.B = ly.wqkv; g.ldb = d; g.M = nb; g.N = 3 * d; g.K = d;
-    g.C = m->qkvA; g.ldc = 3 * d;
-    int rc = run_gemm(m, g, true, true, EPI_STORE, false, s, false); if (rc) return rc;
-    qkv_rope(m->qkvA, nb, m->H, m->hd, B0, m->csA, m->qA, ly.kring, ly.vring, ly.vtring, nullptr, ly.cap,
-             bf, s);
-    AttnParams ap;
-    ap.q = m->qA; ap.ldq = d; ap.kring = ly.kring; ap.vring = ly.vring; ap.vtring = ly.vtring; ap.cap = ly.cap;
-    ap.n = nb; ap.H = m->H; ap.hd = m->hd; ap.window = m->W; ap.pos0 = B0; ap.o = m->oA; ap.ldo = d;
-    {
-      Scope t(m, CLS_ATTN_FWD, s, 4.0 * d * pairs(B0, nb, m->W, 0, nullptr));
-      swa_fwd(ap, bf, s);
-    }
-    GemmParams go;
-    go.A = m->oA; go.lda = d; go.B = ly.wo; go.ldb = d; go.M = nb; go.N = d; go.K = d;
-    go.C = hA; go.ldc = d; go.R = hA; go.ldr = d;
-    rc = run_gemm(m, go, true, true, EPI_RESID, true, s, false); if (rc) return rc;
-    if (l == m->f0) break;
-    layernorm_fwd(hA, d, nb, d, m->c.ln_eps, m->aA, d, nullptr, nullptr, bf, s);
-    GemmParams gu;
-    gu.A = m->aA; gu.lda = d; gu.B = ly.wup; gu.ldb = d; gu.M = nb; gu.N = F2; gu.K = d;
-    gu.C = m->zA; gu.ldc = F2; gu.C2 = m->actA; gu.ldc2 = F;
-    rc = run_gemm(m, gu, true, true, m->c.mlp == TTT_MLP_SWIGLU ? EPI_SWIGLU : EPI_GELU, false, s, false);
+    const int rc = block_fwd(m, l, B0, nb, hA, m->csA, l < m->f0, s);
     if (rc) return rc;
-    GemmParams gd;
-    gd.A = m->actA; gd.lda = F; gd.B = ly.wdn; gd.ldb = F; gd.M = nb; gd.N = d; gd.K = F;
-    gd.C = hA; gd.ldc = d; gd.R = hA; gd.ldr = d;
-    rc = run_gemm(m, gd, true, true, EPI_RESID, true, s, false); if (rc) return rc;
   }
   return TTT_OK;
 }
@@ -638,6 +653,58 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
   return TTT_OK;
 }
 
+// ------------------------------------------------------- forward only
+// One block of positions [B0, B0+nb) read with the loaded weights and no
+// update: every block batched over the rows (the fast blocks too, since
+// their MLPs keep their initial values), then the final LayerNorm and the
+// fused head + cross-entropy statistics per chunk.  The fast blocks' rings
+// hold window + max_chunk positions, so their layers run over sub-blocks
+// that never overwrite a key a later query of the block still reads.
+int forward_block(ttt_model* m, const int32_t* tokens, int64_t T, int64_t B0, int nb, int chunk,
+                  float* losses, hipStream_t s) {
+  const int d = m->d, half = m->hd / 2;
+  const bool bf = m->bf;
+  float* x = m->hAb[0];
+  embed(tokens + B0, nb, m->E, d, m->V, bf, x, m->err, s);
+  rope_table(B0, nb, half, m->theta, m->csA, s);
+  for (int l = 0; l < m->L; ++l) {
+    for (int o = 0; o < nb;) {
+      // rows [p, p+sb) write sb ring slots and read keys back to
+      // max(0, p - W + 1): all distinct modulo cap while the span fits;
+      // whole 64-row groups where possible
+      const int64_t p = B0 + o;
+      int64_t room = m->layers[l].cap - std::min<int64_t>(p, m->W - 1);
+      if (room >= 64) room -= room % 64;
+      const int sb = (int)std::min<int64_t>(nb - o, room);
+      const int rc = block_fwd(m, l, p, sb, x + (int64_t)o * d, m->csA + (int64_t)o * half, true, s);
+      if (rc) return rc;
+      o += sb;
+    }
+  }
+  for (int64_t c0 = B0; c0 < B0 + nb; c0 += chunk) {
+    const int n = (int)std::min<int64_t>(chunk, T - c0);
+    const int n_tgt = (int)std::min<int64_t>(n, T - 1 - c0);
+    layernorm_fwd(x + (c0 - B0) * d, d, n, d, m->c.ln_eps, m->fN, d, nullptr, nullptr, bf, s);
+    {
+      Scope t(m, CLS_CE, s, 2.0 * n * (double)d * m->V);
+      GemmParams gs;
+      gs.A = m->fN; gs.lda = d; gs.B = m->U; gs.ldb = d; gs.M = n; gs.N = m->V; gs.K = d;
+      gs.tgt = tokens + c0 + 1; gs.n_tgt = n_tgt; gs.part_max = m->pmax; gs.part_sum = m->psum;
+      gs.ldpart = m->Cmax; gs.tgt_logit = m->tlog;
+      if (gemm(gs, bf, true, true, EPI_CESTAT, true, s)) return fail(TTT_ERR_CONFIG, "internal: CE variant");
+      ce_finish(m->pmax, m->psum, m->nparts, m->Cmax, m->tlog, n, n_tgt, m->lse_ce,
+                losses + (c0 / chunk), m->err, s);
+    }
+    if (c0 + n == T) {   // first decode token: argmax of the last position's logits
+      const char* frow = static_cast<const char*>(m->fN) + (size_t)(n - 1) * d * m->es;
+      dgemv_vec(m->U, nullptr, m->V, d, frow, m->logits, nullptr, nullptr, nullptr, m->amax, bf, s);
+      argmax_part(m->amax, dgemv_blocks(m->V), m->cur_tok, nullptr, nullptr, false, s);
+      dec_set(m->dstate, T, 0, s);
+    }
+  }
+  return TTT_OK;
+}
+
 // One decode token: read the current token at position dstate[0], append
 // its K/V to every ring, and leave the next greedy token in cur_tok.  No
 // argument depends on the position, so the launches can be captured once.
@@ -703,6 +770,7 @@ int reset_state(ttt_model* m, hipStream_t s) {
   m->pos = 0;
   m->dchunk0 = 0;
   m->prefilled = false;
+  m->no_update = false;
   return TTT_OK;
 }
 
@@ -880,8 +948,34 @@ int ttt_prefill(ttt_model* m, const int32_t* tokens, int64_t T, int32_t chunk, f
   return TTT_OK;
 }
 
-int ttt_fast_weight(ttt_model* m, int32_t fast_idx, int32_t mat, float* dst, int64_t n,
-                    void* stream) {
+int ttt_forward(ttt_model* m, const int32_t* tokens, int64_t T, int32_t chunk, float* chunk_losses,
+                void* stream) {
+  if (!m || !tokens || !chunk_losses) return fail(TTT_ERR_ARG, "NULL argument");
+  if (T < 2) return fail(TTT_ERR_ARG, "T must be >= 2");
+  if (chunk < 1 || chunk > m->Cmax) return fail(TTT_ERR_ARG, "chunk must be in [1, max_chunk]");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int rc = reset_state(m, s);
+  if (rc) return rc;
+  m->lr = 0.f;
+  m->steps = 1;
+  m->chunk = chunk;
+  const int64_t blk = std::max<int64_t>(chunk, (m->MA / chunk) * (int64_t)chunk);
+  for (int64_t B0 = 0; B0 < T; B0 += blk) {
+    rc = forward_block(m, tokens, T, B0, (int)std::min<int64_t>(blk, T - B0), chunk, chunk_losses, s);
+    if (rc) return rc;
+  }
+  rc = sync_and_check(m, s);
+  if (rc) return rc;
+  m->pos = T;
+  m->dchunk0 = T;
+  m->prefilled = true;
+  m->no_update = true;
+  return TTT_OK;
+}
+
+namespace {
+int export_fast(ttt_model* m, int32_t fast_idx, int32_t mat, float* dst, int64_t n, bool delta_only,
+                void* stream) {
   if (!m || !dst) return fail(TTT_ERR_ARG, "NULL argument");
   if (fast_idx < 0 || fast_idx >= m->q) return fail(TTT_ERR_ARG, "fast_idx out of range");
   const bool sw = m->c.mlp == TTT_MLP_SWIGLU;
@@ -892,9 +986,20 @@ int ttt_fast_weight(ttt_model* m, int32_t fast_idx, int32_t mat, float* dst, int
   hipStream_t s = static_cast<hipStream_t>(stream);
   FastLayer& f = m->fast[fast_idx];
   Layer& ly = m->layers[m->f0 + fast_idx];
-  if (mat == nmat - 1) export_weight(ly.wdn, f.m_dn, d, F, 0, 0, dst, m->bf, s);          // [F][d]
-  else export_weight(ly.wup, f.m_up, F, d, sw ? 1 : 0, mat, dst, m->bf, s);               // [d][F]
+  if (mat == nmat - 1) export_weight(delta_only ? nullptr : ly.wdn, f.m_dn, d, F, 0, 0, dst, m->bf, s);  // [F][d]
+  else export_weight(delta_only ? nullptr : ly.wup, f.m_up, F, d, sw ? 1 : 0, mat, dst, m->bf, s);       // [d][F]
   return TTT_OK;
+}
+}  // namespace
+
+int ttt_fast_weight(ttt_model* m, int32_t fast_idx, int32_t mat, float* dst, int64_t n,
+                    void* stream) {
+  return export_fast(m, fast_idx, mat, dst, n, false, stream);
+}
+
+int ttt_fast_weight_delta(ttt_model* m, int32_t fast_idx, int32_t mat, float* dst, int64_t n,
+                          void* stream) {
+  return export_fast(m, fast_idx, mat, dst, n, true, stream);
 }
 
 int ttt_decode_step(ttt_model* m, int32_t* next_token, float* logits_out, float* update_loss,
@@ -923,7 +1028,11 @@ int ttt_decode_step(ttt_model* m, int32_t* next_token, float* logits_out, float*
   if (logits_out) copy_f32(m->logits, logits_out, m->V, s);
   m->pos += 1;
   bool updated = false;
-  if (m->pos - m->dchunk0 == m->chunk) {
+  if (m->pos - m->dchunk0 == m->chunk && m->no_update) {
+    // after ttt_forward: the chunk bookkeeping restarts, no update is made
+    m->dchunk0 = m->pos;
+    dec_set(m->dstate, m->pos, 0, s);
+  } else if (m->pos - m->dchunk0 == m->chunk) {
     // the decode chunk is complete: its targets are known, make the update
     const int n = m->chunk;
     for (int st = 0; st < m->steps; ++st) {

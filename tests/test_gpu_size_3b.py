@@ -1,0 +1,188 @@
+"""Parity at the full 3B shape, in the launch configuration of the timed
+prefill: 28 layers, d 3072, 24 heads of 128, SwiGLU 8192, vocabulary 32000,
+window 8192, the MLPs of the last 7 blocks fast, chunk 1024, lr 1e-4, bf16
+storage, frozen blocks batched over 8192 tokens, a 131072-token context.
+
+The float64 oracle cannot run the whole context (hours on the host), so the
+outputs it can compute one by one are sampled: the first two chunk losses of
+the full-context prefill (they depend only on tokens 0..2048 and on the
+update made after chunk 0), and, from a 2048-token prefill in the same
+configuration, both chunk losses, every fast matrix after the two updates
+and the logits of three greedy decode positions; the same 2048-token case
+also runs in the float32 check mode (bar 1e-4).  The rest of the 131072
+positions are checked by properties: every chunk loss is finite, and the
+first two agree with the 2048-token run.
+
+The context read without updates (the static-weight model) is checked the
+same way, at window 8192 and with full attention (window = T = 131072):
+chunk 0 against the oracle, every chunk against the prefill at lr = 0
+(window 8192), and the first 8 chunks of the two windows against each other
+(no query before position 8192 has more keys than either window holds).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import ttt_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+BAR = 2e-2   # bf16 storage, fp32 accumulation
+_REF = {}    # oracle values shared by the tests of this module
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def rel(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+@pytest.fixture(scope="module")
+def c4():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import long_context_lm_chunk_amd as T_
+    cfg = synth.config("c4")
+    say("case 3B shape: weights and model load")
+    w = synth.gen_weights(cfg, device="cuda:0")
+    x = synth.gen_tokens(cfg)
+    m = T_.Model(cfg, w, max_chunk=cfg["chunk"])
+    yield cfg, w, x, m
+    m.close()
+
+
+@pytest.mark.timeout(1200)
+def test_3b_full_context_first_chunks_weights_and_decode_match_oracle(c4):
+    cfg, w, x, m = c4
+    C, lr = cfg["chunk"], cfg["lr"]
+    T = cfg["T"]
+    tok = torch.from_numpy(x).cuda()
+
+    say(f"case 3B full-context prefill T={T} chunk={C} lr={lr}")
+    full = m.prefill(tok, C, lr).cpu().numpy()
+    torch.cuda.synchronize()
+    assert full.shape == (T // C,)
+    assert np.all(np.isfinite(full))
+
+    say("case 3B prefill T=2048, fast weights, 3 decode positions")
+    two = m.prefill(tok[:2048], C, lr).cpu().numpy()
+    fw = [t.cpu().numpy() for t in m.fast_weights()]
+    fd = [t.cpu().numpy() for t in m.fast_weights(delta=True)]
+    toks, logits = [], []
+    for _ in range(3):
+        t, lg, _ = m.decode_step(want_logits=True)
+        toks.append(int(t.item()))
+        logits.append(lg.cpu().numpy())
+    torch.cuda.synchronize()
+
+    say("case 3B fp32 check mode (the same bf16 values held as float32): prefill T=2048, "
+        "fast weights, 3 decode positions")
+    import long_context_lm_chunk_amd as T_
+    m32 = T_.Model(cfg, [t.float() for t in w], dtype="fp32", max_chunk=C)
+    two32 = m32.prefill(tok[:2048], C, lr).cpu().numpy()
+    fw32 = [t.cpu().numpy() for t in m32.fast_weights()]
+    fd32 = [t.cpu().numpy() for t in m32.fast_weights(delta=True)]
+    toks32, logits32 = [], []
+    for _ in range(3):
+        t, lg, _ = m32.decode_step(want_logits=True)
+        toks32.append(int(t.item()))
+        logits32.append(lg.cpu().numpy())
+    torch.cuda.synchronize()
+    m32.close()
+    del m32
+
+    say("case 3B oracle: two chunks of 1024 and three decode positions (float64, host)")
+    wc = [t.cpu() for t in w]
+    st = O.prefill(cfg, wc, x[:2048], C, lr, return_state=True)
+    del wc
+    ref = st["losses"]
+    _REF["loss0"] = float(ref[0])   # chunk 0's loss is read before any update
+    w0 = [a for f in st["model"].initial_fast() for a in f.values()]
+    rfw = O.fast_weights_canonical(st)
+    first = int(np.argmax(st["last_logits"]))
+    ll = np.sort(st["last_logits"])
+    gap0 = ll[-1] - ll[-2]
+    # decode leaves the prefill state's cache and weights as they were (no
+    # update within 3 positions; the cache list is replaced, not modified)
+    d = O.decode(dict(st), 3, forced=np.array(toks + [int(np.argmax(logits[-1]))]))
+    d32 = O.decode(dict(st), 3, forced=np.array(toks32 + [int(np.argmax(logits32[-1]))]))
+
+    e_two = float(np.max(np.abs(two - ref) / np.abs(ref)))
+    e_full = float(np.max(np.abs(full[:2] - ref) / np.abs(ref)))
+    e_w = max(rel(a, b) for a, b in zip(fw, rfw))
+    e_dw = max(rel(a, b - c) for a, b, c in zip(fd, rfw, w0))
+    L = np.array(logits)
+    e_lg = float(np.abs(L - d["logits"]).max() / np.abs(d["logits"]).max())
+    say(f"  errors: losses(T=2048) {e_two:.2e} losses(full, chunks 0-1) {e_full:.2e} "
+        f"W {e_w:.2e} dW {e_dw:.2e} decode logits {e_lg:.2e}; "
+        f"full vs 2048 run {np.max(np.abs(full[:2] - two) / np.abs(two)):.2e}")
+    assert e_two < BAR and e_full < BAR and e_w < BAR and e_lg < BAR
+    assert e_dw < 0.1
+    e32 = dict(loss=float(np.max(np.abs(two32 - ref) / np.abs(ref))),
+               W=max(rel(a, b) for a, b in zip(fw32, rfw)),
+               dW=max(rel(a, b - c) for a, b, c in zip(fd32, rfw, w0)),
+               logits=float(np.abs(np.array(logits32) - d32["logits"]).max() / np.abs(d32["logits"]).max()))
+    say("  fp32 check mode errors: " + ", ".join(f"{k} {v:.2e}" for k, v in e32.items()))
+    assert e32["loss"] < 1e-4 and e32["W"] < 1e-4 and e32["logits"] < 1e-4
+    assert e32["dW"] < 1e-2
+    # the two GPU runs compute the same first two chunks
+    np.testing.assert_allclose(full[:2], two, rtol=1e-3)
+    # greedy tokens agree wherever the oracle's top-2 gap is clear
+    if gap0 > 1e-2:
+        assert toks[0] == first
+    srt = np.sort(d["logits"], axis=-1)
+    for i in range(2):
+        if srt[i, -1] - srt[i, -2] > 1e-2:
+            assert toks[i + 1] == int(np.argmax(d["logits"][i]))
+
+
+def _oracle_loss0(cfg, w, x):
+    if "loss0" not in _REF:
+        say("case 3B oracle: chunk 0 forward (float64, host)")
+        per = O.sequence_forward_losses(cfg, [t.cpu() for t in w], x[:cfg["chunk"] + 1])
+        _REF["loss0"] = float(per.mean())
+    return _REF["loss0"]
+
+
+@pytest.mark.timeout(1200)
+def test_3b_forward_without_updates_and_full_attention(c4):
+    import long_context_lm_chunk_amd as T_
+    cfg, w, x, m = c4
+    C, T = cfg["chunk"], cfg["T"]
+    tok = torch.from_numpy(x).cuda()
+    say(f"case 3B forward without updates, window {cfg['window']}, T={T}")
+    fw = m.forward(tok, C).cpu().numpy()
+    p0 = m.prefill(tok, C, 0.0).cpu().numpy()
+    torch.cuda.synchronize()
+    assert np.all(np.isfinite(fw))
+    say(f"  forward vs prefill(lr=0): {np.max(np.abs(fw - p0) / np.abs(p0)):.2e}")
+    np.testing.assert_allclose(fw, p0, rtol=1e-3)
+
+    say(f"case 3B full attention: window = T = {T}, forward and 2 decode positions")
+    fa = T_.Model(synth.config(cfg, window=T), w, max_chunk=C)
+    ffa = fa.forward(tok, C).cpu().numpy()
+    dec = []
+    for _ in range(2):
+        t, lg, ul = fa.decode_step(want_logits=True)
+        dec.append((int(t.item()), bool(torch.isfinite(lg).all().item()), float(ul.item())))
+    torch.cuda.synchronize()
+    fa.close()
+    del fa
+    assert np.all(np.isfinite(ffa))
+    say(f"  full vs window-8192 forward, chunks 0-7: {np.max(np.abs(ffa[:8] - fw[:8]) / np.abs(fw[:8])):.2e}")
+    np.testing.assert_allclose(ffa[:8], fw[:8], rtol=1e-3)
+    for t, fin, ul in dec:
+        assert 0 <= t < cfg["vocab"] and fin and np.isnan(ul)
+
+    l0 = _oracle_loss0(cfg, w, x)
+    e = max(abs(fw[0] - l0), abs(ffa[0] - l0)) / l0
+    say(f"  chunk 0 vs oracle: {e:.2e}")
+    assert e < BAR
