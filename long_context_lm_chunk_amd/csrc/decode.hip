@@ -376,36 +376,6 @@ __global__ __launch_bounds__(256) void swa_decode_part_k(const T* __restrict__ q
   }
 }
 
-// Combine the splits of head h: o = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s.
-// Any number of splits: the first wave finds M, then every output lane walks
-// the splits (every split wrote its partial, possibly empty: m = -inf, l = 0).
-template <typename T>
-__global__ void swa_decode_combine_k(const float* __restrict__ ws, int nsplit, int H, int hd,
-                                     T* __restrict__ o) {
-  __shared__ float Ms;
-  const int h = blockIdx.x, j = threadIdx.x;
-  const float* wh = ws + (int64_t)h * nsplit * (2 + hd);
-  if (j < 64) {
-    float mv = -INFINITY;
-    for (int sp = j; sp < nsplit; sp += 64) mv = fmaxf(mv, wh[(int64_t)sp * (2 + hd)]);
-    const float M = wave_max(mv);
-    if (j == 0) Ms = M;
-  }
-  __syncthreads();
-  if (j >= hd) return;
-  const float M = Ms;
-  float acc = 0.f, L = 0.f;
-  for (int sp = 0; sp < nsplit; ++sp) {
-    const float* w = wh + (int64_t)sp * (2 + hd);
-    const float mv = w[0];
-    if (mv == -INFINITY) continue;
-    const float f = __expf(mv - M);
-    L += w[1] * f;
-    acc += w[2 + j] * f;
-  }
-  o[h * hd + j] = from_f32<T>(acc / L);
-}
-
 // ---------------------------------------------------------------------------
 // Decode bookkeeping kernels (graph-safe: no memcpy/memset nodes).
 // dstate = {pos, ci}: position being read, index within the decode chunk.
@@ -477,6 +447,47 @@ __global__ __launch_bounds__(1024) void argmax_part_k(const float2* __restrict__
   }
 }
 
+// Combine the splits of head h = blockIdx.x for 16 output columns starting
+// at 16 * blockIdx.y: o = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s,
+// M = max_s m_s (a split with no key wrote m = -inf, l = 0).  Thread t takes
+// column t % 16 of the splits t / 16, t / 16 + 16, ...; the 16 groups meet in
+// LDS in a fixed order.  Any number of splits, so long windows (full
+// attention) spread their combine over H * hd / 16 workgroups.
+template <typename T>
+__global__ __launch_bounds__(256) void swa_decode_combine_k(const float* __restrict__ ws, int nsplit,
+                                                            int hd, T* __restrict__ o) {
+  __shared__ float sacc[16][17];
+  __shared__ float sl[16];
+  __shared__ float wm[4];
+  const int h = blockIdx.x, col = blockIdx.y * 16 + (threadIdx.x & 15), g = threadIdx.x >> 4;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float* wh = ws + (int64_t)h * nsplit * (2 + hd);
+  float mv = -INFINITY;
+  for (int sp = g; sp < nsplit; sp += 16) mv = fmaxf(mv, wh[(int64_t)sp * (2 + hd)]);
+  mv = wave_max(mv);
+  if (lane == 0) wm[wave] = mv;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
+  const bool live = col < hd;
+  float acc = 0.f, lp = 0.f;
+  for (int sp = g; sp < nsplit; sp += 16) {
+    const float* w = wh + (int64_t)sp * (2 + hd);
+    const float m = w[0];
+    const float f = (m == -INFINITY) ? 0.f : __expf(m - M);
+    lp += w[1] * f;
+    if (live) acc += w[2 + col] * f;
+  }
+  sacc[g][threadIdx.x & 15] = acc;
+  if ((threadIdx.x & 15) == 0) sl[g] = lp;
+  __syncthreads();
+  if (threadIdx.x < 16 && live) {
+    float A = 0.f, L = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { A += sacc[i][threadIdx.x]; L += sl[i]; }
+    o[h * hd + col] = from_f32<T>(A / L);
+  }
+}
+
 template <typename T>
 void swa_decode_t(const void* q, const void* kring, const void* vring, int64_t cap, int H, int hd,
                   int window, const int64_t* dstate, void* o, float* ws, hipStream_t s) {
@@ -489,7 +500,7 @@ void swa_decode_t(const void* q, const void* kring, const void* vring, int64_t c
 #undef CASE
     default: return;
   }
-  hipLaunchKernelGGL(swa_decode_combine_k<T>, dim3(H), dim3(128), 0, s, ws, nsplit, H, hd, (T*)o);
+  hipLaunchKernelGGL(swa_decode_combine_k<T>, dim3(H, (hd + 15) / 16), dim3(256), 0, s, ws, nsplit, hd, (T*)o);
 }
 
 template <typename T, bool LN, int OUT, bool DUAL, int UN = 4, int KS = 1>
