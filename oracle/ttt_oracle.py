@@ -16,6 +16,10 @@ What it computes (End-to-End Test-Time Training for Long Context):
   per mini-batch (chunk) of the context (forum post TL;DR, "Inner Loop");
 * only MLP layers are updated, attention and embeddings stay static, and
   only the last quarter of the blocks is updated (podcast 6:36 and 7:08);
+* optionally (``static_mlp``) each updated block also carries a second,
+  frozen MLP that keeps pre-trained knowledge (podcast 7:08); read as a
+  pre-LN residual sublayer of the same shape and activation placed after
+  the fast MLP, so the gradient into the fast MLP passes through it;
 * window ~8K and mini-batch ~1K tokens at the 3B operating point
   (podcast 6:36).
 
@@ -45,7 +49,8 @@ notes of the repository):
   same loss.
 
 Parity pins (tests/test_oracle_pins.py): finite differences of the fast
-weight gradient, lr = 0 against a one-shot sequence forward, window >= T
+weight gradient (also through the frozen second MLP), a zero second MLP
+reducing to the plain block, lr = 0 against a one-shot sequence forward, window >= T
 against library causal attention, U = 0 and V = 2 closed forms, RoPE shift
 invariance, first-order descent, planted-repeat loss drop, decode against
 prefill.
@@ -205,15 +210,24 @@ class OracleModel:
         L = cfg["n_layers"]
         names = ["Wq", "Wk", "Wv", "Wo"] + (["W1", "W2"] if cfg["mlp"] == "gelu" else ["Wg", "Wu", "Wd"])
         self.mlp_names = names[4:]
+        self.first_fast = L - cfg["n_fast"]
+        # the frozen second MLP of the fast blocks (podcast 7:08), when the
+        # configuration asks for it: same shapes and activation as the first
+        self.static_mlp = bool(cfg.get("static_mlp", 0))
         w = [_to_f64(t) for t in weights]
-        per = len(names)
-        assert len(w) == 2 + L * per, "weight count does not match the configuration"
+        n_static = cfg["n_fast"] * len(self.mlp_names) if self.static_mlp else 0
+        assert len(w) == 2 + L * len(names) + n_static, "weight count does not match the configuration"
         self.E = w[0]
         self.U = w[-1]
         self.layers = []
+        self.static = []
+        i = 1
         for l in range(L):
-            self.layers.append({n: w[1 + l * per + j] for j, n in enumerate(names)})
-        self.first_fast = L - cfg["n_fast"]
+            self.layers.append({n: w[i + j] for j, n in enumerate(names)})
+            i += len(names)
+            if self.static_mlp and l >= self.first_fast:
+                self.static.append({n: w[i + j] for j, n in enumerate(self.mlp_names)})
+                i += len(self.mlp_names)
 
     def initial_fast(self):
         """Copies of the MLP matrices of the last ``n_fast`` layers."""
@@ -295,9 +309,16 @@ def forward_chunk(model: OracleModel, fast, cache, tokens, pos0: int):
         h2 = h + o.reshape(n, -1) @ Wl["Wo"]
         b, r2 = layer_norm(h2, eps)
         m, mact = _mlp_forward(cfg, Wm, b)
-        acts.append(dict(h=h, a=a, r1=r1, q=q, k=k, v=v, kall=kall, vall=vall, p=p,
-                         ncache=len(cpos), h2=h2, b=b, r2=r2, mact=mact))
+        A = dict(h=h, a=a, r1=r1, q=q, k=k, v=v, kall=kall, vall=vall, p=p,
+                 ncache=len(cpos), h2=h2, b=b, r2=r2, mact=mact)
         h = h2 + m
+        if fl >= 0 and model.static_mlp:
+            # frozen second MLP after the fast one, its own pre-LayerNorm
+            c, r3 = layer_norm(h, eps)
+            m2, mact2 = _mlp_forward(cfg, model.static[fl], c)
+            A.update(c=c, r3=r3, mact2=mact2)
+            h = h + m2
+        acts.append(A)
     f, rf = layer_norm(h, eps)
     logits = f @ model.U
     return dict(layers=acts, hL=h, f=f, rf=rf, logits=logits, pos=pos, cos=cos, sin=sin)
@@ -319,6 +340,10 @@ def backward_chunk(model: OracleModel, fast, fw, dlogits):
         Wl = model.layers[l]
         fl = l - model.first_fast
         need = l > model.first_fast
+        if model.static_mlp:
+            # through the frozen second MLP (its weight gradient is not used)
+            _, dc = _mlp_backward(cfg, model.static[fl], A["c"], A["mact2"], dh, True)
+            dh = dh + layer_norm_backward(dc, A["c"], A["r3"])
         g, db = _mlp_backward(cfg, fast[fl], A["b"], A["mact"], dh, need)
         grads[fl] = g
         if not need:

@@ -107,11 +107,20 @@ def gen_tokens(cfg: dict, T: int | None = None, seed: int | None = None,
     return (x, copied) if return_copies else x
 
 
+def _has_static(cfg: dict, l: int) -> bool:
+    """Layer l carries the frozen second MLP (fast layers of a static_mlp
+    variant)."""
+    return bool(cfg.get("static_mlp", 0)) and l >= cfg["n_layers"] - cfg["n_fast"]
+
+
 def weight_names(cfg: dict) -> list[str]:
     names = ["E"]
     mlp = ["W1", "W2"] if cfg["mlp"] == "gelu" else ["Wg", "Wu", "Wd"]
+    smlp = ["S1", "S2"] if cfg["mlp"] == "gelu" else ["Sg", "Su", "Sd"]
     for l in range(cfg["n_layers"]):
         names += [f"L{l}.{n}" for n in ["Wq", "Wk", "Wv", "Wo"] + mlp]
+        if _has_static(cfg, l):
+            names += [f"L{l}.{n}" for n in smlp]
     names.append("U")
     return names
 
@@ -120,8 +129,10 @@ def weight_shapes(cfg: dict) -> list[tuple[int, int]]:
     d, F, V = cfg["d_model"], cfg["d_ff"], cfg["vocab"]
     shapes = [(V, d)]
     mlp = [(d, F), (F, d)] if cfg["mlp"] == "gelu" else [(d, F), (d, F), (F, d)]
-    for _ in range(cfg["n_layers"]):
+    for l in range(cfg["n_layers"]):
         shapes += [(d, d)] * 4 + mlp
+        if _has_static(cfg, l):
+            shapes += mlp
     shapes.append((d, V))
     return shapes
 

@@ -150,13 +150,16 @@ def test_cross_entropy_two_class_closed_form():
 
 # ---------------------------------------------------------- whole inner loop
 
-@pytest.mark.parametrize("n_fast,mlp", [(1, "gelu"), (2, "gelu"), (2, "swiglu"), (3, "swiglu")])
-def test_fast_weight_gradient_finite_differences(n_fast, mlp):
+@pytest.mark.parametrize("n_fast,mlp,static", [(1, "gelu", 0), (2, "gelu", 0), (2, "swiglu", 0),
+                                               (3, "swiglu", 0), (1, "swiglu", 1), (2, "gelu", 1)])
+def test_fast_weight_gradient_finite_differences(n_fast, mlp, static):
     """The spec pin: analytic fast-weight gradient of a chunk loss vs
     central finite differences, relative error <= 1e-6.  The chunk is the
     second one, so attention sees cached keys that must stay constant
-    (stop-gradient); n_fast >= 2 exercises the attention backward."""
-    cfg = tiny_cfg(n_fast=n_fast, mlp=mlp)
+    (stop-gradient); n_fast >= 2 exercises the attention backward; static = 1
+    puts the frozen second MLP after every fast one, so the gradient passes
+    through it."""
+    cfg = tiny_cfg(n_fast=n_fast, mlp=mlp, static_mlp=static)
     w = weights_std(cfg, 0.3)
     x = synth.gen_tokens(cfg)
     model = O.OracleModel(cfg, w)
@@ -194,6 +197,36 @@ def test_fast_weight_gradient_finite_differences(n_fast, mlp):
     fd = (loss_dir(h) - loss_dir(-h)) / (2 * h)
     an = sum(float((grads[i][n] * dirs[i][n]).sum()) for i in range(n_fast) for n in grads[i])
     assert abs(fd - an) / abs(an) <= 1e-6
+
+
+@pytest.mark.parametrize("mlp", ["gelu", "swiglu"])
+def test_zero_static_mlp_is_the_plain_block(mlp):
+    """Special case: a frozen second MLP whose output projection is zero adds
+    nothing, forward or backward, so losses and updated fast weights equal
+    those of the blocks without it, exactly; with random weights it does
+    change them, and it is never updated."""
+    cfg = tiny_cfg(mlp=mlp)
+    cfs = synth.config(cfg, static_mlp=1)
+    w = weights_std(cfg, 0.3)
+    ws = weights_std(cfs, 0.3)
+    names, names_s = synth.weight_names(cfg), synth.weight_names(cfs)
+    by = dict(zip(names, w))
+    z = [by[n] if n in by else (torch.zeros_like(t) if n.endswith(("S2", "Sd")) else t)
+         for n, t in zip(names_s, ws)]
+    x = synth.gen_tokens(cfg)
+    a = O.prefill(cfg, w, x, 8, 0.05)
+    b = O.prefill(cfs, z, x, 8, 0.05)
+    np.testing.assert_array_equal(a["losses"], b["losses"])
+    for fa, fb in zip(a["fast"], b["fast"]):
+        for n in fa:
+            np.testing.assert_array_equal(fa[n], fb[n])
+    r = [by[n] if n in by else t for n, t in zip(names_s, ws)]
+    c = O.prefill(cfs, r, x, 8, 0.05, return_state=True)
+    assert np.abs(c["losses"] - a["losses"]).max() > 1e-3
+    for st, n in zip(c["model"].static, range(cfg["n_fast"])):
+        l = cfg["n_layers"] - cfg["n_fast"] + n
+        for k, arr in st.items():
+            np.testing.assert_array_equal(arr, ws[names_s.index(f"L{l}.{k.replace('W', 'S')}")].numpy())
 
 
 def test_lr_zero_is_plain_swa_forward():
