@@ -62,6 +62,11 @@ def prefill_flops(cfg, T):
     fwd = 2 * (T * L * (4 * d * d + k * d * F) + L * d * 2 * sum_n + (T - 1) * d * V)
     bwd = 2 * ((T - 1) * d * V + T * (k + 1) * d * F + (q - 1) * T * (2 * k * d * F + 4 * d * d)
                + (q - 1) * d * (2 * sum_n + 2 * sum_m))
+    if cfg.get("static_mlp"):
+        # frozen second MLP of every fast block: its forward, and the two
+        # input-gradient products of its backward (no weight gradient)
+        fwd += 2 * T * q * k * d * F
+        bwd += 2 * T * q * k * d * F
     return float(fwd + bwd)
 
 
@@ -71,7 +76,8 @@ def forward_flops(cfg, T):
     L, d, F, V, W = (cfg[k] for k in ("n_layers", "d_model", "d_ff", "vocab", "window"))
     k = 3 if cfg["mlp"] == "swiglu" else 2
     sum_n = sum(min(t + 1, W) for t in range(T))
-    return float(2 * (T * L * (4 * d * d + k * d * F) + L * d * 2 * sum_n + (T - 1) * d * V))
+    extra = 2 * T * cfg["n_fast"] * k * d * F if cfg.get("static_mlp") else 0
+    return float(2 * (T * L * (4 * d * d + k * d * F) + L * d * 2 * sum_n + (T - 1) * d * V) + extra)
 
 
 def sgd_bytes_per_launch(cfg, T):
@@ -140,6 +146,8 @@ def main():
     ap.add_argument("--decode-tokens", type=int, default=2048,
                     help="greedy decode tokens timed after the prefill (2048 reach two "
                          "decode-time updates at chunk 1024)")
+    ap.add_argument("--static-mlp", action="store_true",
+                    help="the variant whose fast blocks also carry a frozen second MLP")
     ap.add_argument("--no-static", action="store_true",
                     help="skip the reads without updates (window 8192, and full attention)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -162,6 +170,8 @@ def main():
     import long_context_lm_chunk_amd as T_
 
     cfg = synth.config(args.config)
+    if args.static_mlp:
+        cfg = synth.config(cfg, static_mlp=1, name=cfg["name"] + "+static-second-MLP")
     T = args.T or cfg["T"]
     dev = torch.device("cuda:0")
     t_setup = time.perf_counter()
@@ -336,6 +346,7 @@ def main():
                    "window": cfg["window"], "layers": cfg["n_layers"], "d_model": cfg["d_model"],
                    "heads": cfg["n_heads"], "d_ff": cfg["d_ff"], "vocab": cfg["vocab"],
                    "fast_layers": cfg["n_fast"], "lr": cfg["lr"], "steps_per_chunk": 1,
+                   "static_second_mlp": bool(cfg.get("static_mlp", 0)),
                    "parallelism": "single GPU"},
         "decode_ms_per_token": None if dec is None else dec["ms_per_token"],
         "decode": dec,

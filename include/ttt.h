@@ -72,6 +72,10 @@ typedef struct {
   float ln_eps;          /* 1e-5 */
   int32_t max_chunk;     /* largest chunk a prefill call may use */
   int32_t prefill_block; /* tokens per frozen-layer block; 0 = default (8192) */
+  int32_t static_mlp;    /* 1: every fast block also has a frozen second MLP (podcast
+                            7:08: pre-trained knowledge kept static beside the updated
+                            MLP), a pre-LN residual sublayer of the same shape and
+                            activation after the fast MLP; 0: none */
 } ttt_config;
 
 /* Workspace bytes needed for `cfg` (device memory, 256-byte aligned). */
@@ -84,7 +88,9 @@ int ttt_workspace_bytes(const ttt_config* cfg, size_t* bytes);
  *   E [vocab][d_model];
  *   for each layer: Wq, Wk, Wv, Wo [d_model][d_model], then
  *     GELU:   W1 [d_model][d_ff], W2 [d_ff][d_model]
- *     SwiGLU: Wg [d_model][d_ff], Wu [d_model][d_ff], Wd [d_ff][d_model];
+ *     SwiGLU: Wg [d_model][d_ff], Wu [d_model][d_ff], Wd [d_ff][d_model],
+ *     and, in each of the last n_fast layers when static_mlp = 1, the
+ *     frozen second MLP's matrices in the same order and shapes;
  *   U [d_model][vocab].
  * Every matrix is [in][out] row-major (a layer computes y = x W).  The
  * weights are copied into the workspace (in the library's own layout), so

@@ -33,6 +33,7 @@ class TTTConfig(ctypes.Structure):
         ("window", ctypes.c_int32), ("n_fast", ctypes.c_int32), ("mlp", ctypes.c_int32),
         ("dtype", ctypes.c_int32), ("rope_base", ctypes.c_float), ("ln_eps", ctypes.c_float),
         ("max_chunk", ctypes.c_int32), ("prefill_block", ctypes.c_int32),
+        ("static_mlp", ctypes.c_int32),
     ]
 
 
@@ -114,7 +115,7 @@ def config_from_dict(cfg: dict, max_chunk: int | None = None, prefill_block: int
         n_fast=cfg["n_fast"], mlp=TTT_MLP_SWIGLU if cfg["mlp"] == "swiglu" else TTT_MLP_GELU,
         dtype=TTT_BF16 if dt == "bf16" else TTT_FP32, rope_base=cfg.get("rope_base", 10000.0),
         ln_eps=cfg.get("ln_eps", 1e-5), max_chunk=max_chunk or cfg["chunk"],
-        prefill_block=prefill_block)
+        prefill_block=prefill_block, static_mlp=int(bool(cfg.get("static_mlp", 0))))
 
 
 def workspace_bytes(c: TTTConfig) -> int:

@@ -101,6 +101,10 @@ struct Layer {
   void* ktring = nullptr;                          // [d][cap]: K transposed, key-permuted (fast blocks: dQ)
   void* wqkvT = nullptr;  // [d][3d] and [d][d]: transposed copies for the input-gradient
   void* woT = nullptr;    // products (fast blocks above the first)
+  // frozen second MLP of a fast block (static_mlp): forward layout like
+  // wup / wdn, and transposed copies for the input-gradient products
+  void* swup = nullptr; void* swdn = nullptr;    // [F2][d], [d][F]
+  void* swupT = nullptr; void* swdnT = nullptr;  // [d][F2], [F][d]
   int64_t cap = 0;
 };
 
@@ -109,6 +113,9 @@ struct PB {  // phase-B buffers of one fast layer (chunk rows)
   float* mean1 = nullptr; float* rstd1 = nullptr; float* mean2 = nullptr; float* rstd2 = nullptr;
   void* a = nullptr; void* q = nullptr; void* o = nullptr; float* lse = nullptr;
   void* b = nullptr; void* z = nullptr; void* act = nullptr;
+  // frozen second MLP: its input (the residual after the fast MLP), LayerNorm
+  // statistics and pre-activations (for the activation backward)
+  float* xm = nullptr; float* mean3 = nullptr; float* rstd3 = nullptr; void* z2 = nullptr;
 };
 
 }  // namespace
@@ -140,6 +147,7 @@ struct ttt_model {
   void* qkvB = nullptr;
   float* pmax = nullptr; float* psum = nullptr; float* tlog = nullptr; float* lse_ce = nullptr;
   float* zce = nullptr;                 // the chunk's logits [C][V] fp32 (head statistics pass)
+  void* cS = nullptr; void* actS = nullptr; void* dzS = nullptr;   // second-MLP temporaries [C][..]
   void* G = nullptr;
   float* dh = nullptr; void* dh_lo = nullptr; void* dz = nullptr;
   // transposed operands of the weight-gradient products, one set per fast
@@ -200,6 +208,7 @@ int check_config(const ttt_config* c) {
   }
   if (c->max_chunk < 1 || c->max_chunk > (1 << 16)) return fail(TTT_ERR_CONFIG, "max_chunk must be in [1, 65536]");
   if (c->prefill_block < 0) return fail(TTT_ERR_CONFIG, "prefill_block must be >= 0");
+  if (c->static_mlp != 0 && c->static_mlp != 1) return fail(TTT_ERR_CONFIG, "static_mlp must be 0 or 1");
   if (!(c->ln_eps > 0.f) || !(c->rope_base > 1.f)) return fail(TTT_ERR_CONFIG, "ln_eps > 0 and rope_base > 1 required");
   return TTT_OK;
 }
@@ -231,6 +240,12 @@ size_t layout(ttt_model* m, void* base) {
     if (l > m->f0) {
       ly.wqkvT = cv.take<void>((size_t)3 * d * d * es);
       ly.woT = cv.take<void>((size_t)d * d * es);
+    }
+    if (m->c.static_mlp && l >= m->f0) {
+      ly.swup = cv.take<void>((size_t)F2 * d * es);
+      ly.swdn = cv.take<void>((size_t)d * F * es);
+      ly.swupT = cv.take<void>((size_t)F2 * d * es);
+      ly.swdnT = cv.take<void>((size_t)d * F * es);
     }
   }
   m->UT = cv.take<void>((size_t)V * d * es);
@@ -281,6 +296,17 @@ size_t layout(ttt_model* m, void* base) {
     b.b = cv.take<void>((size_t)C * d * es);
     b.z = cv.take<void>((size_t)C * F2 * es);
     b.act = cv.take<void>((size_t)C * F * es);
+    if (m->c.static_mlp) {
+      b.xm = cv.take<float>((size_t)C * d * 4);
+      b.mean3 = cv.take<float>((size_t)C * 4);
+      b.rstd3 = cv.take<float>((size_t)C * 4);
+      b.z2 = cv.take<void>((size_t)C * F2 * es);
+    }
+  }
+  if (m->c.static_mlp) {
+    m->cS = cv.take<void>((size_t)C * d * es);
+    m->actS = cv.take<void>((size_t)C * F * es);
+    m->dzS = cv.take<void>((size_t)C * F2 * es);
   }
   m->xL = cv.take<float>((size_t)C * d * 4);
   m->meanf = cv.take<float>((size_t)C * 4);
@@ -388,9 +414,10 @@ int run_gemm(ttt_model* m, const GemmParams& p0, bool a_kc, bool b_kc, int epi, 
   int rc;
   {
     Scope t0(m, CLS_GEMM, s, fl);
-    // class 5 is one kernel symbol: the up-projection with a single B (the
-    // frozen blocks); the fast blocks' two-B launches are a different kernel
-    const bool up1 = (epi == EPI_GELU || epi == EPI_SWIGLU) && p.B2 == nullptr;
+    // class 5 is one kernel symbol: the up-projection with a single B over a
+    // whole block of rows (the frozen blocks, unsplit); the fast blocks'
+    // two-B launches and the chunk-sized second-MLP launches are other kernels
+    const bool up1 = (epi == EPI_GELU || epi == EPI_SWIGLU) && p.B2 == nullptr && !allow_split;
     Scope t4(m, epi == EPI_SGD ? CLS_SGD : up1 ? CLS_MLP_UP : NCLS - 1, s,
              (epi == EPI_SGD || up1) ? fl : 0.0);
     rc = gemm(p, m->bf, a_kc, b_kc, epi, out_f32, s);
@@ -455,6 +482,14 @@ int block_fwd(ttt_model* m, int l, int64_t pos0, int nb, float* x, const float2*
   GemmParams gd;
   gd.A = m->actA; gd.lda = F; gd.B = ly.wdn; gd.ldb = F; gd.M = nb; gd.N = d; gd.K = F;
   gd.C = x; gd.ldc = d; gd.R = x; gd.ldr = d;
+  rc = run_gemm(m, gd, true, true, EPI_RESID, true, s, false);
+  if (rc || !ly.swup) return rc;
+  // the frozen second MLP of a fast block: LN3 -> up + activation -> down + residual
+  layernorm_fwd(x, d, nb, d, m->c.ln_eps, m->aA, d, nullptr, nullptr, bf, s);
+  gu.B = ly.swup;
+  rc = run_gemm(m, gu, true, true, m->c.mlp == TTT_MLP_SWIGLU ? EPI_SWIGLU : EPI_GELU, false, s, false);
+  if (rc) return rc;
+  gd.B = ly.swdn;
   return run_gemm(m, gd, true, true, EPI_RESID, true, s, false);
 }
 
@@ -515,10 +550,24 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
     gu.A = b.b; gu.lda = d; gu.B = ly.wup; gu.B2 = m->fast[j].s_up; gu.ldb = d; gu.M = n; gu.N = F2; gu.K = d;
     gu.C = b.z; gu.ldc = F2; gu.C2 = b.act; gu.ldc2 = F;
     rc = run_gemm(m, gu, true, true, upepi, false, s); if (rc) return rc;
+    float* xout = (j + 1 < q) ? m->pb[j + 1].xin : m->xL;
     GemmParams gd;
     gd.A = b.act; gd.lda = F; gd.B = ly.wdn; gd.B2 = m->fast[j].s_dn; gd.ldb = F; gd.M = n; gd.N = d; gd.K = F;
-    gd.C = (j + 1 < q) ? m->pb[j + 1].xin : m->xL; gd.ldc = d; gd.R = x2; gd.ldr = d;
+    gd.C = ly.swup ? b.xm : xout; gd.ldc = d; gd.R = x2; gd.ldr = d;
     rc = run_gemm(m, gd, true, true, EPI_RESID, true, s); if (rc) return rc;
+    if (ly.swup) {
+      // frozen second MLP: LN3 -> up + activation (pre-activations kept for
+      // the backward) -> down + residual
+      layernorm_fwd(b.xm, d, n, d, eps, m->cS, d, b.mean3, b.rstd3, bf, s);
+      GemmParams su;
+      su.A = m->cS; su.lda = d; su.B = ly.swup; su.ldb = d; su.M = n; su.N = F2; su.K = d;
+      su.C = b.z2; su.ldc = F2; su.C2 = m->actS; su.ldc2 = F;
+      rc = run_gemm(m, su, true, true, upepi, false, s); if (rc) return rc;
+      GemmParams sd;
+      sd.A = m->actS; sd.lda = F; sd.B = ly.swdn; sd.ldb = F; sd.M = n; sd.N = d; sd.K = F;
+      sd.C = xout; sd.ldc = d; sd.R = b.xm; sd.ldr = d;
+      rc = run_gemm(m, sd, true, true, EPI_RESID, true, s); if (rc) return rc;
+    }
   }
   layernorm_fwd(m->xL, d, n, d, eps, m->fN, d, m->meanf, m->rstdf, bf, s);
 
@@ -565,6 +614,20 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
     // gradients transposed to [features][tokens] (tokens padded to a multiple
     // of 8 with zeros, which add nothing to the reduction).
     const int np = (n + 7) & ~7;
+    if (ly.swup) {
+      // back through the frozen second MLP (no weight gradient): dz2 =
+      // act'(z2) (dh . Wdn2), dc = dz2 . Wup2, dh += LN3_backward(dc)
+      GemmParams sa2;
+      sa2.A = m->dh_lo; sa2.lda = d; sa2.B = ly.swdnT; sa2.ldb = d; sa2.M = n; sa2.N = F; sa2.K = d;
+      sa2.C = m->dzS; sa2.ldc = F2; sa2.Z = b.z2; sa2.ldz = F2; sa2.act_swiglu = m->c.mlp == TTT_MLP_SWIGLU;
+      rc = run_gemm(m, sa2, true, true, EPI_ACTBWD, false, s); if (rc) return rc;
+      GemmParams sb2;
+      sb2.A = m->dzS; sb2.lda = F2; sb2.B = ly.swupT; sb2.ldb = F2; sb2.M = n; sb2.N = d; sb2.K = F2;
+      sb2.C = m->dtmp; sb2.ldc = d; sb2.split_defer = &nsl;
+      nsl = 1;
+      rc = run_gemm(m, sb2, true, true, EPI_STORE, true, s); if (rc) return rc;
+      layernorm_bwd_acc(dy_of(), b.xm, b.mean3, b.rstd3, n, d, m->dh, m->dh_lo, bf, s, nsl, (int64_t)n * d);
+    }
     // dz = act'(z) (dh . Wdn): the activation backward runs in the product's
     // epilogue (the product reads the weights before their update: Wdn^T
     // [F][d]).  dz is rewritten here: the update stream must have read the
@@ -730,6 +793,10 @@ void decode_body(ttt_model* m, hipStream_t s) {
     const void* ddn = j >= 0 ? m->fast[j].s_dn : nullptr;
     dgemv_ln_act(ly.wup, dup, F, d, m->xd, eps, sw, m->actd, bf, s);   // LN2 -> up -> act
     dgemv_vec(ly.wdn, ddn, d, F, m->actd, m->xd, m->xd, nullptr, nullptr, nullptr, bf, s);
+    if (ly.swup) {   // frozen second MLP
+      dgemv_ln_act(ly.swup, nullptr, F, d, m->xd, eps, sw, m->actd, bf, s);
+      dgemv_vec(ly.swdn, nullptr, d, F, m->actd, m->xd, m->xd, nullptr, nullptr, nullptr, bf, s);
+    }
   }
   dgemv_ln_head(m->U, V, d, m->xd, eps, m->logits, m->amax, bf, s);
   argmax_part(m->amax, dgemv_blocks(V), m->cur_tok, m->hist, m->dstate, true, s);
@@ -795,9 +862,11 @@ int ttt_model_load(const ttt_config* cfg, const void* const* weights, int32_t n_
   if (rc) return rc;
   if (!out) return fail(TTT_ERR_ARG, "out is NULL");
   *out = nullptr;
-  const int per = 4 + (cfg->mlp == TTT_MLP_SWIGLU ? 3 : 2);
-  if (!weights || n_weights != 2 + cfg->n_layers * per)
-    return fail(TTT_ERR_ARG, "n_weights must be 2 + n_layers * (4 + mlp matrices)");
+  const int nm = cfg->mlp == TTT_MLP_SWIGLU ? 3 : 2;
+  const int per = 4 + nm;
+  if (!weights || n_weights != 2 + cfg->n_layers * per + (cfg->static_mlp ? cfg->n_fast * nm : 0))
+    return fail(TTT_ERR_ARG, "n_weights must be 2 + n_layers * (4 + mlp matrices) "
+                             "(+ n_fast * mlp matrices with static_mlp)");
   for (int i = 0; i < n_weights; ++i)
     if (!weights[i]) return fail(TTT_ERR_ARG, "a weight pointer is NULL");
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255))
@@ -836,20 +905,29 @@ int ttt_model_load(const ttt_config* cfg, const void* const* weights, int32_t n_
   // E [V][d] stays as is; U canonical [d][V] -> [V][d]
   convert_weight(weights[0], V, d, false, -1, m->E, bf, s);
   convert_weight(weights[n_weights - 1], d, V, true, -1, m->U, bf, s);
-  for (int l = 0; l < m->L; ++l) {
-    const void* const* w = weights + 1 + l * per;
+  auto load_mlp = [&](const void* const* w, void* up, void* dn) {
+    if (cfg->mlp == TTT_MLP_SWIGLU) {
+      convert_weight(w[0], d, F, true, 0, up, bf, s);
+      convert_weight(w[1], d, F, true, 1, up, bf, s);
+      convert_weight(w[2], F, d, true, -1, dn, bf, s);
+    } else {
+      convert_weight(w[0], d, F, true, -1, up, bf, s);
+      convert_weight(w[1], F, d, true, -1, dn, bf, s);
+    }
+  };
+  const void* const* w = weights + 1;
+  for (int l = 0; l < m->L; ++l, w += per) {
     Layer& ly = m->layers[l];
     char* qkv = static_cast<char*>(ly.wqkv);
     for (int p = 0; p < 3; ++p)   // Wq, Wk, Wv [d][d] -> rows p*d.. of [3d][d]
       convert_weight(w[p], d, d, true, -1, qkv + (size_t)p * d * d * m->es, bf, s);
     convert_weight(w[3], d, d, true, -1, ly.wo, bf, s);
-    if (cfg->mlp == TTT_MLP_SWIGLU) {
-      convert_weight(w[4], d, F, true, 0, ly.wup, bf, s);
-      convert_weight(w[5], d, F, true, 1, ly.wup, bf, s);
-      convert_weight(w[6], F, d, true, -1, ly.wdn, bf, s);
-    } else {
-      convert_weight(w[4], d, F, true, -1, ly.wup, bf, s);
-      convert_weight(w[5], F, d, true, -1, ly.wdn, bf, s);
+    load_mlp(w + 4, ly.wup, ly.wdn);
+    if (ly.swup) {   // the frozen second MLP follows the layer's own matrices
+      w += nm;
+      load_mlp(w + 4, ly.swup, ly.swdn);
+      transpose(ly.swup, m->F2, d, d, ly.swupT, m->F2, m->F2, bf, s);
+      transpose(ly.swdn, d, F, F, ly.swdnT, d, d, bf, s);
     }
   }
   // transposed copies read by the input-gradient products

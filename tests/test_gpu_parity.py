@@ -195,6 +195,22 @@ def test_prefill_small_models(dtype, mlp, hd, q):
     assert r["dloss"] < (1e-2 if dtype == "fp32" else 0.2)
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("mlp,hd,q", [("swiglu", 32, 2), ("gelu", 64, 1), ("swiglu", 128, 3)])
+def test_prefill_static_second_mlp(dtype, mlp, hd, q):
+    """The variant whose fast blocks also carry a frozen second MLP after the
+    updated one: the gradient into every fast MLP passes through it (for the
+    lowest fast block too), several phase-A blocks, a ragged last chunk."""
+    H = 2 if hd <= 64 else 1
+    cfg = small_cfg(mlp=mlp, head_dim=hd, n_heads=H, d_model=H * hd, n_fast=q,
+                    n_layers=max(3, q + 1), static_mlp=1)
+    r = run_pair(cfg, dtype=dtype, std=0.05, prefill_block=64)
+    assert r["loss"] < BAR[dtype] and r["W"] < BAR[dtype]
+    assert r["loss0"] < BAR[dtype]
+    assert r["dW"] < (1e-2 if dtype == "fp32" else 0.1)
+    assert r["dloss"] < (1e-2 if dtype == "fp32" else 0.2)
+
+
 def test_prefill_two_steps_per_chunk_fp32():
     r = run_pair(small_cfg(n_fast=2), steps=2, std=0.05)
     assert r["loss"] < 1e-4 and r["W"] < 1e-4
@@ -226,14 +242,16 @@ def test_prefill_125m_shape_prefix_fp32_check_mode():
     assert r["loss"] < BAR["fp32"] and r["W"] < BAR["fp32"]
 
 
-def test_decode_teacher_forced_matches_oracle():
+@pytest.mark.parametrize("static", [0, 1])
+def test_decode_teacher_forced_matches_oracle(static):
     """Prefill, then greedy decode through two decode-chunk updates; the
     oracle replays the emitted tokens (teacher forcing) and must give the
     same logits and update losses; the argmax must agree wherever the
-    oracle's top-2 gap is clear."""
+    oracle's top-2 gap is clear.  static = 1: fast blocks with the frozen
+    second MLP."""
     T_ = _gpu()
-    cfg = small_cfg(T=64, chunk=16, n_fast=2, window=24)
-    say("case decode small fp32")
+    cfg = small_cfg(T=64, chunk=16, n_fast=2, window=24, static_mlp=static)
+    say(f"case decode small fp32 static_mlp={static}")
     w = [t.float() for t in synth.gen_weights(cfg, std=0.3)]
     x = synth.gen_tokens(cfg, T=64)
     m = T_.Model(cfg, [t.cuda() for t in w], max_chunk=16)
@@ -271,8 +289,8 @@ def _chunk_means(per_pos, T, C):
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
-@pytest.mark.parametrize("window,block", [(48, 256), (48, 64), (1000, 0)])
-def test_forward_without_updates_matches_oracle(dtype, window, block):
+@pytest.mark.parametrize("window,block,static", [(48, 256, 0), (48, 64, 0), (1000, 0, 0), (48, 256, 1)])
+def test_forward_without_updates_matches_oracle(dtype, window, block, static):
     """The context read with the loaded weights and no update: per-chunk
     losses equal chunk means of the oracle's one-shot forward of the whole
     sequence (no chunking, no cache), and the prefill's losses at lr = 0.
@@ -280,8 +298,9 @@ def test_forward_without_updates_matches_oracle(dtype, window, block):
     (their rings hold window + chunk positions); block 64 spans several
     batches; window 1000 > T is full causal attention."""
     T_ = _gpu()
-    cfg = small_cfg(window=window, dtype=dtype, mlp="gelu" if window == 1000 else "swiglu")
-    say(f"case forward dtype={dtype} window={window} block={block}")
+    cfg = small_cfg(window=window, dtype=dtype, mlp="gelu" if window == 1000 else "swiglu",
+                    static_mlp=static)
+    say(f"case forward dtype={dtype} window={window} block={block} static_mlp={static}")
     w = synth.gen_weights(cfg, std=0.05)
     if dtype == "fp32":
         w = [t.float() for t in w]

@@ -186,3 +186,36 @@ def test_3b_forward_without_updates_and_full_attention(c4):
     e = max(abs(fw[0] - l0), abs(ffa[0] - l0)) / l0
     say(f"  chunk 0 vs oracle: {e:.2e}")
     assert e < BAR
+
+
+@pytest.mark.timeout(1200)
+def test_3b_static_second_mlp_first_chunks_match_oracle():
+    """The variant whose 7 fast blocks also carry a frozen second MLP, at the
+    3B shape in the same launch configuration: a 2048-token prefill (two
+    chunks of 1024, frozen blocks batched over 8192) against the oracle,
+    losses, fast matrices and their exact changes."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import long_context_lm_chunk_amd as T_
+    cfg = synth.config("c4", static_mlp=1)
+    C, lr = cfg["chunk"], cfg["lr"]
+    say("case 3B static second MLP: prefill T=2048")
+    w = synth.gen_weights(cfg, device="cuda:0")
+    x = synth.gen_tokens(cfg, T=2048)
+    m = T_.Model(cfg, w, max_chunk=C)
+    got = m.prefill(torch.from_numpy(x).cuda(), C, lr).cpu().numpy()
+    fw = [t.cpu().numpy() for t in m.fast_weights()]
+    fd = [t.cpu().numpy() for t in m.fast_weights(delta=True)]
+    torch.cuda.synchronize()
+    m.close()
+    say("case 3B static second MLP: oracle, two chunks (float64, host)")
+    wc = [t.cpu() for t in w]
+    del w
+    st = O.prefill(cfg, wc, x, C, lr, return_state=True)
+    rfw = O.fast_weights_canonical(st)
+    w0 = [a for f in st["model"].initial_fast() for a in f.values()]
+    e_l = float(np.max(np.abs(got - st["losses"]) / np.abs(st["losses"])))
+    e_w = max(rel(a, b) for a, b in zip(fw, rfw))
+    e_dw = max(rel(a, b - c) for a, b, c in zip(fd, rfw, w0))
+    say(f"  errors: losses {e_l:.2e} W {e_w:.2e} dW {e_dw:.2e}")
+    assert e_l < BAR and e_w < BAR and e_dw < 0.1
