@@ -316,8 +316,8 @@ def main():
                    else None)
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic,
-                "kernel": "gemm_kernel<bf16, A k-contig, B k-contig, SGD epilogue> (fused weight "
-                          "gradient + SGD of the fast MLPs: [d][F] and [2F][d] over the chunk's tokens)",
+                "kernel": "gemm256_kernel<SGD epilogue, bf16> (fused weight gradient + SGD of the "
+                          "fast MLPs: [d][F] and [2F][d] over the chunk's tokens, 256x256 tiles)",
                 "algorithmic_bytes_per_launch": round(by), "flops_per_launch": round(sgd_flops_per_launch(
                     dict(cfg, T=T), T)),
                 "avg_launch_ms": round(avg_ms, 4), "launches_per_step": sg["launches"],
