@@ -146,6 +146,9 @@ def main():
     ap.add_argument("--decode-tokens", type=int, default=2048,
                     help="greedy decode tokens timed after the prefill (2048 reach two "
                          "decode-time updates at chunk 1024)")
+    ap.add_argument("--contexts", type=int, default=1,
+                    help="also time this many independent contexts prefilled at once "
+                         "(one model each, chains interleaved on their own streams)")
     ap.add_argument("--static-mlp", action="store_true",
                     help="the variant whose fast blocks also carry a frozen second MLP")
     ap.add_argument("--no-static", action="store_true",
@@ -164,6 +167,10 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    if args.contexts > 1:
+        # every context brings its own four streams: enough hardware queues
+        # for them not to share one (set before the runtime starts)
+        os.environ.setdefault("GPU_MAX_HW_QUEUES", str(min(32, 4 * args.contexts + 2)))
     import numpy as np
     import torch
     import synth
@@ -255,6 +262,33 @@ def main():
     if args.decode_tokens > 0:
         dec = timed_decode(model, args.decode_tokens)
         print(f"# decode: {dec}", file=sys.stderr, flush=True)
+
+    # Several independent contexts prefilled at once (one model each: own
+    # fast weights and rings; the same weights, other token seeds).
+    multi = None
+    if args.contexts > 1:
+        extra = [T_.Model(cfg, weights, max_chunk=cfg["chunk"], prefill_block=args.prefill_block)
+                 for _ in range(args.contexts - 1)]
+        mods = [model] + extra
+        toks = [tokens] + [torch.from_numpy(synth.gen_tokens(cfg, T=T, seed=cfg["token_seed"] + 1000 + i))
+                           .to(dev) for i in range(args.contexts - 1)]
+        T_.prefill_many(mods, toks, cfg["chunk"], cfg["lr"])
+        torch.cuda.synchronize()
+        reps = 2
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            outs = T_.prefill_many(mods, toks, cfg["chunk"], cfg["lr"])
+        torch.cuda.synchronize()
+        t_m = (time.perf_counter() - t0) / reps
+        assert all(bool(torch.isfinite(o).all().item()) for o in outs), "non-finite loss (contexts)"
+        multi = {"contexts": args.contexts, "ms": round(t_m * 1e3, 1),
+                 "tokens_per_s": round(args.contexts * T / t_m, 1),
+                 "speedup_over_one_context": round(args.contexts * (dt / args.steps) / t_m, 3)}
+        print(f"# {args.contexts} contexts at once: {multi}", file=sys.stderr, flush=True)
+        for e in extra:
+            e.close()
+        del extra, mods, toks
+        torch.cuda.empty_cache()
 
     # The same context read without updates (the static-weight models the
     # pages compare TTT-E2E with): window 8192, then full attention (window
@@ -351,6 +385,7 @@ def main():
         "decode_ms_per_token": None if dec is None else dec["ms_per_token"],
         "decode": dec,
         "static_reads": static,
+        "contexts_at_once": multi,
         "mfma_util_pct": round(mfma_pct, 2),
         "algorithmic_tflop_per_step": round(fl / 1e12, 1),
         "kernel_classes_ms_per_step": {k: round(v["ms"], 2) for k, v in ktime.items()},

@@ -125,6 +125,25 @@ int ttt_prefill(struct ttt_model* m, const int32_t* tokens, int64_t T, int32_t c
                 int32_t steps, float* chunk_losses, void* stream);
 
 /*
+ * Several independent contexts at once, one model handle each (every
+ * context has its own fast weights and K/V rings; the handles may share a
+ * configuration and weights or not): the same inner loop as ttt_prefill for
+ * every context, with one T, chunk, lr and steps.  Each context's chunk
+ * chain runs on a stream of its own handle, and the contexts' chunks are
+ * enqueued in turn, so their kernels occupy the GPU together (independent
+ * contexts are the data-parallel unit of the method: each keeps its own
+ * fast weights).  The caller's stream waits for every context.
+ *   models        host array of n distinct handles
+ *   tokens        host array of n device int32 [T] pointers
+ *   chunk_losses  host array of n device float [ceil(T/chunk) * steps]
+ * The result of each context equals that of ttt_prefill on it.  Errors:
+ * as ttt_prefill (the first context's error is returned after every
+ * context has run); TTT_ERR_ARG for a repeated handle.
+ */
+int ttt_prefill_many(struct ttt_model* const* models, int32_t n, const int32_t* const* tokens, int64_t T,
+                     int32_t chunk, float lr, int32_t steps, float* const* chunk_losses, void* stream);
+
+/*
  * The same context read without test-time training: the static-weight
  * model whose latency the pages set against TTT-E2E (blog Figure 1, right
  * panel; paper abstract: constant latency versus full attention, whose

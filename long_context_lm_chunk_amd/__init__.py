@@ -12,7 +12,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["lib", "TTTConfig", "Model", "TTTError", "config_from_dict", "LIB_PATH"]
+__all__ = ["lib", "TTTConfig", "Model", "TTTError", "config_from_dict", "LIB_PATH", "prefill_many"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libttt.so")
 
@@ -49,6 +49,8 @@ def _load():
                             ctypes.POINTER(vp)], ctypes.c_int),
         "ttt_prefill": ([vp, vp, i64, i32, f32, i32, vp, vp], ctypes.c_int),
         "ttt_forward": ([vp, vp, i64, i32, vp, vp], ctypes.c_int),
+        "ttt_prefill_many": ([ctypes.POINTER(vp), i32, ctypes.POINTER(vp), i64, i32, f32, i32,
+                              ctypes.POINTER(vp), vp], ctypes.c_int),
         "ttt_fast_weight": ([vp, i32, i32, vp, i64, vp], ctypes.c_int),
         "ttt_fast_weight_delta": ([vp, i32, i32, vp, i64, vp], ctypes.c_int),
         "ttt_decode_step": ([vp, vp, vp, vp, vp], ctypes.c_int),
@@ -71,7 +73,7 @@ def _load():
 
 lib = _load()
 
-EXPORTED = ["ttt_workspace_bytes", "ttt_model_load", "ttt_prefill", "ttt_forward", "ttt_fast_weight",
+EXPORTED = ["ttt_workspace_bytes", "ttt_model_load", "ttt_prefill", "ttt_forward", "ttt_prefill_many", "ttt_fast_weight",
             "ttt_fast_weight_delta",
             "ttt_decode_step", "ttt_reset", "ttt_model_free", "ttt_status_str", "ttt_last_error",
             "ttt_timing_enable", "ttt_timing_read", "ttt_diag_gemm", "ttt_diag_gemm_core"]
@@ -122,6 +124,27 @@ def workspace_bytes(c: TTTConfig) -> int:
     n = ctypes.c_size_t(0)
     _check(lib.ttt_workspace_bytes(ctypes.byref(c), ctypes.byref(n)))
     return n.value
+
+
+def prefill_many(models, tokens_list, chunk: int, lr: float, steps: int = 1, stream=None):
+    """The inner loop over several independent contexts at once, one model
+    per context (see ttt_prefill_many); returns each context's losses."""
+    import torch
+    if len(models) != len(tokens_list) or not models:
+        raise ValueError("one token tensor per model")
+    dev = models[0].device
+    toks = [t.to(dev, torch.int32).contiguous() for t in tokens_list]
+    T = toks[0].numel()
+    if any(t.numel() != T for t in toks):
+        raise ValueError("every context must have the same length")
+    outs = [torch.empty(math.ceil(T / chunk) * steps, dtype=torch.float32, device=dev) for _ in models]
+    n = len(models)
+    hs = (ctypes.c_void_p * n)(*[m.h.value for m in models])
+    tp = (ctypes.c_void_p * n)(*[t.data_ptr() for t in toks])
+    lp = (ctypes.c_void_p * n)(*[o.data_ptr() for o in outs])
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    _check(lib.ttt_prefill_many(hs, n, tp, T, chunk, float(lr), steps, lp, ctypes.c_void_p(s.cuda_stream)))
+    return outs
 
 
 class Model:

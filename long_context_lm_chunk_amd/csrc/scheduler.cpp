@@ -161,6 +161,8 @@ struct ttt_model {
   std::vector<hipEvent_t> evR1, evR2;   // per fast block: dh_lo / dz read by the update stream
   hipEvent_t evC = nullptr;             // all updates of the chunk done
   hipStream_t sk = nullptr;             // dK/dV of the attention backward, beside dQ
+  hipStream_t sb = nullptr;             // the chunk chain when several contexts run at once
+  hipEvent_t evOut = nullptr;           // end of this context's work in such a run
   hipEvent_t evK0 = nullptr, evK1 = nullptr;
   float* dtmp = nullptr; void* dout = nullptr; void* dqkv = nullptr; float* Dattn = nullptr;
   float* attn_part = nullptr; float* attn_ml = nullptr;   // key-range split partials
@@ -841,6 +843,111 @@ int reset_state(ttt_model* m, hipStream_t s) {
   return TTT_OK;
 }
 
+// ------------------------------------------------------------ prefill run
+// One context's prefill as a sequence of enqueue steps (one chunk and all
+// its steps at a time), so that several contexts can be interleaved.
+struct PrefillRun {
+  ttt_model* m = nullptr;
+  const int32_t* tokens = nullptr;
+  int64_t T = 0;
+  int chunk = 1;
+  float lr = 0.f;
+  int steps = 1;
+  float* losses = nullptr;
+  hipStream_t s = nullptr;     // the chunk chain's stream
+  int64_t blk = 0, nblocks = 0;
+  int64_t b = 0, c0 = 0, k = 0;   // current block, next chunk start, its index
+};
+
+int prefill_check(ttt_model* m, const int32_t* tokens, int64_t T, int32_t chunk, float lr, int32_t steps,
+                  float* chunk_losses) {
+  if (!m || !tokens || !chunk_losses) return fail(TTT_ERR_ARG, "NULL argument");
+  if (T < 2) return fail(TTT_ERR_ARG, "T must be >= 2");
+  if (chunk < 1 || chunk > m->Cmax) return fail(TTT_ERR_ARG, "chunk must be in [1, max_chunk]");
+  if (steps < 1) return fail(TTT_ERR_ARG, "steps must be >= 1");
+  if (!std::isfinite(lr)) return fail(TTT_ERR_ARG, "lr must be finite");
+  return TTT_OK;
+}
+
+// Phase A of block b+1 (frozen layers, independent of the fast weights)
+// runs on m->sa while phase B of block b runs on the chain stream.
+// evA[b%2]: block b's phase-A output is ready; evB[b%2]: phase B is done
+// reading it, so the buffer can take block b+2.
+int prefill_launch_a(PrefillRun& r, int64_t b) {
+  ttt_model* m = r.m;
+  const int64_t B0 = b * r.blk;
+  const int nb = (int)std::min<int64_t>(r.blk, r.T - B0);
+  if (b >= 2) HIPCHK(hipStreamWaitEvent(m->sa, m->evB[b % 2], 0));
+  const int rc = phase_a(m, r.tokens, B0, nb, m->hAb[b % 2], m->sa);
+  if (rc) return rc;
+  HIPCHK(hipEventRecord(m->evA[b % 2], m->sa));
+  return TTT_OK;
+}
+
+int prefill_begin(PrefillRun& r) {
+  ttt_model* m = r.m;
+  int rc = reset_state(m, r.s);
+  if (rc) return rc;
+  m->lr = r.lr;
+  m->steps = r.steps;
+  m->chunk = r.chunk;
+  r.blk = std::max<int64_t>(r.chunk, (m->MA / r.chunk) * (int64_t)r.chunk);
+  r.nblocks = (r.T + r.blk - 1) / r.blk;
+  r.b = r.c0 = r.k = 0;
+  HIPCHK(hipEventRecord(m->ev0, r.s));
+  HIPCHK(hipStreamWaitEvent(m->sa, m->ev0, 0));
+  return prefill_launch_a(r, 0);
+}
+
+// Enqueue the next chunk (with all its steps).
+int prefill_next(PrefillRun& r) {
+  ttt_model* m = r.m;
+  const int d = m->d;
+  const int64_t B0 = r.b * r.blk;
+  const int nb = (int)std::min<int64_t>(r.blk, r.T - B0);
+  if (r.c0 == B0) {   // the block's first chunk
+    if (r.b + 1 < r.nblocks) {
+      const int rc = prefill_launch_a(r, r.b + 1);
+      if (rc) return rc;
+    }
+    HIPCHK(hipStreamWaitEvent(r.s, m->evA[r.b % 2], 0));
+  }
+  const float* hAblk = m->hAb[r.b % 2];
+  const int64_t c0 = r.c0;
+  const int n = (int)std::min<int64_t>(r.chunk, r.T - c0);
+  const int n_tgt = (int)std::min<int64_t>(n, r.T - 1 - c0);
+  for (int st = 0; st < r.steps; ++st) {
+    const int rc = chunk_step(m, c0, n, hAblk + (c0 - B0) * (int64_t)d, r.tokens + c0 + 1, n_tgt, r.lr,
+                              r.losses + r.k * r.steps + st, r.s);
+    if (rc) return rc;
+  }
+  if (c0 + n == r.T) {
+    // first decode token: argmax of the last position's logits from this
+    // chunk's last read
+    const char* frow = static_cast<const char*>(m->fN) + (size_t)(n - 1) * d * m->es;
+    dgemv_vec(m->U, nullptr, m->V, d, frow, m->logits, nullptr, nullptr, nullptr, m->amax, m->bf, r.s);
+    argmax_part(m->amax, dgemv_blocks(m->V), m->cur_tok, nullptr, nullptr, false, r.s);
+    dec_set(m->dstate, r.T, 0, r.s);
+  }
+  r.c0 += n;
+  r.k += 1;
+  if (r.c0 >= B0 + nb) {   // the block is done: its phase-A buffer may be refilled
+    HIPCHK(hipEventRecord(m->evB[r.b % 2], r.s));
+    r.b += 1;
+  }
+  return TTT_OK;
+}
+
+int prefill_finish(PrefillRun& r, hipStream_t s) {
+  ttt_model* m = r.m;
+  const int rc = sync_and_check(m, s);
+  if (rc) return rc;
+  m->pos = r.T;
+  m->dchunk0 = r.T;
+  m->prefilled = true;
+  return TTT_OK;
+}
+
 }  // namespace
 
 // ======================================================================= ABI
@@ -882,12 +989,13 @@ int ttt_model_load(const ttt_config* cfg, const void* const* weights, int32_t n_
     hipError_t e1 = hipStreamCreateWithFlags(&m->sa, hipStreamNonBlocking);
     if (e1 == hipSuccess) e1 = hipStreamCreateWithFlags(&m->sc, hipStreamNonBlocking);
     if (e1 == hipSuccess) e1 = hipStreamCreateWithFlags(&m->sk, hipStreamNonBlocking);
+    if (e1 == hipSuccess) e1 = hipStreamCreateWithFlags(&m->sb, hipStreamNonBlocking);
     m->evT1.assign(m->q, nullptr);
     m->evT2.assign(m->q, nullptr);
     m->evR1.assign(m->q, nullptr);
     m->evR2.assign(m->q, nullptr);
     std::vector<hipEvent_t*> evs = {&m->ev0, &m->evA[0], &m->evA[1], &m->evB[0], &m->evB[1], &m->evC,
-                                    &m->evK0, &m->evK1};
+                                    &m->evK0, &m->evK1, &m->evOut};
     for (int j = 0; j < m->q; ++j) {
       evs.push_back(&m->evT1[j]); evs.push_back(&m->evT2[j]);
       evs.push_back(&m->evR1[j]); evs.push_back(&m->evR2[j]);
@@ -957,73 +1065,61 @@ int ttt_model_load(const ttt_config* cfg, const void* const* weights, int32_t n_
 
 int ttt_prefill(ttt_model* m, const int32_t* tokens, int64_t T, int32_t chunk, float lr,
                 int32_t steps, float* chunk_losses, void* stream) {
-  if (!m || !tokens || !chunk_losses) return fail(TTT_ERR_ARG, "NULL argument");
-  if (T < 2) return fail(TTT_ERR_ARG, "T must be >= 2");
-  if (chunk < 1 || chunk > m->Cmax) return fail(TTT_ERR_ARG, "chunk must be in [1, max_chunk]");
-  if (steps < 1) return fail(TTT_ERR_ARG, "steps must be >= 1");
-  if (!std::isfinite(lr)) return fail(TTT_ERR_ARG, "lr must be finite");
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  int rc = reset_state(m, s);
+  int rc = prefill_check(m, tokens, T, chunk, lr, steps, chunk_losses);
   if (rc) return rc;
-  m->lr = lr;
-  m->steps = steps;
-  m->chunk = chunk;
-  const int d = m->d;
-  const int64_t blk = std::max<int64_t>(chunk, (m->MA / chunk) * (int64_t)chunk);
-  const int64_t nblocks = (T + blk - 1) / blk;
-  // Phase A of block b+1 (frozen layers, independent of the fast weights)
-  // runs on m->sa while phase B of block b runs on s.  evA[b%2]: block b's
-  // phase-A output is ready; evB[b%2]: phase B is done reading it, so the
-  // buffer can take block b+2.
-  HIPCHK(hipEventRecord(m->ev0, s));
-  HIPCHK(hipStreamWaitEvent(m->sa, m->ev0, 0));
-  auto launch_a = [&](int64_t b) -> int {
-    const int64_t B0 = b * blk;
-    const int nb = (int)std::min<int64_t>(blk, T - B0);
-    if (b >= 2) HIPCHK(hipStreamWaitEvent(m->sa, m->evB[b % 2], 0));
-    const int r = phase_a(m, tokens, B0, nb, m->hAb[b % 2], m->sa);
-    if (r) return r;
-    HIPCHK(hipEventRecord(m->evA[b % 2], m->sa));
-    return TTT_OK;
-  };
-  rc = launch_a(0);
+  PrefillRun r;
+  r.m = m; r.tokens = tokens; r.T = T; r.chunk = chunk; r.lr = lr; r.steps = steps;
+  r.losses = chunk_losses; r.s = static_cast<hipStream_t>(stream);
+  rc = prefill_begin(r);
+  while (!rc && r.b < r.nblocks) rc = prefill_next(r);
   if (rc) return rc;
-  int64_t k = 0;
-  for (int64_t b = 0; b < nblocks; ++b) {
-    const int64_t B0 = b * blk;
-    const int nb = (int)std::min<int64_t>(blk, T - B0);
-    if (b + 1 < nblocks) {
-      rc = launch_a(b + 1);
-      if (rc) return rc;
-    }
-    HIPCHK(hipStreamWaitEvent(s, m->evA[b % 2], 0));
-    float* hAblk = m->hAb[b % 2];
-    for (int64_t c0 = B0; c0 < B0 + nb; c0 += chunk, ++k) {
-      const int n = (int)std::min<int64_t>(chunk, T - c0);
-      const int n_tgt = (int)std::min<int64_t>(n, T - 1 - c0);
-      for (int st = 0; st < steps; ++st) {
-        rc = chunk_step(m, c0, n, hAblk + (c0 - B0) * (int64_t)d, tokens + c0 + 1, n_tgt, lr,
-                        chunk_losses + k * steps + st, s);
-        if (rc) return rc;
-      }
-      if (c0 + n == T) {
-        // first decode token: argmax of the last position's logits from this
-        // chunk's last read
-        const char* frow = static_cast<const char*>(m->fN) + (size_t)(n - 1) * d * m->es;
-        dgemv_vec(m->U, nullptr, m->V, d, frow, m->logits, nullptr, nullptr, nullptr, m->amax,
-                  m->bf, s);
-        argmax_part(m->amax, dgemv_blocks(m->V), m->cur_tok, nullptr, nullptr, false, s);
-        dec_set(m->dstate, T, 0, s);
-      }
-    }
-    HIPCHK(hipEventRecord(m->evB[b % 2], s));
+  return prefill_finish(r, r.s);
+}
+
+int ttt_prefill_many(ttt_model* const* models, int32_t n, const int32_t* const* tokens, int64_t T,
+                     int32_t chunk, float lr, int32_t steps, float* const* chunk_losses, void* stream) {
+  if (!models || !tokens || !chunk_losses || n < 1) return fail(TTT_ERR_ARG, "NULL argument or n < 1");
+  for (int i = 0; i < n; ++i) {
+    for (int j = 0; j < i; ++j)
+      if (models[i] == models[j]) return fail(TTT_ERR_ARG, "a model handle appears twice");
+    const int rc = prefill_check(models[i], tokens[i], T, chunk, lr, steps, chunk_losses[i]);
+    if (rc) return rc;
   }
-  rc = sync_and_check(m, s);
-  if (rc) return rc;
-  m->pos = T;
-  m->dchunk0 = T;
-  m->prefilled = true;
-  return TTT_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // every context's chain runs on its own stream (its phase A, updates and
+  // dK/dV on theirs), enqueued chunk by chunk in turn, so the contexts'
+  // kernels fill the GPU together; the caller's stream joins them at the end
+  HIPCHK(hipEventRecord(models[0]->evOut, s));
+  std::vector<PrefillRun> runs(n);
+  for (int i = 0; i < n; ++i) {
+    HIPCHK(hipStreamWaitEvent(models[i]->sb, models[0]->evOut, 0));
+    PrefillRun& r = runs[i];
+    r.m = models[i]; r.tokens = tokens[i]; r.T = T; r.chunk = chunk; r.lr = lr; r.steps = steps;
+    r.losses = chunk_losses[i]; r.s = models[i]->sb;
+  }
+  for (int i = 0; i < n; ++i) {
+    const int rc = prefill_begin(runs[i]);
+    if (rc) return rc;
+  }
+  for (bool more = true; more;) {
+    more = false;
+    for (int i = 0; i < n; ++i) {
+      if (runs[i].b >= runs[i].nblocks) continue;
+      const int rc = prefill_next(runs[i]);
+      if (rc) return rc;
+      more = more || runs[i].b < runs[i].nblocks;
+    }
+  }
+  for (int i = 0; i < n; ++i) {
+    HIPCHK(hipEventRecord(models[i]->evOut, models[i]->sb));
+    HIPCHK(hipStreamWaitEvent(s, models[i]->evOut, 0));
+  }
+  int first = TTT_OK;
+  for (int i = 0; i < n; ++i) {
+    const int rc = prefill_finish(runs[i], s);
+    if (rc && !first) first = rc;
+  }
+  return first;
 }
 
 int ttt_forward(ttt_model* m, const int32_t* tokens, int64_t T, int32_t chunk, float* chunk_losses,
@@ -1139,14 +1235,16 @@ void ttt_model_free(ttt_model* m) {
     for (auto e : t.ev) (void)hipEventDestroy(e);
   if (m->sc) (void)hipStreamSynchronize(m->sc);
   if (m->sk) (void)hipStreamSynchronize(m->sk);
+  if (m->sb) (void)hipStreamSynchronize(m->sb);
   std::vector<hipEvent_t> evs = {m->ev0, m->evA[0], m->evA[1], m->evB[0], m->evB[1], m->evC,
-                                 m->evK0, m->evK1};
+                                 m->evK0, m->evK1, m->evOut};
   for (auto* v : {&m->evT1, &m->evT2, &m->evR1, &m->evR2}) evs.insert(evs.end(), v->begin(), v->end());
   for (auto e : evs)
     if (e) (void)hipEventDestroy(e);
   if (m->sa) (void)hipStreamDestroy(m->sa);
   if (m->sc) (void)hipStreamDestroy(m->sc);
   if (m->sk) (void)hipStreamDestroy(m->sk);
+  if (m->sb) (void)hipStreamDestroy(m->sb);
   delete m;
 }
 

@@ -342,6 +342,38 @@ def test_decode_after_forward_makes_no_update():
     assert all(math.isnan(u) for u in upd)
 
 
+def test_prefill_many_contexts_equal_separate_runs():
+    """Three independent contexts in one call (their own handles, weights,
+    tokens and types; chains interleaved chunk by chunk on their own
+    streams): every context's losses and fast weights equal those of its own
+    prefill bit for bit, and the first one matches the oracle; decode goes on
+    from each; a repeated handle is refused."""
+    T_ = _gpu()
+    cfgs = [small_cfg(dtype="bf16"), small_cfg(dtype="bf16", weight_seed=222, token_seed=22),
+            small_cfg(mlp="gelu", n_fast=1, weight_seed=333, token_seed=33)]
+    say("case prefill_many: 3 contexts")
+    ws = [synth.gen_weights(c, std=0.05) for c in cfgs]
+    ws[2] = [t.float() for t in ws[2]]
+    xs = [synth.gen_tokens(c) for c in cfgs]
+    ms = [T_.Model(c, [t.cuda() for t in w], max_chunk=32, prefill_block=64) for c, w in zip(cfgs, ws)]
+    toks = [torch.from_numpy(x).cuda() for x in xs]
+    many = [o.cpu() for o in T_.prefill_many(ms, toks, 32, 0.05)]
+    fmany = [[t.cpu() for t in m.fast_weights()] for m in ms]
+    nxt = [int(m.decode_step()[0].item()) for m in ms]
+    for i, m in enumerate(ms):
+        one = m.prefill(toks[i], 32, 0.05).cpu()
+        assert torch.equal(one, many[i]), i
+        assert all(torch.equal(a, b.cpu()) for a, b in zip(fmany[i], m.fast_weights())), i
+        assert 0 <= nxt[i] < cfgs[i]["vocab"]
+    ref = O.prefill(cfgs[0], ws[0], xs[0], 32, 0.05)
+    e = float(np.max(np.abs(many[0].numpy() - ref["losses"]) / np.abs(ref["losses"])))
+    say(f"  context 0 vs oracle: {e:.2e}")
+    assert e < BAR["bf16"]
+    with pytest.raises(T_.TTTError) as err:
+        T_.prefill_many([ms[0], ms[0]], [toks[0], toks[0]], 32, 0.05)
+    assert err.value.status == -1
+
+
 def test_prefill_is_deterministic():
     T_ = _gpu()
     cfg = small_cfg(dtype="bf16")
