@@ -146,6 +146,9 @@ def main():
     ap.add_argument("--decode-tokens", type=int, default=2048,
                     help="greedy decode tokens timed after the prefill (2048 reach two "
                          "decode-time updates at chunk 1024)")
+    ap.add_argument("--decode-sweep", default="",
+                    help="comma-separated prefill lengths after each of which 256 decode tokens are "
+                         "timed (decode cost against context length)")
     ap.add_argument("--contexts", type=int, default=1,
                     help="also time this many independent contexts prefilled at once "
                          "(one model each, chains interleaved on their own streams)")
@@ -236,7 +239,7 @@ def main():
     # decode after the prefill (constant per-token cost once T >= window); the
     # decode-time updates fire when 1024 decode positions are complete, each
     # token is bracketed by events so update tokens are seen separately
-    def timed_decode(mdl, n):
+    def timed_decode(mdl, n, ctx=None):
         for _ in range(4):
             mdl.decode_step()
         torch.cuda.synchronize()
@@ -255,13 +258,29 @@ def main():
                "updates": int(upd.sum()),
                "update_token_ms": round(float(per[upd].mean()), 3) if upd.any() else None,
                "ms_per_token_without_updates": round(float(per[~upd].mean()), 4) if (~upd).any() else None,
-               "first_position": int(T + 4)}
+               "first_position": int((T if ctx is None else ctx) + 4)}
         return res
 
     dec = None
     if args.decode_tokens > 0:
         dec = timed_decode(model, args.decode_tokens)
         print(f"# decode: {dec}", file=sys.stderr, flush=True)
+
+    # Decode cost against the context length read before it.
+    sweep = None
+    if args.decode_sweep:
+        try:
+            sweep = []
+            for Ts in [int(v) for v in args.decode_sweep.split(",")]:
+                tk = torch.from_numpy(synth.gen_tokens(cfg, T=Ts)).to(dev)
+                model.prefill(tk, cfg["chunk"], cfg["lr"])
+                r = timed_decode(model, 256, Ts)
+                sweep.append({"T": Ts, "ms_per_token": r["ms_per_token"], "p50": r["ms_per_token_p50"],
+                              "p99": r["ms_per_token_p99"]})
+                print(f"# decode after T={Ts}: {sweep[-1]}", file=sys.stderr, flush=True)
+                del tk
+        except Exception as e:   # noqa: BLE001
+            sweep = {"error": f"{type(e).__name__}: {e}"}
 
     # Several independent contexts prefilled at once (one model each: own
     # fast weights and rings; the same weights, other token seeds).
@@ -381,7 +400,9 @@ def main():
         cpu = cpu_baseline(cfg, weights, tokens_np, args.cpu_sample)
 
     out = {
-        "metric": "TTT-E2E prefill context tokens/s at 3B/128K (decode ms/token and MFMA util % alongside)",
+        "metric": ("TTT-E2E prefill context tokens/s at 3B/128K; decode ms/token; MFMA util %"
+                   if args.config == "c4" and T == 131072 and not args.static_mlp else
+                   f"TTT-E2E prefill context tokens/s ({cfg['name']}, T={T}); decode ms/token; MFMA util %"),
         "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 2), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
@@ -396,6 +417,7 @@ def main():
         "decode": dec,
         "static_reads": static,
         "contexts_at_once": multi,
+        "decode_by_context_length": sweep,
         "mfma_util_pct": round(mfma_pct, 2),
         "algorithmic_tflop_per_step": round(fl / 1e12, 1),
         "kernel_classes_ms_per_step": {k: round(v["ms"], 2) for k, v in ktime.items()},
