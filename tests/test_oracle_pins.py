@@ -153,7 +153,7 @@ def test_cross_entropy_two_class_closed_form():
 @pytest.mark.parametrize("n_fast,mlp,static", [(1, "gelu", 0), (2, "gelu", 0), (2, "swiglu", 0),
                                                (3, "swiglu", 0), (1, "swiglu", 1), (2, "gelu", 1)])
 def test_fast_weight_gradient_finite_differences(n_fast, mlp, static):
-    """The spec pin: analytic fast-weight gradient of a chunk loss vs
+    """The central pin: analytic fast-weight gradient of a chunk loss vs
     central finite differences, relative error <= 1e-6.  The chunk is the
     second one, so attention sees cached keys that must stay constant
     (stop-gradient); n_fast >= 2 exercises the attention backward; static = 1
