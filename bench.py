@@ -36,8 +36,8 @@ PEAK_HBM_GBS = 8000.0
 # (FETCH_SIZE reads 0.5x the bytes read, WRITE_SIZE 1.0x the bytes written),
 # averaged over the two launch shapes.  Valid only for the GEMM source it was
 # measured on (sha256 of csrc/gemm.hip); otherwise reported as null.
-SGD_TRAFFIC = {"gemm_src_sha256": "9f52d3b4b38d41a4f49363122b0c488c5a2ccd21e65263ddc7e894cd1f82b14a",
-               "bytes_per_launch": 655.8e6,
+SGD_TRAFFIC = {"gemm_src_sha256": "56257134119c3aa43c50e0b9e7df638cadf9b61f209f65f3e3008a5c40522d77",
+               "bytes_per_launch": 659.4e6,
                "profile": "profiles/sgd_gemm_3B_chunk1024_traffic.md"}
 
 

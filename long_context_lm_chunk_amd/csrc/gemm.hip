@@ -499,10 +499,7 @@ constexpr int LDS_BYTES = NS * STAGE;        // 128 KB of the 160 KB per CU (a f
                                              // stage measured no faster)
 constexpr int SLAB_LOADS = BM * ROWB / 1024 / NW;   // 1 KB loads per wave per operand slab (2)
 constexpr int LOADS = 2 * SLAB_LOADS;        // per wave per stage
-constexpr int ES = BN + 8;                   // epilogue fp32 row pitch: the two lane
-                                             // halves (4 rows apart) on disjoint banks
-constexpr int EROWS = 64;                    // rows per epilogue pass
-static_assert(EROWS * ES * 4 <= LDS_BYTES, "epilogue pass fits");
+static_assert(NW * 32 * (BN / WN + 4) * 4 <= LDS_BYTES, "per-wave epilogue areas fit");
 // s_waitcnt immediates with vmcnt n (expcnt and lgkmcnt not waited for)
 constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 static_assert((NS - 2) * LOADS < 64, "vmcnt range");
@@ -529,7 +526,7 @@ DEVI void load_slab(__amdgpu_buffer_rsrc_t rs, uint32_t ldb, int row0, int rows,
 template <int EPI, typename TO, bool DUAL>
 __global__ __launch_bounds__(big::NT, 1) void gemm256_kernel(GemmParams p) {
   constexpr int BM = big::BM, BN = big::BN, BK = big::BK, NT = big::NT, NS = big::NS, ROWB = big::ROWB;
-  constexpr int STAGE_A = big::STAGE_A, STAGE = big::STAGE, ES = big::ES, EROWS = big::EROWS;
+  constexpr int STAGE_A = big::STAGE_A, STAGE = big::STAGE;
   constexpr int TM = big::TM, TN = big::TN, FI = big::FI, FJ = big::FJ, WN = big::WN;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -630,25 +627,93 @@ __global__ __launch_bounds__(big::NT, 1) void gemm256_kernel(GemmParams p) {
   __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0): the zero-fill loads past the end
   __syncthreads();                         // all waves done with the operand stages
 
-  // Epilogue in four passes of 64 tile rows: the waves holding those rows
-  // stage them in LDS, then all threads apply the epilogue.
-  float* st = reinterpret_cast<float*>(smem);
+  if constexpr (EPI == EPI_SGD) {
+    // Each wave updates its own 128 x 64 block, 32 rows at a time, through a
+    // private LDS area: no workgroup barrier, every load of a 32-row part in
+    // flight at once, and the accumulators of a part are free once staged.
+    constexpr int P = TN + 4;                          // row pitch (floats)
+    float* ws = reinterpret_cast<float*>(smem) + wave * 32 * P;
+    const int cbase = n0 + wn * TN;
 #pragma unroll
-  for (int pass = 0; pass < BM / EROWS; ++pass) {
-    if (wm == pass / (TM / EROWS)) {
+    for (int i = 0; i < FI; ++i) {
+      const int rbase = m0 + wm * TM + i * 32;
 #pragma unroll
-      for (int ii = 0; ii < EROWS / 32; ++ii) {
-        const int i = (pass % (TM / EROWS)) * (EROWS / 32) + ii;
+      for (int j = 0; j < FJ; ++j)
 #pragma unroll
-        for (int j = 0; j < FJ; ++j)
+        for (int r = 0; r < 16; ++r) ws[(8 * (r >> 2) + 4 * fhi + (r & 3)) * P + j * 32 + frow] = acc[i][j][r];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // 32 rows x 16 groups of 4 columns = 512 groups, 8 per lane, all loaded first
+      float4 v[8], w[8], w0[8];
+      bool ok[8];
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            st[(ii * 32 + 8 * (r >> 2) + 4 * fhi + (r & 3)) * ES + wn * TN + j * 32 + frow] = acc[i][j][r];
+      for (int u = 0; u < 8; ++u) {
+        const int g = u * 64 + lane, r = g >> 4, c = (g & 15) * 4;
+        const int row = rbase + r, col = cbase + c;
+        ok[u] = row < p.M && col < p.N;
+        if (ok[u]) {
+          const int64_t ci = (int64_t)row * p.ldc + col;
+          v[u] = *reinterpret_cast<const float4*>(ws + r * P + c);
+          w[u] = *reinterpret_cast<const float4*>(static_cast<const float*>(p.C) + ci);
+          w0[u] = load4<TO>(static_cast<const TO*>(p.W0) + ci);
+        }
       }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (!ok[u]) continue;
+        const int g = u * 64 + lane, r = g >> 4, c = (g & 15) * 4;
+        const int row = rbase + r, col = cbase + c;
+        const int64_t ci = (int64_t)row * p.ldc + col;
+        float4 x = w[u];
+        x.x -= p.alpha * v[u].x; x.y -= p.alpha * v[u].y; x.z -= p.alpha * v[u].z; x.w -= p.alpha * v[u].w;
+        *reinterpret_cast<float4*>(static_cast<float*>(p.C) + ci) = x;
+        if (p.C2) store4<TO>(static_cast<TO*>(p.C2) + (int64_t)row * p.ldc2 + col, x);
+        float4 cur;
+        cur.x = w0[u].x + x.x; cur.y = w0[u].y + x.y; cur.z = w0[u].z + x.z; cur.w = w0[u].w + x.w;
+        *reinterpret_cast<float4*>(ws + r * P + c) = cur;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // transposed current weights: 64 columns x 8 groups of 4 rows, 8 per lane
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int g = u * 64 + lane, c = g >> 3, r = (g & 7) * 4;
+        const int row = rbase + r, col = cbase + c;
+        if (row >= p.M || col >= p.N) continue;
+        TO* dst = static_cast<TO*>(p.C3) + (int64_t)col * p.ldc3 + row;
+        if (row + 3 < p.M) {
+          float4 t;
+          t.x = ws[r * P + c]; t.y = ws[(r + 1) * P + c]; t.z = ws[(r + 2) * P + c]; t.w = ws[(r + 3) * P + c];
+          store4<TO>(dst, t);
+        } else {
+          for (int e = 0; row + e < p.M; ++e) dst[e] = from_f32<TO>(ws[(r + e) * P + c]);
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
-    __syncthreads();
-    epi_apply<EPI, TO>(p, st, ES, EROWS, BN, m0 + pass * EROWS, n0, tid, NT);
-    __syncthreads();
+  } else {
+    // The other epilogues the same way: each wave applies it to its own
+    // 128 x 64 block, 32 rows at a time, staged in a private LDS area.
+    constexpr int P = TN + 4;
+    float* ws = reinterpret_cast<float*>(smem) + wave * 32 * P;
+#pragma unroll
+    for (int i = 0; i < FI; ++i) {
+#pragma unroll
+      for (int j = 0; j < FJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ws[(8 * (r >> 2) + 4 * fhi + (r & 3)) * P + j * 32 + frow] = acc[i][j][r];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      epi_apply<EPI, TO>(p, ws, P, 32, TN, m0 + wm * TM + i * 32, n0 + wn * TN, lane, 64);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
   }
 }
 
