@@ -38,11 +38,17 @@ def test_workspace_sizes_and_bounded_memory():
     assert 10e9 < c4 < 40e9
     c1 = T.workspace_bytes(T.config_from_dict(synth.config("c1")))
     assert c1 < 100e6
+    # the frozen second MLP adds its weights, their transposes and its
+    # activations; a window of T = 131072 (full attention at 128K) grows the rings
+    cs = T.workspace_bytes(T.config_from_dict(synth.config("c4", static_mlp=1)))
+    assert c4 < cs < c4 + 4e9
+    cf = T.workspace_bytes(T.config_from_dict(synth.config("c4", window=131072)))
+    assert 60e9 < cf < 120e9
 
 
 @pytest.mark.parametrize("field,value", [("head_dim", 48), ("n_fast", 0), ("vocab", 100),
                                          ("dtype", 7), ("mlp", 3), ("window", 0), ("d_ff", 100),
-                                         ("max_chunk", 0)])
+                                         ("max_chunk", 0), ("static_mlp", 2), ("window", (1 << 22) + 1)])
 def test_config_validation(field, value):
     import long_context_lm_chunk_amd as T
     c = T.config_from_dict(synth.config("c1"))
@@ -63,6 +69,11 @@ def test_argument_errors_without_device_work():
     assert T.lib.ttt_decode_step(None, None, None, None, None) == -1
     assert T.lib.ttt_reset(None, None) == -1
     assert T.lib.ttt_fast_weight(None, 0, 0, None, 0, None) == -1
+    assert T.lib.ttt_fast_weight_delta(None, 0, 0, None, 0, None) == -1
+    assert T.lib.ttt_forward(None, None, 10, 4, None, None) == -1
+    assert T.lib.ttt_prefill_many(None, 0, None, 10, 4, 0.1, 1, None, None) == -1
+    one = (ctypes.c_void_p * 1)(None)
+    assert T.lib.ttt_prefill_many(one, 1, one, 10, 4, 0.1, 1, one, None) == -1   # a NULL handle
     c = T.config_from_dict(synth.config("c1"))
     h = ctypes.c_void_p(0)
     assert T.lib.ttt_model_load(ctypes.byref(c), None, 0, None, 0, None, ctypes.byref(h)) == -1
