@@ -938,6 +938,14 @@ int prefill_next(PrefillRun& r) {
   return TTT_OK;
 }
 
+// After a failed enqueue: wait for what the model's own streams still hold,
+// so that a later call cannot race with it (the caller's stream orders the
+// rest).
+void drain(ttt_model* m) {
+  for (hipStream_t q : {m->sa, m->sc, m->sk, m->sb})
+    if (q) (void)hipStreamSynchronize(q);
+}
+
 int prefill_finish(PrefillRun& r, hipStream_t s) {
   ttt_model* m = r.m;
   const int rc = sync_and_check(m, s);
@@ -1072,7 +1080,10 @@ int ttt_prefill(ttt_model* m, const int32_t* tokens, int64_t T, int32_t chunk, f
   r.losses = chunk_losses; r.s = static_cast<hipStream_t>(stream);
   rc = prefill_begin(r);
   while (!rc && r.b < r.nblocks) rc = prefill_next(r);
-  if (rc) return rc;
+  if (rc) {
+    drain(m);
+    return rc;
+  }
   return prefill_finish(r, r.s);
 }
 
@@ -1097,16 +1108,20 @@ int ttt_prefill_many(ttt_model* const* models, int32_t n, const int32_t* const* 
     r.m = models[i]; r.tokens = tokens[i]; r.T = T; r.chunk = chunk; r.lr = lr; r.steps = steps;
     r.losses = chunk_losses[i]; r.s = models[i]->sb;
   }
+  auto fail_all = [&](int rc) {
+    for (int i = 0; i < n; ++i) drain(models[i]);
+    return rc;
+  };
   for (int i = 0; i < n; ++i) {
     const int rc = prefill_begin(runs[i]);
-    if (rc) return rc;
+    if (rc) return fail_all(rc);
   }
   for (bool more = true; more;) {
     more = false;
     for (int i = 0; i < n; ++i) {
       if (runs[i].b >= runs[i].nblocks) continue;
       const int rc = prefill_next(runs[i]);
-      if (rc) return rc;
+      if (rc) return fail_all(rc);
       more = more || runs[i].b < runs[i].nblocks;
     }
   }
