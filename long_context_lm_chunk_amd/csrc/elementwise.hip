@@ -166,6 +166,74 @@ __global__ __launch_bounds__(256) void ln_fwd_reg_k(const float* __restrict__ x,
   }
 }
 
+// The same with one 256-thread block per row (d = 1024 * NQ): each thread
+// holds NQ float4 of every array, the K-split slabs (up to 4) are loaded
+// together with the row, and the two row sums meet through LDS, so a chunk
+// of rows keeps 16 waves per CU busy instead of 4.
+template <typename T, int NQ>
+__global__ __launch_bounds__(256) void ln_bwd_blk_k(const float* __restrict__ dy, const float* __restrict__ x,
+                                                    const float* __restrict__ mean,
+                                                    const float* __restrict__ rstd, int n,
+                                                    float* __restrict__ acc, T* __restrict__ acc_lo,
+                                                    int nslab, int64_t slab_stride) {
+  constexpr int D = 1024 * NQ;
+  __shared__ float red[8];
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (row >= n) return;
+  const float4* g = reinterpret_cast<const float4*>(dy + (int64_t)row * D);
+  const float4* xr = reinterpret_cast<const float4*>(x + (int64_t)row * D);
+  float4* a = reinterpret_cast<float4*>(acc + (int64_t)row * D);
+  const float mu = mean[row], rs = rstd[row];
+  float4 gv[NQ], yh[NQ], av[NQ], gz[3][NQ];
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    gv[i] = g[tid + 256 * i];
+    yh[i] = xr[tid + 256 * i];
+    av[i] = a[tid + 256 * i];
+  }
+#pragma unroll
+  for (int z = 0; z < 3; ++z)
+    if (z + 1 < nslab) {
+      const float4* gs = reinterpret_cast<const float4*>(dy + (z + 1) * slab_stride + (int64_t)row * D);
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) gz[z][i] = gs[tid + 256 * i];
+    }
+  // partial slabs of a K-split product, summed in slab order
+#pragma unroll
+  for (int z = 0; z < 3; ++z)
+    if (z + 1 < nslab) {
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) {
+        gv[i].x += gz[z][i].x; gv[i].y += gz[z][i].y; gv[i].z += gz[z][i].z; gv[i].w += gz[z][i].w;
+      }
+    }
+  float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    yh[i].x = (yh[i].x - mu) * rs; yh[i].y = (yh[i].y - mu) * rs;
+    yh[i].z = (yh[i].z - mu) * rs; yh[i].w = (yh[i].w - mu) * rs;
+    s1 += (gv[i].x + gv[i].y) + (gv[i].z + gv[i].w);
+    s2 += (gv[i].x * yh[i].x + gv[i].y * yh[i].y) + (gv[i].z * yh[i].z + gv[i].w * yh[i].w);
+  }
+  s1 = wave_sum(s1);
+  s2 = wave_sum(s2);
+  if (lane == 0) { red[wave] = s1; red[4 + wave] = s2; }
+  __syncthreads();
+  const float m1 = ((red[0] + red[1]) + (red[2] + red[3])) / D;
+  const float m2 = ((red[4] + red[5]) + (red[6] + red[7])) / D;
+  T* lo = acc_lo ? acc_lo + (int64_t)row * D : nullptr;
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    float4 nv;
+    nv.x = av[i].x + rs * (gv[i].x - m1 - yh[i].x * m2);
+    nv.y = av[i].y + rs * (gv[i].y - m1 - yh[i].y * m2);
+    nv.z = av[i].z + rs * (gv[i].z - m1 - yh[i].z * m2);
+    nv.w = av[i].w + rs * (gv[i].w - m1 - yh[i].w * m2);
+    a[tid + 256 * i] = nv;
+    if (lo) store4v<T>(lo + 4 * (tid + 256 * i), nv);
+  }
+}
+
 template <typename T, int NV>
 __global__ __launch_bounds__(256) void ln_bwd_reg_k(const float* __restrict__ dy, const float* __restrict__ x,
                                                     const float* __restrict__ mean,
@@ -572,6 +640,15 @@ void layernorm_bwd_acc(const float* dy, const float* x, const float* mean, const
                        int d, float* acc, void* acc_lo, bool bf, hipStream_t s, int nslab,
                        int64_t slab_stride) {
   if (n <= 0) return;
+  if (d % 1024 == 0 && d <= 4096 && nslab <= 4) {
+    switch (d / 1024) {
+#define LNQ(NQ) case NQ: TSEL(bf, hipLaunchKernelGGL((ln_bwd_blk_k<bf16, NQ>), dim3(n), dim3(256), 0, s, dy, x, mean, rstd, n, acc, (bf16*)acc_lo, nslab, slab_stride), \
+                               hipLaunchKernelGGL((ln_bwd_blk_k<float, NQ>), dim3(n), dim3(256), 0, s, dy, x, mean, rstd, n, acc, (float*)acc_lo, nslab, slab_stride)); return;
+      LNQ(1) LNQ(2) LNQ(3) LNQ(4)
+#undef LNQ
+      default: break;
+    }
+  }
   if (d % 256 == 0 && d <= 4096) {
     switch (d / 256) {
 #define LNB(NV) case NV: TSEL(bf, hipLaunchKernelGGL((ln_bwd_reg_k<bf16, NV>), dim3(nblk(n, 4)), dim3(256), 0, s, dy, x, mean, rstd, n, acc, (bf16*)acc_lo, nslab, slab_stride), \
