@@ -266,6 +266,17 @@ def main():
         dec = timed_decode(model, args.decode_tokens)
         print(f"# decode: {dec}", file=sys.stderr, flush=True)
 
+    # The matrix cores' own peak on this GPU (bf16 products from registers)
+    # and the shader clock they ran at, beside the specified peak.
+    mpeak = None
+    try:
+        tf, mhz = T_.diag_mfma_peak()
+        mpeak = {"tflops": round(tf, 1), "clock_mhz": round(mhz, 0),
+                 "mfma_util_pct_of_measured_peak": round(100.0 * fl / (dt / args.steps) / (tf * 1e12), 2)}
+        print(f"# measured bf16 matrix-core peak: {mpeak}", file=sys.stderr, flush=True)
+    except Exception as e:   # noqa: BLE001
+        mpeak = {"error": f"{type(e).__name__}: {e}"}
+
     # Decode cost against the context length read before it.
     sweep = None
     if args.decode_sweep:
@@ -419,6 +430,7 @@ def main():
         "contexts_at_once": multi,
         "decode_by_context_length": sweep,
         "mfma_util_pct": round(mfma_pct, 2),
+        "mfma_peak_measured": mpeak,
         "algorithmic_tflop_per_step": round(fl / 1e12, 1),
         "kernel_classes_ms_per_step": {k: round(v["ms"], 2) for k, v in ktime.items()},
         "roofline": roof,

@@ -252,6 +252,15 @@ int ttt_diag_gemm(int32_t dtype, int32_t a_kc, int32_t b_kc, int32_t M, int32_t 
  */
 int ttt_diag_gemm_core(int32_t mode);
 
+/*
+ * Diagnostic: the matrix-core throughput this GPU reaches on bf16 32x32x16
+ * products fed from registers (no memory traffic), and the shader clock they
+ * ran at, for reporting utilisation against a measured peak beside the
+ * specified one.  scratch: device float [2048 * 256]; clk: device int64 [2].
+ * Synchronises the stream; *tflops and *clock_mhz are host outputs.
+ */
+int ttt_diag_mfma_peak(float* scratch, int64_t* clk, double* tflops, double* clock_mhz, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -63,6 +63,8 @@ def _load():
                              ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
         "ttt_diag_gemm": ([i32, i32, i32, i32, i32, i32, vp, i64, vp, i64, vp, i64, vp], ctypes.c_int),
         "ttt_diag_gemm_core": ([i32], ctypes.c_int),
+        "ttt_diag_mfma_peak": ([vp, vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double), vp],
+                               ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -76,7 +78,8 @@ lib = _load()
 EXPORTED = ["ttt_workspace_bytes", "ttt_model_load", "ttt_prefill", "ttt_forward", "ttt_prefill_many", "ttt_fast_weight",
             "ttt_fast_weight_delta",
             "ttt_decode_step", "ttt_reset", "ttt_model_free", "ttt_status_str", "ttt_last_error",
-            "ttt_timing_enable", "ttt_timing_read", "ttt_diag_gemm", "ttt_diag_gemm_core"]
+            "ttt_timing_enable", "ttt_timing_read", "ttt_diag_gemm", "ttt_diag_gemm_core",
+            "ttt_diag_mfma_peak"]
 
 
 GEMM_CORE_AUTO, GEMM_CORE_BIG, GEMM_CORE_SMALL = 0, 1, 2
@@ -86,6 +89,19 @@ def diag_gemm_core(mode: int) -> int:
     """Select the GEMM core for bf16 k-contiguous products (see
     ttt_diag_gemm_core); returns the previous mode."""
     return int(lib.ttt_diag_gemm_core(int(mode)))
+
+
+def diag_mfma_peak():
+    """(TFLOP/s, MHz): bf16 matrix-core throughput from registers and the
+    shader clock it ran at, measured on the current device."""
+    import torch
+    scratch = torch.empty(2048 * 256, dtype=torch.float32, device="cuda")
+    clk = torch.zeros(2, dtype=torch.int64, device="cuda")
+    tf, mhz = ctypes.c_double(0), ctypes.c_double(0)
+    s = torch.cuda.current_stream()
+    _check(lib.ttt_diag_mfma_peak(ctypes.c_void_p(scratch.data_ptr()), ctypes.c_void_p(clk.data_ptr()),
+                                  ctypes.byref(tf), ctypes.byref(mhz), ctypes.c_void_p(s.cuda_stream)))
+    return tf.value, mhz.value
 
 
 def diag_gemm(A, B, M, N, K, a_kc: bool, b_kc: bool, C=None):

@@ -845,12 +845,54 @@ int dispatch(const GemmParams& p, bool a_kc, bool b_kc, int epi, bool out_f32, h
   return -1;
 }
 
+// Matrix-core throughput probe: every wave issues `iters` rounds of eight
+// independent 32x32x16 bf16 products on register operands (no memory
+// traffic), then writes its accumulators so nothing is optimised away.
+// Wave 0 of block 0 also reads the shader-clock and the 100 MHz real-time
+// counters around its loop, giving the clock the products ran at.
+__global__ __launch_bounds__(256) void mfma_peak_k(int iters, float* out, int64_t* clk) {
+  const int lane = threadIdx.x & 63;
+  bf16x8 a, b;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    a[j] = static_cast<bf16>(0.001f * (float)(lane + j));
+    b[j] = static_cast<bf16>(0.002f * (float)(lane - j));
+  }
+  f32x16 acc[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[u][r] = 0.f;
+  const bool timer = blockIdx.x == 0 && threadIdx.x == 0;
+  int64_t t0 = 0, r0 = 0;
+  if (timer) { t0 = __builtin_amdgcn_s_memtime(); r0 = __builtin_amdgcn_s_memrealtime(); }
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[u], 0, 0, 0);
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sum += acc[u][r];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = sum;
+  if (timer) {
+    const int64_t t1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+    clk[0] = t1 - t0;
+    clk[1] = r1 - r0;
+  }
+}
+
 }  // namespace
 
 int gemm_core(int mode) {
   const int prev = g_gemm_core;
   if (mode == GEMM_CORE_AUTO || mode == GEMM_CORE_BIG || mode == GEMM_CORE_SMALL) g_gemm_core = mode;
   return prev;
+}
+
+void mfma_peak(int blocks, int iters, float* out, int64_t* clk, hipStream_t s) {
+  hipLaunchKernelGGL(mfma_peak_k, dim3(blocks), dim3(256), 0, s, iters, out, clk);
 }
 
 int gemm(const GemmParams& p, bool bf16_operands, bool a_kc, bool b_kc, int epi, bool out_f32,

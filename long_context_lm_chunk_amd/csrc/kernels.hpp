@@ -41,6 +41,10 @@ struct GemmParams {
 // the previous mode
 enum { GEMM_CORE_AUTO = 0, GEMM_CORE_BIG = 1, GEMM_CORE_SMALL = 2 };
 int gemm_core(int mode);
+// matrix-core throughput probe: blocks x 256 threads, each wave iters x 8
+// bf16 32x32x16 products; out [blocks*256] floats, clk[2] = shader-clock and
+// 100 MHz real-time ticks of one wave's loop
+void mfma_peak(int blocks, int iters, float* out, int64_t* clk, hipStream_t s);
 int gemm(const GemmParams& p, bool bf16_operands, bool a_kc, bool b_kc, int epi, bool out_f32,
          hipStream_t s);
 

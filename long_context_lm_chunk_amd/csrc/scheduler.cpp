@@ -1327,4 +1327,29 @@ int ttt_diag_gemm(int32_t dtype, int32_t a_kc, int32_t b_kc, int32_t M, int32_t 
 
 int ttt_diag_gemm_core(int32_t mode) { return gemm_core(mode); }
 
+int ttt_diag_mfma_peak(float* scratch, int64_t* clk, double* tflops, double* clock_mhz, void* stream) {
+  if (!scratch || !clk || !tflops || !clock_mhz) return fail(TTT_ERR_ARG, "NULL argument");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int blocks = 2048, iters = 4096;
+  mfma_peak(blocks, 64, scratch, clk, s);   // warm-up (clocks ramp)
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  HIPCHK(hipEventCreate(&e0));
+  HIPCHK(hipEventCreate(&e1));
+  HIPCHK(hipEventRecord(e0, s));
+  mfma_peak(blocks, iters, scratch, clk, s);
+  HIPCHK(hipEventRecord(e1, s));
+  HIPCHK(hipEventSynchronize(e1));
+  float ms = 0.f;
+  const hipError_t e = hipEventElapsedTime(&ms, e0, e1);
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (e != hipSuccess) return fail(TTT_ERR_HIP, hipGetErrorString(e));
+  int64_t t[2] = {0, 0};
+  HIPCHK(hipMemcpy(t, clk, sizeof(t), hipMemcpyDeviceToHost));
+  const double flops = (double)blocks * 4 * iters * 8 * 2.0 * 32 * 32 * 16;
+  *tflops = flops / (ms * 1e-3) / 1e12;
+  *clock_mhz = t[1] > 0 ? (double)t[0] / (double)t[1] * 100.0 : 0.0;
+  return TTT_OK;
+}
+
 }  // extern "C"
