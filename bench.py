@@ -276,6 +276,25 @@ def main():
         print(f"# measured bf16 matrix-core peak: {mpeak}", file=sys.stderr, flush=True)
     except Exception as e:   # noqa: BLE001
         mpeak = {"error": f"{type(e).__name__}: {e}"}
+    # and the HBM rate of a plain 2 GiB device copy (read + write), beside
+    # the specified 8 TB/s
+    try:
+        src = torch.ones(1 << 29, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        ce0, ce1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ce0.record()
+        for _ in range(10):
+            dst.copy_(src)
+        ce1.record()
+        torch.cuda.synchronize()
+        copy_gbs = 2 * src.numel() * 4 * 10 / (ce0.elapsed_time(ce1) / 1e3) / 1e9
+        mpeak = dict(mpeak or {}, hbm_copy_gbs=round(copy_gbs, 1))
+        del src, dst
+        torch.cuda.empty_cache()
+    except Exception as e:   # noqa: BLE001
+        mpeak = dict(mpeak or {}, hbm_copy_error=f"{type(e).__name__}: {e}")
 
     # Decode cost against the context length read before it.
     sweep = None
