@@ -767,11 +767,13 @@ bool launch_big(const GemmParams& p, hipStream_t s) {
 // Which core runs the bf16 k-contiguous products: measured on MI355X, the
 // 256x256 core wins on long reductions (K, doubled for W0 + delta, >= 6144)
 // and on grids of >= 1024 of its tiles; below that its 256 CUs are filled
-// unevenly and the 128x128 core is as fast or faster.  The weight-gradient
-// + SGD products take the 256x256 core at every size: in a prefill, where
-// they run beside the backward chain, that is 1.3% faster overall (the
-// half-size operand re-reads of the 128x128 tiles cost more than the
-// uneven fill).
+// unevenly and the 128x128 core is as fast or faster alone.  In a prefill,
+// where products of several streams share the GPU, two more kinds run
+// faster overall on the 256x256 core: the weight-gradient + SGD products
+// (+1.3%: the half-size operand re-reads of the 128x128 tiles cost more than
+// the uneven fill) and every product over a block of >= 4096 rows (+0.4%:
+// the frozen blocks' output projection); the chunk-sized products that the
+// rule leaves on the 128x128 core are 0.5% slower on the other.
 int g_gemm_core = GEMM_CORE_AUTO;
 
 template <typename T, bool AK, bool BK_, int EPI, typename TO>
@@ -782,7 +784,8 @@ void launch_t(const GemmParams& p, hipStream_t s) {
     const int64_t keff = (int64_t)p.K * (p.B2 ? 2 : 1);
     const int64_t tiles = (int64_t)((p.M + 255) / 256) * ((p.N + 255) / 256);
     const bool want = g_gemm_core == GEMM_CORE_BIG ||
-                      (g_gemm_core == GEMM_CORE_AUTO && (keff >= 6144 || tiles >= 1024 || EPI == EPI_SGD));
+                      (g_gemm_core == GEMM_CORE_AUTO &&
+                       (keff >= 6144 || tiles >= 1024 || EPI == EPI_SGD || p.M >= 4096));
     if (want && launch_big<EPI, TO>(p, s)) return;
   }
   const int tiles = ((p.N + BN - 1) / BN) * ((p.M + BM - 1) / BM);
