@@ -407,6 +407,23 @@ def test_device_detected_errors():
     with pytest.raises(T_.TTTError) as e:
         m.prefill(ok, 64, 0.05)        # chunk > max_chunk
     assert e.value.status == -1
+    # a context of one position, and a step count of zero, are refused
+    # before any work
+    with pytest.raises(T_.TTTError) as e:
+        m.prefill(ok[:1], 32, 0.05)
+    assert e.value.status == -1
+    with pytest.raises(T_.TTTError) as e:
+        m.forward(ok[:1], 32)
+    assert e.value.status == -1
+    with pytest.raises(T_.TTTError) as e:
+        m.prefill(ok, 32, 0.05, steps=0)
+    assert e.value.status == -1
+    # decode needs a prefill (or a read without updates) first
+    fresh = T_.Model(cfg, w, max_chunk=32)
+    with pytest.raises(T_.TTTError) as e:
+        fresh.decode_step()
+    assert e.value.status == -6
+    fresh.close()
     # the model is still usable afterwards
     r = m.prefill(ok, 32, 0.05)
     assert torch.isfinite(r).all()
