@@ -593,7 +593,8 @@ __global__ __launch_bounds__(big::NT, 1) void gemm256_kernel(GemmParams p) {
   // (kt - 1) % NS, which nobody reads any more, for stage kt + NS - 1.
   // (Against a wait and barrier at the start of each stage this removes
   // the LDS-latency bubble before every stage's first products: 8-15 %
-  // on the large shapes.)
+  // on the large shapes.)  Within a k-step the next step's fragment reads
+  // are interleaved one per product (2-6 % on the large shapes alone).
   static_assert(BK == 32 && NS >= 4, "two k-steps per stage; stage kt + 1 waited for mid-stage");
   bf16x8 fa0[FI], fb0[FJ], fa1[FI], fb1[FJ];
   if (kt_begin < kt_end) {
@@ -606,22 +607,33 @@ __global__ __launch_bounds__(big::NT, 1) void gemm256_kernel(GemmParams p) {
   }
   for (int kt = kt_begin; kt < kt_end; ++kt) {
     frags(kt, 1, fa1, fb1);
-    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < FI; ++i)
 #pragma unroll
       for (int j = 0; j < FJ; ++j) mma32x32x16(fa0[i], fb0[j], acc[i][j]);
+    // one fragment read between consecutive products
+#pragma unroll
+    for (int u = 0; u < FI + FJ; ++u) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, FI * FJ - (FI + FJ), 0);
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(big::vmcnt_imm((NS - 3) * big::LOADS));    // stage kt + 1
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     issue(kt + NS - 1);
     frags(kt + 1, 0, fa0, fb0);            // past the end: zeros, unused
-    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < FI; ++i)
 #pragma unroll
       for (int j = 0; j < FJ; ++j) mma32x32x16(fa1[i], fb1[j], acc[i][j]);
+#pragma unroll
+    for (int u = 0; u < FI + FJ; ++u) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, FI * FJ - (FI + FJ), 0);
     __builtin_amdgcn_sched_barrier(0);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0): the zero-fill loads past the end
