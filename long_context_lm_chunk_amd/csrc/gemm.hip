@@ -360,18 +360,33 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(GemmParams p) {
     if (kt + 1 < kt_end) load(kt + 1);
     const T* As = lds[cur];
     const T* Bs = lds[cur] + BM * C::LS;
-#pragma unroll
-    for (int ks = 0; ks < C::BK / 32; ++ks) {
-      typename Frag<T>::type af[4], bfr[4];
+    // fragments of k-step ks + 1 read between the products of k-step ks
+    typename Frag<T>::type af[2][4], bfr[2][4];
+    auto rd = [&](int ks, int b) {
       const int kk = ks * 32 + 8 * (lane >> 4);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = lds_frag8<T>(As + (wm * 64 + i * 16 + (lane & 15)) * C::LS + kk);
+      for (int i = 0; i < 4; ++i) af[b][i] = lds_frag8<T>(As + (wm * 64 + i * 16 + (lane & 15)) * C::LS + kk);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bfr[j] = lds_frag8<T>(Bs + (wn * 64 + j * 16 + (lane & 15)) * C::LS + kk);
+      for (int j = 0; j < 4; ++j) bfr[b][j] = lds_frag8<T>(Bs + (wn * 64 + j * 16 + (lane & 15)) * C::LS + kk);
+    };
+    rd(0, 0);
+#pragma unroll
+    for (int ks = 0; ks < C::BK / 32; ++ks) {
+      const int b = ks & 1;
+      if (ks + 1 < C::BK / 32) rd(ks + 1, b ^ 1);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) mma16x16x32(af[i], bfr[j], acc[i][j]);
+        for (int j = 0; j < 4; ++j) mma16x16x32(af[b][i], bfr[b][j], acc[i][j]);
+      if (ks + 1 < C::BK / 32) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (kt + 1 < kt_end) {
       la.store(lds[cur ^ 1], tid);
