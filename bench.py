@@ -36,7 +36,7 @@ PEAK_HBM_GBS = 8000.0
 # (FETCH_SIZE reads 0.5x the bytes read, WRITE_SIZE 1.0x the bytes written),
 # averaged over the two launch shapes.  Valid only for the GEMM source it was
 # measured on (sha256 of csrc/gemm.hip); otherwise reported as null.
-SGD_TRAFFIC = {"gemm_src_sha256": "fc9709c5d7cd0794d9bc0372e012b3f03aa480206a25f80d521ba39d7935d1d4",
+SGD_TRAFFIC = {"gemm_src_sha256": "7f6a99f39ed67be3fd22bb871162f42461bff06b35e1c1de504d27aef2b14d3d",
                "bytes_per_launch": 659.4e6,
                "profile": "profiles/sgd_gemm_3B_chunk1024_traffic.md"}
 
