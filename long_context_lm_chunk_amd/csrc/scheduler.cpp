@@ -160,6 +160,12 @@ struct ttt_model {
   std::vector<hipEvent_t> evT1, evT2;   // per fast block: update operands ready
   std::vector<hipEvent_t> evR1, evR2;   // per fast block: dh_lo / dz read by the update stream
   hipEvent_t evC = nullptr;             // all updates of the chunk done
+  // Within a prefill the chain does not wait for the chunk's updates at its
+  // end: the next chunk's forward waits for the first fast block's up
+  // update (evR1[0]) before that block's MLP and for its down update (evC)
+  // before the down product.  sgd_defer asks chunk_step for that; sgd_open
+  // says such waits are owed.
+  bool sgd_defer = false, sgd_open = false;
   hipStream_t sk = nullptr;             // dK/dV of the attention backward, beside dQ
   hipStream_t sb = nullptr;             // the chunk chain when several contexts run at once
   hipEvent_t evOut = nullptr;           // end of this context's work in such a run
@@ -547,12 +553,20 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
       rc = run_gemm(m, go, true, true, EPI_RESID, true, s); if (rc) return rc;
       x2 = b.x2;
     }
+    // the previous chunk's updates of block 0 (up, then down; every other
+    // block's ran before them on the in-order update stream)
+    const bool owed = j == 0 && m->sgd_open;
+    if (owed) HIPCHK(hipStreamWaitEvent(s, m->evR1[0], 0));   // up updated, b and act read
     layernorm_fwd(x2, d, n, d, eps, b.b, d, b.mean2, b.rstd2, bf, s);
     GemmParams gu;
     gu.A = b.b; gu.lda = d; gu.B = ly.wup; gu.B2 = m->fast[j].s_up; gu.ldb = d; gu.M = n; gu.N = F2; gu.K = d;
     gu.C = b.z; gu.ldc = F2; gu.C2 = b.act; gu.ldc2 = F;
     rc = run_gemm(m, gu, true, true, upepi, false, s); if (rc) return rc;
     float* xout = (j + 1 < q) ? m->pb[j + 1].xin : m->xL;
+    if (owed) {
+      HIPCHK(hipStreamWaitEvent(s, m->evC, 0));                // down updated
+      m->sgd_open = false;
+    }
     GemmParams gd;
     gd.A = b.act; gd.lda = F; gd.B = ly.wdn; gd.B2 = m->fast[j].s_dn; gd.ldb = F; gd.M = n; gd.N = d; gd.K = F;
     gd.C = ly.swup ? b.xm : xout; gd.ldc = d; gd.R = x2; gd.ldr = d;
@@ -640,38 +654,52 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
     ga.C = m->dz; ga.ldc = F2; ga.Z = b.z; ga.ldz = F2; ga.act_swiglu = m->c.mlp == TTT_MLP_SWIGLU;
     rc = run_gemm(m, ga, true, true, EPI_ACTBWD, false, s); if (rc) return rc;
     // Wdn -= lr * dh^T act   ([d][F], reduction over the chunk's tokens).
-    // The update runs on the update stream: its operands are transposed here
+    // The update runs on the update stream: its operands are transposed there
     // (after ga has read the old weights), then the chain goes on at once.
     ttt_model::TOps& to = m->tops[j];
-    HIPCHK(hipEventRecord(m->evT1[j], s));
-    HIPCHK(hipStreamWaitEvent(m->sc, m->evT1[j], 0));
-    transpose(m->dh_lo, n, d, d, to.dhT, m->Cp, np, bf, m->sc);
-    transpose(b.act, n, F, F, to.actT, m->Cp, np, bf, m->sc);
-    HIPCHK(hipEventRecord(m->evR1[j], m->sc));      // dh_lo read: the chain may overwrite it
-    GemmParams gw;
-    gw.A = to.dhT; gw.lda = m->Cp; gw.B = to.actT; gw.ldb = m->Cp; gw.M = d; gw.N = F; gw.K = np;
-    gw.C = fw.m_dn; gw.ldc = F; gw.C2 = bf ? fw.s_dn : nullptr; gw.ldc2 = F; gw.alpha = lr;
-    gw.C3 = fw.ct_dn; gw.ldc3 = d; gw.W0 = ly.wdn;
-    rc = run_gemm(m, gw, true, true, EPI_SGD, true, m->sc); if (rc) return rc;
-    if (j > 0) {
+    auto update_dn = [&]() -> int {
+      HIPCHK(hipEventRecord(m->evT1[j], s));
+      HIPCHK(hipStreamWaitEvent(m->sc, m->evT1[j], 0));
+      transpose(m->dh_lo, n, d, d, to.dhT, m->Cp, np, bf, m->sc);
+      transpose(b.act, n, F, F, to.actT, m->Cp, np, bf, m->sc);
+      HIPCHK(hipEventRecord(m->evR1[j], m->sc));      // dh_lo and act read
+      GemmParams gw;
+      gw.A = to.dhT; gw.lda = m->Cp; gw.B = to.actT; gw.ldb = m->Cp; gw.M = d; gw.N = F; gw.K = np;
+      gw.C = fw.m_dn; gw.ldc = F; gw.C2 = bf ? fw.s_dn : nullptr; gw.ldc2 = F; gw.alpha = lr;
+      gw.C3 = fw.ct_dn; gw.ldc3 = d; gw.W0 = ly.wdn;
+      return run_gemm(m, gw, true, true, EPI_SGD, true, m->sc);
+    };
+    // Wup -= lr * dz^T b  (update stream, after ga has produced dz and, above
+    // block 0, gb has read the old weights)
+    auto update_up = [&]() -> int {
+      HIPCHK(hipEventRecord(m->evT2[j], s));
+      HIPCHK(hipStreamWaitEvent(m->sc, m->evT2[j], 0));
+      transpose(m->dz, n, F2, F2, to.dzT, m->Cp, np, bf, m->sc);
+      transpose(b.b, n, d, d, to.bT, m->Cp, np, bf, m->sc);
+      HIPCHK(hipEventRecord(m->evR2[j], m->sc));      // dz and b read
+      GemmParams gw2;
+      gw2.A = to.dzT; gw2.lda = m->Cp; gw2.B = to.bT; gw2.ldb = m->Cp; gw2.M = F2; gw2.N = d; gw2.K = np;
+      gw2.C = fw.m_up; gw2.ldc = d; gw2.C2 = bf ? fw.s_up : nullptr; gw2.ldc2 = d; gw2.alpha = lr;
+      gw2.C3 = fw.ct_up; gw2.ldc3 = F2; gw2.W0 = ly.wup;
+      return run_gemm(m, gw2, true, true, EPI_SGD, true, m->sc);
+    };
+    if (j == 0) {
+      // block 0 is the last to be updated and the first the next chunk
+      // reads, up matrix first: up, then down, so that the next chunk's up
+      // product can run beside the down update
+      rc = update_up(); if (rc) return rc;
+      rc = update_dn(); if (rc) return rc;
+      break;   // no gradient below the first fast MLP
+    }
+    rc = update_dn(); if (rc) return rc;
+    {
       GemmParams gb;   // db = dz . Wup (before its update: Wup^T [d][F2])
       gb.A = m->dz; gb.lda = F2; gb.B = fw.ct_up; gb.ldb = F2; gb.M = n; gb.N = d; gb.K = F2;
       gb.C = m->dtmp; gb.ldc = d; gb.split_defer = &nsl;
       nsl = 1;
       rc = run_gemm(m, gb, true, true, EPI_STORE, true, s); if (rc) return rc;
     }
-    // Wup -= lr * dz^T b  (update stream, after gb has read the old weights)
-    HIPCHK(hipEventRecord(m->evT2[j], s));
-    HIPCHK(hipStreamWaitEvent(m->sc, m->evT2[j], 0));
-    transpose(m->dz, n, F2, F2, to.dzT, m->Cp, np, bf, m->sc);
-    transpose(b.b, n, d, d, to.bT, m->Cp, np, bf, m->sc);
-    HIPCHK(hipEventRecord(m->evR2[j], m->sc));      // dz read
-    GemmParams gw2;
-    gw2.A = to.dzT; gw2.lda = m->Cp; gw2.B = to.bT; gw2.ldb = m->Cp; gw2.M = F2; gw2.N = d; gw2.K = np;
-    gw2.C = fw.m_up; gw2.ldc = d; gw2.C2 = bf ? fw.s_up : nullptr; gw2.ldc2 = d; gw2.alpha = lr;
-    gw2.C3 = fw.ct_up; gw2.ldc3 = F2; gw2.W0 = ly.wup;
-    rc = run_gemm(m, gw2, true, true, EPI_SGD, true, m->sc); if (rc) return rc;
-    if (j == 0) break;   // no gradient below the first fast MLP
+    rc = update_up(); if (rc) return rc;
     HIPCHK(hipStreamWaitEvent(s, m->evR1[j], 0));   // dh_lo is rewritten below
     layernorm_bwd_acc(dy_of(), x2, b.mean2, b.rstd2, n, d, m->dh, m->dh_lo, bf, s, nsl, (int64_t)n * d);
     GemmParams gdo;   // dO = dh . Wo  (Wo^T [d][d])
@@ -711,10 +739,12 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
     rc = run_gemm(m, gq, true, true, EPI_STORE, true, s); if (rc) return rc;
     layernorm_bwd_acc(dy_of(), b.xin, b.mean1, b.rstd1, n, d, m->dh, m->dh_lo, bf, s, nsl, (int64_t)n * d);
   }
-  // every update of this chunk lands before anything else on s (the next
-  // chunk's forward reads the new weights)
+  // every update of this chunk lands before the next chunk's forward reads
+  // the new weights: here, or (within a prefill) at block 0's MLP of that
+  // forward
   HIPCHK(hipEventRecord(m->evC, m->sc));
-  HIPCHK(hipStreamWaitEvent(s, m->evC, 0));
+  if (m->sgd_defer) m->sgd_open = true;
+  else HIPCHK(hipStreamWaitEvent(s, m->evC, 0));
   return TTT_OK;
 }
 
@@ -888,6 +918,7 @@ int prefill_begin(PrefillRun& r) {
   ttt_model* m = r.m;
   int rc = reset_state(m, r.s);
   if (rc) return rc;
+  m->sgd_open = false;
   m->lr = r.lr;
   m->steps = r.steps;
   m->chunk = r.chunk;
@@ -917,8 +948,11 @@ int prefill_next(PrefillRun& r) {
   const int n = (int)std::min<int64_t>(r.chunk, r.T - c0);
   const int n_tgt = (int)std::min<int64_t>(n, r.T - 1 - c0);
   for (int st = 0; st < r.steps; ++st) {
+    // the last step of the last chunk joins its updates before returning
+    m->sgd_defer = c0 + n < r.T || st + 1 < r.steps;
     const int rc = chunk_step(m, c0, n, hAblk + (c0 - B0) * (int64_t)d, r.tokens + c0 + 1, n_tgt, r.lr,
                               r.losses + r.k * r.steps + st, r.s);
+    m->sgd_defer = false;
     if (rc) return rc;
   }
   if (c0 + n == r.T) {
