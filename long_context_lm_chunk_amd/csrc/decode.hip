@@ -513,12 +513,17 @@ void dgemv_launch(const DecGemv& a, hipStream_t s) {
 // Launch shapes from a sweep on MI355X (bf16, 3B shapes): two loads in flight
 // with the k range split over the block's four waves is best or within a
 // few per cent for the LayerNorm and down products; the 32000-row head
-// prefers one row per wave, the 3072-square output product UN = 2, KS = 1.
-enum { SHAPE_SPLIT = 0, SHAPE_ROWS = 1, SHAPE_ROWS2 = 2 };
+// prefers one row per wave, the 3072-square output product UN = 2, KS = 1,
+// and the LayerNorm + QKV + RoPE product (4608 row pairs) two row pairs per
+// block with the k range split over two waves (half as many workgroups:
+// about one round of resident blocks instead of two and a quarter; decode
+// 0.5-1% faster than with the four-wave split).
+enum { SHAPE_SPLIT = 0, SHAPE_ROWS = 1, SHAPE_ROWS2 = 2, SHAPE_SPLIT2 = 3 };
 template <typename T, bool LN, int OUT, bool DUAL>
 void dgemv_shaped(const DecGemv& a, int shape, hipStream_t s) {
   if (shape == SHAPE_ROWS) dgemv_launch<T, LN, OUT, DUAL, 1, 1>(a, s);
   else if (shape == SHAPE_ROWS2) dgemv_launch<T, LN, OUT, DUAL, 2, 1>(a, s);
+  else if (shape == SHAPE_SPLIT2) dgemv_launch<T, LN, OUT, DUAL, 2, 2>(a, s);
   else dgemv_launch<T, LN, OUT, DUAL, 2, 4>(a, s);
 }
 
@@ -555,7 +560,7 @@ void dgemv_ln_rope(const void* Wqkv, int d, const float* x, float eps, int H, in
   a.W = Wqkv; a.N = 3 * d; a.K = d; a.x = x; a.eps = eps;
   a.H = H; a.hd = hd; a.theta = theta; a.dstate = dstate;
   a.q = q; a.kr = kring; a.vr = vring; a.cap = cap;
-  if (bf) dgemv_t<bf16>(a, true, OUT_ROPE, SHAPE_SPLIT, s);
+  if (bf) dgemv_t<bf16>(a, true, OUT_ROPE, SHAPE_SPLIT2, s);
   else dgemv_t<float>(a, true, OUT_ROPE, SHAPE_SPLIT, s);
 }
 
