@@ -928,6 +928,12 @@ void mfma_peak(int blocks, int iters, float* out, int64_t* clk, hipStream_t s) {
 int gemm(const GemmParams& p, bool bf16_operands, bool a_kc, bool b_kc, int epi, bool out_f32,
          hipStream_t s) {
   if (p.M <= 0 || p.N <= 0) return 0;
+  // Operands are read through buffer resources (32-bit byte offsets, range
+  // at most 2^31 - 1 bytes): refuse larger ones instead of reading zeros.
+  const int64_t es = bf16_operands ? 2 : 4;
+  const int64_t abytes = (a_kc ? (int64_t)p.M : (int64_t)p.K) * p.lda * es;
+  const int64_t bbytes = (b_kc ? (int64_t)p.N : (int64_t)p.K) * p.ldb * es;
+  if (abytes > 0x7fffffff || bbytes > 0x7fffffff) return GEMM_TOO_LARGE;
   return bf16_operands ? dispatch<bf16>(p, a_kc, b_kc, epi, out_f32, s)
                        : dispatch<float>(p, a_kc, b_kc, epi, out_f32, s);
 }

@@ -45,6 +45,10 @@ int gemm_core(int mode);
 // bf16 32x32x16 products; out [blocks*256] floats, clk[2] = shader-clock and
 // 100 MHz real-time ticks of one wave's loop
 void mfma_peak(int blocks, int iters, float* out, int64_t* clk, hipStream_t s);
+// Returns 0, -1 for a variant that is not built, or GEMM_TOO_LARGE when an
+// operand spans more than 2^31 - 1 bytes (nothing is launched then).
+constexpr int GEMM_TOO_LARGE = -2;
+constexpr int64_t GEMM_MAX_OPERAND_BYTES = 0x7fffffff;
 int gemm(const GemmParams& p, bool bf16_operands, bool a_kc, bool b_kc, int epi, bool out_f32,
          hipStream_t s);
 

@@ -218,6 +218,24 @@ int check_config(const ttt_config* c) {
   if (c->prefill_block < 0) return fail(TTT_ERR_CONFIG, "prefill_block must be >= 0");
   if (c->static_mlp != 0 && c->static_mlp != 1) return fail(TTT_ERR_CONFIG, "static_mlp must be 0 or 1");
   if (!(c->ln_eps > 0.f) || !(c->rope_base > 1.f)) return fail(TTT_ERR_CONFIG, "ln_eps > 0 and rope_base > 1 required");
+  {
+    // Every operand of a matrix product is read through a buffer resource
+    // (32-bit byte offsets): none may span more than 2^31 - 1 bytes.  Rows x
+    // row length of each operand: phase-A blocks (MA rows), chunk rows (C),
+    // the weights and the transposed activations of the weight gradients.
+    const int64_t es = esz(*c), d = c->d_model, F = c->d_ff, V = c->vocab;
+    const int64_t F2 = c->mlp == TTT_MLP_SWIGLU ? 2 * F : F;
+    const int64_t C = c->max_chunk;
+    const int64_t MA = std::max<int64_t>(c->prefill_block > 0 ? c->prefill_block : 8192, C);
+    const int64_t Cp = (C + 7) / 8 * 8;
+    const int64_t rows_x_len[] = {MA * d, MA * F, C * V, C * F2, C * 3 * d, V * d, F2 * d, 3 * d * d,
+                                  F2 * Cp, F * Cp};
+    for (const int64_t e : rows_x_len)
+      if (e * es > GEMM_MAX_OPERAND_BYTES)
+        return fail(TTT_ERR_CONFIG, "a matrix-product operand would span more than 2^31 - 1 bytes "
+                                    "(bound vocab * max_chunk, prefill_block * d_ff, max_chunk * d_ff, "
+                                    "vocab * d_model)");
+  }
   return TTT_OK;
 }
 
@@ -411,6 +429,11 @@ struct Scope {
 
 enum { CLS_GEMM = 0, CLS_ATTN_FWD = 1, CLS_ATTN_BWD = 2, CLS_CE = 3, CLS_SGD = 4, CLS_MLP_UP = 5 };
 
+int gemm_fail(int rc) {
+  if (rc == GEMM_TOO_LARGE) return fail(TTT_ERR_CONFIG, "a GEMM operand spans more than 2^31 - 1 bytes");
+  return fail(TTT_ERR_CONFIG, "internal: GEMM variant not built");
+}
+
 int run_gemm(ttt_model* m, const GemmParams& p0, bool a_kc, bool b_kc, int epi, bool out_f32,
              hipStream_t s, bool allow_split = true) {
   GemmParams p = p0;
@@ -430,7 +453,7 @@ int run_gemm(ttt_model* m, const GemmParams& p0, bool a_kc, bool b_kc, int epi, 
              (epi == EPI_SGD || up1) ? fl : 0.0);
     rc = gemm(p, m->bf, a_kc, b_kc, epi, out_f32, s);
   }
-  return rc == 0 ? TTT_OK : fail(TTT_ERR_CONFIG, "internal: GEMM variant not built");
+  return rc == 0 ? TTT_OK : gemm_fail(rc);
 }
 
 // Algorithmic attention work: the number of (query, key) pairs inside the
@@ -595,7 +618,7 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
     gs.tgt = tgt; gs.n_tgt = n_tgt; gs.part_max = m->pmax; gs.part_sum = m->psum;
     gs.ldpart = m->Cmax; gs.tgt_logit = m->tlog;
     gs.C = m->zce; gs.ldc = V;      // logits kept for the gradient pass
-    if (gemm(gs, bf, true, true, EPI_CESTAT, true, s)) return fail(TTT_ERR_CONFIG, "internal: CE variant");
+    if (const int rg = gemm(gs, bf, true, true, EPI_CESTAT, true, s)) return gemm_fail(rg);
     ce_finish(m->pmax, m->psum, m->nparts, m->Cmax, m->tlog, n, n_tgt, m->lse_ce, loss_out, m->err, s);
   }
   if (n_tgt <= 0) return TTT_OK;   // nothing to learn from this chunk
@@ -613,7 +636,7 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
     gx.A = m->G; gx.lda = V; gx.B = m->UT; gx.ldb = V; gx.M = n; gx.N = d; gx.K = V;
     gx.C = m->dtmp; gx.ldc = d;
     gx.split_ws = m->split_ws; gx.split_cap = m->split_cap; gx.split_defer = &nsl;
-    if (gemm(gx, bf, true, true, EPI_STORE, true, s)) return fail(TTT_ERR_CONFIG, "internal: CE variant");
+    if (const int rg = gemm(gx, bf, true, true, EPI_STORE, true, s)) return gemm_fail(rg);
   }
   fill_f32(m->dh, (int64_t)n * d, 0.f, s);
   layernorm_bwd_acc(dy_of(), m->xL, m->meanf, m->rstdf, n, d, m->dh, m->dh_lo, bf, s, nsl, (int64_t)n * d);
@@ -786,7 +809,7 @@ int forward_block(ttt_model* m, const int32_t* tokens, int64_t T, int64_t B0, in
       gs.A = m->fN; gs.lda = d; gs.B = m->U; gs.ldb = d; gs.M = n; gs.N = m->V; gs.K = d;
       gs.tgt = tokens + c0 + 1; gs.n_tgt = n_tgt; gs.part_max = m->pmax; gs.part_sum = m->psum;
       gs.ldpart = m->Cmax; gs.tgt_logit = m->tlog;
-      if (gemm(gs, bf, true, true, EPI_CESTAT, true, s)) return fail(TTT_ERR_CONFIG, "internal: CE variant");
+      if (const int rg = gemm(gs, bf, true, true, EPI_CESTAT, true, s)) return gemm_fail(rg);
       ce_finish(m->pmax, m->psum, m->nparts, m->Cmax, m->tlog, n, n_tgt, m->lse_ce,
                 losses + (c0 / chunk), m->err, s);
     }
@@ -1354,8 +1377,9 @@ int ttt_diag_gemm(int32_t dtype, int32_t a_kc, int32_t b_kc, int32_t M, int32_t 
   int epi = EPI_STORE;
   if (!a_kc && !b_kc) { epi = EPI_SGD; p.alpha = -1.f; }
   else if (!a_kc) return fail(TTT_ERR_ARG, "layout (0,1) is not used by the inner loop");
-  if (gemm(p, dtype == TTT_BF16, a_kc != 0, b_kc != 0, epi, true, static_cast<hipStream_t>(stream)))
-    return fail(TTT_ERR_ARG, "GEMM variant not built");
+  const int rg = gemm(p, dtype == TTT_BF16, a_kc != 0, b_kc != 0, epi, true, static_cast<hipStream_t>(stream));
+  if (rg == GEMM_TOO_LARGE) return fail(TTT_ERR_ARG, "a GEMM operand spans more than 2^31 - 1 bytes");
+  if (rg) return fail(TTT_ERR_ARG, "GEMM variant not built");
   return TTT_OK;
 }
 

@@ -63,6 +63,31 @@ def test_config_validation(field, value):
     assert T.lib.ttt_last_error()
 
 
+@pytest.mark.parametrize("overrides", [
+    dict(max_chunk=65536),                          # chunk logits: 65536 x 32000 bf16 = 4.2 GB
+    dict(prefill_block=131072),                     # phase-A activations: 131072 x 8192 bf16
+    dict(max_chunk=40000, prefill_block=40000),     # SwiGLU chunk rows: 40000 x 16384 bf16
+    dict(dtype="fp32", max_chunk=20000),            # fp32 chunk logits: 20000 x 32000 x 4
+])
+def test_config_refuses_gemm_operands_beyond_2gib(overrides):
+    """Matrix-product operands are read with 32-bit byte offsets: a shape
+    whose operand would span more than 2^31 - 1 bytes is refused when the
+    configuration is checked (nothing is allocated or launched), while the
+    3B workload and its 64K-chunk variant with a small vocabulary pass."""
+    import long_context_lm_chunk_amd as T
+    cfg = synth.config("c4")
+    blk = overrides.pop("prefill_block", 0)
+    mc = overrides.pop("max_chunk", None)
+    c = T.config_from_dict(synth.config(cfg, **overrides), max_chunk=mc, prefill_block=blk)
+    n = ctypes.c_size_t(0)
+    assert T.lib.ttt_workspace_bytes(ctypes.byref(c), ctypes.byref(n)) == -2
+    assert b"2^31" in T.lib.ttt_last_error()
+    ok = T.config_from_dict(cfg)
+    assert T.lib.ttt_workspace_bytes(ctypes.byref(ok), ctypes.byref(n)) == 0
+    small = T.config_from_dict(synth.config(cfg, vocab=4096, d_ff=4096), max_chunk=65536)
+    assert T.lib.ttt_workspace_bytes(ctypes.byref(small), ctypes.byref(n)) == 0
+
+
 def test_argument_errors_without_device_work():
     import long_context_lm_chunk_amd as T
     assert T.lib.ttt_prefill(None, None, 10, 4, 0.1, 1, None, None) == -1

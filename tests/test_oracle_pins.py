@@ -93,6 +93,42 @@ def test_rope_relative_position_and_transpose():
     assert abs(c0[1, 0] - math.cos(3.0)) < 1e-15
 
 
+def test_rope_frequency_law_literal_values():
+    """Closed form of the frequency law theta_i = base^(-2i/hd): with hd = 8
+    and base 10000 the four pairs turn by 1, 0.1, 0.01 and 0.001 rad per
+    position, so position 7 turns pair 1 by 0.7 rad and pair 3 by 0.007 rad;
+    with hd = 4, pair 1 turns by 0.01 rad per position (0.05 rad at position
+    5).  The expected cosines and sines are written out as numbers."""
+    c, s = O.rope_cos_sin(np.array([7]), 8, 10000.0)
+    assert abs(c[0, 0] - 0.7539022543433046) < 1e-15 and abs(s[0, 0] - 0.6569865987187891) < 1e-15
+    assert abs(c[0, 1] - 0.7648421872844885) < 1e-15 and abs(s[0, 1] - 0.644217687237691) < 1e-15
+    assert abs(c[0, 3] - 0.9999755001000415) < 1e-15 and abs(s[0, 3] - 0.006999942833473391) < 1e-15
+    c4, s4 = O.rope_cos_sin(np.array([5]), 4, 10000.0)
+    assert abs(c4[0, 1] - 0.9987502603949663) < 1e-15
+    assert abs(s4[0, 1] - 0.04997916927067833) < 1e-15
+
+
+def test_rope_rotate_half_pairing():
+    """Rotate-half layout: component i is paired with i + hd/2 (an
+    interleaved layout would pair 2i with 2i + 1).  With hd = 8: e_0 at
+    position 1 becomes cos(1) e_0 + sin(1) e_4 and nothing else; e_5 (the
+    second half of pair 1) at position 7 becomes cos(0.7) e_5 - sin(0.7) e_1;
+    the backward (rotation by the negative angle) takes e_4 at position 1 to
+    sin(1) e_0 + cos(1) e_4.  Values written out as numbers."""
+    def unit(i):
+        x = np.zeros((1, 1, 8))
+        x[0, 0, i] = 1.0
+        return x
+    c1, s1 = O.rope_cos_sin(np.array([1]), 8, 10000.0)
+    c7, s7 = O.rope_cos_sin(np.array([7]), 8, 10000.0)
+    e = np.zeros(8); e[0] = 0.5403023058681398; e[4] = 0.8414709848078965
+    np.testing.assert_allclose(O.rope_apply(unit(0), c1, s1)[0, 0], e, rtol=0, atol=1e-15)
+    e = np.zeros(8); e[5] = 0.7648421872844885; e[1] = -0.644217687237691
+    np.testing.assert_allclose(O.rope_apply(unit(5), c7, s7)[0, 0], e, rtol=0, atol=1e-15)
+    e = np.zeros(8); e[0] = 0.8414709848078965; e[4] = 0.5403023058681398
+    np.testing.assert_allclose(O.rope_backward(unit(4), c1, s1)[0, 0], e, rtol=0, atol=1e-15)
+
+
 @pytest.mark.parametrize("window", [1, 3, 6, 100])
 def test_window_attention_against_torch_sdpa(window):
     """Library routine: torch's scaled_dot_product_attention with an explicit
@@ -397,6 +433,46 @@ def test_steps_return_every_loss_and_commit_last_read():
     np.testing.assert_array_equal(r["losses"][0::2], r["losses"][1::2])
     r2 = O.prefill(cfg, w, x, 8, 0.05, steps=2)
     assert np.all(r2["losses"][1::2] < r2["losses"][0::2])
+
+
+def test_steps_two_keep_the_last_reads_keys_and_values():
+    """steps = 2 built by hand from the pinned pieces: chunk 0 is read, the
+    fast weights take one SGD step, chunk 0 is read again and takes a second
+    step; the cache that chunk 1 attends to then holds the keys and values of
+    the second read (they differ from the first read's above the lowest fast
+    block, whose MLP changed in between).  The prefill's four losses equal
+    this construction, and chunk 1's losses differ clearly from those of a
+    cache built from the first read."""
+    cfg = tiny_cfg(T=16, chunk=8, n_fast=2, window=12)
+    w = weights_std(cfg, 0.3)
+    x = synth.gen_tokens(cfg)
+    lr = 0.05
+    r = O.prefill(cfg, w, x, 8, lr, steps=2)
+    model = O.OracleModel(cfg, w)
+    empty = O.empty_cache(cfg)
+
+    def step(fast, g):
+        return [{n: f[n] - lr * gg[n] for n in f} for f, gg in zip(fast, g)]
+
+    f0 = model.initial_fast()
+    l00, g00, fw00 = O.chunk_loss_and_grad(model, f0, empty, x[:8], x[1:9], 0)
+    f1 = step(f0, g00)
+    l01, g01, fw01 = O.chunk_loss_and_grad(model, f1, empty, x[:8], x[1:9], 0)
+    f2 = step(f1, g01)
+
+    def cache_of(fw):
+        return [(np.arange(8), fw["layers"][l]["k"], fw["layers"][l]["v"]) for l in range(cfg["n_layers"])]
+
+    def chunk1(cache):
+        l10, g10, _ = O.chunk_loss_and_grad(model, f2, cache, x[8:16], x[9:16], 8)
+        l11 = O.chunk_loss_and_grad(model, step(f2, g10), cache, x[8:16], x[9:16], 8)[0]
+        return l10, l11
+
+    last, first = chunk1(cache_of(fw01)), chunk1(cache_of(fw00))
+    np.testing.assert_allclose(r["losses"], [l00, l01, last[0], last[1]], rtol=1e-13)
+    assert min(abs(last[0] - first[0]), abs(last[1] - first[1])) > 1e-6
+    top = cfg["n_layers"] - 1
+    assert np.abs(fw01["layers"][top]["k"] - fw00["layers"][top]["k"]).max() > 1e-6
 
 
 def test_target_less_final_chunk():
