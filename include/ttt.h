@@ -103,7 +103,12 @@ int ttt_model_load(const ttt_config* cfg, const void* const* weights, int32_t n_
                    void* workspace, size_t ws_bytes, void* stream, struct ttt_model** out);
 
 /*
- * The inner loop over a whole context.  Resets the model (fast weights back
+ * The inner loop over a whole context (forum post TL;DR "Inner Loop": the
+ * model keeps learning at test time by mini-gradient descent on the context,
+ * updating specific MLP layers; podcast 6:36 and 7:08: mini-batches of about
+ * 1,000 tokens, only the MLPs of the last quarter of the blocks updated;
+ * NVIDIA blog "Our method": the next-token loss taken at the end of the
+ * network).  Resets the model (fast weights back
  * to their loaded values, empty K/V rings), then for each chunk k of
  * positions [k*chunk, min((k+1)*chunk, T)) and each of `steps` steps:
  * forward with the current fast weights (attention over the window of
@@ -164,8 +169,12 @@ int ttt_forward(struct ttt_model* m, const int32_t* tokens, int64_t T, int32_t c
 /*
  * Copy fast-weight matrix `mat` of fast layer `fast_idx` (0 = the first
  * fast layer) as float32 in canonical [in][out] layout into `dst` (device,
- * n floats, n == rows*cols).  mat: GELU 0 = W1, 1 = W2; SwiGLU 0 = Wg,
- * 1 = Wu, 2 = Wd.
+ * n floats, n == rows*cols): the MLP weights as updated so far by the inner
+ * loop (forum post TL;DR "Inner Loop"; podcast 7:08: only the MLP layers of
+ * the last quarter of the blocks change).  mat: GELU 0 = W1, 1 = W2;
+ * SwiGLU 0 = Wg, 1 = Wu, 2 = Wd.  Errors: TTT_ERR_ARG for a NULL handle or
+ * dst, an index out of range or n != rows*cols (nothing is copied).
+ * Asynchronous on `stream`.
  */
 int ttt_fast_weight(struct ttt_model* m, int32_t fast_idx, int32_t mat, float* dst, int64_t n,
                     void* stream);
@@ -183,7 +192,10 @@ int ttt_fast_weight_delta(struct ttt_model* m, int32_t fast_idx, int32_t mat, fl
 
 /*
  * One greedy decode step after ttt_prefill or ttt_forward (or a previous
- * decode step).
+ * decode step).  Generation after reading the context costs the same per
+ * token whatever the context length (paper summary "Key claims": constant
+ * inference latency; blog Figure 1, right panel caption): attention reads
+ * the window's K/V rings, the fast weights carry the rest of the context.
  * The first call emits argmax of the last prefill position's logits; every
  * call then reads the emitted token at the next position (its K/V join the
  * rings) and prepares the next argmax (lowest id on ties).  When `chunk`
@@ -240,6 +252,24 @@ int ttt_timing_read(struct ttt_model* m, int32_t cls, double* total_ms, int64_t*
 int ttt_diag_gemm(int32_t dtype, int32_t a_kc, int32_t b_kc, int32_t M, int32_t N, int32_t K,
                   const void* A, int64_t lda, const void* B, int64_t ldb, float* C, int64_t ldc,
                   void* stream);
+
+/*
+ * Diagnostic access to the fused weight-gradient + SGD product that updates
+ * the fast weights (forum post TL;DR "Inner Loop": a gradient step per
+ * mini-batch), the same kernels and epilogue the inner loop launches:
+ *   G[m][n]      = sum_k A[m][k] * B[n][k]      A [M][K], B [N][K] (row strides lda, ldb)
+ *   master[m][n] -= lr * G[m][n]                float [M][N], read and written
+ *   copy[m][n]    = master[m][n] rounded         bf16 [M][N] (TTT_BF16 only; NULL for TTT_FP32)
+ *   cur_t[n][m]   = w0[m][n] + master[m][n]      [N][M] (transposed), rounded to the element type
+ * A, B, w0, copy and cur_t have the element type of dtype (bf16 or float);
+ * master is always float.  All pointers are device memory owned by the
+ * caller.  K and the row strides must be multiples of 16 bytes (lda, ldb >=
+ * K), M and N multiples of 4, lr finite; otherwise TTT_ERR_ARG and nothing
+ * is launched.  The GEMM core is chosen as in the inner loop (see
+ * ttt_diag_gemm_core).  Asynchronous on `stream`.
+ */
+int ttt_diag_sgd(int32_t dtype, int32_t M, int32_t N, int32_t K, const void* A, int64_t lda, const void* B,
+                 int64_t ldb, float lr, float* master, void* copy, const void* w0, void* cur_t, void* stream);
 
 /*
  * Diagnostic choice of the GEMM core for the bf16 products whose operands

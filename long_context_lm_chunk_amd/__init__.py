@@ -63,6 +63,7 @@ def _load():
                              ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
         "ttt_diag_gemm": ([i32, i32, i32, i32, i32, i32, vp, i64, vp, i64, vp, i64, vp], ctypes.c_int),
         "ttt_diag_gemm_core": ([i32], ctypes.c_int),
+        "ttt_diag_sgd": ([i32, i32, i32, i32, vp, i64, vp, i64, f32, vp, vp, vp, vp, vp], ctypes.c_int),
         "ttt_diag_mfma_peak": ([vp, vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double), vp],
                                ctypes.c_int),
     }
@@ -79,7 +80,7 @@ EXPORTED = ["ttt_workspace_bytes", "ttt_model_load", "ttt_prefill", "ttt_forward
             "ttt_fast_weight_delta",
             "ttt_decode_step", "ttt_reset", "ttt_model_free", "ttt_status_str", "ttt_last_error",
             "ttt_timing_enable", "ttt_timing_read", "ttt_diag_gemm", "ttt_diag_gemm_core",
-            "ttt_diag_mfma_peak"]
+            "ttt_diag_sgd", "ttt_diag_mfma_peak"]
 
 
 GEMM_CORE_AUTO, GEMM_CORE_BIG, GEMM_CORE_SMALL = 0, 1, 2
@@ -116,6 +117,23 @@ def diag_gemm(A, B, M, N, K, a_kc: bool, b_kc: bool, C=None):
     _check(lib.ttt_diag_gemm(dt, int(a_kc), int(b_kc), M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb,
                              C.data_ptr(), C.shape[1], s))
     return C
+
+
+def diag_sgd(A, B, lr: float, master, w0):
+    """The fused weight-gradient + SGD product on A [M][K], B [N][K] (see
+    ttt_diag_sgd): updates ``master`` [M][N] (float32) in place and returns
+    (copy [M][N] or None, cur_t [N][M]) in the element type of A."""
+    import torch
+    M, K = A.shape
+    N = B.shape[0]
+    bf = A.dtype == torch.bfloat16
+    copy = torch.empty(M, N, dtype=A.dtype, device=A.device) if bf else None
+    cur_t = torch.empty(N, M, dtype=A.dtype, device=A.device)
+    s = torch.cuda.current_stream(A.device).cuda_stream
+    _check(lib.ttt_diag_sgd(TTT_BF16 if bf else TTT_FP32, M, N, K, A.data_ptr(), A.stride(0), B.data_ptr(),
+                            B.stride(0), float(lr), master.data_ptr(), copy.data_ptr() if bf else None,
+                            w0.data_ptr(), cur_t.data_ptr(), s))
+    return copy, cur_t
 
 
 def _check(rc: int):
@@ -177,12 +195,12 @@ class Model:
         self.device = weights[0].device
         if self.device.type != "cuda":
             raise ValueError("weights must be device (cuda/HIP) tensors")
-        ws = workspace_bytes(self.c)
-        self.workspace = torch.empty(ws, dtype=torch.uint8, device=self.device)
         ws_weights = [w.to(self.dtype).contiguous() for w in weights]
         ptrs = (ctypes.c_void_p * len(ws_weights))(*[w.data_ptr() for w in ws_weights])
         h = ctypes.c_void_p(0)
         self._stream = stream
+        ws = workspace_bytes(self.c)
+        self.workspace = torch.empty(ws, dtype=torch.uint8, device=self.device)
         _check(lib.ttt_model_load(ctypes.byref(self.c), ptrs, len(ws_weights),
                                   self.workspace.data_ptr(), ws, self._s(), ctypes.byref(h)))
         self.h = h

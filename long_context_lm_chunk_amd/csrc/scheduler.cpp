@@ -1383,6 +1383,28 @@ int ttt_diag_gemm(int32_t dtype, int32_t a_kc, int32_t b_kc, int32_t M, int32_t 
   return TTT_OK;
 }
 
+int ttt_diag_sgd(int32_t dtype, int32_t M, int32_t N, int32_t K, const void* A, int64_t lda, const void* B,
+                 int64_t ldb, float lr, float* master, void* copy, const void* w0, void* cur_t, void* stream) {
+  if (!A || !B || !master || !w0 || !cur_t || M <= 0 || N <= 0 || K <= 0)
+    return fail(TTT_ERR_ARG, "bad SGD arguments");
+  if (dtype != TTT_BF16 && dtype != TTT_FP32) return fail(TTT_ERR_ARG, "bad dtype");
+  if (dtype == TTT_BF16 && !copy) return fail(TTT_ERR_ARG, "bf16 needs the copy output");
+  const int vec = dtype == TTT_BF16 ? 8 : 4;
+  if (lda % vec || ldb % vec || K % vec || lda < K || ldb < K)
+    return fail(TTT_ERR_ARG, "K and the row strides must be multiples of 16 bytes, strides >= K");
+  if (M % 4 || N % 4) return fail(TTT_ERR_ARG, "M and N must be multiples of 4");
+  if (!std::isfinite(lr)) return fail(TTT_ERR_ARG, "lr must be finite");
+  GemmParams p;
+  p.A = A; p.lda = lda; p.B = B; p.ldb = ldb; p.M = M; p.N = N; p.K = K;
+  p.C = master; p.ldc = N; p.alpha = lr;
+  p.C2 = dtype == TTT_BF16 ? copy : nullptr; p.ldc2 = N;
+  p.C3 = cur_t; p.ldc3 = M; p.W0 = w0;
+  const int rg = gemm(p, dtype == TTT_BF16, true, true, EPI_SGD, true, static_cast<hipStream_t>(stream));
+  if (rg == GEMM_TOO_LARGE) return fail(TTT_ERR_ARG, "a GEMM operand spans more than 2^31 - 1 bytes");
+  if (rg) return fail(TTT_ERR_ARG, "GEMM variant not built");
+  return TTT_OK;
+}
+
 int ttt_diag_gemm_core(int32_t mode) { return gemm_core(mode); }
 
 int ttt_diag_mfma_peak(float* scratch, int64_t* clk, double* tflops, double* clock_mhz, void* stream) {

@@ -202,10 +202,16 @@ def cross_entropy(logits: np.ndarray, targets: np.ndarray):
 # --------------------------------------------------------------------------
 
 class OracleModel:
-    """Frozen weights (float64, canonical ``[in, out]`` layout) plus the
-    configuration.  Fast weights live in a separate list of dicts."""
+    """Frozen weights (canonical ``[in, out]`` layout) plus the
+    configuration.  Fast weights live in a separate list of dicts, always
+    float64.
 
-    def __init__(self, cfg: dict, weights):
+    ``frozen_dtype``: storage of the frozen matrices.  float64 by default;
+    float32 halves the memory of the 3B shape and is exact for weights that
+    are bf16 or float32 values.  Every product still runs in float64 (numpy
+    promotes the float32 operand exactly), so the arithmetic is the same."""
+
+    def __init__(self, cfg: dict, weights, frozen_dtype=np.float64):
         self.cfg = cfg
         L = cfg["n_layers"]
         names = ["Wq", "Wk", "Wv", "Wo"] + (["W1", "W2"] if cfg["mlp"] == "gelu" else ["Wg", "Wu", "Wd"])
@@ -214,7 +220,7 @@ class OracleModel:
         # the frozen second MLP of the fast blocks (podcast 7:08), when the
         # configuration asks for it: same shapes and activation as the first
         self.static_mlp = bool(cfg.get("static_mlp", 0))
-        w = [_to_f64(t) for t in weights]
+        w = [_to_f64(t) if frozen_dtype == np.float64 else _to_f32_exact(t) for t in weights]
         n_static = cfg["n_fast"] * len(self.mlp_names) if self.static_mlp else 0
         assert len(w) == 2 + L * len(names) + n_static, "weight count does not match the configuration"
         self.E = w[0]
@@ -231,8 +237,19 @@ class OracleModel:
 
     def initial_fast(self):
         """Copies of the MLP matrices of the last ``n_fast`` layers."""
-        return [{n: self.layers[l][n].copy() for n in self.mlp_names}
+        return [{n: self.layers[l][n].astype(np.float64) for n in self.mlp_names}
                 for l in range(self.first_fast, self.cfg["n_layers"])]
+
+
+def _to_f32_exact(t):
+    """float32 copy of a bf16 or float32 tensor (exact: no rounding)."""
+    import torch
+    if isinstance(t, torch.Tensor):
+        assert t.dtype in (torch.bfloat16, torch.float32), "float32 storage needs bf16/float32 weights"
+        return t.detach().to("cpu", torch.float32).numpy()
+    t = np.asarray(t)
+    assert t.dtype == np.float32, "float32 storage needs float32 weights"
+    return t
 
 
 def _to_f64(t):
@@ -291,7 +308,7 @@ def forward_chunk(model: OracleModel, fast, cache, tokens, pos0: int):
     n = len(tokens)
     pos = np.arange(pos0, pos0 + n)
     cos, sin = rope_cos_sin(pos, cfg["head_dim"], cfg["rope_base"])
-    h = model.E[np.asarray(tokens)]
+    h = model.E[np.asarray(tokens)].astype(np.float64)
     acts = []
     for l in range(cfg["n_layers"]):
         Wl = model.layers[l]
@@ -309,8 +326,15 @@ def forward_chunk(model: OracleModel, fast, cache, tokens, pos0: int):
         h2 = h + o.reshape(n, -1) @ Wl["Wo"]
         b, r2 = layer_norm(h2, eps)
         m, mact = _mlp_forward(cfg, Wm, b)
-        A = dict(h=h, a=a, r1=r1, q=q, k=k, v=v, kall=kall, vall=vall, p=p,
-                 ncache=len(cpos), h2=h2, b=b, r2=r2, mact=mact)
+        # saved for the cache (every layer) and for the backward pass (the
+        # MLP of every fast block; the attention of fast blocks above the
+        # first), nothing else
+        A = dict(k=k, v=v)
+        if fl >= 0:
+            A.update(b=b, r2=r2, mact=mact)
+        if fl > 0:
+            A.update(h=h, a=a, r1=r1, q=q, kall=kall, vall=vall, p=p, ncache=len(cpos), h2=h2)
+        del p, kall, vall
         h = h2 + m
         if fl >= 0 and model.static_mlp:
             # frozen second MLP after the fast one, its own pre-LayerNorm
@@ -398,7 +422,8 @@ def _sgd(fast, grads, lr):
 
 
 def prefill(cfg, weights, tokens, chunk: int, lr: float, steps: int = 1, pos_offset: int = 0,
-            model: OracleModel | None = None, return_state: bool = False, max_chunks=None):
+            model: OracleModel | None = None, return_state: bool = False, max_chunks=None,
+            progress: bool = False):
     """The inner loop over a whole context.
 
     For each chunk ``k`` (positions ``[kC, min(kC+C, T))``) and each step:
@@ -408,7 +433,8 @@ def prefill(cfg, weights, tokens, chunk: int, lr: float, steps: int = 1, pos_off
     ``phi <- phi - lr * g``.  Then the chunk's K/V (last read) join the cache.
 
     Returns ``dict(losses [N*steps], fast, last_logits, ...)``.
-    ``max_chunks`` stops early (bounded CPU-baseline samples).
+    ``max_chunks`` stops early (bounded CPU-baseline samples); ``progress``
+    prints a line per chunk.
     """
     model = model or OracleModel(cfg, weights)
     tokens = np.asarray(tokens)
@@ -435,6 +461,8 @@ def prefill(cfg, weights, tokens, chunk: int, lr: float, steps: int = 1, pos_off
                 _sgd(fast, grads, lr)
         cache = _commit(cfg, cache, fw, keep)
         last_logits = fw["logits"][-1].copy()
+        if progress:
+            print(f"  oracle chunk {k + 1}/{nchunks}: loss {losses[-steps]:.6f}", flush=True)
     out = dict(losses=np.array(losses), fast=fast, last_logits=last_logits)
     if return_state:
         out.update(model=model, cache=cache, T=T, pos_offset=pos_offset, chunk=C, lr=lr,
@@ -496,11 +524,11 @@ def decode(state: dict, n_tokens: int, forced=None):
     return dict(tokens=np.array(toks), logits=np.array(logits_all), update_losses=upd)
 
 
-def sequence_forward_losses(cfg, weights, tokens, pos_offset: int = 0):
+def sequence_forward_losses(cfg, weights, tokens, pos_offset: int = 0, frozen_dtype=np.float64):
     """One-shot forward of the whole sequence with the initial weights (no
     chunks, no cache, no updates); per-position next-token losses
     ``[T-1]``."""
-    model = OracleModel(cfg, weights)
+    model = OracleModel(cfg, weights, frozen_dtype=frozen_dtype)
     tokens = np.asarray(tokens)
     fw = forward_chunk(model, model.initial_fast(), empty_cache(cfg), tokens, pos_offset)
     z = fw["logits"][:-1]

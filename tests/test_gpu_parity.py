@@ -4,10 +4,11 @@ Every test runs the library's kernels on the GPU and the oracle on the CPU
 on the same seeded inputs.  Relative errors (the checks of the inner loop):
   losses:        max_k |l_k - l*_k| / |l*_k|
   fast weights:  ||W - W*||_F / ||W*||_F for every fast matrix
-Bars: 1e-4 in the float32 check mode, 2e-2 with bf16 storage.  Also
-asserted, looser, as diagnostics that are not dominated by W0 and ln V:
-  dW:    ||(W - W0) - (W* - W0)|| / ||W* - W0||, W - W0 read from the
-         library's exact float32 master of the change
+  dW:            max |dW - dW*| / max |dW*| per fast matrix, element by
+                 element, with dW = W - W0 read from the library's exact
+                 float32 master of the change (W itself is dominated by W0)
+Bars: 1e-4 in the float32 check mode, 2e-2 with bf16 storage, for all three.
+Also asserted as a diagnostic:
   dloss: the loss change caused by the updates, (l(lr) - l(0)) vs oracle.
 """
 import math
@@ -24,6 +25,10 @@ from oracle import ttt_oracle as O
 pytestmark = pytest.mark.gpu
 
 BAR = {"fp32": 1e-4, "bf16": 2e-2}
+# The loss change caused by the updates, l(lr) - l(0), is a difference of two
+# numbers near ln V, so its relative error is the loss error magnified by
+# |l| / |l(lr) - l(0)| (10^2 to 10^3 here); a diagnostic, with a bar of its own.
+DLOSS_BAR = {"fp32": 1e-3, "bf16": 5e-2}
 
 
 def _gpu():
@@ -83,6 +88,8 @@ def run_pair(cfg, dtype=None, std=0.02, T=None, chunk=None, lr=None, steps=1, pr
         loss=float(np.max(np.abs(losses - ref["losses"]) / np.maximum(np.abs(ref["losses"]), 1e-12))),
         W=max(rel(a, b) for a, b in zip(fw, rfw)),
         dW=max(rel(a, b - c) for a, b, c in zip(fd, rfw, w0)),
+        dWmax=max(float(np.abs(a - (b - c)).max() / max(np.abs(b - c).max(), 1e-300))
+                  for a, b, c in zip(fd, rfw, w0)),
         losses=losses, ref=ref["losses"], model=m, w=w, x=x)
     if lr0_too:
         l0 = m.prefill(tok, chunk, 0.0, steps).cpu().numpy()
@@ -90,7 +97,7 @@ def run_pair(cfg, dtype=None, std=0.02, T=None, chunk=None, lr=None, steps=1, pr
         dg, dr = losses - l0, ref["losses"] - r0
         out["dloss"] = float(np.linalg.norm(dg - dr) / max(np.linalg.norm(dr), 1e-300))
         out["loss0"] = float(np.max(np.abs(l0 - r0) / np.maximum(np.abs(r0), 1e-12)))
-    say(f"  errors: loss {out['loss']:.2e} W {out['W']:.2e} dW {out['dW']:.2e} "
+    say(f"  errors: loss {out['loss']:.2e} W {out['W']:.2e} dW {out['dW']:.2e} dW(max/max) {out['dWmax']:.2e} "
         f"dloss {out.get('dloss', float('nan')):.2e} loss(lr=0) {out.get('loss0', float('nan')):.2e}")
     return out
 
@@ -152,6 +159,43 @@ def test_gemm_large_tile_core_matches_torch(gemm_core, core, shape):
     assert err < 1e-5, err
 
 
+@pytest.mark.parametrize("core", ["auto", "small"])
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+@pytest.mark.parametrize("shape", [(520, 772, 1000), (3072, 1024, 1024), (16, 8, 8), (1028, 260, 40)])
+def test_sgd_epilogue_every_output(gemm_core, core, dt, shape):
+    """The fused weight-gradient + SGD product as the inner loop launches it
+    (256x256 core by default for bf16, 128x128 core forced or for fp32), on
+    several tiles with ragged M, N and K: the fp32 master after
+    master -= lr * A B^T against a float64 reference; its bf16 copy equal to
+    the master rounded; the transposed current weight round(W0 + master)
+    equal, bit for bit, to the rounding of the float sum."""
+    T = _gpu()
+    if dt == "fp32" and core == "small":
+        pytest.skip("fp32 runs the 128x128 core in both modes")
+    gemm_core(T.GEMM_CORE_SMALL if core == "small" else T.GEMM_CORE_AUTO)
+    M, N, K = shape
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    say(f"case sgd epilogue {dt} core={core} M={M} N={N} K={K}")
+    g = torch.Generator().manual_seed(M * 3 + N * 5 + K)
+    A = torch.randn(M, K, generator=g).to(tdt)
+    B = torch.randn(N, K, generator=g).to(tdt)
+    master0 = torch.randn(M, N, generator=g) * 1e-3
+    w0 = (torch.randn(M, N, generator=g) * 0.02).to(tdt)
+    lr = 0.37
+    prod = A.double() @ B.double().T
+    ref = master0.double() - lr * prod
+    master = master0.cuda()
+    copy, cur_t = T.diag_sgd(A.cuda(), B.cuda(), lr, master, w0.cuda())
+    torch.cuda.synchronize()
+    mc = master.cpu()
+    err = (mc.double() - ref).abs().max().item() / (lr * prod).abs().max().item()
+    say(f"  master err {err:.2e}")
+    assert err < 1e-5
+    if dt == "bf16":
+        assert torch.equal(copy.cpu(), mc.to(torch.bfloat16))
+    assert torch.equal(cur_t.cpu(), (w0.float() + mc).to(tdt).T.contiguous())
+
+
 @pytest.mark.parametrize("mlp,hd,q", [("swiglu", 128, 2), ("gelu", 64, 3)])
 def test_prefill_small_models_large_tile_core(gemm_core, mlp, hd, q):
     """The bf16 small models with every k-contiguous product on the 256x256
@@ -165,7 +209,7 @@ def test_prefill_small_models_large_tile_core(gemm_core, mlp, hd, q):
     r = run_pair(cfg, dtype="bf16", std=0.05, prefill_block=64)
     assert r["loss"] < BAR["bf16"] and r["W"] < BAR["bf16"]
     assert r["loss0"] < BAR["bf16"]
-    assert r["dW"] < 0.1 and r["dloss"] < 0.2
+    assert r["dWmax"] < BAR["bf16"] and r["dloss"] < DLOSS_BAR["bf16"]
 
 
 # ------------------------------------------------------- whole inner loop
@@ -175,7 +219,7 @@ def test_prefill_tiny_fp32_workload():
     16, T 256, lr 0.01): losses and fast weights within 1e-4."""
     r = run_pair(synth.config("c1"))
     assert r["loss"] < BAR["fp32"] and r["W"] < BAR["fp32"]
-    assert r["dW"] < 1e-2 and r["dloss"] < 1e-2 and r["loss0"] < BAR["fp32"]
+    assert r["dWmax"] < BAR["fp32"] and r["dloss"] < DLOSS_BAR["fp32"] and r["loss0"] < BAR["fp32"]
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
@@ -191,8 +235,8 @@ def test_prefill_small_models(dtype, mlp, hd, q):
     r = run_pair(cfg, dtype=dtype, std=0.05, prefill_block=64)
     assert r["loss"] < BAR[dtype] and r["W"] < BAR[dtype]
     assert r["loss0"] < BAR[dtype]
-    assert r["dW"] < (1e-2 if dtype == "fp32" else 0.1)
-    assert r["dloss"] < (1e-2 if dtype == "fp32" else 0.2)
+    assert r["dWmax"] < BAR[dtype]
+    assert r["dloss"] < DLOSS_BAR[dtype]
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
@@ -207,25 +251,25 @@ def test_prefill_static_second_mlp(dtype, mlp, hd, q):
     r = run_pair(cfg, dtype=dtype, std=0.05, prefill_block=64)
     assert r["loss"] < BAR[dtype] and r["W"] < BAR[dtype]
     assert r["loss0"] < BAR[dtype]
-    assert r["dW"] < (1e-2 if dtype == "fp32" else 0.1)
-    assert r["dloss"] < (1e-2 if dtype == "fp32" else 0.2)
+    assert r["dWmax"] < BAR[dtype]
+    assert r["dloss"] < DLOSS_BAR[dtype]
 
 
 def test_prefill_two_steps_per_chunk_fp32():
     r = run_pair(small_cfg(n_fast=2), steps=2, std=0.05)
-    assert r["loss"] < 1e-4 and r["W"] < 1e-4
+    assert r["loss"] < 1e-4 and r["W"] < 1e-4 and r["dWmax"] < 1e-4
 
 
 def test_window_larger_than_context_and_window_one():
     for W in (1, 1000):
         r = run_pair(small_cfg(window=W, T=96), std=0.05)
-        assert r["loss"] < 1e-4 and r["W"] < 1e-4
+        assert r["loss"] < 1e-4 and r["W"] < 1e-4 and r["dWmax"] < 1e-4
 
 
 def test_chunk_of_one_and_chunk_covering_context():
     for C in (1, 97):
         r = run_pair(small_cfg(T=97), chunk=C, std=0.05, lr0_too=False)
-        assert r["loss"] < 1e-4 and r["W"] < 1e-4
+        assert r["loss"] < 1e-4 and r["W"] < 1e-4 and r["dWmax"] < 1e-4
 
 
 def test_prefill_125m_shape_prefix_bf16():
@@ -234,12 +278,12 @@ def test_prefill_125m_shape_prefix_bf16():
     1280 tokens: 5 chunks, the window fills, a ragged vocabulary tile."""
     r = run_pair(synth.config("c2"), T=1280)
     assert r["loss"] < BAR["bf16"] and r["W"] < BAR["bf16"]
-    assert r["dW"] < 0.1
+    assert r["dWmax"] < BAR["bf16"]
 
 
 def test_prefill_125m_shape_prefix_fp32_check_mode():
     r = run_pair(synth.config("c2"), dtype="fp32", T=768)
-    assert r["loss"] < BAR["fp32"] and r["W"] < BAR["fp32"]
+    assert r["loss"] < BAR["fp32"] and r["W"] < BAR["fp32"] and r["dWmax"] < BAR["fp32"]
 
 
 @pytest.mark.parametrize("static", [0, 1])
