@@ -103,6 +103,24 @@ int ttt_model_load(const ttt_config* cfg, const void* const* weights, int32_t n_
                    void* workspace, size_t ws_bytes, void* stream, struct ttt_model** out);
 
 /*
+ * ttt_model_load without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops and
+ * harnesses that forbid hipMalloc): the model's device state lives in a
+ * static array of the library, 64 MiB on every GPU it runs on (held until
+ * the process ends), on the device current at the call.  It allocates no
+ * device memory.  Arguments and results otherwise as ttt_model_load.
+ * Errors: TTT_ERR_WORKSPACE when ttt_workspace_bytes(cfg) exceeds 64 MiB
+ * (the tiny and small configurations fit; the 125M shape does not);
+ * TTT_ERR_STATE while another model loaded this way on the same device is
+ * alive (one at a time per device; ttt_model_free releases it).  The array
+ * keeps the last model's contents; loading clears what must start at zero.
+ * Calls on the two models of the same device that overlap in time would
+ * race on it, which the ownership check rules out.
+ */
+int ttt_model_load_static(const ttt_config* cfg, const void* const* weights, int32_t n_weights, void* stream,
+                          struct ttt_model** out);
+
+/*
  * The inner loop over a whole context (forum post TL;DR "Inner Loop": the
  * model keeps learning at test time by mini-gradient descent on the context,
  * updating specific MLP layers; podcast 6:36 and 7:08: mini-batches of about

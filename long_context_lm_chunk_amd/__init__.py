@@ -47,6 +47,8 @@ def _load():
         "ttt_workspace_bytes": ([ctypes.POINTER(TTTConfig), ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
         "ttt_model_load": ([ctypes.POINTER(TTTConfig), ctypes.POINTER(vp), i32, vp, ctypes.c_size_t, vp,
                             ctypes.POINTER(vp)], ctypes.c_int),
+        "ttt_model_load_static": ([ctypes.POINTER(TTTConfig), ctypes.POINTER(vp), i32, vp, ctypes.POINTER(vp)],
+                                  ctypes.c_int),
         "ttt_prefill": ([vp, vp, i64, i32, f32, i32, vp, vp], ctypes.c_int),
         "ttt_forward": ([vp, vp, i64, i32, vp, vp], ctypes.c_int),
         "ttt_prefill_many": ([ctypes.POINTER(vp), i32, ctypes.POINTER(vp), i64, i32, f32, i32,
@@ -76,7 +78,7 @@ def _load():
 
 lib = _load()
 
-EXPORTED = ["ttt_workspace_bytes", "ttt_model_load", "ttt_prefill", "ttt_forward", "ttt_prefill_many", "ttt_fast_weight",
+EXPORTED = ["ttt_workspace_bytes", "ttt_model_load", "ttt_model_load_static", "ttt_prefill", "ttt_forward", "ttt_prefill_many", "ttt_fast_weight",
             "ttt_fast_weight_delta",
             "ttt_decode_step", "ttt_reset", "ttt_model_free", "ttt_status_str", "ttt_last_error",
             "ttt_timing_enable", "ttt_timing_read", "ttt_diag_gemm", "ttt_diag_gemm_core",
@@ -186,7 +188,7 @@ class Model:
     the device."""
 
     def __init__(self, cfg: dict, weights, dtype: str | None = None, max_chunk: int | None = None,
-                 prefill_block: int = 0, stream=None):
+                 prefill_block: int = 0, stream=None, static_workspace: bool = False):
         import torch
         self.torch = torch
         self.cfg = cfg
@@ -199,10 +201,17 @@ class Model:
         ptrs = (ctypes.c_void_p * len(ws_weights))(*[w.data_ptr() for w in ws_weights])
         h = ctypes.c_void_p(0)
         self._stream = stream
-        ws = workspace_bytes(self.c)
-        self.workspace = torch.empty(ws, dtype=torch.uint8, device=self.device)
-        _check(lib.ttt_model_load(ctypes.byref(self.c), ptrs, len(ws_weights),
-                                  self.workspace.data_ptr(), ws, self._s(), ctypes.byref(h)))
+        if static_workspace:
+            # device state in the library's static array (ttt_model_load_static)
+            self.workspace = None
+            with torch.cuda.device(self.device):
+                _check(lib.ttt_model_load_static(ctypes.byref(self.c), ptrs, len(ws_weights), self._s(),
+                                                 ctypes.byref(h)))
+        else:
+            ws = workspace_bytes(self.c)
+            self.workspace = torch.empty(ws, dtype=torch.uint8, device=self.device)
+            _check(lib.ttt_model_load(ctypes.byref(self.c), ptrs, len(ws_weights),
+                                      self.workspace.data_ptr(), ws, self._s(), ctypes.byref(h)))
         self.h = h
         del ws_weights
 

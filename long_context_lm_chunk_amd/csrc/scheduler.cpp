@@ -24,6 +24,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -192,6 +193,7 @@ struct ttt_model {
   bool no_update = false; // read by ttt_forward: decode makes no updates
   float lr = 0.f; int steps = 1; int chunk = 1;
   Timing tm[NCLS];
+  int static_dev = -1;    // device whose static workspace holds this model (ttt_model_load_static)
 };
 
 namespace {
@@ -1028,8 +1030,72 @@ int ttt_workspace_bytes(const ttt_config* cfg, size_t* bytes) {
   return TTT_OK;
 }
 
+// ------------------------------------------------------- static workspace
+// Device state of a model loaded by ttt_model_load_static, for callers that
+// cannot allocate device memory: a file-scope device array, of which every
+// GPU the library runs on holds its own copy until the process ends.  In
+// host code `scratch` only names the symbol (passing it to a kernel would
+// hand the kernel a host address); its address on each device is taken once
+// with hipGetSymbolAddress, with that device current, and kept per device.
+constexpr size_t kStaticWorkspaceBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticWorkspaceBytes];
+
+namespace {
+
+struct StaticWorkspace {
+  void* ptr = nullptr;          // device address of `scratch` on this device
+  ttt_model* owner = nullptr;   // the model whose state lives there, if any
+};
+std::mutex g_static_mu;
+std::vector<StaticWorkspace> g_static;   // indexed by device ordinal
+
+int load_impl(const ttt_config* cfg, const void* const* weights, int32_t n_weights, void* workspace,
+              size_t ws_bytes, void* stream, ttt_model** out);
+
+}  // namespace
+
 int ttt_model_load(const ttt_config* cfg, const void* const* weights, int32_t n_weights,
                    void* workspace, size_t ws_bytes, void* stream, ttt_model** out) {
+  return load_impl(cfg, weights, n_weights, workspace, ws_bytes, stream, out);
+}
+
+int ttt_model_load_static(const ttt_config* cfg, const void* const* weights, int32_t n_weights, void* stream,
+                          ttt_model** out) {
+  if (!out) return fail(TTT_ERR_ARG, "out is NULL");
+  *out = nullptr;
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  {
+    ttt_model probe;
+    init_dims(&probe, *cfg);
+    const size_t need = layout(&probe, nullptr);
+    if (need > kStaticWorkspaceBytes)
+      return fail(TTT_ERR_WORKSPACE, "the configuration needs " + std::to_string(need) +
+                                         " bytes of device state; the static workspace holds " +
+                                         std::to_string(kStaticWorkspaceBytes));
+  }
+  int dev = 0;
+  HIPCHK(hipGetDevice(&dev));
+  std::lock_guard<std::mutex> lk(g_static_mu);
+  if ((int)g_static.size() <= dev) g_static.resize(dev + 1);
+  StaticWorkspace& sw = g_static[dev];
+  if (!sw.ptr) {
+    void* p = nullptr;
+    HIPCHK(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p || (reinterpret_cast<uintptr_t>(p) & 255)) return fail(TTT_ERR_HIP, "static workspace address");
+    sw.ptr = p;
+  }
+  if (sw.owner) return fail(TTT_ERR_STATE, "the static workspace of this device holds another model");
+  rc = load_impl(cfg, weights, n_weights, sw.ptr, kStaticWorkspaceBytes, stream, out);
+  if (rc) return rc;
+  (*out)->static_dev = dev;
+  sw.owner = *out;
+  return TTT_OK;
+}
+
+namespace {
+int load_impl(const ttt_config* cfg, const void* const* weights, int32_t n_weights, void* workspace,
+              size_t ws_bytes, void* stream, ttt_model** out) {
   int rc = check_config(cfg);
   if (rc) return rc;
   if (!out) return fail(TTT_ERR_ARG, "out is NULL");
@@ -1127,6 +1193,7 @@ int ttt_model_load(const ttt_config* cfg, const void* const* weights, int32_t n_
   *out = m;
   return TTT_OK;
 }
+}  // namespace
 
 int ttt_prefill(ttt_model* m, const int32_t* tokens, int64_t T, int32_t chunk, float lr,
                 int32_t steps, float* chunk_losses, void* stream) {
@@ -1317,6 +1384,10 @@ void ttt_model_free(ttt_model* m) {
   if (m->sc) (void)hipStreamDestroy(m->sc);
   if (m->sk) (void)hipStreamDestroy(m->sk);
   if (m->sb) (void)hipStreamDestroy(m->sb);
+  if (m->static_dev >= 0) {   // the device's static workspace is free again
+    std::lock_guard<std::mutex> lk(g_static_mu);
+    if (g_static[m->static_dev].owner == m) g_static[m->static_dev].owner = nullptr;
+  }
   delete m;
 }
 
