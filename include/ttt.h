@@ -290,6 +290,17 @@ int ttt_diag_sgd(int32_t dtype, int32_t M, int32_t N, int32_t K, const void* A, 
                  int64_t ldb, float lr, float* master, void* copy, const void* w0, void* cur_t, void* stream);
 
 /*
+ * Diagnostic: the logits (float32, [rows][vocab]) of every position of the
+ * last chunk read with updates (by ttt_prefill, or by the update of a
+ * completed decode chunk), as the fused head kept them between its
+ * statistics and gradient passes.  ttt_diag_chunk_logit_rows gives rows (0
+ * before any such chunk).  n must equal rows * vocab (TTT_ERR_ARG); before
+ * any chunk TTT_ERR_STATE.  Asynchronous on `stream`.
+ */
+int ttt_diag_chunk_logits(struct ttt_model* m, float* dst, int64_t n, void* stream);
+int64_t ttt_diag_chunk_logit_rows(const struct ttt_model* m);
+
+/*
  * Diagnostic choice of the GEMM core for the bf16 products whose operands
  * are both k-contiguous (forward products, head): mode 0 = by shape (the
  * default: the 256x256 core for long reductions and large grids, the

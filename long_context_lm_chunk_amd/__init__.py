@@ -65,6 +65,8 @@ def _load():
                              ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
         "ttt_diag_gemm": ([i32, i32, i32, i32, i32, i32, vp, i64, vp, i64, vp, i64, vp], ctypes.c_int),
         "ttt_diag_gemm_core": ([i32], ctypes.c_int),
+        "ttt_diag_chunk_logits": ([vp, vp, i64, vp], ctypes.c_int),
+        "ttt_diag_chunk_logit_rows": ([vp], i64),
         "ttt_diag_sgd": ([i32, i32, i32, i32, vp, i64, vp, i64, f32, vp, vp, vp, vp, vp], ctypes.c_int),
         "ttt_diag_mfma_peak": ([vp, vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double), vp],
                                ctypes.c_int),
@@ -82,7 +84,7 @@ EXPORTED = ["ttt_workspace_bytes", "ttt_model_load", "ttt_model_load_static", "t
             "ttt_fast_weight_delta",
             "ttt_decode_step", "ttt_reset", "ttt_model_free", "ttt_status_str", "ttt_last_error",
             "ttt_timing_enable", "ttt_timing_read", "ttt_diag_gemm", "ttt_diag_gemm_core",
-            "ttt_diag_sgd", "ttt_diag_mfma_peak"]
+            "ttt_diag_sgd", "ttt_diag_chunk_logits", "ttt_diag_chunk_logit_rows", "ttt_diag_mfma_peak"]
 
 
 GEMM_CORE_AUTO, GEMM_CORE_BIG, GEMM_CORE_SMALL = 0, 1, 2
@@ -265,6 +267,15 @@ class Model:
         _check(lib.ttt_decode_step(self.h, tok.data_ptr(), lg.data_ptr() if lg is not None else None,
                                    ul.data_ptr(), self._s()))
         return tok, lg, ul
+
+    def chunk_logits(self):
+        """Logits [rows][vocab] of the last chunk read with updates (see
+        ttt_diag_chunk_logits)."""
+        torch = self.torch
+        rows = int(lib.ttt_diag_chunk_logit_rows(self.h))
+        out = torch.empty(rows, self.cfg["vocab"], dtype=torch.float32, device=self.device)
+        _check(lib.ttt_diag_chunk_logits(self.h, out.data_ptr(), out.numel(), self._s()))
+        return out
 
     def reset(self):
         _check(lib.ttt_reset(self.h, self._s()))

@@ -189,6 +189,7 @@ struct ttt_model {
   // state
   int64_t pos = 0;        // next position to read
   int64_t dchunk0 = 0;    // first position of the current decode chunk
+  int64_t logit_rows = 0; // rows of the chunk logits kept in zce (the last chunk read by chunk_step)
   bool prefilled = false;
   bool no_update = false; // read by ttt_forward: decode makes no updates
   float lr = 0.f; int steps = 1; int chunk = 1;
@@ -549,6 +550,7 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
   const int upepi = m->c.mlp == TTT_MLP_SWIGLU ? EPI_SWIGLU : EPI_GELU;
   int rc;
   rope_table(p0, n, m->hd / 2, m->theta, m->csB, s);
+  m->logit_rows = n;
   // ---------------- forward of the fast blocks
   for (int j = 0; j < q; ++j) {
     const int l = m->f0 + j;
@@ -1475,6 +1477,16 @@ int ttt_diag_sgd(int32_t dtype, int32_t M, int32_t N, int32_t K, const void* A, 
   if (rg) return fail(TTT_ERR_ARG, "GEMM variant not built");
   return TTT_OK;
 }
+
+int ttt_diag_chunk_logits(ttt_model* m, float* dst, int64_t n, void* stream) {
+  if (!m || !dst) return fail(TTT_ERR_ARG, "NULL argument");
+  if (m->logit_rows <= 0) return fail(TTT_ERR_STATE, "no chunk has been read with updates yet");
+  if (n != m->logit_rows * m->V) return fail(TTT_ERR_ARG, "n must equal rows * vocab of the last chunk");
+  HIPCHK(hipMemcpyAsync(dst, m->zce, (size_t)n * 4, hipMemcpyDeviceToDevice, static_cast<hipStream_t>(stream)));
+  return TTT_OK;
+}
+
+int64_t ttt_diag_chunk_logit_rows(const ttt_model* m) { return m ? m->logit_rows : 0; }
 
 int ttt_diag_gemm_core(int32_t mode) { return gemm_core(mode); }
 

@@ -333,7 +333,9 @@ def forward_chunk(model: OracleModel, fast, cache, tokens, pos0: int):
         if fl >= 0:
             A.update(b=b, r2=r2, mact=mact)
         if fl > 0:
-            A.update(h=h, a=a, r1=r1, q=q, kall=kall, vall=vall, p=p, ncache=len(cpos), h2=h2)
+            # the attention probabilities are not kept: the backward pass
+            # recomputes them from the same inputs (identical values)
+            A.update(h=h, a=a, r1=r1, q=q, kall=kall, vall=vall, kpos=kpos, ncache=len(cpos), h2=h2)
         del p, kall, vall
         h = h2 + m
         if fl >= 0 and model.static_mlp:
@@ -375,7 +377,9 @@ def backward_chunk(model: OracleModel, fast, fw, dlogits):
         dh2 = dh + layer_norm_backward(db, A["b"], A["r2"])
         n = dh2.shape[0]
         do = _heads(dh2 @ Wl["Wo"].T, cfg)
-        dq, dkall, dvall = window_attention_backward(do, A["q"], A["kall"], A["vall"], A["p"])
+        _, p = window_attention(A["q"], A["kall"], A["vall"], fw["pos"], A["kpos"], cfg["window"])
+        dq, dkall, dvall = window_attention_backward(do, A["q"], A["kall"], A["vall"], p)
+        del p
         nc = A["ncache"]
         dk = dkall[nc:]                      # cached keys/values: stop-gradient
         dv = dvall[nc:]
