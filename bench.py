@@ -80,12 +80,14 @@ def forward_flops(cfg, T):
     return float(2 * (T * L * (4 * d * d + k * d * F) + L * d * 2 * sum_n + (T - 1) * d * V) + extra)
 
 
-def sgd_bytes_per_launch(cfg, T):
+def sgd_bytes_per_launch(cfg, T, per_weight=10.0):
     """Algorithmic HBM bytes of one fused weight-gradient + SGD launch,
-    averaged over the launches of a prefill: the fp32 delta master read and
-    written (8 B), its storage-type copy (2 B), W0 read (2 B), the transposed
-    current weight written (2 B) per weight, plus both bf16 operands
-    ([out][tokens] and [in][tokens], tokens padded to 8)."""
+    averaged over the launches of a prefill: per fast weight the SGD step's
+    own traffic, an fp32 master read and written and a bf16 copy written for
+    the next forward (10 B), plus both bf16 operands ([out][tokens] and
+    [in][tokens], tokens padded to 8).  per_weight=14 gives the design's
+    bytes: it also reads W0 (2 B) and writes the transposed current weight
+    round(W0 + delta) (2 B) for the input-gradient products."""
     d, F, C = cfg["d_model"], cfg["d_ff"], cfg["chunk"]
     F2 = 2 * F if cfg["mlp"] == "swiglu" else F
     tot, launches = 0.0, 0
@@ -93,7 +95,7 @@ def sgd_bytes_per_launch(cfg, T):
         n = min(C, T - c0)
         np_ = (n + 7) // 8 * 8
         for (M, N) in ((d, F), (F2, d)):
-            tot += 14.0 * M * N + 2.0 * (M + N) * np_
+            tot += per_weight * M * N + 2.0 * (M + N) * np_
             launches += 1
     return tot / max(launches, 1)
 
@@ -146,9 +148,9 @@ def main():
     ap.add_argument("--decode-tokens", type=int, default=2048,
                     help="greedy decode tokens timed after the prefill (2048 reach two "
                          "decode-time updates at chunk 1024)")
-    ap.add_argument("--decode-sweep", default="",
+    ap.add_argument("--decode-sweep", default="8192,32768,131072,524288",
                     help="comma-separated prefill lengths after each of which 256 decode tokens are "
-                         "timed (decode cost against context length)")
+                         "timed (decode cost against context length); empty to skip")
     ap.add_argument("--contexts", type=int, default=1,
                     help="also time this many independent contexts prefilled at once "
                          "(one model each, chains interleaved on their own streams)")
@@ -208,8 +210,8 @@ def main():
         torch.cuda.synchronize()
         print(f"# warmup {i} done", file=sys.stderr, flush=True)
 
-    # dominant kernel (the MLP up-projection GEMM of the frozen blocks) and
-    # the other classes timed with HIP events on the library's stream
+    # kernel classes timed with HIP events on the streams they run on; the
+    # dominant kernel (the fused weight-gradient + SGD products) is class 4
     classes = {0: "gemm_all", 1: "attn_fwd", 2: "attn_bwd", 3: "head_ce", 4: "dw_sgd", 5: "mlp_up"}
     for c in classes:
         model.timing_enable(c, True)
@@ -404,6 +406,7 @@ def main():
     if sg["launches"] and (sg["ms"] >= up["ms"] or not up["launches"]):
         avg_ms = sg["ms"] / sg["launches"]
         by = sgd_bytes_per_launch(dict(cfg, T=T), T)
+        by_design = sgd_bytes_per_launch(dict(cfg, T=T), T, per_weight=14.0)
         ach = by / (avg_ms / 1e3) / 1e9
         traffic = (SGD_TRAFFIC["bytes_per_launch"] if _gemm_src_sha() == SGD_TRAFFIC["gemm_src_sha256"]
                    else None)
@@ -411,8 +414,12 @@ def main():
                 "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic,
                 "kernel": "gemm256_kernel<SGD epilogue, bf16> (fused weight gradient + SGD of the "
                           "fast MLPs: [d][F] and [2F][d] over the chunk's tokens, 256x256 tiles)",
-                "algorithmic_bytes_per_launch": round(by), "flops_per_launch": round(sgd_flops_per_launch(
-                    dict(cfg, T=T), T)),
+                "algorithmic_bytes_per_launch": round(by),
+                "algorithmic_bytes_rule": "10 B per fast weight (fp32 master read + write, bf16 copy write) "
+                                          "+ both bf16 operands",
+                "design_bytes_per_launch": round(by_design),
+                "design_gbs": round(by_design / (avg_ms / 1e3) / 1e9, 1),
+                "flops_per_launch": round(sgd_flops_per_launch(dict(cfg, T=T), T)),
                 "avg_launch_ms": round(avg_ms, 4), "launches_per_step": sg["launches"],
                 "stream": "fast-weight update stream (concurrent with the backward chain)"}
     elif up["launches"]:

@@ -15,6 +15,10 @@ dispatches, average duration, and whichever of these the counters allow:
                 max(GRBM_GUI_ACTIVE)
   bf16 TFLOP/s  SQ_INSTS_VALU_MFMA_MOPS_BF16 * 512 / duration
   HBM GB/s      (FETCH_SIZE + WRITE_SIZE) KiB / duration, unscaled
+  LDS active %  rocprof's LDS utilisation: 100 * sum(SQ_LDS_IDX_ACTIVE) /
+                (max(GRBM_GUI_ACTIVE) * CU_NUM)
+  LDS conflict % the same with SQ_LDS_BANK_CONFLICT (cycles stalled by bank
+                conflicts)
 
 The CSV gives every counter summed over its instances; GRBM_GUI_ACTIVE has
 one instance per XCD, so its maximum is taken as the sum over the XCDs
@@ -90,25 +94,30 @@ def summarise(paths, title="", cmds=(), match=None, top=30, cus=256, xcc=8) -> s
         va = mean("SQ_ACTIVE_INST_VALU")
         mops = mean("SQ_INSTS_VALU_MFMA_MOPS_BF16")
         fe, wr = mean("FETCH_SIZE"), mean("WRITE_SIZE")
+        lds, bc = mean("SQ_LDS_IDX_ACTIVE"), mean("SQ_LDS_BANK_CONFLICT")
         avg_ns = ns / n
         rows.append(dict(
             k=k, n=int(n), tot_ms=ns / 1e6, avg_us=avg_ns / 1e3,
             mfma=None if (gui is None or mf is None) else 100 * mf / (gui / xcc * 4 * cus),
             valu=None if (gui is None or va is None) else 100 * va / cus / (gui / xcc),
             tf=None if mops is None else mops * 512 / avg_ns / 1e3,
-            gbs=None if (fe is None and wr is None) else ((fe or 0) + (wr or 0)) * 1024 / avg_ns))
+            gbs=None if (fe is None and wr is None) else ((fe or 0) + (wr or 0)) * 1024 / avg_ns,
+            lds=None if (gui is None or lds is None) else 100 * lds / (gui / xcc * cus),
+            bc=None if (gui is None or bc is None) else 100 * bc / (gui / xcc * cus)))
     rows.sort(key=lambda r: -r["tot_ms"])
     total = sum(r["tot_ms"] for r in rows) or 1.0
     f = lambda v, fmt: "" if v is None else format(v, fmt)   # noqa: E731
     out = [f"# {title}" if title else "# counter summary", ""]
     if cmds:
         out += ["Commands (one counter pass each):", "", "```"] + list(cmds) + ["```", ""]
-    out += ["| kernel | dispatches | total ms | avg us | share | MFMA busy % | VALU busy % | bf16 TFLOP/s | HBM GB/s (raw) |",
-            "|---|---|---|---|---|---|---|---|---|"]
+    cols = [("MFMA busy %", "mfma", ".1f"), ("VALU busy %", "valu", ".1f"), ("bf16 TFLOP/s", "tf", ".0f"),
+            ("HBM GB/s (raw)", "gbs", ".0f"), ("LDS active %", "lds", ".1f"), ("LDS conflict %", "bc", ".1f")]
+    cols = [c for c in cols if any(r[c[1]] is not None for r in rows)]
+    out += ["| kernel | dispatches | total ms | avg us | share | " + " | ".join(c[0] for c in cols) + " |",
+            "|---|---|---|---|---|" + "---|" * len(cols)]
     for r in rows[:top]:
         out.append(f"| `{r['k']}` | {r['n']} | {r['tot_ms']:.2f} | {r['avg_us']:.1f} | "
-                   f"{100 * r['tot_ms'] / total:.1f}% | {f(r['mfma'], '.1f')} | {f(r['valu'], '.1f')} | "
-                   f"{f(r['tf'], '.0f')} | {f(r['gbs'], '.0f')} |")
+                   f"{100 * r['tot_ms'] / total:.1f}% | " + " | ".join(f(r[c[1]], c[2]) for c in cols) + " |")
     return "\n".join(out) + "\n"
 
 

@@ -23,11 +23,15 @@ def test_prefill_flops(name, tflop):
 def test_forward_flops_and_sgd_bytes_3b():
     cfg = synth.config("c4")
     assert bench.forward_flops(cfg, cfg["T"]) / 1e12 == pytest.approx(1214.9, rel=2e-4)
-    # per fast weight 14 B, plus both bf16 operands over the chunk's 1024 tokens
+    # per fast weight 10 B (fp32 master read + write, bf16 copy), plus both
+    # bf16 operands over the chunk's 1024 tokens: 408.9 MB per launch on
+    # average; the design's 14 B per weight: 559.9 MB
     d, F = 3072, 8192
-    up = 14 * 2 * F * d + 2 * (2 * F + d) * 1024
-    dn = 14 * d * F + 2 * (d + F) * 1024
+    up = 10 * 2 * F * d + 2 * (2 * F + d) * 1024
+    dn = 10 * d * F + 2 * (d + F) * 1024
     assert bench.sgd_bytes_per_launch(cfg, cfg["T"]) == pytest.approx((up + dn) / 2, rel=1e-9)
+    assert bench.sgd_bytes_per_launch(cfg, cfg["T"]) / 1e6 == pytest.approx(408.9, abs=0.05)
+    assert bench.sgd_bytes_per_launch(cfg, cfg["T"], per_weight=14) / 1e6 == pytest.approx(559.9, abs=0.05)
     assert bench.sgd_flops_per_launch(cfg, cfg["T"]) == pytest.approx(2.0 * (d * F + 2 * F * d) * 1024 / 2,
                                                                       rel=1e-9)
 
