@@ -82,12 +82,10 @@ def summarise(paths, title="", cmds=(), match=None, top=30, cus=256, xcc=8) -> s
         ns = c["_dispatch_ns_" + p0]
 
         def mean(counter):
+            # one row per counter and dispatch (its instances summed): the
+            # mean over every dispatch that reported it, whichever pass
             cnt = c.get("_n_" + counter)
-            if not cnt:
-                return None
-            # counters are summed over their instance rows; per dispatch:
-            d = c["_dispatches_" + next(p for p in paths if c.get("_dispatches_" + p))]
-            return c[counter] / d
+            return c[counter] / cnt if cnt else None
 
         gui = mean("GRBM_GUI_ACTIVE")
         mf = mean("SQ_VALU_MFMA_BUSY_CYCLES")
