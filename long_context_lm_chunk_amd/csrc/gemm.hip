@@ -520,10 +520,13 @@ constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 static_assert((NS - 2) * LOADS < 64, "vmcnt range");
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Issue the loads of one 256-row operand slab (rows row0.., k k0..k0+31)
-// into LDS at dst: 16 wave instructions of 1 KB (16 rows), SLAB_LOADS per wave.
-DEVI void load_slab(__amdgpu_buffer_rsrc_t rs, uint32_t ldb, int row0, int rows, int k0, int K,
-                    char* dst, int wave, int lane) {
+// The loads of one 256-row operand slab (rows row0.., k k0..k0+31) into
+// LDS: 16 wave instructions of 1 KB (16 rows), SLAB_LOADS per wave.  The
+// buffer offsets are computed first (slab_offsets, out of OOB past the
+// operand's rows or K) and the loads issued later (slab_fire), so that the
+// address arithmetic can run under the products before the stage barrier.
+DEVI void slab_offsets(uint32_t ldb, int row0, int rows, int k0, int K, int wave, int lane,
+                       uint32_t (&off)[SLAB_LOADS]) {
   const int rl = lane >> 2, p = lane & 3;
 #pragma unroll
   for (int i = 0; i < SLAB_LOADS; ++i) {
@@ -532,9 +535,14 @@ DEVI void load_slab(__amdgpu_buffer_rsrc_t rs, uint32_t ldb, int row0, int rows,
     const int c = p ^ ((r >> 2) & 3);                   // logical chunk at slot p
     const int k = k0 + 8 * c;
     const bool ok = row0 + r < rows && k < K;
-    const uint32_t off = ok ? (uint32_t)(row0 + r) * ldb + (uint32_t)k * 2u : OOB;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + blk * 1024), 16, off, 0, 0, 0);
+    off[i] = ok ? (uint32_t)(row0 + r) * ldb + (uint32_t)k * 2u : OOB;
   }
+}
+DEVI void slab_fire(__amdgpu_buffer_rsrc_t rs, const uint32_t (&off)[SLAB_LOADS], char* dst, int wave) {
+#pragma unroll
+  for (int i = 0; i < SLAB_LOADS; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + (wave * SLAB_LOADS + i) * 1024), 16, off[i],
+                                             0, 0, 0);
 }
 }  // namespace big
 
@@ -578,20 +586,31 @@ __global__ __launch_bounds__(big::NT, 1) void gemm256_kernel(GemmParams p) {
   const __amdgpu_buffer_rsrc_t rb2 = make_rsrc(DUAL ? p.B2 : p.B, (int64_t)p.N * p.ldb * 2);
   const uint32_t lda = (uint32_t)p.lda * 2u, ldb = (uint32_t)p.ldb * 2u;
   // k-tile kt into ring slot kt % NS; past kt_end the loads read zeros
-  auto issue = [&](int kt) {
+  typedef uint32_t Offs[big::SLAB_LOADS];
+  auto prep = [&](int kt, Offs& oa, Offs& ob) {
     const bool live = kt < kt_end;
     const bool second = DUAL && kt >= nk1;
     const int k0 = live ? (second ? kt - nk1 : kt) * BK : p.K;
-    char* st = smem + ((kt - kt_begin) % NS) * STAGE;
-    big::load_slab(ra, lda, m0, p.M, k0, p.K, st, wave, lane);
-    big::load_slab(second ? rb2 : rb, ldb, n0, p.N, k0, p.K, st + STAGE_A, wave, lane);
+    big::slab_offsets(lda, m0, p.M, k0, p.K, wave, lane, oa);
+    big::slab_offsets(ldb, n0, p.N, k0, p.K, wave, lane, ob);
+  };
+  auto fire = [&](int kt, const Offs& oa, const Offs& ob) {
+    const bool second = DUAL && kt >= nk1;
+    char* st = smem + ((unsigned)(kt - kt_begin) % NS) * STAGE;
+    big::slab_fire(ra, oa, st, wave);
+    big::slab_fire(second ? rb2 : rb, ob, st + STAGE_A, wave);
+  };
+  auto issue = [&](int kt) {
+    Offs oa, ob;
+    prep(kt, oa, ob);
+    fire(kt, oa, ob);
   };
   // fragment addressing: lane reads row (l & 31) of a 32-row block, logical
   // chunk 2*ks + (l >> 5), at slot chunk ^ ((row >> 2) & 3) = chunk ^ ((l >> 2) & 3)
   const int frow = lane & 31, fsw = (lane >> 2) & 3, fhi = lane >> 5;
   const int abase = (wm * TM + frow) * ROWB, bbase = STAGE_A + (wn * TN + frow) * ROWB;
   auto frags = [&](int kt, int ks, bf16x8 (&a)[FI], bf16x8 (&b)[FJ]) {
-    const char* st = smem + ((kt - kt_begin) % NS) * STAGE;
+    const char* st = smem + ((unsigned)(kt - kt_begin) % NS) * STAGE;
     const int slot = ((2 * ks + fhi) ^ fsw) * 16;
 #pragma unroll
     for (int i = 0; i < FI; ++i) a[i] = *reinterpret_cast<const bf16x8*>(st + abase + i * 32 * ROWB + slot);
@@ -609,7 +628,11 @@ __global__ __launch_bounds__(big::NT, 1) void gemm256_kernel(GemmParams p) {
   // (Against a wait and barrier at the start of each stage this removes
   // the LDS-latency bubble before every stage's first products: 8-15 %
   // on the large shapes.)  Within a k-step the next step's fragment reads
-  // are interleaved one per product (2-6 % on the large shapes alone).
+  // are interleaved one per product (2-6 % on the large shapes alone).  The
+  // next stage's load offsets are computed before the barrier, under the
+  // first k-step's products, and its loads go out between the second
+  // k-step's products, so the matrix unit resumes right after the barrier
+  // (3-12 % on the 3B shapes alone, +1.2 % prefill).
   static_assert(BK == 32 && NS >= 4, "two k-steps per stage; stage kt + 1 waited for mid-stage");
   bf16x8 fa0[FI], fb0[FJ], fa1[FI], fb1[FJ];
   if (kt_begin < kt_end) {
@@ -621,6 +644,8 @@ __global__ __launch_bounds__(big::NT, 1) void gemm256_kernel(GemmParams p) {
     frags(kt_begin, 0, fa0, fb0);
   }
   for (int kt = kt_begin; kt < kt_end; ++kt) {
+    Offs oa, ob;
+    prep(kt + NS - 1, oa, ob);             // address arithmetic under this k-step's products
     frags(kt, 1, fa1, fb1);
 #pragma unroll
     for (int i = 0; i < FI; ++i)
@@ -637,7 +662,7 @@ __global__ __launch_bounds__(big::NT, 1) void gemm256_kernel(GemmParams p) {
     __builtin_amdgcn_s_waitcnt(big::vmcnt_imm((NS - 3) * big::LOADS));    // stage kt + 1
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    issue(kt + NS - 1);
+    fire(kt + NS - 1, oa, ob);
     frags(kt + 1, 0, fa0, fb0);            // past the end: zeros, unused
 #pragma unroll
     for (int i = 0; i < FI; ++i)
@@ -646,6 +671,7 @@ __global__ __launch_bounds__(big::NT, 1) void gemm256_kernel(GemmParams p) {
 #pragma unroll
     for (int u = 0; u < FI + FJ; ++u) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (u < big::LOADS) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, FI * FJ - (FI + FJ), 0);
