@@ -492,47 +492,56 @@ __global__ void gemm_reduce_k(GemmParams p, int nz) {
 // Workgroup tile 256x256, eight waves in 2x4 (two per SIMD, so one wave's
 // barrier and load issue hide behind the other's products), each wave
 // 128x64 = 4x2 blocks of 32x32 accumulators (v_mfma_f32_32x32x16_bf16).
-// K advances 32 per stage through a ring of four 32 KB stages filled by
-// direct global->LDS 16-byte loads (buffer_load ... lds: no staging
-// registers; out-of-range rows and columns read as zero), issued three
-// stages ahead.
+// K advances 64 per stage through two 64 KB stages filled by direct
+// global->LDS 16-byte loads (buffer_load ... lds: no staging registers;
+// out-of-range rows and columns read as zero).  A 1 KB wave load covers 8
+// rows of 128 contiguous bytes, whole cache lines: with 32-wide stages
+// (64-byte row pieces, four 32 KB stages) the same bytes took twice the
+// address work, the vector-memory address and command queues were full
+// most of the time (rocprof's SQ_VMEM_TA_ADDR_FIFO_FULL 27x hipBLASLt's on
+// the same product) and the products ran 4-8% slower on the 3B shapes
+// (2.4% in the prefill).
 // Every stage slot issues the same number of loads (past the end of K they
 // read zeros into a slot nobody uses), so the wait for a stage is a fixed
-// vmcnt.  LDS rows are 64 bytes; 16-byte chunk c of row r sits at slot
-// c ^ ((r >> 2) & 3): a fragment read (one chunk of 32 consecutive rows)
-// then runs at the full 128-bit LDS read rate (measured on gfx950 against
-// linear addressing; the unswizzled layout runs at a third of it).
+// vmcnt.  LDS rows are 128 bytes; 16-byte chunk c of row r sits at slot
+// c ^ ((r >> 1) & 7): the 16 lanes of one LDS read pass (16 consecutive
+// rows, one chunk) then hit 16 distinct 16-byte bank groups.
 namespace big {
-constexpr int BM = 256, BN = 256, BK = 32, NS = 4;
+constexpr int BM = 256, BN = 256, BK = 64, NS = 2;   // two 64-wide k stages
 constexpr int WM = 2, WN = 4, NW = WM * WN, NT = 64 * NW;   // 8 waves, 2 per SIMD
 constexpr int TM = BM / WM, TN = BN / WN;    // wave tile 128 x 64
 constexpr int FI = TM / 32, FJ = TN / 32;    // 32x32 accumulator blocks per wave (4 x 2)
 constexpr int ROWB = BK * 2;                 // bytes per LDS row
-constexpr int STAGE_A = BM * ROWB;           // 16 KB
-constexpr int STAGE = (BM + BN) * ROWB;      // 32 KB
-constexpr int LDS_BYTES = NS * STAGE;        // 128 KB of the 160 KB per CU (a fifth
-                                             // stage measured no faster)
-constexpr int SLAB_LOADS = BM * ROWB / 1024 / NW;   // 1 KB loads per wave per operand slab (2)
+constexpr int STAGE_A = BM * ROWB;
+constexpr int STAGE = (BM + BN) * ROWB;
+constexpr int LDS_BYTES = NS * STAGE;        // 128 KB of the 160 KB per CU
+constexpr int CHUNKS = ROWB / 16;            // 16-byte chunks per LDS row
+constexpr int RPL = 64 / CHUNKS;             // rows per 1 KB wave load
+constexpr int SLAB_LOADS = BM / RPL / NW;    // 1 KB loads per wave per operand slab
 constexpr int LOADS = 2 * SLAB_LOADS;        // per wave per stage
 static_assert(NW * 32 * (BN / WN + 4) * 4 <= LDS_BYTES, "per-wave epilogue areas fit");
+// slot of 16-byte chunk c of row r: c ^ swz(r), so that the 16 lanes of one
+// LDS read pass (16 consecutive rows, one chunk) hit 16 distinct 16-byte
+// bank groups
+DEVI int swz(int r) { return (r >> 1) & 7; }
 // s_waitcnt immediates with vmcnt n (expcnt and lgkmcnt not waited for)
 constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
-static_assert((NS - 2) * LOADS < 64, "vmcnt range");
+static_assert((NS - 1) * LOADS < 64, "vmcnt range");
 typedef __attribute__((address_space(3))) void lds_void;
 
-// The loads of one 256-row operand slab (rows row0.., k k0..k0+31) into
-// LDS: 16 wave instructions of 1 KB (16 rows), SLAB_LOADS per wave.  The
+// The loads of one 256-row operand slab (rows row0.., k k0..k0+BK-1) into
+// LDS: wave instructions of 1 KB (RPL rows), SLAB_LOADS per wave.  The
 // buffer offsets are computed first (slab_offsets, out of OOB past the
 // operand's rows or K) and the loads issued later (slab_fire), so that the
 // address arithmetic can run under the products before the stage barrier.
 DEVI void slab_offsets(uint32_t ldb, int row0, int rows, int k0, int K, int wave, int lane,
                        uint32_t (&off)[SLAB_LOADS]) {
-  const int rl = lane >> 2, p = lane & 3;
+  const int rl = lane / CHUNKS, p = lane % CHUNKS;
 #pragma unroll
   for (int i = 0; i < SLAB_LOADS; ++i) {
-    const int blk = wave * SLAB_LOADS + i;              // 16-row block of the slab
-    const int r = blk * 16 + rl;                        // row within the slab
-    const int c = p ^ ((r >> 2) & 3);                   // logical chunk at slot p
+    const int blk = wave * SLAB_LOADS + i;              // RPL-row block of the slab
+    const int r = blk * RPL + rl;                       // row within the slab
+    const int c = p ^ swz(r);                           // logical chunk at slot p
     const int k = k0 + 8 * c;
     const bool ok = row0 + r < rows && k < K;
     off[i] = ok ? (uint32_t)(row0 + r) * ldb + (uint32_t)k * 2u : OOB;
@@ -607,7 +616,7 @@ __global__ __launch_bounds__(big::NT, 1) void gemm256_kernel(GemmParams p) {
   };
   // fragment addressing: lane reads row (l & 31) of a 32-row block, logical
   // chunk 2*ks + (l >> 5), at slot chunk ^ ((row >> 2) & 3) = chunk ^ ((l >> 2) & 3)
-  const int frow = lane & 31, fsw = (lane >> 2) & 3, fhi = lane >> 5;
+  const int frow = lane & 31, fsw = big::swz(frow), fhi = lane >> 5;
   const int abase = (wm * TM + frow) * ROWB, bbase = STAGE_A + (wn * TN + frow) * ROWB;
   auto frags = [&](int kt, int ks, bf16x8 (&a)[FI], bf16x8 (&b)[FJ]) {
     const char* st = smem + ((unsigned)(kt - kt_begin) % NS) * STAGE;
@@ -617,65 +626,59 @@ __global__ __launch_bounds__(big::NT, 1) void gemm256_kernel(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < FJ; ++j) b[j] = *reinterpret_cast<const bf16x8*>(st + bbase + j * 32 * ROWB + slot);
   };
-  // Fragments run one k-step ahead of the products, across stage borders:
-  // the reads of (kt, 1) go out before the products of (kt, 0), those of
-  // (kt + 1, 0) before the products of (kt, 1).  Stage kt + 1 must then be
-  // complete in LDS half-way through stage kt, so the wait and the barrier
-  // sit between the two k-steps: this wave's loads of stage kt + 1 have
-  // landed once only the NS - 3 younger stages' are outstanding, the
-  // barrier makes that hold for every wave and also frees slot
-  // (kt - 1) % NS, which nobody reads any more, for stage kt + NS - 1.
-  // (Against a wait and barrier at the start of each stage this removes
-  // the LDS-latency bubble before every stage's first products: 8-15 %
-  // on the large shapes.)  Within a k-step the next step's fragment reads
-  // are interleaved one per product (2-6 % on the large shapes alone).  The
-  // next stage's load offsets are computed before the barrier, under the
-  // first k-step's products, and its loads go out between the second
-  // k-step's products, so the matrix unit resumes right after the barrier
-  // (3-12 % on the 3B shapes alone, +1.2 % prefill).
-  static_assert(BK == 32 && NS >= 4, "two k-steps per stage; stage kt + 1 waited for mid-stage");
   bf16x8 fa0[FI], fb0[FJ], fa1[FI], fb1[FJ];
-  if (kt_begin < kt_end) {
+  // products of one k-step on (a, b) with the fragment reads of the next
+  // (issued by the caller just before) interleaved one per product, and the
+  // VL vector loads of a later stage among the first products
+  auto kstep = [&](const bf16x8 (&a)[FI], const bf16x8 (&b)[FJ], auto vl) {
 #pragma unroll
-    for (int u = 0; u < NS - 1; ++u) issue(kt_begin + u);
-    __builtin_amdgcn_s_waitcnt(big::vmcnt_imm((NS - 2) * big::LOADS));    // stage kt_begin
+    for (int i = 0; i < FI; ++i)
+#pragma unroll
+      for (int j = 0; j < FJ; ++j) mma32x32x16(a[i], b[j], acc[i][j]);
+#pragma unroll
+    for (int u = 0; u < FI + FJ; ++u) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (u < decltype(vl)::value) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, FI * FJ - (FI + FJ), 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  using none = std::integral_constant<int, 0>;
+  using all = std::integral_constant<int, big::LOADS>;
+  // Two 64-wide stages, four k-steps each.  Fragments run one k-step
+  // ahead of the products, across the stage border: the reads of
+  // (kt + 1, 0) go out during the products of (kt, 3).  So before that
+  // k-step stage kt + 1 must be complete in LDS (this wave's loads:
+  // vmcnt 0; every wave's: the barrier), and every wave must be done
+  // reading stage kt (lgkmcnt 0, then the barrier), whose slot then takes
+  // stage kt + 2, loaded during the products of (kt, 3) ... (kt + 1, 2).
+  // Each 1 KB load covers 8 rows of 128 contiguous bytes (whole cache
+  // lines: half the address work per byte of 64-byte rows), and one
+  // barrier serves four k-steps.
+  if (kt_begin < kt_end) {
+    issue(kt_begin);
+    issue(kt_begin + 1);
+    __builtin_amdgcn_s_waitcnt(big::vmcnt_imm(big::LOADS));     // stage kt_begin
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     frags(kt_begin, 0, fa0, fb0);
   }
   for (int kt = kt_begin; kt < kt_end; ++kt) {
     Offs oa, ob;
-    prep(kt + NS - 1, oa, ob);             // address arithmetic under this k-step's products
+    prep(kt + 2, oa, ob);                // address arithmetic under these products
     frags(kt, 1, fa1, fb1);
-#pragma unroll
-    for (int i = 0; i < FI; ++i)
-#pragma unroll
-      for (int j = 0; j < FJ; ++j) mma32x32x16(fa0[i], fb0[j], acc[i][j]);
-    // one fragment read between consecutive products
-#pragma unroll
-    for (int u = 0; u < FI + FJ; ++u) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, FI * FJ - (FI + FJ), 0);
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(big::vmcnt_imm((NS - 3) * big::LOADS));    // stage kt + 1
+    kstep(fa0, fb0, none());
+    frags(kt, 2, fa0, fb0);
+    kstep(fa1, fb1, none());
+    frags(kt, 3, fa1, fb1);
+    kstep(fa0, fb0, none());
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): stage kt + 1 in, stage kt read
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    fire(kt + NS - 1, oa, ob);
-    frags(kt + 1, 0, fa0, fb0);            // past the end: zeros, unused
-#pragma unroll
-    for (int i = 0; i < FI; ++i)
-#pragma unroll
-      for (int j = 0; j < FJ; ++j) mma32x32x16(fa1[i], fb1[j], acc[i][j]);
-#pragma unroll
-    for (int u = 0; u < FI + FJ; ++u) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (u < big::LOADS) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, FI * FJ - (FI + FJ), 0);
-    __builtin_amdgcn_sched_barrier(0);
+    fire(kt + 2, oa, ob);
+    frags(kt + 1, 0, fa0, fb0);          // past the end: zeros, unused
+    kstep(fa1, fb1, all());
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0): the zero-fill loads past the end
   __syncthreads();                         // all waves done with the operand stages
