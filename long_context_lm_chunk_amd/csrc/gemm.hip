@@ -243,9 +243,11 @@ DEVI void epi_apply(const GemmParams& p, float* st, int ES, int nr, int nc, int 
       if (row >= p.M || n0 + cg >= p.N) continue;   // N % 32 == 0: gate in => up in
       const float4 gv = *reinterpret_cast<const float4*>(st + r * ES + cg);
       const float4 uv = *reinterpret_cast<const float4*>(st + r * ES + cg + 16);
-      TO* z = static_cast<TO*>(p.C) + (int64_t)row * p.ldc + n0;
-      store4<TO>(z + cg, gv);
-      store4<TO>(z + cg + 16, uv);
+      if (p.C) {                                    // pre-activations kept (for a backward)
+        TO* z = static_cast<TO*>(p.C) + (int64_t)row * p.ldc + n0;
+        store4<TO>(z + cg, gv);
+        store4<TO>(z + cg + 16, uv);
+      }
       float4 a;
       a.x = silu(gv.x) * uv.x; a.y = silu(gv.y) * uv.y; a.z = silu(gv.z) * uv.z; a.w = silu(gv.w) * uv.w;
       store4<TO>(static_cast<TO*>(p.C2) + (int64_t)row * p.ldc2 + n0 / 2 + (q / 4) * 16 + (q % 4) * 4, a);
@@ -265,7 +267,7 @@ DEVI void epi_apply(const GemmParams& p, float* st, int ES, int nr, int nc, int 
         float4 o; o.x = rr.x + v.x; o.y = rr.y + v.y; o.z = rr.z + v.z; o.w = rr.w + v.w;
         *reinterpret_cast<float4*>(static_cast<float*>(p.C) + ci) = o;
       } else if constexpr (EPI == EPI_GELU) {
-        store4<TO>(static_cast<TO*>(p.C) + ci, v);
+        if (p.C) store4<TO>(static_cast<TO*>(p.C) + ci, v);   // pre-activations kept (for a backward)
         float4 a; a.x = gelu_erf(v.x); a.y = gelu_erf(v.y); a.z = gelu_erf(v.z); a.w = gelu_erf(v.w);
         store4<TO>(static_cast<TO*>(p.C2) + (int64_t)row * p.ldc2 + col, a);
       } else if constexpr (EPI == EPI_ACTBWD) {

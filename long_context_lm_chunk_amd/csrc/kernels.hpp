@@ -12,7 +12,7 @@ struct GemmParams {
   const void* B = nullptr; int64_t ldb = 0;  // k-contiguous [N][K] or n-contiguous [K][N]
   const void* B2 = nullptr;                  // optional second B (same layout): C = A.(B + B2)
   int M = 0, N = 0, K = 0;
-  void* C = nullptr; int64_t ldc = 0;        // primary output
+  void* C = nullptr; int64_t ldc = 0;        // primary output (GELU/SWIGLU: pre-activations, optional)
   const float* R = nullptr; int64_t ldr = 0; // residual input (RESID)
   void* C2 = nullptr; int64_t ldc2 = 0;      // act (GELU/SWIGLU), delta copy (SGD)
   void* C3 = nullptr; const void* W0 = nullptr;  // SGD: C3 = round(W0 + delta), written

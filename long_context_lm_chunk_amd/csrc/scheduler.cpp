@@ -141,7 +141,7 @@ struct ttt_model {
   float* hA = nullptr; void* aA = nullptr; void* qkvA = nullptr; void* qA = nullptr; void* oA = nullptr;
   hipStream_t sa = nullptr;
   hipEvent_t ev0 = nullptr, evA[2] = {nullptr, nullptr}, evB[2] = {nullptr, nullptr};
-  void* zA = nullptr; void* actA = nullptr;
+  void* actA = nullptr;
   // phase B
   std::vector<PB> pb;
   float* xL = nullptr; float* meanf = nullptr; float* rstdf = nullptr; void* fN = nullptr;
@@ -304,7 +304,6 @@ size_t layout(ttt_model* m, void* base) {
   m->qkvA = cv.take<void>((size_t)MA * 3 * d * es);
   m->qA = cv.take<void>((size_t)MA * d * es);
   m->oA = cv.take<void>((size_t)MA * d * es);
-  m->zA = cv.take<void>((size_t)MA * F2 * es);
   m->actA = cv.take<void>((size_t)MA * F * es);
   // phase B
   m->pb.assign(m->q, PB());
@@ -510,7 +509,7 @@ int block_fwd(ttt_model* m, int l, int64_t pos0, int nb, float* x, const float2*
   layernorm_fwd(x, d, nb, d, m->c.ln_eps, m->aA, d, nullptr, nullptr, bf, s);
   GemmParams gu;
   gu.A = m->aA; gu.lda = d; gu.B = ly.wup; gu.ldb = d; gu.M = nb; gu.N = F2; gu.K = d;
-  gu.C = m->zA; gu.ldc = F2; gu.C2 = m->actA; gu.ldc2 = F;
+  gu.C2 = m->actA; gu.ldc2 = F;     // no backward here: the pre-activations are not kept
   rc = run_gemm(m, gu, true, true, m->c.mlp == TTT_MLP_SWIGLU ? EPI_SWIGLU : EPI_GELU, false, s, false);
   if (rc) return rc;
   GemmParams gd;
