@@ -460,20 +460,22 @@ __global__ __launch_bounds__(stg::NTHR, 1) void swa_bwd_dq_bf16_128_k(AttnParams
   const __amdgpu_buffer_rsrc_t rt = rsrc(p.ktring, (int64_t)d * p.cap * 2);
   // ring slot of the next tile to load, advanced by one tile per issue
   // (tiles never wrap: cap % 64 == 0)
-  int64_t slot_next = (ktA + (int64_t)tb * KT) % p.cap;
-  auto issue = [&](int stage) {
-    const int64_t slot0 = slot_next;
-    slot_next = slot_next + KT == p.cap ? 0 : slot_next + KT;
-    char* st = smem + stage * STAGE;
+  // (32-bit offsets: the launch admits rings of at most 2^31 - 1 bytes)
+  uint32_t slot_next = (uint32_t)((ktA + (int64_t)tb * KT) % p.cap);
+  const uint32_t ucap = (uint32_t)p.cap, ud = (uint32_t)d;
+  // the next tile's buffer offsets, computed under the current tile's
+  // products (prep) and used by its loads after the barrier (fire)
+  uint32_t offk[PER], offt[PER];
+  auto prep = [&]() {
+    const uint32_t slot0 = slot_next;
+    slot_next = slot_next + KT == ucap ? 0u : slot_next + KT;
     // K and V: 16 instructions of 4 rows (1 KB) each per tile
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int q = wave * PER + i;
       const int row = q * 4 + (lane >> 4), pc = lane & 15;
       const int c = pc ^ (row & 15);
-      const uint32_t off = (uint32_t)(((slot0 + row) * d + h * HD + 8 * c) * 2);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(st + q * 1024), 16, off, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(st + TILE_K + q * 1024), 16, off, 0, 0, 0);
+      offk[i] = ((slot0 + row) * ud + h * HD + 8 * c) * 2u;
     }
     // K^T: 16 instructions of 8 rows (head dims) each
 #pragma unroll
@@ -481,17 +483,34 @@ __global__ __launch_bounds__(stg::NTHR, 1) void swa_bwd_dq_bf16_128_k(AttnParams
       const int q = wave * PER + i;
       const int row = q * 8 + (lane >> 3), pc = lane & 7;
       const int c = pc ^ ((row >> 1) & 7);
-      const uint32_t off = (uint32_t)((((int64_t)(h * HD + row)) * p.cap + slot0 + 8 * c) * 2);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, (lds_void*)(st + 2 * TILE_K + q * 1024), 16, off, 0, 0, 0);
+      offt[i] = ((uint32_t)(h * HD + row) * ucap + slot0 + 8 * c) * 2u;
     }
   };
+  auto fire = [&](int stage) {
+    char* st = smem + stage * STAGE;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int q = wave * PER + i;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(st + q * 1024), 16, offk[i], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(st + TILE_K + q * 1024), 16, offk[i], 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, (lds_void*)(st + 2 * TILE_K + (wave * PER + i) * 1024), 16,
+                                               offt[i], 0, 0, 0);
+  };
 
-  if (tb < te) issue(0);
+  if (tb < te) {
+    prep();
+    fire(0);
+    prep();                                // offsets of tile tb + 1
+  }
   for (int it = tb; it < te; ++it) {
     const int stage = (it - tb) & 1;
+    __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(0x0F70);    // vmcnt(0): this wave's loads of tile it
     __syncthreads();                       // every wave's; the other stage is free
-    if (it + 1 < te) issue(stage ^ 1);
+    if (it + 1 < te) fire(stage ^ 1);
     const char* Ks = smem + stage * STAGE;
     const char* Vs = Ks + TILE_K;
     const char* Ts = Ks + 2 * TILE_K;
@@ -546,6 +565,7 @@ __global__ __launch_bounds__(stg::NTHR, 1) void swa_bwd_dq_bf16_128_k(AttnParams
         for (int b = 0; b < 4; ++b) mma32x32x16(tf[hf][b], df, dacc[b]);
       }
     }
+    if (it + 2 < te) prep();               // offsets of tile it + 2, under these products
   }
 
   if (!qok) return;
@@ -615,35 +635,52 @@ __global__ __launch_bounds__(stg::NTHR, 1) void swa_fwd_bf16_128_k(AttnParams p)
   const __amdgpu_buffer_rsrc_t rt = rsrc(p.vtring, (int64_t)d * p.cap * 2);
   // ring slot of the next tile to load, advanced by one tile per issue
   // (tiles never wrap: cap % 64 == 0)
-  int64_t slot_next = (ktA + (int64_t)tb * KT) % p.cap;
-  auto issue = [&](int stage) {
-    const int64_t slot0 = slot_next;
-    slot_next = slot_next + KT == p.cap ? 0 : slot_next + KT;
-    char* st = smem + stage * STAGE_F;
+  // (32-bit offsets: the launch admits rings of at most 2^31 - 1 bytes)
+  uint32_t slot_next = (uint32_t)((ktA + (int64_t)tb * KT) % p.cap);
+  const uint32_t ucap = (uint32_t)p.cap, ud = (uint32_t)d;
+  // the next tile's buffer offsets, computed under the current tile's
+  // products (prep) and used by its loads after the barrier (fire)
+  uint32_t offk[PER], offt[PER];
+  auto prep = [&]() {
+    const uint32_t slot0 = slot_next;
+    slot_next = slot_next + KT == ucap ? 0u : slot_next + KT;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int q = wave * PER + i;
       const int row = q * 4 + (lane >> 4), pc = lane & 15;
       const int c = pc ^ (row & 15);
-      const uint32_t off = (uint32_t)(((slot0 + row) * d + h * HD + 8 * c) * 2);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(st + q * 1024), 16, off, 0, 0, 0);
+      offk[i] = ((slot0 + row) * ud + h * HD + 8 * c) * 2u;
     }
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int q = wave * PER + i;
       const int row = q * 8 + (lane >> 3), pc = lane & 7;
       const int c = pc ^ ((row >> 1) & 7);
-      const uint32_t off = (uint32_t)((((int64_t)(h * HD + row)) * p.cap + slot0 + 8 * c) * 2);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, (lds_void*)(st + TILE_K + q * 1024), 16, off, 0, 0, 0);
+      offt[i] = ((uint32_t)(h * HD + row) * ucap + slot0 + 8 * c) * 2u;
     }
   };
+  auto fire = [&](int stage) {
+    char* st = smem + stage * STAGE_F;
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(st + (wave * PER + i) * 1024), 16, offk[i], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, (lds_void*)(st + TILE_K + (wave * PER + i) * 1024), 16, offt[i],
+                                               0, 0, 0);
+  };
 
-  if (tb < te) issue(0);
+  if (tb < te) {
+    prep();
+    fire(0);
+    prep();                                // offsets of tile tb + 1
+  }
   for (int it = tb; it < te; ++it) {
     const int stage = (it - tb) & 1;
+    __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(0x0F70);    // vmcnt(0): this wave's loads of tile it
     __syncthreads();                       // every wave's; the other stage is free
-    if (it + 1 < te) issue(stage ^ 1);
+    if (it + 1 < te) fire(stage ^ 1);
     const char* Ks = smem + stage * STAGE_F;
     const char* Vt = Ks + TILE_K;
     const int64_t kt = ktA + (int64_t)it * KT;
@@ -726,6 +763,7 @@ __global__ __launch_bounds__(stg::NTHR, 1) void swa_fwd_bf16_128_k(AttnParams p)
 #pragma unroll
         for (int b = 0; b < 4; ++b) mma32x32x16(fr[kb * 8 + hf * 4 + b], pf, oacc[b]);
       }
+    if (it + 2 < te) prep();               // offsets of tile it + 2, under these products
   }
 
   if (!qok) return;
