@@ -302,9 +302,9 @@ int64_t ttt_diag_chunk_logit_rows(const struct ttt_model* m);
 
 /*
  * Diagnostic choice of the GEMM core for the bf16 products whose operands
- * are both k-contiguous (forward products, head): mode 0 = by shape (the
- * default: the 256x256 core for long reductions and large grids, the
- * 128x128 core otherwise), 1 = the 256x256 core wherever it applies, 2 = the
+ * are both k-contiguous (forward products, head): mode 0 = the default
+ * (the 256x256 core for every epilogue it has, the 128x128 core for the
+ * rest), 1 = the 256x256 core wherever it applies (the same today), 2 = the
  * 128x128 core only.  Process-wide; returns the previous mode, or the
  * current one unchanged for any other value.  For parity tests that must
  * reach a core the default would not pick at their sizes.

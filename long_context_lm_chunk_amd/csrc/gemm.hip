@@ -845,28 +845,23 @@ bool launch_big(const GemmParams& p, hipStream_t s) {
   return true;
 }
 
-// Which core runs the bf16 k-contiguous products: measured on MI355X, the
-// 256x256 core wins on long reductions (K, doubled for W0 + delta, >= 6144)
-// and on grids of >= 1024 of its tiles; below that its 256 CUs are filled
-// unevenly and the 128x128 core is as fast or faster alone.  In a prefill,
-// where products of several streams share the GPU, two more kinds run
-// faster overall on the 256x256 core: the weight-gradient + SGD products
-// (+1.3%: the half-size operand re-reads of the 128x128 tiles cost more than
-// the uneven fill) and every product over a block of >= 4096 rows (+0.4%:
-// the frozen blocks' output projection); the chunk-sized products that the
-// rule leaves on the 128x128 core are 0.5% slower on the other.
+// Which core runs the bf16 k-contiguous products: the 256x256 core, for
+// every epilogue it has.  Alone, on grids of fewer than ~1024 of its tiles
+// with short reductions, the 128x128 core (two workgroups per CU) fills
+// the CUs more evenly and is as fast or faster; in a prefill, where the
+// products of several streams share the GPU, the larger tiles' fewer
+// operand re-reads per flop win (measured against the 128x128 core for
+// those products: +0.5%, and +0.06% more for the activation-backward
+// products).  The 128x128 core keeps the fp32 products, the other operand
+// layouts and the cross-entropy statistics.
 int g_gemm_core = GEMM_CORE_AUTO;
 
 template <typename T, bool AK, bool BK_, int EPI, typename TO>
 void launch_t(const GemmParams& p, hipStream_t s) {
   if constexpr (std::is_same<T, bf16>::value && AK && BK_ &&
                 (EPI == EPI_STORE || EPI == EPI_RESID || EPI == EPI_GELU || EPI == EPI_SWIGLU ||
-                 EPI == EPI_SGD)) {
-    const int64_t keff = (int64_t)p.K * (p.B2 ? 2 : 1);
-    const int64_t tiles = (int64_t)((p.M + 255) / 256) * ((p.N + 255) / 256);
-    const bool want = g_gemm_core == GEMM_CORE_BIG ||
-                      (g_gemm_core == GEMM_CORE_AUTO &&
-                       (keff >= 6144 || tiles >= 1024 || EPI == EPI_SGD || p.M >= 4096));
+                 EPI == EPI_SGD || EPI == EPI_ACTBWD)) {
+    const bool want = g_gemm_core != GEMM_CORE_SMALL;
     if (want && launch_big<EPI, TO>(p, s)) return;
   }
   const int tiles = ((p.N + BN - 1) / BN) * ((p.M + BM - 1) / BM);

@@ -139,15 +139,17 @@ def gemm_core():
     T.diag_gemm_core(T.GEMM_CORE_AUTO)
 
 
-@pytest.mark.parametrize("core", ["auto", "big"])
-@pytest.mark.parametrize("shape", [(300, 544, 6160), (257, 3104, 7000), (64, 96, 32), (513, 264, 8)])
+@pytest.mark.parametrize("core", ["auto", "big", "small"])
+@pytest.mark.parametrize("shape", [(300, 544, 6160), (257, 3104, 7000), (64, 96, 32), (513, 264, 8),
+                                   (1024, 3072, 1000)])
 def test_gemm_large_tile_core_matches_torch(gemm_core, core, shape):
-    """The 256x256 bf16 core (direct-to-LDS four-stage ring, swizzled rows):
-    ragged M and N tails, a K that ends inside a 32-wide stage, K shorter
-    than one stage; reached by its own shape rule (long K) or forced."""
+    """Both bf16 cores on the k-contiguous layout: the 256x256 core (two
+    64-wide direct-to-LDS stages, swizzled rows; the default) and the
+    128x128 core (register-staged; forced): ragged M and N tails, a K that
+    ends inside a stage, K shorter than one stage."""
     T = _gpu()
     M, N, K = shape
-    gemm_core(T.GEMM_CORE_BIG if core == "big" else T.GEMM_CORE_AUTO)
+    gemm_core({"big": T.GEMM_CORE_BIG, "small": T.GEMM_CORE_SMALL}.get(core, T.GEMM_CORE_AUTO))
     say(f"case gemm large-tile core={core} M={M} N={N} K={K}")
     g = torch.Generator().manual_seed(M * 5 + N * 11 + K)
     A = torch.randn(M, K, generator=g).to(torch.bfloat16)
