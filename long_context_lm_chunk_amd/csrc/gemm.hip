@@ -776,6 +776,72 @@ __global__ __launch_bounds__(big::NT, 1) void gemm256_kernel(GemmParams p) {
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
+  } else if constexpr (EPI == EPI_CESTAT) {
+    // rows = tokens, cols = vocab: per row the (max, sum of exp) of each
+    // 64-column group (partial index col / 64, as in the 128x128 core), the
+    // target logit where the target falls in the group, and (when C is set)
+    // the logits themselves for the gradient pass.  Each wave stages its
+    // 128 x 64 block 32 rows at a time; two lanes per row then take 32
+    // columns each.
+    constexpr int P = TN + 4;
+    float* ws = reinterpret_cast<float*>(smem) + wave * 32 * P;
+    const int cb = n0 + wn * TN;
+    const int part = cb / 64;
+    const int sr = lane >> 1, sh = lane & 1;
+#pragma unroll
+    for (int i = 0; i < FI; ++i) {
+      const int rbase = m0 + wm * TM + i * 32;
+#pragma unroll
+      for (int j = 0; j < FJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ws[(8 * (r >> 2) + 4 * fhi + (r & 3)) * P + j * 32 + frow] = acc[i][j][r];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      if (p.C) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int g = u * 64 + lane, r = g >> 4, c = (g & 15) * 4;
+          const int row = rbase + r, col = cb + c;
+          if (row >= p.M || col >= p.N) continue;
+          float* dst = static_cast<float*>(p.C) + (int64_t)row * p.ldc + col;
+          const float4 v = *reinterpret_cast<const float4*>(ws + r * P + c);
+          if (col + 3 < p.N) {
+            *reinterpret_cast<float4*>(dst) = v;
+          } else {
+            dst[0] = v.x;
+            if (col + 1 < p.N) dst[1] = v.y;
+            if (col + 2 < p.N) dst[2] = v.z;
+          }
+        }
+      }
+      const int row = rbase + sr;
+      const float* wr = ws + sr * P + sh * 32;
+      const int c1 = cb + sh * 32;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int c = 0; c < 32; ++c)
+        if (c1 + c < p.N) mx = fmaxf(mx, wr[c]);
+      mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
+      float sm = 0.f;
+      const int t = (row < p.n_tgt) ? p.tgt[row] : -1;
+#pragma unroll
+      for (int c = 0; c < 32; ++c)
+        if (c1 + c < p.N) sm += __expf(wr[c] - mx);
+      sm += __shfl_xor(sm, 1, 64);
+      if (row < p.M) {
+        // the partial arrays hold 2 * ceil(N / 128) groups (the 128x128
+        // core's count): the groups past N up to there read (-inf, 0)
+        if (sh == 0 && part < 2 * ((p.N + 127) / 128)) {
+          p.part_max[(int64_t)part * p.ldpart + row] = mx;
+          p.part_sum[(int64_t)part * p.ldpart + row] = sm;
+        }
+        if (t >= c1 && t < c1 + 32 && t < p.N) p.tgt_logit[row] = wr[t - c1];
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
   } else {
     // The other epilogues the same way: each wave applies it to its own
     // 128 x 64 block, 32 rows at a time, staged in a private LDS area.
@@ -852,15 +918,15 @@ bool launch_big(const GemmParams& p, hipStream_t s) {
 // products of several streams share the GPU, the larger tiles' fewer
 // operand re-reads per flop win (measured against the 128x128 core for
 // those products: +0.5%, and +0.06% more for the activation-backward
-// products).  The 128x128 core keeps the fp32 products, the other operand
-// layouts and the cross-entropy statistics.
+// products, +0.5% for the cross-entropy statistics).  The 128x128 core
+// keeps the fp32 products and the other operand layouts.
 int g_gemm_core = GEMM_CORE_AUTO;
 
 template <typename T, bool AK, bool BK_, int EPI, typename TO>
 void launch_t(const GemmParams& p, hipStream_t s) {
   if constexpr (std::is_same<T, bf16>::value && AK && BK_ &&
                 (EPI == EPI_STORE || EPI == EPI_RESID || EPI == EPI_GELU || EPI == EPI_SWIGLU ||
-                 EPI == EPI_SGD || EPI == EPI_ACTBWD)) {
+                 EPI == EPI_SGD || EPI == EPI_ACTBWD || EPI == EPI_CESTAT)) {
     const bool want = g_gemm_core != GEMM_CORE_SMALL;
     if (want && launch_big<EPI, TO>(p, s)) return;
   }

@@ -214,6 +214,21 @@ def test_prefill_small_models_large_tile_core(gemm_core, mlp, hd, q):
     assert r["dWmax"] < BAR["bf16"] and r["dloss"] < DLOSS_BAR["bf16"]
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("vocab", [200, 296])
+def test_prefill_vocab_not_a_multiple_of_the_tile(dtype, vocab):
+    """A vocabulary that ends inside a 256-column tile of the head's
+    statistics product (bf16: the 256x256 core, whose tiles also cover
+    64-column groups past the vocabulary's end; fp32: the 128x128 core):
+    losses and fast weights against the oracle."""
+    cfg = small_cfg(vocab=vocab, mlp="swiglu", head_dim=32, n_heads=2, d_model=64)
+    r = run_pair(cfg, dtype=dtype, std=0.05, prefill_block=64)
+    assert r["loss"] < BAR[dtype] and r["W"] < BAR[dtype]
+    assert r["loss0"] < BAR[dtype]
+    assert r["dWmax"] < BAR[dtype]
+    assert r["dloss"] < DLOSS_BAR[dtype]
+
+
 # ------------------------------------------------------- whole inner loop
 
 def test_prefill_tiny_fp32_workload():
