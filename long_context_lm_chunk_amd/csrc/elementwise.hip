@@ -456,20 +456,47 @@ __global__ void rope_bwd_tab_k(T* __restrict__ g, int n, int H, int hd, const fl
 template <typename T>
 __global__ __launch_bounds__(256) void transpose_k(const T* __restrict__ src, int rows, int cols,
                                                    int64_t lds_, T* __restrict__ dst, int64_t ldd,
-                                                   int rows_pad, int perm) {
+                                                   int rows_pad, int perm, int vec_in, int vec_out) {
+  // 64 x 64 tile: 16-byte loads along the source rows (V elements), then
+  // runs of 4 source rows written as one 4-element store per output row
+  // (with perm, kperm moves aligned runs of 4 as a whole)
+  constexpr int V = 16 / (int)sizeof(T);
   __shared__ T tile[64][65];
   const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const int t = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int r = r0 + ty * 16 + i, c = c0 + tx;
-    tile[ty * 16 + i][tx] = (r < rows && c < cols) ? src[(int64_t)r * lds_ + c] : from_f32<T>(0.f);
+  for (int idx = t; idx < 64 * (64 / V); idx += 256) {
+    const int row = idx / (64 / V), cv = (idx % (64 / V)) * V;
+    const int r = r0 + row, c = c0 + cv;
+    T v[V];
+    if (vec_in && r < rows && c + V <= cols) {
+      *reinterpret_cast<uint4*>(v) = *reinterpret_cast<const uint4*>(src + (int64_t)r * lds_ + c);
+    } else {
+#pragma unroll
+      for (int e = 0; e < V; ++e) v[e] = (r < rows && c + e < cols) ? src[(int64_t)r * lds_ + c + e] : from_f32<T>(0.f);
+    }
+#pragma unroll
+    for (int e = 0; e < V; ++e) tile[row][cv + e] = v[e];
   }
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int c = c0 + ty * 16 + i, r = r0 + tx;
-    if (c < cols && r < rows_pad) dst[(int64_t)c * ldd + (perm ? kperm(r) : r)] = tile[tx][ty * 16 + i];
+  for (int idx = t; idx < 64 * 16; idx += 256) {
+    const int j = idx / 16, rg = (idx % 16) * 4;
+    const int c = c0 + j, r = r0 + rg;
+    if (c >= cols || r >= rows_pad) continue;
+    T w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = tile[rg + e][j];
+    T* drow = dst + (int64_t)c * ldd;
+    if (vec_out && r + 3 < rows_pad) {
+      T* d4 = drow + (perm ? kperm(r) : r);
+      if constexpr (sizeof(T) == 2) *reinterpret_cast<uint2*>(d4) = *reinterpret_cast<const uint2*>(w);
+      else *reinterpret_cast<uint4*>(d4) = *reinterpret_cast<const uint4*>(w);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (r + e < rows_pad) drow[perm ? kperm(r + e) : r + e] = w[e];
+    }
   }
 }
 
@@ -704,8 +731,13 @@ void transpose(const void* src, int rows, int cols, int64_t lds_, void* dst, int
   if (rows_pad <= 0 || cols <= 0) return;
   dim3 grid((cols + 63) / 64, (rows_pad + 63) / 64);
   const int pm = perm16 ? 1 : 0;
-  TSEL(bf, hipLaunchKernelGGL(transpose_k<bf16>, grid, dim3(256), 0, s, (const bf16*)src, rows, cols, lds_, (bf16*)dst, ldd, rows_pad, pm),
-       hipLaunchKernelGGL(transpose_k<float>, grid, dim3(256), 0, s, (const float*)src, rows, cols, lds_, (float*)dst, ldd, rows_pad, pm));
+  const int es = bf ? 2 : 4;
+  // 16-byte loads need 16-byte aligned source rows, 4-element stores
+  // 4-element aligned destination rows
+  const int vin = (lds_ * es) % 16 == 0 && reinterpret_cast<uintptr_t>(src) % 16 == 0;
+  const int vout = ldd % 4 == 0 && reinterpret_cast<uintptr_t>(dst) % (4 * es) == 0;
+  TSEL(bf, hipLaunchKernelGGL(transpose_k<bf16>, grid, dim3(256), 0, s, (const bf16*)src, rows, cols, lds_, (bf16*)dst, ldd, rows_pad, pm, vin, vout),
+       hipLaunchKernelGGL(transpose_k<float>, grid, dim3(256), 0, s, (const float*)src, rows, cols, lds_, (float*)dst, ldd, rows_pad, pm, vin, vout));
 }
 
 void rope_bwd(void* dqkv, int n, int H, int hd, const float2* cs, bool bf, hipStream_t s) {
