@@ -8,6 +8,15 @@
 namespace ttt {
 namespace {
 
+// 16-byte load with the non-temporal hint, for intermediates read once (the
+// K-split partial slabs, the head's kept logits, the transposes' sources),
+// so that the caches keep what the products read again.
+DEVI float4 ldnt4(const float4* p) {
+  const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  return make_float4(t.x, t.y, t.z, t.w);
+}
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+
 // 4 consecutive values to T (16 bytes of fp32 or 8 of bf16)
 template <typename T> DEVI void store4v(T* p, const float4& v);
 template <> DEVI void store4v<float>(float* p, const float4& v) { *reinterpret_cast<float4*>(p) = v; }
@@ -196,7 +205,7 @@ __global__ __launch_bounds__(256) void ln_bwd_blk_k(const float* __restrict__ dy
     if (z + 1 < nslab) {
       const float4* gs = reinterpret_cast<const float4*>(dy + (z + 1) * slab_stride + (int64_t)row * D);
 #pragma unroll
-      for (int i = 0; i < NQ; ++i) gz[z][i] = gs[tid + 256 * i];
+      for (int i = 0; i < NQ; ++i) gz[z][i] = ldnt4(gs + tid + 256 * i);
     }
   // partial slabs of a K-split product, summed in slab order
 #pragma unroll
@@ -470,7 +479,8 @@ __global__ __launch_bounds__(256) void transpose_k(const T* __restrict__ src, in
     const int r = r0 + row, c = c0 + cv;
     T v[V];
     if (vec_in && r < rows && c + V <= cols) {
-      *reinterpret_cast<uint4*>(v) = *reinterpret_cast<const uint4*>(src + (int64_t)r * lds_ + c);
+      *reinterpret_cast<u32x4v*>(v) =
+          __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(src + (int64_t)r * lds_ + c));
     } else {
 #pragma unroll
       for (int e = 0; e < V; ++e) v[e] = (r < rows && c + e < cols) ? src[(int64_t)r * lds_ + c + e] : from_f32<T>(0.f);
@@ -582,7 +592,7 @@ __global__ void ce_grad_k(const float* __restrict__ z, int64_t ldz, const float*
   const int row = (int)(idx / (V / 4)), col = (int)(idx % (V / 4)) * 4;
   float4 o = {0.f, 0.f, 0.f, 0.f};
   if (row < n_tgt) {
-    const float4 v = *reinterpret_cast<const float4*>(z + (int64_t)row * ldz + col);
+    const float4 v = ldnt4(reinterpret_cast<const float4*>(z + (int64_t)row * ldz + col));
     const float l = lse[row];
     const int t = tgt[row];
     o.x = (__expf(v.x - l) - (col == t ? 1.f : 0.f)) * alpha;
