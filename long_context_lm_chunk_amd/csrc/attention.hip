@@ -368,11 +368,32 @@ template <typename T>
 __global__ void dq_combine_k(AttnParams p, int nsplit) {
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   const int d = p.H * p.hd;
-  if (idx >= p.n * d) return;
-  const int row = idx / d, c = idx % d;
-  float acc = 0.f;
-  for (int z = 0; z < nsplit; ++z) acc += p.part[((int64_t)z * p.n + row) * d + c];
-  static_cast<T*>(p.dq)[(int64_t)row * p.ldg + c] = from_f32<T>(acc);
+  if (!p.rope_cs) {
+    if (idx >= p.n * d) return;
+    const int row = idx / d, c = idx % d;
+    float acc = 0.f;
+    for (int z = 0; z < nsplit; ++z) acc += p.part[((int64_t)z * p.n + row) * d + c];
+    static_cast<T*>(p.dq)[(int64_t)row * p.ldg + c] = from_f32<T>(acc);
+    return;
+  }
+  // with RoPE^-1: one thread per pair (i, i + hd/2) of a head, each summed
+  // and rounded to T, then turned back by the row's angle and rounded again
+  const int half = p.hd / 2;
+  if (idx >= p.n * (d / 2)) return;
+  const int row = idx / (d / 2), r = idx % (d / 2), h = r / half, i = r % half;
+  const int c = h * p.hd + i;
+  float a = 0.f, b = 0.f;
+  for (int z = 0; z < nsplit; ++z) {
+    const float* pz = p.part + ((int64_t)z * p.n + row) * d + c;
+    a += pz[0];
+    b += pz[half];
+  }
+  a = to_f32(from_f32<T>(a));
+  b = to_f32(from_f32<T>(b));
+  const float2 w = p.rope_cs[(int64_t)row * half + i];
+  T* o = static_cast<T*>(p.dq) + (int64_t)row * p.ldg + c;
+  o[0] = from_f32<T>(a * w.x + b * w.y);
+  o[half] = from_f32<T>(b * w.x - a * w.y);
 }
 
 // ------------------------------------------------ backward dQ, bf16, hd 128
@@ -411,6 +432,31 @@ DEVI __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nb, 0x00020000);
 }
 }  // namespace stg
+
+// RoPE^-1 of one row of a head-dim-128 gradient held in 32x32 accumulator
+// blocks (block b has dims b*32 + 8g + 4*hl + e): the gradient is scaled and
+// rounded to bf16 first, then each pair (i, i + 64) is turned back by the
+// row's angle (cs[i] = (cos, sin)) and rounded again, as the separate RoPE
+// backward pass does on the stored gradient.
+DEVI void store_rope_bwd(bf16* dst, const f32x16 (&acc)[4], float scale, const float2* cs, int hl) {
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int c = b * 32 + 8 * g + 4 * hl;
+      bf16x4 oa, ob;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float a = static_cast<float>(static_cast<bf16>(acc[b][4 * g + e] * scale));
+        const float bb = static_cast<float>(static_cast<bf16>(acc[b + 2][4 * g + e] * scale));
+        const float2 w = cs[c + e];
+        oa[e] = static_cast<bf16>(a * w.x + bb * w.y);
+        ob[e] = static_cast<bf16>(bb * w.x - a * w.y);
+      }
+      *reinterpret_cast<bf16x4*>(dst + c) = oa;
+      *reinterpret_cast<bf16x4*>(dst + c + 64) = ob;
+    }
+}
 
 __global__ __launch_bounds__(stg::NTHR, 1) void swa_bwd_dq_bf16_128_k(AttnParams p) {
   using namespace stg;
@@ -570,6 +616,24 @@ __global__ __launch_bounds__(stg::NTHR, 1) void swa_bwd_dq_bf16_128_k(AttnParams
 
   if (!qok) return;
   const float scale = 1.f / sqrtf((float)HD);
+  if (gridDim.z == 1) {
+    bf16* dst = static_cast<bf16*>(p.dq) + (int64_t)qrow * p.ldg + h * HD;
+    if (p.rope_cs) {
+      // dims c and c + 64 (blocks b and b + 2) are the lane's own pairs
+      store_rope_bwd(dst, dacc, scale, p.rope_cs + (int64_t)qrow * (HD / 2), hl);
+    } else {
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          bf16x4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = static_cast<bf16>(dacc[b][4 * g + e] * scale);
+          *reinterpret_cast<bf16x4*>(dst + b * 32 + 8 * g + 4 * hl) = o;
+        }
+    }
+    return;
+  }
 #pragma unroll
   for (int b = 0; b < 4; ++b)
 #pragma unroll
@@ -578,14 +642,7 @@ __global__ __launch_bounds__(stg::NTHR, 1) void swa_bwd_dq_bf16_128_k(AttnParams
       float4 v;
       v.x = dacc[b][4 * g] * scale; v.y = dacc[b][4 * g + 1] * scale;
       v.z = dacc[b][4 * g + 2] * scale; v.w = dacc[b][4 * g + 3] * scale;
-      if (gridDim.z == 1) {
-        bf16x4 o;
-        o[0] = static_cast<bf16>(v.x); o[1] = static_cast<bf16>(v.y);
-        o[2] = static_cast<bf16>(v.z); o[3] = static_cast<bf16>(v.w);
-        *reinterpret_cast<bf16x4*>(static_cast<bf16*>(p.dq) + (int64_t)qrow * p.ldg + h * HD + c) = o;
-      } else {
-        *reinterpret_cast<float4*>(p.part + ((int64_t)bz * p.n + qrow) * d + h * HD + c) = v;
-      }
+      *reinterpret_cast<float4*>(p.part + ((int64_t)bz * p.n + qrow) * d + h * HD + c) = v;
     }
 }
 
@@ -1072,6 +1129,7 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_dkdv_bf16_128_k(AttnParams p) 
   const float scale = 1.f / sqrtf((float)HD);
   bf16* DK = static_cast<bf16*>(p.dk) + (int64_t)krow * p.ldg + h * HD;
   bf16* DV = static_cast<bf16*>(p.dv) + (int64_t)krow * p.ldg + h * HD;
+  if (p.rope_cs) store_rope_bwd(DK, dk, scale, p.rope_cs + (int64_t)krow * (HD / 2), hl);
 #pragma unroll
   for (int b = 0; b < 4; ++b)
 #pragma unroll
@@ -1083,7 +1141,7 @@ __global__ __launch_bounds__(256, 1) void swa_bwd_dkdv_bf16_128_k(AttnParams p) 
         ok4[e] = static_cast<bf16>(dk[b][4 * g + e] * scale);
         ov4[e] = static_cast<bf16>(dv[b][4 * g + e]);
       }
-      *reinterpret_cast<bf16x4*>(DK + c) = ok4;
+      if (!p.rope_cs) *reinterpret_cast<bf16x4*>(DK + c) = ok4;
       *reinterpret_cast<bf16x4*>(DV + c) = ov4;
     }
 }
@@ -1170,7 +1228,7 @@ void fwd_t(const AttnParams& p, hipStream_t s) {
   }
 }
 template <typename T>
-void bwd_t(const AttnParams& p, hipStream_t s, hipStream_t s2) {
+int bwd_t(const AttnParams& p, hipStream_t s, hipStream_t s2) {
   // bf16 / head_dim 128 / 64-aligned ring: the staged 256-query dQ kernel
   // (one workgroup per CU: 256 resident workgroups); otherwise the general one
   const bool wide = staged_ok<T>(p);
@@ -1210,12 +1268,18 @@ void bwd_t(const AttnParams& p, hipStream_t s, hipStream_t s2) {
     if (!wide_kv) hipLaunchKernelGGL((swa_bwd_dkdv32_k<T, HDV>), gk, dim3(256), 0, s2, p); break;
     CASE(16) CASE(32) CASE(64) CASE(96) CASE(128)
 #undef CASE
-    default: return;
+    default: return 0;
   }
+  int rotated = 0;
   if (nz > 1) {
-    const int tot = p.n * p.H * p.hd;
+    const int tot = p.n * p.H * p.hd / (p.rope_cs ? 2 : 1);
     hipLaunchKernelGGL(dq_combine_k<T>, dim3((tot + 255) / 256), dim3(256), 0, s, p, nz);
+    if (p.rope_cs) rotated |= 1;
+  } else if (wide && p.rope_cs) {
+    rotated |= 1;
   }
+  if (wide_kv && p.rope_cs) rotated |= 2;
+  return rotated;
 }
 
 }  // namespace
@@ -1225,9 +1289,9 @@ void swa_fwd(const AttnParams& p, bool bf, hipStream_t s) {
   if (bf) fwd_t<bf16>(p, s); else fwd_t<float>(p, s);
 }
 
-void swa_bwd(const AttnParams& p, bool bf, hipStream_t s, hipStream_t s_kv) {
-  if (p.n <= 0) return;
-  if (bf) bwd_t<bf16>(p, s, s_kv); else bwd_t<float>(p, s, s_kv);
+int swa_bwd(const AttnParams& p, bool bf, hipStream_t s, hipStream_t s_kv) {
+  if (p.n <= 0) return 0;
+  return bf ? bwd_t<bf16>(p, s, s_kv) : bwd_t<float>(p, s, s_kv);
 }
 
 bool swa_bwd_reads_transposes(int hd, bool bf) { return bf && hd == stg::HD; }

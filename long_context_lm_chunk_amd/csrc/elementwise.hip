@@ -433,7 +433,8 @@ __global__ __launch_bounds__(256) void qkv_rope_k(const T* __restrict__ qkv, int
 // Transposed rotation of dQ and dK inside dqkv [n][3d] (the rotation's
 // transpose), 8 pairs per thread with 16-byte accesses, angles from the table.
 template <typename T>
-__global__ void rope_bwd_tab_k(T* __restrict__ g, int n, int H, int hd, const float2* __restrict__ cs) {
+__global__ void rope_bwd_tab_k(T* __restrict__ g, int n, int H, int hd, const float2* __restrict__ cs,
+                               int parts) {
   const int half = hd >> 1, nc = half / 8;
   const int64_t total = (int64_t)n * H * nc;
   const int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
@@ -443,6 +444,7 @@ __global__ void rope_bwd_tab_k(T* __restrict__ g, int n, int H, int hd, const fl
   const float2* e = cs + (int64_t)t * half + i0;
 #pragma unroll
   for (int part = 0; part < 2; ++part) {
+    if (!((parts >> part) & 1)) continue;
     T* r = g + (int64_t)t * 3 * d + part * d + h * hd;
     float a[8], b[8], ra[8], rb[8];
     ld8<T>(r + i0, a);
@@ -750,11 +752,11 @@ void transpose(const void* src, int rows, int cols, int64_t lds_, void* dst, int
        hipLaunchKernelGGL(transpose_k<float>, grid, dim3(256), 0, s, (const float*)src, rows, cols, lds_, (float*)dst, ldd, rows_pad, pm, vin, vout));
 }
 
-void rope_bwd(void* dqkv, int n, int H, int hd, const float2* cs, bool bf, hipStream_t s) {
+void rope_bwd(void* dqkv, int n, int H, int hd, const float2* cs, bool bf, hipStream_t s, int parts) {
   const int64_t total = (int64_t)n * H * (hd / 16);
-  if (total <= 0) return;
-  TSEL(bf, hipLaunchKernelGGL(rope_bwd_tab_k<bf16>, dim3(nblk(total, 256)), dim3(256), 0, s, (bf16*)dqkv, n, H, hd, cs),
-       hipLaunchKernelGGL(rope_bwd_tab_k<float>, dim3(nblk(total, 256)), dim3(256), 0, s, (float*)dqkv, n, H, hd, cs));
+  if (total <= 0 || !(parts & 3)) return;
+  TSEL(bf, hipLaunchKernelGGL(rope_bwd_tab_k<bf16>, dim3(nblk(total, 256)), dim3(256), 0, s, (bf16*)dqkv, n, H, hd, cs, parts),
+       hipLaunchKernelGGL(rope_bwd_tab_k<float>, dim3(nblk(total, 256)), dim3(256), 0, s, (float*)dqkv, n, H, hd, cs, parts));
 }
 
 

@@ -511,6 +511,16 @@ __global__ void gemm_reduce_k(GemmParams p, int nz) {
     *reinterpret_cast<float4*>(static_cast<float*>(p.C) + ci) = v;
   } else {
     store4<TO>(static_cast<TO*>(p.C) + ci, v);
+    if (p.rd_D) {
+      // rowsum over a head of rd_o times the stored values: the head's
+      // rd_hd / 4 threads are consecutive lanes of one wave
+      const float4 o = load4<TO>(static_cast<const TO*>(p.rd_o) + ci);
+      float t = o.x * to_f32(from_f32<TO>(v.x)) + o.y * to_f32(from_f32<TO>(v.y)) +
+                o.z * to_f32(from_f32<TO>(v.z)) + o.w * to_f32(from_f32<TO>(v.w));
+      const int lanes = p.rd_hd / 4;
+      for (int m = lanes / 2; m > 0; m >>= 1) t += __shfl_xor(t, m, 64);
+      if (((col / 4) & (lanes - 1)) == 0) p.rd_D[(int64_t)(col / p.rd_hd) * p.M + row] = t;
+    }
   }
 }
 
@@ -891,6 +901,19 @@ __global__ __launch_bounds__(big::NT, 1) void gemm256_kernel(GemmParams p) {
   }
 }
 
+// The reduction pass's parameters: its rowsum option (rd_D) is kept for a
+// STORE whose head lane groups line up, and then reported done.
+template <int EPI>
+GemmParams reduce_params(const GemmParams& p) {
+  GemmParams q = p;
+  const int lanes = p.rd_hd / 4;
+  const bool ok = EPI == EPI_STORE && p.rd_D && p.rd_o && lanes > 0 && lanes <= 64 &&
+                  (lanes & (lanes - 1)) == 0 && (p.N / 4) % lanes == 0;
+  if (!ok) q.rd_D = nullptr;
+  else if (p.rd_done) *p.rd_done = 1;
+  return q;
+}
+
 // A split STORE with fp32 output whose caller takes the partial slabs
 // itself (split_defer set): report the slab count, skip the reduction.
 template <int EPI, typename TO>
@@ -932,7 +955,8 @@ bool launch_big(const GemmParams& p, hipStream_t s) {
     if (defer_split<EPI, TO>(p, nz)) return true;
     if (nz > 1) {
       const int64_t groups = (int64_t)p.M * (p.N / 4);
-      hipLaunchKernelGGL((gemm_reduce_k<EPI, TO>), dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, s, p, nz);
+      hipLaunchKernelGGL((gemm_reduce_k<EPI, TO>), dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, s,
+                         reduce_params<EPI>(p), nz);
     }
   }
   return true;
@@ -979,7 +1003,8 @@ void launch_t(const GemmParams& p, hipStream_t s) {
   if constexpr (EPI == EPI_STORE || EPI == EPI_RESID) {
     if (nz > 1) {
       const int64_t groups = (int64_t)p.M * (p.N / 4);
-      hipLaunchKernelGGL((gemm_reduce_k<EPI, TO>), dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, s, p, nz);
+      hipLaunchKernelGGL((gemm_reduce_k<EPI, TO>), dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, s,
+                         reduce_params<EPI>(p), nz);
     }
   }
 }

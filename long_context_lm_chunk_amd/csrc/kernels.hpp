@@ -34,6 +34,12 @@ struct GemmParams {
   // order) instead of reducing them into C; *split_defer receives nz (1 when
   // the launch was not split and C holds the result)
   int* split_defer = nullptr;
+  // STORE, when the launch is split and reduced into C: the reduction pass
+  // also writes rd_D[h][row] = sum over the rd_hd columns of head h of
+  // rd_o (bf16 or fp32 as C, row stride ldc) times C as stored (the
+  // attention backward's rowsum(O * dO)), and sets *rd_done = 1; it is left
+  // alone otherwise (rd_hd / 4 a power of two <= 64 dividing N / 4)
+  const void* rd_o = nullptr; float* rd_D = nullptr; int rd_hd = 0; int* rd_done = nullptr;
 };
 
 // Returns 0, or -1 for an epilogue/layout combination that is not built.
@@ -77,8 +83,9 @@ void rope_table(int64_t pos0, int n, int half, const double* theta, float2* cs, 
 // hd <= 128, hd % 16 == 0, cap % 16 == 0
 void qkv_rope(const void* qkv, int n, int H, int hd, int64_t pos0, const float2* cs, void* q_out,
               void* kring, void* vring, void* vtring, void* ktring, int64_t cap, bool bf16, hipStream_t s);
-// the rotation's transpose applied to dQ and dK inside dqkv [n][3*H*hd]
-void rope_bwd(void* dqkv, int n, int H, int hd, const float2* cs, bool bf16, hipStream_t s);
+// the rotation's transpose applied to dQ (parts bit 0) and dK (bit 1) inside
+// dqkv [n][3*H*hd]
+void rope_bwd(void* dqkv, int n, int H, int hd, const float2* cs, bool bf16, hipStream_t s, int parts = 3);
 void convert_weight(const void* src, int rows, int cols, bool transpose, int interleave16_half,
                     void* dst, bool bf16, hipStream_t s);
 // dst (canonical [in][out] fp32) = W0 + delta (delta alone when w0 is null), from the
@@ -122,11 +129,18 @@ struct AttnParams {
   // key-range split scratch (optional): part [max_split][n][H*hd] fp32,
   // part_ml [max_split][H][n][2]
   float* part = nullptr; float* part_ml = nullptr; int max_split = 1;
+  // optional: (cos, sin) of each row's rotary angles, [n][hd/2] (rope_table):
+  // the backward then applies the rotation's transpose to dQ and dK where its
+  // kernels can (swa_bwd's return value says which)
+  const float2* rope_cs = nullptr;
 };
 void swa_fwd(const AttnParams& p, bool bf16, hipStream_t s);
 // dQ on s, dK/dV on s_kv (the two are independent; the caller orders s_kv
-// after the inputs and joins it before using dK/dV; s_kv may equal s)
-void swa_bwd(const AttnParams& p, bool bf16, hipStream_t s, hipStream_t s_kv);
+// after the inputs and joins it before using dK/dV; s_kv may equal s).
+// Returns which gradients left rotated back when rope_cs is set: bit 0 dQ
+// (the staged dQ kernel or the split combine), bit 1 dK (the staged dK/dV
+// kernel); the caller applies rope_bwd to the others.
+int swa_bwd(const AttnParams& p, bool bf16, hipStream_t s, hipStream_t s_kv);
 // whether swa_bwd takes its staged dK/dV path (which reads qtr / gtr) for
 // this head size and type
 bool swa_bwd_reads_transposes(int hd, bool bf16);

@@ -731,8 +731,12 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
     GemmParams gdo;   // dO = dh . Wo  (Wo^T [d][d])
     gdo.A = m->dh_lo; gdo.lda = d; gdo.B = ly.woT; gdo.ldb = d; gdo.M = n; gdo.N = d; gdo.K = d;
     gdo.C = m->dout; gdo.ldc = d;
+    // D = rowsum(O * dO) per head: in the split product's reduction pass
+    // when it has one, else by its own pass
+    int rd_done = 0;
+    gdo.rd_o = b.o; gdo.rd_D = m->Dattn; gdo.rd_hd = m->hd; gdo.rd_done = &rd_done;
     rc = run_gemm(m, gdo, true, true, EPI_STORE, false, s); if (rc) return rc;
-    attn_rowdot(b.o, m->dout, n, m->H, m->hd, m->Dattn, bf, s);
+    if (!rd_done) attn_rowdot(b.o, m->dout, n, m->H, m->hd, m->Dattn, bf, s);
     AttnParams ap;
     ap.q = b.q; ap.ldq = d; ap.kring = ly.kring; ap.vring = ly.vring; ap.cap = ly.cap;
     ap.n = n; ap.H = m->H; ap.hd = m->hd; ap.window = m->W; ap.pos0 = p0;
@@ -741,6 +745,8 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
     ap.part = m->attn_part; ap.part_ml = m->attn_ml; ap.max_split = kMaxSplit;
     ap.dq = m->dqkv; ap.dk = static_cast<char*>(m->dqkv) + (size_t)d * m->es;
     ap.dv = static_cast<char*>(m->dqkv) + (size_t)2 * d * m->es; ap.ldg = 3 * d; ap.kmin = p0;
+    ap.rope_cs = m->csB;                             // RoPE^-1 inside the kernels where they can
+    int rotated = 0;
     {
       double in = 0;
       const double tot = pairs(p0, n, m->W, p0, &in);
@@ -753,11 +759,11 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
         transpose(m->dout, n, d, d, m->gT, m->Cq, npad, bf, m->sk, true);
         ap.qtr = m->qT; ap.gtr = m->gT; ap.ldtr = m->Cq;
       }
-      swa_bwd(ap, bf, s, m->sk);
+      rotated = swa_bwd(ap, bf, s, m->sk);
       HIPCHK(hipEventRecord(m->evK1, m->sk));
       HIPCHK(hipStreamWaitEvent(s, m->evK1, 0));     // dK/dV in place for the RoPE backward
     }
-    rope_bwd(m->dqkv, n, m->H, m->hd, m->csB, bf, s);
+    rope_bwd(m->dqkv, n, m->H, m->hd, m->csB, bf, s, 3 & ~rotated);
     GemmParams gq;   // da = dqkv . Wqkv  (Wqkv^T [d][3d])
     gq.A = m->dqkv; gq.lda = 3 * d; gq.B = ly.wqkvT; gq.ldb = 3 * d; gq.M = n; gq.N = d; gq.K = 3 * d;
     gq.C = m->dtmp; gq.ldc = d; gq.split_defer = &nsl;
