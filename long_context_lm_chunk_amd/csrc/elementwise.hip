@@ -142,15 +142,41 @@ __global__ void ln_bwd_k(const float* __restrict__ dy, const float* __restrict__
 template <typename T, int NV>
 __global__ __launch_bounds__(256) void ln_fwd_reg_k(const float* __restrict__ x, int64_t ldx, int n,
                                                     float eps, T* __restrict__ y, int64_t ldy,
-                                                    float* __restrict__ mean, float* __restrict__ rstd) {
+                                                    float* __restrict__ mean, float* __restrict__ rstd,
+                                                    const float* __restrict__ sl, int nsl, int64_t sls,
+                                                    float* __restrict__ xo) {
   constexpr int D = 256 * NV;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= n) return;
   const float4* xr = reinterpret_cast<const float4*>(x + (int64_t)row * ldx);
   float4 v[NV];
+  if (sl) {
+    // the row is the residual x plus a product left as nsl K-split slabs
+    // (rows of D floats): summed in slab order, then x added, as the
+    // reduction pass would have done; the sum is stored to xo
+    const float4* s0 = reinterpret_cast<const float4*>(sl + (int64_t)row * D);
 #pragma unroll
-  for (int i = 0; i < NV; ++i) v[i] = xr[lane + 64 * i];
+    for (int i = 0; i < NV; ++i) v[i] = ldnt4(s0 + lane + 64 * i);
+    for (int z = 1; z < nsl; ++z) {
+      const float4* sz = reinterpret_cast<const float4*>(sl + z * sls + (int64_t)row * D);
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const float4 w = ldnt4(sz + lane + 64 * i);
+        v[i].x += w.x; v[i].y += w.y; v[i].z += w.z; v[i].w += w.w;
+      }
+    }
+    float4* xw = reinterpret_cast<float4*>(xo + (int64_t)row * D);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const float4 r = xr[lane + 64 * i];
+      v[i].x += r.x; v[i].y += r.y; v[i].z += r.z; v[i].w += r.w;
+      xw[lane + 64 * i] = v[i];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) v[i] = xr[lane + 64 * i];
+  }
   float s = 0.f;
 #pragma unroll
   for (int i = 0; i < NV; ++i) s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
@@ -336,6 +362,27 @@ template <> DEVI void ld8<float>(const float* p, float* v) {
   const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
   v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
+// 8 consecutive outputs of a product at element off: read from src (T), or,
+// when the product left nsl > 1 fp32 K-split slabs (slab stride sls), their
+// sum in slab order rounded to T, as the reduction pass would have stored it
+template <typename T>
+DEVI void ld8_out(const T* src, const float* sl, int nsl, int64_t sls, int64_t off, float* v) {
+  if (nsl <= 1) {
+    ld8<T>(src + off, v);
+    return;
+  }
+  float4 a = ldnt4(reinterpret_cast<const float4*>(sl + off));
+  float4 b = ldnt4(reinterpret_cast<const float4*>(sl + off + 4));
+  for (int z = 1; z < nsl; ++z) {
+    const float4 c = ldnt4(reinterpret_cast<const float4*>(sl + z * sls + off));
+    const float4 e = ldnt4(reinterpret_cast<const float4*>(sl + z * sls + off + 4));
+    a.x += c.x; a.y += c.y; a.z += c.z; a.w += c.w;
+    b.x += e.x; b.y += e.y; b.z += e.z; b.w += e.w;
+  }
+  const float w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = to_f32(from_f32<T>(w[j]));
+}
 template <typename T> DEVI void st8(T* p, const float* v);
 template <> DEVI void st8<bf16>(bf16* p, const float* v) {
   bf16x8 x;
@@ -354,7 +401,8 @@ template <> DEVI void st8<float>(float* p, const float* v) {
 // kt is set) k -> the position-permuted transposed rings [H*hd][cap] (the
 // column of a slot is kperm(slot)).  qkv [n][3*H*hd]; hd <= 128, hd % 16 == 0.
 template <typename T>
-__global__ __launch_bounds__(256) void qkv_rope_k(const T* __restrict__ qkv, int n, int H, int hd,
+__global__ __launch_bounds__(256) void qkv_rope_k(const T* __restrict__ qkv, const float* __restrict__ sl,
+                                                  int nsl, int64_t sls, int n, int H, int hd,
                                                   int64_t pos0, const float2* __restrict__ cs,
                                                   T* __restrict__ qo, T* __restrict__ kr, T* __restrict__ vr,
                                                   T* __restrict__ vt, T* __restrict__ kt, int64_t cap) {
@@ -369,11 +417,11 @@ __global__ __launch_bounds__(256) void qkv_rope_k(const T* __restrict__ qkv, int
     const int t = it / nc, c = it % nc, i0 = 8 * c;
     if (it >= 64 * nc || t0 + t >= n) continue;
     const int64_t slot = (pos0 + t0 + t) % cap;
-    const T* row = qkv + (int64_t)(t0 + t) * 3 * d + h * hd;
+    const int64_t row = (int64_t)(t0 + t) * 3 * d + h * hd;
     const float2* e = cs + (int64_t)(t0 + t) * half + i0;
     float a[8], b[8], ra[8], rb[8];
-    ld8<T>(row + i0, a);
-    ld8<T>(row + half + i0, b);
+    ld8_out<T>(qkv, sl, nsl, sls, row + i0, a);
+    ld8_out<T>(qkv, sl, nsl, sls, row + half + i0, b);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const float2 w = e[j];
@@ -383,8 +431,8 @@ __global__ __launch_bounds__(256) void qkv_rope_k(const T* __restrict__ qkv, int
     T* qr = qo + (int64_t)(t0 + t) * d + h * hd;
     st8<T>(qr + i0, ra);
     st8<T>(qr + half + i0, rb);
-    ld8<T>(row + d + i0, a);
-    ld8<T>(row + d + half + i0, b);
+    ld8_out<T>(qkv, sl, nsl, sls, row + d + i0, a);
+    ld8_out<T>(qkv, sl, nsl, sls, row + d + half + i0, b);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const float2 w = e[j];
@@ -394,8 +442,8 @@ __global__ __launch_bounds__(256) void qkv_rope_k(const T* __restrict__ qkv, int
     T* krow = kr + slot * d + h * hd;
     st8<T>(krow + i0, kv[u]);
     st8<T>(krow + half + i0, kv[u] + 8);
-    ld8<T>(row + 2 * d + i0, a);
-    ld8<T>(row + 2 * d + half + i0, b);
+    ld8_out<T>(qkv, sl, nsl, sls, row + 2 * d + i0, a);
+    ld8_out<T>(qkv, sl, nsl, sls, row + 2 * d + half + i0, b);
     T* vrow = vr + slot * d + h * hd;
     st8<T>(vrow + i0, a);
     st8<T>(vrow + half + i0, b);
@@ -639,6 +687,23 @@ __global__ void rowdot_k(const T* __restrict__ o, const T* __restrict__ g, int n
   if (lane == 0) D[(int64_t)h * n + t] = s;
 }
 
+// x_out = (sum of nsl K-split slabs in slab order) + R, 4 floats per thread
+// (rows of d floats, d % 4 == 0): the reduction pass of a split product with
+// a residual, for the LayerNorm paths that do not take the slabs themselves
+__global__ void resid_slabs_k(const float* __restrict__ sl, int nsl, int64_t sls, const float* __restrict__ R,
+                              float* __restrict__ xo, int64_t groups) {
+  const int64_t g = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (g >= groups) return;
+  float4 v = ldnt4(reinterpret_cast<const float4*>(sl) + g);
+  for (int z = 1; z < nsl; ++z) {
+    const float4 w = ldnt4(reinterpret_cast<const float4*>(sl + z * sls) + g);
+    v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
+  }
+  const float4 r = reinterpret_cast<const float4*>(R)[g];
+  v.x += r.x; v.y += r.y; v.z += r.z; v.w += r.w;
+  reinterpret_cast<float4*>(xo)[g] = v;
+}
+
 inline unsigned nblk(int64_t n, int b) { return (unsigned)((n + b - 1) / b); }
 inline unsigned gs_blocks(int64_t n) { int64_t b = (n + 255) / 256; return (unsigned)(b > 65536 ? 65536 : (b < 1 ? 1 : b)); }
 
@@ -663,8 +728,8 @@ void layernorm_fwd(const float* x, int64_t ldx, int n, int d, float eps, void* y
   }
   if (d % 256 == 0 && d <= 4096 && ldx % 4 == 0 && ldy % 4 == 0) {
     switch (d / 256) {
-#define LNF(NV) case NV: TSEL(bf, hipLaunchKernelGGL((ln_fwd_reg_k<bf16, NV>), dim3(nblk(n, 4)), dim3(256), 0, s, x, ldx, n, eps, (bf16*)y, ldy, mean, rstd), \
-                               hipLaunchKernelGGL((ln_fwd_reg_k<float, NV>), dim3(nblk(n, 4)), dim3(256), 0, s, x, ldx, n, eps, (float*)y, ldy, mean, rstd)); return;
+#define LNF(NV) case NV: TSEL(bf, hipLaunchKernelGGL((ln_fwd_reg_k<bf16, NV>), dim3(nblk(n, 4)), dim3(256), 0, s, x, ldx, n, eps, (bf16*)y, ldy, mean, rstd, nullptr, 0, (int64_t)0, nullptr), \
+                               hipLaunchKernelGGL((ln_fwd_reg_k<float, NV>), dim3(nblk(n, 4)), dim3(256), 0, s, x, ldx, n, eps, (float*)y, ldy, mean, rstd, nullptr, 0, (int64_t)0, nullptr)); return;
       LNF(1) LNF(2) LNF(3) LNF(4) LNF(5) LNF(6) LNF(7) LNF(8) LNF(9) LNF(10) LNF(11) LNF(12)
       LNF(13) LNF(14) LNF(15) LNF(16)
 #undef LNF
@@ -673,6 +738,25 @@ void layernorm_fwd(const float* x, int64_t ldx, int n, int d, float eps, void* y
   }
   TSEL(bf, hipLaunchKernelGGL(ln_fwd_k<bf16>, dim3(nblk(n, 4)), dim3(256), 0, s, x, ldx, n, d, eps, (bf16*)y, ldy, mean, rstd),
        hipLaunchKernelGGL(ln_fwd_k<float>, dim3(nblk(n, 4)), dim3(256), 0, s, x, ldx, n, d, eps, (float*)y, ldy, mean, rstd));
+}
+
+void layernorm_fwd_resid(const float* slabs, int nsl, const float* R, float* x_out, int n, int d, float eps,
+                         void* y, int64_t ldy, float* mean, float* rstd, bool bf, hipStream_t s) {
+  if (n <= 0) return;
+  const int64_t sls = (int64_t)n * d;
+  if (n >= 64 && d % 256 == 0 && d <= 4096 && ldy % 4 == 0) {
+    switch (d / 256) {
+#define LNF(NV) case NV: TSEL(bf, hipLaunchKernelGGL((ln_fwd_reg_k<bf16, NV>), dim3(nblk(n, 4)), dim3(256), 0, s, R, (int64_t)d, n, eps, (bf16*)y, ldy, mean, rstd, slabs, nsl, sls, x_out), \
+                               hipLaunchKernelGGL((ln_fwd_reg_k<float, NV>), dim3(nblk(n, 4)), dim3(256), 0, s, R, (int64_t)d, n, eps, (float*)y, ldy, mean, rstd, slabs, nsl, sls, x_out)); return;
+      LNF(1) LNF(2) LNF(3) LNF(4) LNF(5) LNF(6) LNF(7) LNF(8) LNF(9) LNF(10) LNF(11) LNF(12)
+      LNF(13) LNF(14) LNF(15) LNF(16)
+#undef LNF
+      default: break;
+    }
+  }
+  const int64_t groups = (int64_t)n * (d / 4);
+  hipLaunchKernelGGL(resid_slabs_k, dim3(nblk(groups, 256)), dim3(256), 0, s, slabs, nsl, sls, R, x_out, groups);
+  layernorm_fwd(x_out, d, n, d, eps, y, ldy, mean, rstd, bf, s);
 }
 
 void layernorm_bwd_acc(const float* dy, const float* x, const float* mean, const float* rstd, int n,
@@ -730,11 +814,13 @@ void rope_table(int64_t pos0, int n, int half, const double* theta, float2* cs, 
 }
 
 void qkv_rope(const void* qkv, int n, int H, int hd, int64_t pos0, const float2* cs, void* q_out,
-              void* kring, void* vring, void* vtring, void* ktring, int64_t cap, bool bf, hipStream_t s) {
+              void* kring, void* vring, void* vtring, void* ktring, int64_t cap, bool bf, hipStream_t s,
+              const float* slabs, int nsl) {
   if (n <= 0) return;
   dim3 grid((n + 63) / 64, H);
-  TSEL(bf, hipLaunchKernelGGL(qkv_rope_k<bf16>, grid, dim3(256), 0, s, (const bf16*)qkv, n, H, hd, pos0, cs, (bf16*)q_out, (bf16*)kring, (bf16*)vring, (bf16*)vtring, (bf16*)ktring, cap),
-       hipLaunchKernelGGL(qkv_rope_k<float>, grid, dim3(256), 0, s, (const float*)qkv, n, H, hd, pos0, cs, (float*)q_out, (float*)kring, (float*)vring, (float*)vtring, (float*)ktring, cap));
+  const int64_t sls = (int64_t)n * 3 * H * hd;
+  TSEL(bf, hipLaunchKernelGGL(qkv_rope_k<bf16>, grid, dim3(256), 0, s, (const bf16*)qkv, slabs, nsl, sls, n, H, hd, pos0, cs, (bf16*)q_out, (bf16*)kring, (bf16*)vring, (bf16*)vtring, (bf16*)ktring, cap),
+       hipLaunchKernelGGL(qkv_rope_k<float>, grid, dim3(256), 0, s, (const float*)qkv, slabs, nsl, sls, n, H, hd, pos0, cs, (float*)q_out, (float*)kring, (float*)vring, (float*)vtring, (float*)ktring, cap));
 }
 
 void transpose(const void* src, int rows, int cols, int64_t lds_, void* dst, int64_t ldd, int rows_pad,

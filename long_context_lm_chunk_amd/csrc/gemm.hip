@@ -914,11 +914,11 @@ GemmParams reduce_params(const GemmParams& p) {
   return q;
 }
 
-// A split STORE with fp32 output whose caller takes the partial slabs
-// itself (split_defer set): report the slab count, skip the reduction.
+// A split STORE or RESID whose caller takes the partial slabs itself
+// (split_defer set): report the slab count, skip the reduction.
 template <int EPI, typename TO>
 bool defer_split(const GemmParams& p, int nz) {
-  if (EPI != EPI_STORE || sizeof(TO) != 4 || !p.split_defer) return false;
+  if ((EPI != EPI_STORE && EPI != EPI_RESID) || !p.split_defer) return false;
   *p.split_defer = nz;
   return true;
 }

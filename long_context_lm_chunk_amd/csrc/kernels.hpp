@@ -29,10 +29,11 @@ struct GemmParams {
   // split-K scratch (optional; STORE/RESID launches with too few tiles):
   // split_ws holds up to split_cap floats
   float* split_ws = nullptr; int64_t split_cap = 0;
-  // STORE with fp32 output only: when set, a split launch leaves its nz
-  // partial slabs in split_ws ([nz][M][N], summed by the consumer in slab
-  // order) instead of reducing them into C; *split_defer receives nz (1 when
-  // the launch was not split and C holds the result)
+  // STORE or RESID: when set, a split launch leaves its nz partial slabs in
+  // split_ws ([nz][M][N], summed by the consumer in slab order, then the
+  // residual added, then rounded to C's type) instead of reducing them into
+  // C; *split_defer receives nz (1 when the launch was not split and C holds
+  // the result)
   int* split_defer = nullptr;
   // STORE, when the launch is split and reduced into C: the reduction pass
   // also writes rd_D[h][row] = sum over the rd_hd columns of head h of
@@ -67,6 +68,10 @@ void embed(const int32_t* tok, int n, const void* E, int d, int V, bool bf16, fl
            hipStream_t s);
 void layernorm_fwd(const float* x, int64_t ldx, int n, int d, float eps, void* y, int64_t ldy,
                    float* mean, float* rstd, bool bf16, hipStream_t s);
+// x_out = R + (sum of the nsl fp32 K-split slabs [nsl][n][d] of a product,
+// in slab order), then the LayerNorm of x_out as layernorm_fwd
+void layernorm_fwd_resid(const float* slabs, int nsl, const float* R, float* x_out, int n, int d, float eps,
+                         void* y, int64_t ldy, float* mean, float* rstd, bool bf16, hipStream_t s);
 // acc += LN_backward(dy) ; optionally acc_lo = low-precision copy of the new acc.
 // dy may be nslab partial slabs (row r of slab z at dy + z*slab_stride +
 // r*d), summed in slab order.
@@ -81,8 +86,11 @@ void rope_table(int64_t pos0, int n, int half, const double* theta, float2* cs, 
 // (pos0 + t) mod cap; v and (when ktring is set) k also to the transposed
 // rings [H*hd][cap], column kperm(slot); cs from rope_table(pos0, n, hd/2).
 // hd <= 128, hd % 16 == 0, cap % 16 == 0
+// (slabs, nsl > 1: the QKV product was left as nsl fp32 K-split slabs
+// [nsl][n][3*H*hd], read instead of qkv)
 void qkv_rope(const void* qkv, int n, int H, int hd, int64_t pos0, const float2* cs, void* q_out,
-              void* kring, void* vring, void* vtring, void* ktring, int64_t cap, bool bf16, hipStream_t s);
+              void* kring, void* vring, void* vtring, void* ktring, int64_t cap, bool bf16, hipStream_t s,
+              const float* slabs = nullptr, int nsl = 1);
 // the rotation's transpose applied to dQ (parts bit 0) and dK (bit 1) inside
 // dqkv [n][3*H*hd]
 void rope_bwd(void* dqkv, int n, int H, int hd, const float2* cs, bool bf16, hipStream_t s, int parts = 3);

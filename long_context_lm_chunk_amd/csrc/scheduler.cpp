@@ -551,19 +551,29 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
   rope_table(p0, n, m->hd / 2, m->theta, m->csB, s);
   m->logit_rows = n;
   // ---------------- forward of the fast blocks
+  // The QKV, output and down products of a chunk leave their K-split
+  // partial slabs (when split) for their consumer to sum: the RoPE pass for
+  // QKV, the next LayerNorm (which adds the residual and stores the sum) for
+  // the others; pend / pend_r: a down product still owed to the residual.
+  int pend = 1;
+  const float* pend_r = nullptr;
   for (int j = 0; j < q; ++j) {
     const int l = m->f0 + j;
     Layer& ly = m->layers[l];
     PB& b = m->pb[j];
     const float* x2 = x2_0;
+    int npo = 1;                                     // slabs of the output product
     if (j > 0) {
-      layernorm_fwd(b.xin, d, n, d, eps, b.a, d, b.mean1, b.rstd1, bf, s);
+      if (pend > 1) layernorm_fwd_resid(m->split_ws, pend, pend_r, b.xin, n, d, eps, b.a, d, b.mean1, b.rstd1, bf, s);
+      else layernorm_fwd(b.xin, d, n, d, eps, b.a, d, b.mean1, b.rstd1, bf, s);
+      pend = 1;
       GemmParams g;
+      int nq = 1;
       g.A = b.a; g.lda = d; g.B = ly.wqkv; g.ldb = d; g.M = n; g.N = 3 * d; g.K = d;
-      g.C = m->qkvB; g.ldc = 3 * d;
+      g.C = m->qkvB; g.ldc = 3 * d; g.split_defer = &nq;
       rc = run_gemm(m, g, true, true, EPI_STORE, false, s); if (rc) return rc;
       qkv_rope(m->qkvB, n, m->H, m->hd, p0, m->csB, b.q, ly.kring, ly.vring, ly.vtring, ly.ktring, ly.cap,
-               bf, s);
+               bf, s, nq > 1 ? m->split_ws : nullptr, nq);
       AttnParams ap;
       ap.q = b.q; ap.ldq = d; ap.kring = ly.kring; ap.vring = ly.vring; ap.vtring = ly.vtring; ap.cap = ly.cap;
       ap.n = n; ap.H = m->H; ap.hd = m->hd; ap.window = m->W; ap.pos0 = p0; ap.o = b.o; ap.ldo = d;
@@ -575,7 +585,7 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
       }
       GemmParams go;
       go.A = b.o; go.lda = d; go.B = ly.wo; go.ldb = d; go.M = n; go.N = d; go.K = d;
-      go.C = b.x2; go.ldc = d; go.R = b.xin; go.ldr = d;
+      go.C = b.x2; go.ldc = d; go.R = b.xin; go.ldr = d; go.split_defer = &npo;
       rc = run_gemm(m, go, true, true, EPI_RESID, true, s); if (rc) return rc;
       x2 = b.x2;
     }
@@ -583,7 +593,8 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
     // block's ran before them on the in-order update stream)
     const bool owed = j == 0 && m->sgd_open;
     if (owed) HIPCHK(hipStreamWaitEvent(s, m->evR1[0], 0));   // up updated, b and act read
-    layernorm_fwd(x2, d, n, d, eps, b.b, d, b.mean2, b.rstd2, bf, s);
+    if (npo > 1) layernorm_fwd_resid(m->split_ws, npo, b.xin, b.x2, n, d, eps, b.b, d, b.mean2, b.rstd2, bf, s);
+    else layernorm_fwd(x2, d, n, d, eps, b.b, d, b.mean2, b.rstd2, bf, s);
     GemmParams gu;
     gu.A = b.b; gu.lda = d; gu.B = ly.wup; gu.B2 = m->fast[j].s_up; gu.ldb = d; gu.M = n; gu.N = F2; gu.K = d;
     gu.C = b.z; gu.ldc = F2; gu.C2 = b.act; gu.ldc2 = F;
@@ -594,9 +605,12 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
       m->sgd_open = false;
     }
     GemmParams gd;
+    int nd = 1;
     gd.A = b.act; gd.lda = F; gd.B = ly.wdn; gd.B2 = m->fast[j].s_dn; gd.ldb = F; gd.M = n; gd.N = d; gd.K = F;
     gd.C = ly.swup ? b.xm : xout; gd.ldc = d; gd.R = x2; gd.ldr = d;
+    if (!ly.swup) gd.split_defer = &nd;
     rc = run_gemm(m, gd, true, true, EPI_RESID, true, s); if (rc) return rc;
+    if (nd > 1) { pend = nd; pend_r = x2; }
     if (ly.swup) {
       // frozen second MLP: LN3 -> up + activation (pre-activations kept for
       // the backward) -> down + residual
@@ -611,7 +625,8 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
       rc = run_gemm(m, sd, true, true, EPI_RESID, true, s); if (rc) return rc;
     }
   }
-  layernorm_fwd(m->xL, d, n, d, eps, m->fN, d, m->meanf, m->rstdf, bf, s);
+  if (pend > 1) layernorm_fwd_resid(m->split_ws, pend, pend_r, m->xL, n, d, eps, m->fN, d, m->meanf, m->rstdf, bf, s);
+  else layernorm_fwd(m->xL, d, n, d, eps, m->fN, d, m->meanf, m->rstdf, bf, s);
 
   // ---------------- fused head + cross-entropy
   {
