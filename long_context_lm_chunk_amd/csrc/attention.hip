@@ -727,6 +727,15 @@ __global__ __launch_bounds__(stg::NTHR, 1) void swa_fwd_bf16_128_k(AttnParams p)
                                                0, 0, 0);
   };
 
+  // the lane's fragment offsets within a stage: K fragment ks of key half kb
+  // at ka[ks] + kb * 32 rows, V^T fragment (kb, hf) of head-dim block b at
+  // va[2 * kb + hf] + b * 32 rows (the swizzle depends on the lane only)
+  uint32_t ka[8], va[4];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) ka[ks] = ql * ROWK + (((2 * ks + hl) ^ (ql & 15)) * 16);
+#pragma unroll
+  for (int kh = 0; kh < 4; ++kh) va[kh] = TILE_K + ql * ROWT + (((2 * kh + hl) ^ ((ql >> 1) & 7)) * 16);
+
   if (tb < te) {
     prep();
     fire(0);
@@ -739,19 +748,16 @@ __global__ __launch_bounds__(stg::NTHR, 1) void swa_fwd_bf16_128_k(AttnParams p)
     __syncthreads();                       // every wave's; the other stage is free
     if (it + 1 < te) fire(stage ^ 1);
     const char* Ks = smem + stage * STAGE_F;
-    const char* Vt = Ks + TILE_K;
     const int64_t kt = ktA + (int64_t)it * KT;
     // all 16 K fragments of the tile first, then the 16 score products;
     // the registers then take the 16 V^T fragments, whose reads run under
     // the softmax arithmetic
     bf16x8 fr[16];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int krow = kb * 32 + ql;
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks)
-        fr[kb * 8 + ks] = *reinterpret_cast<const bf16x8*>(Ks + krow * ROWK + (((2 * ks + hl) ^ (krow & 15)) * 16));
-    }
+        fr[kb * 8 + ks] = *reinterpret_cast<const bf16x8*>(Ks + ka[ks] + kb * 32 * ROWK);
     __builtin_amdgcn_sched_barrier(0);
     f32x16 s[2];
     const f32x16 zero = {};
@@ -766,10 +772,8 @@ __global__ __launch_bounds__(stg::NTHR, 1) void swa_fwd_bf16_128_k(AttnParams p)
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const int c = 4 * kb + 2 * hf + hl, trow = b * 32 + ql;
-          fr[kb * 8 + hf * 4 + b] = *reinterpret_cast<const bf16x8*>(Vt + trow * ROWT + ((c ^ ((trow >> 1) & 7)) * 16));
-        }
+        for (int b = 0; b < 4; ++b)
+          fr[kb * 8 + hf * 4 + b] = *reinterpret_cast<const bf16x8*>(Ks + va[2 * kb + hf] + b * 32 * ROWT);
     __builtin_amdgcn_sched_barrier(0);
     const bool interior = (kt + KT - 1 <= first) && (kt > last - p.window);
     if (!interior) {
@@ -782,12 +786,15 @@ __global__ __launch_bounds__(stg::NTHR, 1) void swa_fwd_bf16_128_k(AttnParams p)
           s[kb][r] = (uint32_t)(-rel) < wlen ? s[kb][r] : -INFINITY;
         }
     }
+    // (IEEE maximum: one three-input instruction per two scores, and no
+    // quieting of the products' outputs first, which maxnum needs)
     float tmax = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) tmax = fmaxf(tmax, fmaxf(s[kb][r], s[kb][r + 1]));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * sc;
+      for (int r = 0; r < 16; r += 2)
+        tmax = __builtin_elementwise_maximum(tmax, __builtin_elementwise_maximum(s[kb][r], s[kb][r + 1]));
+    tmax = __builtin_elementwise_maximum(tmax, __shfl_xor(tmax, 32, 64)) * sc;
     // lazy rescaling as in swa_fwd32_k
     const bool bump = tmax > m + 8.f;
     if (__any(bump)) {
