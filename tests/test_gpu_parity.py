@@ -20,6 +20,7 @@ import pytest
 import torch
 
 import synth
+from oracle import cpp
 from oracle import ttt_oracle as O
 
 pytestmark = pytest.mark.gpu
@@ -29,6 +30,8 @@ BAR = {"fp32": 1e-4, "bf16": 2e-2}
 # numbers near ln V, so its relative error is the loss error magnified by
 # |l| / |l(lr) - l(0)| (10^2 to 10^3 here); a diagnostic, with a bar of its own.
 DLOSS_BAR = {"fp32": 1e-3, "bf16": 5e-2}
+# Models up to this width are also checked against the plain C++ oracle.
+CPP_ORACLE_MAX_D = 256
 
 
 def _gpu():
@@ -84,13 +87,23 @@ def run_pair(cfg, dtype=None, std=0.02, T=None, chunk=None, lr=None, steps=1, pr
     rfw = O.fast_weights_canonical(ref)
     model0 = O.OracleModel(cfg, w)
     w0 = [a for f in model0.initial_fast() for a in f.values()]
-    out = dict(
-        loss=float(np.max(np.abs(losses - ref["losses"]) / np.maximum(np.abs(ref["losses"]), 1e-12))),
-        W=max(rel(a, b) for a, b in zip(fw, rfw)),
-        dW=max(rel(a, b - c) for a, b, c in zip(fd, rfw, w0)),
-        dWmax=max(float(np.abs(a - (b - c)).max() / max(np.abs(b - c).max(), 1e-300))
-                  for a, b, c in zip(fd, rfw, w0)),
-        losses=losses, ref=ref["losses"], model=m, w=w, x=x)
+
+    def errors(ref_losses, ref_fw):
+        return dict(
+            loss=float(np.max(np.abs(losses - ref_losses) / np.maximum(np.abs(ref_losses), 1e-12))),
+            W=max(rel(a, b) for a, b in zip(fw, ref_fw)),
+            dW=max(rel(a, b - c) for a, b, c in zip(fd, ref_fw, w0)),
+            dWmax=max(float(np.abs(a - (b - c)).max() / max(np.abs(b - c).max(), 1e-300))
+                      for a, b, c in zip(fd, ref_fw, w0)))
+
+    out = errors(ref["losses"], rfw)
+    if cfg["d_model"] <= CPP_ORACLE_MAX_D:
+        # the plain C++ oracle too: each error is the larger of the two
+        cref = cpp.prefill(cfg, w, x, chunk, lr, steps)
+        ce = errors(cref["losses"], cref["fast"])
+        say(f"  C++ oracle: loss {ce['loss']:.2e} W {ce['W']:.2e} dW(max/max) {ce['dWmax']:.2e}")
+        out = {k: max(out[k], ce[k]) for k in out}
+    out.update(losses=losses, ref=ref["losses"], model=m, w=w, x=x)
     if lr0_too:
         l0 = m.prefill(tok, chunk, 0.0, steps).cpu().numpy()
         r0 = O.prefill(cfg, w, x, chunk, 0.0, steps)["losses"]
@@ -326,11 +339,19 @@ def test_decode_teacher_forced_matches_oracle(static):
     st = O.prefill(cfg, w, x, 16, 0.05, return_state=True)
     first = int(np.argmax(st["last_logits"]))
     assert toks[0] == first
-    d = O.decode(st, 40, forced=np.array(toks + [int(np.argmax(logits[-1]))]))
+    forced = np.array(toks + [int(np.argmax(logits[-1]))])
+    d = O.decode(st, 40, forced=forced)
     L = np.array(logits)
     err = np.abs(L - d["logits"]).max() / np.abs(d["logits"]).max()
     say(f"  decode logits err {err:.2e}")
     assert err < 1e-4
+    co = cpp.CppOracle(cfg, w)
+    co.prefill(x, 16, 0.05)
+    dc = co.decode(41, forced=forced)
+    errc = np.abs(L - dc["logits"][:40]).max() / np.abs(dc["logits"]).max()
+    say(f"  decode logits err (C++ oracle) {errc:.2e}")
+    assert errc < 1e-4
+    np.testing.assert_allclose(dc["update_losses"], d["update_losses"], rtol=1e-10)
     for i in range(39):
         srt = np.sort(d["logits"][i])
         if srt[-1] - srt[-2] > 1e-3:
