@@ -36,8 +36,8 @@ PEAK_HBM_GBS = 8000.0
 # (FETCH_SIZE reads 0.5x the bytes read, WRITE_SIZE 1.0x the bytes written),
 # averaged over the two launch shapes.  Valid only for the GEMM source it was
 # measured on (sha256 of csrc/gemm.hip); otherwise reported as null.
-SGD_TRAFFIC = {"gemm_src_sha256": "d47d60e8bb567725c2b97b2aaca27f57bd5ce8c7dd467fd49f9d29f78e6211b2",
-               "bytes_per_launch": 659.5e6,
+SGD_TRAFFIC = {"gemm_src_sha256": "757c73ed1714f323c1667233b4ee441fba84acc2d61e9b30584ddb91be2b081c",
+               "bytes_per_launch": 656.8e6,
                "profile": "profiles/sgd_gemm_3B_chunk1024_traffic.md"}
 
 
