@@ -6,7 +6,7 @@ file and stored next to it (``<case>.npz``).  The script calls only the
 oracle (``oracle/``) and the seeded input generator (``synth/``): no stored
 value comes from the HIP path.
 
-    python tests/golden/oracle_fixtures.py c2_full c3_5120 c4_10240
+    python tests/golden/oracle_fixtures.py c2_full c3_5120 c3_full c4_10240
 
 Each case is a workload read with the test-time inner loop over a prefix of
 its context (every chunk's loss returned before that chunk's update, End-to-
@@ -17,6 +17,8 @@ End Test-Time Training for Long Context, forum post TL;DR "Inner Loop"):
 * ``c3_5120``   the 760M-shape workload (head size 96, SwiGLU, 6 fast blocks)
   over 5120 tokens: the 4096-key window fills and the fast blocks' K/V rings
   (4096 + 512 positions) wrap;
+* ``c3_full``   the same workload over its whole context (32768 tokens, 64
+  chunks of 512);
 * ``c4_10240``  the 3B-shape workload over 10240 tokens: full 8192-key
   windows, the fast blocks' rings (8192 + 1024 positions) wrap, two blocks
   of the frozen layers.
@@ -47,6 +49,7 @@ import synth  # noqa: E402
 CASES = {
     "c2_full": dict(workload="c2", T=8192),
     "c3_5120": dict(workload="c3", T=5120),
+    "c3_full": dict(workload="c3", T=32768),
     "c4_10240": dict(workload="c4", T=10240),
 }
 # The positions of the 512K-context workload on the tiny fp32 model: its
