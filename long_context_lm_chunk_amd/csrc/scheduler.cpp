@@ -163,8 +163,9 @@ struct ttt_model {
   hipEvent_t evC = nullptr;             // all updates of the chunk done
   // Within a prefill the chain does not wait for the chunk's updates at its
   // end: the next chunk's forward waits for the first fast block's up
-  // update (evR1[0]) before that block's MLP and for its down update (evC)
-  // before the down product.  sgd_defer asks chunk_step for that; sgd_open
+  // update (evR1[0]) before that block's up product (for the transposes of
+  // its operands (evR2[0]) before the LayerNorm feeding it) and for its down
+  // update (evC) before the down product.  sgd_defer asks chunk_step for that; sgd_open
   // says such waits are owed.
   bool sgd_defer = false, sgd_open = false;
   hipStream_t sk = nullptr;             // dK/dV of the attention backward, beside dQ
@@ -591,10 +592,15 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
     }
     // the previous chunk's updates of block 0 (up, then down; every other
     // block's ran before them on the in-order update stream)
+    // The LayerNorm only rewrites b, which the up update's operand
+    // transposes have read (evR2[0]), so it runs beside that update; the up
+    // product needs the updated matrix and act read by the down update's
+    // transposes (evR1[0]).
     const bool owed = j == 0 && m->sgd_open;
-    if (owed) HIPCHK(hipStreamWaitEvent(s, m->evR1[0], 0));   // up updated, b and act read
+    if (owed) HIPCHK(hipStreamWaitEvent(s, m->evR2[0], 0));   // b read
     if (npo > 1) layernorm_fwd_resid(m->split_ws, npo, b.xin, b.x2, n, d, eps, b.b, d, b.mean2, b.rstd2, bf, s);
     else layernorm_fwd(x2, d, n, d, eps, b.b, d, b.mean2, b.rstd2, bf, s);
+    if (owed) HIPCHK(hipStreamWaitEvent(s, m->evR1[0], 0));   // up updated, act read
     GemmParams gu;
     gu.A = b.b; gu.lda = d; gu.B = ly.wup; gu.B2 = m->fast[j].s_up; gu.ldb = d; gu.M = n; gu.N = F2; gu.K = d;
     gu.C = b.z; gu.ldc = F2; gu.C2 = b.act; gu.ldc2 = F;
