@@ -696,34 +696,22 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
     // [F][d]).  dz is rewritten here: the update stream must have read the
     // block above's.
     if (j + 1 < q) HIPCHK(hipStreamWaitEvent(s, m->evR2[j + 1], 0));
-    GemmParams ga;
-    ga.A = m->dh_lo; ga.lda = d; ga.B = fw.ct_dn; ga.ldb = d; ga.M = n; ga.N = F; ga.K = d;
-    ga.C = m->dz; ga.ldc = F2; ga.Z = b.z; ga.ldz = F2; ga.act_swiglu = m->c.mlp == TTT_MLP_SWIGLU;
-    rc = run_gemm(m, ga, true, true, EPI_ACTBWD, false, s); if (rc) return rc;
-    // Wdn -= lr * dh^T act   ([d][F], reduction over the chunk's tokens).
-    // The update runs on the update stream: its operands are transposed there
-    // (after ga has read the old weights), then the chain goes on at once.
     ttt_model::TOps& to = m->tops[j];
-    auto update_dn = [&]() -> int {
-      HIPCHK(hipEventRecord(m->evT1[j], s));
-      HIPCHK(hipStreamWaitEvent(m->sc, m->evT1[j], 0));
+    // The update stream's pieces: operand transposes, then the SGD products.
+    auto trans_dn = [&]() {               // operands of the down update
       transpose(m->dh_lo, n, d, d, to.dhT, m->Cp, np, bf, m->sc);
       transpose(b.act, n, F, F, to.actT, m->Cp, np, bf, m->sc);
-      HIPCHK(hipEventRecord(m->evR1[j], m->sc));      // dh_lo and act read
+    };
+    // Wdn -= lr * dh^T act   ([d][F], reduction over the chunk's tokens)
+    auto sgd_dn = [&]() -> int {
       GemmParams gw;
       gw.A = to.dhT; gw.lda = m->Cp; gw.B = to.actT; gw.ldb = m->Cp; gw.M = d; gw.N = F; gw.K = np;
       gw.C = fw.m_dn; gw.ldc = F; gw.C2 = bf ? fw.s_dn : nullptr; gw.ldc2 = F; gw.alpha = lr;
       gw.C3 = fw.ct_dn; gw.ldc3 = d; gw.W0 = ly.wdn;
       return run_gemm(m, gw, true, true, EPI_SGD, true, m->sc);
     };
-    // Wup -= lr * dz^T b  (update stream, after ga has produced dz and, above
-    // block 0, gb has read the old weights)
-    auto update_up = [&]() -> int {
-      HIPCHK(hipEventRecord(m->evT2[j], s));
-      HIPCHK(hipStreamWaitEvent(m->sc, m->evT2[j], 0));
-      transpose(m->dz, n, F2, F2, to.dzT, m->Cp, np, bf, m->sc);
-      transpose(b.b, n, d, d, to.bT, m->Cp, np, bf, m->sc);
-      HIPCHK(hipEventRecord(m->evR2[j], m->sc));      // dz and b read
+    // Wup -= lr * dz^T b
+    auto sgd_up = [&]() -> int {
       GemmParams gw2;
       gw2.A = to.dzT; gw2.lda = m->Cp; gw2.B = to.bT; gw2.ldb = m->Cp; gw2.M = F2; gw2.N = d; gw2.K = np;
       gw2.C = fw.m_up; gw2.ldc = d; gw2.C2 = bf ? fw.s_up : nullptr; gw2.ldc2 = d; gw2.alpha = lr;
@@ -731,13 +719,54 @@ int chunk_step(ttt_model* m, int64_t p0, int n, const float* x2_0, const int32_t
       return run_gemm(m, gw2, true, true, EPI_SGD, true, m->sc);
     };
     if (j == 0) {
+      // Block 0's update operands other than dz (dh_lo, act, b) are final
+      // here: they are transposed on the update stream while ga runs, so
+      // that only dz's transpose and the up update stand between ga and
+      // the next chunk's up product.
+      HIPCHK(hipEventRecord(m->evT1[0], s));
+      HIPCHK(hipStreamWaitEvent(m->sc, m->evT1[0], 0));
+      trans_dn();
+      transpose(b.b, n, d, d, to.bT, m->Cp, np, bf, m->sc);
+    }
+    // dz = act'(z) (dh . Wdn): the activation backward runs in the product's
+    // epilogue (the product reads the weights before their update: Wdn^T
+    // [F][d]).  dz is rewritten here: the update stream must have read the
+    // block above's.
+    GemmParams ga;
+    ga.A = m->dh_lo; ga.lda = d; ga.B = fw.ct_dn; ga.ldb = d; ga.M = n; ga.N = F; ga.K = d;
+    ga.C = m->dz; ga.ldc = F2; ga.Z = b.z; ga.ldz = F2; ga.act_swiglu = m->c.mlp == TTT_MLP_SWIGLU;
+    rc = run_gemm(m, ga, true, true, EPI_ACTBWD, false, s); if (rc) return rc;
+    // The updates run on the update stream, after ga has read the old
+    // weights; the chain goes on at once.
+    if (j == 0) {
       // block 0 is the last to be updated and the first the next chunk
       // reads, up matrix first: up, then down, so that the next chunk's up
       // product can run beside the down update
-      rc = update_up(); if (rc) return rc;
-      rc = update_dn(); if (rc) return rc;
+      HIPCHK(hipEventRecord(m->evT2[0], s));
+      HIPCHK(hipStreamWaitEvent(m->sc, m->evT2[0], 0));
+      transpose(m->dz, n, F2, F2, to.dzT, m->Cp, np, bf, m->sc);
+      HIPCHK(hipEventRecord(m->evR2[0], m->sc));      // dz and b read
+      rc = sgd_up(); if (rc) return rc;
+      HIPCHK(hipEventRecord(m->evR1[0], m->sc));      // up updated; dh_lo and act read
+      rc = sgd_dn(); if (rc) return rc;
       break;   // no gradient below the first fast MLP
     }
+    auto update_dn = [&]() -> int {
+      HIPCHK(hipEventRecord(m->evT1[j], s));
+      HIPCHK(hipStreamWaitEvent(m->sc, m->evT1[j], 0));
+      trans_dn();
+      HIPCHK(hipEventRecord(m->evR1[j], m->sc));      // dh_lo and act read
+      return sgd_dn();
+    };
+    // (after gb has read the old up weights)
+    auto update_up = [&]() -> int {
+      HIPCHK(hipEventRecord(m->evT2[j], s));
+      HIPCHK(hipStreamWaitEvent(m->sc, m->evT2[j], 0));
+      transpose(m->dz, n, F2, F2, to.dzT, m->Cp, np, bf, m->sc);
+      transpose(b.b, n, d, d, to.bT, m->Cp, np, bf, m->sc);
+      HIPCHK(hipEventRecord(m->evR2[j], m->sc));      // dz and b read
+      return sgd_up();
+    };
     rc = update_dn(); if (rc) return rc;
     {
       GemmParams gb;   // db = dz . Wup (before its update: Wup^T [d][F2])
