@@ -6,7 +6,7 @@ file and stored next to it (``<case>.npz``).  The script calls only the
 oracle (``oracle/``) and the seeded input generator (``synth/``): no stored
 value comes from the HIP path.
 
-    python tests/golden/oracle_fixtures.py c2_full c3_5120 c3_full c4_10240
+    python tests/golden/oracle_fixtures.py c2_full c3_5120 c3_full c4_10240 c4_20480
 
 Each case is a workload read with the test-time inner loop over a prefix of
 its context (every chunk's loss returned before that chunk's update, End-to-
@@ -21,7 +21,9 @@ End Test-Time Training for Long Context, forum post TL;DR "Inner Loop"):
   chunks of 512);
 * ``c4_10240``  the 3B-shape workload over 10240 tokens: full 8192-key
   windows, the fast blocks' rings (8192 + 1024 positions) wrap, two blocks
-  of the frozen layers.
+  of the frozen layers;
+* ``c4_20480``  the same over 20480 tokens: 20 chunks, three blocks of the
+  frozen layers, the fast rings wrapped twice.
 
 Stored per case: every chunk loss; for every fast matrix (canonical
 ``[in][out]`` layout) its change over the whole prefill, dW = W - W0, at one
@@ -51,6 +53,7 @@ CASES = {
     "c3_5120": dict(workload="c3", T=5120),
     "c3_full": dict(workload="c3", T=32768),
     "c4_10240": dict(workload="c4", T=10240),
+    "c4_20480": dict(workload="c4", T=20480),
 }
 # The positions of the 512K-context workload on the tiny fp32 model: its
 # chunk of 1024, a window of 32, 525312 = 513 x 1024 tokens (positions up
