@@ -26,6 +26,7 @@ import pytest
 import torch
 
 import synth
+from greedy import greedy_ok
 from oracle import ttt_oracle as O
 
 pytestmark = pytest.mark.gpu
@@ -106,9 +107,6 @@ def test_3b_full_context_first_chunks_weights_and_decode_match_oracle(c4):
     _REF["loss0"] = float(ref[0])   # chunk 0's loss is read before any update
     w0 = [a for f in st["model"].initial_fast() for a in f.values()]
     rfw = O.fast_weights_canonical(st)
-    first = int(np.argmax(st["last_logits"]))
-    ll = np.sort(st["last_logits"])
-    gap0 = ll[-1] - ll[-2]
     # decode leaves the prefill state's cache and weights as they were (no
     # update within 3 positions; the cache list is replaced, not modified)
     d = O.decode(dict(st), 3, forced=np.array(toks + [int(np.argmax(logits[-1]))]))
@@ -138,13 +136,11 @@ def test_3b_full_context_first_chunks_weights_and_decode_match_oracle(c4):
     assert e32["dW"] < 1e-4
     # the two GPU runs compute the same first two chunks
     np.testing.assert_allclose(full[:2], two, rtol=1e-3)
-    # greedy tokens agree wherever the oracle's top-2 gap is clear
-    if gap0 > 1e-2:
-        assert toks[0] == first
-    srt = np.sort(d["logits"], axis=-1)
+    # greedy tokens: the oracle's argmax where its top-2 gap is clear, a
+    # near-tie elsewhere
+    assert greedy_ok(toks[0], st["last_logits"], BAR)
     for i in range(2):
-        if srt[i, -1] - srt[i, -2] > 1e-2:
-            assert toks[i + 1] == int(np.argmax(d["logits"][i]))
+        assert greedy_ok(toks[i + 1], d["logits"][i], BAR)
 
 
 @pytest.mark.timeout(1200)
@@ -219,9 +215,7 @@ def test_3b_decode_time_update_matches_oracle(c4):
     # positions where bf16 at this depth already exceeds it
     assert e_lg < max(BAR, 1.25 * e_lg_chunk_keep)
     assert max(e_tot) < BAR
-    s0 = np.sort(fw0["logits"][-1])
-    if s0[-1] - s0[-2] > 1e-2:
-        assert toks[0] == int(np.argmax(fw0["logits"][-1]))
+    assert greedy_ok(toks[0], fw0["logits"][-1], BAR)
 
 
 def _oracle_loss0(cfg, w, x):

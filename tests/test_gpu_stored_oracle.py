@@ -15,7 +15,8 @@ the inner loop through the C ABI and compares:
   W        the fast matrices themselves at the same elements:
            max |W - W*| / max |W*|
   token    the first greedy decode token equals the oracle's argmax of the
-           last position's logits wherever the top-2 gap is clear
+           last position's logits where the top-2 gap exceeds twice the
+           logit tolerance, and is one of the near-ties elsewhere
 
 Bars: 1e-4 in the float32 check mode for all of them, 2e-2 with bf16
 storage (see BF16_DW_BAR for the size of the bf16 error in dW).
@@ -31,6 +32,7 @@ import synth
 
 sys.path.insert(0, os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden"))
 import oracle_fixtures as FX  # noqa: E402
+from greedy import greedy_ok  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -114,8 +116,7 @@ def test_prefill_matches_stored_oracle(case, dtype):
     assert e_loss < BAR[dtype]
     assert max(e_w) < BAR[dtype]
     assert max(e_dw) < (BAR["fp32"] if dtype == "fp32" else BF16_DW_BAR)
-    if top[-1] - top[-2] > 1e-2:
-        assert first_tok == int(np.argmax(lg))
+    assert greedy_ok(first_tok, lg, BAR[dtype])
 
 
 @pytest.mark.timeout(600)
