@@ -19,6 +19,7 @@ chunk 0 against the oracle, every chunk against the prefill at lr = 0
 (window 8192), and the first 8 chunks of the two windows against each other
 (no query before position 8192 has more keys than either window holds).
 """
+import math
 import sys
 
 import numpy as np
@@ -216,6 +217,58 @@ def test_3b_decode_time_update_matches_oracle(c4):
     assert e_lg < max(BAR, 1.25 * e_lg_chunk_keep)
     assert max(e_tot) < BAR
     assert greedy_ok(toks[0], fw0["logits"][-1], BAR)
+
+
+@pytest.mark.timeout(1200)
+def test_3b_512k_decode_time_update_equals_prefill_of_the_same_tokens(c4):
+    """The 512K-context workload at its own size (the C4 weights, 524288
+    context tokens, positions past 2^19), by a property the oracle cannot
+    reach there: after the 512-chunk prefill, 1024 greedy decode positions
+    make one decode-time update, and a prefill of the context followed by
+    the emitted tokens makes, for its chunk 512, the same update (the
+    decode-time update equals a prefill chunk's, pinned on the oracle by
+    test_decode_update_equals_prefill_chunk).  The two runs share chunks
+    0-510 bit for bit; chunk 511 has one target more in the longer run (the
+    context's last position predicts the first emitted token there, and has
+    no target at the end of the context), which moves that chunk's update
+    by about 1/1024 of itself; beyond that they differ only in how the
+    frozen layers read the decode chunk (matrix-vector products during
+    decode, batched products in the prefill).  So the update's loss and its
+    own change of every fast matrix must agree to the bf16 bar."""
+    cfg5 = synth.config("c5")
+    cfg, w, x_unused, m = c4
+    C, lr, T = cfg["chunk"], cfg["lr"], cfg5["T"]
+    x = synth.gen_tokens(cfg5)
+    tok = torch.from_numpy(x).cuda()
+    say(f"case 3B 512K: prefill T={T}, then {C} greedy decode positions (one decode-time update)")
+    la = m.prefill(tok[:T], C, lr).cpu().numpy()
+    fd_pre = m.fast_weights(delta=True)
+    toks, upd, last = [], [], None
+    for i in range(C):
+        t, lg, ul = m.decode_step(want_logits=i == C - 1)
+        toks.append(int(t.item()))
+        upd.append(float(ul.item()))
+        if lg is not None:
+            last = int(torch.argmax(lg).item())
+    fd_a = m.fast_weights(delta=True)
+    got = [u for u in upd if not math.isnan(u)]
+    say(f"case 3B 512K: prefill of the context and the {C + 1} emitted tokens (T={T + C + 1})")
+    y = torch.cat([tok[:T], torch.tensor(toks + [last], dtype=torch.int32, device="cuda")])
+    lb = m.prefill(y, C, lr).cpu().numpy()
+    fd_b = m.fast_weights(delta=True)
+    e_dw = [float(((a - p0) - (b - p0)).abs().max() / (b - p0).abs().max())
+            for a, b, p0 in zip(fd_a, fd_b, fd_pre)]
+    e_loss = abs(got[0] - lb[T // C]) / abs(lb[T // C])
+    same = bool(np.array_equal(la[:T // C - 1], lb[:T // C - 1]))
+    say(f"  update loss {got[0]:.6f} vs prefill chunk {T // C} {lb[T // C]:.6f}: {e_loss:.2e}; "
+        f"chunk losses 0-{T // C - 2} equal: {same}; chunk {T // C - 1}: {la[-1]:.6f} (1023 targets) "
+        f"vs {lb[T // C - 1]:.6f} (1024)")
+    say("  the update's own dW max/max per matrix: " + " ".join(f"{v:.1e}" for v in e_dw))
+    assert np.all(np.isfinite(la)) and same
+    assert len(got) == 1 and not math.isnan(upd[C - 1])
+    assert lb[T // C + 1] == 0.0                       # the last chunk has no target
+    assert e_loss < BAR
+    assert max(e_dw) < BAR
 
 
 def _oracle_loss0(cfg, w, x):
